@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged tree attention hot path on one MI355X.
+
+One step = the whole hot path over one batch: append the candidates' K/V rows
+into their paged slots (taco_kv_append), then paged tree attention over every
+sequence's context (split-K partials + log-sum-exp merge where the workload is
+configured for it).  Inputs are synthetic, seeded and resident in HBM before
+the timed region; R independent input sets are rotated step to step so the
+256 MB last-level cache cannot serve the KV stream from a previous step.
+
+Prints ONE JSON line.  `value` is KV HBM bytes (algorithmic: every K/V byte of
+every sequence's context counted once) per second of attention time, in GB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KV HBM GB/s (% of peak) + verified candidate tokens/s, paged tree attn, 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+HEADLINE = "llama3_8b_decode"
+
+# launch configuration of each workload: split-K partition length (None = one
+# pass per sequence) and kernel family (auto picks by rows per KV head)
+LAUNCH = {
+    "tiny_decode": dict(split=None, path="auto"),
+    "llama3_8b_decode": dict(split=512, path="auto"),
+    "llama31_70b_verify": dict(split=1024, path="auto"),
+    "long_splitk_verify": dict(split=2048, path="auto"),
+    "fp8_kv_chain": dict(split=2048, path="auto"),
+}
+
+KERNEL_SOURCES = ["pta_device.h", "pta_valu.hip", "pta_mfma.hip", "pta_aux.hip", "pta_api.hip"]
+
+
+def launch_config(name: str) -> dict:
+    return dict(LAUNCH[name])
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_speculative_verify_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ accounting
+def kv_bytes(w) -> int:
+    """Algorithmic KV bytes of one attention pass: each K and V element of every
+    sequence's context once, plus the per-(page, KV head) scales for fp8."""
+    s = w.spec
+    elem = {"f32": 4, "bf16": 2, "fp8": 1}[s.kv_dtype]
+    Hkv, D = w.k_cache.shape[1], w.k_cache.shape[3]
+    n = int(w.ctx_lens.astype(np.int64).sum()) * Hkv * D * 2 * elem
+    if s.kv_dtype == "fp8":
+        n += int(w.pages_used.astype(np.int64).sum()) * Hkv * 2 * 4
+    return n
+
+
+def attn_flops(w) -> int:
+    """Algorithmic flops: 4 * D per (q-head, candidate, visible key) pair."""
+    D = w.q.shape[3]
+    Hq = w.q.shape[2]
+    tot = 0
+    for b in range(w.q.shape[0]):
+        C, qb = int(w.ctx_lens[b]), int(w.q_lens[b])
+        L = C - qb
+        vis = L * qb + int((w.tree_mask[b, :qb, :qb] != 0).sum())
+        tot += vis
+    return 4 * D * Hq * tot
+
+
+# ------------------------------------------------------------------ device setup
+class DeviceSet:
+    """One input set on the device plus its KV-append operands."""
+
+    def __init__(self, w, torch):
+        from workload.device import to_device
+        self.w = w
+        self.d = to_device(w)
+        s = w.spec
+        B, Qmax, Hq, D = w.q.shape
+        Hkv = w.k_cache.shape[1]
+        # the candidates' slots: logical positions L..C-1 of every sequence
+        pos = [(b, t) for b in range(B) for t in range(int(w.ctx_lens[b]) - int(w.q_lens[b]), int(w.ctx_lens[b]))]
+        slots = np.array([int(w.block_tables[b, t // 16]) * 16 + t % 16 for b, t in pos], dtype=np.int64)
+        # new rows equal to what the slots already hold, so re-appending every step is idempotent
+        # (fp8: the rows are code * scale in float32, which re-encode to the same codes)
+        if s.kv_dtype == "fp8":
+            import torch as _t
+            ks = np.empty((len(pos), Hkv, D), np.float32)
+            vs = np.empty_like(ks)
+            for n, (b, t) in enumerate(pos):
+                page, off = int(w.block_tables[b, t // 16]), t % 16
+                kc = _t.from_numpy(w.k_cache[page, :, off].copy()).view(_t.float8_e4m3fn).float().numpy()
+                vc = _t.from_numpy(w.v_cache[page, :, off].copy()).view(_t.float8_e4m3fn).float().numpy()
+                ks[n] = kc * w.k_scale[page][:, None]
+                vs[n] = vc * w.v_scale[page][:, None]
+            self.k_new = torch.from_numpy(ks).cuda()
+            self.v_new = torch.from_numpy(vs).cuda()
+        else:
+            kn = np.stack([w.k_cache[int(w.block_tables[b, t // 16]), :, t % 16] for b, t in pos])
+            vn = np.stack([w.v_cache[int(w.block_tables[b, t // 16]), :, t % 16] for b, t in pos])
+            self.k_new = torch.from_numpy(kn).cuda()
+            self.v_new = torch.from_numpy(vn).cuda()
+            if s.kv_dtype == "bf16":
+                self.k_new = self.k_new.view(torch.bfloat16)
+                self.v_new = self.v_new.view(torch.bfloat16)
+        self.slots = torch.from_numpy(slots).cuda()
+        self.out = torch.empty_like(self.d.q)
+        self.lse = torch.empty((B, Hq, Qmax), dtype=torch.float32, device=self.d.q.device)
+        self.workspace = None
+
+
+def run_append(psv, ds):
+    d = ds.d
+    psv.taco_kv_append(ds.k_new, ds.v_new, ds.slots, d.k_cache, d.v_cache, k_scale=d.k_scale,
+                       v_scale=d.v_scale)
+
+
+def run_attention(psv, ds, cfg):
+    d = ds.d
+    if cfg["split"] is None:
+        psv.taco_paged_tree_attn(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
+                                 d.tree_mask, d.scale, out=ds.out, lse=ds.lse, k_scale=d.k_scale,
+                                 v_scale=d.v_scale, max_ctx_len=d.max_ctx_len, path=cfg["path"])
+    else:
+        psv.taco_paged_tree_attn_splitk(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
+                                        d.q_lens, d.tree_mask, d.scale, cfg["split"], out=ds.out,
+                                        lse=ds.lse, k_scale=d.k_scale, v_scale=d.v_scale,
+                                        workspace=ds.workspace, max_ctx_len=d.max_ctx_len,
+                                        path=cfg["path"])
+
+
+# ------------------------------------------------------------------ CPU baseline (oracle)
+def cpu_baseline(w, gpu_out, budget_s=12.0):
+    """Time the fp64 oracle on whole sequences of the same workload until the time budget is
+    spent; report its KV GB/s and its max |difference| from the GPU output on that sample."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    s = w.spec
+    elem = {"f32": 4, "bf16": 2, "fp8": 1}[s.kv_dtype]
+    Hkv, D = w.k_cache.shape[1], w.k_cache.shape[3]
+    done, kvb, err = [], 0, 0.0
+    t_total = 0.0
+    with threadpool_limits(limits=1):
+        for b in range(w.q.shape[0]):
+            sel = np.array([b])
+            t0 = time.perf_counter()
+            ref, _ = oracle.paged_tree_attn(w.q[sel], w.k_cache, w.v_cache, w.block_tables[sel],
+                                            w.ctx_lens[sel], w.q_lens[sel], w.tree_mask[sel], w.scale,
+                                            q_dtype=s.q_dtype, kv_dtype=s.kv_dtype, k_scale=w.k_scale,
+                                            v_scale=w.v_scale)
+            t_total += time.perf_counter() - t0
+            done.append(b)
+            kvb += int(w.ctx_lens[b]) * Hkv * D * 2 * elem
+            v = ~np.isnan(ref[0])
+            err = max(err, float(np.abs(gpu_out[b][v] - ref[0][v]).max()))
+            if t_total >= budget_s:
+                break
+    return {"value": kvb / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(done)} of {w.q.shape[0]} sequences (whole contexts, {kvb / 1e6:.0f} MB of KV) "
+                      f"in {t_total:.1f} s, fp64 numpy, BLAS limited to 1 thread",
+            "max_abs_diff_vs_gpu": err}
+
+
+def load_traffic(config_name: str, src_hash: str):
+    """HBM bytes per launch from the committed counter summary, if it matches the kernels."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != src_hash:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ main
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=HEADLINE, choices=sorted(LAUNCH))
+    ap.add_argument("--sets", type=int, default=3, help="input sets rotated step to step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 1 GiB device copy (for scaling HBM byte counters)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    import paged_speculative_verify_amd as psv
+    from workload import make
+    psv.load()
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch_each_way": n, "launches": 5}))
+        return 0
+
+    name = args.config
+    cfg = launch_config(name)
+    print(f"[bench] generating {args.sets} input set(s) for {name}", file=sys.stderr, flush=True)
+    sets = []
+    for r in range(args.sets):
+        w = make(name, seed=None if r == 0 else 1000 + r)
+        sets.append(DeviceSet(w, torch))
+        print(f"[bench] set {r}: ctx sum {int(w.ctx_lens.sum())}, KV {kv_bytes(w) / 1e6:.1f} MB",
+              file=sys.stderr, flush=True)
+    if cfg["split"] is not None:
+        for ds in sets:
+            nbytes = psv.taco_paged_tree_attn_splitk_workspace_size(
+                ds.d.q, ds.d.k_cache, ds.d.block_tables, cfg["split"], max_ctx_len=ds.d.max_ctx_len)
+            ds.workspace = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        ds = sets[i % len(sets)]
+        run_append(psv, ds)
+        run_attention(psv, ds, cfg)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    order = [(args.warmup + i) % len(sets) for i in range(K)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(K):
+        ds = sets[order[i]]
+        e0, e1, e2 = ev[i]
+        e0.record(stream)
+        run_append(psv, ds)
+        e1.record(stream)
+        run_attention(psv, ds, cfg)
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    step_ms = [e0.elapsed_time(e2) for e0, _, e2 in ev]
+    attn_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev]
+    kvb = [kv_bytes(sets[o].w) for o in order]
+    cands = [int(sets[o].w.q_lens.sum()) for o in order]
+    flops = {r: attn_flops(sets[r].w) for r in set(order)}
+
+    attn_avg_s = sum(attn_ms) / K / 1e3
+    kv_per_launch = sum(kvb) / K
+    achieved_gbs = kv_per_launch / attn_avg_s / 1e9
+    ms_per_step = wall / K * 1e3
+    value = kv_per_launch / (ms_per_step / 1e3) / 1e9          # whole-step throughput
+    cand_per_s = (sum(cands) / K) / (ms_per_step / 1e3)
+    tflops = (sum(flops[o] for o in order) / K) / attn_avg_s / 1e12
+
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(name, src_hash)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 KV, bf16 Q"}[sets[0].w.spec.kv_dtype],
+        "data": "synthetic",
+        "config": {"workload": name, "batch": sets[0].w.q.shape[0], "q_heads": sets[0].w.q.shape[2],
+                   "kv_heads": sets[0].w.k_cache.shape[1], "head_dim": sets[0].w.q.shape[3],
+                   "max_q_len": sets[0].w.q.shape[1], "page": 16, "split_tokens": cfg["split"],
+                   "path": cfg["path"], "input_sets_rotated": len(sets)},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "candidates_per_s": round(cand_per_s, 1),
+        "attention_ms": round(attn_avg_s * 1e3, 5),
+        "attention_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 5),
+                                 round(float(np.percentile(attn_ms, 90)), 5)],
+        "kv_append_ms": round(sum(a - b for a, b in zip(step_ms, attn_ms)) / K, 5),
+        "attention_tflops": round(tflops, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "paged tree attention pass (attention kernel"
+                               + (" + split-K merge kernel)" if cfg["split"] else ")"),
+                     "algorithmic_bytes_per_launch": int(kv_per_launch)},
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        w0 = sets[order[-1]].w
+        run_attention(psv, sets[order[-1]], cfg)
+        torch.cuda.synchronize()
+        gpu_out = sets[order[-1]].out.to(torch.float64).cpu().numpy()
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w0, gpu_out)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,171 @@
+/*
+ * libpta — paged tree attention for AMD Instinct MI355X (gfx950).
+ *
+ * Plain C ABI.  Every array argument is a DEVICE pointer, except the dims
+ * struct, which is a HOST pointer read during the call.  The caller owns every
+ * buffer (including the split-K workspace); the library never allocates,
+ * frees, synchronises or keeps a pointer after a call returns.  Work is
+ * enqueued asynchronously on `stream` (a hipStream_t; NULL = default stream).
+ * Errors are returned as a status, never thrown: all host-checkable errors
+ * are detected before any HIP call is made; a failed launch returns
+ * PTA_ERR_HIP.  The library has no global mutable state.
+ *
+ * What is computed (sources: the TACO-LLM pages):
+ *   - KV cache split into fixed-size blocks of tokens; each sequence's
+ *     consecutive logical blocks map to non-contiguous physical blocks through
+ *     a block table (design talk "大模型倍速推理引擎 TACO-LLM 的设计与实践",
+ *     section "4. 支持 Paged Attention").
+ *   - Lookahead verification: each sequence carries q_len >= 1 candidate
+ *     tokens arranged as a tree; candidates sharing a prefix are computed in
+ *     one tree attention (same talk, sections "优化方案设计思路" and
+ *     "优化策略总结" item 1), which turns the per-sequence decode GEMV into a
+ *     small GEMM ("整体方案分为两大部分", TurboAttention bullets).
+ *   - FlashAttention-style streaming so on-chip resources do not depend on
+ *     sequence length (same bullets; "优化策略总结" item 2), and a split over
+ *     the sequence for long contexts (618zxw.cn article, section
+ *     "長シーケンス推論最適化におけるTurboAttention").
+ *   - 8-bit floating point KV storage with fast dequantisation inside the
+ *     attention operator (618zxw.cn article, section "LLM量子化技術による
+ *     推論コストの削減"; talk section "5. 支持 Quantization").
+ *
+ * Semantics (exact masked softmax attention; rounding aside):
+ *   for sequence b: C = ctx_lens[b] (INCLUDES the q_b = q_lens[b] candidates,
+ *   whose K/V occupy logical positions L..C-1, L = C - q_b).  Logical
+ *   position t is slot t % 16 of physical block block_tables[b][t / 16].
+ *   q-head h uses KV head h / (Hq / Hkv).  Candidate i (< q_b) sees every
+ *   t < L, and t = L + j iff tree_mask[b][i][j] != 0.  Then
+ *     s_t   = scale * <q[b][i][h][:], K_t>
+ *     out   = sum_t softmax(s)_t * V_t        (rounded to the q dtype)
+ *     lse   = ln sum_t exp(s_t)               (natural log, fp32)
+ *   A row with no visible key gives out = 0, lse = -inf.
+ *
+ * Layouts (row-major, contiguous):
+ *   q, out        [num_seqs][max_q_len][num_q_heads][head_dim]  (q dtype)
+ *   k_cache,
+ *   v_cache       [num_blocks][num_kv_heads][page_size][head_dim] (kv dtype)
+ *   k_scale,
+ *   v_scale       [num_blocks][num_kv_heads] float (fp8 KV only, else NULL):
+ *                 stored value x is represented by code * scale
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32
+ *   ctx_lens,
+ *   q_lens        [num_seqs] int32
+ *   tree_mask     [num_seqs][max_q_len][max_q_len] uint8 (may be NULL only
+ *                 when max_q_len == 1)
+ *   lse           [num_seqs][num_q_heads][max_q_len] float, or NULL
+ * Rows i >= q_lens[b] of out and lse are not written.
+ *
+ * Caller contract checked only on the device (see taco_pta_validate):
+ *   1 <= q_lens[b] <= max_q_len, q_lens[b] <= ctx_lens[b] <= max_ctx_len,
+ *   ctx_lens[b] <= page_size * max_blocks_per_seq, and every table entry
+ *   below ceil(ctx_lens[b] / page_size) is in [0, num_blocks).  Breaking it
+ *   gives undefined results.  Table entries past that count and cache slots
+ *   past ctx_lens[b] are never read for their values (they may hold NaN).
+ */
+#ifndef PTA_H
+#define PTA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PTA_OK = 0,
+  PTA_ERR_NULL_PTR = 1,          /* a required pointer is NULL */
+  PTA_ERR_BAD_DIMS = 2,          /* a size is out of range or inconsistent */
+  PTA_ERR_BAD_DTYPE = 3,         /* unsupported dtype or dtype combination */
+  PTA_ERR_UNSUPPORTED = 4,       /* valid request outside what is built (e.g. forced path) */
+  PTA_ERR_WORKSPACE_TOO_SMALL = 5,
+  PTA_ERR_HIP = 6                /* a HIP runtime call or launch failed */
+} pta_status;
+
+typedef enum { PTA_F32 = 0, PTA_BF16 = 1, PTA_FP8_E4M3FN = 2 } pta_dtype;
+
+/* Kernel family selection.  AUTO picks per call from the rows per KV head
+ * (G * max_q_len): vector ALU for small row counts, MFMA otherwise. */
+typedef enum { PTA_PATH_AUTO = 0, PTA_PATH_VALU = 1, PTA_PATH_MFMA = 2 } pta_path;
+
+typedef struct {
+  int32_t num_seqs;            /* B >= 0 (0 is a no-op) */
+  int32_t num_q_heads;         /* Hq >= 1, multiple of num_kv_heads */
+  int32_t num_kv_heads;        /* Hkv >= 1 */
+  int32_t head_dim;            /* 64 or 128 */
+  int32_t page_size;           /* must be 16 */
+  int32_t max_q_len;           /* row stride of q/out/tree_mask; 1..64 */
+  int32_t max_blocks_per_seq;  /* block_tables row stride, >= 1 */
+  int32_t max_ctx_len;         /* host-known bound on ctx_lens (grid sizing), >= 1 */
+  int64_t num_blocks;          /* physical blocks in the pool, >= 1 */
+  int32_t q_dtype;             /* pta_dtype: F32 or BF16; out has the same dtype */
+  int32_t kv_dtype;            /* pta_dtype: F32 (needs F32 q), BF16 or FP8_E4M3FN (need BF16 q) */
+  int32_t path;                /* pta_path */
+  int32_t reserved;            /* must be 0 */
+} pta_dims;
+
+/* Paged tree attention, one pass over each sequence's whole context.
+ * scale: softmax scale (finite).  lse may be NULL. */
+pta_status taco_paged_tree_attn(const pta_dims* dims, const void* q, const void* k_cache,
+                                const void* v_cache, const float* k_scale, const float* v_scale,
+                                const int32_t* block_tables, const int32_t* ctx_lens,
+                                const int32_t* q_lens, const uint8_t* tree_mask, float scale,
+                                void* out, float* lse, void* stream);
+
+/* Bytes of device workspace taken by taco_paged_tree_attn_splitk for these dims
+ * and partition length (0 on invalid input). */
+size_t taco_paged_tree_attn_splitk_workspace_size(const pta_dims* dims, int32_t partition_tokens);
+
+/* Split-K paged tree attention for long contexts: each sequence is cut into
+ * partitions of partition_tokens logical positions (a positive multiple of
+ * 32), attention over each partition runs as an independent work unit that
+ * writes its normalised partial output and log-sum-exp into `workspace`, and
+ * a second kernel on the same stream merges the partials by log-sum-exp into
+ * out/lse.  Arguments otherwise as taco_paged_tree_attn.  workspace is caller-
+ * owned device memory of at least workspace_bytes >=
+ * taco_paged_tree_attn_splitk_workspace_size(dims, partition_tokens); its
+ * contents on entry do not matter. */
+pta_status taco_paged_tree_attn_splitk(const pta_dims* dims, const void* q, const void* k_cache,
+                                       const void* v_cache, const float* k_scale,
+                                       const float* v_scale, const int32_t* block_tables,
+                                       const int32_t* ctx_lens, const int32_t* q_lens,
+                                       const uint8_t* tree_mask, float scale, void* out,
+                                       float* lse, int32_t partition_tokens, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/* KV append: write num_tokens new K/V rows into their cache slots, as blocks
+ * are handed out while tokens are generated (Paged Attention section of the
+ * design talk).
+ *   k_new, v_new  [num_tokens][num_kv_heads][head_dim] in new_dtype
+ *                 (F32 or BF16; must equal kv_dtype unless kv_dtype is FP8)
+ *   slot_mapping  [num_tokens] int64: slot = block * page_size + offset, or
+ *                 negative to skip the token.  Slots must be < num_blocks *
+ *                 page_size and distinct (duplicates race).
+ *   fp8 caches store RNE-to-nearest-even e4m3fn of (x / scale) computed in
+ *   float32, saturated to +-448, with the block's existing k_scale / v_scale.
+ * Uses dims->num_kv_heads, head_dim, page_size, num_blocks, kv_dtype. */
+pta_status taco_kv_append(const pta_dims* dims, const void* k_new, const void* v_new,
+                          int32_t new_dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                          void* k_cache, void* v_cache, const float* k_scale,
+                          const float* v_scale, void* stream);
+
+/* Device-side check of the caller contract above.  Writes into *d_flags (a
+ * device int32, caller-owned; it is first cleared) the OR of:
+ *   1 q_lens out of [1, max_q_len]     2 ctx_lens < q_lens or > max_ctx_len
+ *   4 ctx_lens > page_size * max_blocks_per_seq
+ *   8 a used block-table entry outside [0, num_blocks)
+ * A debug/test aid: the attention entry points do not call it. */
+pta_status taco_pta_validate(const pta_dims* dims, const int32_t* block_tables,
+                             const int32_t* ctx_lens, const int32_t* q_lens, int32_t* d_flags,
+                             void* stream);
+
+/* Static, never NULL. */
+const char* taco_pta_status_string(pta_status status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t taco_pta_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PTA_H */

@@ -1,0 +1,21 @@
+"""Paged tree attention for AMD Instinct MI355X (gfx950).
+
+The compute path is libpta.so (hand-written HIP kernels behind a C ABI, see
+include/pta.h); this package is its thin Python binding.  PyTorch supplies
+device memory and streams only.
+"""
+from ._lib import (  # noqa: F401
+    PATHS,
+    PtaDims,
+    PtaError,
+    declared_functions,
+    load,
+    make_dims,
+    taco_kv_append,
+    taco_paged_tree_attn,
+    taco_paged_tree_attn_splitk,
+    taco_paged_tree_attn_splitk_workspace_size,
+    taco_pta_status_string,
+    taco_pta_validate,
+    taco_pta_version,
+)

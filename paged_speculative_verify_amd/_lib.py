@@ -1,0 +1,303 @@
+"""ctypes binding of libpta.so (argument marshalling only).
+
+Every function here validates tensor placement, dtype and shape, fills the
+C dims struct, passes raw device pointers and the current HIP stream, and
+turns a non-zero status into an exception.  All arithmetic runs in the
+library's HIP kernels; there is no fallback path.  If libpta.so is missing the
+first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpta.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "pta.h")
+
+PTA_F32, PTA_BF16, PTA_FP8_E4M3FN = 0, 1, 2
+PATHS = {"auto": 0, "valu": 1, "mfma": 2}
+STATUS = {0: "PTA_OK", 1: "PTA_ERR_NULL_PTR", 2: "PTA_ERR_BAD_DIMS", 3: "PTA_ERR_BAD_DTYPE",
+          4: "PTA_ERR_UNSUPPORTED", 5: "PTA_ERR_WORKSPACE_TOO_SMALL", 6: "PTA_ERR_HIP"}
+
+
+class PtaDims(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_q_len", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_ctx_len", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("path", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class PtaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def declared_functions() -> list:
+    """Names of the functions include/pta.h declares."""
+    with open(HEADER, encoding="utf-8") as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(taco_\w+)\s*\(", text)))
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_speculative_verify_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    D = ctypes.POINTER(PtaDims)
+    lib.taco_paged_tree_attn.argtypes = [D, P, P, P, P, P, P, P, P, P, F, P, P, P]
+    lib.taco_paged_tree_attn.restype = ctypes.c_int
+    lib.taco_paged_tree_attn_splitk_workspace_size.argtypes = [D, I32]
+    lib.taco_paged_tree_attn_splitk_workspace_size.restype = SZ
+    lib.taco_paged_tree_attn_splitk.argtypes = [D, P, P, P, P, P, P, P, P, P, F, P, P, I32, P, SZ, P]
+    lib.taco_paged_tree_attn_splitk.restype = ctypes.c_int
+    lib.taco_kv_append.argtypes = [D, P, P, I32, P, I32, P, P, P, P, P]
+    lib.taco_kv_append.restype = ctypes.c_int
+    lib.taco_pta_validate.argtypes = [D, P, P, P, P, P]
+    lib.taco_pta_validate.restype = ctypes.c_int
+    lib.taco_pta_status_string.argtypes = [ctypes.c_int]
+    lib.taco_pta_status_string.restype = ctypes.c_char_p
+    lib.taco_pta_version.argtypes = []
+    lib.taco_pta_version.restype = I32
+    _lib = lib
+    return lib
+
+
+def _check(st: int) -> None:
+    if st != 0:
+        msg = load().taco_pta_status_string(st).decode()
+        raise PtaError(st, msg)
+
+
+# ---------------------------------------------------------------- tensor helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _q_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PTA_F32
+    if t.dtype == torch.bfloat16:
+        return PTA_BF16
+    raise ValueError(f"q/new-token dtype must be float32 or bfloat16, got {t.dtype}")
+
+
+def _kv_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PTA_F32
+    if t.dtype == torch.bfloat16:
+        return PTA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PTA_FP8_E4M3FN
+    raise ValueError(f"cache dtype must be float32, bfloat16 or fp8 e4m3fn/uint8, got {t.dtype}")
+
+
+def _need(t, name, ndim=None, dtype=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def make_dims(q, k_cache, block_tables, max_ctx_len=None, path="auto") -> PtaDims:
+    B, Qmax, Hq, D = q.shape
+    NB, Hkv, page, D2 = k_cache.shape
+    if D2 != D:
+        raise ValueError("head_dim of q and the caches differ")
+    MBS = block_tables.shape[1]
+    return PtaDims(num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=page,
+                   max_q_len=Qmax, max_blocks_per_seq=MBS,
+                   max_ctx_len=int(max_ctx_len) if max_ctx_len is not None else MBS * page,
+                   num_blocks=NB, q_dtype=_q_code(q), kv_dtype=_kv_code(k_cache),
+                   path=PATHS[path], reserved=0)
+
+
+def _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale):
+    torch = _torch()
+    _need(q, "q", 4)
+    dev = q.device
+    _need(k_cache, "k_cache", 4, device=dev)
+    _need(v_cache, "v_cache", 4, dtype=k_cache.dtype, device=dev)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    _need(block_tables, "block_tables", 2, torch.int32, dev)
+    _need(ctx_lens, "ctx_lens", 1, torch.int32, dev)
+    _need(q_lens, "q_lens", 1, torch.int32, dev)
+    B, Qmax = q.shape[0], q.shape[1]
+    if block_tables.shape[0] != B or ctx_lens.shape[0] != B or q_lens.shape[0] != B:
+        raise ValueError("batch sizes of q, block_tables, ctx_lens, q_lens differ")
+    if tree_mask is not None:
+        _need(tree_mask, "tree_mask", 3, torch.uint8, dev)
+        if tuple(tree_mask.shape) != (B, Qmax, Qmax):
+            raise ValueError(f"tree_mask must be [{B}, {Qmax}, {Qmax}]")
+    if _kv_code(k_cache) == PTA_FP8_E4M3FN:
+        for nm, s in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if s is None:
+                raise ValueError(f"{nm} is required for an fp8 cache")
+            _need(s, nm, 2, torch.float32, dev)
+            if tuple(s.shape) != tuple(k_cache.shape[:2]):
+                raise ValueError(f"{nm} must be [num_blocks, num_kv_heads]")
+
+
+def _alloc_out(q, out, lse):
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", 4, q.dtype, q.device)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if lse is not None:
+        _need(lse, "lse", 3, torch.float32, q.device)
+        B, Qmax, Hq, _ = q.shape
+        if tuple(lse.shape) != (B, Hq, Qmax):
+            raise ValueError(f"lse must be [{B}, {Hq}, {Qmax}]")
+    return out, lse
+
+
+# ---------------------------------------------------------------- entry points
+def taco_paged_tree_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, scale,
+                         out=None, lse=None, k_scale=None, v_scale=None, max_ctx_len=None,
+                         path="auto", stream=None):
+    """Paged tree attention over each sequence's whole context (see include/pta.h)."""
+    lib = load()
+    _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale)
+    out, lse = _alloc_out(q, out, lse)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    _check(lib.taco_paged_tree_attn(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), _ptr(ctx_lens),
+                                    _ptr(q_lens), _ptr(tree_mask), float(scale), _ptr(out), _ptr(lse),
+                                    _stream(stream)))
+    return out
+
+
+def taco_paged_tree_attn_splitk_workspace_size(q, k_cache, block_tables, partition_tokens,
+                                               max_ctx_len=None, path="auto") -> int:
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    return int(load().taco_paged_tree_attn_splitk_workspace_size(ctypes.byref(dims), int(partition_tokens)))
+
+
+def taco_paged_tree_attn_splitk(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask,
+                                scale, partition_tokens, out=None, lse=None, k_scale=None,
+                                v_scale=None, workspace=None, max_ctx_len=None, path="auto",
+                                stream=None):
+    """Split-K paged tree attention with a log-sum-exp merge (see include/pta.h).
+
+    workspace: a caller-owned uint8 device tensor of at least
+    taco_paged_tree_attn_splitk_workspace_size(...) bytes; allocated here if None.
+    """
+    torch = _torch()
+    lib = load()
+    _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale)
+    out, lse = _alloc_out(q, out, lse)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    need = int(lib.taco_paged_tree_attn_splitk_workspace_size(ctypes.byref(dims), int(partition_tokens)))
+    if workspace is None:
+        if need == 0:
+            raise ValueError("invalid dims or partition_tokens for split-K")
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    else:
+        _need(workspace, "workspace", device=q.device)
+    _check(lib.taco_paged_tree_attn_splitk(
+        ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask), float(scale), _ptr(out),
+        _ptr(lse), int(partition_tokens), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out
+
+
+def taco_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None,
+                   stream=None):
+    """Write new tokens' K/V rows into their paged cache slots (see include/pta.h)."""
+    torch = _torch()
+    lib = load()
+    _need(k_new, "k_new", 3)
+    dev = k_new.device
+    _need(v_new, "v_new", 3, k_new.dtype, dev)
+    _need(slot_mapping, "slot_mapping", 1, torch.int64, dev)
+    _need(k_cache, "k_cache", 4, device=dev)
+    _need(v_cache, "v_cache", 4, k_cache.dtype, dev)
+    N, Hkv, D = k_new.shape
+    if v_new.shape != k_new.shape or slot_mapping.shape[0] != N:
+        raise ValueError("k_new, v_new and slot_mapping disagree on the token count")
+    if k_cache.shape[1] != Hkv or k_cache.shape[3] != D or v_cache.shape != k_cache.shape:
+        raise ValueError("new rows and caches disagree on heads / head_dim")
+    dims = PtaDims(num_seqs=0, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=D, page_size=k_cache.shape[2],
+                   max_q_len=1, max_blocks_per_seq=1, max_ctx_len=1, num_blocks=k_cache.shape[0],
+                   q_dtype=PTA_BF16, kv_dtype=_kv_code(k_cache), path=0, reserved=0)
+    _check(lib.taco_kv_append(ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _q_code(k_new),
+                              _ptr(slot_mapping), N, _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                              _ptr(v_scale), _stream(stream)))
+
+
+def taco_pta_validate(block_tables, ctx_lens, q_lens, max_q_len, num_blocks, max_ctx_len=None,
+                      flags=None, stream=None) -> int:
+    """Device-side contract check; returns the flag bits (synchronises the stream)."""
+    torch = _torch()
+    lib = load()
+    dev = block_tables.device
+    _need(block_tables, "block_tables", 2, torch.int32)
+    _need(ctx_lens, "ctx_lens", 1, torch.int32, dev)
+    _need(q_lens, "q_lens", 1, torch.int32, dev)
+    B, MBS = block_tables.shape
+    if flags is None:
+        flags = torch.empty(1, dtype=torch.int32, device=dev)
+    dims = PtaDims(num_seqs=B, num_q_heads=1, num_kv_heads=1, head_dim=128, page_size=16,
+                   max_q_len=int(max_q_len), max_blocks_per_seq=MBS,
+                   max_ctx_len=int(max_ctx_len) if max_ctx_len is not None else MBS * 16,
+                   num_blocks=int(num_blocks), q_dtype=PTA_BF16, kv_dtype=PTA_BF16, path=0, reserved=0)
+    _check(lib.taco_pta_validate(ctypes.byref(dims), _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens),
+                                 _ptr(flags), _stream(stream)))
+    return int(flags.item())
+
+
+def taco_pta_status_string(status: int) -> str:
+    return load().taco_pta_status_string(int(status)).decode()
+
+
+def taco_pta_version() -> int:
+    return int(load().taco_pta_version())

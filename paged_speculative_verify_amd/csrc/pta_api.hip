@@ -1,0 +1,250 @@
+// C ABI of libpta: host-side argument checks, path selection and launches.
+// All checks run before any HIP call; no allocation, no synchronisation.
+#include "../../include/pta.h"
+#include "pta_device.h"
+#include "pta_launch.h"
+
+#include <math.h>
+
+using namespace pta;
+
+namespace {
+
+constexpr int kMaxQLen = 64;
+constexpr int kValuMaxRows = 8;     // largest G * max_q_len of the vector-ALU path
+constexpr int kMfmaMaxRows = 256;   // 8 waves x 32 rows
+constexpr int kAutoValuRows = 4;    // AUTO: vector ALU up to this many rows
+
+bool dtype_ok(int q, int kv) {
+  return (q == PTA_F32 && kv == PTA_F32) || (q == PTA_BF16 && (kv == PTA_BF16 || kv == PTA_FP8_E4M3FN));
+}
+
+int pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+pta_status check_dims(const pta_dims* d) {
+  if (d == nullptr) return PTA_ERR_NULL_PTR;
+  if (d->num_seqs < 0 || d->num_seqs > 65535 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
+      d->num_kv_heads > 65535 || d->num_q_heads % d->num_kv_heads != 0)
+    return PTA_ERR_BAD_DIMS;
+  if (d->head_dim != 64 && d->head_dim != 128) return PTA_ERR_BAD_DIMS;
+  if (d->page_size != kPage) return PTA_ERR_BAD_DIMS;
+  if (d->max_q_len < 1 || d->max_q_len > kMaxQLen) return PTA_ERR_BAD_DIMS;
+  if (d->max_blocks_per_seq < 1 || d->max_ctx_len < 1 ||
+      (int64_t)d->max_ctx_len > (int64_t)d->page_size * d->max_blocks_per_seq)
+    return PTA_ERR_BAD_DIMS;
+  if (d->num_blocks < 1) return PTA_ERR_BAD_DIMS;
+  if (d->reserved != 0) return PTA_ERR_BAD_DIMS;
+  if (!dtype_ok(d->q_dtype, d->kv_dtype)) return PTA_ERR_BAD_DTYPE;
+  if (d->path < PTA_PATH_AUTO || d->path > PTA_PATH_MFMA) return PTA_ERR_BAD_DIMS;
+  return PTA_OK;
+}
+
+struct Plan {
+  bool mfma;
+  int rows_pow2;   // VALU
+  int nwave;       // MFMA
+};
+
+pta_status plan_for(const pta_dims* d, Plan* p) {
+  const int G = d->num_q_heads / d->num_kv_heads;
+  const int rows = G * d->max_q_len;
+  const bool valu_ok = rows <= kValuMaxRows;
+  const bool mfma_ok = d->q_dtype == PTA_BF16 && rows <= kMfmaMaxRows;
+  bool mfma;
+  if (d->path == PTA_PATH_VALU) {
+    if (!valu_ok) return PTA_ERR_UNSUPPORTED;
+    mfma = false;
+  } else if (d->path == PTA_PATH_MFMA) {
+    if (!mfma_ok) return PTA_ERR_UNSUPPORTED;
+    mfma = true;
+  } else {
+    if (valu_ok && (rows <= kAutoValuRows || !mfma_ok)) mfma = false;
+    else if (mfma_ok) mfma = true;
+    else return PTA_ERR_UNSUPPORTED;
+  }
+  p->mfma = mfma;
+  p->rows_pow2 = pow2_at_least(rows);
+  p->nwave = pow2_at_least((rows + 31) / 32);
+  return PTA_OK;
+}
+
+pta_status check_attn_ptrs(const pta_dims* d, const void* q, const void* k, const void* v,
+                           const float* ks, const float* vs, const int32_t* tables,
+                           const int32_t* ctx, const int32_t* ql, const uint8_t* mask,
+                           const void* out) {
+  if (!q || !k || !v || !tables || !ctx || !ql || !out) return PTA_ERR_NULL_PTR;
+  if (d->max_q_len > 1 && !mask) return PTA_ERR_NULL_PTR;
+  if (d->kv_dtype == PTA_FP8_E4M3FN && (!ks || !vs)) return PTA_ERR_NULL_PTR;
+  return PTA_OK;
+}
+
+AttnArgs make_args(const pta_dims* d, const void* q, const void* k, const void* v,
+                   const float* ks, const float* vs, const int32_t* tables, const int32_t* ctx,
+                   const int32_t* ql, const uint8_t* mask, float scale, void* out, float* lse) {
+  AttnArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.k_scale = ks; a.v_scale = vs;
+  a.tables = tables; a.ctx = ctx; a.qlen = ql;
+  a.mask = d->max_q_len > 1 ? mask : nullptr;
+  a.out = out; a.lse = lse;
+  a.scale_log2 = scale * kLog2e;
+  a.B = d->num_seqs; a.Hq = d->num_q_heads; a.Hkv = d->num_kv_heads;
+  a.G = d->num_q_heads / d->num_kv_heads;
+  a.Qmax = d->max_q_len; a.MBS = d->max_blocks_per_seq;
+  a.num_blocks = d->num_blocks;
+  return a;
+}
+
+pta_status run_attn(const pta_dims* d, const AttnArgs& a, const Plan& p, hipStream_t s) {
+  const dim3 grid((unsigned)a.num_parts, (unsigned)a.Hkv, (unsigned)a.B);
+  hipError_t e = p.mfma ? launch_mfma(a, d->kv_dtype, d->head_dim, p.nwave, grid, s)
+                        : launch_valu(a, d->q_dtype, d->kv_dtype, d->head_dim, p.rows_pow2, grid, s);
+  return e == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+}
+
+struct SplitLayout {
+  int64_t parts;
+  size_t o_bytes, lse_off, total;
+};
+
+bool split_layout(const pta_dims* d, int32_t T, SplitLayout* L) {
+  if (T <= 0 || T % 32 != 0) return false;
+  L->parts = ((int64_t)d->max_ctx_len + T - 1) / T;
+  const int64_t rows = (int64_t)d->num_seqs * d->num_q_heads * d->max_q_len * L->parts;
+  L->o_bytes = (size_t)rows * d->head_dim * sizeof(float);
+  L->lse_off = (L->o_bytes + 255) & ~(size_t)255;
+  L->total = L->lse_off + (((size_t)rows * sizeof(float) + 255) & ~(size_t)255);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+pta_status taco_paged_tree_attn(const pta_dims* d, const void* q, const void* k_cache,
+                                const void* v_cache, const float* k_scale, const float* v_scale,
+                                const int32_t* block_tables, const int32_t* ctx_lens,
+                                const int32_t* q_lens, const uint8_t* tree_mask, float scale,
+                                void* out, float* lse, void* stream) {
+  pta_status st = check_dims(d);
+  if (st != PTA_OK) return st;
+  if (!isfinite(scale)) return PTA_ERR_BAD_DIMS;
+  Plan p;
+  st = plan_for(d, &p);
+  if (st != PTA_OK) return st;
+  if (d->num_seqs == 0) return PTA_OK;
+  st = check_attn_ptrs(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
+                       tree_mask, out);
+  if (st != PTA_OK) return st;
+  AttnArgs a = make_args(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
+                         tree_mask, scale, out, lse);
+  a.part_tokens = 0;
+  a.num_parts = 1;
+  return run_attn(d, a, p, (hipStream_t)stream);
+}
+
+size_t taco_paged_tree_attn_splitk_workspace_size(const pta_dims* d, int32_t partition_tokens) {
+  if (check_dims(d) != PTA_OK) return 0;
+  SplitLayout L;
+  if (!split_layout(d, partition_tokens, &L)) return 0;
+  return L.total;
+}
+
+pta_status taco_paged_tree_attn_splitk(const pta_dims* d, const void* q, const void* k_cache,
+                                       const void* v_cache, const float* k_scale,
+                                       const float* v_scale, const int32_t* block_tables,
+                                       const int32_t* ctx_lens, const int32_t* q_lens,
+                                       const uint8_t* tree_mask, float scale, void* out,
+                                       float* lse, int32_t partition_tokens, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  pta_status st = check_dims(d);
+  if (st != PTA_OK) return st;
+  if (!isfinite(scale)) return PTA_ERR_BAD_DIMS;
+  SplitLayout L;
+  if (!split_layout(d, partition_tokens, &L)) return PTA_ERR_BAD_DIMS;
+  if (L.parts > 65535) return PTA_ERR_UNSUPPORTED;
+  Plan p;
+  st = plan_for(d, &p);
+  if (st != PTA_OK) return st;
+  if (d->num_seqs == 0) return PTA_OK;
+  st = check_attn_ptrs(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
+                       tree_mask, out);
+  if (st != PTA_OK) return st;
+  if (workspace == nullptr) return PTA_ERR_NULL_PTR;
+  if (workspace_bytes < L.total) return PTA_ERR_WORKSPACE_TOO_SMALL;
+  AttnArgs a = make_args(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
+                         tree_mask, scale, out, lse);
+  a.part_o = reinterpret_cast<float*>(workspace);
+  a.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + L.lse_off);
+  a.part_tokens = partition_tokens;
+  a.num_parts = (int32_t)L.parts;
+  hipStream_t s = (hipStream_t)stream;
+  st = run_attn(d, a, p, s);
+  if (st != PTA_OK) return st;
+  MergeArgs m{};
+  m.part_o = a.part_o; m.part_lse = a.part_lse;
+  m.ctx = ctx_lens; m.qlen = q_lens;
+  m.out = out; m.lse = lse;
+  m.B = d->num_seqs; m.Hq = d->num_q_heads; m.Qmax = d->max_q_len;
+  m.P = (int32_t)L.parts; m.part_tokens = partition_tokens;
+  return launch_merge(m, d->q_dtype, d->head_dim, s) == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+}
+
+pta_status taco_kv_append(const pta_dims* d, const void* k_new, const void* v_new,
+                          int32_t new_dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                          void* k_cache, void* v_cache, const float* k_scale,
+                          const float* v_scale, void* stream) {
+  if (d == nullptr) return PTA_ERR_NULL_PTR;
+  if (d->num_kv_heads < 1 || d->num_kv_heads > 65535 || (d->head_dim != 64 && d->head_dim != 128) || d->page_size != kPage ||
+      d->num_blocks < 1 || num_tokens < 0 || num_tokens > 65535 * 64)
+    return PTA_ERR_BAD_DIMS;
+  const int kv = d->kv_dtype;
+  const bool ok = (kv == PTA_F32 && new_dtype == PTA_F32) || (kv == PTA_BF16 && new_dtype == PTA_BF16) ||
+                  (kv == PTA_FP8_E4M3FN && (new_dtype == PTA_F32 || new_dtype == PTA_BF16));
+  if (!ok) return PTA_ERR_BAD_DTYPE;
+  if (num_tokens == 0) return PTA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PTA_ERR_NULL_PTR;
+  if (kv == PTA_FP8_E4M3FN && (!k_scale || !v_scale)) return PTA_ERR_NULL_PTR;
+  AppendArgs p{};
+  p.k_new = k_new; p.v_new = v_new; p.slots = slot_mapping;
+  p.k_cache = k_cache; p.v_cache = v_cache; p.k_scale = k_scale; p.v_scale = v_scale;
+  p.N = num_tokens; p.Hkv = d->num_kv_heads; p.D = d->head_dim;
+  p.num_slots = d->num_blocks * kPage;
+  return launch_append(p, new_dtype, kv, (hipStream_t)stream) == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+}
+
+pta_status taco_pta_validate(const pta_dims* d, const int32_t* block_tables, const int32_t* ctx_lens,
+                             const int32_t* q_lens, int32_t* d_flags, void* stream) {
+  if (d == nullptr) return PTA_ERR_NULL_PTR;
+  if (d->num_seqs < 0 || d->max_q_len < 1 || d->max_blocks_per_seq < 1 || d->page_size != kPage ||
+      d->num_blocks < 1)
+    return PTA_ERR_BAD_DIMS;
+  if (!d_flags) return PTA_ERR_NULL_PTR;
+  if (d->num_seqs > 0 && (!block_tables || !ctx_lens || !q_lens)) return PTA_ERR_NULL_PTR;
+  ValidateArgs v{};
+  v.tables = block_tables; v.ctx = ctx_lens; v.qlen = q_lens; v.flags = d_flags;
+  v.B = d->num_seqs; v.Qmax = d->max_q_len; v.MBS = d->max_blocks_per_seq;
+  v.max_ctx = d->max_ctx_len; v.page = d->page_size; v.num_blocks = d->num_blocks;
+  return launch_validate(v, (hipStream_t)stream) == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+}
+
+const char* taco_pta_status_string(pta_status s) {
+  switch (s) {
+    case PTA_OK: return "ok";
+    case PTA_ERR_NULL_PTR: return "a required pointer is NULL";
+    case PTA_ERR_BAD_DIMS: return "invalid or inconsistent dimensions";
+    case PTA_ERR_BAD_DTYPE: return "unsupported dtype or dtype combination";
+    case PTA_ERR_UNSUPPORTED: return "request not supported by the built kernels";
+    case PTA_ERR_WORKSPACE_TOO_SMALL: return "split-K workspace too small";
+    case PTA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t taco_pta_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+// Split-K merge, KV append and contract validation kernels.
+#include "pta_device.h"
+#include "pta_launch.h"
+
+namespace pta {
+
+// ---------------------------------------------------------------- split-K merge
+// One wave per output row (b, h, i).  The partial of partition p is the
+// normalised output O_p and LSE_p over that partition's keys; the merged row is
+//   LSE = ln sum_p exp(LSE_p),   out = sum_p exp(LSE_p - LSE) O_p
+// (the long-sequence design of the 618zxw.cn article, section
+// "長シーケンス推論最適化におけるTurboAttention": partitions of the sequence
+// are processed independently and combined).
+template <typename QT, int D>
+__global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
+  constexpr int EPL = D / 64;
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  const int lane = threadIdx.x;
+  const int64_t rowid = blockIdx.x;                   // ((b * Hq + h) * Qmax + i)
+  const int i = (int)(rowid % a.Qmax);
+  const int h = (int)((rowid / a.Qmax) % a.Hq);
+  const int b = (int)(rowid / ((int64_t)a.Qmax * a.Hq));
+  if (i >= a.qlen[b]) return;
+  // partitions holding this sequence's context (never more than the workspace holds)
+  const int np = min((a.ctx[b] + a.part_tokens - 1) / a.part_tokens, a.P);
+  const float* lsep = a.part_lse + rowid * a.P;
+  const float* op = a.part_o + rowid * a.P * D;
+
+  float mx = NEG_INF;
+  for (int p = lane; p < np; p += 64) mx = fmaxf(mx, lsep[p]);
+  mx = wave_max_range<1, 64>(mx);
+  const float muse = mx == NEG_INF ? 0.f : mx;
+  float wsum = 0.f;
+  for (int p = lane; p < np; p += 64) wsum += __expf(lsep[p] - muse);
+  wsum = wave_sum_range<1, 64>(wsum);
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int p = 0; p < np; ++p) {
+    const float w = __expf(lsep[p] - muse) * inv;   // exp(-inf) = 0 for empty partitions
+    if (w == 0.f) continue;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, op[(int64_t)p * D + lane * EPL + e], acc[e]);
+  }
+  const int64_t obase = (((int64_t)b * a.Qmax + i) * a.Hq + h) * D + lane * EPL;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    if constexpr (QT::bytes == 4) reinterpret_cast<float*>(a.out)[obase + e] = acc[e];
+    else reinterpret_cast<uint16_t*>(a.out)[obase + e] = f32_to_bf16(acc[e]);
+  }
+  if (lane == 0 && a.lse != nullptr)
+    a.lse[rowid] = wsum > 0.f ? muse + __logf(wsum) : NEG_INF;
+}
+
+hipError_t launch_merge(const MergeArgs& m, int q_dtype, int D, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)m.B * m.Hq * m.Qmax));
+  if (grid.x == 0) return hipSuccess;
+  if (q_dtype == 0 && D == 64) hipLaunchKernelGGL((merge_kernel<F32, 64>), grid, dim3(64), 0, s, m);
+  else if (q_dtype == 0 && D == 128) hipLaunchKernelGGL((merge_kernel<F32, 128>), grid, dim3(64), 0, s, m);
+  else if (q_dtype == 1 && D == 64) hipLaunchKernelGGL((merge_kernel<BF16, 64>), grid, dim3(64), 0, s, m);
+  else if (q_dtype == 1 && D == 128) hipLaunchKernelGGL((merge_kernel<BF16, 128>), grid, dim3(64), 0, s, m);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- KV append
+// One wave per (token, KV head); slot = block * 16 + offset, negative = skip.
+// Pages are filled as tokens arrive (design talk section
+// "4. 支持 Paged Attention"); fp8 caches store RNE-saturated e4m3fn codes of
+// x / scale with the block's own scale.
+template <typename NT, typename KT>
+__global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
+  const int n = blockIdx.x, hk = blockIdx.y, lane = threadIdx.x;
+  const int64_t slot = a.slots[n];
+  if (slot < 0 || slot >= a.num_slots) return;
+  const int64_t blk = slot / kPage, off = slot % kPage;
+  const int64_t src = ((int64_t)n * a.Hkv + hk) * a.D;
+  const int64_t dst = ((blk * a.Hkv + hk) * kPage + off) * a.D;
+  for (int which = 0; which < 2; ++which) {
+    const void* in = which == 0 ? a.k_new : a.v_new;
+    void* cache = which == 0 ? a.k_cache : a.v_cache;
+    if constexpr (KT::bytes == 1) {
+      const float scl = (which == 0 ? a.k_scale : a.v_scale)[blk * a.Hkv + hk];
+      for (int d = lane; d < a.D; d += 64) {
+        float x;
+        if constexpr (NT::bytes == 4) x = reinterpret_cast<const float*>(in)[src + d];
+        else x = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(in)[src + d] << 16);
+        reinterpret_cast<uint8_t*>(cache)[dst + d] = (uint8_t)f32_to_e4m3fn_sat(__fdiv_rn(x, scl));
+      }
+    } else {
+      using S = typename KT::storage;
+      for (int d = lane; d < a.D; d += 64)
+        reinterpret_cast<S*>(cache)[dst + d] = reinterpret_cast<const S*>(in)[src + d];
+    }
+  }
+}
+
+hipError_t launch_append(const AppendArgs& p, int new_dtype, int kv_dtype, hipStream_t s) {
+  const dim3 grid((unsigned)p.N, (unsigned)p.Hkv);
+  if (p.N == 0) return hipSuccess;
+  if (kv_dtype == 0 && new_dtype == 0) hipLaunchKernelGGL((append_kernel<F32, F32>), grid, dim3(64), 0, s, p);
+  else if (kv_dtype == 1 && new_dtype == 1) hipLaunchKernelGGL((append_kernel<BF16, BF16>), grid, dim3(64), 0, s, p);
+  else if (kv_dtype == 2 && new_dtype == 0) hipLaunchKernelGGL((append_kernel<F32, FP8>), grid, dim3(64), 0, s, p);
+  else if (kv_dtype == 2 && new_dtype == 1) hipLaunchKernelGGL((append_kernel<BF16, FP8>), grid, dim3(64), 0, s, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- validation
+__global__ __launch_bounds__(64) void clear_flag_kernel(int32_t* f) {
+  if (threadIdx.x == 0) *f = 0;
+}
+
+__global__ __launch_bounds__(64) void validate_kernel(ValidateArgs v) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int C = v.ctx[b], q = v.qlen[b];
+  int flags = 0;
+  if (q < 1 || q > v.Qmax) flags |= 1;
+  if (C < q || C > v.max_ctx) flags |= 2;
+  if (C > v.page * v.MBS) flags |= 4;
+  const int pages = min((max(C, 0) + v.page - 1) / v.page, v.MBS);
+  for (int p = lane; p < pages; p += 64) {
+    const int32_t blk = v.tables[(int64_t)b * v.MBS + p];
+    if (blk < 0 || (int64_t)blk >= v.num_blocks) flags |= 8;
+  }
+  if (flags) atomicOr(v.flags, flags);
+}
+
+hipError_t launch_validate(const ValidateArgs& v, hipStream_t s) {
+  hipLaunchKernelGGL(clear_flag_kernel, dim3(1), dim3(64), 0, s, v.flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || v.B == 0) return e;
+  hipLaunchKernelGGL(validate_kernel, dim3((unsigned)v.B), dim3(64), 0, s, v);
+  return hipGetLastError();
+}
+
+}  // namespace pta

@@ -1,0 +1,124 @@
+// Internal device-side definitions for libpta (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pta {
+
+// ---------------------------------------------------------------- element tags
+struct F32 { using storage = float; static constexpr int bytes = 4; };
+struct BF16 { using storage = uint16_t; static constexpr int bytes = 2; };
+struct FP8 { using storage = uint8_t; static constexpr int bytes = 1; };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPage = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Everything one attention launch needs.  Passed by value.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* tables;
+  const int32_t* ctx;
+  const int32_t* qlen;
+  const uint8_t* mask;     // may be null when Qmax == 1
+  void* out;
+  float* lse;              // may be null
+  float* part_o;           // split-K partial outputs [B][Hq][Qmax][P][D], or null (unsplit)
+  float* part_lse;         // split-K partial LSE     [B][Hq][Qmax][P]
+  float scale_log2;        // softmax scale * log2(e)
+  int32_t B, Hq, Hkv, G, Qmax, MBS;
+  int32_t part_tokens;     // partition length in tokens (split) or 0
+  int32_t num_parts;       // partitions per sequence (grid.x)
+  int64_t num_blocks;
+};
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 p;
+  p[0] = (__bf16)lo;
+  p[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+// two e4m3fn codes (bytes sel*2, sel*2+1 of w) -> two floats, exact (hardware convert)
+template <bool HI>
+__device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+// two e4m3fn codes -> two bf16 (packed), exact: every finite e4m3fn value is a bf16 value
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Round a float32 to an OCP e4m3fn code: nearest, ties to even, saturating at
+// +-448; NaN -> 0x7F.  Written from the format's definition (1 sign bit,
+// 4 exponent bits with bias 7, 3 mantissa bits, subnormal step 2^-9).
+__device__ __forceinline__ uint32_t f32_to_e4m3fn_sat(float x) {
+  uint32_t bits = __float_as_uint(x);
+  uint32_t s = (bits >> 24) & 0x80u;
+  uint32_t mag = bits & 0x7fffffffu;
+  if (mag > 0x7f800000u) return 0x7fu;                 // NaN
+  float a = __uint_as_float(mag);
+  if (a >= 448.0f) return s | 0x7eu;                    // saturate (also +-inf)
+  if (a < 0.015625f) {                                  // below 2^-6: multiples of 2^-9
+    int m = __float2int_rn(a * 512.0f);                 // exact scaling, ties to even
+    return s | (uint32_t)m;                             // m == 8 is code 0x08 = 2^-6
+  }
+  int e = (int)(mag >> 23) - 127;                       // -6..8
+  uint32_t mant = mag & 0x7fffffu;
+  uint32_t keep = mant >> 20, rem = mant & 0xfffffu;
+  if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) keep += 1u;
+  uint32_t code = ((uint32_t)(e + 7) << 3) + keep;      // a carry out of keep bumps the exponent
+  if (code > 0x7eu) code = 0x7eu;
+  return s | code;
+}
+
+// ---------------------------------------------------------------- wave helpers
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+template <int LO, int HI>   // reduce max over lanes differing in bits [log2 LO, log2 HI)
+__device__ __forceinline__ float wave_max_range(float v) {
+#pragma unroll
+  for (int o = LO; o < HI; o <<= 1) v = fmaxf(v, shfl_xor(v, o));
+  return v;
+}
+template <int LO, int HI>
+__device__ __forceinline__ float wave_sum_range(float v) {
+#pragma unroll
+  for (int o = LO; o < HI; o <<= 1) v += shfl_xor(v, o);
+  return v;
+}
+
+// Candidate-mask row i of sequence b as a 64-bit set (bit j = mask[b][i][j], j < qb).
+__device__ __forceinline__ uint64_t load_mask_row(const uint8_t* mask, int b, int i, int qb,
+                                                  int Qmax) {
+  if (mask == nullptr) return 1ull;          // Qmax == 1: the candidate sees itself
+  const uint8_t* row = mask + ((int64_t)b * Qmax + i) * Qmax;
+  uint64_t bits = 0;
+  for (int j = 0; j < qb; ++j) bits |= (uint64_t)(row[j] != 0) << j;
+  return bits;
+}
+
+}  // namespace pta

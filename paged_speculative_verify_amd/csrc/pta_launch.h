@@ -1,0 +1,51 @@
+// Internal launch entry points of the kernel files (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pta {
+
+struct AttnArgs;
+
+// dtype codes follow pta_dtype: 0 f32, 1 bf16, 2 fp8 e4m3fn
+hipError_t launch_valu(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, int rows_pow2,
+                       dim3 grid, hipStream_t s);
+hipError_t launch_mfma(const AttnArgs& a, int kv_dtype, int head_dim, int nwave, dim3 grid,
+                       hipStream_t s);
+
+struct MergeArgs {
+  const float* part_o;      // [B][Hq][Qmax][P][D]
+  const float* part_lse;    // [B][Hq][Qmax][P]
+  const int32_t* ctx;
+  const int32_t* qlen;
+  void* out;                // [B][Qmax][Hq][D] in q dtype
+  float* lse;               // [B][Hq][Qmax] or null
+  int32_t B, Hq, Qmax, P, part_tokens;
+};
+hipError_t launch_merge(const MergeArgs& m, int q_dtype, int head_dim, hipStream_t s);
+
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  const int64_t* slots;
+  void* k_cache;
+  void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t N, Hkv, D;
+  int64_t num_slots;        // num_blocks * page_size
+};
+hipError_t launch_append(const AppendArgs& p, int new_dtype, int kv_dtype, hipStream_t s);
+
+struct ValidateArgs {
+  const int32_t* tables;
+  const int32_t* ctx;
+  const int32_t* qlen;
+  int32_t* flags;
+  int32_t B, Qmax, MBS, max_ctx, page;
+  int64_t num_blocks;
+};
+hipError_t launch_validate(const ValidateArgs& v, hipStream_t s);
+
+}  // namespace pta

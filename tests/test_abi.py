@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/pta.h declares, and rejects bad arguments on the host (before any HIP
+call) with the documented status codes."""
+from __future__ import annotations
+
+import ctypes
+
+import pytest
+
+import paged_speculative_verify_amd as psv
+from paged_speculative_verify_amd._lib import PtaDims
+
+OK, NULLP, DIMS, DTYPE, UNSUP, WS = 0, 1, 2, 3, 4, 5
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails host checks
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return psv.load()
+
+
+def dims(**kw):
+    base = dict(num_seqs=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, max_q_len=1,
+                max_blocks_per_seq=256, max_ctx_len=4096, num_blocks=20000, q_dtype=1, kv_dtype=1,
+                path=0, reserved=0)
+    base.update(kw)
+    return PtaDims(**base)
+
+
+def attn(lib, d, mask=FAKE, ks=None, vs=None, out=FAKE, scale=0.1):
+    return lib.taco_paged_tree_attn(ctypes.byref(d) if d is not None else None, FAKE, FAKE, FAKE, ks, vs,
+                                    FAKE, FAKE, FAKE, mask, scale, out, None, None)
+
+
+def test_exports_every_declared_function(lib):
+    names = psv.declared_functions()
+    assert set(names) >= {"taco_paged_tree_attn", "taco_paged_tree_attn_splitk",
+                          "taco_paged_tree_attn_splitk_workspace_size", "taco_kv_append",
+                          "taco_pta_validate", "taco_pta_status_string", "taco_pta_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert psv.taco_pta_version() == 100
+    for st in range(7):
+        assert psv.taco_pta_status_string(st)
+    assert psv.taco_pta_status_string(99) == "unknown status"
+
+
+def test_dims_struct_layout():
+    assert ctypes.sizeof(PtaDims) == 56
+    assert PtaDims.num_blocks.offset == 32
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=30), DIMS),                 # Hq % Hkv != 0
+    (dict(head_dim=96), DIMS),
+    (dict(page_size=32), DIMS),
+    (dict(max_q_len=0), DIMS),
+    (dict(max_q_len=65), DIMS),
+    (dict(max_ctx_len=4097), DIMS),               # > page * max_blocks
+    (dict(num_blocks=0), DIMS),
+    (dict(num_seqs=-1), DIMS),
+    (dict(reserved=1), DIMS),
+    (dict(path=3), DIMS),
+    (dict(q_dtype=0, kv_dtype=1), DTYPE),         # fp32 q with bf16 KV
+    (dict(q_dtype=0, kv_dtype=2), DTYPE),
+    (dict(q_dtype=2, kv_dtype=2), DTYPE),
+    (dict(q_dtype=0, kv_dtype=0, path=2), UNSUP),  # MFMA needs bf16 q
+    (dict(max_q_len=16, num_q_heads=64, path=1), UNSUP),   # 128 rows on the VALU path
+    (dict(max_q_len=64, num_q_heads=64), UNSUP),   # 512 rows per KV head
+])
+def test_host_validation(lib, kw, status):
+    assert attn(lib, dims(**kw)) == status
+
+
+def test_null_pointers(lib):
+    assert attn(lib, None) == NULLP
+    assert attn(lib, dims(), out=None) == NULLP
+    assert attn(lib, dims(max_q_len=4), mask=None) == NULLP
+    assert attn(lib, dims(kv_dtype=2)) == NULLP                    # fp8 without scales
+    assert attn(lib, dims(), scale=float("nan")) == DIMS
+
+
+def test_zero_batch_is_a_noop(lib):
+    assert attn(lib, dims(num_seqs=0)) == OK
+
+
+def test_splitk_workspace(lib):
+    d = dims(num_seqs=4, max_q_len=32, num_q_heads=64, max_ctx_len=131072, max_blocks_per_seq=8192)
+    n = lib.taco_paged_tree_attn_splitk_workspace_size(ctypes.byref(d), 2048)
+    rows = 4 * 64 * 32 * 64
+    assert n >= rows * 129 * 4 and n % 256 == 0
+    assert lib.taco_paged_tree_attn_splitk_workspace_size(ctypes.byref(d), 100) == 0   # not a multiple of 32
+    assert lib.taco_paged_tree_attn_splitk_workspace_size(ctypes.byref(dims(head_dim=80)), 2048) == 0
+    st = lib.taco_paged_tree_attn_splitk(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE,
+                                         FAKE, 0.1, FAKE, None, 2048, FAKE, n - 1, None)
+    assert st == WS
+    st = lib.taco_paged_tree_attn_splitk(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE,
+                                         FAKE, 0.1, FAKE, None, 2048, None, n, None)
+    assert st == NULLP
+    st = lib.taco_paged_tree_attn_splitk(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE,
+                                         FAKE, 0.1, FAKE, None, 48, FAKE, n, None)
+    assert st == DIMS
+
+
+def test_kv_append_validation(lib):
+    d = dims()
+    f = lambda new_dt, n=8, dd=d, **kw: lib.taco_kv_append(
+        ctypes.byref(dd), kw.get("k", FAKE), FAKE, new_dt, FAKE, n, FAKE, FAKE,
+        kw.get("ks"), kw.get("vs"), None)
+    assert f(0) == DTYPE            # f32 rows into a bf16 cache
+    assert f(1, n=-1) == DIMS
+    assert f(1, n=0) == OK
+    assert f(1, k=None) == NULLP
+    assert f(1, dd=dims(kv_dtype=2)) == NULLP     # fp8 cache without scales
+    assert f(1, dd=dims(head_dim=32)) == DIMS
+
+
+def test_validate_host_checks(lib):
+    assert lib.taco_pta_validate(ctypes.byref(dims()), FAKE, FAKE, FAKE, None, None) == NULLP
+    assert lib.taco_pta_validate(ctypes.byref(dims(page_size=8)), FAKE, FAKE, FAKE, FAKE, None) == DIMS

@@ -1,0 +1,330 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances (max |out - oracle| over valid rows): 1e-5 for fp32 inputs, 1e-2
+for bf16, 3e-2 for fp8 KV; LSE is checked to 1e-4 / 2e-2 / 4e-2.  Indexing
+and masking are checked bit-exactly with probes whose exact answer is a
+stored integer, and by bit-identity under a relabelling of physical pages.
+"""
+from __future__ import annotations
+
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from workload import Spec, make, permute_pool
+from workload.device import out_to_f64, to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 3e-2}
+LSE_TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 4e-2}
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_speculative_verify_amd as psv
+    psv.load()
+    return torch
+
+
+def tol_key(spec):
+    return "fp8" if spec.kv_dtype == "fp8" else spec.q_dtype
+
+
+def run_gpu(torch, w, split=None, path="auto", want_lse=True):
+    import paged_speculative_verify_amd as psv
+    d = to_device(w)
+    out = torch.full_like(d.q, float("nan"))
+    B, Qmax, Hq, D = w.q.shape
+    lse = torch.full((B, Hq, Qmax), float("nan"), dtype=torch.float32, device=d.q.device) if want_lse else None
+    if split is None:
+        psv.taco_paged_tree_attn(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
+                                 d.tree_mask, d.scale, out=out, lse=lse, k_scale=d.k_scale,
+                                 v_scale=d.v_scale, max_ctx_len=d.max_ctx_len, path=path)
+    else:
+        psv.taco_paged_tree_attn_splitk(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
+                                        d.q_lens, d.tree_mask, d.scale, split, out=out, lse=lse,
+                                        k_scale=d.k_scale, v_scale=d.v_scale,
+                                        max_ctx_len=d.max_ctx_len, path=path)
+    torch.cuda.synchronize()
+    return out_to_f64(out), (lse.cpu().numpy().astype(np.float64) if want_lse else None)
+
+
+def run_oracle(w, rows=None):
+    s = w.spec
+    sel = slice(None) if rows is None else rows
+    return oracle.paged_tree_attn(w.q[sel], w.k_cache, w.v_cache, w.block_tables[sel], w.ctx_lens[sel],
+                                  w.q_lens[sel], w.tree_mask[sel], w.scale, q_dtype=s.q_dtype,
+                                  kv_dtype=s.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+
+
+def assert_parity(w, out, lse, ref, ref_lse, seqs=None):
+    key = tol_key(w.spec)
+    if seqs is not None:
+        out, lse = out[seqs], (lse[seqs] if lse is not None else None)
+    valid = ~np.isnan(ref)
+    # rows past q_len are untouched (still NaN), valid rows are finite
+    assert np.isnan(out[~valid]).all(), "padding rows were written"
+    assert np.isfinite(out[valid]).all(), "non-finite output in a valid row"
+    err = np.abs(out[valid] - ref[valid]).max()
+    assert err <= TOL[key], f"max abs err {err} > {TOL[key]}"
+    if lse is not None:
+        lv = ~np.isnan(ref_lse)
+        assert np.isnan(lse[~lv]).all()
+        lerr = np.abs(lse[lv] - ref_lse[lv]).max()
+        assert lerr <= LSE_TOL[key], f"lse err {lerr}"
+    return err
+
+
+def spec(name, B, Hq, Hkv, D, qd, kvd, ctx, q_len, tree="random", depth=None, ragged=False, seed=0,
+         **kw):
+    return Spec(name, B, Hq, Hkv, D, qd, kvd, ctx_range=ctx, q_len=q_len, q_len_ragged=ragged,
+                tree=tree, depth_cap=depth, seed=seed, **kw)
+
+
+# -------------------------------------------------------------- small cases
+CASES = [
+    # (id, spec, split, path)
+    ("tiny_decode_f32", "tiny_decode", None, "auto"),
+    ("tiny_decode_f32_split32", "tiny_decode", 32, "auto"),
+    ("decode_bf16_valu", spec("d", 6, 32, 8, 128, "bf16", "bf16", (1, 700), 1, "chain", seed=1), None, "valu"),
+    ("decode_bf16_mfma", spec("d", 6, 32, 8, 128, "bf16", "bf16", (1, 700), 1, "chain", seed=1), None, "mfma"),
+    ("decode_bf16_d64_valu", spec("d", 5, 8, 2, 64, "bf16", "bf16", (3, 300), 1, "chain", seed=2), None, "valu"),
+    ("decode_bf16_split_valu", spec("d", 6, 32, 8, 128, "bf16", "bf16", (100, 3000), 1, "chain", seed=3), 256, "valu"),
+    ("decode_f32_d128_mr8", spec("d", 3, 8, 1, 128, "f32", "f32", (20, 400), 1, "chain", seed=4), None, "valu"),
+    ("small_tree_valu_mr8", spec("t", 4, 4, 2, 128, "bf16", "bf16", (8, 200), 4, "random", seed=5), None, "valu"),
+    ("small_tree_mfma", spec("t", 4, 4, 2, 128, "bf16", "bf16", (8, 200), 4, "random", seed=5), None, "mfma"),
+    ("verify_tree16_g8", spec("v", 4, 64, 8, 128, "bf16", "bf16", (16, 900), 16, "random", 6, seed=6), None, "auto"),
+    ("verify_tree16_g8_split", spec("v", 4, 64, 8, 128, "bf16", "bf16", (16, 900), 16, "random", 6, seed=6), 128, "auto"),
+    ("verify_tree32_g8_split", spec("l", 2, 64, 8, 128, "bf16", "bf16", (300, 3000), 32, "random", 8, seed=7), 2048, "auto"),
+    ("verify_tree32_split64", spec("l", 2, 64, 8, 128, "bf16", "bf16", (33, 700), 32, "random", 8, seed=8), 64, "auto"),
+    ("ragged_tree_mfma", spec("r", 7, 16, 2, 128, "bf16", "bf16", (1, 500), 12, "random", ragged=True, seed=9), None, "auto"),
+    ("ragged_tree_d64", spec("r", 5, 16, 4, 64, "bf16", "bf16", (1, 300), 20, "random", ragged=True, seed=10), None, "auto"),
+    ("fp8_chain8_mfma", spec("f", 6, 32, 8, 128, "bf16", "fp8", (8, 1500), 8, "chain", seed=11), None, "auto"),
+    ("fp8_chain8_split", spec("f", 6, 32, 8, 128, "bf16", "fp8", (8, 1500), 8, "chain", seed=11), 512, "auto"),
+    ("fp8_decode_valu", spec("f", 6, 32, 8, 128, "bf16", "fp8", (1, 900), 1, "chain", seed=12), None, "valu"),
+    ("fp8_d64_tree", spec("f", 4, 16, 2, 64, "bf16", "fp8", (5, 400), 6, "random", seed=13), None, "auto"),
+    ("gqa1_tree64", spec("w", 2, 4, 4, 128, "bf16", "bf16", (64, 400), 64, "random", seed=14), None, "mfma"),
+    ("flat_forest", spec("ff", 3, 16, 2, 128, "bf16", "bf16", (10, 200), 10, "flat", seed=15), None, "auto"),
+]
+
+
+@pytest.mark.parametrize("cid,sp,split,path", CASES, ids=[c[0] for c in CASES])
+def test_parity_small(torch_cuda, cid, sp, split, path):
+    w = make(sp, poison=True)
+    say(cid, "B", w.q.shape[0], "ctx", w.ctx_lens.tolist()[:8], "split", split, "path", path)
+    out, lse = run_gpu(torch_cuda, w, split=split, path=path)
+    ref, ref_lse = run_oracle(w)
+    err = assert_parity(w, out, lse, ref, ref_lse)
+    say(cid, "max abs err", err)
+
+
+def test_split_matches_unsplit(torch_cuda):
+    w = make(spec("s", 3, 64, 8, 128, "bf16", "bf16", (200, 2500), 16, "random", 6, seed=21))
+    say("split_vs_unsplit")
+    a, _ = run_gpu(torch_cuda, w)
+    b, _ = run_gpu(torch_cuda, w, split=256)
+    v = ~np.isnan(a)
+    assert np.abs(a[v] - b[v]).max() <= 1e-2
+
+
+def test_permutation_and_repeat_bit_identical(torch_cuda):
+    for sp, path in ((spec("p", 4, 32, 8, 128, "bf16", "bf16", (30, 800), 1, "chain", seed=31), "valu"),
+                     (spec("p", 4, 64, 8, 128, "bf16", "bf16", (30, 800), 16, "random", 6, seed=32), "mfma"),
+                     (spec("p", 4, 32, 8, 128, "bf16", "fp8", (30, 800), 8, "chain", seed=33), "mfma")):
+        w = make(sp)
+        say("permutation", sp.kv_dtype, path)
+        a, la = run_gpu(torch_cuda, w, path=path)
+        a2, la2 = run_gpu(torch_cuda, w, path=path)
+        b, lb = run_gpu(torch_cuda, permute_pool(w, 5), path=path)
+        assert np.array_equal(a, a2, equal_nan=True) and np.array_equal(la, la2, equal_nan=True)
+        assert np.array_equal(a, b, equal_nan=True) and np.array_equal(la, lb, equal_nan=True)
+
+
+def _probe_workload(sp, seed=3):
+    """One-hot probe: per (seq, head, candidate) one visible key dominates by a score gap of
+    >= 1000; V channel 0/1 hold (position mod 256, head + 3*seq) so the output names the
+    exact logical position and head that were read."""
+    from tests.test_oracle_pins import enc
+    from tests import refs
+    rng = np.random.default_rng(seed)
+    w = make(sp)
+    kv, qd = sp.kv_dtype, sp.q_dtype
+    B, Qmax, Hq, D = w.q.shape
+    Hkv = w.k_cache.shape[1]
+    G = Hq // Hkv
+    wrap = 16 if kv == "fp8" else 256
+    if w.k_scale is not None:
+        w.k_scale[...] = 1.0
+        w.v_scale[...] = 1.0
+    w.q[...] = 0
+    w.k_cache[...] = 0
+    w.v_cache[...] = 0
+    want = np.full((B, Qmax, Hq, 2), np.nan)
+    one = enc(1.0, kv)
+    for b in range(B):
+        C, Qb = int(w.ctx_lens[b]), int(w.q_lens[b])
+        vis = refs.vis_from_parents(C, Qb, w.parents[b])
+        for t in range(C):
+            page, slot = w.block_tables[b, t // 16], t % 16
+            for hk in range(Hkv):
+                w.v_cache[page, hk, slot, 0] = enc(t % wrap, kv)
+                w.v_cache[page, hk, slot, 1] = enc((hk + 3 * b) % wrap, kv)
+        for h in range(Hq):
+            hk = h // G
+            for i in range(Qb):
+                t = int(rng.choice(np.flatnonzero(vis[i])))
+                page, slot = w.block_tables[b, t // 16], t % 16
+                ch = 2 + (h % G) * Qmax + i
+                w.k_cache[page, hk, slot, ch] = one
+                w.q[b, i, h, ch] = enc(2.0 ** math.ceil(math.log2(1000.0 / w.scale)), qd)
+                want[b, i, h] = (t % wrap, (hk + 3 * b) % wrap)
+    return w, want
+
+
+@pytest.mark.parametrize("cid,sp,path", [
+    ("probe_decode_valu", spec("o", 3, 8, 4, 64, "bf16", "bf16", (5, 300), 1, "chain", seed=41), "valu"),
+    ("probe_tree_mfma", spec("o", 3, 4, 1, 128, "bf16", "bf16", (12, 300), 12, "random", seed=42), "mfma"),
+    ("probe_tree_valu", spec("o", 3, 2, 1, 64, "bf16", "bf16", (12, 300), 4, "random", seed=43), "valu"),
+    ("probe_fp8_mfma", spec("o", 2, 4, 1, 128, "bf16", "fp8", (8, 200), 8, "chain", seed=44), "mfma"),
+    ("probe_f32", spec("o", 2, 2, 2, 64, "f32", "f32", (5, 200), 3, "random", seed=45), "valu"),
+])
+def test_one_hot_indexing_bit_exact(torch_cuda, cid, sp, path):
+    w, want = _probe_workload(sp)
+    say(cid)
+    for split in (None, 32):
+        out, _ = run_gpu(torch_cuda, w, split=split, path=path, want_lse=False)
+        v = ~np.isnan(want[..., 0])
+        assert np.array_equal(out[..., :2][v], want[v]), (cid, split)
+
+
+@pytest.mark.parametrize("path", ["mfma", "valu"])
+def test_mask_bit_exact(torch_cuda, path):
+    """K = 0, prefix V = 0, candidate j's V = e_j: out_i[j] > 0 exactly where the mask is set."""
+    from tests.test_oracle_pins import enc
+    Hq = 16 if path == "mfma" else 2
+    q_len = 16 if path == "mfma" else 4
+    w = make(spec("m", 3, Hq, 2 if path == "valu" else 1, 64, "bf16", "bf16", (20, 200), q_len, "random",
+                  5, seed=51))
+    say("mask probe", path)
+    w.k_cache[...] = 0
+    w.v_cache[...] = 0
+    for b in range(3):
+        C, Qb = int(w.ctx_lens[b]), int(w.q_lens[b])
+        for j in range(Qb):
+            t = C - Qb + j
+            w.v_cache[w.block_tables[b, t // 16], :, t % 16, j] = enc(1.0, "bf16")
+    out, _ = run_gpu(torch_cuda, w, path=path, want_lse=False)
+    for b in range(3):
+        Qb = int(w.q_lens[b])
+        got = out[b, :Qb, :, :Qb] > 0
+        want = (w.tree_mask[b, :Qb, :Qb] != 0)[:, None, :].repeat(out.shape[2], axis=1)
+        assert np.array_equal(got, want)
+        assert (out[b, :Qb, :, Qb:] == 0).all()
+
+
+def test_kv_append_parity(torch_cuda):
+    import torch
+    import paged_speculative_verify_amd as psv
+    from workload.gen import f32_to_bf16_bits
+    for kv, new_dt in (("bf16", "bf16"), ("f32", "f32"), ("fp8", "bf16"), ("fp8", "f32")):
+        w = make(spec("a", 5, 8, 4, 128, "bf16" if kv != "f32" else "f32", kv, (10, 300), 6, "chain", seed=61))
+        say("kv_append", kv, new_dt)
+        rng = np.random.default_rng(62)
+        pos = [(b, int(w.ctx_lens[b]) - int(w.q_lens[b]) + j) for b in range(5) for j in range(int(w.q_lens[b]))]
+        slots = np.array([w.block_tables[b, t // 16] * 16 + t % 16 for b, t in pos] + [-1, -7], np.int64)
+        x = (rng.standard_normal((len(slots), 4, 128)) * 3).astype(np.float32)
+        x[0, 0, :4] = [1e6, -1e6, 0.0, -0.0]
+        new = x if new_dt == "f32" else f32_to_bf16_bits(x)
+        ref_k, ref_v = oracle.kv_append(w.k_cache, w.v_cache, new, new[:, ::-1].copy(), slots,
+                                        cache_dtype=kv, new_dtype=new_dt, k_scale=w.k_scale, v_scale=w.v_scale)
+        d = to_device(w)
+        nv = torch.bfloat16 if new_dt == "bf16" else None
+        kn = torch.from_numpy(new).cuda()
+        vn = torch.from_numpy(new[:, ::-1].copy()).cuda()
+        if nv is not None:
+            kn, vn = kn.view(nv), vn.view(nv)
+        psv.taco_kv_append(kn, vn, torch.from_numpy(slots).cuda(), d.k_cache, d.v_cache,
+                           k_scale=d.k_scale, v_scale=d.v_scale)
+        torch.cuda.synchronize()
+        gk = d.k_cache.view(torch.uint8).cpu().numpy().view(ref_k.dtype).reshape(ref_k.shape)
+        gv = d.v_cache.view(torch.uint8).cpu().numpy().view(ref_v.dtype).reshape(ref_v.shape)
+        assert np.array_equal(gk.view(np.uint8), ref_k.view(np.uint8))
+        assert np.array_equal(gv.view(np.uint8), ref_v.view(np.uint8))
+
+
+def test_validate_flags(torch_cuda):
+    import torch
+    import paged_speculative_verify_amd as psv
+    w = make(spec("c", 4, 8, 2, 64, "bf16", "bf16", (20, 100), 4, "chain", seed=71))
+    say("validate")
+    d = to_device(w)
+    args = dict(max_q_len=4, num_blocks=w.num_blocks, max_ctx_len=int(w.ctx_lens.max()))
+    assert psv.taco_pta_validate(d.block_tables, d.ctx_lens, d.q_lens, **args) == 0
+    bt = d.block_tables.clone()
+    bt[1, 0] = w.num_blocks
+    assert psv.taco_pta_validate(bt, d.ctx_lens, d.q_lens, **args) == 8
+    ql = d.q_lens.clone()
+    ql[2] = 5
+    assert psv.taco_pta_validate(d.block_tables, d.ctx_lens, ql, **args) & 1
+    cl = d.ctx_lens.clone()
+    cl[0] = 2
+    assert psv.taco_pta_validate(d.block_tables, cl, d.q_lens, **args) & 2
+
+
+def test_empty_batch_and_errors(torch_cuda):
+    import torch
+    import paged_speculative_verify_amd as psv
+    w = make(spec("e", 2, 8, 2, 64, "bf16", "bf16", (20, 100), 4, "chain", seed=81))
+    d = to_device(w)
+    say("errors and empty batch")
+    with pytest.raises(psv.PtaError):      # max_ctx_len beyond page_size * max_blocks_per_seq
+        psv.taco_paged_tree_attn(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
+                                 d.tree_mask, d.scale, max_ctx_len=10 ** 9)
+    with pytest.raises(psv.PtaError):      # 8 * 4 = 32 rows on the vector-ALU path
+        psv.taco_paged_tree_attn(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
+                                 d.tree_mask, d.scale, path="valu")
+    e = lambda t: t[:0]
+    out = psv.taco_paged_tree_attn(e(d.q), d.k_cache, d.v_cache, e(d.block_tables), e(d.ctx_lens),
+                                   e(d.q_lens), e(d.tree_mask), d.scale)
+    torch.cuda.synchronize()
+    assert out.shape[0] == 0
+
+
+# -------------------------------------------------------------- full-size configs, sampled sequences
+FULL = [
+    ("llama3_8b_decode", [0, 17, 42, 63]),
+    ("llama31_70b_verify", [0, 9, 31]),
+    ("long_splitk_verify", [1]),
+    ("fp8_kv_chain", [0, 77, 127]),
+]
+
+
+@pytest.mark.parametrize("name,seqs", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(torch_cuda, name, seqs):
+    import bench
+    w = make(name)
+    cfg = bench.launch_config(name)
+    say("full", name, "split", cfg["split"], "path", cfg["path"], "sampled seqs", seqs)
+    out, lse = run_gpu(torch_cuda, w, split=cfg["split"], path=cfg["path"])
+    ref, ref_lse = run_oracle(w, rows=np.array(seqs))
+    err = assert_parity(w, out, lse, ref, ref_lse, seqs=np.array(seqs))
+    say("full", name, "max abs err", err)
+    # every other row is finite and every padding row untouched
+    B = w.q.shape[0]
+    for b in range(B):
+        qb = int(w.q_lens[b])
+        assert np.isfinite(out[b, :qb]).all()
+        assert np.isnan(out[b, qb:]).all()
