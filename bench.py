@@ -198,6 +198,10 @@ def main(argv=None) -> int:
     ap.add_argument("--config", default=HEADLINE, choices=sorted(LAUNCH))
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated step to step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=["auto", "valu", "mfma"], default=None,
+                    help="override the kernel family of the workload's launch configuration")
+    ap.add_argument("--split", type=int, default=None,
+                    help="override the split-K partition length (0 = one pass per sequence)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args(argv)
@@ -227,6 +231,10 @@ def main(argv=None) -> int:
 
     name = args.config
     cfg = launch_config(name)
+    if args.path is not None:
+        cfg["path"] = args.path
+    if args.split is not None:
+        cfg["split"] = args.split if args.split > 0 else None
     print(f"[bench] generating {args.sets} input set(s) for {name}", file=sys.stderr, flush=True)
     sets = []
     for r in range(args.sets):
