@@ -119,11 +119,20 @@ size_t taco_paged_tree_attn_splitk_workspace_size(const pta_dims* dims, int32_t 
  * partitions of partition_tokens logical positions (a positive multiple of
  * 32), attention over each partition runs as an independent work unit that
  * writes its normalised partial output and log-sum-exp into `workspace`, and
- * a second kernel on the same stream merges the partials by log-sum-exp into
- * out/lse.  Arguments otherwise as taco_paged_tree_attn.  workspace is caller-
- * owned device memory of at least workspace_bytes >=
- * taco_paged_tree_attn_splitk_workspace_size(dims, partition_tokens); its
- * contents on entry do not matter. */
+ * the last unit of each (sequence, KV head) to finish merges the partitions by
+ * log-sum-exp into out/lse, inside the same kernel launch (the long-sequence
+ * part of the 618zxw.cn article, section "長シーケンス推論最適化における
+ * TurboAttention": the sequence is processed in independent parts that are
+ * combined).  The merge reads partitions in index order, so results do not
+ * depend on scheduling.  Arguments otherwise as taco_paged_tree_attn.
+ *
+ * workspace: caller-owned device memory of at least workspace_bytes >=
+ * taco_paged_tree_attn_splitk_workspace_size(dims, partition_tokens).  Its
+ * first region (num_seqs * num_kv_heads int32 arrival counters, padded to 256
+ * bytes) must be zero before the first call that uses this workspace (e.g. a
+ * zero-filled allocation); every call leaves it zero again.  The rest of the
+ * workspace needs no initialisation.  Calls that may run concurrently must not
+ * share a workspace. */
 pta_status taco_paged_tree_attn_splitk(const pta_dims* dims, const void* q, const void* k_cache,
                                        const void* v_cache, const float* k_scale,
                                        const float* v_scale, const int32_t* block_tables,

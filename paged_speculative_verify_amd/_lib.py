@@ -228,7 +228,9 @@ def taco_paged_tree_attn_splitk(q, k_cache, v_cache, block_tables, ctx_lens, q_l
     """Split-K paged tree attention with a log-sum-exp merge (see include/pta.h).
 
     workspace: a caller-owned uint8 device tensor of at least
-    taco_paged_tree_attn_splitk_workspace_size(...) bytes; allocated here if None.
+    taco_paged_tree_attn_splitk_workspace_size(...) bytes whose arrival-counter
+    region is zero before its first use (torch.zeros does it; every call leaves
+    the counters zero again); allocated zero-filled here if None.
     """
     torch = _torch()
     lib = load()
@@ -239,7 +241,7 @@ def taco_paged_tree_attn_splitk(q, k_cache, v_cache, block_tables, ctx_lens, q_l
     if workspace is None:
         if need == 0:
             raise ValueError("invalid dims or partition_tokens for split-K")
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     else:
         _need(workspace, "workspace", device=q.device)
     _check(lib.taco_paged_tree_attn_splitk(

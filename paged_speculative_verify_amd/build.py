@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpta.so")
-SOURCES = ["pta_api.hip", "pta_valu.hip", "pta_mfma.hip", "pta_aux.hip"]
+SOURCES = ["pta_api.hip", "pta_valu.hip", "pta_stream.hip", "pta_mfma.hip", "pta_aux.hip"]
 HEADERS = ["pta_device.h", "pta_launch.h"]
 
 ARCH = "gfx950"
@@ -26,6 +26,8 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 vector ops stay off: plain float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators stay in ordinary VGPRs (no AGPR copies around VALU work)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"),
 ]
 

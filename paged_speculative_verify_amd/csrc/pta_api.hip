@@ -13,7 +13,7 @@ namespace {
 constexpr int kMaxQLen = 64;
 constexpr int kValuMaxRows = 8;     // largest G * max_q_len of the vector-ALU path
 constexpr int kMfmaMaxRows = 256;   // 8 waves x 32 rows
-constexpr int kAutoValuRows = 4;    // AUTO: vector ALU up to this many rows
+constexpr int kStreamMaxRows = 32;  // largest G * max_q_len of the streaming matrix-core path
 
 bool dtype_ok(int q, int kv) {
   return (q == PTA_F32 && kv == PTA_F32) || (q == PTA_BF16 && (kv == PTA_BF16 || kv == PTA_FP8_E4M3FN));
@@ -43,10 +43,19 @@ pta_status check_dims(const pta_dims* d) {
   return PTA_OK;
 }
 
+// Kernel families:
+//   VALU    vector-ALU page stream, any q dtype, rows per KV head <= 8
+//   STREAM  matrix-core page stream (bf16 q), rows per KV head <= 32: each wave
+//           walks its own pages with no barrier
+//   TILE    matrix-core shared-tile kernel (bf16 q), rows per KV head <= 256:
+//           one wave per 32 rows, K/V tiles shared through LDS
+enum Family { FAM_VALU, FAM_STREAM, FAM_TILE };
+
 struct Plan {
-  bool mfma;
+  Family fam;
   int rows_pow2;   // VALU
-  int nwave;       // MFMA
+  int rb;          // STREAM: 16-row blocks
+  int nw;          // STREAM / TILE: waves per workgroup
 };
 
 pta_status plan_for(const pta_dims* d, Plan* p) {
@@ -62,13 +71,22 @@ pta_status plan_for(const pta_dims* d, Plan* p) {
     if (!mfma_ok) return PTA_ERR_UNSUPPORTED;
     mfma = true;
   } else {
-    if (valu_ok && (rows <= kAutoValuRows || !mfma_ok)) mfma = false;
-    else if (mfma_ok) mfma = true;
+    if (mfma_ok) mfma = true;
+    else if (valu_ok) mfma = false;
     else return PTA_ERR_UNSUPPORTED;
   }
-  p->mfma = mfma;
   p->rows_pow2 = pow2_at_least(rows);
-  p->nwave = pow2_at_least((rows + 31) / 32);
+  if (!mfma) {
+    p->fam = FAM_VALU;
+    p->nw = 4;
+  } else if (rows <= kStreamMaxRows) {
+    p->fam = FAM_STREAM;
+    p->rb = rows <= 16 ? 1 : 2;
+    p->nw = 4;
+  } else {
+    p->fam = FAM_TILE;
+    p->nw = pow2_at_least((rows + 31) / 32);
+  }
   return PTA_OK;
 }
 
@@ -101,23 +119,30 @@ AttnArgs make_args(const pta_dims* d, const void* q, const void* k, const void* 
 
 pta_status run_attn(const pta_dims* d, const AttnArgs& a, const Plan& p, hipStream_t s) {
   const dim3 grid((unsigned)a.num_parts, (unsigned)a.Hkv, (unsigned)a.B);
-  hipError_t e = p.mfma ? launch_mfma(a, d->kv_dtype, d->head_dim, p.nwave, grid, s)
-                        : launch_valu(a, d->q_dtype, d->kv_dtype, d->head_dim, p.rows_pow2, grid, s);
+  hipError_t e;
+  switch (p.fam) {
+    case FAM_STREAM: e = launch_stream(a, d->kv_dtype, d->head_dim, p.rb, p.nw, grid, s); break;
+    case FAM_TILE: e = launch_mfma(a, d->kv_dtype, d->head_dim, p.nw, grid, s); break;
+    default: e = launch_valu(a, d->q_dtype, d->kv_dtype, d->head_dim, p.rows_pow2, grid, s); break;
+  }
   return e == hipSuccess ? PTA_OK : PTA_ERR_HIP;
 }
 
 struct SplitLayout {
   int64_t parts;
-  size_t o_bytes, lse_off, total;
+  size_t o_off, lse_off, total;
 };
 
+// Workspace: [counters int32 B*Hkv | partial O float B*Hq*Qmax*P*D | partial LSE float B*Hq*Qmax*P],
+// each region 256-byte aligned.  Only the counters must be zero on entry; the call leaves them zero.
 bool split_layout(const pta_dims* d, int32_t T, SplitLayout* L) {
   if (T <= 0 || T % 32 != 0) return false;
   L->parts = ((int64_t)d->max_ctx_len + T - 1) / T;
   const int64_t rows = (int64_t)d->num_seqs * d->num_q_heads * d->max_q_len * L->parts;
-  L->o_bytes = (size_t)rows * d->head_dim * sizeof(float);
-  L->lse_off = (L->o_bytes + 255) & ~(size_t)255;
-  L->total = L->lse_off + (((size_t)rows * sizeof(float) + 255) & ~(size_t)255);
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  L->o_off = up((size_t)d->num_seqs * d->num_kv_heads * sizeof(int32_t));
+  L->lse_off = L->o_off + up((size_t)rows * d->head_dim * sizeof(float));
+  L->total = L->lse_off + up((size_t)rows * sizeof(float));
   return true;
 }
 
@@ -178,20 +203,13 @@ pta_status taco_paged_tree_attn_splitk(const pta_dims* d, const void* q, const v
   if (workspace_bytes < L.total) return PTA_ERR_WORKSPACE_TOO_SMALL;
   AttnArgs a = make_args(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
                          tree_mask, scale, out, lse);
-  a.part_o = reinterpret_cast<float*>(workspace);
-  a.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + L.lse_off);
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.counters = reinterpret_cast<int32_t*>(ws);
+  a.part_o = reinterpret_cast<float*>(ws + L.o_off);
+  a.part_lse = reinterpret_cast<float*>(ws + L.lse_off);
   a.part_tokens = partition_tokens;
   a.num_parts = (int32_t)L.parts;
-  hipStream_t s = (hipStream_t)stream;
-  st = run_attn(d, a, p, s);
-  if (st != PTA_OK) return st;
-  MergeArgs m{};
-  m.part_o = a.part_o; m.part_lse = a.part_lse;
-  m.ctx = ctx_lens; m.qlen = q_lens;
-  m.out = out; m.lse = lse;
-  m.B = d->num_seqs; m.Hq = d->num_q_heads; m.Qmax = d->max_q_len;
-  m.P = (int32_t)L.parts; m.part_tokens = partition_tokens;
-  return launch_merge(m, d->q_dtype, d->head_dim, s) == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+  return run_attn(d, a, p, (hipStream_t)stream);
 }
 
 pta_status taco_kv_append(const pta_dims* d, const void* k_new, const void* v_new,

@@ -1,69 +1,8 @@
-// Split-K merge, KV append and contract validation kernels.
+// KV append and contract validation kernels.
 #include "pta_device.h"
 #include "pta_launch.h"
 
 namespace pta {
-
-// ---------------------------------------------------------------- split-K merge
-// One wave per output row (b, h, i).  The partial of partition p is the
-// normalised output O_p and LSE_p over that partition's keys; the merged row is
-//   LSE = ln sum_p exp(LSE_p),   out = sum_p exp(LSE_p - LSE) O_p
-// (the long-sequence design of the 618zxw.cn article, section
-// "長シーケンス推論最適化におけるTurboAttention": partitions of the sequence
-// are processed independently and combined).
-template <typename QT, int D>
-__global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
-  constexpr int EPL = D / 64;
-  constexpr float NEG_INF = -__builtin_huge_valf();
-  const int lane = threadIdx.x;
-  const int64_t rowid = blockIdx.x;                   // ((b * Hq + h) * Qmax + i)
-  const int i = (int)(rowid % a.Qmax);
-  const int h = (int)((rowid / a.Qmax) % a.Hq);
-  const int b = (int)(rowid / ((int64_t)a.Qmax * a.Hq));
-  if (i >= a.qlen[b]) return;
-  // partitions holding this sequence's context (never more than the workspace holds)
-  const int np = min((a.ctx[b] + a.part_tokens - 1) / a.part_tokens, a.P);
-  const float* lsep = a.part_lse + rowid * a.P;
-  const float* op = a.part_o + rowid * a.P * D;
-
-  float mx = NEG_INF;
-  for (int p = lane; p < np; p += 64) mx = fmaxf(mx, lsep[p]);
-  mx = wave_max_range<1, 64>(mx);
-  const float muse = mx == NEG_INF ? 0.f : mx;
-  float wsum = 0.f;
-  for (int p = lane; p < np; p += 64) wsum += __expf(lsep[p] - muse);
-  wsum = wave_sum_range<1, 64>(wsum);
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-
-  float acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const float w = __expf(lsep[p] - muse) * inv;   // exp(-inf) = 0 for empty partitions
-    if (w == 0.f) continue;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, op[(int64_t)p * D + lane * EPL + e], acc[e]);
-  }
-  const int64_t obase = (((int64_t)b * a.Qmax + i) * a.Hq + h) * D + lane * EPL;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    if constexpr (QT::bytes == 4) reinterpret_cast<float*>(a.out)[obase + e] = acc[e];
-    else reinterpret_cast<uint16_t*>(a.out)[obase + e] = f32_to_bf16(acc[e]);
-  }
-  if (lane == 0 && a.lse != nullptr)
-    a.lse[rowid] = wsum > 0.f ? muse + __logf(wsum) : NEG_INF;
-}
-
-hipError_t launch_merge(const MergeArgs& m, int q_dtype, int D, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)m.B * m.Hq * m.Qmax));
-  if (grid.x == 0) return hipSuccess;
-  if (q_dtype == 0 && D == 64) hipLaunchKernelGGL((merge_kernel<F32, 64>), grid, dim3(64), 0, s, m);
-  else if (q_dtype == 0 && D == 128) hipLaunchKernelGGL((merge_kernel<F32, 128>), grid, dim3(64), 0, s, m);
-  else if (q_dtype == 1 && D == 64) hipLaunchKernelGGL((merge_kernel<BF16, 64>), grid, dim3(64), 0, s, m);
-  else if (q_dtype == 1 && D == 128) hipLaunchKernelGGL((merge_kernel<BF16, 128>), grid, dim3(64), 0, s, m);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
 
 // ---------------------------------------------------------------- KV append
 // One wave per (token, KV head); slot = block * 16 + offset, negative = skip.

@@ -36,6 +36,7 @@ struct AttnArgs {
   float* lse;              // may be null
   float* part_o;           // split-K partial outputs [B][Hq][Qmax][P][D], or null (unsplit)
   float* part_lse;         // split-K partial LSE     [B][Hq][Qmax][P]
+  int32_t* counters;       // split-K arrival counters [B][Hkv] (zero between calls)
   float scale_log2;        // softmax scale * log2(e)
   int32_t B, Hq, Hkv, G, Qmax, MBS;
   int32_t part_tokens;     // partition length in tokens (split) or 0
@@ -119,6 +120,104 @@ __device__ __forceinline__ uint64_t load_mask_row(const uint8_t* mask, int b, in
   uint64_t bits = 0;
   for (int j = 0; j < qb; ++j) bits |= (uint64_t)(row[j] != 0) << j;
   return bits;
+}
+
+// ---------------------------------------------------------------- split-K finish
+// Partials travel between work units through device-coherent single-word
+// accesses (agent-scope atomic stores / loads: write-through and re-read at the
+// device coherence point, so no unit needs a whole-cache write-back or
+// invalidate).  A unit's partial stores complete (s_waitcnt) before its
+// arrival is counted.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// True when this work unit's results go to workspace partials (split-K and the
+// sequence spans more than one partition); a sequence that fits in one
+// partition is written straight to out/lse with no partial and no merge.
+__device__ __forceinline__ bool unit_writes_partials(const AttnArgs& a, int C) {
+  return a.part_o != nullptr && C > a.part_tokens;
+}
+
+// Called by every thread of a split-K work unit (sequence b, KV head hkv) once
+// its normalised partial output and log-sum-exp are stored with
+// store_coherent.  The last unit of (b, hkv) to arrive merges the partitions
+// of all its rows:
+//   LSE = ln sum_p exp(LSE_p),   out = sum_p exp(LSE_p - LSE) O_p
+// (the long-sequence design of the 618zxw.cn article, section
+// "長シーケンス推論最適化におけるTurboAttention": the sequence is cut into
+// parts processed independently and combined).  The merge reads partitions in
+// index order, so the result does not depend on which unit arrives last.  The
+// arrival counter is reset to zero for the next call.
+template <typename QT, int D>
+__device__ __forceinline__ void splitk_finish(const AttnArgs& a, int b, int hkv, int C, int qb) {
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);            // this thread's partial stores have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  const int np = (C + a.part_tokens - 1) / a.part_tokens;
+  int32_t* cnt = a.counters + (int64_t)b * a.Hkv + hkv;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const int M = a.G * qb;
+  constexpr int Q4 = D / 4;
+  constexpr int PB = 8;                     // partitions fetched per round trip
+  for (int idx = threadIdx.x; idx < M * Q4; idx += blockDim.x) {
+    const int r = idx / Q4, d = (idx % Q4) * 4;
+    const int h = hkv * a.G + r / qb, i = r % qb;
+    const int64_t prow = (((int64_t)b * a.Hq + h) * a.Qmax + i) * a.num_parts;
+    // online log-sum-exp over the partitions, PB at a time with every load in flight
+    float mrun = NEG_INF, wsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < np; p0 += PB) {
+      float lp[PB];
+      f32x4 op[PB];
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        const bool ok = p0 + j < np;
+        const int64_t pr = prow + (ok ? p0 + j : 0);
+        lp[j] = ok ? load_coherent(a.part_lse + pr) : NEG_INF;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) op[j][e] = ok ? load_coherent(a.part_o + pr * D + d + e) : 0.f;
+      }
+      float mx = mrun;
+#pragma unroll
+      for (int j = 0; j < PB; ++j) mx = fmaxf(mx, lp[j]);
+      const float muse = mx == NEG_INF ? 0.f : mx;
+      const float alpha = __expf(mrun - muse);          // 0 while nothing has been seen
+      wsum *= alpha;
+      acc *= alpha;
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        const float w = __expf(lp[j] - muse);           // exp(-inf) = 0: no visible key there
+        wsum += w;
+        acc += w * op[j];
+      }
+      mrun = mx;
+    }
+    const float muse = mrun == NEG_INF ? 0.f : mrun;
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    acc *= inv;
+    const int64_t o = (((int64_t)b * a.Qmax + i) * a.Hq + h) * D + d;
+    if constexpr (QT::bytes == 4) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = acc;
+    } else {
+      uint2 w;
+      w.x = pack_bf16x2(acc[0], acc[1]);
+      w.y = pack_bf16x2(acc[2], acc[3]);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + o) = w;
+    }
+    if (d == 0 && a.lse != nullptr)
+      a.lse[((int64_t)b * a.Hq + h) * a.Qmax + i] = wsum > 0.f ? muse + __logf(wsum) : NEG_INF;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace pta

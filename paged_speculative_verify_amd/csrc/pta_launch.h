@@ -11,19 +11,10 @@ struct AttnArgs;
 // dtype codes follow pta_dtype: 0 f32, 1 bf16, 2 fp8 e4m3fn
 hipError_t launch_valu(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, int rows_pow2,
                        dim3 grid, hipStream_t s);
+hipError_t launch_stream(const AttnArgs& a, int kv_dtype, int head_dim, int rb, int nw, dim3 grid,
+                         hipStream_t s);
 hipError_t launch_mfma(const AttnArgs& a, int kv_dtype, int head_dim, int nwave, dim3 grid,
                        hipStream_t s);
-
-struct MergeArgs {
-  const float* part_o;      // [B][Hq][Qmax][P][D]
-  const float* part_lse;    // [B][Hq][Qmax][P]
-  const int32_t* ctx;
-  const int32_t* qlen;
-  void* out;                // [B][Qmax][Hq][D] in q dtype
-  float* lse;               // [B][Hq][Qmax] or null
-  int32_t B, Hq, Qmax, P, part_tokens;
-};
-hipError_t launch_merge(const MergeArgs& m, int q_dtype, int head_dim, hipStream_t s);
 
 struct AppendArgs {
   const void* k_new;

@@ -90,6 +90,7 @@ __global__ __launch_bounds__(NWAVE * 64) void mfma_attn_kernel(AttnArgs a) {
     t1 = min(C, t0 + a.part_tokens);
     if (t0 >= t1) return;
   }
+  const bool split_out = unit_writes_partials(a, C);   // else: final output written directly
   const int nst = (t1 - t0 + 31) / 32;
 
   // ---- this lane's row and its Q^T operand (B of S^T = K Q^T)
@@ -265,11 +266,11 @@ __global__ __launch_bounds__(NWAVE * 64) void mfma_attn_kernel(AttnArgs a) {
 
   // ---- epilogue: this lane's row, dims 32mb + 8(r/4) + 4*half + (r%4)
   const float lt = lpart + shfl_xor(lpart, 32);   // the two halves of the row's 32 tokens
-  if (!row_ok) return;
+  if (row_ok) {
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float muse = m == NEG_INF ? 0.f : m;
   const float lse = lt > 0.f ? (muse + fast_log2(lt)) * kLn2 : NEG_INF;
-  if (a.part_o != nullptr) {
+  if (split_out) {
     const int64_t prow = (((int64_t)b * a.Hq + h) * a.Qmax + ci) * a.num_parts + part;
     float* op = a.part_o + prow * D;
 #pragma unroll
@@ -277,12 +278,10 @@ __global__ __launch_bounds__(NWAVE * 64) void mfma_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = mb * 32 + 8 * q4 + 4 * half;
-        f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = oacc[mb][4 * q4 + e] * inv;
-        *reinterpret_cast<f32x4*>(op + d) = v;
+        for (int e = 0; e < 4; ++e) store_coherent(op + d + e, oacc[mb][4 * q4 + e] * inv);
       }
-    if (half == 0) a.part_lse[prow] = lse;
+    if (half == 0) store_coherent(a.part_lse + prow, lse);
   } else {
     uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (((int64_t)b * a.Qmax + ci) * a.Hq + h) * D;
 #pragma unroll
@@ -297,6 +296,8 @@ __global__ __launch_bounds__(NWAVE * 64) void mfma_attn_kernel(AttnArgs a) {
       }
     if (half == 0 && a.lse != nullptr) a.lse[((int64_t)b * a.Hq + h) * a.Qmax + ci] = lse;
   }
+  }
+  if (split_out) splitk_finish<BF16, D>(a, b, hkv, C, qb);
 }
 
 // ---------------------------------------------------------------- launchers

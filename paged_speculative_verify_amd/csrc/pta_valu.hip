@@ -102,6 +102,7 @@ __global__ __launch_bounds__(NW * 64) void valu_attn_kernel(AttnArgs a) {
     t1 = min(C, t0 + a.part_tokens);
     if (t0 >= t1) return;               // partition past this sequence's context
   }
+  const bool split_out = unit_writes_partials(a, C);   // else: final output written directly
 
   // rows: r = g * qb + i  ->  q-head hkv * G + g, candidate i
   float qv[MR][EPL];
@@ -258,15 +259,16 @@ __global__ __launch_bounds__(NW * 64) void valu_attn_kernel(AttnArgs a) {
     const float o = lt > 0.f ? ot / lt : 0.f;
     const float lse = lt > 0.f ? (muse + fast_log2(lt)) * kLn2 : NEG_INF;
     const int g = r / qb, i = r % qb, h = hkv * a.G + g;
-    if (a.part_o != nullptr) {
+    if (split_out) {
       const int64_t row = (((int64_t)b * a.Hq + h) * a.Qmax + i) * a.num_parts + part;
-      a.part_o[row * D + d] = o;
-      if (d == 0) a.part_lse[row] = lse;
+      store_coherent(a.part_o + row * D + d, o);
+      if (d == 0) store_coherent(a.part_lse + row, lse);
     } else {
       store_out<QT>(a.out, (((int64_t)b * a.Qmax + i) * a.Hq + h) * D + d, o);
       if (d == 0 && a.lse != nullptr) a.lse[((int64_t)b * a.Hq + h) * a.Qmax + i] = lse;
     }
   }
+  if (split_out) splitk_finish<QT, D>(a, b, hkv, C, qb);
 }
 
 // ---------------------------------------------------------------- launchers

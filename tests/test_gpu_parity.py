@@ -328,3 +328,35 @@ def test_full_size_sampled(torch_cuda, name, seqs):
         qb = int(w.q_lens[b])
         assert np.isfinite(out[b, :qb]).all()
         assert np.isnan(out[b, qb:]).all()
+
+
+def test_splitk_workspace_reused_across_calls(torch_cuda):
+    """One zero-filled workspace serves several split-K calls in a row (the
+    fused merge resets its arrival counters), with changing partition lengths
+    and batches, and every call matches the oracle."""
+    import torch
+    import paged_speculative_verify_amd as psv
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    for n, (sp, split) in enumerate([
+            (spec("w", 5, 32, 8, 128, "bf16", "bf16", (40, 3000), 1, "chain", seed=91), 256),
+            (spec("w", 3, 32, 8, 128, "bf16", "bf16", (40, 3000), 1, "chain", seed=92), 64),
+            (spec("w", 4, 64, 8, 128, "bf16", "bf16", (40, 2000), 16, "random", 6, seed=93), 128),
+            (spec("w", 5, 32, 8, 128, "bf16", "fp8", (40, 3000), 8, "chain", seed=94), 512),
+            (spec("w", 5, 32, 8, 128, "bf16", "bf16", (40, 3000), 1, "chain", seed=91), 256)]):
+        w = make(sp, poison=True)
+        say("workspace reuse", n, sp.kv_dtype, "q", sp.q_len, "split", split)
+        d = to_device(w)
+        need = psv.taco_paged_tree_attn_splitk_workspace_size(d.q, d.k_cache, d.block_tables, split,
+                                                               max_ctx_len=d.max_ctx_len)
+        assert 0 < need <= ws.numel()
+        out = torch.full_like(d.q, float("nan"))
+        B, Qmax, Hq, D = w.q.shape
+        lse = torch.full((B, Hq, Qmax), float("nan"), dtype=torch.float32, device="cuda")
+        psv.taco_paged_tree_attn_splitk(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
+                                        d.tree_mask, d.scale, split, out=out, lse=lse, k_scale=d.k_scale,
+                                        v_scale=d.v_scale, workspace=ws, max_ctx_len=d.max_ctx_len)
+        torch.cuda.synchronize()
+        ref, ref_lse = run_oracle(w)
+        assert_parity(w, out_to_f64(out), lse.cpu().numpy().astype(np.float64), ref, ref_lse)
+        counters = ws[:B * w.k_cache.shape[1] * 4].view(torch.int32)
+        assert int(counters.abs().sum()) == 0, "arrival counters not reset"
