@@ -32,14 +32,16 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 HEADLINE = "llama3_8b_decode"
 
-# launch configuration of each workload: split-K partition length (None = one
-# pass per sequence) and kernel family (auto picks by rows per KV head)
+# launch configuration of each workload: entry point ("whole": one pass per
+# sequence, "split": split-K partitions of `split` tokens, "balanced": equal
+# page slices per wave of a persistent grid) and kernel family (auto picks by
+# rows per KV head)
 LAUNCH = {
-    "tiny_decode": dict(split=None, path="auto"),
-    "llama3_8b_decode": dict(split=None, path="auto"),
-    "llama31_70b_verify": dict(split=1024, path="auto"),
-    "long_splitk_verify": dict(split=2048, path="auto"),
-    "fp8_kv_chain": dict(split=None, path="auto"),
+    "tiny_decode": dict(mode="whole", split=None, path="auto"),
+    "llama3_8b_decode": dict(mode="whole", split=None, path="auto"),
+    "llama31_70b_verify": dict(mode="split", split=1024, path="auto"),
+    "long_splitk_verify": dict(mode="split", split=2048, path="auto"),
+    "fp8_kv_chain": dict(mode="whole", split=None, path="auto"),
 }
 
 KERNEL_SOURCES = ["pta_device.h", "pta_valu.hip", "pta_stream.hip", "pta_mfma.hip", "pta_aux.hip", "pta_api.hip"]
@@ -125,15 +127,14 @@ class DeviceSet:
         self.workspace = None
 
 
-def run_append(psv, ds):
-    d = ds.d
-    psv.taco_kv_append(ds.k_new, ds.v_new, ds.slots, d.k_cache, d.v_cache, k_scale=d.k_scale,
-                       v_scale=d.v_scale)
-
-
 def run_attention(psv, ds, cfg):
     d = ds.d
-    if cfg["split"] is None:
+    if cfg["mode"] == "balanced":
+        psv.taco_paged_tree_attn_balanced(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
+                                          d.q_lens, d.tree_mask, d.scale, out=ds.out, lse=ds.lse,
+                                          k_scale=d.k_scale, v_scale=d.v_scale, workspace=ds.workspace,
+                                          max_ctx_len=d.max_ctx_len, path=cfg["path"])
+    elif cfg["mode"] == "whole":
         psv.taco_paged_tree_attn(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
                                  d.tree_mask, d.scale, out=ds.out, lse=ds.lse, k_scale=d.k_scale,
                                  v_scale=d.v_scale, max_ctx_len=d.max_ctx_len, path=cfg["path"])
@@ -201,7 +202,8 @@ def main(argv=None) -> int:
     ap.add_argument("--path", choices=["auto", "valu", "mfma"], default=None,
                     help="override the kernel family of the workload's launch configuration")
     ap.add_argument("--split", type=int, default=None,
-                    help="override the split-K partition length (0 = one pass per sequence)")
+                    help="override the entry point: split-K partition length, 0 = one pass per "
+                         "sequence, -1 = balanced page slices")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args(argv)
@@ -234,6 +236,7 @@ def main(argv=None) -> int:
     if args.path is not None:
         cfg["path"] = args.path
     if args.split is not None:
+        cfg["mode"] = "split" if args.split > 0 else ("whole" if args.split == 0 else "balanced")
         cfg["split"] = args.split if args.split > 0 else None
     print(f"[bench] generating {args.sets} input set(s) for {name}", file=sys.stderr, flush=True)
     sets = []
@@ -242,18 +245,33 @@ def main(argv=None) -> int:
         sets.append(DeviceSet(w, torch))
         print(f"[bench] set {r}: ctx sum {int(w.ctx_lens.sum())}, KV {kv_bytes(w) / 1e6:.1f} MB",
               file=sys.stderr, flush=True)
-    if cfg["split"] is not None:
-        for ds in sets:
+    for ds in sets:
+        if cfg["mode"] == "split":
             nbytes = psv.taco_paged_tree_attn_splitk_workspace_size(
                 ds.d.q, ds.d.k_cache, ds.d.block_tables, cfg["split"], max_ctx_len=ds.d.max_ctx_len)
-            ds.workspace = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        elif cfg["mode"] == "balanced":
+            nbytes = psv.taco_paged_tree_attn_balanced_workspace_size(
+                ds.d.q, ds.d.k_cache, ds.d.block_tables, max_ctx_len=ds.d.max_ctx_len)
+        else:
+            continue
+        ds.workspace = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+    # validated once, then re-issued with no per-call Python checks so the host stays ahead
+    for ds in sets:
+        d = ds.d
+        ds.append_call = psv.prepare_kv_append(ds.k_new, ds.v_new, ds.slots, d.k_cache, d.v_cache,
+                                               k_scale=d.k_scale, v_scale=d.v_scale)
+        ds.attn_call = psv.prepare_paged_tree_attn(
+            cfg["mode"], d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens, d.tree_mask,
+            d.scale, ds.out, lse=ds.lse, k_scale=d.k_scale, v_scale=d.v_scale,
+            partition_tokens=cfg["split"], workspace=ds.workspace, max_ctx_len=d.max_ctx_len,
+            path=cfg["path"])
     for i in range(args.warmup):
         ds = sets[i % len(sets)]
-        run_append(psv, ds)
-        run_attention(psv, ds, cfg)
+        ds.append_call()
+        ds.attn_call()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -266,10 +284,11 @@ def main(argv=None) -> int:
         ds = sets[order[i]]
         e0, e1, e2 = ev[i]
         e0.record(stream)
-        run_append(psv, ds)
+        ds.append_call()
         e1.record(stream)
-        run_attention(psv, ds, cfg)
+        ds.attn_call()
         e2.record(stream)
+    t_enqueue = time.perf_counter() - t_wall
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     step_ms = [e0.elapsed_time(e2) for e0, _, e2 in ev]
@@ -303,7 +322,8 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": name, "batch": sets[0].w.q.shape[0], "q_heads": sets[0].w.q.shape[2],
                    "kv_heads": sets[0].w.k_cache.shape[1], "head_dim": sets[0].w.q.shape[3],
-                   "max_q_len": sets[0].w.q.shape[1], "page": 16, "split_tokens": cfg["split"],
+                   "max_q_len": sets[0].w.q.shape[1], "page": 16, "entry": cfg["mode"],
+                   "split_tokens": cfg["split"],
                    "path": cfg["path"], "input_sets_rotated": len(sets)},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "candidates_per_s": round(cand_per_s, 1),
@@ -311,12 +331,12 @@ def main(argv=None) -> int:
         "attention_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 5),
                                  round(float(np.percentile(attn_ms, 90)), 5)],
         "kv_append_ms": round(sum(a - b for a, b in zip(step_ms, attn_ms)) / K, 5),
+        "host_enqueue_ms_per_step": round(t_enqueue / K * 1e3, 5),
         "attention_tflops": round(tflops, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "paged tree attention kernel"
-                               + (" (split-K, merge fused)" if cfg["split"] else ""),
+                     "kernel": "paged tree attention kernel (" + cfg["mode"] + " entry, merge fused)",
                      "algorithmic_bytes_per_launch": int(kv_per_launch)},
         "kernel_source_hash": src_hash,
     }

@@ -141,6 +141,34 @@ pta_status taco_paged_tree_attn_splitk(const pta_dims* dims, const void* q, cons
                                        float* lse, int32_t partition_tokens, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace taken by taco_paged_tree_attn_balanced for these
+ * dims on the current device (0 on invalid input or when the balanced mode
+ * does not serve these dims). */
+size_t taco_paged_tree_attn_balanced_workspace_size(const pta_dims* dims);
+
+/* Work-balanced paged tree attention.  The pages of every (sequence, KV head)
+ * unit are laid end to end and cut into equal contiguous slices, one per wave
+ * of a persistent grid sized to the current device, so ragged context lengths
+ * cost no load imbalance (sequence-dimension parallelism, design talk
+ * "优化策略总结" item 2; a sequence processed in parts that are combined,
+ * 618zxw.cn article section "長シーケンス推論最適化におけるTurboAttention").
+ * A slice holding a whole unit writes its rows directly; a slice that ends
+ * inside a unit writes a normalised partial and log-sum-exp, and the unit's
+ * last slice to finish merges the unit's partials in order inside the same
+ * launch.  Served for bf16 q with G * max_q_len <= 32 rows per KV head (the
+ * matrix-core streaming path) and num_seqs <= 16383; otherwise
+ * PTA_ERR_UNSUPPORTED.  Arguments as taco_paged_tree_attn; workspace as for
+ * taco_paged_tree_attn_splitk (caller-owned, counter region zero before first
+ * use and left zero, no sharing between concurrent calls) with
+ * workspace_bytes >= taco_paged_tree_attn_balanced_workspace_size(dims). */
+pta_status taco_paged_tree_attn_balanced(const pta_dims* dims, const void* q, const void* k_cache,
+                                         const void* v_cache, const float* k_scale,
+                                         const float* v_scale, const int32_t* block_tables,
+                                         const int32_t* ctx_lens, const int32_t* q_lens,
+                                         const uint8_t* tree_mask, float scale, void* out,
+                                         float* lse, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
 /* KV append: write num_tokens new K/V rows into their cache slots, as blocks
  * are handed out while tokens are generated (Paged Attention section of the
  * design talk).

@@ -6,12 +6,17 @@ device memory and streams only.
 """
 from ._lib import (  # noqa: F401
     PATHS,
+    PreparedCall,
+    prepare_kv_append,
+    prepare_paged_tree_attn,
     PtaDims,
     PtaError,
     declared_functions,
     load,
     make_dims,
     taco_kv_append,
+    taco_paged_tree_attn_balanced,
+    taco_paged_tree_attn_balanced_workspace_size,
     taco_paged_tree_attn,
     taco_paged_tree_attn_splitk,
     taco_paged_tree_attn_splitk_workspace_size,

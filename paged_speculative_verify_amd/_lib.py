@@ -72,6 +72,10 @@ def load() -> ctypes.CDLL:
     lib.taco_paged_tree_attn_splitk_workspace_size.restype = SZ
     lib.taco_paged_tree_attn_splitk.argtypes = [D, P, P, P, P, P, P, P, P, P, F, P, P, I32, P, SZ, P]
     lib.taco_paged_tree_attn_splitk.restype = ctypes.c_int
+    lib.taco_paged_tree_attn_balanced_workspace_size.argtypes = [D]
+    lib.taco_paged_tree_attn_balanced_workspace_size.restype = SZ
+    lib.taco_paged_tree_attn_balanced.argtypes = [D, P, P, P, P, P, P, P, P, P, F, P, P, P, SZ, P]
+    lib.taco_paged_tree_attn_balanced.restype = ctypes.c_int
     lib.taco_kv_append.argtypes = [D, P, P, I32, P, I32, P, P, P, P, P]
     lib.taco_kv_append.restype = ctypes.c_int
     lib.taco_pta_validate.argtypes = [D, P, P, P, P, P]
@@ -252,6 +256,40 @@ def taco_paged_tree_attn_splitk(q, k_cache, v_cache, block_tables, ctx_lens, q_l
     return out
 
 
+def taco_paged_tree_attn_balanced_workspace_size(q, k_cache, block_tables, max_ctx_len=None,
+                                                 path="auto") -> int:
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    return int(load().taco_paged_tree_attn_balanced_workspace_size(ctypes.byref(dims)))
+
+
+def taco_paged_tree_attn_balanced(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask,
+                                  scale, out=None, lse=None, k_scale=None, v_scale=None,
+                                  workspace=None, max_ctx_len=None, path="auto", stream=None):
+    """Work-balanced paged tree attention (see include/pta.h).
+
+    workspace: a caller-owned uint8 device tensor of at least
+    taco_paged_tree_attn_balanced_workspace_size(...) bytes whose arrival-counter
+    region is zero before its first use; allocated zero-filled here if None.
+    """
+    torch = _torch()
+    lib = load()
+    _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale)
+    out, lse = _alloc_out(q, out, lse)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    need = int(lib.taco_paged_tree_attn_balanced_workspace_size(ctypes.byref(dims)))
+    if workspace is None:
+        if need == 0:
+            raise PtaError(4, "the balanced mode does not serve these dims")
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    else:
+        _need(workspace, "workspace", device=q.device)
+    _check(lib.taco_paged_tree_attn_balanced(
+        ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask), float(scale), _ptr(out),
+        _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
 def taco_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None,
                    stream=None):
     """Write new tokens' K/V rows into their paged cache slots (see include/pta.h)."""
@@ -303,3 +341,83 @@ def taco_pta_status_string(status: int) -> str:
 
 def taco_pta_version() -> int:
     return int(load().taco_pta_version())
+
+
+# ---------------------------------------------------------------- prepared calls
+class PreparedCall:
+    """A library call whose arguments were validated and marshalled once.
+
+    Calling it re-issues the same C call (same tensors, same stream) with no
+    per-call Python checks, for tight loops where the host must stay ahead of
+    the GPU.  The tensors passed to the preparing function must stay alive and
+    keep their storage for as long as the prepared call is used.
+    """
+
+    def __init__(self, fn, args, keep):
+        self._fn = fn
+        self._args = args
+        self._keep = keep           # references that keep the tensors alive
+
+    def __call__(self) -> None:
+        _check(self._fn(*self._args))
+
+
+def prepare_paged_tree_attn(mode, q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask,
+                            scale, out, lse=None, k_scale=None, v_scale=None, partition_tokens=None,
+                            workspace=None, max_ctx_len=None, path="auto", stream=None) -> PreparedCall:
+    """Validate once and return a PreparedCall for one of the attention entry points.
+
+    mode: "whole" (taco_paged_tree_attn), "split" (taco_paged_tree_attn_splitk with
+    partition_tokens) or "balanced" (taco_paged_tree_attn_balanced).  out (and, for
+    split/balanced, a zero-initialised workspace of sufficient size) must be given.
+    """
+    torch = _torch()
+    lib = load()
+    _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale)
+    out, lse = _alloc_out(q, out, lse)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    common = (ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+              _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask), float(scale),
+              _ptr(out), _ptr(lse))
+    keep = (dims, q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, out, lse, k_scale,
+            v_scale, workspace)
+    st = _stream(stream)
+    if mode == "whole":
+        return PreparedCall(lib.taco_paged_tree_attn, common + (st,), keep)
+    if workspace is None:
+        raise ValueError("prepared split/balanced calls need a caller-owned workspace")
+    _need(workspace, "workspace", device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    if mode == "split":
+        need = int(lib.taco_paged_tree_attn_splitk_workspace_size(ctypes.byref(dims), int(partition_tokens)))
+        if need == 0 or need > wbytes:
+            raise ValueError(f"split-K workspace must hold {need} bytes")
+        return PreparedCall(lib.taco_paged_tree_attn_splitk,
+                            common + (int(partition_tokens), _ptr(workspace), wbytes, st), keep)
+    if mode == "balanced":
+        need = int(lib.taco_paged_tree_attn_balanced_workspace_size(ctypes.byref(dims)))
+        if need == 0 or need > wbytes:
+            raise ValueError(f"balanced workspace must hold {need} bytes (0: dims not served)")
+        return PreparedCall(lib.taco_paged_tree_attn_balanced, common + (_ptr(workspace), wbytes, st), keep)
+    raise ValueError(f"unknown mode {mode!r}")
+
+
+def prepare_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None,
+                      stream=None) -> PreparedCall:
+    """Validate once and return a PreparedCall of taco_kv_append."""
+    torch = _torch()
+    lib = load()
+    _need(k_new, "k_new", 3)
+    dev = k_new.device
+    _need(v_new, "v_new", 3, k_new.dtype, dev)
+    _need(slot_mapping, "slot_mapping", 1, torch.int64, dev)
+    _need(k_cache, "k_cache", 4, device=dev)
+    _need(v_cache, "v_cache", 4, k_cache.dtype, dev)
+    N, Hkv, D = k_new.shape
+    dims = PtaDims(num_seqs=0, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=D, page_size=k_cache.shape[2],
+                   max_q_len=1, max_blocks_per_seq=1, max_ctx_len=1, num_blocks=k_cache.shape[0],
+                   q_dtype=PTA_BF16, kv_dtype=_kv_code(k_cache), path=0, reserved=0)
+    args = (ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _q_code(k_new), _ptr(slot_mapping), N,
+            _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _stream(stream))
+    return PreparedCall(lib.taco_kv_append, args,
+                        (dims, k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale))

@@ -146,6 +146,43 @@ bool split_layout(const pta_dims* d, int32_t T, SplitLayout* L) {
   return true;
 }
 
+// Balanced mode: [counters int32 B*Hkv | partial O float S*Mmax*D | partial LSE float S*Mmax]
+// with S = (workgroups + B*Hkv/nw) * nw partial slots and Mmax = G * max_q_len rows per slot;
+// nw = waves per workgroup = the head group (largest of 8, 4, 2, 1 dividing Hkv; at most 4
+// for two 16-row blocks).
+struct BalancedLayout {
+  int nwg, nw;
+  size_t o_off, lse_off, total;
+};
+
+int head_group(int hkv, int rb) {
+  for (int nw = rb == 1 ? 8 : 4; nw > 1; nw >>= 1)
+    if (hkv % nw == 0) return nw;
+  return 1;
+}
+
+constexpr int kBalancedMaxSeqs = 16383;   // sequence page prefix lives in LDS
+
+pta_status balanced_layout(const pta_dims* d, const Plan& p, BalancedLayout* L) {
+  if (p.fam != FAM_STREAM) return PTA_ERR_UNSUPPORTED;
+  if (d->num_seqs > kBalancedMaxSeqs) return PTA_ERR_UNSUPPORTED;
+  if ((int64_t)d->num_seqs * d->max_blocks_per_seq >= ((int64_t)1 << 31)) return PTA_ERR_UNSUPPORTED;
+  const int nw = head_group(d->num_kv_heads, p.rb);
+  int nwg = 0;
+  if (stream_balanced(nullptr, d->kv_dtype, d->head_dim, p.rb, nw, d->num_seqs, &nwg, nullptr) != hipSuccess)
+    return PTA_ERR_HIP;
+  const int64_t units = (int64_t)d->num_seqs * d->num_kv_heads;
+  const int64_t slots = (int64_t)nwg * nw + units;
+  const int64_t rows = slots * (d->num_q_heads / d->num_kv_heads) * d->max_q_len;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  L->nwg = nwg;
+  L->nw = nw;
+  L->o_off = up((size_t)units * sizeof(int32_t));
+  L->lse_off = L->o_off + up((size_t)rows * d->head_dim * sizeof(float));
+  L->total = L->lse_off + up((size_t)rows * sizeof(float));
+  return PTA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -210,6 +247,51 @@ pta_status taco_paged_tree_attn_splitk(const pta_dims* d, const void* q, const v
   a.part_tokens = partition_tokens;
   a.num_parts = (int32_t)L.parts;
   return run_attn(d, a, p, (hipStream_t)stream);
+}
+
+size_t taco_paged_tree_attn_balanced_workspace_size(const pta_dims* d) {
+  if (check_dims(d) != PTA_OK) return 0;
+  Plan p;
+  if (plan_for(d, &p) != PTA_OK) return 0;
+  BalancedLayout L;
+  if (balanced_layout(d, p, &L) != PTA_OK) return 0;
+  return L.total;
+}
+
+pta_status taco_paged_tree_attn_balanced(const pta_dims* d, const void* q, const void* k_cache,
+                                         const void* v_cache, const float* k_scale,
+                                         const float* v_scale, const int32_t* block_tables,
+                                         const int32_t* ctx_lens, const int32_t* q_lens,
+                                         const uint8_t* tree_mask, float scale, void* out, float* lse,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  pta_status st = check_dims(d);
+  if (st != PTA_OK) return st;
+  if (!isfinite(scale)) return PTA_ERR_BAD_DIMS;
+  Plan p;
+  st = plan_for(d, &p);
+  if (st != PTA_OK) return st;
+  if (p.fam != FAM_STREAM) return PTA_ERR_UNSUPPORTED;
+  if (d->num_seqs == 0) return PTA_OK;
+  st = check_attn_ptrs(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
+                       tree_mask, out);
+  if (st != PTA_OK) return st;
+  if (workspace == nullptr) return PTA_ERR_NULL_PTR;
+  BalancedLayout L;
+  st = balanced_layout(d, p, &L);
+  if (st != PTA_OK) return st;
+  if (workspace_bytes < L.total) return PTA_ERR_WORKSPACE_TOO_SMALL;
+  AttnArgs a = make_args(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
+                         tree_mask, scale, out, lse);
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.counters = reinterpret_cast<int32_t*>(ws);
+  a.part_o = reinterpret_cast<float*>(ws + L.o_off);
+  a.part_lse = reinterpret_cast<float*>(ws + L.lse_off);
+  a.total_waves = L.nwg * L.nw;
+  int nwg = L.nwg;
+  return stream_balanced(&a, d->kv_dtype, d->head_dim, p.rb, L.nw, d->num_seqs, &nwg, (hipStream_t)stream) ==
+                 hipSuccess
+             ? PTA_OK
+             : PTA_ERR_HIP;
 }
 
 pta_status taco_kv_append(const pta_dims* d, const void* k_new, const void* v_new,

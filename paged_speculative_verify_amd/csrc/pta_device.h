@@ -37,6 +37,7 @@ struct AttnArgs {
   float* part_o;           // split-K partial outputs [B][Hq][Qmax][P][D], or null (unsplit)
   float* part_lse;         // split-K partial LSE     [B][Hq][Qmax][P]
   int32_t* counters;       // split-K arrival counters [B][Hkv] (zero between calls)
+  int32_t total_waves;     // balanced mode: waves in the persistent grid
   float scale_log2;        // softmax scale * log2(e)
   int32_t B, Hq, Hkv, G, Qmax, MBS;
   int32_t part_tokens;     // partition length in tokens (split) or 0
@@ -142,38 +143,24 @@ __device__ __forceinline__ bool unit_writes_partials(const AttnArgs& a, int C) {
   return a.part_o != nullptr && C > a.part_tokens;
 }
 
-// Called by every thread of a split-K work unit (sequence b, KV head hkv) once
-// its normalised partial output and log-sum-exp are stored with
-// store_coherent.  The last unit of (b, hkv) to arrive merges the partitions
-// of all its rows:
+// Merge np partial results of the M rows of work unit (b, hkv) by
+// log-sum-exp and store the final rows (out in the q dtype, lse):
 //   LSE = ln sum_p exp(LSE_p),   out = sum_p exp(LSE_p - LSE) O_p
 // (the long-sequence design of the 618zxw.cn article, section
-// "長シーケンス推論最適化におけるTurboAttention": the sequence is cut into
-// parts processed independently and combined).  The merge reads partitions in
-// index order, so the result does not depend on which unit arrives last.  The
-// arrival counter is reset to zero for the next call.
-template <typename QT, int D>
-__device__ __forceinline__ void splitk_finish(const AttnArgs& a, int b, int hkv, int C, int qb) {
+// "長シーケンス推論最適化におけるTurboAttention": the sequence is processed in
+// parts that are combined).  slot(r, p) gives the partial output row (D
+// floats) and its log-sum-exp word for row r, part p; parts are read in index
+// order, so the result does not depend on which worker merges.  Executed by
+// nthr threads; each takes (row, 4 dims) items, with every load of a batch of
+// PB parts in flight at once and an online rescale across batches.
+template <typename QT, int D, typename SlotFn>
+__device__ __forceinline__ void merge_rows(const AttnArgs& a, int b, int hkv, int qb, int M, int np,
+                                           SlotFn slot, int tid, int nthr) {
   constexpr float NEG_INF = -__builtin_huge_valf();
-  __shared__ int s_last;
-  __builtin_amdgcn_s_waitcnt(0);            // this thread's partial stores have completed
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
-  const int np = (C + a.part_tokens - 1) / a.part_tokens;
-  int32_t* cnt = a.counters + (int64_t)b * a.Hkv + hkv;
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  const int M = a.G * qb;
   constexpr int Q4 = D / 4;
-  constexpr int PB = 8;                     // partitions fetched per round trip
-  for (int idx = threadIdx.x; idx < M * Q4; idx += blockDim.x) {
+  constexpr int PB = 8;
+  for (int idx = tid; idx < M * Q4; idx += nthr) {
     const int r = idx / Q4, d = (idx % Q4) * 4;
-    const int h = hkv * a.G + r / qb, i = r % qb;
-    const int64_t prow = (((int64_t)b * a.Hq + h) * a.Qmax + i) * a.num_parts;
-    // online log-sum-exp over the partitions, PB at a time with every load in flight
     float mrun = NEG_INF, wsum = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int p0 = 0; p0 < np; p0 += PB) {
@@ -182,10 +169,10 @@ __device__ __forceinline__ void splitk_finish(const AttnArgs& a, int b, int hkv,
 #pragma unroll
       for (int j = 0; j < PB; ++j) {
         const bool ok = p0 + j < np;
-        const int64_t pr = prow + (ok ? p0 + j : 0);
-        lp[j] = ok ? load_coherent(a.part_lse + pr) : NEG_INF;
+        const auto s = slot(r, ok ? p0 + j : 0);
+        lp[j] = ok ? load_coherent(s.lse) : NEG_INF;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) op[j][e] = ok ? load_coherent(a.part_o + pr * D + d + e) : 0.f;
+        for (int e = 0; e < 4; ++e) op[j][e] = ok ? load_coherent(s.o + d + e) : 0.f;
       }
       float mx = mrun;
 #pragma unroll
@@ -205,6 +192,7 @@ __device__ __forceinline__ void splitk_finish(const AttnArgs& a, int b, int hkv,
     const float muse = mrun == NEG_INF ? 0.f : mrun;
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     acc *= inv;
+    const int h = hkv * a.G + r / qb, i = r % qb;
     const int64_t o = (((int64_t)b * a.Qmax + i) * a.Hq + h) * D + d;
     if constexpr (QT::bytes == 4) {
       *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = acc;
@@ -217,6 +205,36 @@ __device__ __forceinline__ void splitk_finish(const AttnArgs& a, int b, int hkv,
     if (d == 0 && a.lse != nullptr)
       a.lse[((int64_t)b * a.Hq + h) * a.Qmax + i] = wsum > 0.f ? muse + __logf(wsum) : NEG_INF;
   }
+}
+
+struct PartSlot {
+  const float* o;     // D floats
+  const float* lse;   // one word
+};
+
+// Called by every thread of a split-K work unit (sequence b, KV head hkv) once
+// its normalised partial output and log-sum-exp are stored with
+// store_coherent.  The last unit of (b, hkv) to arrive merges the partitions
+// of all its rows and resets the arrival counter to zero for the next call.
+template <typename QT, int D>
+__device__ __forceinline__ void splitk_finish(const AttnArgs& a, int b, int hkv, int C, int qb) {
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);            // this thread's partial stores have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  const int np = (C + a.part_tokens - 1) / a.part_tokens;
+  int32_t* cnt = a.counters + (int64_t)b * a.Hkv + hkv;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  auto slot = [&](int r, int p) {
+    const int h = hkv * a.G + r / qb, i = r % qb;
+    const int64_t prow = (((int64_t)b * a.Hq + h) * a.Qmax + i) * a.num_parts + p;
+    return PartSlot{a.part_o + prow * D, a.part_lse + prow};
+  };
+  merge_rows<QT, D>(a, b, hkv, qb, a.G * qb, np, slot, threadIdx.x, blockDim.x);
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -3,19 +3,22 @@
 // sequence's decode GEMV into a small GEMM (TACO-LLM design talk
 // "大模型倍速推理引擎 TACO-LLM 的设计与实践", TurboAttention bullets of
 // "整体方案分为两大部分"); with so few rows the work is a pure HBM stream, and
-// the kernel is written so that almost nothing but the page loads costs time:
+// the kernels are written so that almost nothing but the page loads costs time:
 //
-//   * Work unit = (sequence, KV head, token partition).  Every query row of the
-//     unit (the GQA group's q-heads times the candidates) is handled by every
-//     wave, so each KV page tile crosses HBM once per group.  The NW waves of
-//     the workgroup take the unit's pages round-robin, each wave with its own
-//     flash-style softmax state (on-chip state independent of the context
-//     length, "优化策略总结" item 2); the waves are merged in LDS at the end.
-//   * No barrier in the main loop.  K is loaded from HBM straight into the
-//     A-operand layout of v_mfma_f32_16x16x32_bf16 (lane (g, m) holds 8
-//     consecutive dims of token m), so S^T = K Q^T needs no LDS.  V is copied
-//     into a per-wave LDS tile and read back with ds_read_b64_tr_b16, whose
-//     16-lane transpose yields exactly the A operand of O^T += V^T P^T
+//   * Every query row of a (sequence, KV head) unit -- the GQA group's q-heads
+//     times the candidates -- is handled by the same wave, so each KV page
+//     tile crosses HBM once per group.  Each wave keeps its own flash-style
+//     softmax state (on-chip state independent of the context length,
+//     "优化策略总结" item 2).
+//   * No barrier while streaming.  Every page load instruction reads 1 KiB
+//     contiguous (lane l: bytes 16 l + 1024 j of the page tile): loading K
+//     straight into the MFMA operand layout would make each instruction touch
+//     16 rows x 64 B, which measures ~20% below contiguous tiles on MI355X.
+//     K and V go into a per-wave LDS tile pair (fp8 decoded to bf16 on the
+//     way); K comes back with ds_read_b128 as the A operand of
+//     v_mfma_f32_16x16x32_bf16 (lane (g, m): 8 consecutive dims of token m) for
+//     S^T = K Q^T, and V with ds_read_b64_tr_b16, whose 16-lane transpose
+//     yields exactly the A operand of O^T += V^T P^T
 //     (v_mfma_f32_16x16x16_bf16); P^T is the S^T accumulator itself.
 //   * The next page's loads are issued before the current page is computed
 //     (two register sets, ping-pong), keeping one page per wave in flight.
@@ -27,6 +30,17 @@
 //     fast dequantisation inside attention, 618zxw.cn article section
 //     "LLM量子化技術による推論コストの削減"); the per-(page, KV head) scales
 //     are folded into the score multiplier and into P.
+//
+// Two kernels share this core:
+//   stream_attn_kernel      one workgroup per (unit, token partition); its
+//                           waves take the pages round-robin and are merged
+//                           in LDS (whole-context and split-K entry points).
+//   stream_balanced_kernel  persistent grid; the pages of all units are laid
+//                           end to end and every wave takes an equal
+//                           contiguous slice, so ragged context lengths cost
+//                           no load imbalance.  A slice that ends inside a
+//                           unit leaves a partial that the unit's last slice
+//                           merges.
 #include "pta_device.h"
 #include "pta_launch.h"
 
@@ -36,58 +50,325 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLazyTau = 8.0f;   // log2 headroom before a row's reference max moves
+constexpr int kMinSlicePages = 8;  // balanced mode: fewest pages per wave slice
 
 template <typename KT, int D>
 struct StreamTile {
   static constexpr int KK = D / 32;                           // 16x16x32 k-steps over the head dim
   static constexpr int DB = D / 16;                           // 16-dim blocks of O^T
-  static constexpr int K_LOADS = KK;                          // per lane per page
-  static constexpr int V_LOADS = (kPage * D * KT::bytes) / 1024;   // 16-byte loads per lane per page
-  static constexpr int VSTR = 2 * D + 32;                     // bytes per bf16 V row in LDS (bank skew)
-  static constexpr int V_BYTES = kPage * VSTR;                // per-wave V tile
+  static constexpr int LOADS = (kPage * D * KT::bytes) / 1024;     // 16-byte loads per lane per tile
+  static constexpr int STR = 2 * D + 32;                      // bytes per bf16 row in LDS (bank skew)
+  static constexpr int TILE_LDS = kPage * STR;                // one bf16 tile in LDS
+  static constexpr int WAVE_LDS = 2 * TILE_LDS;               // per-wave K tile + V tile
 };
 
-template <typename KT>
-struct KChunk;
-template <>
-struct KChunk<BF16> {
-  using raw = uint4;
-  static __device__ __forceinline__ raw load(const char* p) { return *reinterpret_cast<const uint4*>(p); }
-  static __device__ __forceinline__ bf16x8 op(const raw& r) { return __builtin_bit_cast(bf16x8, r); }
-};
-template <>
-struct KChunk<FP8> {
-  using raw = uint2;
-  static __device__ __forceinline__ raw load(const char* p) { return *reinterpret_cast<const uint2*>(p); }
-  static __device__ __forceinline__ bf16x8 op(const raw& r) {
-    uint4 o;
-    o.x = fp8x2_to_bf16x2<false>(r.x);
-    o.y = fp8x2_to_bf16x2<true>(r.x);
-    o.z = fp8x2_to_bf16x2<false>(r.y);
-    o.w = fp8x2_to_bf16x2<true>(r.y);
-    return __builtin_bit_cast(bf16x8, o);
-  }
-};
-
-// One page's operands in flight.
+// One page's K and V chunks in flight (lane l holds bytes 16 l + 1024 j).
 template <typename KT, int D>
 struct PageRegs {
-  typename KChunk<KT>::raw k[StreamTile<KT, D>::K_LOADS];
-  uint4 v[StreamTile<KT, D>::V_LOADS];
+  uint4 k[StreamTile<KT, D>::LOADS];
+  uint4 v[StreamTile<KT, D>::LOADS];
   float ks, vs;
 };
 
+// Write one page tile's chunks into a bf16 LDS tile (fp8 codes decoded
+// exactly); rows at or past `valid` are zeroed when `partial`.
+template <typename KT, int D>
+__device__ __forceinline__ void stage_tile(char* dst, const uint4 (&c)[StreamTile<KT, D>::LOADS], int lane,
+                                           bool partial, int valid) {
+  using T = StreamTile<KT, D>;
+  if constexpr (KT::bytes == 2) {
+#pragma unroll
+    for (int j = 0; j < T::LOADS; ++j) {
+      const int byte = 1024 * j + 16 * lane;
+      const int t = byte / (2 * D), col = byte % (2 * D);
+      uint4 w = c[j];
+      if (partial) {
+        if (t >= valid) w = make_uint4(0, 0, 0, 0);
+      }
+      *reinterpret_cast<uint4*>(dst + t * T::STR + col) = w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < T::LOADS; ++j) {
+      const int byte = 1024 * j + 16 * lane;
+      const int t = byte / D, d0 = byte % D;
+      const uint4 w = c[j];
+      uint4 lo, hi;
+      lo.x = fp8x2_to_bf16x2<false>(w.x); lo.y = fp8x2_to_bf16x2<true>(w.x);
+      lo.z = fp8x2_to_bf16x2<false>(w.y); lo.w = fp8x2_to_bf16x2<true>(w.y);
+      hi.x = fp8x2_to_bf16x2<false>(w.z); hi.y = fp8x2_to_bf16x2<true>(w.z);
+      hi.z = fp8x2_to_bf16x2<false>(w.w); hi.w = fp8x2_to_bf16x2<true>(w.w);
+      if (partial) {
+        if (t >= valid) { lo = make_uint4(0, 0, 0, 0); hi = lo; }
+      }
+      *reinterpret_cast<uint4*>(dst + t * T::STR + 2 * d0) = lo;
+      *reinterpret_cast<uint4*>(dst + t * T::STR + 2 * d0 + 16) = hi;
+    }
+  }
+}
+
+// The rows a lane owns (row = 16 rb + m of the unit): Q^T operands, candidate
+// mask bits and output coordinates.
+template <int D, int RB>
+struct StreamRows {
+  bf16x8 qop[RB][D / 32];
+  uint64_t mbits[RB];
+  bool ok[RB];
+  int h[RB], i[RB];
+};
+
+template <int D, int RB>
+__device__ __forceinline__ void load_rows(StreamRows<D, RB>& R, const AttnArgs& a, int b, int hkv, int qb,
+                                          int M, int g, int m) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = rb * 16 + m;
+    R.ok[rb] = row < M;
+    R.h[rb] = hkv * a.G + (R.ok[rb] ? row / qb : 0);
+    R.i[rb] = R.ok[rb] ? row % qb : 0;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         (((int64_t)b * a.Qmax + R.i[rb]) * a.Hq + R.h[rb]) * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const uint4 w = R.ok[rb] ? *reinterpret_cast<const uint4*>(qp + 32 * kk) : make_uint4(0, 0, 0, 0);
+      R.qop[rb][kk] = __builtin_bit_cast(bf16x8, w);
+    }
+    R.mbits[rb] = R.ok[rb] ? load_mask_row(a.mask, b, R.i[rb], qb, a.Qmax) : 0ull;
+  }
+}
+
+// Flash state of a lane's rows: O^T accumulators (dims 16 db + 4 g + r), the
+// reference maximum (log2 units) and the partial row sum of this lane's tokens.
+template <int D, int RB>
+struct StreamState {
+  f32x4 o[RB][D / 16];
+  float m[RB], l[RB];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      m[rb] = -__builtin_huge_valf();
+      l[rb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) o[rb][db] = {};
+    }
+  }
+};
+
+// Stream the pages pg = pg0 + k * stride (k < nk) of unit (b, hkv) through the
+// state.  Tokens at or past t1 (the end of the sequence or of the partition)
+// are masked, and their V rows zeroed, so unused page slots are never read for
+// their values.  vl: this wave's LDS tile pair.
+template <typename KT, int D, int RB>
+__device__ __forceinline__ void stream_pages(const AttnArgs& a, const StreamRows<D, RB>& rows,
+                                             StreamState<D, RB>& st, int b, int hkv, int L, int t1,
+                                             int pg0, int stride, int nk, char* vl, int lane) {
+  using T = StreamTile<KT, D>;
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  const int g = lane >> 4, m = lane & 15;
+  const int32_t* table = a.tables + (int64_t)b * a.MBS;
+  const char* kbase = reinterpret_cast<const char*>(a.k);
+  const char* vbase = reinterpret_cast<const char*>(a.v);
+  constexpr int64_t TILE_BYTES = (int64_t)kPage * D * KT::bytes;
+
+  // physical block of page k (wave-uniform: a scalar load)
+  auto phys_of = [&](int k) -> int { return table[pg0 + k * stride]; };
+
+  auto issue = [&](PageRegs<KT, D>& R, int phys32) {
+    const int64_t phys = phys32;
+    const int64_t tile = (phys * a.Hkv + hkv) * TILE_BYTES + 16 * lane;
+#pragma unroll
+    for (int j = 0; j < T::LOADS; ++j) R.k[j] = *reinterpret_cast<const uint4*>(kbase + tile + 1024 * j);
+#pragma unroll
+    for (int j = 0; j < T::LOADS; ++j) R.v[j] = *reinterpret_cast<const uint4*>(vbase + tile + 1024 * j);
+    if constexpr (KT::bytes == 1) {
+      R.ks = a.k_scale[phys * a.Hkv + hkv];
+      R.vs = a.v_scale[phys * a.Hkv + hkv];
+    } else {
+      R.ks = 1.f;
+      R.vs = 1.f;
+    }
+  };
+
+  char* kl = vl;                    // this wave's K tile, then its V tile
+  char* vt_l = vl + T::TILE_LDS;
+  auto consume = [&](const PageRegs<KT, D>& R, int k) {
+    const int pbase = (pg0 + k * stride) * kPage;
+    const bool partial = pbase + kPage > t1;
+
+    // 1. K and V tiles -> LDS as bf16 rows (V rows past t1 zeroed; K rows
+    //    past t1 are masked out of the scores)
+    stage_tile<KT, D>(kl, R.k, lane, false, kPage);
+    stage_tile<KT, D>(vt_l, R.v, lane, partial, t1 - pbase);
+
+    // 2. S^T[16 tokens][16 rows] = K Q^T per row block (A operand from LDS)
+    f32x4 sacc[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) sacc[rb] = {};
+    const char* krd = kl + m * T::STR + 16 * g;
+#pragma unroll
+    for (int kk = 0; kk < T::KK; ++kk) {
+      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(krd + 64 * kk);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, rows.qop[rb][kk], sacc[rb], 0, 0, 0);
+    }
+
+    // 3. scores in log2 units, mask by select; lazy reference-max update
+    const float c = a.scale_log2 * R.ks;
+    const bool plain = pbase + kPage <= min(L, t1);
+    float x[RB][4];
+    bool need = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float pm = NEG_INF;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = sacc[rb][r] * c;
+        if (!plain) {
+          const int t = pbase + 4 * g + r;
+          const int sh = t - L;
+          const bool cand = (unsigned)sh < 64u && ((rows.mbits[rb] >> (sh & 63)) & 1ull);
+          v = (t < t1 && (t < L || cand)) ? v : NEG_INF;
+        }
+        v = rows.ok[rb] ? v : NEG_INF;
+        x[rb][r] = v;
+        pm = fmaxf(pm, v);
+      }
+      need |= pm > st.m[rb] + kLazyTau;
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float pm = fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]));
+        pm = fmaxf(pm, shfl_xor(pm, 16));
+        pm = fmaxf(pm, shfl_xor(pm, 32));
+        const float mnew = fmaxf(st.m[rb], pm);
+        const float alpha = fast_exp2(st.m[rb] - (mnew == NEG_INF ? 0.f : mnew));
+        st.m[rb] = mnew;
+        st.l[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) st.o[rb][db] *= alpha;
+      }
+    }
+
+    // 4. P^T (bf16) straight from the S^T registers; O^T += V^T P^T
+    s16x4 pop[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float muse = st.m[rb] == NEG_INF ? 0.f : st.m[rb];
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = fast_exp2(x[rb][r] - muse);
+        st.l[rb] += p[r];
+      }
+      const uint32_t w0 = pack_bf16x2(p[0] * R.vs, p[1] * R.vs);
+      const uint32_t w1 = pack_bf16x2(p[2] * R.vs, p[3] * R.vs);
+      pop[rb] = __builtin_bit_cast(s16x4, make_uint2(w0, w1));
+    }
+    const char* vrd = vt_l + (4 * g + (m >> 2)) * T::STR + 8 * (m & 3);
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+      const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrd + 32 * db));
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        st.o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pop[rb], st.o[rb][db], 0, 0, 0);
+    }
+  };
+
+  // Two register sets, the next page always in flight.  The prefetch is
+  // issued unconditionally (the last one re-reads the final page, which is
+  // still in cache) so the compiler's load counters stay exact and the wait
+  // before each page covers only that page's own loads.  Block-table entries
+  // are read two pages ahead of their use.
+  if (nk <= 0) return;
+  PageRegs<KT, D> r0, r1;
+  int ph_a = phys_of(0), ph_b = phys_of(min(1, nk - 1));
+  issue(r0, ph_a);
+  for (int k = 0;; k += 2) {
+    ph_a = phys_of(min(k + 2, nk - 1));
+    issue(r1, ph_b);
+    consume(r0, k);
+    if (k + 1 >= nk) break;
+    ph_b = phys_of(min(k + 3, nk - 1));
+    issue(r0, ph_a);
+    consume(r1, k + 1);
+    if (k + 2 >= nk) break;
+  }
+}
+
+// Row sums over the lane's four 16-lane groups (every group holds 4 of each
+// page's 16 tokens).
+template <int D, int RB>
+__device__ __forceinline__ void reduce_row_sums(StreamState<D, RB>& st) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    st.l[rb] += shfl_xor(st.l[rb], 16);
+    st.l[rb] += shfl_xor(st.l[rb], 32);
+  }
+}
+
+// Final rows of a lane: out = O / l (bf16), lse = ln l + max.
+template <int D, int RB>
+__device__ __forceinline__ void store_final_rows(const AttnArgs& a, const StreamRows<D, RB>& rows,
+                                                 const StreamState<D, RB>& st, int b, int g) {
+  constexpr float NEG_INF = -__builtin_huge_valf();
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    if (!rows.ok[rb]) continue;
+    const float lt = st.l[rb];
+    const float muse = st.m[rb] == NEG_INF ? 0.f : st.m[rb];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse = lt > 0.f ? (muse + fast_log2(lt)) * kLn2 : NEG_INF;
+    const int h = rows.h[rb], i = rows.i[rb];
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (((int64_t)b * a.Qmax + i) * a.Hq + h) * D + 4 * g;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      uint2 w;
+      w.x = pack_bf16x2(st.o[rb][db][0] * inv, st.o[rb][db][1] * inv);
+      w.y = pack_bf16x2(st.o[rb][db][2] * inv, st.o[rb][db][3] * inv);
+      *reinterpret_cast<uint2*>(op + 16 * db) = w;
+    }
+    if (g == 0 && a.lse != nullptr) a.lse[((int64_t)b * a.Hq + h) * a.Qmax + i] = lse;
+  }
+}
+
+// Partial rows of a lane (normalised O and natural-log LSE), stored with
+// device-coherent word stores.  row_addr(rb, o, l) gives the row's O words and
+// LSE word.
+template <int D, int RB, typename AddrFn>
+__device__ __forceinline__ void store_partial_rows(const StreamRows<D, RB>& rows,
+                                                   const StreamState<D, RB>& st, int g, AddrFn row_addr) {
+  constexpr float NEG_INF = -__builtin_huge_valf();
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    if (!rows.ok[rb]) continue;
+    const float lt = st.l[rb];
+    const float muse = st.m[rb] == NEG_INF ? 0.f : st.m[rb];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse = lt > 0.f ? (muse + fast_log2(lt)) * kLn2 : NEG_INF;
+    float* o;
+    float* l;
+    row_addr(rb, o, l);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_coherent(o + 16 * db + 4 * g + e, st.o[rb][db][e] * inv);
+    if (g == 0) store_coherent(l, lse);
+  }
+}
+
+// ============================================================ per-unit kernel
 template <typename KT, int D, int RB, int NW>
 __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(AttnArgs a) {
   using T = StreamTile<KT, D>;
-  using KC = KChunk<KT>;
   constexpr float NEG_INF = -__builtin_huge_valf();
   constexpr int ROWS = 16 * RB;
 
-  __shared__ __attribute__((aligned(16))) char vlds[NW][T::V_BYTES];
+  __shared__ __attribute__((aligned(16))) char vlds[NW][T::WAVE_LDS];
   __shared__ float red_m[NW][ROWS];
   __shared__ float red_l[NW][ROWS];
-  static_assert(NW == 1 || RB * T::DB * 64 * 16 <= NW * T::V_BYTES, "merge buffer must fit the V tiles");
+  static_assert(NW == 1 || RB * T::DB * 64 * 16 <= NW * T::WAVE_LDS, "merge buffer must fit the tiles");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -107,214 +388,25 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(AttnArgs a) {
   }
   const bool split_out = unit_writes_partials(a, C);   // else: final output written directly
 
-  // ---- rows of this lane (row = 16 rb + m) and their Q^T operands
-  bf16x8 qop[RB][T::KK];
-  uint64_t mbits[RB];
-  bool row_ok[RB];
-  int row_h[RB], row_i[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = rb * 16 + m;
-    row_ok[rb] = row < M;
-    row_h[rb] = hkv * a.G + (row_ok[rb] ? row / qb : 0);
-    row_i[rb] = row_ok[rb] ? row % qb : 0;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                         (((int64_t)b * a.Qmax + row_i[rb]) * a.Hq + row_h[rb]) * D + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < T::KK; ++kk) {
-      const uint4 w = row_ok[rb] ? *reinterpret_cast<const uint4*>(qp + 32 * kk) : make_uint4(0, 0, 0, 0);
-      qop[rb][kk] = __builtin_bit_cast(bf16x8, w);
-    }
-    mbits[rb] = row_ok[rb] ? load_mask_row(a.mask, b, row_i[rb], qb, a.Qmax) : 0ull;
-  }
+  StreamRows<D, RB> rows;
+  load_rows(rows, a, b, hkv, qb, M, g, m);
+  StreamState<D, RB> st;
+  st.init();
 
-  // ---- this wave's pages: pg = pgA + wave + k * NW, k < nk
+  // this wave's pages: pg = pgA + wave + k * NW, k < nk
   const int pgA = t0 / kPage;
   const int npg = (t1 + kPage - 1) / kPage - pgA;
   const int nk = npg > wave ? (npg - wave + NW - 1) / NW : 0;
-  const int32_t* table = a.tables + (int64_t)b * a.MBS;
-  const char* kbase = reinterpret_cast<const char*>(a.k);
-  const char* vbase = reinterpret_cast<const char*>(a.v);
-  constexpr int64_t TILE_BYTES = (int64_t)kPage * D * KT::bytes;
-  constexpr int ROW_BYTES = D * KT::bytes;
-
-  // physical block of this wave's page k (wave-uniform: a scalar load)
-  auto phys_of = [&](int k) -> int { return table[pgA + wave + k * NW]; };
-
-  auto issue = [&](PageRegs<KT, D>& R, int phys32) {
-    const int64_t phys = phys32;
-    const int64_t tile = (phys * a.Hkv + hkv) * TILE_BYTES;
-    const char* kp = kbase + tile + m * ROW_BYTES + 8 * g * KT::bytes;
-#pragma unroll
-    for (int kk = 0; kk < T::K_LOADS; ++kk) R.k[kk] = KC::load(kp + 32 * kk * KT::bytes);
-    const char* vp = vbase + tile + 16 * lane;
-#pragma unroll
-    for (int j = 0; j < T::V_LOADS; ++j) R.v[j] = *reinterpret_cast<const uint4*>(vp + 1024 * j);
-    if constexpr (KT::bytes == 1) {
-      R.ks = a.k_scale[phys * a.Hkv + hkv];
-      R.vs = a.v_scale[phys * a.Hkv + hkv];
-    } else {
-      R.ks = 1.f;
-      R.vs = 1.f;
-    }
-  };
-
-  f32x4 oacc[RB][T::DB];
-  float m_run[RB], l_run[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = NEG_INF;
-    l_run[rb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < T::DB; ++db) oacc[rb][db] = {};
-  }
-  char* vl = vlds[wave];
-
-  auto consume = [&](const PageRegs<KT, D>& R, int k) {
-    const int pg = pgA + wave + k * NW;
-    const int pbase = pg * kPage;
-    const bool partial = pbase + kPage > t1;
-
-    // 1. V tile -> LDS as bf16 rows (tail slots past the context are zeroed)
-    if constexpr (KT::bytes == 2) {
-#pragma unroll
-      for (int j = 0; j < T::V_LOADS; ++j) {
-        const int byte = 1024 * j + 16 * lane;
-        const int t = byte / (2 * D), col = byte % (2 * D);
-        uint4 w = R.v[j];
-        if (partial) {
-          if (pbase + t >= t1) w = make_uint4(0, 0, 0, 0);
-        }
-        *reinterpret_cast<uint4*>(vl + t * T::VSTR + col) = w;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < T::V_LOADS; ++j) {
-        const int byte = 1024 * j + 16 * lane;
-        const int t = byte / D, d0 = byte % D;
-        const uint4 c = R.v[j];
-        uint4 lo, hi;
-        lo.x = fp8x2_to_bf16x2<false>(c.x); lo.y = fp8x2_to_bf16x2<true>(c.x);
-        lo.z = fp8x2_to_bf16x2<false>(c.y); lo.w = fp8x2_to_bf16x2<true>(c.y);
-        hi.x = fp8x2_to_bf16x2<false>(c.z); hi.y = fp8x2_to_bf16x2<true>(c.z);
-        hi.z = fp8x2_to_bf16x2<false>(c.w); hi.w = fp8x2_to_bf16x2<true>(c.w);
-        if (partial) {
-          if (pbase + t >= t1) { lo = make_uint4(0, 0, 0, 0); hi = lo; }
-        }
-        *reinterpret_cast<uint4*>(vl + t * T::VSTR + 2 * d0) = lo;
-        *reinterpret_cast<uint4*>(vl + t * T::VSTR + 2 * d0 + 16) = hi;
-      }
-    }
-
-    // 2. S^T[16 tokens][16 rows] = K Q^T per row block
-    f32x4 sacc[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) sacc[rb] = {};
-#pragma unroll
-    for (int kk = 0; kk < T::KK; ++kk) {
-      const bf16x8 kop = KC::op(R.k[kk]);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[rb][kk], sacc[rb], 0, 0, 0);
-    }
-
-    // 3. scores in log2 units, mask by select; lazy reference-max update
-    const float c = a.scale_log2 * R.ks;
-    const bool plain = pbase + kPage <= min(L, t1);
-    float x[RB][4];
-    bool need = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float pm = NEG_INF;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = sacc[rb][r] * c;
-        if (!plain) {
-          const int t = pbase + 4 * g + r;
-          const int sh = t - L;
-          const bool cand = (unsigned)sh < 64u && ((mbits[rb] >> (sh & 63)) & 1ull);
-          v = (t < t1 && (t < L || cand)) ? v : NEG_INF;
-        }
-        v = row_ok[rb] ? v : NEG_INF;
-        x[rb][r] = v;
-        pm = fmaxf(pm, v);
-      }
-      need |= pm > m_run[rb] + kLazyTau;
-    }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        float pm = fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]));
-        pm = fmaxf(pm, shfl_xor(pm, 16));
-        pm = fmaxf(pm, shfl_xor(pm, 32));
-        const float mnew = fmaxf(m_run[rb], pm);
-        const float alpha = fast_exp2(m_run[rb] - (mnew == NEG_INF ? 0.f : mnew));
-        m_run[rb] = mnew;
-        l_run[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < T::DB; ++db) oacc[rb][db] *= alpha;
-      }
-    }
-
-    // 4. P^T (bf16) straight from the S^T registers; O^T += V^T P^T
-    s16x4 pop[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float muse = m_run[rb] == NEG_INF ? 0.f : m_run[rb];
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = fast_exp2(x[rb][r] - muse);
-        l_run[rb] += p[r];
-      }
-      const uint32_t w0 = pack_bf16x2(p[0] * R.vs, p[1] * R.vs);
-      const uint32_t w1 = pack_bf16x2(p[2] * R.vs, p[3] * R.vs);
-      pop[rb] = __builtin_bit_cast(s16x4, make_uint2(w0, w1));
-    }
-    const char* vrd = vl + (4 * g + (m >> 2)) * T::VSTR + 8 * (m & 3);
-#pragma unroll
-    for (int db = 0; db < T::DB; ++db) {
-      const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrd + 32 * db));
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        oacc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pop[rb], oacc[rb][db], 0, 0, 0);
-    }
-  };
-
-  // ---- main loop: two register sets, the next page always in flight.  The
-  // prefetch is issued unconditionally (the last one re-reads the final page,
-  // which is still in cache) so the compiler's load counters stay exact and
-  // the wait before each page covers only that page's own loads.
-  PageRegs<KT, D> r0, r1;
-  if (nk > 0) {
-    // block-table entries are read two pages ahead of their use
-    int ph_a = phys_of(0), ph_b = phys_of(min(1, nk - 1));
-    issue(r0, ph_a);
-    for (int k = 0;; k += 2) {
-      ph_a = phys_of(min(k + 2, nk - 1));
-      issue(r1, ph_b);
-      consume(r0, k);
-      if (k + 1 >= nk) break;
-      ph_b = phys_of(min(k + 3, nk - 1));
-      issue(r0, ph_a);
-      consume(r1, k + 1);
-      if (k + 2 >= nk) break;
-    }
-  }
+  stream_pages<KT, D, RB>(a, rows, st, b, hkv, L, t1, pgA + wave, NW, nk, vlds[wave], lane);
+  reduce_row_sums(st);
 
   // ---- merge the waves: row max, row sum, then O^T accumulated in LDS in wave order
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    l_run[rb] += shfl_xor(l_run[rb], 16);
-    l_run[rb] += shfl_xor(l_run[rb], 32);
-  }
-  float Ltot[RB], Muse[RB];
   if constexpr (NW > 1) {
     if (g == 0) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        red_m[wave][rb * 16 + m] = m_run[rb];
-        red_l[wave][rb * 16 + m] = l_run[rb];
+        red_m[wave][rb * 16 + m] = st.m[rb];
+        red_l[wave][rb * 16 + m] = st.l[rb];
       }
     }
     __syncthreads();
@@ -323,16 +415,17 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(AttnArgs a) {
       float mx = NEG_INF;
 #pragma unroll
       for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red_m[w][rb * 16 + m]);
-      Muse[rb] = mx == NEG_INF ? 0.f : mx;
+      const float muse = mx == NEG_INF ? 0.f : mx;
       float lt = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) lt += red_l[w][rb * 16 + m] * fast_exp2(red_m[w][rb * 16 + m] - Muse[rb]);
-      Ltot[rb] = lt;
-      const float f = fast_exp2(m_run[rb] - Muse[rb]);
+      for (int w = 0; w < NW; ++w) lt += red_l[w][rb * 16 + m] * fast_exp2(red_m[w][rb * 16 + m] - muse);
+      const float f = fast_exp2(st.m[rb] - muse);
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db) oacc[rb][db] *= f;
+      for (int db = 0; db < T::DB; ++db) st.o[rb][db] *= f;
+      st.m[rb] = mx;
+      st.l[rb] = lt;
     }
-    f32x4* ob = reinterpret_cast<f32x4*>(&vlds[0][0]);   // V tiles are dead after the barrier
+    f32x4* ob = reinterpret_cast<f32x4*>(&vlds[0][0]);   // page tiles are dead after the barrier
     for (int w = 0; w < NW; ++w) {
       if (wave == w) {
 #pragma unroll
@@ -340,49 +433,160 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int db = 0; db < T::DB; ++db) {
             f32x4& slot = ob[(rb * T::DB + db) * 64 + lane];
-            if (w > 0) oacc[rb][db] += slot;
-            if (w < NW - 1) slot = oacc[rb][db];
+            if (w > 0) st.o[rb][db] += slot;
+            if (w < NW - 1) slot = st.o[rb][db];
           }
       }
       if (w < NW - 1) __syncthreads();
     }
-  } else {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      Muse[rb] = m_run[rb] == NEG_INF ? 0.f : m_run[rb];
-      Ltot[rb] = l_run[rb];
-    }
   }
 
-  // ---- epilogue (last wave): row 16 rb + m, dims 16 db + 4 g + r
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    if (wave != NW - 1 || !row_ok[rb]) continue;
-    const float lt = Ltot[rb];
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse = lt > 0.f ? (Muse[rb] + fast_log2(lt)) * kLn2 : NEG_INF;
-    const int h = row_h[rb], i = row_i[rb];
+  // ---- epilogue (last wave holds the merged rows)
+  if (wave == NW - 1) {
     if (split_out) {
-      const int64_t prow = (((int64_t)b * a.Hq + h) * a.Qmax + i) * a.num_parts + part;
-      float* op = a.part_o + prow * D + 4 * g;
-#pragma unroll
-      for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) store_coherent(op + 16 * db + e, oacc[rb][db][e] * inv);
-      if (g == 0) store_coherent(a.part_lse + prow, lse);
+      auto addr = [&](int rb, float*& o, float*& l) {
+        const int64_t prow =
+            (((int64_t)b * a.Hq + rows.h[rb]) * a.Qmax + rows.i[rb]) * a.num_parts + part;
+        o = a.part_o + prow * D;
+        l = a.part_lse + prow;
+      };
+      store_partial_rows(rows, st, g, addr);
     } else {
-      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (((int64_t)b * a.Qmax + i) * a.Hq + h) * D + 4 * g;
-#pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        uint2 w;
-        w.x = pack_bf16x2(oacc[rb][db][0] * inv, oacc[rb][db][1] * inv);
-        w.y = pack_bf16x2(oacc[rb][db][2] * inv, oacc[rb][db][3] * inv);
-        *reinterpret_cast<uint2*>(op + 16 * db) = w;
-      }
-      if (g == 0 && a.lse != nullptr) a.lse[((int64_t)b * a.Hq + h) * a.Qmax + i] = lse;
+      store_final_rows(a, rows, st, b, g);
     }
   }
   if (split_out) splitk_finish<BF16, D>(a, b, hkv, C, qb);
+}
+
+// ============================================================ balanced kernel
+// A workgroup has one wave per KV head of a head group (NW adjacent heads),
+// and its waves always stream the same pages: a physical block keeps the tiles
+// of adjacent KV heads next to each other ([block][head][16][D]), so the
+// workgroup reads NW * 4 KiB (bf16) contiguous per page of K and of V, which
+// HBM serves much better than isolated 4 KiB tiles.
+//
+// Global page line: unit u' = b * HG + hg (HG = Hkv / NW head groups) owns
+// positions [S, S + P_b) with P_b = ceil(C_b / 16) and S = HG * PS_b + hg * P_b
+// (PS = exclusive prefix of P over sequences).  With W positions in all and N
+// working workgroups, workgroup w owns [w W / N, (w + 1) W / N); the one owning
+// position x is ((x + 1) N - 1) / W.  N <= W, so every working workgroup owns
+// a position and the slices touching u' are exactly workgroups wg_of(S) ..
+// wg_of(S + P_b - 1).  The partial of (workgroup w, unit u', wave h) lives in
+// slot (w + u') * NW + h, unique because workgroups and units are both
+// ordered along the line.  Slices hold at least kMinSlicePages pages.
+// Dynamic LDS: PS[0..B] (int32).
+template <typename KT, int D, int RB, int NW>
+__global__ __launch_bounds__(NW * 64) void stream_balanced_kernel(AttnArgs a) {
+  using T = StreamTile<KT, D>;
+  __shared__ __attribute__((aligned(16))) char vlds[NW][T::WAVE_LDS];
+  __shared__ int scan_tmp[NW * 64];
+  extern __shared__ int ps[];       // [B + 1]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, m = lane & 15;
+  const int B = a.B;
+  const int HG = a.Hkv / NW;
+
+  // ---- exclusive prefix of pages per sequence (every workgroup computes it)
+  {
+    constexpr int NT = NW * 64;
+    const int chunk = (B + NT - 1) / NT;
+    const int lo = min(B, tid * chunk), hi = min(B, lo + chunk);
+    int s = 0;
+    for (int bb = lo; bb < hi; ++bb) s += (a.ctx[bb] + kPage - 1) / kPage;
+    scan_tmp[tid] = s;
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int t = 0; t < NT; ++t) {
+        const int v = scan_tmp[t];
+        scan_tmp[t] = run;
+        run += v;
+      }
+      ps[B] = run;
+    }
+    __syncthreads();
+    int base = scan_tmp[tid];
+    for (int bb = lo; bb < hi; ++bb) {
+      ps[bb] = base;
+      base += (a.ctx[bb] + kPage - 1) / kPage;
+    }
+    __syncthreads();
+  }
+  const int64_t W = (int64_t)HG * __builtin_amdgcn_readfirstlane(ps[B]);
+  const int64_t N = min((int64_t)gridDim.x, max((int64_t)1, W / kMinSlicePages));
+  const int64_t w = blockIdx.x;
+  if (w >= N) return;
+  const int Mmax = a.G * a.Qmax;
+  auto wg_of = [&](int64_t x) -> int64_t { return ((x + 1) * N - 1) / W; };
+
+  int64_t x = w * W / N;
+  const int64_t xe = (w + 1) * W / N;
+  while (x < xe) {
+    // locate the unit holding position x: largest b with PS_b <= x / HG
+    const int key = (int)(x / HG);
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (__builtin_amdgcn_readfirstlane(ps[mid]) <= key) lo = mid;
+      else hi = mid - 1;
+    }
+    const int b = lo;
+    const int psb = __builtin_amdgcn_readfirstlane(ps[b]);
+    const int Pb = __builtin_amdgcn_readfirstlane(ps[b + 1]) - psb;
+    const int64_t off = x - (int64_t)HG * psb;
+    const int hg = (int)(off / Pb);
+    const int k0 = (int)(off % Pb);
+    const int k1 = (int)min((int64_t)Pb, k0 + (xe - x));
+    const int ug = b * HG + hg;             // unit of the head group
+    const int hkv = hg * NW + wave;
+    const int u = b * a.Hkv + hkv;          // (sequence, KV head) of this wave
+
+    const int C = a.ctx[b];
+    const int qb = a.qlen[b];
+    const int L = C - qb;
+    const int M = a.G * qb;
+    StreamRows<D, RB> rows;
+    load_rows(rows, a, b, hkv, qb, M, g, m);
+    StreamState<D, RB> st;
+    st.init();
+    stream_pages<KT, D, RB>(a, rows, st, b, hkv, L, C, k0, 1, k1 - k0, vlds[wave], lane);
+    reduce_row_sums(st);
+
+    if (k0 == 0 && k1 == Pb) {
+      store_final_rows(a, rows, st, b, g);        // the whole unit in this slice
+    } else {
+      const int64_t S = (int64_t)HG * psb + (int64_t)hg * Pb;
+      const int64_t wfirst = wg_of(S), wlast = wg_of(S + Pb - 1);
+      const int np = (int)(wlast - wfirst + 1);
+      const int64_t slot0 = (wfirst + ug) * NW + wave;
+      const int64_t slot = (w + ug) * NW + wave;
+      auto addr = [&](int rb, float*& o, float*& l) {
+        const int64_t r = slot * Mmax + rb * 16 + m;
+        o = a.part_o + r * D;
+        l = a.part_lse + r;
+      };
+      store_partial_rows(rows, st, g, addr);
+      __builtin_amdgcn_s_waitcnt(0);             // partial stores complete before the arrival
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      int32_t* cnt = a.counters + u;
+      int last = 0;
+      if (lane == 0) last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
+      last = __builtin_amdgcn_readfirstlane(last);
+      if (last) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        auto pslot = [&](int r, int p) {
+          const int64_t rr = (slot0 + (int64_t)p * NW) * Mmax + r;
+          return PartSlot{a.part_o + rr * D, a.part_lse + rr};
+        };
+        merge_rows<BF16, D>(a, b, hkv, qb, M, np, pslot, lane, 64);
+        if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    x += k1 - k0;
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -396,10 +600,6 @@ template <typename KT, int D>
 static hipError_t launch_stream_d(const AttnArgs& a, int rb, int nw, dim3 grid, hipStream_t s) {
   if (rb == 1 && nw == 4) return launch_stream_t<KT, D, 1, 4>(a, grid, s);
   if (rb == 2 && nw == 4) return launch_stream_t<KT, D, 2, 4>(a, grid, s);
-  if (rb == 1 && nw == 8) return launch_stream_t<KT, D, 1, 8>(a, grid, s);
-  if (rb == 2 && nw == 8) return launch_stream_t<KT, D, 2, 8>(a, grid, s);
-  if (rb == 1 && nw == 1) return launch_stream_t<KT, D, 1, 1>(a, grid, s);
-  if (rb == 2 && nw == 1) return launch_stream_t<KT, D, 2, 1>(a, grid, s);
   return hipErrorInvalidValue;
 }
 
@@ -411,6 +611,60 @@ hipError_t launch_stream(const AttnArgs& a, int kv_dtype, int D, int rb, int nw,
   } else if (kv_dtype == 2) {
     if (D == 64) return launch_stream_d<FP8, 64>(a, rb, nw, grid, s);
     if (D == 128) return launch_stream_d<FP8, 128>(a, rb, nw, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Balanced kernel.  With a == nullptr: report the persistent grid size
+// (workgroups) for the current device, from its compute-unit count and the
+// kernel's occupancy.  Otherwise launch *nwg workgroups.
+template <typename KT, int D, int RB, int NW>
+static hipError_t balanced_t(const AttnArgs* a, int B, int* nwg, hipStream_t s) {
+  const size_t dyn = (size_t)(B + 1) * sizeof(int);
+  if (a == nullptr) {
+    int dev = 0, cus = 0, per = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, stream_balanced_kernel<KT, D, RB, NW>, NW * 64, dyn);
+    if (e != hipSuccess) return e;
+    *nwg = cus * (per > 0 ? per : 1);
+    return hipSuccess;
+  }
+  hipLaunchKernelGGL((stream_balanced_kernel<KT, D, RB, NW>), dim3((unsigned)*nwg), dim3(NW * 64), dyn, s, *a);
+  return hipGetLastError();
+}
+
+// Head groups of 8 waves only for 16-row blocks: with two row blocks a wave
+// needs more than the 256 VGPRs an 8-wave workgroup may use per wave.
+template <typename KT, int D, int RB>
+static hipError_t balanced_r(const AttnArgs* a, int nw, int B, int* nwg, hipStream_t s) {
+  switch (nw) {
+    case 1: return balanced_t<KT, D, RB, 1>(a, B, nwg, s);
+    case 2: return balanced_t<KT, D, RB, 2>(a, B, nwg, s);
+    case 4: return balanced_t<KT, D, RB, 4>(a, B, nwg, s);
+    case 8:
+      if constexpr (RB == 1) return balanced_t<KT, D, RB, 8>(a, B, nwg, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename KT, int D>
+static hipError_t balanced_d(const AttnArgs* a, int rb, int nw, int B, int* nwg, hipStream_t s) {
+  if (rb == 1) return balanced_r<KT, D, 1>(a, nw, B, nwg, s);
+  if (rb == 2) return balanced_r<KT, D, 2>(a, nw, B, nwg, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t stream_balanced(const AttnArgs* a, int kv_dtype, int D, int rb, int nw, int B, int* nwg,
+                           hipStream_t s) {
+  if (kv_dtype == 1) {
+    if (D == 64) return balanced_d<BF16, 64>(a, rb, nw, B, nwg, s);
+    if (D == 128) return balanced_d<BF16, 128>(a, rb, nw, B, nwg, s);
+  } else if (kv_dtype == 2) {
+    if (D == 64) return balanced_d<FP8, 64>(a, rb, nw, B, nwg, s);
+    if (D == 128) return balanced_d<FP8, 128>(a, rb, nw, B, nwg, s);
   }
   return hipErrorInvalidValue;
 }

@@ -43,13 +43,21 @@ def tol_key(spec):
     return "fp8" if spec.kv_dtype == "fp8" else spec.q_dtype
 
 
-def run_gpu(torch, w, split=None, path="auto", want_lse=True):
+def run_gpu(torch, w, split=None, path="auto", want_lse=True, mode=None, workspace=None):
+    """mode: "whole", "split" (split-K with `split` tokens) or "balanced"; by default
+    "split" when split is given, else "whole"."""
     import paged_speculative_verify_amd as psv
     d = to_device(w)
     out = torch.full_like(d.q, float("nan"))
     B, Qmax, Hq, D = w.q.shape
     lse = torch.full((B, Hq, Qmax), float("nan"), dtype=torch.float32, device=d.q.device) if want_lse else None
-    if split is None:
+    mode = mode or ("whole" if split is None else "split")
+    if mode == "balanced":
+        psv.taco_paged_tree_attn_balanced(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
+                                          d.q_lens, d.tree_mask, d.scale, out=out, lse=lse,
+                                          k_scale=d.k_scale, v_scale=d.v_scale, workspace=workspace,
+                                          max_ctx_len=d.max_ctx_len, path=path)
+    elif mode == "whole":
         psv.taco_paged_tree_attn(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
                                  d.tree_mask, d.scale, out=out, lse=lse, k_scale=d.k_scale,
                                  v_scale=d.v_scale, max_ctx_len=d.max_ctx_len, path=path)
@@ -317,8 +325,8 @@ def test_full_size_sampled(torch_cuda, name, seqs):
     import bench
     w = make(name)
     cfg = bench.launch_config(name)
-    say("full", name, "split", cfg["split"], "path", cfg["path"], "sampled seqs", seqs)
-    out, lse = run_gpu(torch_cuda, w, split=cfg["split"], path=cfg["path"])
+    say("full", name, "entry", cfg["mode"], "split", cfg["split"], "path", cfg["path"], "sampled seqs", seqs)
+    out, lse = run_gpu(torch_cuda, w, split=cfg["split"], path=cfg["path"], mode=cfg["mode"])
     ref, ref_lse = run_oracle(w, rows=np.array(seqs))
     err = assert_parity(w, out, lse, ref, ref_lse, seqs=np.array(seqs))
     say("full", name, "max abs err", err)
@@ -360,3 +368,63 @@ def test_splitk_workspace_reused_across_calls(torch_cuda):
         assert_parity(w, out_to_f64(out), lse.cpu().numpy().astype(np.float64), ref, ref_lse)
         counters = ws[:B * w.k_cache.shape[1] * 4].view(torch.int32)
         assert int(counters.abs().sum()) == 0, "arrival counters not reset"
+
+
+# -------------------------------------------------------------- work-balanced entry point
+BALANCED = [
+    ("bal_decode_bf16", spec("b", 9, 32, 8, 128, "bf16", "bf16", (1, 2500), 1, "chain", seed=101)),
+    ("bal_decode_long_ragged", spec("b", 5, 32, 8, 128, "bf16", "bf16", (1, 9000), 1, "chain", seed=102)),
+    ("bal_tree_g2", spec("b", 7, 16, 8, 128, "bf16", "bf16", (5, 1500), 8, "random", 4, True, seed=103)),
+    ("bal_fp8_chain8", spec("b", 6, 32, 8, 128, "bf16", "fp8", (8, 3000), 8, "chain", seed=104)),
+    ("bal_d64", spec("b", 6, 16, 4, 64, "bf16", "bf16", (2, 2000), 4, "random", ragged=True, seed=105)),
+    ("bal_fp8_d64", spec("b", 4, 8, 2, 64, "bf16", "fp8", (3, 1200), 6, "random", seed=106)),
+    ("bal_tiny_units", spec("b", 40, 8, 2, 128, "bf16", "bf16", (1, 20), 1, "chain", seed=107)),
+    ("bal_one_seq", spec("b", 1, 8, 1, 128, "bf16", "bf16", (30000, 30000), 2, "chain", seed=108)),
+]
+
+
+@pytest.mark.parametrize("cid,sp", BALANCED, ids=[c[0] for c in BALANCED])
+def test_balanced_parity(torch_cuda, cid, sp):
+    w = make(sp, poison=True)
+    say(cid, "B", w.q.shape[0], "ctx", w.ctx_lens.tolist()[:8], "q", sp.q_len, sp.kv_dtype)
+    out, lse = run_gpu(torch_cuda, w, mode="balanced")
+    ref, ref_lse = run_oracle(w)
+    err = assert_parity(w, out, lse, ref, ref_lse)
+    say(cid, "max abs err", err)
+
+
+def test_balanced_repeat_and_workspace_reuse(torch_cuda):
+    """The same zero-filled workspace serves repeated calls (the merging slices reset their
+    counters); results are bit-identical from call to call and unchanged by a relabelling
+    of physical pages."""
+    import torch
+    import paged_speculative_verify_amd as psv
+    w = make(spec("r", 8, 32, 8, 128, "bf16", "bf16", (100, 6000), 1, "chain", seed=111))
+    d = to_device(w)
+    need = psv.taco_paged_tree_attn_balanced_workspace_size(d.q, d.k_cache, d.block_tables,
+                                                            max_ctx_len=d.max_ctx_len)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    say("balanced repeat, workspace", need)
+    a1, l1 = run_gpu(torch_cuda, w, mode="balanced", workspace=ws)
+    a2, l2 = run_gpu(torch_cuda, w, mode="balanced", workspace=ws)
+    b1, m1 = run_gpu(torch_cuda, permute_pool(w, 7), mode="balanced", workspace=ws)
+    assert np.array_equal(a1, a2, equal_nan=True) and np.array_equal(l1, l2, equal_nan=True)
+    assert np.array_equal(a1, b1, equal_nan=True) and np.array_equal(l1, m1, equal_nan=True)
+    U = w.q.shape[0] * w.k_cache.shape[1]
+    assert int(ws[:4 * U].view(torch.int32).abs().sum()) == 0, "arrival counters not reset"
+    ref, ref_lse = run_oracle(w)
+    assert_parity(w, a1, l1, ref, ref_lse)
+
+
+def test_balanced_rejects_unserved_dims(torch_cuda):
+    import paged_speculative_verify_amd as psv
+    w = make("tiny_decode")                     # fp32 q: not served by the matrix-core stream
+    d = to_device(w)
+    with pytest.raises(psv.PtaError):
+        psv.taco_paged_tree_attn_balanced(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
+                                          d.q_lens, d.tree_mask, d.scale, max_ctx_len=d.max_ctx_len)
+    w = make(spec("x", 2, 64, 8, 128, "bf16", "bf16", (20, 100), 16, "random", seed=112))   # 128 rows
+    d = to_device(w)
+    with pytest.raises(psv.PtaError):
+        psv.taco_paged_tree_attn_balanced(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
+                                          d.q_lens, d.tree_mask, d.scale, max_ctx_len=d.max_ctx_len)
