@@ -44,7 +44,7 @@ LAUNCH = {
     "fp8_kv_chain": dict(mode="whole", split=None, path="auto"),
 }
 
-KERNEL_SOURCES = ["pta_device.h", "pta_valu.hip", "pta_stream.hip", "pta_mfma.hip", "pta_aux.hip", "pta_api.hip"]
+KERNEL_SOURCES = ["pta_device.h", "pta_flash.h", "pta_valu.hip", "pta_stream.hip", "pta_tile.hip", "pta_aux.hip", "pta_api.hip"]
 
 
 def launch_config(name: str) -> dict:

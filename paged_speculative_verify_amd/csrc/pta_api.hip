@@ -85,7 +85,7 @@ pta_status plan_for(const pta_dims* d, Plan* p) {
     p->nw = 4;
   } else {
     p->fam = FAM_TILE;
-    p->nw = pow2_at_least((rows + 31) / 32);
+    p->nw = pow2_at_least((rows + 31) / 32);     // 2, 4 or 8 waves of 32 rows
   }
   return PTA_OK;
 }
@@ -122,7 +122,7 @@ pta_status run_attn(const pta_dims* d, const AttnArgs& a, const Plan& p, hipStre
   hipError_t e;
   switch (p.fam) {
     case FAM_STREAM: e = launch_stream(a, d->kv_dtype, d->head_dim, p.rb, p.nw, grid, s); break;
-    case FAM_TILE: e = launch_mfma(a, d->kv_dtype, d->head_dim, p.nw, grid, s); break;
+    case FAM_TILE: e = launch_tile(a, d->kv_dtype, d->head_dim, p.nw, grid, s); break;
     default: e = launch_valu(a, d->q_dtype, d->kv_dtype, d->head_dim, p.rows_pow2, grid, s); break;
   }
   return e == hipSuccess ? PTA_OK : PTA_ERR_HIP;

@@ -118,8 +118,17 @@ __device__ __forceinline__ uint64_t load_mask_row(const uint8_t* mask, int b, in
                                                   int Qmax) {
   if (mask == nullptr) return 1ull;          // Qmax == 1: the candidate sees itself
   const uint8_t* row = mask + ((int64_t)b * Qmax + i) * Qmax;
+  // 16 independent byte loads per group (indices clamped into the row), so a
+  // row costs one memory round trip per 16 candidates rather than one each
   uint64_t bits = 0;
-  for (int j = 0; j < qb; ++j) bits |= (uint64_t)(row[j] != 0) << j;
+  for (int j0 = 0; j0 < qb; j0 += 16) {
+    uint8_t v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = row[min(j0 + e, qb - 1)];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (j0 + e < qb && v[e] != 0) bits |= 1ull << (j0 + e);
+  }
   return bits;
 }
 

@@ -1,0 +1,411 @@
+// Flash-attention building blocks shared by the matrix-core kernels (gfx950):
+// page tiles staged in LDS as bf16 rows, the rows a lane owns, its online
+// softmax state, the per-page update with v_mfma_f32_16x16x32_bf16 (S^T = K Q^T)
+// and v_mfma_f32_16x16x16_bf16 with ds_read_b64_tr_b16 (O^T += V^T P^T), and
+// the stores of final or partial rows.
+//
+// Lane (g, m) = (lane / 16, lane % 16) owns rows 16 rb + m of the unit and, in
+// every 16-token page, tokens 4 g + r (r < 4) of the S^T accumulator; its O^T
+// accumulators hold dims 16 db + 4 g + r of the same rows.
+#pragma once
+
+#include "pta_device.h"
+
+namespace pta {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kLazyTau = 8.0f;   // log2 headroom before a row's reference max moves
+constexpr int kMinSlicePages = 8;  // balanced mode: fewest pages per wave slice
+
+template <typename KT, int D>
+struct StreamTile {
+  static constexpr int KK = D / 32;                           // 16x16x32 k-steps over the head dim
+  static constexpr int DB = D / 16;                           // 16-dim blocks of O^T
+  static constexpr int LOADS = (kPage * D * KT::bytes) / 1024;     // 16-byte loads per lane per tile
+  static constexpr int STR = 2 * D + 32;                      // bytes per bf16 row in LDS (bank skew)
+  static constexpr int TILE_LDS = kPage * STR;                // one bf16 tile in LDS
+  static constexpr int WAVE_LDS = 2 * TILE_LDS;               // per-wave K tile + V tile
+};
+
+// One page's K and V chunks in flight (lane l holds bytes 16 l + 1024 j).
+template <typename KT, int D>
+struct PageRegs {
+  uint4 k[StreamTile<KT, D>::LOADS];
+  uint4 v[StreamTile<KT, D>::LOADS];
+  float ks, vs;
+};
+
+// Write 1 KiB load chunk j of a page tile (lane l holds bytes 16 l + 1024 j)
+// into a bf16 LDS tile (fp8 codes decoded exactly); rows at or past `valid`
+// are zeroed when `partial`.
+template <typename KT, int D>
+__device__ __forceinline__ void stage_chunk(char* dst, uint4 w, int j, int lane, bool partial, int valid) {
+  constexpr int STR = StreamTile<KT, D>::STR;
+  const int byte = 1024 * j + 16 * lane;
+  if constexpr (KT::bytes == 2) {
+    const int t = byte / (2 * D), col = byte % (2 * D);
+    if (partial) {
+      if (t >= valid) w = make_uint4(0, 0, 0, 0);
+    }
+    *reinterpret_cast<uint4*>(dst + t * STR + col) = w;
+  } else {
+    const int t = byte / D, d0 = byte % D;
+    uint4 lo, hi;
+    lo.x = fp8x2_to_bf16x2<false>(w.x); lo.y = fp8x2_to_bf16x2<true>(w.x);
+    lo.z = fp8x2_to_bf16x2<false>(w.y); lo.w = fp8x2_to_bf16x2<true>(w.y);
+    hi.x = fp8x2_to_bf16x2<false>(w.z); hi.y = fp8x2_to_bf16x2<true>(w.z);
+    hi.z = fp8x2_to_bf16x2<false>(w.w); hi.w = fp8x2_to_bf16x2<true>(w.w);
+    if (partial) {
+      if (t >= valid) { lo = make_uint4(0, 0, 0, 0); hi = lo; }
+    }
+    *reinterpret_cast<uint4*>(dst + t * STR + 2 * d0) = lo;
+    *reinterpret_cast<uint4*>(dst + t * STR + 2 * d0 + 16) = hi;
+  }
+}
+
+// All chunks of one page tile.
+template <typename KT, int D>
+__device__ __forceinline__ void stage_tile(char* dst, const uint4 (&c)[StreamTile<KT, D>::LOADS], int lane,
+                                           bool partial, int valid) {
+#pragma unroll
+  for (int j = 0; j < StreamTile<KT, D>::LOADS; ++j) stage_chunk<KT, D>(dst, c[j], j, lane, partial, valid);
+}
+
+// The rows a lane owns (row = row0 + 16 rb + m of the unit): Q^T operands,
+// candidate mask bits and output coordinates.
+template <int D, int RB>
+struct StreamRows {
+  bf16x8 qop[RB][D / 32];
+  uint64_t mbits[RB];
+  bool ok[RB];
+  int h[RB], i[RB];
+};
+
+template <int D, int RB>
+__device__ __forceinline__ void load_rows(StreamRows<D, RB>& R, const AttnArgs& a, int b, int hkv, int qb,
+                                          int M, int g, int m, int row0 = 0) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = row0 + rb * 16 + m;
+    R.ok[rb] = row < M;
+    R.h[rb] = hkv * a.G + (R.ok[rb] ? row / qb : 0);
+    R.i[rb] = R.ok[rb] ? row % qb : 0;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         (((int64_t)b * a.Qmax + R.i[rb]) * a.Hq + R.h[rb]) * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const uint4 w = R.ok[rb] ? *reinterpret_cast<const uint4*>(qp + 32 * kk) : make_uint4(0, 0, 0, 0);
+      R.qop[rb][kk] = __builtin_bit_cast(bf16x8, w);
+    }
+    R.mbits[rb] = R.ok[rb] ? load_mask_row(a.mask, b, R.i[rb], qb, a.Qmax) : 0ull;
+  }
+}
+
+// Flash state of a lane's rows: O^T accumulators (dims 16 db + 4 g + r), the
+// reference maximum (log2 units) and the partial row sum of this lane's tokens.
+template <int D, int RB>
+struct StreamState {
+  f32x4 o[RB][D / 16];
+  float m[RB], l[RB];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      m[rb] = -__builtin_huge_valf();
+      l[rb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) o[rb][db] = {};
+    }
+  }
+};
+
+// One page of the flash update for a lane's rows, from bf16 K and V tiles in
+// LDS (16 rows of STR bytes): S^T = K Q^T, scores in log2 units (c = softmax
+// scale * log2 e * the page's K scale), mask by select (tokens at or past t1,
+// and candidate tokens off the row's tree mask), lazy reference-max update,
+// then O^T += V^T P^T with P scaled by the page's V scale vs and carried as a
+// bf16 hi/lo pair.  pbase: logical
+// position of the page's first token.
+template <int D, int RB>
+__device__ __forceinline__ void page_compute(const StreamRows<D, RB>& rows, StreamState<D, RB>& st,
+                                             const char* kl, const char* vt_l, int pbase, int L, int t1,
+                                             float c, float vs, int lane) {
+  constexpr int KK = D / 32, DB = D / 16, STR = 2 * D + 32;
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  const int g = lane >> 4, m = lane & 15;
+  // 2. S^T[16 tokens][16 rows] = K Q^T per row block (A operand from LDS)
+  f32x4 sacc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) sacc[rb] = {};
+  const char* krd = kl + m * STR + 16 * g;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const bf16x8 kop = *reinterpret_cast<const bf16x8*>(krd + 64 * kk);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, rows.qop[rb][kk], sacc[rb], 0, 0, 0);
+  }
+
+  // 3. scores in log2 units, mask by select; lazy reference-max update
+  const bool plain = pbase + kPage <= min(L, t1);
+  float x[RB][4];
+  bool need = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float pm = NEG_INF;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = sacc[rb][r] * c;
+      if (!plain) {
+        const int t = pbase + 4 * g + r;
+        const int sh = t - L;
+        const bool cand = (unsigned)sh < 64u && ((rows.mbits[rb] >> (sh & 63)) & 1ull);
+        v = (t < t1 && (t < L || cand)) ? v : NEG_INF;
+      }
+      v = rows.ok[rb] ? v : NEG_INF;
+      x[rb][r] = v;
+      pm = fmaxf(pm, v);
+    }
+    need |= pm > st.m[rb] + kLazyTau;
+  }
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float pm = fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]));
+      pm = fmaxf(pm, shfl_xor(pm, 16));
+      pm = fmaxf(pm, shfl_xor(pm, 32));
+      const float mnew = fmaxf(st.m[rb], pm);
+      const float alpha = fast_exp2(st.m[rb] - (mnew == NEG_INF ? 0.f : mnew));
+      st.m[rb] = mnew;
+      st.l[rb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) st.o[rb][db] *= alpha;
+    }
+  }
+
+  // 4. P^T straight from the S^T registers as a bf16 pair P_hi + P_lo (P_hi =
+  //    bf16(P), P_lo = bf16(P - P_hi): P to ~2^-16 relative, so the weights
+  //    cost no accuracy even when the lazy reference max leaves them above 1);
+  //    O^T += V^T P_hi^T + V^T P_lo^T
+  s16x4 phi[RB], plo[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float muse = st.m[rb] == NEG_INF ? 0.f : st.m[rb];
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = fast_exp2(x[rb][r] - muse);
+      st.l[rb] += p[r];
+      p[r] *= vs;
+    }
+    const uint32_t h0 = pack_bf16x2(p[0], p[1]);
+    const uint32_t h1 = pack_bf16x2(p[2], p[3]);
+    const uint32_t l0 = pack_bf16x2(p[0] - bf16_lo(h0), p[1] - bf16_hi(h0));
+    const uint32_t l1 = pack_bf16x2(p[2] - bf16_lo(h1), p[3] - bf16_hi(h1));
+    phi[rb] = __builtin_bit_cast(s16x4, make_uint2(h0, h1));
+    plo[rb] = __builtin_bit_cast(s16x4, make_uint2(l0, l1));
+  }
+  const char* vrd = vt_l + (4 * g + (m >> 2)) * STR + 8 * (m & 3);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrd + 32 * db));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      st.o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi[rb], st.o[rb][db], 0, 0, 0);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      st.o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo[rb], st.o[rb][db], 0, 0, 0);
+  }
+}
+
+// Byte offset of 16-byte unit `u` of row `r` in a bf16 LDS tile of D dims.
+// Padded tiles put rows STR = 2 D + 32 bytes apart; swizzled tiles keep rows
+// 2 D bytes apart (so a tile is contiguous, as direct global-to-LDS loads
+// write it) and XOR the unit with the row, which spreads row-strided operand
+// reads over the banks.
+template <int D, bool SWZ>
+__device__ __forceinline__ int tile_off(int r, int u) {
+  if constexpr (SWZ) {
+    constexpr int UPR = 2 * D / 16;           // 16-byte units per row
+    return r * 2 * D + ((u ^ (r & (UPR - 1))) << 4);
+  } else {
+    return r * (2 * D + 32) + (u << 4);
+  }
+}
+
+// Two consecutive pages of the flash update at once (tiles kl0/vl0 and
+// kl1/vl1, first token at pbase): S^T per page as in page_compute, one lazy
+// max check over both, and a single 32-token O^T += V^T P^T step with
+// v_mfma_f32_16x16x32_bf16 (full rate on gfx950, where the 16-token
+// instruction runs at half rate).  The k index of that step runs over tokens
+// {4 g + e, 16 + 4 g + e} for lane group g: the B operand is the lane's two
+// S^T accumulators (P as a bf16 hi/lo pair) and the A operand is two
+// ds_read_b64_tr_b16 reads, one from each V tile.  A missing second page must
+// be presented with its V tile zeroed and its tokens at or past t1 (masked).
+template <int D, int RB, bool SWZ = false>
+__device__ __forceinline__ void pair_compute(const StreamRows<D, RB>& rows, StreamState<D, RB>& st,
+                                             const char* kl0, const char* kl1, const char* vl0,
+                                             const char* vl1, int pbase, int L, int t1, float c0,
+                                             float c1, float vs0, float vs1, int lane) {
+  constexpr int KK = D / 32, DB = D / 16, STR = 2 * D + 32;
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  const int g = lane >> 4, m = lane & 15;
+
+  // S^T for both pages
+  f32x4 sacc[2][RB];
+#pragma unroll
+  for (int pg = 0; pg < 2; ++pg) {
+    const char* kt = pg ? kl1 : kl0;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) sacc[pg][rb] = {};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kt + tile_off<D, SWZ>(m, 4 * kk + g));
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        sacc[pg][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, rows.qop[rb][kk], sacc[pg][rb], 0, 0, 0);
+    }
+  }
+
+  // scores in log2 units, mask by select, lazy reference-max update
+  const bool plain = pbase + 2 * kPage <= min(L, t1);
+  float x[RB][8];
+  bool need = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float pm = NEG_INF;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pg = e >> 2, r = e & 3;
+      float v = sacc[pg][rb][r] * (pg ? c1 : c0);
+      if (!plain) {
+        const int t = pbase + 16 * pg + 4 * g + r;
+        const int sh = t - L;
+        const bool cand = (unsigned)sh < 64u && ((rows.mbits[rb] >> (sh & 63)) & 1ull);
+        v = (t < t1 && (t < L || cand)) ? v : NEG_INF;
+      }
+      v = rows.ok[rb] ? v : NEG_INF;
+      x[rb][e] = v;
+      pm = fmaxf(pm, v);
+    }
+    need |= pm > st.m[rb] + kLazyTau;
+  }
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float pm = x[rb][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) pm = fmaxf(pm, x[rb][e]);
+      pm = fmaxf(pm, shfl_xor(pm, 16));
+      pm = fmaxf(pm, shfl_xor(pm, 32));
+      const float mnew = fmaxf(st.m[rb], pm);
+      const float alpha = fast_exp2(st.m[rb] - (mnew == NEG_INF ? 0.f : mnew));
+      st.m[rb] = mnew;
+      st.l[rb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) st.o[rb][db] *= alpha;
+    }
+  }
+
+  // P as a bf16 hi/lo pair over the lane's 8 tokens; O^T += V^T P^T (k = 32 tokens)
+  bf16x8 phi[RB], plo[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float muse = st.m[rb] == NEG_INF ? 0.f : st.m[rb];
+    uint32_t h[4], lo[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e0 = 2 * k, e1 = 2 * k + 1;
+      float p0 = fast_exp2(x[rb][e0] - muse), p1 = fast_exp2(x[rb][e1] - muse);
+      st.l[rb] += p0 + p1;
+      const float v = k < 2 ? vs0 : vs1;
+      p0 *= v;
+      p1 *= v;
+      h[k] = pack_bf16x2(p0, p1);
+      lo[k] = pack_bf16x2(p0 - bf16_lo(h[k]), p1 - bf16_hi(h[k]));
+    }
+    phi[rb] = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+    plo[rb] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+  }
+  const int vrow = 4 * g + (m >> 2);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int voff = tile_off<D, SWZ>(vrow, 2 * db + ((m & 3) >> 1)) + 8 * (m & 1);
+    const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl0 + voff));
+    const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl1 + voff));
+    const bf16x8 vt = __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint2, va).x,
+                                                           __builtin_bit_cast(uint2, va).y,
+                                                           __builtin_bit_cast(uint2, vb).x,
+                                                           __builtin_bit_cast(uint2, vb).y));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      st.o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi[rb], st.o[rb][db], 0, 0, 0);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      st.o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, plo[rb], st.o[rb][db], 0, 0, 0);
+  }
+}
+
+// Row sums over the lane's four 16-lane groups (every group holds 4 of each
+// page's 16 tokens).
+template <int D, int RB>
+__device__ __forceinline__ void reduce_row_sums(StreamState<D, RB>& st) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    st.l[rb] += shfl_xor(st.l[rb], 16);
+    st.l[rb] += shfl_xor(st.l[rb], 32);
+  }
+}
+
+// Final rows of a lane: out = O / l (bf16), lse = ln l + max.
+template <int D, int RB>
+__device__ __forceinline__ void store_final_rows(const AttnArgs& a, const StreamRows<D, RB>& rows,
+                                                 const StreamState<D, RB>& st, int b, int g) {
+  constexpr float NEG_INF = -__builtin_huge_valf();
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    if (!rows.ok[rb]) continue;
+    const float lt = st.l[rb];
+    const float muse = st.m[rb] == NEG_INF ? 0.f : st.m[rb];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse = lt > 0.f ? (muse + fast_log2(lt)) * kLn2 : NEG_INF;
+    const int h = rows.h[rb], i = rows.i[rb];
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (((int64_t)b * a.Qmax + i) * a.Hq + h) * D + 4 * g;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      uint2 w;
+      w.x = pack_bf16x2(st.o[rb][db][0] * inv, st.o[rb][db][1] * inv);
+      w.y = pack_bf16x2(st.o[rb][db][2] * inv, st.o[rb][db][3] * inv);
+      *reinterpret_cast<uint2*>(op + 16 * db) = w;
+    }
+    if (g == 0 && a.lse != nullptr) a.lse[((int64_t)b * a.Hq + h) * a.Qmax + i] = lse;
+  }
+}
+
+// Partial rows of a lane (normalised O and natural-log LSE), stored with
+// device-coherent word stores.  row_addr(rb, o, l) gives the row's O words and
+// LSE word.
+template <int D, int RB, typename AddrFn>
+__device__ __forceinline__ void store_partial_rows(const StreamRows<D, RB>& rows,
+                                                   const StreamState<D, RB>& st, int g, AddrFn row_addr) {
+  constexpr float NEG_INF = -__builtin_huge_valf();
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    if (!rows.ok[rb]) continue;
+    const float lt = st.l[rb];
+    const float muse = st.m[rb] == NEG_INF ? 0.f : st.m[rb];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse = lt > 0.f ? (muse + fast_log2(lt)) * kLn2 : NEG_INF;
+    float* o;
+    float* l;
+    row_addr(rb, o, l);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_coherent(o + 16 * db + 4 * g + e, st.o[rb][db][e] * inv);
+    if (g == 0) store_coherent(l, lse);
+  }
+}
+
+}  // namespace pta

@@ -19,8 +19,8 @@ hipError_t launch_stream(const AttnArgs& a, int kv_dtype, int head_dim, int rb, 
 // (workgroups) for the current device; otherwise *nwg workgroups are launched.
 hipError_t stream_balanced(const AttnArgs* a, int kv_dtype, int head_dim, int rb, int nw, int B, int* nwg,
                            hipStream_t s);
-hipError_t launch_mfma(const AttnArgs& a, int kv_dtype, int head_dim, int nwave, dim3 grid,
-                       hipStream_t s);
+// Matrix-core shared-tile kernel (rows per KV head 33..256): nwr waves of 32 rows.
+hipError_t launch_tile(const AttnArgs& a, int kv_dtype, int head_dim, int nwr, dim3 grid, hipStream_t s);
 
 struct AppendArgs {
   const void* k_new;

@@ -42,117 +42,10 @@
 //                           unit leaves a partial that the unit's last slice
 //                           merges.
 #include "pta_device.h"
+#include "pta_flash.h"
 #include "pta_launch.h"
 
 namespace pta {
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-constexpr float kLazyTau = 8.0f;   // log2 headroom before a row's reference max moves
-constexpr int kMinSlicePages = 8;  // balanced mode: fewest pages per wave slice
-
-template <typename KT, int D>
-struct StreamTile {
-  static constexpr int KK = D / 32;                           // 16x16x32 k-steps over the head dim
-  static constexpr int DB = D / 16;                           // 16-dim blocks of O^T
-  static constexpr int LOADS = (kPage * D * KT::bytes) / 1024;     // 16-byte loads per lane per tile
-  static constexpr int STR = 2 * D + 32;                      // bytes per bf16 row in LDS (bank skew)
-  static constexpr int TILE_LDS = kPage * STR;                // one bf16 tile in LDS
-  static constexpr int WAVE_LDS = 2 * TILE_LDS;               // per-wave K tile + V tile
-};
-
-// One page's K and V chunks in flight (lane l holds bytes 16 l + 1024 j).
-template <typename KT, int D>
-struct PageRegs {
-  uint4 k[StreamTile<KT, D>::LOADS];
-  uint4 v[StreamTile<KT, D>::LOADS];
-  float ks, vs;
-};
-
-// Write one page tile's chunks into a bf16 LDS tile (fp8 codes decoded
-// exactly); rows at or past `valid` are zeroed when `partial`.
-template <typename KT, int D>
-__device__ __forceinline__ void stage_tile(char* dst, const uint4 (&c)[StreamTile<KT, D>::LOADS], int lane,
-                                           bool partial, int valid) {
-  using T = StreamTile<KT, D>;
-  if constexpr (KT::bytes == 2) {
-#pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) {
-      const int byte = 1024 * j + 16 * lane;
-      const int t = byte / (2 * D), col = byte % (2 * D);
-      uint4 w = c[j];
-      if (partial) {
-        if (t >= valid) w = make_uint4(0, 0, 0, 0);
-      }
-      *reinterpret_cast<uint4*>(dst + t * T::STR + col) = w;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) {
-      const int byte = 1024 * j + 16 * lane;
-      const int t = byte / D, d0 = byte % D;
-      const uint4 w = c[j];
-      uint4 lo, hi;
-      lo.x = fp8x2_to_bf16x2<false>(w.x); lo.y = fp8x2_to_bf16x2<true>(w.x);
-      lo.z = fp8x2_to_bf16x2<false>(w.y); lo.w = fp8x2_to_bf16x2<true>(w.y);
-      hi.x = fp8x2_to_bf16x2<false>(w.z); hi.y = fp8x2_to_bf16x2<true>(w.z);
-      hi.z = fp8x2_to_bf16x2<false>(w.w); hi.w = fp8x2_to_bf16x2<true>(w.w);
-      if (partial) {
-        if (t >= valid) { lo = make_uint4(0, 0, 0, 0); hi = lo; }
-      }
-      *reinterpret_cast<uint4*>(dst + t * T::STR + 2 * d0) = lo;
-      *reinterpret_cast<uint4*>(dst + t * T::STR + 2 * d0 + 16) = hi;
-    }
-  }
-}
-
-// The rows a lane owns (row = 16 rb + m of the unit): Q^T operands, candidate
-// mask bits and output coordinates.
-template <int D, int RB>
-struct StreamRows {
-  bf16x8 qop[RB][D / 32];
-  uint64_t mbits[RB];
-  bool ok[RB];
-  int h[RB], i[RB];
-};
-
-template <int D, int RB>
-__device__ __forceinline__ void load_rows(StreamRows<D, RB>& R, const AttnArgs& a, int b, int hkv, int qb,
-                                          int M, int g, int m) {
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = rb * 16 + m;
-    R.ok[rb] = row < M;
-    R.h[rb] = hkv * a.G + (R.ok[rb] ? row / qb : 0);
-    R.i[rb] = R.ok[rb] ? row % qb : 0;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                         (((int64_t)b * a.Qmax + R.i[rb]) * a.Hq + R.h[rb]) * D + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      const uint4 w = R.ok[rb] ? *reinterpret_cast<const uint4*>(qp + 32 * kk) : make_uint4(0, 0, 0, 0);
-      R.qop[rb][kk] = __builtin_bit_cast(bf16x8, w);
-    }
-    R.mbits[rb] = R.ok[rb] ? load_mask_row(a.mask, b, R.i[rb], qb, a.Qmax) : 0ull;
-  }
-}
-
-// Flash state of a lane's rows: O^T accumulators (dims 16 db + 4 g + r), the
-// reference maximum (log2 units) and the partial row sum of this lane's tokens.
-template <int D, int RB>
-struct StreamState {
-  f32x4 o[RB][D / 16];
-  float m[RB], l[RB];
-  __device__ __forceinline__ void init() {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      m[rb] = -__builtin_huge_valf();
-      l[rb] = 0.f;
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) o[rb][db] = {};
-    }
-  }
-};
 
 // Stream the pages pg = pg0 + k * stride (k < nk) of unit (b, hkv) through the
 // state.  Tokens at or past t1 (the end of the sequence or of the partition)
@@ -200,80 +93,7 @@ __device__ __forceinline__ void stream_pages(const AttnArgs& a, const StreamRows
     stage_tile<KT, D>(kl, R.k, lane, false, kPage);
     stage_tile<KT, D>(vt_l, R.v, lane, partial, t1 - pbase);
 
-    // 2. S^T[16 tokens][16 rows] = K Q^T per row block (A operand from LDS)
-    f32x4 sacc[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) sacc[rb] = {};
-    const char* krd = kl + m * T::STR + 16 * g;
-#pragma unroll
-    for (int kk = 0; kk < T::KK; ++kk) {
-      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(krd + 64 * kk);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, rows.qop[rb][kk], sacc[rb], 0, 0, 0);
-    }
-
-    // 3. scores in log2 units, mask by select; lazy reference-max update
-    const float c = a.scale_log2 * R.ks;
-    const bool plain = pbase + kPage <= min(L, t1);
-    float x[RB][4];
-    bool need = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float pm = NEG_INF;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = sacc[rb][r] * c;
-        if (!plain) {
-          const int t = pbase + 4 * g + r;
-          const int sh = t - L;
-          const bool cand = (unsigned)sh < 64u && ((rows.mbits[rb] >> (sh & 63)) & 1ull);
-          v = (t < t1 && (t < L || cand)) ? v : NEG_INF;
-        }
-        v = rows.ok[rb] ? v : NEG_INF;
-        x[rb][r] = v;
-        pm = fmaxf(pm, v);
-      }
-      need |= pm > st.m[rb] + kLazyTau;
-    }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        float pm = fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]));
-        pm = fmaxf(pm, shfl_xor(pm, 16));
-        pm = fmaxf(pm, shfl_xor(pm, 32));
-        const float mnew = fmaxf(st.m[rb], pm);
-        const float alpha = fast_exp2(st.m[rb] - (mnew == NEG_INF ? 0.f : mnew));
-        st.m[rb] = mnew;
-        st.l[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < T::DB; ++db) st.o[rb][db] *= alpha;
-      }
-    }
-
-    // 4. P^T (bf16) straight from the S^T registers; O^T += V^T P^T
-    s16x4 pop[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float muse = st.m[rb] == NEG_INF ? 0.f : st.m[rb];
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = fast_exp2(x[rb][r] - muse);
-        st.l[rb] += p[r];
-      }
-      const uint32_t w0 = pack_bf16x2(p[0] * R.vs, p[1] * R.vs);
-      const uint32_t w1 = pack_bf16x2(p[2] * R.vs, p[3] * R.vs);
-      pop[rb] = __builtin_bit_cast(s16x4, make_uint2(w0, w1));
-    }
-    const char* vrd = vt_l + (4 * g + (m >> 2)) * T::STR + 8 * (m & 3);
-#pragma unroll
-    for (int db = 0; db < T::DB; ++db) {
-      const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrd + 32 * db));
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        st.o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pop[rb], st.o[rb][db], 0, 0, 0);
-    }
+    page_compute<D, RB>(rows, st, kl, vt_l, pbase, L, t1, a.scale_log2 * R.ks, R.vs, lane);
   };
 
   // Two register sets, the next page always in flight.  The prefetch is
@@ -294,67 +114,6 @@ __device__ __forceinline__ void stream_pages(const AttnArgs& a, const StreamRows
     issue(r0, ph_a);
     consume(r1, k + 1);
     if (k + 2 >= nk) break;
-  }
-}
-
-// Row sums over the lane's four 16-lane groups (every group holds 4 of each
-// page's 16 tokens).
-template <int D, int RB>
-__device__ __forceinline__ void reduce_row_sums(StreamState<D, RB>& st) {
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    st.l[rb] += shfl_xor(st.l[rb], 16);
-    st.l[rb] += shfl_xor(st.l[rb], 32);
-  }
-}
-
-// Final rows of a lane: out = O / l (bf16), lse = ln l + max.
-template <int D, int RB>
-__device__ __forceinline__ void store_final_rows(const AttnArgs& a, const StreamRows<D, RB>& rows,
-                                                 const StreamState<D, RB>& st, int b, int g) {
-  constexpr float NEG_INF = -__builtin_huge_valf();
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    if (!rows.ok[rb]) continue;
-    const float lt = st.l[rb];
-    const float muse = st.m[rb] == NEG_INF ? 0.f : st.m[rb];
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse = lt > 0.f ? (muse + fast_log2(lt)) * kLn2 : NEG_INF;
-    const int h = rows.h[rb], i = rows.i[rb];
-    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (((int64_t)b * a.Qmax + i) * a.Hq + h) * D + 4 * g;
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      uint2 w;
-      w.x = pack_bf16x2(st.o[rb][db][0] * inv, st.o[rb][db][1] * inv);
-      w.y = pack_bf16x2(st.o[rb][db][2] * inv, st.o[rb][db][3] * inv);
-      *reinterpret_cast<uint2*>(op + 16 * db) = w;
-    }
-    if (g == 0 && a.lse != nullptr) a.lse[((int64_t)b * a.Hq + h) * a.Qmax + i] = lse;
-  }
-}
-
-// Partial rows of a lane (normalised O and natural-log LSE), stored with
-// device-coherent word stores.  row_addr(rb, o, l) gives the row's O words and
-// LSE word.
-template <int D, int RB, typename AddrFn>
-__device__ __forceinline__ void store_partial_rows(const StreamRows<D, RB>& rows,
-                                                   const StreamState<D, RB>& st, int g, AddrFn row_addr) {
-  constexpr float NEG_INF = -__builtin_huge_valf();
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    if (!rows.ok[rb]) continue;
-    const float lt = st.l[rb];
-    const float muse = st.m[rb] == NEG_INF ? 0.f : st.m[rb];
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse = lt > 0.f ? (muse + fast_log2(lt)) * kLn2 : NEG_INF;
-    float* o;
-    float* l;
-    row_addr(rb, o, l);
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) store_coherent(o + 16 * db + 4 * g + e, st.o[rb][db][e] * inv);
-    if (g == 0) store_coherent(l, lse);
   }
 }
 
