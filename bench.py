@@ -14,7 +14,6 @@ every sequence's context counted once) per second of attention time, in GB/s.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -44,19 +43,12 @@ LAUNCH = {
     "fp8_kv_chain": dict(mode="whole", split=None, path="auto"),
 }
 
-KERNEL_SOURCES = ["pta_device.h", "pta_flash.h", "pta_valu.hip", "pta_stream.hip", "pta_tile.hip", "pta_aux.hip", "pta_api.hip"]
 
 
 def launch_config(name: str) -> dict:
     return dict(LAUNCH[name])
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_speculative_verify_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 # ------------------------------------------------------------------ accounting
@@ -305,6 +297,7 @@ def main(argv=None) -> int:
     cand_per_s = (sum(cands) / K) / (ms_per_step / 1e3)
     tflops = (sum(flops[o] for o in order) / K) / attn_avg_s / 1e12
 
+    from paged_speculative_verify_amd.profsum import kernel_source_hash
     src_hash = kernel_source_hash()
     traffic = load_traffic(name, src_hash)
     result = {

@@ -1,0 +1,176 @@
+"""Summaries of rocprofv3 output for the kernels of libpta.
+
+Two summaries, both written as short text under ``profiles/``:
+
+* ``trace``: the ``--kernel-trace --stats`` table (calls, mean and total time
+  per kernel) of one bench run, as Markdown.
+* ``traffic``: HBM bytes per launch of the attention kernel from two ``--pmc``
+  runs (``FETCH_SIZE`` and ``WRITE_SIZE``, KiB per dispatch). Each counter is
+  scaled by what it reads for a device copy of known size, measured in runs of
+  their own (``bench.py --copy-calibration``): on MI355X a 1 GiB copy reads as
+  0.5 GiB fetched and 1 GiB written. The JSON twin carries the hash of the
+  kernel sources it was taken on, and the bench reports the figure only while
+  that hash still matches.
+
+Usage::
+
+    python -m paged_speculative_verify_amd.profsum trace --csv <dir>/run_kernel_stats.csv \
+        --title <workload> --command "<rocprofv3 command>" --out profiles/<name>.md
+    python -m paged_speculative_verify_amd.profsum traffic --config <workload> \
+        --fetch <dir>/run_counter_collection.csv --write <dir>/run_counter_collection.csv \
+        --copy-fetch <csv> --copy-write <csv> --command "<commands>" --out-dir profiles
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+KERNEL_SOURCES = ["pta_device.h", "pta_flash.h", "pta_launch.h", "pta_valu.hip", "pta_stream.hip",
+                  "pta_tile.hip", "pta_aux.hip", "pta_api.hip"]
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30                      # bench.py --copy-calibration copies 1 GiB
+ATTN_KERNELS = ("stream_attn_kernel", "stream_balanced_kernel", "tile_dma_kernel",
+                "tile_attn_kernel", "valu_attn_kernel")
+
+
+def kernel_source_hash() -> str:
+    """Short hash over every source that goes into the attention kernels."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _short(name: str) -> str:
+    """Kernel name without the argument list (rocprofv3 prints demangled names)."""
+    name = name.strip('"')
+    return name.split("(")[0] if "(" in name else name
+
+
+def _is_attention(name: str) -> bool:
+    return any(k in name for k in ATTN_KERNELS)
+
+
+def counter_per_dispatch(path: str, counter: str, want) -> tuple[float, int, str]:
+    """Mean counter value over the dispatches whose kernel name passes ``want``."""
+    vals, names = [], set()
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter or not want(row["Kernel_Name"]):
+                continue
+            vals.append(float(row["Counter_Value"]))
+            names.add(_short(row["Kernel_Name"]))
+    if not vals:
+        raise SystemExit(f"{path}: no {counter} rows for the kernel asked for")
+    return statistics.fmean(vals), len(vals), ", ".join(sorted(names))
+
+
+def cmd_traffic(a) -> int:
+    fetch_kib, n_f, kname = counter_per_dispatch(a.fetch, "FETCH_SIZE", _is_attention)
+    write_kib, n_w, _ = counter_per_dispatch(a.write, "WRITE_SIZE", _is_attention)
+    cf_kib, _, _ = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", lambda n: COPY_KERNEL in n)
+    cw_kib, _, _ = counter_per_dispatch(a.copy_write, "WRITE_SIZE", lambda n: COPY_KERNEL in n)
+    f_scale = COPY_BYTES / (cf_kib * 1024.0)
+    w_scale = COPY_BYTES / (cw_kib * 1024.0)
+    fetch_b = fetch_kib * 1024.0 * f_scale
+    write_b = write_kib * 1024.0 * w_scale
+    rec = {
+        "workload": a.config,
+        "kernel": kname,
+        "dispatches": {"fetch": n_f, "write": n_w},
+        "fetch_kib_per_dispatch": round(fetch_kib, 1),
+        "write_kib_per_dispatch": round(write_kib, 1),
+        "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": round(cf_kib, 1),
+                             "write_kib": round(cw_kib, 1), "fetch_scale": round(f_scale, 4),
+                             "write_scale": round(w_scale, 4)},
+        "hbm_bytes_per_launch": round(fetch_b + write_b),
+        "hbm_fetch_bytes_per_launch": round(fetch_b),
+        "hbm_write_bytes_per_launch": round(write_b),
+        "kernel_source_hash": kernel_source_hash(),
+        "command": a.command,
+    }
+    os.makedirs(a.out_dir, exist_ok=True)
+    with open(os.path.join(a.out_dir, f"traffic_{a.config}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    lines = [
+        f"# HBM traffic of {kname} on {a.config}",
+        "",
+        "Commands:",
+        "",
+        "```",
+        a.command,
+        "```",
+        "",
+        "| quantity | value |",
+        "|---|---|",
+        f"| dispatches counted | {n_f} (FETCH_SIZE), {n_w} (WRITE_SIZE) |",
+        f"| FETCH_SIZE per dispatch | {fetch_kib:.1f} KiB |",
+        f"| WRITE_SIZE per dispatch | {write_kib:.1f} KiB |",
+        f"| 1 GiB copy reads as | {cf_kib:.1f} KiB fetched, {cw_kib:.1f} KiB written |",
+        f"| scale (fetch, write) | {f_scale:.4f}, {w_scale:.4f} |",
+        f"| HBM bytes per launch | {fetch_b + write_b:.4g} ({fetch_b:.4g} read, {write_b:.4g} written) |",
+        f"| kernel source hash | {rec['kernel_source_hash']} |",
+        "",
+    ]
+    with open(os.path.join(a.out_dir, f"traffic_{a.config}.md"), "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps(rec))
+    return 0
+
+
+def cmd_trace(a) -> int:
+    rows = []
+    with open(a.csv, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append(r)
+    lines = [f"# Kernel trace: {a.title}", "", "Command:", "", "```", a.command, "```", ""]
+    if a.bench_json and os.path.exists(a.bench_json):
+        with open(a.bench_json) as f:
+            txt = f.read().strip().splitlines()
+        if txt:
+            lines += ["Bench line of the same run:", "", "```", txt[-1], "```", ""]
+    lines += ["| kernel | calls | mean (us) | min (us) | max (us) | total (ms) | share |",
+              "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| {} | {} | {:.2f} | {:.2f} | {:.2f} | {:.3f} | {:.1f}% |".format(
+            _short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+    lines.append("")
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+    return 0
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--config", required=True)
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-fetch", required=True)
+    t.add_argument("--copy-write", required=True)
+    t.add_argument("--command", required=True)
+    t.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    k = sub.add_parser("trace")
+    k.add_argument("--csv", required=True)
+    k.add_argument("--title", required=True)
+    k.add_argument("--command", required=True)
+    k.add_argument("--bench-json", default=None)
+    k.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    return cmd_traffic(a) if a.cmd == "traffic" else cmd_trace(a)
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())
