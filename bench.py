@@ -191,7 +191,7 @@ def main(argv=None) -> int:
     ap.add_argument("--config", default=HEADLINE, choices=sorted(LAUNCH))
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated step to step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=["auto", "valu", "mfma"], default=None,
+    ap.add_argument("--path", choices=["auto", "valu", "mfma", "tile"], default=None,
                     help="override the kernel family of the workload's launch configuration")
     ap.add_argument("--split", type=int, default=None,
                     help="override the entry point: split-K partition length, 0 = one pass per "

@@ -39,7 +39,7 @@ pta_status check_dims(const pta_dims* d) {
   if (d->num_blocks < 1) return PTA_ERR_BAD_DIMS;
   if (d->reserved != 0) return PTA_ERR_BAD_DIMS;
   if (!dtype_ok(d->q_dtype, d->kv_dtype)) return PTA_ERR_BAD_DTYPE;
-  if (d->path < PTA_PATH_AUTO || d->path > PTA_PATH_MFMA) return PTA_ERR_BAD_DIMS;
+  if (d->path < PTA_PATH_AUTO || d->path > PTA_PATH_TILE) return PTA_ERR_BAD_DIMS;
   return PTA_OK;
 }
 
@@ -64,6 +64,13 @@ pta_status plan_for(const pta_dims* d, Plan* p) {
   const bool valu_ok = rows <= kValuMaxRows;
   const bool mfma_ok = d->q_dtype == PTA_BF16 && rows <= kMfmaMaxRows;
   bool mfma;
+  p->rows_pow2 = pow2_at_least(rows);
+  if (d->path == PTA_PATH_TILE) {
+    if (!mfma_ok) return PTA_ERR_UNSUPPORTED;
+    p->fam = FAM_TILE;
+    p->nw = max(2, pow2_at_least((rows + 31) / 32));
+    return PTA_OK;
+  }
   if (d->path == PTA_PATH_VALU) {
     if (!valu_ok) return PTA_ERR_UNSUPPORTED;
     mfma = false;
@@ -146,12 +153,16 @@ bool split_layout(const pta_dims* d, int32_t T, SplitLayout* L) {
   return true;
 }
 
-// Balanced mode: [counters int32 B*Hkv | partial O float S*Mmax*D | partial LSE float S*Mmax]
-// with S = (workgroups + B*Hkv/nw) * nw partial slots and Mmax = G * max_q_len rows per slot;
-// nw = waves per workgroup = the head group (largest of 8, 4, 2, 1 dividing Hkv; at most 4
-// for two 16-row blocks).
+// Balanced mode: [counters int32 | partial O float S*Mmax*D | partial LSE float S*Mmax]
+// with Mmax = G * max_q_len rows per slot.
+//   stream family: counters B*Hkv, S = (workgroups + B*Hkv/nw) * nw partial slots;
+//     nw = waves per workgroup = the head group (largest of 8, 4, 2, 1 dividing Hkv;
+//     at most 4 for two 16-row blocks).
+//   tile family (bf16 KV): nw waves of 32 rows per workgroup (2 or 4), rg row groups per
+//     slice, ns slices (a multiple of 8 with ns * rg workgroups fitting the device at
+//     once); counters B*Hkv*rg, S = ns + B*Hkv slots.
 struct BalancedLayout {
-  int nwg, nw;
+  int nwg, nw, rg;
   size_t o_off, lse_off, total;
 };
 
@@ -163,10 +174,34 @@ int head_group(int hkv, int rb) {
 
 constexpr int kBalancedMaxSeqs = 16383;   // sequence page prefix lives in LDS
 
+pta_status tile_balanced_layout(const pta_dims* d, BalancedLayout* L) {
+  const int rows = (d->num_q_heads / d->num_kv_heads) * d->max_q_len;
+  const int waves = (rows + 31) / 32;
+  const int nw = waves <= 2 ? 2 : 4;
+  const int rg = (waves + nw - 1) / nw;
+  int fit = 0;
+  if (tile_balanced(nullptr, d->head_dim, nw, d->num_seqs, &fit, nullptr) != hipSuccess) return PTA_ERR_HIP;
+  const int ns = (fit / rg) & ~7;
+  if (ns < 8) return PTA_ERR_UNSUPPORTED;
+  const int64_t units = (int64_t)d->num_seqs * d->num_kv_heads;
+  const int64_t slot_rows = ((int64_t)ns + units) * rows;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  L->nwg = ns * rg;
+  L->nw = nw;
+  L->rg = rg;
+  L->o_off = up((size_t)units * rg * sizeof(int32_t));
+  L->lse_off = L->o_off + up((size_t)slot_rows * d->head_dim * sizeof(float));
+  L->total = L->lse_off + up((size_t)slot_rows * sizeof(float));
+  return PTA_OK;
+}
+
 pta_status balanced_layout(const pta_dims* d, const Plan& p, BalancedLayout* L) {
-  if (p.fam != FAM_STREAM) return PTA_ERR_UNSUPPORTED;
   if (d->num_seqs > kBalancedMaxSeqs) return PTA_ERR_UNSUPPORTED;
   if ((int64_t)d->num_seqs * d->max_blocks_per_seq >= ((int64_t)1 << 31)) return PTA_ERR_UNSUPPORTED;
+  if ((int64_t)d->num_kv_heads * d->num_seqs * d->max_blocks_per_seq >= ((int64_t)1 << 31))
+    return PTA_ERR_UNSUPPORTED;
+  if (p.fam == FAM_TILE && d->kv_dtype == PTA_BF16) return tile_balanced_layout(d, L);
+  if (p.fam != FAM_STREAM) return PTA_ERR_UNSUPPORTED;
   const int nw = head_group(d->num_kv_heads, p.rb);
   int nwg = 0;
   if (stream_balanced(nullptr, d->kv_dtype, d->head_dim, p.rb, nw, d->num_seqs, &nwg, nullptr) != hipSuccess)
@@ -177,6 +212,7 @@ pta_status balanced_layout(const pta_dims* d, const Plan& p, BalancedLayout* L) 
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   L->nwg = nwg;
   L->nw = nw;
+  L->rg = 1;
   L->o_off = up((size_t)units * sizeof(int32_t));
   L->lse_off = L->o_off + up((size_t)rows * d->head_dim * sizeof(float));
   L->total = L->lse_off + up((size_t)rows * sizeof(float));
@@ -270,7 +306,7 @@ pta_status taco_paged_tree_attn_balanced(const pta_dims* d, const void* q, const
   Plan p;
   st = plan_for(d, &p);
   if (st != PTA_OK) return st;
-  if (p.fam != FAM_STREAM) return PTA_ERR_UNSUPPORTED;
+  if (p.fam != FAM_STREAM && !(p.fam == FAM_TILE && d->kv_dtype == PTA_BF16)) return PTA_ERR_UNSUPPORTED;
   if (d->num_seqs == 0) return PTA_OK;
   st = check_attn_ptrs(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
                        tree_mask, out);
@@ -288,6 +324,10 @@ pta_status taco_paged_tree_attn_balanced(const pta_dims* d, const void* q, const
   a.part_lse = reinterpret_cast<float*>(ws + L.lse_off);
   a.total_waves = L.nwg * L.nw;
   int nwg = L.nwg;
+  if (p.fam == FAM_TILE)
+    return tile_balanced(&a, d->head_dim, L.nw, d->num_seqs, &nwg, (hipStream_t)stream) == hipSuccess
+               ? PTA_OK
+               : PTA_ERR_HIP;
   return stream_balanced(&a, d->kv_dtype, d->head_dim, p.rb, L.nw, d->num_seqs, &nwg, (hipStream_t)stream) ==
                  hipSuccess
              ? PTA_OK

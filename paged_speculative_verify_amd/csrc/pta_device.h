@@ -152,7 +152,7 @@ __device__ __forceinline__ bool unit_writes_partials(const AttnArgs& a, int C) {
   return a.part_o != nullptr && C > a.part_tokens;
 }
 
-// Merge np partial results of the M rows of work unit (b, hkv) by
+// Merge np partial results of rows r0 .. M - 1 of work unit (b, hkv) by
 // log-sum-exp and store the final rows (out in the q dtype, lse):
 //   LSE = ln sum_p exp(LSE_p),   out = sum_p exp(LSE_p - LSE) O_p
 // (the long-sequence design of the 618zxw.cn article, section
@@ -160,60 +160,114 @@ __device__ __forceinline__ bool unit_writes_partials(const AttnArgs& a, int C) {
 // parts that are combined).  slot(r, p) gives the partial output row (D
 // floats) and its log-sum-exp word for row r, part p; parts are read in index
 // order, so the result does not depend on which worker merges.  Executed by
-// nthr threads; each takes (row, 4 dims) items, with every load of a batch of
-// PB parts in flight at once and an online rescale across batches.
+// nthr threads; each takes IT (row, 4 dims) items at a time, with the loads of
+// PB parts of all of them in flight at once and an online rescale across
+// batches of parts.
 template <typename QT, int D, typename SlotFn>
 __device__ __forceinline__ void merge_rows(const AttnArgs& a, int b, int hkv, int qb, int M, int np,
-                                           SlotFn slot, int tid, int nthr) {
+                                           SlotFn slot, int tid, int nthr, int r0 = 0) {
   constexpr float NEG_INF = -__builtin_huge_valf();
   constexpr int Q4 = D / 4;
-  constexpr int PB = 8;
-  for (int idx = tid; idx < M * Q4; idx += nthr) {
-    const int r = idx / Q4, d = (idx % Q4) * 4;
-    float mrun = NEG_INF, wsum = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int PB = 4;      // parts per batch
+  constexpr int IT = 2;      // items per thread per round: IT * PB partials in flight
+  const int items = (M - r0) * Q4;
+  for (int base = tid; base < items; base += nthr * IT) {
+    float mrun[IT], wsum[IT];
+    f32x4 acc[IT];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      mrun[k] = NEG_INF;
+      wsum[k] = 0.f;
+      acc[k] = {0.f, 0.f, 0.f, 0.f};
+    }
     for (int p0 = 0; p0 < np; p0 += PB) {
-      float lp[PB];
-      f32x4 op[PB];
+      float lp[IT][PB];
+      f32x4 op[IT][PB];
 #pragma unroll
-      for (int j = 0; j < PB; ++j) {
-        const bool ok = p0 + j < np;
-        const auto s = slot(r, ok ? p0 + j : 0);
-        lp[j] = ok ? load_coherent(s.lse) : NEG_INF;
+      for (int k = 0; k < IT; ++k) {
+        const int idx = base + k * nthr;
+        const bool iok = idx < items;
+        const int r = r0 + (iok ? idx : 0) / Q4, d = ((iok ? idx : 0) % Q4) * 4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) op[j][e] = ok ? load_coherent(s.o + d + e) : 0.f;
+        for (int j = 0; j < PB; ++j) {
+          const bool ok = iok && p0 + j < np;
+          const auto sl = slot(r, ok ? p0 + j : 0);
+          lp[k][j] = ok ? load_coherent(sl.lse) : NEG_INF;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) op[k][j][e] = ok ? load_coherent(sl.o + d + e) : 0.f;
+        }
       }
-      float mx = mrun;
 #pragma unroll
-      for (int j = 0; j < PB; ++j) mx = fmaxf(mx, lp[j]);
-      const float muse = mx == NEG_INF ? 0.f : mx;
-      const float alpha = __expf(mrun - muse);          // 0 while nothing has been seen
-      wsum *= alpha;
-      acc *= alpha;
+      for (int k = 0; k < IT; ++k) {
+        float mx = mrun[k];
 #pragma unroll
-      for (int j = 0; j < PB; ++j) {
-        const float w = __expf(lp[j] - muse);           // exp(-inf) = 0: no visible key there
-        wsum += w;
-        acc += w * op[j];
+        for (int j = 0; j < PB; ++j) mx = fmaxf(mx, lp[k][j]);
+        const float muse = mx == NEG_INF ? 0.f : mx;
+        const float alpha = __expf(mrun[k] - muse);          // 0 while nothing has been seen
+        wsum[k] *= alpha;
+        acc[k] *= alpha;
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+          const float w = __expf(lp[k][j] - muse);           // exp(-inf) = 0: no visible key there
+          wsum[k] += w;
+          acc[k] += w * op[k][j];
+        }
+        mrun[k] = mx;
       }
-      mrun = mx;
     }
-    const float muse = mrun == NEG_INF ? 0.f : mrun;
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    acc *= inv;
-    const int h = hkv * a.G + r / qb, i = r % qb;
-    const int64_t o = (((int64_t)b * a.Qmax + i) * a.Hq + h) * D + d;
-    if constexpr (QT::bytes == 4) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = acc;
-    } else {
-      uint2 w;
-      w.x = pack_bf16x2(acc[0], acc[1]);
-      w.y = pack_bf16x2(acc[2], acc[3]);
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + o) = w;
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int idx = base + k * nthr;
+      if (idx >= items) continue;
+      const int r = r0 + idx / Q4, d = (idx % Q4) * 4;
+      const float muse = mrun[k] == NEG_INF ? 0.f : mrun[k];
+      const float inv = wsum[k] > 0.f ? 1.f / wsum[k] : 0.f;
+      const f32x4 res = acc[k] * inv;
+      const int h = hkv * a.G + r / qb, i = r % qb;
+      const int64_t o = (((int64_t)b * a.Qmax + i) * a.Hq + h) * D + d;
+      if constexpr (QT::bytes == 4) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = res;
+      } else {
+        uint2 w;
+        w.x = pack_bf16x2(res[0], res[1]);
+        w.y = pack_bf16x2(res[2], res[3]);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + o) = w;
+      }
+      if (d == 0 && a.lse != nullptr)
+        a.lse[((int64_t)b * a.Hq + h) * a.Qmax + i] = wsum[k] > 0.f ? muse + __logf(wsum[k]) : NEG_INF;
     }
-    if (d == 0 && a.lse != nullptr)
-      a.lse[((int64_t)b * a.Hq + h) * a.Qmax + i] = wsum > 0.f ? muse + __logf(wsum) : NEG_INF;
   }
+}
+
+// Exclusive prefix of KV pages over the sequences, into ps[0..B] (ps[B] =
+// all pages), by the NT threads of a workgroup: each thread sums a contiguous
+// chunk of sequences, a wave scans its threads with shuffles, and the wave
+// totals (wave_tot, NT / 64 words of LDS) are added in front.
+template <int NT>
+__device__ __forceinline__ void page_prefix(const AttnArgs& a, int* ps, int* wave_tot, int tid) {
+  const int B = a.B;
+  const int chunk = (B + NT - 1) / NT;
+  const int lo = min(B, tid * chunk), hi = min(B, lo + chunk);
+  int s = 0;
+  for (int bb = lo; bb < hi; ++bb) s += (a.ctx[bb] + kPage - 1) / kPage;
+  const int lane = tid & 63, wv = tid >> 6;
+  int inc = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) wave_tot[wv] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int j = 0; j < wv; ++j) before += wave_tot[j];
+  int base = before + inc - s;
+  if (tid == NT - 1) ps[B] = before + inc;
+  for (int bb = lo; bb < hi; ++bb) {
+    ps[bb] = base;
+    base += (a.ctx[bb] + kPage - 1) / kPage;
+  }
+  __syncthreads();
 }
 
 struct PartSlot {

@@ -243,34 +243,47 @@ __device__ __forceinline__ int tile_off(int r, int u) {
 // S^T accumulators (P as a bf16 hi/lo pair) and the A operand is two
 // ds_read_b64_tr_b16 reads, one from each V tile.  A missing second page must
 // be presented with its V tile zeroed and its tokens at or past t1 (masked).
-template <int D, int RB, bool SWZ = false>
-__device__ __forceinline__ void pair_compute(const StreamRows<D, RB>& rows, StreamState<D, RB>& st,
-                                             const char* kl0, const char* kl1, const char* vl0,
-                                             const char* vl1, int pbase, int L, int t1, float c0,
-                                             float c1, float vs0, float vs1, int lane) {
-  constexpr int KK = D / 32, DB = D / 16, STR = 2 * D + 32;
-  constexpr float NEG_INF = -__builtin_huge_valf();
-  const int g = lane >> 4, m = lane & 15;
+//
+// The update is split in three phases so that a caller can issue the score
+// products of the next pair while this pair's softmax runs on the vector ALU:
+// pair_scores (matrix core), pair_softmax (masking, lazy max, rescale) and
+// pair_pv (P in bf16 hi/lo, O^T += V^T P^T).
+template <int RB>
+struct PairScores {
+  f32x4 s[2][RB];     // [page][row block]: lane holds tokens 4 g + r of the page, row m
+};
 
-  // S^T for both pages
-  f32x4 sacc[2][RB];
+template <int D, int RB, bool SWZ>
+__device__ __forceinline__ void pair_scores(const StreamRows<D, RB>& rows, PairScores<RB>& S,
+                                            const char* kl0, const char* kl1, int lane) {
+  constexpr int KK = D / 32;
+  const int g = lane >> 4, m = lane & 15;
 #pragma unroll
   for (int pg = 0; pg < 2; ++pg) {
     const char* kt = pg ? kl1 : kl0;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) sacc[pg][rb] = {};
+    for (int rb = 0; rb < RB; ++rb) S.s[pg][rb] = {};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kt + tile_off<D, SWZ>(m, 4 * kk + g));
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        sacc[pg][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, rows.qop[rb][kk], sacc[pg][rb], 0, 0, 0);
+        S.s[pg][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, rows.qop[rb][kk], S.s[pg][rb], 0, 0, 0);
     }
   }
+}
 
-  // scores in log2 units, mask by select, lazy reference-max update
+// Scores in log2 units (page scales c0, c1), masked by select, and the lazy
+// reference-max update with its rescale of O and l.  Rows a lane does not own
+// have zero queries, so their finite scores need no mask.
+template <int D, int RB>
+__device__ __forceinline__ void pair_softmax(const StreamRows<D, RB>& rows, StreamState<D, RB>& st,
+                                             const PairScores<RB>& S, float (&x)[RB][8], int pbase, int L,
+                                             int t1, float c0, float c1, int lane) {
+  constexpr int DB = D / 16;
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  const int g = lane >> 4;
   const bool plain = pbase + 2 * kPage <= min(L, t1);
-  float x[RB][8];
   bool need = false;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -278,14 +291,13 @@ __device__ __forceinline__ void pair_compute(const StreamRows<D, RB>& rows, Stre
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int pg = e >> 2, r = e & 3;
-      float v = sacc[pg][rb][r] * (pg ? c1 : c0);
+      float v = S.s[pg][rb][r] * (pg ? c1 : c0);
       if (!plain) {
         const int t = pbase + 16 * pg + 4 * g + r;
         const int sh = t - L;
         const bool cand = (unsigned)sh < 64u && ((rows.mbits[rb] >> (sh & 63)) & 1ull);
         v = (t < t1 && (t < L || cand)) ? v : NEG_INF;
       }
-      v = rows.ok[rb] ? v : NEG_INF;
       x[rb][e] = v;
       pm = fmaxf(pm, v);
     }
@@ -307,8 +319,16 @@ __device__ __forceinline__ void pair_compute(const StreamRows<D, RB>& rows, Stre
       for (int db = 0; db < DB; ++db) st.o[rb][db] *= alpha;
     }
   }
+}
 
-  // P as a bf16 hi/lo pair over the lane's 8 tokens; O^T += V^T P^T (k = 32 tokens)
+// P = 2^(x - m) as a bf16 hi/lo pair over the lane's 8 tokens (times the
+// pages' V scales vs0, vs1), then O^T += V^T P^T over the 32 tokens.
+template <int D, int RB, bool SWZ>
+__device__ __forceinline__ void pair_pv(StreamState<D, RB>& st, const float (&x)[RB][8], const char* vl0,
+                                        const char* vl1, float vs0, float vs1, int lane) {
+  constexpr int DB = D / 16;
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  const int g = lane >> 4, m = lane & 15;
   bf16x8 phi[RB], plo[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -345,6 +365,18 @@ __device__ __forceinline__ void pair_compute(const StreamRows<D, RB>& rows, Stre
     for (int rb = 0; rb < RB; ++rb)
       st.o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, plo[rb], st.o[rb][db], 0, 0, 0);
   }
+}
+
+template <int D, int RB, bool SWZ = false>
+__device__ __forceinline__ void pair_compute(const StreamRows<D, RB>& rows, StreamState<D, RB>& st,
+                                             const char* kl0, const char* kl1, const char* vl0,
+                                             const char* vl1, int pbase, int L, int t1, float c0,
+                                             float c1, float vs0, float vs1, int lane) {
+  PairScores<RB> S;
+  pair_scores<D, RB, SWZ>(rows, S, kl0, kl1, lane);
+  float x[RB][8];
+  pair_softmax<D, RB>(rows, st, S, x, pbase, L, t1, c0, c1, lane);
+  pair_pv<D, RB, SWZ>(st, x, vl0, vl1, vs0, vs1, lane);
 }
 
 // Row sums over the lane's four 16-lane groups (every group holds 4 of each

@@ -21,6 +21,11 @@ hipError_t stream_balanced(const AttnArgs* a, int kv_dtype, int head_dim, int rb
                            hipStream_t s);
 // Matrix-core shared-tile kernel (rows per KV head 33..256): nwr waves of 32 rows.
 hipError_t launch_tile(const AttnArgs& a, int kv_dtype, int head_dim, int nwr, dim3 grid, hipStream_t s);
+// Persistent work-balanced shared-tile kernel (bf16 KV, rows per KV head
+// 33..256): workgroups of nwr in {2, 4} waves, ceil(rows / (32 nwr)) row groups
+// per slice.  With a == nullptr, *nwg receives the workgroups that fit the
+// device at once; otherwise *nwg workgroups are launched.
+hipError_t tile_balanced(const AttnArgs* a, int head_dim, int nwr, int B, int* nwg, hipStream_t s);
 
 struct AppendArgs {
   const void* k_new;

@@ -238,7 +238,7 @@ template <typename KT, int D, int RB, int NW>
 __global__ __launch_bounds__(NW * 64) void stream_balanced_kernel(AttnArgs a) {
   using T = StreamTile<KT, D>;
   __shared__ __attribute__((aligned(16))) char vlds[NW][T::WAVE_LDS];
-  __shared__ int scan_tmp[NW * 64];
+  __shared__ int wave_tot[NW];
   extern __shared__ int ps[];       // [B + 1]
 
   const int tid = threadIdx.x;
@@ -249,31 +249,7 @@ __global__ __launch_bounds__(NW * 64) void stream_balanced_kernel(AttnArgs a) {
   const int HG = a.Hkv / NW;
 
   // ---- exclusive prefix of pages per sequence (every workgroup computes it)
-  {
-    constexpr int NT = NW * 64;
-    const int chunk = (B + NT - 1) / NT;
-    const int lo = min(B, tid * chunk), hi = min(B, lo + chunk);
-    int s = 0;
-    for (int bb = lo; bb < hi; ++bb) s += (a.ctx[bb] + kPage - 1) / kPage;
-    scan_tmp[tid] = s;
-    __syncthreads();
-    if (tid == 0) {
-      int run = 0;
-      for (int t = 0; t < NT; ++t) {
-        const int v = scan_tmp[t];
-        scan_tmp[t] = run;
-        run += v;
-      }
-      ps[B] = run;
-    }
-    __syncthreads();
-    int base = scan_tmp[tid];
-    for (int bb = lo; bb < hi; ++bb) {
-      ps[bb] = base;
-      base += (a.ctx[bb] + kPage - 1) / kPage;
-    }
-    __syncthreads();
-  }
+  page_prefix<NW * 64>(a, ps, wave_tot, tid);
   const int64_t W = (int64_t)HG * __builtin_amdgcn_readfirstlane(ps[B]);
   const int64_t N = min((int64_t)gridDim.x, max((int64_t)1, W / kMinSlicePages));
   const int64_t w = blockIdx.x;

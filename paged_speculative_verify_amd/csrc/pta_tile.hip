@@ -181,13 +181,15 @@ __global__ __launch_bounds__(NWR * 64) void tile_attn_kernel(AttnArgs a) {
 // bf16 page tiles need no conversion, so they go from HBM straight into LDS
 // with global_load_lds_dwordx4 (gfx950: 16 bytes per lane, the wave's 64
 // lanes fill 1 KiB of LDS at M0 + 16 * lane): no register staging, no VGPR
-// cost for bytes in flight.  Three LDS stage buffers give two stages of loads
-// in flight while one is computed, with one barrier per stage.
+// cost for bytes in flight.  Of NBUF LDS stage buffers one is read while a
+// page pair is computed and NBUF - 1 are in flight, with one barrier per
+// pair; NBUF is chosen per workgroup size to fill about 128 KiB of LDS per
+// compute unit, since HBM latency needs that much in flight.
 //
 // The copies are issued with inline asm so that the compiler, which would
 // otherwise wait for every outstanding copy before any LDS read, leaves the
 // waits to the kernel: before the barrier that opens stage s a wave waits
-// until only its copies of stage s + 1 remain in flight (vector memory
+// until only its copies of later stages remain in flight (vector memory
 // operations complete in issue order, so any compiler-issued load only makes
 // these waits longer, never too short).
 //
@@ -215,39 +217,47 @@ __device__ __forceinline__ void wait_vmem_at_most() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int D, int NWR>
-__global__ __launch_bounds__(NWR * 64) void tile_dma_kernel(AttnArgs a) {
+// Wait until at most k stages of CPW copies each are in flight (k <= K).
+template <int CPW, int K>
+__device__ __forceinline__ void wait_stages(int k) {
+  if constexpr (K == 0) {
+    wait_vmem_at_most<0>();
+  } else {
+    if (k >= K) wait_vmem_at_most<K * CPW>();
+    else wait_stages<CPW, K - 1>(k);
+  }
+}
+
+template <int D, int NWR, int NBUF>
+struct DmaGeom {
+  static constexpr int TILE = kPage * D * 2;                 // bf16 page tile, HBM and LDS
+  static constexpr int CPT = TILE / 1024;                    // 1 KiB copies per tile
+  static constexpr int CHUNKS = 4 * CPT;                     // K page 0, K page 1, V page 0, V page 1
+  static constexpr int CPW = (CHUNKS + NWR - 1) / NWR;       // copies per wave per stage
+  static constexpr int STAGE = 4 * TILE;
+  static constexpr int UPR = 2 * D / 16;                     // 16-byte units per row
+  static constexpr int RPC = 1024 / (2 * D);                 // rows per copy
+  static constexpr int LDS_BYTES = NBUF * STAGE;
+  static_assert(NBUF >= 2 && (NBUF - 2) * CPW < 64, "stages in flight exceed the vmcnt range");
+};
+
+// The 32-row blocks of one (sequence b, KV head hkv) over tokens [t0, t1):
+// wave w owns rows row0 + 32 w .. + 31 of the unit's M = G * q_b rows; every
+// wave takes part in the copies whether or not it owns rows.  On return st
+// holds the wave's unnormalised flash state; the LDS buffers may still be read
+// by other waves (the caller synchronises before reusing them).
+template <int D, int NWR, int NBUF>
+__device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t lds0, StreamRows<D, 2>& rows,
+                                          StreamState<D, 2>& st, int b, int hkv, int qb, int row0,
+                                          int t0, int t1, int wave, int lane) {
+  using Gm = DmaGeom<D, NWR, NBUF>;
   constexpr int RB = 2;
-  constexpr int TILE = kPage * D * 2;                        // bf16 page tile, HBM and LDS
-  constexpr int CPT = TILE / 1024;                           // 1 KiB copies per tile
-  constexpr int CHUNKS = 4 * CPT;                            // K page 0, K page 1, V page 0, V page 1
-  constexpr int CPW = (CHUNKS + NWR - 1) / NWR;              // copies per wave per stage
-  constexpr int STAGE = 4 * TILE;
-  constexpr int NBUF = 3;
-  constexpr int UPR = 2 * D / 16;                            // 16-byte units per row
-  constexpr int RPC = 1024 / (2 * D);                        // rows per copy
-  __shared__ __attribute__((aligned(1024))) char lds[NBUF][STAGE];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, m = lane & 15;
-  const int part = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
-
   const int C = a.ctx[b];
-  const int qb = a.qlen[b];
   const int L = C - qb;
   const int M = a.G * qb;
-  int t0 = 0, t1 = C;
-  if (a.part_tokens > 0) {
-    t0 = part * a.part_tokens;
-    t1 = min(C, t0 + a.part_tokens);
-    if (t0 >= t1) return;           // partition past this sequence's context
-  }
-  const bool split_out = unit_writes_partials(a, C);   // else: final output written directly
-
-  StreamState<D, RB> st;
-  st.init();
-  const bool wave_rows = wave * 32 < M;
+  const int wrow0 = row0 + wave * 32;
+  const bool wave_rows = wrow0 < M;
 
   const int32_t* table = a.tables + (int64_t)b * a.MBS;
   const char* kbase = reinterpret_cast<const char*>(a.k);
@@ -255,68 +265,107 @@ __global__ __launch_bounds__(NWR * 64) void tile_dma_kernel(AttnArgs a) {
   const int pgA = t0 / kPage;
   const int npg = (t1 + kPage - 1) / kPage - pgA;
   const int nst = (npg + 1) / 2;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&lds[0][0];
 
-  // this lane's slot in a copy: row RPC j + l / UPR, unit l % UPR, fetched from
-  // the swizzled unit of the global row
-  const int crow = lane / UPR, cunit = lane % UPR;
-  auto copy_stage = [&](int s) {
-    const int p0 = pgA + 2 * s;
-    const bool has1 = 2 * s + 1 < npg;
-    const int i1 = __builtin_amdgcn_readfirstlane(has1 ? p0 + 1 : p0);
-    int x0, x1;
-    scalar_pair(table + __builtin_amdgcn_readfirstlane(p0), table + i1, x0, x1);
-    const int64_t ph0 = x0, ph1 = x1;
-    const uint32_t dst = lds0 + (uint32_t)((s % NBUF) * STAGE);
+  // DMA stage j (j = -1 .. nst - 1) holds the K tiles of page pair j + 1 and
+  // the V tiles of pair j, in buffer (j + 1) % NBUF: iteration s reads one
+  // buffer (K for the scores of pair s + 1, V for the P.V of pair s) and the
+  // other NBUF - 1 buffers are all in flight.  Stage -1 carries K of pair 0
+  // (its V half repeats pair 0, unused) and stage nst - 1 repeats K of the
+  // last pair (its score products are dropped), so every stage moves the
+  // same number of chunks.  A missing second page of a pair repeats the first
+  // (its tokens are masked, its V rows zeroed).
+  const int crow = lane / Gm::UPR, cunit = lane % Gm::UPR;
+  auto copy_stage = [&](int j) {
+    const int kp = pgA + 2 * min(j + 1, nst - 1), vp = pgA + 2 * max(j, 0);
+    const int k1 = kp + 1 < pgA + npg ? kp + 1 : kp, v1 = vp + 1 < pgA + npg ? vp + 1 : vp;
+    int xk0, xk1, xv0, xv1;
+    scalar_pair(table + __builtin_amdgcn_readfirstlane(kp), table + __builtin_amdgcn_readfirstlane(k1), xk0, xk1);
+    scalar_pair(table + __builtin_amdgcn_readfirstlane(vp), table + __builtin_amdgcn_readfirstlane(v1), xv0, xv1);
+    const uint32_t dst = lds0 + (uint32_t)(((j + 1) % NBUF) * Gm::STAGE);
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
+    for (int i = 0; i < Gm::CPW; ++i) {
       int c = wave + i * NWR;
-      if constexpr (CHUNKS % NWR != 0) c %= CHUNKS;        // surplus waves repeat a copy
-      const int tile = c / CPT, j = c % CPT;
-      const int64_t ph = (tile & 1) ? ph1 : ph0;
-      const int r = RPC * j + crow;
-      const char* src = (tile < 2 ? kbase : vbase) + (ph * a.Hkv + hkv) * TILE + r * 2 * D +
-                        ((cunit ^ (r & (UPR - 1))) << 4);
-      lds_copy16(dst + (uint32_t)(tile * TILE + 1024 * j), src);
+      if constexpr (Gm::CHUNKS % NWR != 0) c %= Gm::CHUNKS;   // surplus waves repeat a copy
+      const int tile = c / Gm::CPT, jj = c % Gm::CPT;
+      const int64_t ph = tile == 0 ? xk0 : tile == 1 ? xk1 : tile == 2 ? xv0 : xv1;
+      const int r = Gm::RPC * jj + crow;
+      const char* src = (tile < 2 ? kbase : vbase) + (ph * a.Hkv + hkv) * Gm::TILE + r * 2 * D +
+                        ((cunit ^ (r & (Gm::UPR - 1))) << 4);
+      lds_copy16(dst + (uint32_t)(tile * Gm::TILE + 1024 * jj), src);
     }
   };
+  auto buf = [&](int j) { return lds + ((j + 1) % NBUF) * Gm::STAGE; };
 
-  // The query rows load behind the first two stages and everything lands
-  // before the loop, so no wait on the query registers sits inside it.
-  if (nst > 0) copy_stage(0);
-  if (nst > 1) copy_stage(1);
-  StreamRows<D, RB> rows;
-  load_rows(rows, a, b, hkv, qb, M, g, m, wave * 32);
+  // The query rows load behind the first stages and everything lands before
+  // the loop, so no wait on the query registers sits inside it.
+  const int pro = min(NBUF, nst + 1);                // stages -1 .. pro - 2
+  for (int j = -1; j < pro - 1; ++j) copy_stage(j);
+  load_rows(rows, a, b, hkv, qb, M, g, m, wrow0);
   wait_vmem_at_most<0>();
-  if (nst > 0) {
-    for (int s = 0; s < nst; ++s) {
-      if (s + 1 < nst) wait_vmem_at_most<CPW>();
-      else wait_vmem_at_most<0>();
-      __syncthreads();        // stage s in LDS for all waves; stage s - 1 fully consumed
-      char* sb = lds[s % NBUF];
-      if (s == nst - 1) {
-        // zero V rows past t1 in the last stage (and the whole V tile of a missing
-        // second page): their slots may hold anything, and 0 * NaN would leak
-        for (int pg = 0; pg < 2; ++pg) {
-          const int pbase = (pgA + 2 * s + pg) * kPage;
-          const int valid = max(0, min(kPage, t1 - pbase));
-          char* vt = sb + (2 + pg) * TILE;
-          for (int idx = threadIdx.x; idx < (kPage - valid) * UPR; idx += NWR * 64)
-            *reinterpret_cast<uint4*>(vt + (valid + idx / UPR) * 2 * D + (idx % UPR) * 16) =
-                make_uint4(0, 0, 0, 0);
-        }
-        __syncthreads();
+  __syncthreads();
+  // Software pipeline: iteration s runs the softmax and P.V of pair s while
+  // the score products of pair s + 1 go to the matrix core.
+  PairScores<RB> sc;
+  if (wave_rows) pair_scores<D, RB, true>(rows, sc, buf(-1), buf(-1) + Gm::TILE, lane);
+  for (int s = 0; s < nst; ++s) {
+    // masking and the lazy max of pair s need only its scores: they run on
+    // the vector ALU while the previous pair's P.V is still in the matrix core
+    float x[RB][8];
+    if (wave_rows)
+      pair_softmax<D, RB>(rows, st, sc, x, (pgA + 2 * s) * kPage, L, t1, a.scale_log2, a.scale_log2, lane);
+    wait_stages<Gm::CPW, NBUF - 2>(min(NBUF - 2, nst - 1 - s));
+    __syncthreads();        // stage s in LDS for all waves; stage s - 1 fully consumed
+    char* sb = buf(s);
+    if (s == nst - 1) {
+      // zero V rows past t1 in the last pair (and the whole V tile of a missing
+      // second page): their slots may hold anything, and 0 * NaN would leak
+      for (int pg = 0; pg < 2; ++pg) {
+        const int pbase = (pgA + 2 * s + pg) * kPage;
+        const int valid = max(0, min(kPage, t1 - pbase));
+        char* vt = sb + (2 + pg) * Gm::TILE;
+        for (int idx = threadIdx.x; idx < (kPage - valid) * Gm::UPR; idx += NWR * 64)
+          *reinterpret_cast<uint4*>(vt + (valid + idx / Gm::UPR) * 2 * D + (idx % Gm::UPR) * 16) =
+              make_uint4(0, 0, 0, 0);
       }
-      if (s + 2 < nst) copy_stage(s + 2);
-      if (wave_rows)
-        pair_compute<D, RB, true>(rows, st, sb, sb + TILE, sb + 2 * TILE, sb + 3 * TILE,
-                                  (pgA + 2 * s) * kPage, L, t1, a.scale_log2, a.scale_log2, 1.f, 1.f,
-                                  lane);
+      __syncthreads();
+    }
+    if (s + NBUF - 1 < nst) copy_stage(s + NBUF - 1);     // into the buffer stage s - 1 used
+    if (wave_rows) {
+      PairScores<RB> sn_sc;
+      pair_scores<D, RB, true>(rows, sn_sc, sb, sb + Gm::TILE, lane);
+      pair_pv<D, RB, true>(st, x, sb + 2 * Gm::TILE, sb + 3 * Gm::TILE, 1.f, 1.f, lane);
+      sc = sn_sc;
     }
   }
+  reduce_row_sums(st);
+}
+
+// Two waves per SIMD must fit: at most 256 VGPRs per wave.
+template <int D, int NWR, int NBUF>
+__global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) void tile_dma_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[DmaGeom<D, NWR, NBUF>::LDS_BYTES];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int part = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+
+  const int C = a.ctx[b];
+  const int qb = a.qlen[b];
+  int t0 = 0, t1 = C;
+  if (a.part_tokens > 0) {
+    t0 = part * a.part_tokens;
+    t1 = min(C, t0 + a.part_tokens);
+    if (t0 >= t1) return;           // partition past this sequence's context
+  }
+  const bool split_out = unit_writes_partials(a, C);   // else: final output written directly
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&lds[0];
+
+  StreamRows<D, 2> rows;
+  StreamState<D, 2> st;
+  st.init();
+  dma_range<D, NWR, NBUF>(a, lds, lds0, rows, st, b, hkv, qb, 0, t0, t1, wave, lane);
 
   // ---- epilogue: each wave owns its rows outright
-  reduce_row_sums(st);
   if (split_out) {
     auto addr = [&](int rb, float*& o, float*& l) {
       const int64_t prow = (((int64_t)b * a.Hq + rows.h[rb]) * a.Qmax + rows.i[rb]) * a.num_parts + part;
@@ -330,11 +379,123 @@ __global__ __launch_bounds__(NWR * 64) void tile_dma_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------ balanced tile grid
+// Persistent grid for many rows per KV head.  Unit u = b * Hkv + hkv owns
+// positions [S_u, S_u + P_b) of one page line (P_b = ceil(C_b / 16),
+// S_u = Hkv * PS_b + hkv * P_b with PS the exclusive prefix of P over the
+// sequences).  The line is cut into N equal slices; slice w is worked by RG
+// workgroups, one per row group of NWR waves * 32 rows, so every row of a
+// unit is covered.  The row groups of one slice are launched 8 workgroup ids
+// apart: workgroups are handed to the 8 XCDs in turn, so they share an XCD
+// and its L2, and the KV pages reach L2 from HBM once.  A slice that covers a
+// whole unit writes its rows; otherwise it stores a normalised partial in
+// slot w + u (unique: slices and units are both ordered along the line) and
+// the unit's last slice to arrive merges them in slice order.
+template <int D, int NWR, int NBUF>
+__global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) void tile_balanced_kernel(AttnArgs a) {
+  using Gm = DmaGeom<D, NWR, NBUF>;
+  __shared__ __attribute__((aligned(1024))) char lds[Gm::LDS_BYTES];
+  __shared__ int wave_tot[NWR];
+  __shared__ int s_last;
+  extern __shared__ int ps[];       // [B + 1]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, m = lane & 15;
+  const int B = a.B;
+  const int Rmax = a.G * a.Qmax;
+  const int RG = (Rmax + NWR * 32 - 1) / (NWR * 32);
+  const int blk = blockIdx.x;
+  const int rg = (blk >> 3) % RG;
+  const int64_t w = (int64_t)((blk >> 3) / RG) * 8 + (blk & 7);
+  const int64_t NS = gridDim.x / RG;
+
+  // ---- exclusive prefix of pages per sequence (every workgroup computes it)
+  page_prefix<NWR * 64>(a, ps, wave_tot, tid);
+  const int64_t W = (int64_t)a.Hkv * __builtin_amdgcn_readfirstlane(ps[B]);
+  const int64_t N = min(NS, max((int64_t)1, W / kMinSlicePages));
+  if (w >= N) return;
+  auto wg_of = [&](int64_t x) -> int64_t { return ((x + 1) * N - 1) / W; };
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&lds[0];
+  const int row0 = rg * NWR * 32;
+
+  int64_t x = w * W / N;
+  const int64_t xe = (w + 1) * W / N;
+  while (x < xe) {
+    // the unit holding position x: largest b with PS_b <= x / Hkv
+    const int key = (int)(x / a.Hkv);
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (__builtin_amdgcn_readfirstlane(ps[mid]) <= key) lo = mid;
+      else hi = mid - 1;
+    }
+    const int b = lo;
+    const int psb = __builtin_amdgcn_readfirstlane(ps[b]);
+    const int Pb = __builtin_amdgcn_readfirstlane(ps[b + 1]) - psb;
+    const int64_t off = x - (int64_t)a.Hkv * psb;
+    const int hkv = (int)(off / Pb);
+    const int k0 = (int)(off % Pb);
+    const int k1 = (int)min((int64_t)Pb, k0 + (xe - x));
+    const int u = b * a.Hkv + hkv;
+    const int C = a.ctx[b];
+    const int qb = a.qlen[b];
+    const int M = a.G * qb;
+
+    __syncthreads();          // LDS stage buffers and s_last free from the previous unit
+    StreamRows<D, 2> rows;
+    StreamState<D, 2> st;
+    st.init();
+    if (row0 < M)
+      dma_range<D, NWR, NBUF>(a, lds, lds0, rows, st, b, hkv, qb, row0, k0 * kPage,
+                              min(C, k1 * kPage), wave, lane);
+
+    if (row0 >= M) {
+      // no rows of this unit in this row group (shorter tree than the widest)
+    } else if (k0 == 0 && k1 == Pb) {
+      store_final_rows(a, rows, st, b, g);        // the whole unit in this slice
+    } else {
+      const int64_t S = (int64_t)a.Hkv * psb + (int64_t)hkv * Pb;
+      const int64_t wfirst = wg_of(S), wlast = wg_of(S + Pb - 1);
+      const int np = (int)(wlast - wfirst + 1);
+      auto addr = [&](int rb, float*& o, float*& l) {
+        const int64_t r = (w + u) * Rmax + row0 + wave * 32 + rb * 16 + m;
+        o = a.part_o + r * D;
+        l = a.part_lse + r;
+      };
+      store_partial_rows(rows, st, g, addr);
+      __builtin_amdgcn_s_waitcnt(0);             // partial stores complete before the arrival
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __syncthreads();
+      int32_t* cnt = a.counters + (int64_t)u * RG + rg;
+      if (tid == 0)
+        s_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
+      __syncthreads();
+      if (s_last) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        auto pslot = [&](int r, int p) {
+          const int64_t rr = (wfirst + p + u) * Rmax + r;
+          return PartSlot{a.part_o + rr * D, a.part_lse + rr};
+        };
+        merge_rows<BF16, D>(a, b, hkv, qb, min(M, row0 + NWR * 32), np, pslot, tid, NWR * 64, row0);
+        if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    x += k1 - k0;
+  }
+}
+
 // ---------------------------------------------------------------- launchers
+// Stage buffers per workgroup size: about 128 KiB of LDS per compute unit at
+// D = 128 (one 8-wave or two 4-wave workgroups).
+template <int NWR>
+constexpr int dma_bufs() { return NWR == 8 ? 8 : 4; }
+
 template <typename KT, int D, int NWR>
 static hipError_t launch_tile_t(const AttnArgs& a, dim3 grid, hipStream_t s) {
   if constexpr (KT::bytes == 2)
-    hipLaunchKernelGGL((tile_dma_kernel<D, NWR>), grid, dim3(NWR * 64), 0, s, a);
+    hipLaunchKernelGGL((tile_dma_kernel<D, NWR, dma_bufs<NWR>()>), grid, dim3(NWR * 64), 0, s, a);
   else
     hipLaunchKernelGGL((tile_attn_kernel<KT, D, NWR>), grid, dim3(NWR * 64), 0, s, a);
   return hipGetLastError();
@@ -357,6 +518,38 @@ hipError_t launch_tile(const AttnArgs& a, int kv_dtype, int D, int nwr, dim3 gri
   } else if (kv_dtype == 2) {
     if (D == 64) return launch_tile_d<FP8, 64>(a, nwr, grid, s);
     if (D == 128) return launch_tile_d<FP8, 128>(a, nwr, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Balanced tile grid.  With a == nullptr: report the workgroups that fit the
+// current device at once (compute units times occupancy).  Otherwise launch
+// *nwg workgroups.
+template <int D, int NWR>
+static hipError_t tile_balanced_t(const AttnArgs* a, int B, int* nwg, hipStream_t s) {
+  constexpr int NBUF = dma_bufs<NWR>();
+  const size_t dyn = (size_t)(B + 1) * sizeof(int);
+  if (a == nullptr) {
+    int dev = 0, cus = 0, per = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, tile_balanced_kernel<D, NWR, NBUF>, NWR * 64, dyn);
+    if (e != hipSuccess) return e;
+    *nwg = cus * (per > 0 ? per : 1);
+    return hipSuccess;
+  }
+  hipLaunchKernelGGL((tile_balanced_kernel<D, NWR, NBUF>), dim3((unsigned)*nwg), dim3(NWR * 64), dyn, s, *a);
+  return hipGetLastError();
+}
+
+hipError_t tile_balanced(const AttnArgs* a, int D, int nwr, int B, int* nwg, hipStream_t s) {
+  if (D == 64) {
+    if (nwr == 2) return tile_balanced_t<64, 2>(a, B, nwg, s);
+    if (nwr == 4) return tile_balanced_t<64, 4>(a, B, nwg, s);
+  } else if (D == 128) {
+    if (nwr == 2) return tile_balanced_t<128, 2>(a, B, nwg, s);
+    if (nwr == 4) return tile_balanced_t<128, 4>(a, B, nwg, s);
   }
   return hipErrorInvalidValue;
 }

@@ -126,6 +126,11 @@ CASES = [
     ("fp8_d64_tree", spec("f", 4, 16, 2, 64, "bf16", "fp8", (5, 400), 6, "random", seed=13), None, "auto"),
     ("gqa1_tree64", spec("w", 2, 4, 4, 128, "bf16", "bf16", (64, 400), 64, "random", seed=14), None, "mfma"),
     ("flat_forest", spec("ff", 3, 16, 2, 128, "bf16", "bf16", (10, 200), 10, "flat", seed=15), None, "auto"),
+    # the shared-tile family forced for small row counts
+    ("decode_bf16_tile", spec("d", 6, 32, 8, 128, "bf16", "bf16", (1, 700), 1, "chain", seed=1), None, "tile"),
+    ("decode_bf16_tile_split", spec("d", 6, 32, 8, 128, "bf16", "bf16", (100, 3000), 1, "chain", seed=3), 256, "tile"),
+    ("decode_d64_tile", spec("d", 5, 8, 2, 64, "bf16", "bf16", (3, 300), 1, "chain", seed=2), None, "tile"),
+    ("fp8_chain8_tile", spec("f", 6, 32, 8, 128, "bf16", "fp8", (8, 1500), 8, "chain", seed=11), None, "tile"),
 ]
 
 
@@ -380,6 +385,14 @@ BALANCED = [
     ("bal_fp8_d64", spec("b", 4, 8, 2, 64, "bf16", "fp8", (3, 1200), 6, "random", seed=106)),
     ("bal_tiny_units", spec("b", 40, 8, 2, 128, "bf16", "bf16", (1, 20), 1, "chain", seed=107)),
     ("bal_one_seq", spec("b", 1, 8, 1, 128, "bf16", "bf16", (30000, 30000), 2, "chain", seed=108)),
+    # shared-tile family (more than 32 rows per KV head, bf16 KV)
+    ("bal_tile_tree16", spec("bt", 5, 64, 8, 128, "bf16", "bf16", (16, 3000), 16, "random", 6, seed=121)),
+    ("bal_tile_tree32_rg2", spec("bt", 2, 64, 8, 128, "bf16", "bf16", (300, 9000), 32, "random", 8, seed=122)),
+    ("bal_tile_ragged_rg2", spec("bt", 6, 32, 4, 128, "bf16", "bf16", (1, 2500), 32, "random", ragged=True,
+                                 seed=123)),
+    ("bal_tile_d64", spec("bt", 5, 16, 4, 64, "bf16", "bf16", (1, 1800), 20, "random", ragged=True, seed=124)),
+    ("bal_tile_rows48", spec("bt", 6, 8, 2, 128, "bf16", "bf16", (12, 2200), 12, "random", seed=125)),
+    ("bal_tile_tiny_units", spec("bt", 50, 16, 2, 128, "bf16", "bf16", (8, 40), 8, "chain", seed=126)),
 ]
 
 
@@ -423,8 +436,45 @@ def test_balanced_rejects_unserved_dims(torch_cuda):
     with pytest.raises(psv.PtaError):
         psv.taco_paged_tree_attn_balanced(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
                                           d.q_lens, d.tree_mask, d.scale, max_ctx_len=d.max_ctx_len)
-    w = make(spec("x", 2, 64, 8, 128, "bf16", "bf16", (20, 100), 16, "random", seed=112))   # 128 rows
+    w = make(spec("x", 2, 64, 8, 128, "bf16", "fp8", (20, 100), 16, "random", seed=112))   # 128 rows, fp8
     d = to_device(w)
     with pytest.raises(psv.PtaError):
         psv.taco_paged_tree_attn_balanced(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
-                                          d.q_lens, d.tree_mask, d.scale, max_ctx_len=d.max_ctx_len)
+                                          d.q_lens, d.tree_mask, d.scale, k_scale=d.k_scale,
+                                          v_scale=d.v_scale, max_ctx_len=d.max_ctx_len)
+
+
+def test_balanced_tile_repeat_and_workspace_reuse(torch_cuda):
+    """Shared-tile balanced grid with two row groups: repeated calls on one workspace are
+    bit-identical, unchanged by a relabelling of physical pages, and leave every arrival
+    counter (one per unit and row group) at zero."""
+    import torch
+    import paged_speculative_verify_amd as psv
+    w = make(spec("rt", 3, 64, 8, 128, "bf16", "bf16", (500, 12000), 32, "random", 8, seed=131))
+    d = to_device(w)
+    need = psv.taco_paged_tree_attn_balanced_workspace_size(d.q, d.k_cache, d.block_tables,
+                                                            max_ctx_len=d.max_ctx_len)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    say("balanced tile repeat, workspace", need)
+    a1, l1 = run_gpu(torch_cuda, w, mode="balanced", workspace=ws)
+    a2, l2 = run_gpu(torch_cuda, w, mode="balanced", workspace=ws)
+    b1, m1 = run_gpu(torch_cuda, permute_pool(w, 9), mode="balanced", workspace=ws)
+    assert np.array_equal(a1, a2, equal_nan=True) and np.array_equal(l1, l2, equal_nan=True)
+    assert np.array_equal(a1, b1, equal_nan=True) and np.array_equal(l1, m1, equal_nan=True)
+    U = w.q.shape[0] * w.k_cache.shape[1] * 2
+    assert int(ws[:4 * U].view(torch.int32).abs().sum()) == 0, "arrival counters not reset"
+    ref, ref_lse = run_oracle(w)
+    assert_parity(w, a1, l1, ref, ref_lse)
+
+
+@pytest.mark.parametrize("cid,sp", [
+    ("bal_decode_tile", spec("bd", 9, 32, 8, 128, "bf16", "bf16", (1, 2500), 1, "chain", seed=141)),
+    ("bal_chain8_tile", spec("bd", 6, 32, 8, 128, "bf16", "bf16", (8, 3000), 8, "chain", seed=142)),
+], ids=["bal_decode_tile", "bal_chain8_tile"])
+def test_balanced_tile_path_small_rows(torch_cuda, cid, sp):
+    w = make(sp, poison=True)
+    say(cid, "B", w.q.shape[0], "ctx", w.ctx_lens.tolist()[:8], "q", sp.q_len)
+    out, lse = run_gpu(torch_cuda, w, mode="balanced", path="tile")
+    ref, ref_lse = run_oracle(w)
+    err = assert_parity(w, out, lse, ref, ref_lse)
+    say(cid, "max abs err", err)
