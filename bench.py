@@ -38,8 +38,8 @@ HEADLINE = "llama3_8b_decode"
 LAUNCH = {
     "tiny_decode": dict(mode="whole", split=None, path="auto"),
     "llama3_8b_decode": dict(mode="whole", split=None, path="auto"),
-    "llama31_70b_verify": dict(mode="split", split=1024, path="auto"),
-    "long_splitk_verify": dict(mode="split", split=2048, path="auto"),
+    "llama31_70b_verify": dict(mode="balanced", split=None, path="auto"),
+    "long_splitk_verify": dict(mode="balanced", split=None, path="auto"),
     "fp8_kv_chain": dict(mode="whole", split=None, path="auto"),
 }
 

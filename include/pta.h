@@ -128,7 +128,8 @@ size_t taco_paged_tree_attn_splitk_workspace_size(const pta_dims* dims, int32_t 
  * combined).  The merge reads partitions in index order, so results do not
  * depend on scheduling.  Arguments otherwise as taco_paged_tree_attn.
  *
- * workspace: caller-owned device memory of at least workspace_bytes >=
+ * workspace: caller-owned device memory, 256-byte aligned (else
+ * PTA_ERR_BAD_DIMS), of at least workspace_bytes >=
  * taco_paged_tree_attn_splitk_workspace_size(dims, partition_tokens).  Its
  * first region (num_seqs * num_kv_heads int32 arrival counters, padded to 256
  * bytes) must be zero before the first call that uses this workspace (e.g. a
@@ -157,12 +158,16 @@ size_t taco_paged_tree_attn_balanced_workspace_size(const pta_dims* dims);
  * A slice holding a whole unit writes its rows directly; a slice that ends
  * inside a unit writes a normalised partial and log-sum-exp, and the unit's
  * last slice to finish merges the unit's partials in order inside the same
- * launch.  Served for bf16 q with G * max_q_len <= 32 rows per KV head (the
- * matrix-core streaming path) and num_seqs <= 16383; otherwise
- * PTA_ERR_UNSUPPORTED.  Arguments as taco_paged_tree_attn; workspace as for
- * taco_paged_tree_attn_splitk (caller-owned, counter region zero before first
- * use and left zero, no sharing between concurrent calls) with
- * workspace_bytes >= taco_paged_tree_attn_balanced_workspace_size(dims). */
+ * launch.  Served for bf16 q with num_seqs <= 16383 and either G * max_q_len
+ * <= 32 rows per KV head (the matrix-core streaming path, one wave per KV head
+ * of a group of adjacent heads) or, with bf16 KV, up to 256 rows (the
+ * shared-tile path: one workgroup per row group of up to 128 rows per slice;
+ * also chosen for fewer rows by path PTA_PATH_TILE); otherwise
+ * PTA_ERR_UNSUPPORTED.  The counter region then holds one word per unit and
+ * row group.  Arguments as taco_paged_tree_attn; workspace as for
+ * taco_paged_tree_attn_splitk (caller-owned, 256-byte aligned, counter region
+ * zero before first use and left zero, no sharing between concurrent calls)
+ * with workspace_bytes >= taco_paged_tree_attn_balanced_workspace_size(dims). */
 pta_status taco_paged_tree_attn_balanced(const pta_dims* dims, const void* q, const void* k_cache,
                                          const void* v_cache, const float* k_scale,
                                          const float* v_scale, const int32_t* block_tables,

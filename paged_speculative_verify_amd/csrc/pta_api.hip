@@ -273,6 +273,7 @@ pta_status taco_paged_tree_attn_splitk(const pta_dims* d, const void* q, const v
                        tree_mask, out);
   if (st != PTA_OK) return st;
   if (workspace == nullptr) return PTA_ERR_NULL_PTR;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return PTA_ERR_BAD_DIMS;
   if (workspace_bytes < L.total) return PTA_ERR_WORKSPACE_TOO_SMALL;
   AttnArgs a = make_args(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
                          tree_mask, scale, out, lse);
@@ -312,6 +313,7 @@ pta_status taco_paged_tree_attn_balanced(const pta_dims* d, const void* q, const
                        tree_mask, out);
   if (st != PTA_OK) return st;
   if (workspace == nullptr) return PTA_ERR_NULL_PTR;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return PTA_ERR_BAD_DIMS;
   BalancedLayout L;
   st = balanced_layout(d, p, &L);
   if (st != PTA_OK) return st;

@@ -141,6 +141,15 @@ __device__ __forceinline__ uint64_t load_mask_row(const uint8_t* mask, int b, in
 __device__ __forceinline__ void store_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Four consecutive words (16-byte aligned) with one device-coherent store: the
+// same write-through as store_coherent, but a whole 16-byte piece per lane,
+// so the memory side sees full sectors instead of one partial write per word.
+// A store of more than 8 bytes reads its data registers after issue, so a
+// vector ALU write to them needs a wait state first; the compiler inserts none
+// after inline asm, hence the s_nop.
+__device__ __forceinline__ void store_coherent4(float* p, f32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(p), "v"(v) : "memory");
+}
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

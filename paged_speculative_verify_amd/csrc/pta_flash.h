@@ -433,9 +433,7 @@ __device__ __forceinline__ void store_partial_rows(const StreamRows<D, RB>& rows
     float* l;
     row_addr(rb, o, l);
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) store_coherent(o + 16 * db + 4 * g + e, st.o[rb][db][e] * inv);
+    for (int db = 0; db < D / 16; ++db) store_coherent4(o + 16 * db + 4 * g, st.o[rb][db] * inv);
     if (g == 0) store_coherent(l, lse);
   }
 }

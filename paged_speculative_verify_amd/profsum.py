@@ -36,7 +36,7 @@ KERNEL_SOURCES = ["pta_device.h", "pta_flash.h", "pta_launch.h", "pta_valu.hip",
                   "pta_tile.hip", "pta_aux.hip", "pta_api.hip"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30                      # bench.py --copy-calibration copies 1 GiB
-ATTN_KERNELS = ("stream_attn_kernel", "stream_balanced_kernel", "tile_dma_kernel",
+ATTN_KERNELS = ("stream_attn_kernel", "stream_balanced_kernel", "tile_dma_kernel", "tile_balanced_kernel",
                 "tile_attn_kernel", "valu_attn_kernel")
 
 
