@@ -155,9 +155,8 @@ bool split_layout(const pta_dims* d, int32_t T, SplitLayout* L) {
 
 // Balanced mode: [counters int32 | partial O float S*Mmax*D | partial LSE float S*Mmax]
 // with Mmax = G * max_q_len rows per slot.
-//   stream family: counters B*Hkv, S = (workgroups + B*Hkv/nw) * nw partial slots;
-//     nw = waves per workgroup = the head group (largest of 8, 4, 2, 1 dividing Hkv;
-//     at most 4 for two 16-row blocks).
+//   stream family: counters B*Hkv, S = workgroups * nw + B*Hkv partial slots (one slice
+//     per wave, nw = 4 waves per workgroup).
 //   tile family (bf16 KV): nw waves of 32 rows per workgroup (2 or 4), rg row groups per
 //     slice, ns slices (a multiple of 8 with ns * rg workgroups fitting the device at
 //     once); counters B*Hkv*rg, S = ns + B*Hkv slots.
@@ -166,11 +165,6 @@ struct BalancedLayout {
   size_t o_off, lse_off, total;
 };
 
-int head_group(int hkv, int rb) {
-  for (int nw = rb == 1 ? 8 : 4; nw > 1; nw >>= 1)
-    if (hkv % nw == 0) return nw;
-  return 1;
-}
 
 constexpr int kBalancedMaxSeqs = 16383;   // sequence page prefix lives in LDS
 
@@ -202,7 +196,7 @@ pta_status balanced_layout(const pta_dims* d, const Plan& p, BalancedLayout* L) 
     return PTA_ERR_UNSUPPORTED;
   if (p.fam == FAM_TILE && d->kv_dtype == PTA_BF16) return tile_balanced_layout(d, L);
   if (p.fam != FAM_STREAM) return PTA_ERR_UNSUPPORTED;
-  const int nw = head_group(d->num_kv_heads, p.rb);
+  const int nw = 4;                                   // waves per workgroup, one slice each
   int nwg = 0;
   if (stream_balanced(nullptr, d->kv_dtype, d->head_dim, p.rb, nw, d->num_seqs, &nwg, nullptr) != hipSuccess)
     return PTA_ERR_HIP;

@@ -13,10 +13,10 @@ hipError_t launch_valu(const AttnArgs& a, int q_dtype, int kv_dtype, int head_di
                        dim3 grid, hipStream_t s);
 hipError_t launch_stream(const AttnArgs& a, int kv_dtype, int head_dim, int rb, int nw, dim3 grid,
                          hipStream_t s);
-// Persistent work-balanced matrix-core stream kernel (rows per KV head <= 32),
-// one wave per KV head of a group of nw adjacent heads (nw in {1, 2, 4, 8},
-// dividing num_kv_heads).  With a == nullptr, *nwg receives the grid size
-// (workgroups) for the current device; otherwise *nwg workgroups are launched.
+// Persistent work-balanced matrix-core stream kernel (rows per KV head <= 32):
+// workgroups of nw = 4 waves, one page slice per wave.  With a == nullptr, *nwg
+// receives the grid size (workgroups) for the current device; otherwise *nwg
+// workgroups are launched.
 hipError_t stream_balanced(const AttnArgs* a, int kv_dtype, int head_dim, int rb, int nw, int B, int* nwg,
                            hipStream_t s);
 // Matrix-core shared-tile kernel (rows per KV head 33..256): nwr waves of 32 rows.
