@@ -40,7 +40,7 @@ LAUNCH = {
     "llama3_8b_decode": dict(mode="whole", split=None, path="auto"),
     "llama31_70b_verify": dict(mode="balanced", split=None, path="auto"),
     "long_splitk_verify": dict(mode="balanced", split=None, path="auto"),
-    "fp8_kv_chain": dict(mode="whole", split=None, path="auto"),
+    "fp8_kv_chain": dict(mode="balanced", split=None, path="auto"),
 }
 
 

@@ -202,6 +202,12 @@ __device__ __forceinline__ void lds_copy16(uint32_t lds_addr, const void* gptr) 
                : "memory", "m0");
 }
 
+// One dword per lane from HBM into LDS at M0 + 4 * lane.
+__device__ __forceinline__ void lds_copy4(uint32_t lds_addr, const void* gptr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" : : "s"(lds_addr), "v"(gptr)
+               : "memory", "m0");
+}
+
 // Two block-table entries through the scalar cache. The copies above are
 // opaque to the compiler, so a table read it schedules as a vector load would
 // be followed by a wait for every copy in flight; a scalar read waits only
@@ -247,9 +253,10 @@ struct DmaGeom {
 // holds the wave's unnormalised flash state; the LDS buffers may still be read
 // by other waves (the caller synchronises before reusing them).
 template <int D, int NWR, int NBUF>
-__device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t lds0, StreamRows<D, 2>& rows,
-                                          StreamState<D, 2>& st, int b, int hkv, int qb, int row0,
-                                          int t0, int t1, int wave, int lane) {
+__device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t lds0, const int* tring,
+                                          uint32_t tring0, StreamRows<D, 2>& rows, StreamState<D, 2>& st,
+                                          int b, int hkv, int qb, int row0, int t0, int t1, int wave,
+                                          int lane) {
   using Gm = DmaGeom<D, NWR, NBUF>;
   constexpr int RB = 2;
   const int g = lane >> 4, m = lane & 15;
@@ -274,13 +281,39 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
   // last pair (its score products are dropped), so every stage moves the
   // same number of chunks.  A missing second page of a pair repeats the first
   // (its tokens are masked, its V rows zeroed).
+  //
+  // Block-table entries of the range are staged in an LDS ring of kRing
+  // entries (relative page e at tring[e % kRing]), 64 entries per dword DMA
+  // issued by wave 0: chunks 0..3 before the loop, chunk c in the iteration
+  // where the copies have just left chunk c - 4 behind, about 90 iterations
+  // before its first use.  Stage copies in the loop then read their four
+  // entries from LDS instead of waiting on the scalar cache.  The first stages
+  // read the table through the scalar cache.
+  constexpr int kRing = 256;
+  const int nch = (npg + 63) / 64;
+  auto issue_chunk = [&](int c) {
+    const int e = min(64 * c + lane, npg - 1);            // clamped: stays inside the range
+    lds_copy4(tring0 + (uint32_t)((c & 3) * 256), table + pgA + e);
+  };
   const int crow = lane / Gm::UPR, cunit = lane % Gm::UPR;
-  auto copy_stage = [&](int j) {
-    const int kp = pgA + 2 * min(j + 1, nst - 1), vp = pgA + 2 * max(j, 0);
-    const int k1 = kp + 1 < pgA + npg ? kp + 1 : kp, v1 = vp + 1 < pgA + npg ? vp + 1 : vp;
+  auto copy_stage = [&](int j, bool ring) {
+    const int kr = 2 * min(j + 1, nst - 1), vr = 2 * max(j, 0);      // relative pages
+    const bool k2 = kr + 1 < npg, v2 = vr + 1 < npg;
     int xk0, xk1, xv0, xv1;
-    scalar_pair(table + __builtin_amdgcn_readfirstlane(kp), table + __builtin_amdgcn_readfirstlane(k1), xk0, xk1);
-    scalar_pair(table + __builtin_amdgcn_readfirstlane(vp), table + __builtin_amdgcn_readfirstlane(v1), xv0, xv1);
+    if (ring) {
+      const int2 kk = *reinterpret_cast<const int2*>(tring + (kr & (kRing - 1)));
+      const int2 vv = *reinterpret_cast<const int2*>(tring + (vr & (kRing - 1)));
+      xk0 = __builtin_amdgcn_readfirstlane(kk.x);
+      xk1 = __builtin_amdgcn_readfirstlane(k2 ? kk.y : kk.x);
+      xv0 = __builtin_amdgcn_readfirstlane(vv.x);
+      xv1 = __builtin_amdgcn_readfirstlane(v2 ? vv.y : vv.x);
+    } else {
+      const int kp = pgA + kr, vp = pgA + vr;
+      scalar_pair(table + __builtin_amdgcn_readfirstlane(kp),
+                  table + __builtin_amdgcn_readfirstlane(k2 ? kp + 1 : kp), xk0, xk1);
+      scalar_pair(table + __builtin_amdgcn_readfirstlane(vp),
+                  table + __builtin_amdgcn_readfirstlane(v2 ? vp + 1 : vp), xv0, xv1);
+    }
     const uint32_t dst = lds0 + (uint32_t)(((j + 1) % NBUF) * Gm::STAGE);
 #pragma unroll
     for (int i = 0; i < Gm::CPW; ++i) {
@@ -299,7 +332,9 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
   // The query rows load behind the first stages and everything lands before
   // the loop, so no wait on the query registers sits inside it.
   const int pro = min(NBUF, nst + 1);                // stages -1 .. pro - 2
-  for (int j = -1; j < pro - 1; ++j) copy_stage(j);
+  if (wave == 0)
+    for (int c = 0; c < min(4, nch); ++c) issue_chunk(c);
+  for (int j = -1; j < pro - 1; ++j) copy_stage(j, false);
   load_rows(rows, a, b, hkv, qb, M, g, m, wrow0);
   wait_vmem_at_most<0>();
   __syncthreads();
@@ -329,7 +364,11 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
       }
       __syncthreads();
     }
-    if (s + NBUF - 1 < nst) copy_stage(s + NBUF - 1);     // into the buffer stage s - 1 used
+    if ((s + NBUF - 1) % 32 == 0 && wave == 0) {
+      const int c = (s + NBUF - 1) / 32 + 3;
+      if (c < nch) issue_chunk(c);
+    }
+    if (s + NBUF - 1 < nst) copy_stage(s + NBUF - 1, true);     // into the buffer stage s - 1 used
     if (wave_rows) {
       PairScores<RB> sn_sc;
       pair_scores<D, RB, true>(rows, sn_sc, sb, sb + Gm::TILE, lane);
@@ -344,6 +383,7 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
 template <int D, int NWR, int NBUF>
 __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) void tile_dma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[DmaGeom<D, NWR, NBUF>::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) int tring[256];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
@@ -359,11 +399,12 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   const bool split_out = unit_writes_partials(a, C);   // else: final output written directly
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&lds[0];
+  const uint32_t tring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)&tring[0];
 
   StreamRows<D, 2> rows;
   StreamState<D, 2> st;
   st.init();
-  dma_range<D, NWR, NBUF>(a, lds, lds0, rows, st, b, hkv, qb, 0, t0, t1, wave, lane);
+  dma_range<D, NWR, NBUF>(a, lds, lds0, tring, tring0, rows, st, b, hkv, qb, 0, t0, t1, wave, lane);
 
   // ---- epilogue: each wave owns its rows outright
   if (split_out) {
@@ -395,6 +436,7 @@ template <int D, int NWR, int NBUF>
 __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) void tile_balanced_kernel(AttnArgs a) {
   using Gm = DmaGeom<D, NWR, NBUF>;
   __shared__ __attribute__((aligned(1024))) char lds[Gm::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) int tring[256];
   __shared__ int wave_tot[NWR];
   __shared__ int s_last;
   extern __shared__ int ps[];       // [B + 1]
@@ -418,6 +460,7 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   if (w >= N) return;
   auto wg_of = [&](int64_t x) -> int64_t { return ((x + 1) * N - 1) / W; };
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&lds[0];
+  const uint32_t tring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)&tring[0];
   const int row0 = rg * NWR * 32;
 
   int64_t x = w * W / N;
@@ -448,7 +491,7 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     StreamState<D, 2> st;
     st.init();
     if (row0 < M)
-      dma_range<D, NWR, NBUF>(a, lds, lds0, rows, st, b, hkv, qb, row0, k0 * kPage,
+      dma_range<D, NWR, NBUF>(a, lds, lds0, tring, tring0, rows, st, b, hkv, qb, row0, k0 * kPage,
                               min(C, k1 * kPage), wave, lane);
 
     if (row0 >= M) {
