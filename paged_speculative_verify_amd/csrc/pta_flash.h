@@ -259,16 +259,18 @@ __device__ __forceinline__ void pair_scores(const StreamRows<D, RB>& rows, PairS
   constexpr int KK = D / 32;
   const int g = lane >> 4, m = lane & 15;
 #pragma unroll
-  for (int pg = 0; pg < 2; ++pg) {
-    const char* kt = pg ? kl1 : kl0;
+  for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) S.s[pg][rb] = {};
+  // 2 * RB independent accumulation chains, interleaved
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kt + tile_off<D, SWZ>(m, 4 * kk + g));
+  for (int kk = 0; kk < KK; ++kk) {
+    const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kl0 + tile_off<D, SWZ>(m, 4 * kk + g));
+    const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kl1 + tile_off<D, SWZ>(m, 4 * kk + g));
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        S.s[pg][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, rows.qop[rb][kk], S.s[pg][rb], 0, 0, 0);
+    for (int rb = 0; rb < RB; ++rb) {
+      S.s[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, rows.qop[rb][kk], S.s[0][rb], 0, 0, 0);
+      S.s[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, rows.qop[rb][kk], S.s[1][rb], 0, 0, 0);
     }
   }
 }
@@ -349,21 +351,31 @@ __device__ __forceinline__ void pair_pv(StreamState<D, RB>& st, const float (&x)
     plo[rb] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
   }
   const int vrow = 4 * g + (m >> 2);
+  // two output blocks at a time: the hi and lo products of one accumulator are
+  // 2 * RB instructions apart
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const int voff = tile_off<D, SWZ>(vrow, 2 * db + ((m & 3) >> 1)) + 8 * (m & 1);
-    const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl0 + voff));
-    const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl1 + voff));
-    const bf16x8 vt = __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint2, va).x,
-                                                           __builtin_bit_cast(uint2, va).y,
-                                                           __builtin_bit_cast(uint2, vb).x,
-                                                           __builtin_bit_cast(uint2, vb).y));
+  for (int db = 0; db < DB; db += 2) {
+    bf16x8 vt[2];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      st.o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi[rb], st.o[rb][db], 0, 0, 0);
+    for (int e = 0; e < 2; ++e) {
+      const int voff = tile_off<D, SWZ>(vrow, 2 * (db + e) + ((m & 3) >> 1)) + 8 * (m & 1);
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl0 + voff));
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl1 + voff));
+      vt[e] = __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint2, va).x,
+                                                   __builtin_bit_cast(uint2, va).y,
+                                                   __builtin_bit_cast(uint2, vb).x,
+                                                   __builtin_bit_cast(uint2, vb).y));
+    }
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      st.o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, plo[rb], st.o[rb][db], 0, 0, 0);
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        st.o[rb][db + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[e], phi[rb], st.o[rb][db + e], 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        st.o[rb][db + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[e], plo[rb], st.o[rb][db + e], 0, 0, 0);
   }
 }
 

@@ -126,6 +126,9 @@ CASES = [
     ("fp8_d64_tree", spec("f", 4, 16, 2, 64, "bf16", "fp8", (5, 400), 6, "random", seed=13), None, "auto"),
     ("gqa1_tree64", spec("w", 2, 4, 4, 128, "bf16", "bf16", (64, 400), 64, "random", seed=14), None, "mfma"),
     ("flat_forest", spec("ff", 3, 16, 2, 128, "bf16", "bf16", (10, 200), 10, "flat", seed=15), None, "auto"),
+    # whole ranges of more than 256 pages: the block-table ring is refilled in the loop
+    ("long_tree32_whole", spec("lw", 2, 64, 8, 128, "bf16", "bf16", (5000, 9000), 32, "random", 8, seed=16), None, "auto"),
+    ("long_tree16_split8192", spec("lw", 3, 64, 8, 128, "bf16", "bf16", (9000, 12000), 16, "random", 6, seed=17), 8192, "auto"),
     # the shared-tile family forced for small row counts
     ("decode_bf16_tile", spec("d", 6, 32, 8, 128, "bf16", "bf16", (1, 700), 1, "chain", seed=1), None, "tile"),
     ("decode_bf16_tile_split", spec("d", 6, 32, 8, 128, "bf16", "bf16", (100, 3000), 1, "chain", seed=3), 256, "tile"),
