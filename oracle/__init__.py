@@ -22,4 +22,5 @@ from .attention import (  # noqa: F401
     merge_partials,
 )
 from .kv_append import kv_append  # noqa: F401
+from .accept import accept_commit, accept_path, tree_parents  # noqa: F401
 from .roofline import decode_io_compute_ms, lookahead_speedup  # noqa: F401
