@@ -192,6 +192,39 @@ pta_status taco_kv_append(const pta_dims* dims, const void* k_new, const void* v
                           void* k_cache, void* v_cache, const float* k_scale,
                           const float* v_scale, void* stream);
 
+/* Acceptance and commit after a verify step (the step to the right of the
+ * attention: the target model's prediction at each candidate decides which
+ * candidates are kept, design talk section on Lookahead Decoding; several
+ * tokens are generated per step, "2. 加速上限分析").  Greedy rule, per sequence:
+ * parent(i) = the largest j < i with tree_mask[b][i][j] != 0 (-1: root); a
+ * root is accepted iff cand_tokens[b][i] == target_prev[b]; another node iff
+ * its parent is accepted and cand_tokens[b][i] == target_tokens[b][parent].
+ * The committed path is the accepted node of greatest depth (lowest index
+ * among equals) with its ancestors, in increasing index order.  Its K/V rows
+ * move from logical position L + path[k] to L + k (L = ctx_lens[b] -
+ * q_lens[b]) for every KV head, one entry after the other; fp8 rows are copied
+ * when the source and destination (block, head) scales are equal, else
+ * re-encoded as RNE_sat(value * s_src / s_dst) in float32.
+ *   cand_tokens, target_tokens  [num_seqs][max_q_len] int32 (rows past q_lens ignored)
+ *   target_prev   [num_seqs] int32: the prediction after the committed prefix
+ *   ctx_lens, q_lens, tree_mask, block_tables: as for the attention call (read only)
+ *   k_cache, v_cache (+ k_scale, v_scale for fp8): updated in place
+ *   n_accepted    [num_seqs] int32 out: path length (0 when no root matches)
+ *   accepted_path [num_seqs][max_q_len] int32 out: node indices, -1 after the path
+ *   bonus_tokens  [num_seqs] int32 out: target_tokens at the path's last node,
+ *                 or target_prev when the path is empty
+ *   new_ctx_lens  [num_seqs] int32 out: L + n_accepted.  Cache rows past it are
+ *                 untouched; blocks from ceil(new_ctx / page_size) on are free.
+ * Errors: as taco_paged_tree_attn (dims, null pointers, dtype); the device
+ * contract (lens, table entries) is the attention call's. */
+pta_status taco_accept_commit(const pta_dims* dims, const int32_t* cand_tokens,
+                              const int32_t* target_tokens, const int32_t* target_prev,
+                              const int32_t* ctx_lens, const int32_t* q_lens,
+                              const uint8_t* tree_mask, const int32_t* block_tables,
+                              void* k_cache, void* v_cache, const float* k_scale,
+                              const float* v_scale, int32_t* n_accepted, int32_t* accepted_path,
+                              int32_t* bonus_tokens, int32_t* new_ctx_lens, void* stream);
+
 /* Device-side check of the caller contract above.  Writes into *d_flags (a
  * device int32, caller-owned; it is first cleared) the OR of:
  *   1 q_lens out of [1, max_q_len]     2 ctx_lens < q_lens or > max_ctx_len

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     declared_functions,
     load,
     make_dims,
+    taco_accept_commit,
     taco_kv_append,
     taco_paged_tree_attn_balanced,
     taco_paged_tree_attn_balanced_workspace_size,

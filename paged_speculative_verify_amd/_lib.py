@@ -78,6 +78,8 @@ def load() -> ctypes.CDLL:
     lib.taco_paged_tree_attn_balanced.restype = ctypes.c_int
     lib.taco_kv_append.argtypes = [D, P, P, I32, P, I32, P, P, P, P, P]
     lib.taco_kv_append.restype = ctypes.c_int
+    lib.taco_accept_commit.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.taco_accept_commit.restype = ctypes.c_int
     lib.taco_pta_validate.argtypes = [D, P, P, P, P, P]
     lib.taco_pta_validate.restype = ctypes.c_int
     lib.taco_pta_status_string.argtypes = [ctypes.c_int]
@@ -312,6 +314,53 @@ def taco_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v
     _check(lib.taco_kv_append(ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _q_code(k_new),
                               _ptr(slot_mapping), N, _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                               _ptr(v_scale), _stream(stream)))
+
+
+def taco_accept_commit(cand_tokens, target_tokens, target_prev, ctx_lens, q_lens, tree_mask, block_tables,
+                       k_cache, v_cache, k_scale=None, v_scale=None, n_accepted=None, accepted_path=None,
+                       bonus_tokens=None, new_ctx_lens=None, stream=None):
+    """Greedy acceptance of verified candidates and commit of the path's K/V
+    rows (see include/pta.h).  Returns (n_accepted, accepted_path, bonus_tokens,
+    new_ctx_lens), int32 device tensors; the caches are updated in place."""
+    torch = _torch()
+    lib = load()
+    _need(cand_tokens, "cand_tokens", 2, torch.int32)
+    dev = cand_tokens.device
+    B, Qmax = cand_tokens.shape
+    _need(target_tokens, "target_tokens", 2, torch.int32, dev)
+    _need(target_prev, "target_prev", 1, torch.int32, dev)
+    _need(ctx_lens, "ctx_lens", 1, torch.int32, dev)
+    _need(q_lens, "q_lens", 1, torch.int32, dev)
+    _need(block_tables, "block_tables", 2, torch.int32, dev)
+    _need(k_cache, "k_cache", 4, device=dev)
+    _need(v_cache, "v_cache", 4, k_cache.dtype, dev)
+    if target_tokens.shape != (B, Qmax) or target_prev.shape[0] != B or ctx_lens.shape[0] != B \
+            or q_lens.shape[0] != B or block_tables.shape[0] != B:
+        raise ValueError("per-sequence inputs disagree on the batch or max_q_len")
+    if Qmax > 1:
+        _need(tree_mask, "tree_mask", 3, torch.uint8, dev)
+        if tree_mask.shape != (B, Qmax, Qmax):
+            raise ValueError("tree_mask must be [num_seqs, max_q_len, max_q_len]")
+    if n_accepted is None:
+        n_accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    if accepted_path is None:
+        accepted_path = torch.empty(B, Qmax, dtype=torch.int32, device=dev)
+    if bonus_tokens is None:
+        bonus_tokens = torch.empty(B, dtype=torch.int32, device=dev)
+    if new_ctx_lens is None:
+        new_ctx_lens = torch.empty(B, dtype=torch.int32, device=dev)
+    NB, Hkv, page, D = k_cache.shape
+    dims = PtaDims(num_seqs=B, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=D, page_size=page,
+                   max_q_len=Qmax, max_blocks_per_seq=block_tables.shape[1],
+                   max_ctx_len=block_tables.shape[1] * page, num_blocks=NB,
+                   q_dtype=PTA_BF16 if _kv_code(k_cache) != 0 else 0, kv_dtype=_kv_code(k_cache),
+                   path=0, reserved=0)
+    _check(lib.taco_accept_commit(ctypes.byref(dims), _ptr(cand_tokens), _ptr(target_tokens),
+                                  _ptr(target_prev), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask),
+                                  _ptr(block_tables), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                  _ptr(v_scale), _ptr(n_accepted), _ptr(accepted_path), _ptr(bonus_tokens),
+                                  _ptr(new_ctx_lens), _stream(stream)))
+    return n_accepted, accepted_path, bonus_tokens, new_ctx_lens
 
 
 def taco_pta_validate(block_tables, ctx_lens, q_lens, max_q_len, num_blocks, max_ctx_len=None,

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpta.so")
-SOURCES = ["pta_api.hip", "pta_valu.hip", "pta_stream.hip", "pta_tile.hip", "pta_aux.hip"]
+SOURCES = ["pta_api.hip", "pta_valu.hip", "pta_stream.hip", "pta_tile.hip", "pta_aux.hip", "pta_accept.hip"]
 HEADERS = ["pta_device.h", "pta_flash.h", "pta_launch.h"]
 
 ARCH = "gfx950"

@@ -353,6 +353,45 @@ pta_status taco_kv_append(const pta_dims* d, const void* k_new, const void* v_ne
   return launch_append(p, new_dtype, kv, (hipStream_t)stream) == hipSuccess ? PTA_OK : PTA_ERR_HIP;
 }
 
+pta_status taco_accept_commit(const pta_dims* d, const int32_t* cand_tokens, const int32_t* target_tokens,
+                              const int32_t* target_prev, const int32_t* ctx_lens, const int32_t* q_lens,
+                              const uint8_t* tree_mask, const int32_t* block_tables, void* k_cache,
+                              void* v_cache, const float* k_scale, const float* v_scale, int32_t* n_accepted,
+                              int32_t* accepted_path, int32_t* bonus_tokens, int32_t* new_ctx_lens,
+                              void* stream) {
+  pta_status st = check_dims(d);
+  if (st != PTA_OK) return st;
+  if (d->kv_dtype != PTA_F32 && d->kv_dtype != PTA_BF16 && d->kv_dtype != PTA_FP8_E4M3FN) return PTA_ERR_BAD_DTYPE;
+  if (d->num_seqs == 0) return PTA_OK;
+  if (!cand_tokens || !target_tokens || !target_prev || !ctx_lens || !q_lens || !block_tables || !k_cache ||
+      !v_cache || !n_accepted || !accepted_path || !bonus_tokens || !new_ctx_lens)
+    return PTA_ERR_NULL_PTR;
+  if (d->max_q_len > 1 && !tree_mask) return PTA_ERR_NULL_PTR;
+  if (d->kv_dtype == PTA_FP8_E4M3FN && (!k_scale || !v_scale)) return PTA_ERR_NULL_PTR;
+  AcceptArgs p{};
+  p.ctx = ctx_lens;
+  p.qlen = q_lens;
+  p.mask = d->max_q_len > 1 ? tree_mask : nullptr;
+  p.cand = cand_tokens;
+  p.target = target_tokens;
+  p.target_prev = target_prev;
+  p.tables = block_tables;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.n_acc = n_accepted;
+  p.path = accepted_path;
+  p.bonus = bonus_tokens;
+  p.new_ctx = new_ctx_lens;
+  p.B = d->num_seqs;
+  p.Hkv = d->num_kv_heads;
+  p.D = d->head_dim;
+  p.Qmax = d->max_q_len;
+  p.MBS = d->max_blocks_per_seq;
+  return launch_accept(p, d->kv_dtype, (hipStream_t)stream) == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+}
+
 pta_status taco_pta_validate(const pta_dims* d, const int32_t* block_tables, const int32_t* ctx_lens,
                              const int32_t* q_lens, int32_t* d_flags, void* stream) {
   if (d == nullptr) return PTA_ERR_NULL_PTR;

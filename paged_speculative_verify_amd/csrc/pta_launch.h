@@ -40,6 +40,26 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs& p, int new_dtype, int kv_dtype, hipStream_t s);
 
+struct AcceptArgs {
+  const int32_t* ctx;
+  const int32_t* qlen;
+  const uint8_t* mask;
+  const int32_t* cand;
+  const int32_t* target;
+  const int32_t* target_prev;
+  const int32_t* tables;
+  void* k;
+  void* v;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t* n_acc;
+  int32_t* path;
+  int32_t* bonus;
+  int32_t* new_ctx;
+  int32_t B, Hkv, D, Qmax, MBS;
+};
+hipError_t launch_accept(const AcceptArgs& p, int kv_dtype, hipStream_t s);
+
 struct ValidateArgs {
   const int32_t* tables;
   const int32_t* ctx;

@@ -122,3 +122,17 @@ def test_kv_append_validation(lib):
 def test_validate_host_checks(lib):
     assert lib.taco_pta_validate(ctypes.byref(dims()), FAKE, FAKE, FAKE, None, None) == NULLP
     assert lib.taco_pta_validate(ctypes.byref(dims(page_size=8)), FAKE, FAKE, FAKE, FAKE, None) == DIMS
+
+
+def test_accept_commit_host_checks(lib):
+    f = lambda dd, **kw: lib.taco_accept_commit(
+        None if dd is None else ctypes.byref(dd), kw.get("cand", FAKE), FAKE, FAKE, FAKE, FAKE,
+        kw.get("mask", FAKE), FAKE, FAKE, FAKE, kw.get("ks"), kw.get("vs"), FAKE, FAKE, FAKE,
+        kw.get("ctx", FAKE), None)
+    assert f(None) == NULLP
+    assert f(dims(num_seqs=0)) == OK
+    assert f(dims(), cand=None) == NULLP
+    assert f(dims(), ctx=None) == NULLP
+    assert f(dims(max_q_len=4), mask=None) == NULLP
+    assert f(dims(kv_dtype=2)) == NULLP                 # fp8 cache without scales
+    assert f(dims(head_dim=96)) == DIMS
