@@ -340,8 +340,43 @@ def main(argv=None) -> int:
         gpu_out = sets[order[-1]].out.to(torch.float64).cpu().numpy()
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w0, gpu_out)
+    if sets[0].w.q.shape[1] > 1:
+        result["accept_commit"] = time_accept_commit(psv, torch, sets[order[-1]], K)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def time_accept_commit(psv, torch, ds, K):
+    """The step after verification: greedy acceptance over each candidate tree and
+    compaction of the accepted rows' K/V (synthetic token ids: every node copies its
+    parent's prediction with probability 0.7).  Runs last: it rewrites cache rows."""
+    from workload import make_tokens
+    w, d = ds.w, ds.d
+    cand, target, tprev = make_tokens(w, 11, p_match=0.7)
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(d.q.device)
+    cand, target, tprev = T(cand), T(target), T(tprev)
+    B, Qmax = cand.shape
+    outs = [torch.empty(B, dtype=torch.int32, device=d.q.device),
+            torch.empty(B, Qmax, dtype=torch.int32, device=d.q.device),
+            torch.empty(B, dtype=torch.int32, device=d.q.device),
+            torch.empty(B, dtype=torch.int32, device=d.q.device)]
+    call = lambda: psv.taco_accept_commit(cand, target, tprev, d.ctx_lens, d.q_lens, d.tree_mask,
+                                          d.block_tables, d.k_cache, d.v_cache, k_scale=d.k_scale,
+                                          v_scale=d.v_scale, n_accepted=outs[0], accepted_path=outs[1],
+                                          bonus_tokens=outs[2], new_ctx_lens=outs[3])
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / K * 1e3
+    n = outs[0].cpu().numpy()
+    return {"us_per_call": round(us, 2), "sequences": int(B), "mean_accepted": round(float(n.mean()), 3),
+            "candidates": int(w.q_lens.sum()), "token_match_prob": 0.7}
 
 
 if __name__ == "__main__":

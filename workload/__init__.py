@@ -12,6 +12,7 @@ from .gen import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make,
+    make_tokens,
     permute_pool,
     sample_tree_parents,
     tree_mask_from_parents,

@@ -321,6 +321,28 @@ def make(spec: Spec | str, *, seed: Optional[int] = None, poison: bool = False,
                     pad_page=pad_page, contiguous_k=contig_k, contiguous_v=contig_v)
 
 
+def make_tokens(w: Workload, seed: int, p_match: float = 0.7, p_root: float = 1.0, vocab: int = 32000):
+    """Synthetic token ids for an acceptance step: candidate ids cand [B, Qmax],
+    the target model's predictions target [B, Qmax] and its prediction after the
+    committed prefix target_prev [B] (all int32).  Each non-root candidate copies
+    its parent's prediction with probability p_match, each root copies
+    target_prev with probability p_root; everything else is a uniform draw."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0xACC]))
+    B, Qmax = w.parents.shape
+    cand = rng.integers(0, vocab, (B, Qmax)).astype(np.int32)
+    target = rng.integers(0, vocab, (B, Qmax)).astype(np.int32)
+    tprev = rng.integers(0, vocab, B).astype(np.int32)
+    u = rng.random((B, Qmax))
+    for b in range(B):
+        for i in range(int(w.q_lens[b])):
+            p = int(w.parents[b, i])
+            if p >= 0 and u[b, i] < p_match:
+                cand[b, i] = target[b, p]
+            elif p < 0 and u[b, i] < p_root:
+                cand[b, i] = tprev[b]
+    return cand, target, tprev
+
+
 def permute_pool(w: Workload, seed: int) -> Workload:
     """Same logical workload with the physical pages relabelled by a random bijection."""
     rng = np.random.default_rng(seed)
