@@ -17,37 +17,27 @@
 // (six rounds for up to 64 nodes) gives every node the AND of its ancestors'
 // matches and its depth; the best node is a wave maximum and the path is read
 // back along the parents with uniform register reads.  Then all waves move
-// the rows, one path entry at a time (a destination row can be the source of
-// a later entry, never of an earlier one, so in-order moves are safe).
+// the rows (a destination row can be the source of a later entry, never of an
+// earlier one, so moves in path order are safe).
 #include "pta_device.h"
 #include "pta_launch.h"
 
 namespace pta {
 
-template <typename KT>
-__device__ __forceinline__ void move_row(const AcceptArgs& p, void* cache, const float* scale, int64_t ps, int os,
-                                         int64_t pd, int od, int tid) {
-  const int n = p.Hkv * p.D;
-  for (int e = tid; e < n; e += 256) {
-    const int h = e / p.D, d = e % p.D;
-    const int64_t si = ((ps * p.Hkv + h) * kPage + os) * p.D + d;
-    const int64_t di = ((pd * p.Hkv + h) * kPage + od) * p.D + d;
-    if constexpr (KT::bytes == 4) {
-      reinterpret_cast<uint32_t*>(cache)[di] = reinterpret_cast<const uint32_t*>(cache)[si];
-    } else if constexpr (KT::bytes == 2) {
-      reinterpret_cast<uint16_t*>(cache)[di] = reinterpret_cast<const uint16_t*>(cache)[si];
-    } else {
-      uint8_t* c8 = reinterpret_cast<uint8_t*>(cache);
-      const uint32_t code = c8[si];
-      const float s_src = scale[ps * p.Hkv + h], s_dst = scale[pd * p.Hkv + h];
-      if (s_src == s_dst) {
-        c8[di] = (uint8_t)code;
-      } else {
-        const float x = fp8x2_to_f32<false>(code)[0] * s_src;
-        c8[di] = (uint8_t)f32_to_e4m3fn_sat(__fdiv_rn(x, s_dst));
-      }
+// 16 fp8 codes from pages of scale s_src re-encoded for a page of scale s_dst.
+__device__ __forceinline__ uint4 fp8_reencode(uint4 w, float s_src, float s_dst) {
+  uint32_t in[4] = {w.x, w.y, w.z, w.w}, out[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = fp8x2_to_f32<false>((in[k] >> (8 * e)) & 0xffu)[0] * s_src;
+      r |= f32_to_e4m3fn_sat(__fdiv_rn(x, s_dst)) << (8 * e);
     }
+    out[k] = r;
   }
+  return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
 template <typename KT>
@@ -99,16 +89,46 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(AcceptArgs p) {
   __syncthreads();
   const int n = s_n;
   if (tid < p.Qmax) p.path[(int64_t)b * p.Qmax + tid] = tid < n ? s_path[tid] : -1;
+  // Moves: thread t owns the same 16-byte pieces (K or V, head, piece) of every
+  // row, so its own program order keeps the in-order rule; within a group of
+  // eight path entries it reads all sources before writing (a destination is
+  // never the source of an earlier entry, and later entries' sources lie past
+  // every destination written so far), which keeps eight loads in flight.
   const int32_t* table = p.tables + (int64_t)b * p.MBS;
-  for (int k = 0; k < n; ++k) {
-    const int node = s_path[k];
-    if (node != k) {
-      const int src = L + node, dst = L + k;
-      const int64_t ps = table[src / kPage], pd = table[dst / kPage];
-      move_row<KT>(p, p.k, p.k_scale, ps, src % kPage, pd, dst % kPage, tid);
-      move_row<KT>(p, p.v, p.v_scale, ps, src % kPage, pd, dst % kPage, tid);
+  const int pieces = p.D * KT::bytes / 16;
+  const int per = p.Hkv * pieces;
+  for (int k0 = 0; k0 < n; k0 += 8) {
+    const int kn = min(8, n - k0);
+    for (int it = tid; it < 2 * per; it += 256) {
+      const int which = it / per, h = (it % per) / pieces, j = it % pieces;
+      char* cache = reinterpret_cast<char*>(which ? p.v : p.k);
+      uint4 buf[8];
+      int64_t src_page[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (e < kn && s_path[k0 + e] != k0 + e) {
+          const int src = L + s_path[k0 + e];
+          src_page[e] = table[src / kPage];
+          const int64_t off = ((src_page[e] * p.Hkv + h) * kPage + src % kPage) * (int64_t)(p.D * KT::bytes);
+          buf[e] = *reinterpret_cast<const uint4*>(cache + off + 16 * j);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (e < kn && s_path[k0 + e] != k0 + e) {
+          const int dst = L + k0 + e;
+          const int64_t dpage = table[dst / kPage];
+          const int64_t off = ((dpage * p.Hkv + h) * kPage + dst % kPage) * (int64_t)(p.D * KT::bytes);
+          uint4 w = buf[e];
+          if constexpr (KT::bytes == 1) {
+            const float* scl = which ? p.v_scale : p.k_scale;
+            const float s_src = scl[src_page[e] * p.Hkv + h], s_dst = scl[dpage * p.Hkv + h];
+            if (s_src != s_dst) w = fp8_reencode(w, s_src, s_dst);
+          }
+          *reinterpret_cast<uint4*>(cache + off + 16 * j) = w;
+        }
+      }
     }
-    __syncthreads();          // entry k fully moved before entry k + 1 reads
   }
 }
 
