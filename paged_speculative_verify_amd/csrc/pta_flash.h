@@ -1,8 +1,8 @@
 // Flash-attention building blocks shared by the matrix-core kernels (gfx950):
 // page tiles staged in LDS as bf16 rows, the rows a lane owns, its online
-// softmax state, the per-page update with v_mfma_f32_16x16x32_bf16 (S^T = K Q^T)
-// and v_mfma_f32_16x16x16_bf16 with ds_read_b64_tr_b16 (O^T += V^T P^T), and
-// the stores of final or partial rows.
+// softmax state, the two-page update with v_mfma_f32_16x16x32_bf16 for both
+// S^T = K Q^T and O^T += V^T P^T (V^T read with ds_read_b64_tr_b16), and the
+// stores of final or partial rows.
 //
 // Lane (g, m) = (lane / 16, lane % 16) owns rows 16 rb + m of the unit and, in
 // every 16-token page, tokens 4 g + r (r < 4) of the S^T accumulator; its O^T
@@ -26,15 +26,7 @@ struct StreamTile {
   static constexpr int LOADS = (kPage * D * KT::bytes) / 1024;     // 16-byte loads per lane per tile
   static constexpr int STR = 2 * D + 32;                      // bytes per bf16 row in LDS (bank skew)
   static constexpr int TILE_LDS = kPage * STR;                // one bf16 tile in LDS
-  static constexpr int WAVE_LDS = 2 * TILE_LDS;               // per-wave K tile + V tile
-};
-
-// One page's K and V chunks in flight (lane l holds bytes 16 l + 1024 j).
-template <typename KT, int D>
-struct PageRegs {
-  uint4 k[StreamTile<KT, D>::LOADS];
-  uint4 v[StreamTile<KT, D>::LOADS];
-  float ks, vs;
+  static constexpr int WAVE_LDS = 4 * TILE_LDS;               // per-wave K and V tiles of a page pair
 };
 
 // Write 1 KiB load chunk j of a page tile (lane l holds bytes 16 l + 1024 j)
@@ -120,105 +112,6 @@ struct StreamState {
   }
 };
 
-// One page of the flash update for a lane's rows, from bf16 K and V tiles in
-// LDS (16 rows of STR bytes): S^T = K Q^T, scores in log2 units (c = softmax
-// scale * log2 e * the page's K scale), mask by select (tokens at or past t1,
-// and candidate tokens off the row's tree mask), lazy reference-max update,
-// then O^T += V^T P^T with P scaled by the page's V scale vs and carried as a
-// bf16 hi/lo pair.  pbase: logical
-// position of the page's first token.
-template <int D, int RB>
-__device__ __forceinline__ void page_compute(const StreamRows<D, RB>& rows, StreamState<D, RB>& st,
-                                             const char* kl, const char* vt_l, int pbase, int L, int t1,
-                                             float c, float vs, int lane) {
-  constexpr int KK = D / 32, DB = D / 16, STR = 2 * D + 32;
-  constexpr float NEG_INF = -__builtin_huge_valf();
-  const int g = lane >> 4, m = lane & 15;
-  // 2. S^T[16 tokens][16 rows] = K Q^T per row block (A operand from LDS)
-  f32x4 sacc[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) sacc[rb] = {};
-  const char* krd = kl + m * STR + 16 * g;
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    const bf16x8 kop = *reinterpret_cast<const bf16x8*>(krd + 64 * kk);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, rows.qop[rb][kk], sacc[rb], 0, 0, 0);
-  }
-
-  // 3. scores in log2 units, mask by select; lazy reference-max update
-  const bool plain = pbase + kPage <= min(L, t1);
-  float x[RB][4];
-  bool need = false;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    float pm = NEG_INF;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v = sacc[rb][r] * c;
-      if (!plain) {
-        const int t = pbase + 4 * g + r;
-        const int sh = t - L;
-        const bool cand = (unsigned)sh < 64u && ((rows.mbits[rb] >> (sh & 63)) & 1ull);
-        v = (t < t1 && (t < L || cand)) ? v : NEG_INF;
-      }
-      v = rows.ok[rb] ? v : NEG_INF;
-      x[rb][r] = v;
-      pm = fmaxf(pm, v);
-    }
-    need |= pm > st.m[rb] + kLazyTau;
-  }
-  if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float pm = fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]));
-      pm = fmaxf(pm, shfl_xor(pm, 16));
-      pm = fmaxf(pm, shfl_xor(pm, 32));
-      const float mnew = fmaxf(st.m[rb], pm);
-      const float alpha = fast_exp2(st.m[rb] - (mnew == NEG_INF ? 0.f : mnew));
-      st.m[rb] = mnew;
-      st.l[rb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) st.o[rb][db] *= alpha;
-    }
-  }
-
-  // 4. P^T straight from the S^T registers as a bf16 pair P_hi + P_lo (P_hi =
-  //    bf16(P), P_lo = bf16(P - P_hi): P to ~2^-16 relative, so the weights
-  //    cost no accuracy even when the lazy reference max leaves them above 1);
-  //    O^T += V^T P_hi^T + V^T P_lo^T
-  s16x4 phi[RB], plo[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float muse = st.m[rb] == NEG_INF ? 0.f : st.m[rb];
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = fast_exp2(x[rb][r] - muse);
-      st.l[rb] += p[r];
-      p[r] *= vs;
-    }
-    const uint32_t h0 = pack_bf16x2(p[0], p[1]);
-    const uint32_t h1 = pack_bf16x2(p[2], p[3]);
-    const uint32_t l0 = pack_bf16x2(p[0] - bf16_lo(h0), p[1] - bf16_hi(h0));
-    const uint32_t l1 = pack_bf16x2(p[2] - bf16_lo(h1), p[3] - bf16_hi(h1));
-    phi[rb] = __builtin_bit_cast(s16x4, make_uint2(h0, h1));
-    plo[rb] = __builtin_bit_cast(s16x4, make_uint2(l0, l1));
-  }
-  const char* vrd = vt_l + (4 * g + (m >> 2)) * STR + 8 * (m & 3);
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrd + 32 * db));
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      st.o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi[rb], st.o[rb][db], 0, 0, 0);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      st.o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo[rb], st.o[rb][db], 0, 0, 0);
-  }
-}
-
 // Byte offset of 16-byte unit `u` of row `r` in a bf16 LDS tile of D dims.
 // Padded tiles put rows STR = 2 D + 32 bytes apart; swizzled tiles keep rows
 // 2 D bytes apart (so a tile is contiguous, as direct global-to-LDS loads
@@ -235,7 +128,7 @@ __device__ __forceinline__ int tile_off(int r, int u) {
 }
 
 // Two consecutive pages of the flash update at once (tiles kl0/vl0 and
-// kl1/vl1, first token at pbase): S^T per page as in page_compute, one lazy
+// kl1/vl1, first token at pbase): S^T = K Q^T per page, one lazy
 // max check over both, and a single 32-token O^T += V^T P^T step with
 // v_mfma_f32_16x16x32_bf16 (full rate on gfx950, where the 16-token
 // instruction runs at half rate).  The k index of that step runs over tokens

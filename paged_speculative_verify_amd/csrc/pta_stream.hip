@@ -14,14 +14,17 @@
 //     contiguous (lane l: bytes 16 l + 1024 j of the page tile): loading K
 //     straight into the MFMA operand layout would make each instruction touch
 //     16 rows x 64 B, which measures ~20% below contiguous tiles on MI355X.
-//     K and V go into a per-wave LDS tile pair (fp8 decoded to bf16 on the
-//     way); K comes back with ds_read_b128 as the A operand of
-//     v_mfma_f32_16x16x32_bf16 (lane (g, m): 8 consecutive dims of token m) for
-//     S^T = K Q^T, and V with ds_read_b64_tr_b16, whose 16-lane transpose
-//     yields exactly the A operand of O^T += V^T P^T
-//     (v_mfma_f32_16x16x16_bf16); P^T is the S^T accumulator itself.
-//   * The next page's loads are issued before the current page is computed
-//     (two register sets, ping-pong), keeping one page per wave in flight.
+//     Pages go in pairs: the K and V tiles of two pages into per-wave LDS
+//     tiles (fp8 decoded to bf16 on the way); K comes back with ds_read_b128
+//     as the A operand of v_mfma_f32_16x16x32_bf16 (lane (g, m): 8 consecutive
+//     dims of token m) for S^T = K Q^T, and V with two ds_read_b64_tr_b16,
+//     whose 16-lane transpose yields the A operand of one 32-token
+//     O^T += V^T P^T step, again v_mfma_f32_16x16x32_bf16 (the 16-token
+//     bf16 instruction runs at half rate on gfx950); P^T is the pair of S^T
+//     accumulators, as a bf16 hi/lo pair.
+//   * The next pair's loads are issued right after the current pair is
+//     written to LDS and before it is computed, so they are in flight while
+//     the wave computes.
 //   * Softmax rescaling is lazy: a row's reference maximum only moves when a
 //     score exceeds it by more than 2^8, so the accumulator rescale (and the
 //     cross-lane max) is skipped on almost every page.  The result is the same
@@ -33,8 +36,9 @@
 //
 // Two kernels share this core:
 //   stream_attn_kernel      one workgroup per (unit, token partition); its
-//                           waves take the pages round-robin and are merged
-//                           in LDS (whole-context and split-K entry points).
+//                           waves take the page pairs round-robin and are
+//                           merged in LDS (whole-context and split-K entry
+//                           points).
 //   stream_balanced_kernel  persistent grid; the pages of all units are laid
 //                           end to end and every wave takes an equal
 //                           contiguous slice, so ragged context lengths cost
@@ -47,73 +51,69 @@
 
 namespace pta {
 
-// Stream the pages pg = pg0 + k * stride (k < nk) of unit (b, hkv) through the
-// state.  Tokens at or past t1 (the end of the sequence or of the partition)
-// are masked, and their V rows zeroed, so unused page slots are never read for
-// their values.  vl: this wave's LDS tile pair.
+// Page pairs j = j0, j0 + js, ... of the range [pA, pB): pair j is pages
+// pA + 2j and, if it is in the range, pA + 2j + 1 (else the first page again,
+// its tokens masked and its V rows zeroed).  One pair's K and V chunks are in
+// registers at a time: they are written to the wave's four LDS tiles, the next
+// pair's loads are issued (unconditionally, the last one repeats the final
+// pair, so the compiler's load counters stay exact), and the pair is computed
+// with one 32-token P.V step per output block (pair_compute).
+template <typename KT, int D>
+struct PairRegs {
+  uint4 k[2][StreamTile<KT, D>::LOADS];
+  uint4 v[2][StreamTile<KT, D>::LOADS];
+  float ks[2], vs[2];
+};
+
 template <typename KT, int D, int RB>
-__device__ __forceinline__ void stream_pages(const AttnArgs& a, const StreamRows<D, RB>& rows,
-                                             StreamState<D, RB>& st, int b, int hkv, int L, int t1,
-                                             int pg0, int stride, int nk, char* vl, int lane) {
+__device__ __forceinline__ void stream_pairs(const AttnArgs& a, const StreamRows<D, RB>& rows,
+                                             StreamState<D, RB>& st, int b, int hkv, int L, int t_end,
+                                             int pA, int pB, int j0, int js, char* wl, int lane) {
   using T = StreamTile<KT, D>;
-  constexpr float NEG_INF = -__builtin_huge_valf();
-  const int g = lane >> 4, m = lane & 15;
+  constexpr int64_t TILE_BYTES = (int64_t)kPage * D * KT::bytes;
+  const int npair = (pB - pA + 1) / 2;
+  const int n = j0 < npair ? (npair - 1 - j0) / js + 1 : 0;
+  if (n <= 0) return;
   const int32_t* table = a.tables + (int64_t)b * a.MBS;
   const char* kbase = reinterpret_cast<const char*>(a.k);
   const char* vbase = reinterpret_cast<const char*>(a.v);
-  constexpr int64_t TILE_BYTES = (int64_t)kPage * D * KT::bytes;
 
-  // physical block of page k (wave-uniform: a scalar load)
-  auto phys_of = [&](int k) -> int { return table[pg0 + k * stride]; };
-
-  auto issue = [&](PageRegs<KT, D>& R, int phys32) {
-    const int64_t phys = phys32;
-    const int64_t tile = (phys * a.Hkv + hkv) * TILE_BYTES + 16 * lane;
+  PairRegs<KT, D> R;
+  auto issue = [&](int idx) {
+    const int p0 = pA + 2 * (j0 + idx * js);
+    const int p1 = p0 + 1 < pB ? p0 + 1 : p0;           // index stays inside the range
+    const int64_t ph[2] = {table[p0], table[p1]};
 #pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) R.k[j] = *reinterpret_cast<const uint4*>(kbase + tile + 1024 * j);
+    for (int pg = 0; pg < 2; ++pg) {
+      const int64_t tile = (ph[pg] * a.Hkv + hkv) * TILE_BYTES + 16 * lane;
 #pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) R.v[j] = *reinterpret_cast<const uint4*>(vbase + tile + 1024 * j);
-    if constexpr (KT::bytes == 1) {
-      R.ks = a.k_scale[phys * a.Hkv + hkv];
-      R.vs = a.v_scale[phys * a.Hkv + hkv];
-    } else {
-      R.ks = 1.f;
-      R.vs = 1.f;
+      for (int j = 0; j < T::LOADS; ++j) R.k[pg][j] = *reinterpret_cast<const uint4*>(kbase + tile + 1024 * j);
+#pragma unroll
+      for (int j = 0; j < T::LOADS; ++j) R.v[pg][j] = *reinterpret_cast<const uint4*>(vbase + tile + 1024 * j);
+      if constexpr (KT::bytes == 1) {
+        R.ks[pg] = a.k_scale[ph[pg] * a.Hkv + hkv];
+        R.vs[pg] = a.v_scale[ph[pg] * a.Hkv + hkv];
+      } else {
+        R.ks[pg] = 1.f;
+        R.vs[pg] = 1.f;
+      }
     }
   };
-
-  char* kl = vl;                    // this wave's K tile, then its V tile
-  char* vt_l = vl + T::TILE_LDS;
-  auto consume = [&](const PageRegs<KT, D>& R, int k) {
-    const int pbase = (pg0 + k * stride) * kPage;
-    const bool partial = pbase + kPage > t1;
-
-    // 1. K and V tiles -> LDS as bf16 rows (V rows past t1 zeroed; K rows
-    //    past t1 are masked out of the scores)
-    stage_tile<KT, D>(kl, R.k, lane, false, kPage);
-    stage_tile<KT, D>(vt_l, R.v, lane, partial, t1 - pbase);
-
-    page_compute<D, RB>(rows, st, kl, vt_l, pbase, L, t1, a.scale_log2 * R.ks, R.vs, lane);
-  };
-
-  // Two register sets, the next page always in flight.  The prefetch is
-  // issued unconditionally (the last one re-reads the final page, which is
-  // still in cache) so the compiler's load counters stay exact and the wait
-  // before each page covers only that page's own loads.  Block-table entries
-  // are read two pages ahead of their use.
-  if (nk <= 0) return;
-  PageRegs<KT, D> r0, r1;
-  int ph_a = phys_of(0), ph_b = phys_of(min(1, nk - 1));
-  issue(r0, ph_a);
-  for (int k = 0;; k += 2) {
-    ph_a = phys_of(min(k + 2, nk - 1));
-    issue(r1, ph_b);
-    consume(r0, k);
-    if (k + 1 >= nk) break;
-    ph_b = phys_of(min(k + 3, nk - 1));
-    issue(r0, ph_a);
-    consume(r1, k + 1);
-    if (k + 2 >= nk) break;
+  char* k0l = wl;
+  char* k1l = wl + T::TILE_LDS;
+  char* v0l = wl + 2 * T::TILE_LDS;
+  char* v1l = wl + 3 * T::TILE_LDS;
+  issue(0);
+  for (int idx = 0; idx < n; ++idx) {
+    const int pb0 = (pA + 2 * (j0 + idx * js)) * kPage;
+    const float c0 = a.scale_log2 * R.ks[0], c1 = a.scale_log2 * R.ks[1];
+    const float vs0 = R.vs[0], vs1 = R.vs[1];
+    stage_tile<KT, D>(k0l, R.k[0], lane, false, kPage);
+    stage_tile<KT, D>(k1l, R.k[1], lane, false, kPage);
+    stage_tile<KT, D>(v0l, R.v[0], lane, pb0 + kPage > t_end, t_end - pb0);
+    stage_tile<KT, D>(v1l, R.v[1], lane, pb0 + 2 * kPage > t_end, t_end - pb0 - kPage);
+    issue(min(idx + 1, n - 1));
+    pair_compute<D, RB, false>(rows, st, k0l, k1l, v0l, v1l, pb0, L, t_end, c0, c1, vs0, vs1, lane);
   }
 }
 
@@ -152,11 +152,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   StreamState<D, RB> st;
   st.init();
 
-  // this wave's pages: pg = pgA + wave + k * NW, k < nk
+  // this wave's page pairs: wave, wave + NW, ... of the unit's range
   const int pgA = t0 / kPage;
-  const int npg = (t1 + kPage - 1) / kPage - pgA;
-  const int nk = npg > wave ? (npg - wave + NW - 1) / NW : 0;
-  stream_pages<KT, D, RB>(a, rows, st, b, hkv, L, t1, pgA + wave, NW, nk, vlds[wave], lane);
+  const int pgB = (t1 + kPage - 1) / kPage;
+  stream_pairs<KT, D, RB>(a, rows, st, b, hkv, L, t1, pgA, pgB, wave, NW, vlds[wave], lane);
   reduce_row_sums(st);
 
   // ---- merge the waves: row max, row sum, then O^T accumulated in LDS in wave order
@@ -282,7 +281,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     load_rows(rows, a, b, hkv, qb, M, g, m);
     StreamState<D, RB> st;
     st.init();
-    stream_pages<KT, D, RB>(a, rows, st, b, hkv, L, C, k0, 1, k1 - k0, vlds[wave], lane);
+    stream_pairs<KT, D, RB>(a, rows, st, b, hkv, L, min(C, k1 * kPage), k0, k1, 0, 1, vlds[wave], lane);
     reduce_row_sums(st);
 
     if (k0 == 0 && k1 == Pb) {
