@@ -272,6 +272,115 @@ __device__ __forceinline__ void pair_pv(StreamState<D, RB>& st, const float (&x)
   }
 }
 
+// ---- the same update split for a software pipeline (tile kernels): the
+// masked scores and lane maxima of a pair (pair_max_prep, straight-line so it
+// can share issue slots with matrix-core work), the rare reference-max move
+// (pair_max_finish: m and l at once, O's factor returned for later), P as a
+// hi/lo pair (pair_p) and the P.V products (pair_pv_mma).
+template <int D, int RB>
+__device__ __forceinline__ void pair_max_prep(const StreamRows<D, RB>& rows, const StreamState<D, RB>& st,
+                                              const PairScores<RB>& S, float (&x)[RB][8], bool& need, int pbase,
+                                              int L, int t1, float c, int lane) {
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  const int g = lane >> 4;
+  const bool plain = pbase + 2 * kPage <= min(L, t1);      // no token of the pair is masked
+  need = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float pm = NEG_INF;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pg = e >> 2, r = e & 3;
+      float v = S.s[pg][rb][r] * c;
+      if (!plain) {
+        const int t = pbase + 16 * pg + 4 * g + r;
+        const int sh = t - L;
+        const bool cand = (unsigned)sh < 64u && ((rows.mbits[rb] >> (sh & 63)) & 1ull);
+        v = (t < t1 && (t < L || cand)) ? v : NEG_INF;
+      }
+      x[rb][e] = v;
+      pm = fmaxf(pm, v);
+    }
+    need |= pm > st.m[rb] + kLazyTau;
+  }
+}
+
+// Returns true (wave-uniform) when some row's reference maximum moved; then
+// alpha holds the factor O must be multiplied by before the products of this
+// pair are added (l is rescaled here).
+template <int D, int RB>
+__device__ __forceinline__ bool pair_max_finish(StreamState<D, RB>& st, const float (&x)[RB][8], bool need,
+                                                float (&alpha)[RB]) {
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  if (__builtin_amdgcn_ballot_w64(need) == 0) return false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float pm = x[rb][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) pm = fmaxf(pm, x[rb][e]);
+    pm = fmaxf(pm, shfl_xor(pm, 16));
+    pm = fmaxf(pm, shfl_xor(pm, 32));
+    const float mnew = fmaxf(st.m[rb], pm);
+    alpha[rb] = fast_exp2(st.m[rb] - (mnew == NEG_INF ? 0.f : mnew));
+    st.m[rb] = mnew;
+    st.l[rb] *= alpha[rb];
+  }
+  return true;
+}
+
+template <int D, int RB>
+__device__ __forceinline__ void pair_p(StreamState<D, RB>& st, const float (&x)[RB][8], bf16x8 (&phi)[RB],
+                                       bf16x8 (&plo)[RB]) {
+  constexpr float NEG_INF = -__builtin_huge_valf();
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float muse = st.m[rb] == NEG_INF ? 0.f : st.m[rb];
+    uint32_t h[4], lo[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float p0 = fast_exp2(x[rb][2 * k] - muse), p1 = fast_exp2(x[rb][2 * k + 1] - muse);
+      st.l[rb] += p0 + p1;
+      h[k] = pack_bf16x2(p0, p1);
+      lo[k] = pack_bf16x2(p0 - bf16_lo(h[k]), p1 - bf16_hi(h[k]));
+    }
+    phi[rb] = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+    plo[rb] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+  }
+}
+
+template <int D, int RB, bool SWZ>
+__device__ __forceinline__ void pair_pv_mma(StreamState<D, RB>& st, const bf16x8 (&phi)[RB],
+                                            const bf16x8 (&plo)[RB], const char* vl0, const char* vl1,
+                                            int lane) {
+  constexpr int DB = D / 16;
+  const int g = lane >> 4, m = lane & 15;
+  const int vrow = 4 * g + (m >> 2);
+#pragma unroll
+  for (int db = 0; db < DB; db += 2) {
+    bf16x8 vt[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int voff = tile_off<D, SWZ>(vrow, 2 * (db + e) + ((m & 3) >> 1)) + 8 * (m & 1);
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl0 + voff));
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl1 + voff));
+      vt[e] = __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint2, va).x,
+                                                   __builtin_bit_cast(uint2, va).y,
+                                                   __builtin_bit_cast(uint2, vb).x,
+                                                   __builtin_bit_cast(uint2, vb).y));
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        st.o[rb][db + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[e], phi[rb], st.o[rb][db + e], 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        st.o[rb][db + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[e], plo[rb], st.o[rb][db + e], 0, 0, 0);
+  }
+}
+
 template <int D, int RB, bool SWZ = false>
 __device__ __forceinline__ void pair_compute(const StreamRows<D, RB>& rows, StreamState<D, RB>& st,
                                              const char* kl0, const char* kl1, const char* vl0,

@@ -250,8 +250,26 @@ struct DmaGeom {
 // The 32-row blocks of one (sequence b, KV head hkv) over tokens [t0, t1):
 // wave w owns rows row0 + 32 w .. + 31 of the unit's M = G * q_b rows; every
 // wave takes part in the copies whether or not it owns rows.  On return st
-// holds the wave's unnormalised flash state; the LDS buffers may still be read
-// by other waves (the caller synchronises before reusing them).
+// holds the wave's flash state with its row sums reduced; the LDS buffers may
+// still be read by other waves (the caller synchronises before reusing them).
+//
+// Software pipeline over page pairs, iteration s:
+//   1. S of pair s + 1 (matrix core)     with  P of pair s (vector ALU)
+//   2. P.V of pair s (matrix core)       with  masking and lane maxima of
+//                                              pair s + 1 (vector ALU)
+//   3. the rare move of a row's reference maximum for pair s + 1
+// so most vector work of one pair has matrix-core work of another to hide
+// behind.  The factor a reference-max move applies to O waits until the P.V
+// of pair s has been added (l and m move at once).
+//
+// DMA stage j (j = -1 .. nst - 1) holds the K tiles of page pair j + 1 and
+// the V tiles of pair j, in buffer (j + 1) % NBUF: iteration s reads one
+// buffer (K for the scores of pair s + 1, V for the P.V of pair s) and the
+// other NBUF - 1 buffers are all in flight.  Stage -1 carries K of pair 0
+// (its V half repeats pair 0, unused) and stage nst - 1 repeats K of the
+// last pair (its score products are masked out), so every stage moves the
+// same number of chunks.  A missing second page of a pair repeats the first
+// (its tokens are masked, its V rows zeroed).
 template <int D, int NWR, int NBUF>
 __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t lds0, const int* tring,
                                           uint32_t tring0, StreamRows<D, 2>& rows, StreamState<D, 2>& st,
@@ -265,6 +283,7 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
   const int M = a.G * qb;
   const int wrow0 = row0 + wave * 32;
   const bool wave_rows = wrow0 < M;
+  const float c = a.scale_log2;
 
   const int32_t* table = a.tables + (int64_t)b * a.MBS;
   const char* kbase = reinterpret_cast<const char*>(a.k);
@@ -273,15 +292,6 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
   const int npg = (t1 + kPage - 1) / kPage - pgA;
   const int nst = (npg + 1) / 2;
 
-  // DMA stage j (j = -1 .. nst - 1) holds the K tiles of page pair j + 1 and
-  // the V tiles of pair j, in buffer (j + 1) % NBUF: iteration s reads one
-  // buffer (K for the scores of pair s + 1, V for the P.V of pair s) and the
-  // other NBUF - 1 buffers are all in flight.  Stage -1 carries K of pair 0
-  // (its V half repeats pair 0, unused) and stage nst - 1 repeats K of the
-  // last pair (its score products are dropped), so every stage moves the
-  // same number of chunks.  A missing second page of a pair repeats the first
-  // (its tokens are masked, its V rows zeroed).
-  //
   // Block-table entries of the range are staged in an LDS ring of kRing
   // entries (relative page e at tring[e % kRing]), 64 entries per dword DMA
   // issued by wave 0: chunks 0..3 before the loop, chunk c in the iteration
@@ -291,9 +301,9 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
   // read the table through the scalar cache.
   constexpr int kRing = 256;
   const int nch = (npg + 63) / 64;
-  auto issue_chunk = [&](int c) {
-    const int e = min(64 * c + lane, npg - 1);            // clamped: stays inside the range
-    lds_copy4(tring0 + (uint32_t)((c & 3) * 256), table + pgA + e);
+  auto issue_chunk = [&](int ch) {
+    const int e = min(64 * ch + lane, npg - 1);           // clamped: stays inside the range
+    lds_copy4(tring0 + (uint32_t)((ch & 3) * 256), table + pgA + e);
   };
   const int crow = lane / Gm::UPR, cunit = lane % Gm::UPR;
   auto copy_stage = [&](int j, bool ring) {
@@ -317,9 +327,9 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
     const uint32_t dst = lds0 + (uint32_t)(((j + 1) % NBUF) * Gm::STAGE);
 #pragma unroll
     for (int i = 0; i < Gm::CPW; ++i) {
-      int c = wave + i * NWR;
-      if constexpr (Gm::CHUNKS % NWR != 0) c %= Gm::CHUNKS;   // surplus waves repeat a copy
-      const int tile = c / Gm::CPT, jj = c % Gm::CPT;
+      int cc = wave + i * NWR;
+      if constexpr (Gm::CHUNKS % NWR != 0) cc %= Gm::CHUNKS;   // surplus waves repeat a copy
+      const int tile = cc / Gm::CPT, jj = cc % Gm::CPT;
       const int64_t ph = tile == 0 ? xk0 : tile == 1 ? xk1 : tile == 2 ? xv0 : xv1;
       const int r = Gm::RPC * jj + crow;
       const char* src = (tile < 2 ? kbase : vbase) + (ph * a.Hkv + hkv) * Gm::TILE + r * 2 * D +
@@ -328,26 +338,51 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
     }
   };
   auto buf = [&](int j) { return lds + ((j + 1) % NBUF) * Gm::STAGE; };
+  auto pbase = [&](int s) { return (pgA + 2 * s) * kPage; };
 
   // The query rows load behind the first stages and everything lands before
   // the loop, so no wait on the query registers sits inside it.
   const int pro = min(NBUF, nst + 1);                // stages -1 .. pro - 2
   if (wave == 0)
-    for (int c = 0; c < min(4, nch); ++c) issue_chunk(c);
+    for (int ch = 0; ch < min(4, nch); ++ch) issue_chunk(ch);
   for (int j = -1; j < pro - 1; ++j) copy_stage(j, false);
   load_rows(rows, a, b, hkv, qb, M, g, m, wrow0);
   wait_vmem_at_most<0>();
   __syncthreads();
-  // Software pipeline: iteration s runs the softmax and P.V of pair s while
-  // the score products of pair s + 1 go to the matrix core.
-  PairScores<RB> sc;
-  if (wave_rows) pair_scores<D, RB, true>(rows, sc, buf(-1), buf(-1) + Gm::TILE, lane);
+
+  float x[RB][8];                    // masked scores of the pair whose P comes next, log2 units
+  float alpha[RB] = {1.f, 1.f};      // O's factor owed before the next P.V
+  bool pend = false;
+  if (wave_rows) {
+    PairScores<RB> sc;
+    pair_scores<D, RB, true>(rows, sc, buf(-1), buf(-1) + Gm::TILE, lane);
+    bool need;
+    pair_max_prep<D, RB>(rows, st, sc, x, need, pbase(0), L, t1, c, lane);
+    pair_max_finish<D, RB>(st, x, need, alpha);     // O is still zero: its factor is moot
+  }
+
+  // One iteration of the pipeline.
+  auto step = [&](int s, char* sb) {
+    if (pend) {                       // the factor owed since pair s's maximum moved
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) st.o[rb][db] *= alpha[rb];
+    }
+    // 1. S of pair s + 1 with P of pair s
+    PairScores<RB> sn;
+    pair_scores<D, RB, true>(rows, sn, sb, sb + Gm::TILE, lane);
+    bf16x8 phi[RB], plo[RB];
+    pair_p<D, RB>(st, x, phi, plo);
+    // 2. P.V of pair s with the masked scores of pair s + 1
+    pair_pv_mma<D, RB, true>(st, phi, plo, sb + 2 * Gm::TILE, sb + 3 * Gm::TILE, lane);
+    bool need;
+    pair_max_prep<D, RB>(rows, st, sn, x, need, pbase(s + 1), L, t1, c, lane);
+    // 3. the rare reference-max move for pair s + 1
+    pend = pair_max_finish<D, RB>(st, x, need, alpha);
+  };
+
   for (int s = 0; s < nst; ++s) {
-    // masking and the lazy max of pair s need only its scores: they run on
-    // the vector ALU while the previous pair's P.V is still in the matrix core
-    float x[RB][8];
-    if (wave_rows)
-      pair_softmax<D, RB>(rows, st, sc, x, (pgA + 2 * s) * kPage, L, t1, a.scale_log2, a.scale_log2, lane);
     wait_stages<Gm::CPW, NBUF - 2>(min(NBUF - 2, nst - 1 - s));
     __syncthreads();        // stage s in LDS for all waves; stage s - 1 fully consumed
     char* sb = buf(s);
@@ -355,8 +390,8 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
       // zero V rows past t1 in the last pair (and the whole V tile of a missing
       // second page): their slots may hold anything, and 0 * NaN would leak
       for (int pg = 0; pg < 2; ++pg) {
-        const int pbase = (pgA + 2 * s + pg) * kPage;
-        const int valid = max(0, min(kPage, t1 - pbase));
+        const int pb = pbase(s) + pg * kPage;
+        const int valid = max(0, min(kPage, t1 - pb));
         char* vt = sb + (2 + pg) * Gm::TILE;
         for (int idx = threadIdx.x; idx < (kPage - valid) * Gm::UPR; idx += NWR * 64)
           *reinterpret_cast<uint4*>(vt + (valid + idx / Gm::UPR) * 2 * D + (idx % Gm::UPR) * 16) =
@@ -365,16 +400,11 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
       __syncthreads();
     }
     if ((s + NBUF - 1) % 32 == 0 && wave == 0) {
-      const int c = (s + NBUF - 1) / 32 + 3;
-      if (c < nch) issue_chunk(c);
+      const int ch = (s + NBUF - 1) / 32 + 3;
+      if (ch < nch) issue_chunk(ch);
     }
     if (s + NBUF - 1 < nst) copy_stage(s + NBUF - 1, true);     // into the buffer stage s - 1 used
-    if (wave_rows) {
-      PairScores<RB> sn_sc;
-      pair_scores<D, RB, true>(rows, sn_sc, sb, sb + Gm::TILE, lane);
-      pair_pv<D, RB, true>(st, x, sb + 2 * Gm::TILE, sb + 3 * Gm::TILE, 1.f, 1.f, lane);
-      sc = sn_sc;
-    }
+    if (wave_rows) step(s, sb);
   }
   reduce_row_sums(st);
 }
