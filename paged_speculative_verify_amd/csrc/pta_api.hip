@@ -162,6 +162,7 @@ bool split_layout(const pta_dims* d, int32_t T, SplitLayout* L) {
 //     once); counters B*Hkv*rg, S = ns + B*Hkv slots.
 struct BalancedLayout {
   int nwg, nw, rg;
+  int merge_after;      // tile path: slices merged by a second launch
   size_t o_off, lse_off, total;
 };
 
@@ -183,6 +184,10 @@ pta_status tile_balanced_layout(const pta_dims* d, BalancedLayout* L) {
   L->nwg = ns * rg;
   L->nw = nw;
   L->rg = rg;
+  // With more than four slices per (unit, row group) on average the last
+  // slice's merge would read many partials alone at the end of the launch;
+  // a second launch spreads those merges over the whole device instead.
+  L->merge_after = units * rg * 4 < ns * rg ? 1 : 0;
   L->o_off = up((size_t)units * rg * sizeof(int32_t));
   L->lse_off = L->o_off + up((size_t)slot_rows * d->head_dim * sizeof(float));
   L->total = L->lse_off + up((size_t)slot_rows * sizeof(float));
@@ -207,6 +212,7 @@ pta_status balanced_layout(const pta_dims* d, const Plan& p, BalancedLayout* L) 
   L->nwg = nwg;
   L->nw = nw;
   L->rg = 1;
+  L->merge_after = 0;
   L->o_off = up((size_t)units * sizeof(int32_t));
   L->lse_off = L->o_off + up((size_t)rows * d->head_dim * sizeof(float));
   L->total = L->lse_off + up((size_t)rows * sizeof(float));
@@ -319,6 +325,7 @@ pta_status taco_paged_tree_attn_balanced(const pta_dims* d, const void* q, const
   a.part_o = reinterpret_cast<float*>(ws + L.o_off);
   a.part_lse = reinterpret_cast<float*>(ws + L.lse_off);
   a.total_waves = L.nwg * L.nw;
+  a.merge_after = L.merge_after;
   int nwg = L.nwg;
   if (p.fam == FAM_TILE)
     return tile_balanced(&a, d->head_dim, L.nw, d->num_seqs, &nwg, (hipStream_t)stream) == hipSuccess

@@ -272,36 +272,48 @@ __device__ __forceinline__ void pair_pv(StreamState<D, RB>& st, const float (&x)
   }
 }
 
-// ---- the same update split for a software pipeline (tile kernels): the
-// masked scores and lane maxima of a pair (pair_max_prep, straight-line so it
-// can share issue slots with matrix-core work), the rare reference-max move
-// (pair_max_finish: m and l at once, O's factor returned for later), P as a
-// hi/lo pair (pair_p) and the P.V products (pair_pv_mma).
+// ---- the same update split for a software pipeline (tile kernels).  Scores
+// stay raw (q . k) until P is formed: the scale c > 0 (log2 units; a caller
+// folds a negative scale into the sign of Q) enters the exponent,
+// p = 2^(c s - m) in one fused multiply-add, and the reference maximum m is c
+// times the raw maximum (rounding is monotonic, so that is the maximum of the
+// scaled scores).  pair_mask sets the scores of invisible tokens to -inf and
+// is only needed for pairs that reach the candidates or the end of the range;
+// pair_max_prep takes lane maxima (straight-line, to share issue slots with
+// matrix-core work); pair_max_finish moves m and l at once when needed and
+// returns O's factor for later; pair_p forms P as a bf16 hi/lo pair; and
+// pair_pv_mma adds the P.V products.
 template <int D, int RB>
-__device__ __forceinline__ void pair_max_prep(const StreamRows<D, RB>& rows, const StreamState<D, RB>& st,
-                                              const PairScores<RB>& S, float (&x)[RB][8], bool& need, int pbase,
-                                              int L, int t1, float c, int lane) {
+__device__ __forceinline__ void pair_mask(const StreamRows<D, RB>& rows, PairScores<RB>& S, int pbase, int L,
+                                          int t1, int lane) {
   constexpr float NEG_INF = -__builtin_huge_valf();
   const int g = lane >> 4;
-  const bool plain = pbase + 2 * kPage <= min(L, t1);      // no token of the pair is masked
-  need = false;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    float pm = NEG_INF;
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int pg = e >> 2, r = e & 3;
-      float v = S.s[pg][rb][r] * c;
-      if (!plain) {
-        const int t = pbase + 16 * pg + 4 * g + r;
-        const int sh = t - L;
-        const bool cand = (unsigned)sh < 64u && ((rows.mbits[rb] >> (sh & 63)) & 1ull);
-        v = (t < t1 && (t < L || cand)) ? v : NEG_INF;
-      }
-      x[rb][e] = v;
-      pm = fmaxf(pm, v);
+      const int t = pbase + 16 * pg + 4 * g + r;
+      const int sh = t - L;
+      const bool cand = (unsigned)sh < 64u && ((rows.mbits[rb] >> (sh & 63)) & 1ull);
+      S.s[pg][rb][r] = (t < t1 && (t < L || cand)) ? S.s[pg][rb][r] : NEG_INF;
     }
-    need |= pm > st.m[rb] + kLazyTau;
+}
+
+template <int D, int RB>
+__device__ __forceinline__ void pair_max_prep(const StreamState<D, RB>& st, const PairScores<RB>& S,
+                                              float (&x)[RB][8], bool& need, float c) {
+  need = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[rb][e] = S.s[e >> 2][rb][e & 3];
+    // NaN-propagating maximum (v_maximum3_f32): no quieting of the matrix-core
+    // results first; masked scores are already -inf, visible ones finite
+    auto mx = [](float u, float v) { return __builtin_elementwise_maximum(u, v); };
+    const float pm = mx(mx(mx(x[rb][0], x[rb][1]), x[rb][2]), mx(mx(x[rb][3], x[rb][4]), x[rb][5]));
+    const float pm2 = mx(pm, mx(x[rb][6], x[rb][7]));
+    need |= c * pm2 > st.m[rb] + kLazyTau;
   }
 }
 
@@ -310,7 +322,7 @@ __device__ __forceinline__ void pair_max_prep(const StreamRows<D, RB>& rows, con
 // pair are added (l is rescaled here).
 template <int D, int RB>
 __device__ __forceinline__ bool pair_max_finish(StreamState<D, RB>& st, const float (&x)[RB][8], bool need,
-                                                float (&alpha)[RB]) {
+                                                float (&alpha)[RB], float c) {
   constexpr float NEG_INF = -__builtin_huge_valf();
   if (__builtin_amdgcn_ballot_w64(need) == 0) return false;
 #pragma unroll
@@ -320,7 +332,7 @@ __device__ __forceinline__ bool pair_max_finish(StreamState<D, RB>& st, const fl
     for (int e = 1; e < 8; ++e) pm = fmaxf(pm, x[rb][e]);
     pm = fmaxf(pm, shfl_xor(pm, 16));
     pm = fmaxf(pm, shfl_xor(pm, 32));
-    const float mnew = fmaxf(st.m[rb], pm);
+    const float mnew = fmaxf(st.m[rb], c * pm);
     alpha[rb] = fast_exp2(st.m[rb] - (mnew == NEG_INF ? 0.f : mnew));
     st.m[rb] = mnew;
     st.l[rb] *= alpha[rb];
@@ -330,15 +342,15 @@ __device__ __forceinline__ bool pair_max_finish(StreamState<D, RB>& st, const fl
 
 template <int D, int RB>
 __device__ __forceinline__ void pair_p(StreamState<D, RB>& st, const float (&x)[RB][8], bf16x8 (&phi)[RB],
-                                       bf16x8 (&plo)[RB]) {
+                                       bf16x8 (&plo)[RB], float c) {
   constexpr float NEG_INF = -__builtin_huge_valf();
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const float muse = st.m[rb] == NEG_INF ? 0.f : st.m[rb];
+    const float nm = st.m[rb] == NEG_INF ? 0.f : -st.m[rb];
     uint32_t h[4], lo[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float p0 = fast_exp2(x[rb][2 * k] - muse), p1 = fast_exp2(x[rb][2 * k + 1] - muse);
+      const float p0 = fast_exp2(fmaf(x[rb][2 * k], c, nm)), p1 = fast_exp2(fmaf(x[rb][2 * k + 1], c, nm));
       st.l[rb] += p0 + p1;
       h[k] = pack_bf16x2(p0, p1);
       lo[k] = pack_bf16x2(p0 - bf16_lo(h[k]), p1 - bf16_hi(h[k]));

@@ -208,15 +208,6 @@ __device__ __forceinline__ void lds_copy4(uint32_t lds_addr, const void* gptr) {
                : "memory", "m0");
 }
 
-// Two block-table entries through the scalar cache. The copies above are
-// opaque to the compiler, so a table read it schedules as a vector load would
-// be followed by a wait for every copy in flight; a scalar read waits only
-// for itself.
-__device__ __forceinline__ void scalar_pair(const int32_t* p0, const int32_t* p1, int& x0, int& x1) {
-  asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
-               : "=&s"(x0), "=&s"(x1) : "s"(p0), "s"(p1));
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vmem_at_most() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -283,7 +274,10 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
   const int M = a.G * qb;
   const int wrow0 = row0 + wave * 32;
   const bool wave_rows = wrow0 < M;
-  const float c = a.scale_log2;
+  // a negative scale moves into the sign of Q (exact), so c > 0 below; a zero
+  // scale becomes the smallest normal float (every visible p is then 1)
+  const bool neg_scale = a.scale_log2 < 0.f;
+  const float c = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
 
   const int32_t* table = a.tables + (int64_t)b * a.MBS;
   const char* kbase = reinterpret_cast<const char*>(a.k);
@@ -296,9 +290,8 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
   // entries (relative page e at tring[e % kRing]), 64 entries per dword DMA
   // issued by wave 0: chunks 0..3 before the loop, chunk c in the iteration
   // where the copies have just left chunk c - 4 behind, about 90 iterations
-  // before its first use.  Stage copies in the loop then read their four
-  // entries from LDS instead of waiting on the scalar cache.  The first stages
-  // read the table through the scalar cache.
+  // before its first use.  Every stage copy reads its four entries from LDS,
+  // so no copy waits on a table load.
   constexpr int kRing = 256;
   const int nch = (npg + 63) / 64;
   auto issue_chunk = [&](int ch) {
@@ -306,24 +299,15 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
     lds_copy4(tring0 + (uint32_t)((ch & 3) * 256), table + pgA + e);
   };
   const int crow = lane / Gm::UPR, cunit = lane % Gm::UPR;
-  auto copy_stage = [&](int j, bool ring) {
+  auto copy_stage = [&](int j) {
     const int kr = 2 * min(j + 1, nst - 1), vr = 2 * max(j, 0);      // relative pages
     const bool k2 = kr + 1 < npg, v2 = vr + 1 < npg;
-    int xk0, xk1, xv0, xv1;
-    if (ring) {
-      const int2 kk = *reinterpret_cast<const int2*>(tring + (kr & (kRing - 1)));
-      const int2 vv = *reinterpret_cast<const int2*>(tring + (vr & (kRing - 1)));
-      xk0 = __builtin_amdgcn_readfirstlane(kk.x);
-      xk1 = __builtin_amdgcn_readfirstlane(k2 ? kk.y : kk.x);
-      xv0 = __builtin_amdgcn_readfirstlane(vv.x);
-      xv1 = __builtin_amdgcn_readfirstlane(v2 ? vv.y : vv.x);
-    } else {
-      const int kp = pgA + kr, vp = pgA + vr;
-      scalar_pair(table + __builtin_amdgcn_readfirstlane(kp),
-                  table + __builtin_amdgcn_readfirstlane(k2 ? kp + 1 : kp), xk0, xk1);
-      scalar_pair(table + __builtin_amdgcn_readfirstlane(vp),
-                  table + __builtin_amdgcn_readfirstlane(v2 ? vp + 1 : vp), xv0, xv1);
-    }
+    const int2 kk = *reinterpret_cast<const int2*>(tring + (kr & (kRing - 1)));
+    const int2 vv = *reinterpret_cast<const int2*>(tring + (vr & (kRing - 1)));
+    const int xk0 = __builtin_amdgcn_readfirstlane(kk.x);
+    const int xk1 = __builtin_amdgcn_readfirstlane(k2 ? kk.y : kk.x);
+    const int xv0 = __builtin_amdgcn_readfirstlane(vv.x);
+    const int xv1 = __builtin_amdgcn_readfirstlane(v2 ? vv.y : vv.x);
     const uint32_t dst = lds0 + (uint32_t)(((j + 1) % NBUF) * Gm::STAGE);
 #pragma unroll
     for (int i = 0; i < Gm::CPW; ++i) {
@@ -339,30 +323,51 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
   };
   auto buf = [&](int j) { return lds + ((j + 1) % NBUF) * Gm::STAGE; };
   auto pbase = [&](int s) { return (pgA + 2 * s) * kPage; };
+  const int plain_end = min(L, t1);     // pairs ending here or before need no mask
 
-  // The query rows load behind the first stages and everything lands before
-  // the loop, so no wait on the query registers sits inside it.
+  // The first table chunks and the query rows load together (one round trip,
+  // and no wait on the query registers inside the loop); the first stages
+  // then read their entries from the ring like every later stage, and only
+  // stage -1 must land before the first score products.
   const int pro = min(NBUF, nst + 1);                // stages -1 .. pro - 2
   if (wave == 0)
     for (int ch = 0; ch < min(4, nch); ++ch) issue_chunk(ch);
-  for (int j = -1; j < pro - 1; ++j) copy_stage(j, false);
   load_rows(rows, a, b, hkv, qb, M, g, m, wrow0);
   wait_vmem_at_most<0>();
   __syncthreads();
+  if (neg_scale) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        uint4 w = __builtin_bit_cast(uint4, rows.qop[rb][kk]);
+        w.x ^= 0x80008000u;
+        w.y ^= 0x80008000u;
+        w.z ^= 0x80008000u;
+        w.w ^= 0x80008000u;
+        rows.qop[rb][kk] = __builtin_bit_cast(bf16x8, w);
+      }
+  }
+  for (int j = -1; j < pro - 1; ++j) copy_stage(j);
+  wait_stages<Gm::CPW, NBUF - 1>(pro - 1);
+  __syncthreads();
 
-  float x[RB][8];                    // masked scores of the pair whose P comes next, log2 units
+  // masked raw scores of the pair whose P comes next, in two register sets
+  // that alternate between iterations (no copy from the score accumulators)
+  float xa[RB][8], xb[RB][8];
   float alpha[RB] = {1.f, 1.f};      // O's factor owed before the next P.V
   bool pend = false;
   if (wave_rows) {
     PairScores<RB> sc;
     pair_scores<D, RB, true>(rows, sc, buf(-1), buf(-1) + Gm::TILE, lane);
+    if (pbase(0) + 2 * kPage > plain_end) pair_mask<D, RB>(rows, sc, pbase(0), L, t1, lane);
     bool need;
-    pair_max_prep<D, RB>(rows, st, sc, x, need, pbase(0), L, t1, c, lane);
-    pair_max_finish<D, RB>(st, x, need, alpha);     // O is still zero: its factor is moot
+    pair_max_prep<D, RB>(st, sc, xa, need, c);
+    pair_max_finish<D, RB>(st, xa, need, alpha, c);  // O is still zero: its factor is moot
   }
 
-  // One iteration of the pipeline.
-  auto step = [&](int s, char* sb) {
+  // One iteration of the pipeline: P of pair s from x, scores of pair s + 1 into xn.
+  auto step = [&](int s, char* sb, float (&x)[RB][8], float (&xn)[RB][8]) {
     if (pend) {                       // the factor owed since pair s's maximum moved
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
@@ -373,16 +378,18 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
     PairScores<RB> sn;
     pair_scores<D, RB, true>(rows, sn, sb, sb + Gm::TILE, lane);
     bf16x8 phi[RB], plo[RB];
-    pair_p<D, RB>(st, x, phi, plo);
+    pair_p<D, RB>(st, x, phi, plo, c);
     // 2. P.V of pair s with the masked scores of pair s + 1
     pair_pv_mma<D, RB, true>(st, phi, plo, sb + 2 * Gm::TILE, sb + 3 * Gm::TILE, lane);
+    if (pbase(s + 1) + 2 * kPage > plain_end) pair_mask<D, RB>(rows, sn, pbase(s + 1), L, t1, lane);
     bool need;
-    pair_max_prep<D, RB>(rows, st, sn, x, need, pbase(s + 1), L, t1, c, lane);
+    pair_max_prep<D, RB>(st, sn, xn, need, c);
     // 3. the rare reference-max move for pair s + 1
-    pend = pair_max_finish<D, RB>(st, x, need, alpha);
+    pend = pair_max_finish<D, RB>(st, xn, need, alpha, c);
   };
 
-  for (int s = 0; s < nst; ++s) {
+  // One stage: wait, the tail's V zeroing, the next copies, the step.
+  auto stage = [&](int s, float (&x)[RB][8], float (&xn)[RB][8]) {
     wait_stages<Gm::CPW, NBUF - 2>(min(NBUF - 2, nst - 1 - s));
     __syncthreads();        // stage s in LDS for all waves; stage s - 1 fully consumed
     char* sb = buf(s);
@@ -403,8 +410,12 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
       const int ch = (s + NBUF - 1) / 32 + 3;
       if (ch < nch) issue_chunk(ch);
     }
-    if (s + NBUF - 1 < nst) copy_stage(s + NBUF - 1, true);     // into the buffer stage s - 1 used
-    if (wave_rows) step(s, sb);
+    if (s + NBUF - 1 < nst) copy_stage(s + NBUF - 1);     // into the buffer stage s - 1 used
+    if (wave_rows) step(s, sb, x, xn);
+  };
+  for (int s = 0; s < nst; s += 2) {
+    stage(s, xa, xb);
+    if (s + 1 < nst) stage(s + 1, xb, xa);
   }
   reduce_row_sums(st);
 }
@@ -538,6 +549,10 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
         l = a.part_lse + r;
       };
       store_partial_rows(rows, st, g, addr);
+      if (a.merge_after) {
+        x += k1 - k0;           // tile_merge_kernel combines the unit's slices
+        continue;
+      }
       __builtin_amdgcn_s_waitcnt(0);             // partial stores complete before the arrival
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __syncthreads();
@@ -557,6 +572,113 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     x += k1 - k0;
   }
+}
+
+// ---------------------------------------------------------------- slice merge
+// Units cut into many slices (long contexts over few (sequence, KV head)
+// units) are merged by this second launch instead of by their last slice: one
+// workgroup per (unit, 32-row block), all slices of the unit read at once
+// with plain 16-byte loads (the attention launch has completed), combined by
+// log-sum-exp in slice order like the in-launch merge.  Slice bounds are
+// recomputed from the same page line as the attention launch (NS slices per
+// row group at most).
+template <typename QT, int D>
+__global__ __launch_bounds__(256) void tile_merge_kernel(AttnArgs a, int NS) {
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  constexpr int TPR = 8;                  // threads per row
+  constexpr int IPT = D / 4 / TPR;        // 16-byte items per thread
+  constexpr int PB = 8;                   // slices per batch
+  __shared__ int red[2][4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int Rmax = a.G * a.Qmax;
+  const int nblk = (Rmax + 31) / 32;
+  const int u = blockIdx.x / nblk, rblk = blockIdx.x % nblk;
+  const int b = u / a.Hkv, hkv = u % a.Hkv;
+  const int qb = a.qlen[b];
+  const int M = a.G * qb;
+  if (rblk * 32 >= M) return;
+
+  int before = 0, total = 0;              // pages of sequences < b, of all sequences
+  for (int j = tid; j < a.B; j += 256) {
+    const int p = (a.ctx[j] + kPage - 1) / kPage;
+    total += p;
+    before += j < b ? p : 0;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    before += __shfl_xor(before, o, 64);
+    total += __shfl_xor(total, o, 64);
+  }
+  if (lane == 0) {
+    red[0][wv] = before;
+    red[1][wv] = total;
+  }
+  __syncthreads();
+  before = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  total = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const int Pb = (a.ctx[b] + kPage - 1) / kPage;
+  const int64_t W = (int64_t)a.Hkv * total;
+  const int64_t N = min((int64_t)NS, max((int64_t)1, W / kMinSlicePages));
+  const int64_t S = (int64_t)a.Hkv * before + (int64_t)hkv * Pb;
+  auto wg_of = [&](int64_t x) -> int64_t { return ((x + 1) * N - 1) / W; };
+  const int64_t wfirst = wg_of(S);
+  const int np = (int)(wg_of(S + Pb - 1) - wfirst + 1);
+  if (np == 1) return;                    // the attention launch wrote this unit's rows
+  const int r = rblk * 32 + tid / TPR;
+  if (r >= M) return;
+  const int d0 = (tid % TPR) * IPT * 4;
+
+  float mrun = NEG_INF, wsum = 0.f;
+  f32x4 acc[IPT];
+#pragma unroll
+  for (int k = 0; k < IPT; ++k) acc[k] = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < np; p0 += PB) {
+    float lp[PB];
+    f32x4 op[PB][IPT];
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const bool ok = p0 + j < np;
+      const int64_t rr = (wfirst + (ok ? p0 + j : 0) + u) * Rmax + r;
+      lp[j] = ok ? a.part_lse[rr] : NEG_INF;
+#pragma unroll
+      for (int k = 0; k < IPT; ++k)
+        op[j][k] = ok ? *reinterpret_cast<const f32x4*>(a.part_o + rr * D + d0 + 4 * k) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float mx = mrun;
+#pragma unroll
+    for (int j = 0; j < PB; ++j) mx = fmaxf(mx, lp[j]);
+    const float muse = mx == NEG_INF ? 0.f : mx;
+    const float alpha = __expf(mrun - muse);
+    wsum *= alpha;
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) acc[k] *= alpha;
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const float w = __expf(lp[j] - muse);
+      wsum += w;
+#pragma unroll
+      for (int k = 0; k < IPT; ++k) acc[k] += w * op[j][k];
+    }
+    mrun = mx;
+  }
+  const float muse = mrun == NEG_INF ? 0.f : mrun;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int h = hkv * a.G + r / qb, i = r % qb;
+  const int64_t o = (((int64_t)b * a.Qmax + i) * a.Hq + h) * D + d0;
+#pragma unroll
+  for (int k = 0; k < IPT; ++k) {
+    const f32x4 res = acc[k] * inv;
+    if constexpr (QT::bytes == 4) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o + 4 * k) = res;
+    } else {
+      uint2 w;
+      w.x = pack_bf16x2(res[0], res[1]);
+      w.y = pack_bf16x2(res[2], res[3]);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + o + 4 * k) = w;
+    }
+  }
+  if (d0 == 0 && a.lse != nullptr)
+    a.lse[((int64_t)b * a.Hq + h) * a.Qmax + i] = wsum > 0.f ? muse + __logf(wsum) : NEG_INF;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -613,6 +735,11 @@ static hipError_t tile_balanced_t(const AttnArgs* a, int B, int* nwg, hipStream_
     return hipSuccess;
   }
   hipLaunchKernelGGL((tile_balanced_kernel<D, NWR, NBUF>), dim3((unsigned)*nwg), dim3(NWR * 64), dyn, s, *a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a->merge_after) return e;
+  const int RG = (a->G * a->Qmax + NWR * 32 - 1) / (NWR * 32);
+  const int64_t blocks = (int64_t)a->B * a->Hkv * ((a->G * a->Qmax + 31) / 32);
+  hipLaunchKernelGGL((tile_merge_kernel<BF16, D>), dim3((unsigned)blocks), dim3(256), 0, s, *a, *nwg / RG);
   return hipGetLastError();
 }
 

@@ -396,6 +396,10 @@ BALANCED = [
     ("bal_tile_d64", spec("bt", 5, 16, 4, 64, "bf16", "bf16", (1, 1800), 20, "random", ragged=True, seed=124)),
     ("bal_tile_rows48", spec("bt", 6, 8, 2, 128, "bf16", "bf16", (12, 2200), 12, "random", seed=125)),
     ("bal_tile_tiny_units", spec("bt", 50, 16, 2, 128, "bf16", "bf16", (8, 40), 8, "chain", seed=126)),
+    # many (sequence, KV head) units: split units merged by their last slice inside the launch
+    # (the cases above have few units and merge in a second launch)
+    ("bal_tile_inline_merge", spec("bt", 40, 32, 4, 128, "bf16", "bf16", (16, 3000), 16, "random", 6,
+                                   seed=127)),
 ]
 
 
