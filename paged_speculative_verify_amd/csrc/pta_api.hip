@@ -159,10 +159,9 @@ bool split_layout(const pta_dims* d, int32_t T, SplitLayout* L) {
 //     per wave, nw = 4 waves per workgroup).
 //   tile family (bf16 KV): nw waves of 32 rows per workgroup (2 or 4), rg row groups per
 //     slice, ns slices (a multiple of 8 with ns * rg workgroups fitting the device at
-//     once); counters B*Hkv*rg, S = ns + B*Hkv slots.
+//     once); no counters (a second launch merges), S = ns + B*Hkv slots.
 struct BalancedLayout {
   int nwg, nw, rg;
-  int merge_after;      // tile path: slices merged by a second launch
   size_t o_off, lse_off, total;
 };
 
@@ -184,11 +183,7 @@ pta_status tile_balanced_layout(const pta_dims* d, BalancedLayout* L) {
   L->nwg = ns * rg;
   L->nw = nw;
   L->rg = rg;
-  // With more than four slices per (unit, row group) on average the last
-  // slice's merge would read many partials alone at the end of the launch;
-  // a second launch spreads those merges over the whole device instead.
-  L->merge_after = units * rg * 4 < ns * rg ? 1 : 0;
-  L->o_off = up((size_t)units * rg * sizeof(int32_t));
+  L->o_off = 0;
   L->lse_off = L->o_off + up((size_t)slot_rows * d->head_dim * sizeof(float));
   L->total = L->lse_off + up((size_t)slot_rows * sizeof(float));
   return PTA_OK;
@@ -212,7 +207,6 @@ pta_status balanced_layout(const pta_dims* d, const Plan& p, BalancedLayout* L) 
   L->nwg = nwg;
   L->nw = nw;
   L->rg = 1;
-  L->merge_after = 0;
   L->o_off = up((size_t)units * sizeof(int32_t));
   L->lse_off = L->o_off + up((size_t)rows * d->head_dim * sizeof(float));
   L->total = L->lse_off + up((size_t)rows * sizeof(float));
@@ -325,7 +319,6 @@ pta_status taco_paged_tree_attn_balanced(const pta_dims* d, const void* q, const
   a.part_o = reinterpret_cast<float*>(ws + L.o_off);
   a.part_lse = reinterpret_cast<float*>(ws + L.lse_off);
   a.total_waves = L.nwg * L.nw;
-  a.merge_after = L.merge_after;
   int nwg = L.nwg;
   if (p.fam == FAM_TILE)
     return tile_balanced(&a, d->head_dim, L.nw, d->num_seqs, &nwg, (hipStream_t)stream) == hipSuccess

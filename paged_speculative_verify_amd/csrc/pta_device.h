@@ -38,7 +38,6 @@ struct AttnArgs {
   float* part_lse;         // split-K partial LSE     [B][Hq][Qmax][P]
   int32_t* counters;       // split-K arrival counters [B][Hkv] (zero between calls)
   int32_t total_waves;     // balanced mode: waves in the persistent grid
-  int32_t merge_after;     // balanced tile mode: partial rows merged by a second launch
   float scale_log2;        // softmax scale * log2(e)
   int32_t B, Hq, Hkv, G, Qmax, MBS;
   int32_t part_tokens;     // partition length in tokens (split) or 0

@@ -471,15 +471,17 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
 // apart: workgroups are handed to the 8 XCDs in turn, so they share an XCD
 // and its L2, and the KV pages reach L2 from HBM once.  A slice that covers a
 // whole unit writes its rows; otherwise it stores a normalised partial in
-// slot w + u (unique: slices and units are both ordered along the line) and
-// the unit's last slice to arrive merges them in slice order.
+// slot w + u (unique: slices and units are both ordered along the line), and
+// tile_merge_kernel, launched right after, merges them in slice order.
+// (Merging inside this launch, by the unit's last slice, leaves a few
+// workgroups reading many partials at the end of the launch while the rest of
+// the device idles.)
 template <int D, int NWR, int NBUF>
 __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) void tile_balanced_kernel(AttnArgs a) {
   using Gm = DmaGeom<D, NWR, NBUF>;
   __shared__ __attribute__((aligned(1024))) char lds[Gm::LDS_BYTES];
   __shared__ __attribute__((aligned(16))) int tring[256];
   __shared__ int wave_tot[NWR];
-  __shared__ int s_last;
   extern __shared__ int ps[];       // [B + 1]
 
   const int tid = threadIdx.x;
@@ -499,7 +501,6 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   const int64_t W = (int64_t)a.Hkv * __builtin_amdgcn_readfirstlane(ps[B]);
   const int64_t N = min(NS, max((int64_t)1, W / kMinSlicePages));
   if (w >= N) return;
-  auto wg_of = [&](int64_t x) -> int64_t { return ((x + 1) * N - 1) / W; };
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&lds[0];
   const uint32_t tring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)&tring[0];
   const int row0 = rg * NWR * 32;
@@ -527,47 +528,22 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     const int qb = a.qlen[b];
     const int M = a.G * qb;
 
-    __syncthreads();          // LDS stage buffers and s_last free from the previous unit
+    __syncthreads();          // LDS stage buffers free from the previous unit
     StreamRows<D, 2> rows;
     StreamState<D, 2> st;
     st.init();
-    if (row0 < M)
+    if (row0 < M) {
       dma_range<D, NWR, NBUF>(a, lds, lds0, tring, tring0, rows, st, b, hkv, qb, row0, k0 * kPage,
                               min(C, k1 * kPage), wave, lane);
-
-    if (row0 >= M) {
-      // no rows of this unit in this row group (shorter tree than the widest)
-    } else if (k0 == 0 && k1 == Pb) {
-      store_final_rows(a, rows, st, b, g);        // the whole unit in this slice
-    } else {
-      const int64_t S = (int64_t)a.Hkv * psb + (int64_t)hkv * Pb;
-      const int64_t wfirst = wg_of(S), wlast = wg_of(S + Pb - 1);
-      const int np = (int)(wlast - wfirst + 1);
-      auto addr = [&](int rb, float*& o, float*& l) {
-        const int64_t r = (w + u) * Rmax + row0 + wave * 32 + rb * 16 + m;
-        o = a.part_o + r * D;
-        l = a.part_lse + r;
-      };
-      store_partial_rows(rows, st, g, addr);
-      if (a.merge_after) {
-        x += k1 - k0;           // tile_merge_kernel combines the unit's slices
-        continue;
-      }
-      __builtin_amdgcn_s_waitcnt(0);             // partial stores complete before the arrival
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __syncthreads();
-      int32_t* cnt = a.counters + (int64_t)u * RG + rg;
-      if (tid == 0)
-        s_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
-      __syncthreads();
-      if (s_last) {
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        auto pslot = [&](int r, int p) {
-          const int64_t rr = (wfirst + p + u) * Rmax + r;
-          return PartSlot{a.part_o + rr * D, a.part_lse + rr};
+      if (k0 == 0 && k1 == Pb) {
+        store_final_rows(a, rows, st, b, g);        // the whole unit in this slice
+      } else {
+        auto addr = [&](int rb, float*& o, float*& l) {
+          const int64_t r = (w + u) * Rmax + row0 + wave * 32 + rb * 16 + m;
+          o = a.part_o + r * D;
+          l = a.part_lse + r;
         };
-        merge_rows<BF16, D>(a, b, hkv, qb, min(M, row0 + NWR * 32), np, pslot, tid, NWR * 64, row0);
-        if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        store_partial_rows(rows, st, g, addr);
       }
     }
     x += k1 - k0;
@@ -575,13 +551,11 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // ---------------------------------------------------------------- slice merge
-// Units cut into many slices (long contexts over few (sequence, KV head)
-// units) are merged by this second launch instead of by their last slice: one
-// workgroup per (unit, 32-row block), all slices of the unit read at once
-// with plain 16-byte loads (the attention launch has completed), combined by
-// log-sum-exp in slice order like the in-launch merge.  Slice bounds are
-// recomputed from the same page line as the attention launch (NS slices per
-// row group at most).
+// Second launch of the balanced tile grid: one workgroup per (unit, 32-row
+// block) merges the partials of a unit cut into several slices, all slices
+// read at once with plain 16-byte loads (the attention launch has completed)
+// and combined by log-sum-exp in slice order.  Slice bounds are recomputed
+// from the same page line as the attention launch (NS slices at most).
 template <typename QT, int D>
 __global__ __launch_bounds__(256) void tile_merge_kernel(AttnArgs a, int NS) {
   constexpr float NEG_INF = -__builtin_huge_valf();
@@ -736,7 +710,7 @@ static hipError_t tile_balanced_t(const AttnArgs* a, int B, int* nwg, hipStream_
   }
   hipLaunchKernelGGL((tile_balanced_kernel<D, NWR, NBUF>), dim3((unsigned)*nwg), dim3(NWR * 64), dyn, s, *a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !a->merge_after) return e;
+  if (e != hipSuccess) return e;
   const int RG = (a->G * a->Qmax + NWR * 32 - 1) / (NWR * 32);
   const int64_t blocks = (int64_t)a->B * a->Hkv * ((a->G * a->Qmax + 31) / 32);
   hipLaunchKernelGGL((tile_merge_kernel<BF16, D>), dim3((unsigned)blocks), dim3(256), 0, s, *a, *nwg / RG);

@@ -396,8 +396,7 @@ BALANCED = [
     ("bal_tile_d64", spec("bt", 5, 16, 4, 64, "bf16", "bf16", (1, 1800), 20, "random", ragged=True, seed=124)),
     ("bal_tile_rows48", spec("bt", 6, 8, 2, 128, "bf16", "bf16", (12, 2200), 12, "random", seed=125)),
     ("bal_tile_tiny_units", spec("bt", 50, 16, 2, 128, "bf16", "bf16", (8, 40), 8, "chain", seed=126)),
-    # many (sequence, KV head) units: split units merged by their last slice inside the launch
-    # (the cases above have few units and merge in a second launch)
+    # many (sequence, KV head) units, most of them cut into two or three slices
     ("bal_tile_inline_merge", spec("bt", 40, 32, 4, 128, "bf16", "bf16", (16, 3000), 16, "random", 6,
                                    seed=127)),
 ]
@@ -453,8 +452,7 @@ def test_balanced_rejects_unserved_dims(torch_cuda):
 
 def test_balanced_tile_repeat_and_workspace_reuse(torch_cuda):
     """Shared-tile balanced grid with two row groups: repeated calls on one workspace are
-    bit-identical, unchanged by a relabelling of physical pages, and leave every arrival
-    counter (one per unit and row group) at zero."""
+    bit-identical and unchanged by a relabelling of physical pages."""
     import torch
     import paged_speculative_verify_amd as psv
     w = make(spec("rt", 3, 64, 8, 128, "bf16", "bf16", (500, 12000), 32, "random", 8, seed=131))
@@ -468,8 +466,6 @@ def test_balanced_tile_repeat_and_workspace_reuse(torch_cuda):
     b1, m1 = run_gpu(torch_cuda, permute_pool(w, 9), mode="balanced", workspace=ws)
     assert np.array_equal(a1, a2, equal_nan=True) and np.array_equal(l1, l2, equal_nan=True)
     assert np.array_equal(a1, b1, equal_nan=True) and np.array_equal(l1, m1, equal_nan=True)
-    U = w.q.shape[0] * w.k_cache.shape[1] * 2
-    assert int(ws[:4 * U].view(torch.int32).abs().sum()) == 0, "arrival counters not reset"
     ref, ref_lse = run_oracle(w)
     assert_parity(w, a1, l1, ref, ref_lse)
 
