@@ -93,6 +93,28 @@ __device__ __forceinline__ void load_rows(StreamRows<D, RB>& R, const AttnArgs& 
     }
     R.mbits[rb] = R.ok[rb] ? load_mask_row(a.mask, b, R.i[rb], qb, a.Qmax) : 0ull;
   }
+  // A negative scale moves into the sign of Q (exact: every score just changes
+  // sign), so the score scale c = |scale| log2(e) used below is positive.
+  if (a.scale_log2 < 0.f) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        uint4 w = __builtin_bit_cast(uint4, R.qop[rb][kk]);
+        w.x ^= 0x80008000u;
+        w.y ^= 0x80008000u;
+        w.z ^= 0x80008000u;
+        w.w ^= 0x80008000u;
+        R.qop[rb][kk] = __builtin_bit_cast(bf16x8, w);
+      }
+  }
+}
+
+// Positive score scale (log2 units) of a page: |scale| log2(e) times the
+// page's K scale, at least the smallest normal float (a zero scale then gives
+// every visible token p = 1, as it should, and -inf scores stay -inf).
+__device__ __forceinline__ float score_scale(const AttnArgs& a, float kscale) {
+  return fmaxf(fabsf(a.scale_log2) * kscale, 1.17549435e-38f);
 }
 
 // Flash state of a lane's rows: O^T accumulators (dims 16 db + 4 g + r), the
@@ -128,19 +150,14 @@ __device__ __forceinline__ int tile_off(int r, int u) {
 }
 
 // Two consecutive pages of the flash update at once (tiles kl0/vl0 and
-// kl1/vl1, first token at pbase): S^T = K Q^T per page, one lazy
-// max check over both, and a single 32-token O^T += V^T P^T step with
+// kl1/vl1, first token at pbase): S^T = K Q^T per page, one lazy max check
+// over both, and a single 32-token O^T += V^T P^T step with
 // v_mfma_f32_16x16x32_bf16 (full rate on gfx950, where the 16-token
 // instruction runs at half rate).  The k index of that step runs over tokens
 // {4 g + e, 16 + 4 g + e} for lane group g: the B operand is the lane's two
 // S^T accumulators (P as a bf16 hi/lo pair) and the A operand is two
 // ds_read_b64_tr_b16 reads, one from each V tile.  A missing second page must
 // be presented with its V tile zeroed and its tokens at or past t1 (masked).
-//
-// The update is split in three phases so that a caller can issue the score
-// products of the next pair while this pair's softmax runs on the vector ALU:
-// pair_scores (matrix core), pair_softmax (masking, lazy max, rescale) and
-// pair_pv (P in bf16 hi/lo, O^T += V^T P^T).
 template <int RB>
 struct PairScores {
   f32x4 s[2][RB];     // [page][row block]: lane holds tokens 4 g + r of the page, row m
@@ -165,110 +182,6 @@ __device__ __forceinline__ void pair_scores(const StreamRows<D, RB>& rows, PairS
       S.s[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, rows.qop[rb][kk], S.s[0][rb], 0, 0, 0);
       S.s[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, rows.qop[rb][kk], S.s[1][rb], 0, 0, 0);
     }
-  }
-}
-
-// Scores in log2 units (page scales c0, c1), masked by select, and the lazy
-// reference-max update with its rescale of O and l.  Rows a lane does not own
-// have zero queries, so their finite scores need no mask.
-template <int D, int RB>
-__device__ __forceinline__ void pair_softmax(const StreamRows<D, RB>& rows, StreamState<D, RB>& st,
-                                             const PairScores<RB>& S, float (&x)[RB][8], int pbase, int L,
-                                             int t1, float c0, float c1, int lane) {
-  constexpr int DB = D / 16;
-  constexpr float NEG_INF = -__builtin_huge_valf();
-  const int g = lane >> 4;
-  const bool plain = pbase + 2 * kPage <= min(L, t1);
-  bool need = false;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    float pm = NEG_INF;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int pg = e >> 2, r = e & 3;
-      float v = S.s[pg][rb][r] * (pg ? c1 : c0);
-      if (!plain) {
-        const int t = pbase + 16 * pg + 4 * g + r;
-        const int sh = t - L;
-        const bool cand = (unsigned)sh < 64u && ((rows.mbits[rb] >> (sh & 63)) & 1ull);
-        v = (t < t1 && (t < L || cand)) ? v : NEG_INF;
-      }
-      x[rb][e] = v;
-      pm = fmaxf(pm, v);
-    }
-    need |= pm > st.m[rb] + kLazyTau;
-  }
-  if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float pm = x[rb][0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) pm = fmaxf(pm, x[rb][e]);
-      pm = fmaxf(pm, shfl_xor(pm, 16));
-      pm = fmaxf(pm, shfl_xor(pm, 32));
-      const float mnew = fmaxf(st.m[rb], pm);
-      const float alpha = fast_exp2(st.m[rb] - (mnew == NEG_INF ? 0.f : mnew));
-      st.m[rb] = mnew;
-      st.l[rb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) st.o[rb][db] *= alpha;
-    }
-  }
-}
-
-// P = 2^(x - m) as a bf16 hi/lo pair over the lane's 8 tokens (times the
-// pages' V scales vs0, vs1), then O^T += V^T P^T over the 32 tokens.
-template <int D, int RB, bool SWZ>
-__device__ __forceinline__ void pair_pv(StreamState<D, RB>& st, const float (&x)[RB][8], const char* vl0,
-                                        const char* vl1, float vs0, float vs1, int lane) {
-  constexpr int DB = D / 16;
-  constexpr float NEG_INF = -__builtin_huge_valf();
-  const int g = lane >> 4, m = lane & 15;
-  bf16x8 phi[RB], plo[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float muse = st.m[rb] == NEG_INF ? 0.f : st.m[rb];
-    uint32_t h[4], lo[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e0 = 2 * k, e1 = 2 * k + 1;
-      float p0 = fast_exp2(x[rb][e0] - muse), p1 = fast_exp2(x[rb][e1] - muse);
-      st.l[rb] += p0 + p1;
-      const float v = k < 2 ? vs0 : vs1;
-      p0 *= v;
-      p1 *= v;
-      h[k] = pack_bf16x2(p0, p1);
-      lo[k] = pack_bf16x2(p0 - bf16_lo(h[k]), p1 - bf16_hi(h[k]));
-    }
-    phi[rb] = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
-    plo[rb] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
-  }
-  const int vrow = 4 * g + (m >> 2);
-  // two output blocks at a time: the hi and lo products of one accumulator are
-  // 2 * RB instructions apart
-#pragma unroll
-  for (int db = 0; db < DB; db += 2) {
-    bf16x8 vt[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int voff = tile_off<D, SWZ>(vrow, 2 * (db + e) + ((m & 3) >> 1)) + 8 * (m & 1);
-      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl0 + voff));
-      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl1 + voff));
-      vt[e] = __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint2, va).x,
-                                                   __builtin_bit_cast(uint2, va).y,
-                                                   __builtin_bit_cast(uint2, vb).x,
-                                                   __builtin_bit_cast(uint2, vb).y));
-    }
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        st.o[rb][db + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[e], phi[rb], st.o[rb][db + e], 0, 0, 0);
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        st.o[rb][db + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[e], plo[rb], st.o[rb][db + e], 0, 0, 0);
   }
 }
 
@@ -393,16 +306,67 @@ __device__ __forceinline__ void pair_pv_mma(StreamState<D, RB>& st, const bf16x8
   }
 }
 
-template <int D, int RB, bool SWZ = false>
+// The whole update of one pair for kernels that do not pipeline it: page
+// score scales c0, c1 > 0 (score_scale), V scales vs0, vs1 folded into P when
+// VS (fp8 pages).  Raw maxima are taken per page and scaled once.
+template <int D, int RB, bool SWZ, bool VS>
 __device__ __forceinline__ void pair_compute(const StreamRows<D, RB>& rows, StreamState<D, RB>& st,
                                              const char* kl0, const char* kl1, const char* vl0,
                                              const char* vl1, int pbase, int L, int t1, float c0,
                                              float c1, float vs0, float vs1, int lane) {
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  constexpr int DB = D / 16;
   PairScores<RB> S;
   pair_scores<D, RB, SWZ>(rows, S, kl0, kl1, lane);
-  float x[RB][8];
-  pair_softmax<D, RB>(rows, st, S, x, pbase, L, t1, c0, c1, lane);
-  pair_pv<D, RB, SWZ>(st, x, vl0, vl1, vs0, vs1, lane);
+  if (pbase + 2 * kPage > min(L, t1)) pair_mask<D, RB>(rows, S, pbase, L, t1, lane);
+  auto mx = [](float u, float v) { return __builtin_elementwise_maximum(u, v); };
+  float xm[RB];
+  bool need = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float pm0 = mx(mx(S.s[0][rb][0], S.s[0][rb][1]), mx(S.s[0][rb][2], S.s[0][rb][3]));
+    const float pm1 = mx(mx(S.s[1][rb][0], S.s[1][rb][1]), mx(S.s[1][rb][2], S.s[1][rb][3]));
+    xm[rb] = fmaxf(c0 * pm0, c1 * pm1);
+    need |= xm[rb] > st.m[rb] + kLazyTau;
+  }
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float pm = xm[rb];
+      pm = fmaxf(pm, shfl_xor(pm, 16));
+      pm = fmaxf(pm, shfl_xor(pm, 32));
+      const float mnew = fmaxf(st.m[rb], pm);
+      const float alpha = fast_exp2(st.m[rb] - (mnew == NEG_INF ? 0.f : mnew));
+      st.m[rb] = mnew;
+      st.l[rb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) st.o[rb][db] *= alpha;
+    }
+  }
+  bf16x8 phi[RB], plo[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float nm = st.m[rb] == NEG_INF ? 0.f : -st.m[rb];
+    uint32_t h[4], lo[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int pg = k >> 1;
+      const float c = pg ? c1 : c0;
+      float p0 = fast_exp2(fmaf(S.s[pg][rb][(2 * k) & 3], c, nm));
+      float p1 = fast_exp2(fmaf(S.s[pg][rb][(2 * k + 1) & 3], c, nm));
+      st.l[rb] += p0 + p1;
+      if constexpr (VS) {
+        const float v = pg ? vs1 : vs0;
+        p0 *= v;
+        p1 *= v;
+      }
+      h[k] = pack_bf16x2(p0, p1);
+      lo[k] = pack_bf16x2(p0 - bf16_lo(h[k]), p1 - bf16_hi(h[k]));
+    }
+    phi[rb] = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+    plo[rb] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+  }
+  pair_pv_mma<D, RB, SWZ>(st, phi, plo, vl0, vl1, lane);
 }
 
 // Row sums over the lane's four 16-lane groups (every group holds 4 of each

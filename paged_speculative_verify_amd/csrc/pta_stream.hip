@@ -106,14 +106,15 @@ __device__ __forceinline__ void stream_pairs(const AttnArgs& a, const StreamRows
   issue(0);
   for (int idx = 0; idx < n; ++idx) {
     const int pb0 = (pA + 2 * (j0 + idx * js)) * kPage;
-    const float c0 = a.scale_log2 * R.ks[0], c1 = a.scale_log2 * R.ks[1];
+    const float c0 = score_scale(a, R.ks[0]), c1 = score_scale(a, R.ks[1]);
     const float vs0 = R.vs[0], vs1 = R.vs[1];
     stage_tile<KT, D>(k0l, R.k[0], lane, false, kPage);
     stage_tile<KT, D>(k1l, R.k[1], lane, false, kPage);
     stage_tile<KT, D>(v0l, R.v[0], lane, pb0 + kPage > t_end, t_end - pb0);
     stage_tile<KT, D>(v1l, R.v[1], lane, pb0 + 2 * kPage > t_end, t_end - pb0 - kPage);
     issue(min(idx + 1, n - 1));
-    pair_compute<D, RB, false>(rows, st, k0l, k1l, v0l, v1l, pb0, L, t_end, c0, c1, vs0, vs1, lane);
+    pair_compute<D, RB, false, KT::bytes == 1>(rows, st, k0l, k1l, v0l, v1l, pb0, L, t_end, c0, c1, vs0, vs1,
+                                               lane);
   }
 }
 

@@ -128,10 +128,11 @@ __global__ __launch_bounds__(NWR * 64) void tile_attn_kernel(AttnArgs a) {
   auto compute = [&](int s, int buf, const Scales& sc) {
     if (!wave_rows) return;
     const char* kl = lds[buf];
-    const float cs = a.scale_log2;
     // a missing second page has its V tile zeroed and its tokens past t1
-    pair_compute<D, RB>(rows, st, kl, kl + T::TILE_LDS, kl + 2 * T::TILE_LDS, kl + 3 * T::TILE_LDS,
-                        (pgA + 2 * s) * kPage, L, t1, cs * sc.k0, cs * sc.k1, sc.v0, sc.v1, lane);
+    pair_compute<D, RB, false, KT::bytes == 1>(rows, st, kl, kl + T::TILE_LDS, kl + 2 * T::TILE_LDS,
+                                               kl + 3 * T::TILE_LDS, (pgA + 2 * s) * kPage, L, t1,
+                                               score_scale(a, sc.k0), score_scale(a, sc.k1), sc.v0, sc.v1,
+                                               lane);
   };
 
   // Pipeline: LDS buffer s & 1 holds stage s while stage s + 1 sits in
@@ -274,10 +275,7 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
   const int M = a.G * qb;
   const int wrow0 = row0 + wave * 32;
   const bool wave_rows = wrow0 < M;
-  // a negative scale moves into the sign of Q (exact), so c > 0 below; a zero
-  // scale becomes the smallest normal float (every visible p is then 1)
-  const bool neg_scale = a.scale_log2 < 0.f;
-  const float c = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
+  const float c = score_scale(a, 1.f);     // Q carries the sign of a negative scale
 
   const int32_t* table = a.tables + (int64_t)b * a.MBS;
   const char* kbase = reinterpret_cast<const char*>(a.k);
@@ -335,19 +333,6 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
   load_rows(rows, a, b, hkv, qb, M, g, m, wrow0);
   wait_vmem_at_most<0>();
   __syncthreads();
-  if (neg_scale) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) {
-        uint4 w = __builtin_bit_cast(uint4, rows.qop[rb][kk]);
-        w.x ^= 0x80008000u;
-        w.y ^= 0x80008000u;
-        w.z ^= 0x80008000u;
-        w.w ^= 0x80008000u;
-        rows.qop[rb][kk] = __builtin_bit_cast(bf16x8, w);
-      }
-  }
   for (int j = -1; j < pro - 1; ++j) copy_stage(j);
   wait_stages<Gm::CPW, NBUF - 1>(pro - 1);
   __syncthreads();

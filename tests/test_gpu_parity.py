@@ -481,3 +481,28 @@ def test_balanced_tile_path_small_rows(torch_cuda, cid, sp):
     ref, ref_lse = run_oracle(w)
     err = assert_parity(w, out, lse, ref, ref_lse)
     say(cid, "max abs err", err)
+
+
+# -------------------------------------------------------------- sign and zero of the scale
+# The matrix-core paths fold a negative scale into the sign of Q and clamp a zero scale to
+# the smallest normal float; both must still give the plain softmax(scale * q.k) result.
+SCALE_CASES = [
+    ("stream_whole", spec("sc", 4, 16, 4, 128, "bf16", "bf16", (20, 900), 4, "random", seed=151), "whole", "mfma"),
+    ("stream_fp8_bal", spec("sc", 4, 32, 8, 128, "bf16", "fp8", (20, 900), 4, "chain", seed=152), "balanced",
+     "auto"),
+    ("tile_whole", spec("sc", 3, 32, 4, 128, "bf16", "bf16", (20, 900), 16, "random", seed=153), "whole", "tile"),
+    ("tile_bal", spec("sc", 3, 32, 4, 128, "bf16", "bf16", (20, 900), 16, "random", seed=154), "balanced", "auto"),
+    ("tile_fp8", spec("sc", 3, 32, 4, 128, "bf16", "fp8", (20, 900), 16, "random", seed=155), "whole", "tile"),
+]
+
+
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0], ids=["negative", "zero"])
+@pytest.mark.parametrize("cid,sp,mode,path", SCALE_CASES, ids=[c[0] for c in SCALE_CASES])
+def test_scale_sign_and_zero(torch_cuda, cid, sp, mode, path, scale):
+    import dataclasses
+    w = make(dataclasses.replace(sp, scale=scale), poison=True)
+    say(cid, "scale", scale, "mode", mode, "path", path)
+    out, lse = run_gpu(torch_cuda, w, mode=mode, path=path)
+    ref, ref_lse = run_oracle(w)
+    err = assert_parity(w, out, lse, ref, ref_lse)
+    say(cid, "max abs err", err)
