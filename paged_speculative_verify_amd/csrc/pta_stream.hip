@@ -79,10 +79,17 @@ __device__ __forceinline__ void stream_pairs(const AttnArgs& a, const StreamRows
   const char* vbase = reinterpret_cast<const char*>(a.v);
 
   PairRegs<KT, D> R;
-  auto issue = [&](int idx) {
+  // Block-table entries are read one pair ahead of the tile loads that need
+  // them, so no tile load waits on a table round trip.
+  int32_t phn[2];
+  auto read_table = [&](int idx) {
     const int p0 = pA + 2 * (j0 + idx * js);
     const int p1 = p0 + 1 < pB ? p0 + 1 : p0;           // index stays inside the range
-    const int64_t ph[2] = {table[p0], table[p1]};
+    phn[0] = table[p0];
+    phn[1] = table[p1];
+  };
+  auto issue = [&]() {
+    const int64_t ph[2] = {__builtin_amdgcn_readfirstlane(phn[0]), __builtin_amdgcn_readfirstlane(phn[1])};
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
       const int64_t tile = (ph[pg] * a.Hkv + hkv) * TILE_BYTES + 16 * lane;
@@ -103,7 +110,9 @@ __device__ __forceinline__ void stream_pairs(const AttnArgs& a, const StreamRows
   char* k1l = wl + T::TILE_LDS;
   char* v0l = wl + 2 * T::TILE_LDS;
   char* v1l = wl + 3 * T::TILE_LDS;
-  issue(0);
+  read_table(0);
+  issue();
+  read_table(min(1, n - 1));
   for (int idx = 0; idx < n; ++idx) {
     const int pb0 = (pA + 2 * (j0 + idx * js)) * kPage;
     const float c0 = score_scale(a, R.ks[0]), c1 = score_scale(a, R.ks[1]);
@@ -112,7 +121,8 @@ __device__ __forceinline__ void stream_pairs(const AttnArgs& a, const StreamRows
     stage_tile<KT, D>(k1l, R.k[1], lane, false, kPage);
     stage_tile<KT, D>(v0l, R.v[0], lane, pb0 + kPage > t_end, t_end - pb0);
     stage_tile<KT, D>(v1l, R.v[1], lane, pb0 + 2 * kPage > t_end, t_end - pb0 - kPage);
-    issue(min(idx + 1, n - 1));
+    issue();                          // pair idx + 1 (the last pair again at the end)
+    read_table(min(idx + 2, n - 1));
     pair_compute<D, RB, false, KT::bytes == 1>(rows, st, k0l, k1l, v0l, v1l, pb0, L, t_end, c0, c1, vs0, vs1,
                                                lane);
   }
