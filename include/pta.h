@@ -150,25 +150,24 @@ pta_status taco_paged_tree_attn_splitk(const pta_dims* dims, const void* q, cons
 size_t taco_paged_tree_attn_balanced_workspace_size(const pta_dims* dims);
 
 /* Work-balanced paged tree attention.  The pages of every (sequence, KV head)
- * unit are laid end to end and cut into equal contiguous slices, one per wave
- * of a persistent grid sized to the current device, so ragged context lengths
- * cost no load imbalance (sequence-dimension parallelism, design talk
+ * unit are laid end to end and cut into equal contiguous slices worked by a
+ * persistent grid sized to the current device, so ragged context lengths cost
+ * no load imbalance (sequence-dimension parallelism, design talk
  * "优化策略总结" item 2; a sequence processed in parts that are combined,
  * 618zxw.cn article section "長シーケンス推論最適化におけるTurboAttention").
  * A slice holding a whole unit writes its rows directly; a slice that ends
- * inside a unit writes a normalised partial and log-sum-exp, merged in slice
- * order.  Served for bf16 q with num_seqs <= 16383 and either G * max_q_len
- * <= 32 rows per KV head (the matrix-core streaming path, one wave per KV head
- * of a group of adjacent heads; the unit's last slice to finish merges its
- * partials inside the same launch, through one counter word per unit) or,
- * with bf16 KV, up to 256 rows (the shared-tile path: one workgroup per row
- * group of up to 128 rows per slice, and a second launch on the same stream
- * merges the partials; no counters; also chosen for fewer rows by path
- * PTA_PATH_TILE); otherwise PTA_ERR_UNSUPPORTED.  Arguments as
- * taco_paged_tree_attn; workspace as for taco_paged_tree_attn_splitk
- * (caller-owned, 256-byte aligned, counter region zero before first use and
- * left zero, no sharing between concurrent calls) with workspace_bytes >=
- * taco_paged_tree_attn_balanced_workspace_size(dims). */
+ * inside a unit writes a normalised partial and log-sum-exp to the workspace,
+ * and a second launch on the same stream merges each unit's partials in
+ * slice order (results do not depend on scheduling).  Served for bf16 q with
+ * num_seqs <= 16383 and either G * max_q_len <= 32 rows per KV head (the
+ * matrix-core streaming path, one slice per wave) or, with bf16 KV, up to 256
+ * rows (the shared-tile path: one workgroup per row group of up to 128 rows
+ * per slice; also chosen for fewer rows by path PTA_PATH_TILE); otherwise
+ * PTA_ERR_UNSUPPORTED.  Arguments as taco_paged_tree_attn.  workspace:
+ * caller-owned device memory, 256-byte aligned (else PTA_ERR_BAD_DIMS), with
+ * workspace_bytes >= taco_paged_tree_attn_balanced_workspace_size(dims); it
+ * needs no initialisation, and calls that may run concurrently must not share
+ * it. */
 pta_status taco_paged_tree_attn_balanced(const pta_dims* dims, const void* q, const void* k_cache,
                                          const void* v_cache, const float* k_scale,
                                          const float* v_scale, const int32_t* block_tables,

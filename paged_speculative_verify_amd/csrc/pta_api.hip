@@ -153,10 +153,10 @@ bool split_layout(const pta_dims* d, int32_t T, SplitLayout* L) {
   return true;
 }
 
-// Balanced mode: [counters int32 | partial O float S*Mmax*D | partial LSE float S*Mmax]
+// Balanced mode: [partial O float S*Mmax*D | partial LSE float S*Mmax]
 // with Mmax = G * max_q_len rows per slot.
-//   stream family: counters B*Hkv, S = workgroups * nw + B*Hkv partial slots (one slice
-//     per wave, nw = 4 waves per workgroup).
+//   stream family: no counters, S = workgroups * nw + B*Hkv partial slots (one slice
+//     per wave, nw = 4 waves per workgroup; a second launch merges).
 //   tile family (bf16 KV): nw waves of 32 rows per workgroup (2 or 4), rg row groups per
 //     slice, ns slices (a multiple of 8 with ns * rg workgroups fitting the device at
 //     once); no counters (a second launch merges), S = ns + B*Hkv slots.
@@ -207,7 +207,7 @@ pta_status balanced_layout(const pta_dims* d, const Plan& p, BalancedLayout* L) 
   L->nwg = nwg;
   L->nw = nw;
   L->rg = 1;
-  L->o_off = up((size_t)units * sizeof(int32_t));
+  L->o_off = 0;
   L->lse_off = L->o_off + up((size_t)rows * d->head_dim * sizeof(float));
   L->total = L->lse_off + up((size_t)rows * sizeof(float));
   return PTA_OK;
@@ -315,7 +315,7 @@ pta_status taco_paged_tree_attn_balanced(const pta_dims* d, const void* q, const
   AttnArgs a = make_args(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
                          tree_mask, scale, out, lse);
   char* ws = reinterpret_cast<char*>(workspace);
-  a.counters = reinterpret_cast<int32_t*>(ws);
+  a.counters = nullptr;                  // both balanced grids merge in a second launch
   a.part_o = reinterpret_cast<float*>(ws + L.o_off);
   a.part_lse = reinterpret_cast<float*>(ws + L.lse_off);
   a.total_waves = L.nwg * L.nw;

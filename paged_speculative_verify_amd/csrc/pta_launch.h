@@ -26,6 +26,9 @@ hipError_t launch_tile(const AttnArgs& a, int kv_dtype, int head_dim, int nwr, d
 // per slice.  With a == nullptr, *nwg receives the workgroups that fit the
 // device at once; otherwise *nwg workgroups are launched.
 hipError_t tile_balanced(const AttnArgs* a, int head_dim, int nwr, int B, int* nwg, hipStream_t s);
+// Second launch of both balanced grids: merge of the slice partials (bf16 out),
+// NS = slices of the attention launch.
+hipError_t launch_slice_merge(const AttnArgs& a, int head_dim, int NS, hipStream_t s);
 
 struct AppendArgs {
   const void* k_new;

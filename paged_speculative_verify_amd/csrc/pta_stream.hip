@@ -65,10 +65,25 @@ struct PairRegs {
   float ks[2], vs[2];
 };
 
+// Issue priority of the calling wave, 0 (lowest) .. 3.
+__device__ __forceinline__ void set_priority(int level) {
+  switch (level) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
+}
+
+// prog_len > 0: the wave owns a slice of prog_len pages of which prog0 come
+// before this range; its issue priority then falls as its share of the slice
+// gets done (3 in the first quarter .. 0 in the last), so the waves sharing
+// a compute unit progress at the same pace instead of the oldest first.
 template <typename KT, int D, int RB>
 __device__ __forceinline__ void stream_pairs(const AttnArgs& a, const StreamRows<D, RB>& rows,
                                              StreamState<D, RB>& st, int b, int hkv, int L, int t_end,
-                                             int pA, int pB, int j0, int js, char* wl, int lane) {
+                                             int pA, int pB, int j0, int js, char* wl, int lane,
+                                             int prog0 = 0, int prog_len = 0) {
   using T = StreamTile<KT, D>;
   constexpr int64_t TILE_BYTES = (int64_t)kPage * D * KT::bytes;
   const int npair = (pB - pA + 1) / 2;
@@ -121,6 +136,7 @@ __device__ __forceinline__ void stream_pairs(const AttnArgs& a, const StreamRows
     stage_tile<KT, D>(k1l, R.k[1], lane, false, kPage);
     stage_tile<KT, D>(v0l, R.v[0], lane, pb0 + kPage > t_end, t_end - pb0);
     stage_tile<KT, D>(v1l, R.v[1], lane, pb0 + 2 * kPage > t_end, t_end - pb0 - kPage);
+    if (prog_len > 0) set_priority(3 - min(3, (prog0 + 2 * idx) * 4 / prog_len));
     issue();                          // pair idx + 1 (the last pair again at the end)
     read_table(min(idx + 2, n - 1));
     pair_compute<D, RB, false, KT::bytes == 1>(rows, st, k0l, k1l, v0l, v1l, pb0, L, t_end, c0, c1, vs0, vs1,
@@ -236,8 +252,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 // x is ((x + 1) N - 1) / W.  N <= W, so every working wave owns a position and
 // the slices touching u are exactly waves wave_of(S_u) .. wave_of(S_u + P_b - 1).
 // The partial of (wave w, unit u) lives in slot w + u, unique because waves
-// and units are both ordered along the line.  Slices hold at least
-// kMinSlicePages pages.  Neighbouring waves stream neighbouring page ranges of
+// and units are both ordered along the line; slice_merge_kernel, launched
+// next, merges them (merging inside this launch would leave the last waves
+// reading partials at the end while the rest of the device idles).  Slices
+// hold at least kMinSlicePages pages.  Neighbouring waves stream neighbouring page ranges of
 // one unit, so the waves in flight at any moment read pages spread over the
 // pool rather than the adjacent head tiles of one block, which HBM serves
 // better (measured on MI355X: about 5.6 TB/s against 4.9 for whole units).
@@ -262,10 +280,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int64_t w = (int64_t)blockIdx.x * NW + wave;
   if (w >= N) return;               // no workgroup barrier follows
   const int Mmax = a.G * a.Qmax;
-  auto wave_of = [&](int64_t x) -> int64_t { return ((x + 1) * N - 1) / W; };
 
-  int64_t x = w * W / N;
+  const int64_t x0 = w * W / N;
   const int64_t xe = (w + 1) * W / N;
+  int64_t x = x0;
   while (x < xe) {
     // the unit holding position x: largest b with PS_b <= x / Hkv
     const int key = (int)(x / a.Hkv);
@@ -292,36 +310,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     load_rows(rows, a, b, hkv, qb, M, g, m);
     StreamState<D, RB> st;
     st.init();
-    stream_pairs<KT, D, RB>(a, rows, st, b, hkv, L, min(C, k1 * kPage), k0, k1, 0, 1, vlds[wave], lane);
+    stream_pairs<KT, D, RB>(a, rows, st, b, hkv, L, min(C, k1 * kPage), k0, k1, 0, 1, vlds[wave], lane,
+                            (int)(x - x0), (int)(xe - x0));
     reduce_row_sums(st);
 
     if (k0 == 0 && k1 == Pb) {
       store_final_rows(a, rows, st, b, g);        // the whole unit in this slice
     } else {
-      const int64_t S = (int64_t)a.Hkv * psb + (int64_t)hkv * Pb;
-      const int64_t wfirst = wave_of(S), wlast = wave_of(S + Pb - 1);
-      const int np = (int)(wlast - wfirst + 1);
       auto addr = [&](int rb, float*& o, float*& l) {
         const int64_t r = (w + u) * Mmax + rb * 16 + m;
         o = a.part_o + r * D;
         l = a.part_lse + r;
       };
-      store_partial_rows(rows, st, g, addr);
-      __builtin_amdgcn_s_waitcnt(0);             // partial stores complete before the arrival
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      int32_t* cnt = a.counters + u;
-      int last = 0;
-      if (lane == 0) last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
-      last = __builtin_amdgcn_readfirstlane(last);
-      if (last) {
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        auto pslot = [&](int r, int p) {
-          const int64_t rr = (wfirst + p + u) * Mmax + r;
-          return PartSlot{a.part_o + rr * D, a.part_lse + rr};
-        };
-        merge_rows<BF16, D>(a, b, hkv, qb, M, np, pslot, lane, 64);
-        if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      store_partial_rows(rows, st, g, addr);        // merged by the second launch
     }
     x += k1 - k0;
   }
@@ -370,7 +371,9 @@ static hipError_t balanced_t(const AttnArgs* a, int B, int* nwg, hipStream_t s) 
     return hipSuccess;
   }
   hipLaunchKernelGGL((stream_balanced_kernel<KT, D, RB, NW>), dim3((unsigned)*nwg), dim3(NW * 64), dyn, s, *a);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_slice_merge(*a, D, *nwg * NW, s);
 }
 
 template <typename KT, int D>

@@ -457,7 +457,7 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
 // and its L2, and the KV pages reach L2 from HBM once.  A slice that covers a
 // whole unit writes its rows; otherwise it stores a normalised partial in
 // slot w + u (unique: slices and units are both ordered along the line), and
-// tile_merge_kernel, launched right after, merges them in slice order.
+// slice_merge_kernel, launched right after, merges them in slice order.
 // (Merging inside this launch, by the unit's last slice, leaves a few
 // workgroups reading many partials at the end of the launch while the rest of
 // the device idles.)
@@ -536,13 +536,14 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // ---------------------------------------------------------------- slice merge
-// Second launch of the balanced tile grid: one workgroup per (unit, 32-row
+// Second launch of both balanced grids: one workgroup per (unit, 32-row
 // block) merges the partials of a unit cut into several slices, all slices
 // read at once with plain 16-byte loads (the attention launch has completed)
 // and combined by log-sum-exp in slice order.  Slice bounds are recomputed
-// from the same page line as the attention launch (NS slices at most).
+// from the same page line as the attention launch (NS slices at most, at
+// least kMinSlicePages pages each); slice w's partial of unit u is slot w + u.
 template <typename QT, int D>
-__global__ __launch_bounds__(256) void tile_merge_kernel(AttnArgs a, int NS) {
+__global__ __launch_bounds__(256) void slice_merge_kernel(AttnArgs a, int NS) {
   constexpr float NEG_INF = -__builtin_huge_valf();
   constexpr int TPR = 8;                  // threads per row
   constexpr int IPT = D / 4 / TPR;        // 16-byte items per thread
@@ -697,8 +698,14 @@ static hipError_t tile_balanced_t(const AttnArgs* a, int B, int* nwg, hipStream_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int RG = (a->G * a->Qmax + NWR * 32 - 1) / (NWR * 32);
-  const int64_t blocks = (int64_t)a->B * a->Hkv * ((a->G * a->Qmax + 31) / 32);
-  hipLaunchKernelGGL((tile_merge_kernel<BF16, D>), dim3((unsigned)blocks), dim3(256), 0, s, *a, *nwg / RG);
+  return launch_slice_merge(*a, D, *nwg / RG, s);
+}
+
+hipError_t launch_slice_merge(const AttnArgs& a, int D, int NS, hipStream_t s) {
+  const int64_t blocks = (int64_t)a.B * a.Hkv * ((a.G * a.Qmax + 31) / 32);
+  if (D == 64) hipLaunchKernelGGL((slice_merge_kernel<BF16, 64>), dim3((unsigned)blocks), dim3(256), 0, s, a, NS);
+  else if (D == 128) hipLaunchKernelGGL((slice_merge_kernel<BF16, 128>), dim3((unsigned)blocks), dim3(256), 0, s, a, NS);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

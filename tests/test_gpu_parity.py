@@ -413,9 +413,8 @@ def test_balanced_parity(torch_cuda, cid, sp):
 
 
 def test_balanced_repeat_and_workspace_reuse(torch_cuda):
-    """The same zero-filled workspace serves repeated calls (the merging slices reset their
-    counters); results are bit-identical from call to call and unchanged by a relabelling
-    of physical pages."""
+    """The same workspace serves repeated calls; results are bit-identical from call to call
+    and unchanged by a relabelling of physical pages."""
     import torch
     import paged_speculative_verify_amd as psv
     w = make(spec("r", 8, 32, 8, 128, "bf16", "bf16", (100, 6000), 1, "chain", seed=111))
@@ -429,8 +428,6 @@ def test_balanced_repeat_and_workspace_reuse(torch_cuda):
     b1, m1 = run_gpu(torch_cuda, permute_pool(w, 7), mode="balanced", workspace=ws)
     assert np.array_equal(a1, a2, equal_nan=True) and np.array_equal(l1, l2, equal_nan=True)
     assert np.array_equal(a1, b1, equal_nan=True) and np.array_equal(l1, m1, equal_nan=True)
-    U = w.q.shape[0] * w.k_cache.shape[1]
-    assert int(ws[:4 * U].view(torch.int32).abs().sum()) == 0, "arrival counters not reset"
     ref, ref_lse = run_oracle(w)
     assert_parity(w, a1, l1, ref, ref_lse)
 
