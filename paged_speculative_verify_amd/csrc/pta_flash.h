@@ -19,6 +19,23 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr float kLazyTau = 8.0f;   // log2 headroom before a row's reference max moves
 constexpr int kMinSlicePages = 8;  // balanced mode: fewest pages per wave slice
 
+// Issue priority of the calling wave, 0 (lowest) .. 3.
+__device__ __forceinline__ void set_priority(int level) {
+  switch (level) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
+}
+
+// Priority that falls as a wave gets through its share of a balanced grid's
+// work (3 in the first quarter .. 0 in the last), so work-groups sharing a
+// compute unit progress at the same pace instead of the oldest first.
+__device__ __forceinline__ void pace(int done, int total) {
+  if (total > 0) set_priority(3 - min(3, (int)((uint32_t)(4 * done) / (uint32_t)total)));
+}
+
 template <typename KT, int D>
 struct StreamTile {
   static constexpr int KK = D / 32;                           // 16x16x32 k-steps over the head dim

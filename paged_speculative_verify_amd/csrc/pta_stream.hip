@@ -65,20 +65,8 @@ struct PairRegs {
   float ks[2], vs[2];
 };
 
-// Issue priority of the calling wave, 0 (lowest) .. 3.
-__device__ __forceinline__ void set_priority(int level) {
-  switch (level) {
-    case 0: __builtin_amdgcn_s_setprio(0); break;
-    case 1: __builtin_amdgcn_s_setprio(1); break;
-    case 2: __builtin_amdgcn_s_setprio(2); break;
-    default: __builtin_amdgcn_s_setprio(3); break;
-  }
-}
-
 // prog_len > 0: the wave owns a slice of prog_len pages of which prog0 come
-// before this range; its issue priority then falls as its share of the slice
-// gets done (3 in the first quarter .. 0 in the last), so the waves sharing
-// a compute unit progress at the same pace instead of the oldest first.
+// before this range, and paces itself by its progress through the slice.
 template <typename KT, int D, int RB>
 __device__ __forceinline__ void stream_pairs(const AttnArgs& a, const StreamRows<D, RB>& rows,
                                              StreamState<D, RB>& st, int b, int hkv, int L, int t_end,
@@ -136,7 +124,7 @@ __device__ __forceinline__ void stream_pairs(const AttnArgs& a, const StreamRows
     stage_tile<KT, D>(k1l, R.k[1], lane, false, kPage);
     stage_tile<KT, D>(v0l, R.v[0], lane, pb0 + kPage > t_end, t_end - pb0);
     stage_tile<KT, D>(v1l, R.v[1], lane, pb0 + 2 * kPage > t_end, t_end - pb0 - kPage);
-    if (prog_len > 0) set_priority(3 - min(3, (prog0 + 2 * idx) * 4 / prog_len));
+    pace(prog0 + 2 * idx, prog_len);
     issue();                          // pair idx + 1 (the last pair again at the end)
     read_table(min(idx + 2, n - 1));
     pair_compute<D, RB, false, KT::bytes == 1>(rows, st, k0l, k1l, v0l, v1l, pb0, L, t_end, c0, c1, vs0, vs1,

@@ -266,7 +266,7 @@ template <int D, int NWR, int NBUF>
 __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t lds0, const int* tring,
                                           uint32_t tring0, StreamRows<D, 2>& rows, StreamState<D, 2>& st,
                                           int b, int hkv, int qb, int row0, int t0, int t1, int wave,
-                                          int lane) {
+                                          int lane, int prog0 = 0, int prog_len = 0) {
   using Gm = DmaGeom<D, NWR, NBUF>;
   constexpr int RB = 2;
   const int g = lane >> 4, m = lane & 15;
@@ -395,6 +395,7 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
       const int ch = (s + NBUF - 1) / 32 + 3;
       if (ch < nch) issue_chunk(ch);
     }
+    pace(prog0 + 2 * s, prog_len);
     if (s + NBUF - 1 < nst) copy_stage(s + NBUF - 1);     // into the buffer stage s - 1 used
     if (wave_rows) step(s, sb, x, xn);
   };
@@ -490,8 +491,9 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   const uint32_t tring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)&tring[0];
   const int row0 = rg * NWR * 32;
 
-  int64_t x = w * W / N;
+  const int64_t x0 = w * W / N;
   const int64_t xe = (w + 1) * W / N;
+  int64_t x = x0;
   while (x < xe) {
     // the unit holding position x: largest b with PS_b <= x / Hkv
     const int key = (int)(x / a.Hkv);
@@ -519,7 +521,7 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     st.init();
     if (row0 < M) {
       dma_range<D, NWR, NBUF>(a, lds, lds0, tring, tring0, rows, st, b, hkv, qb, row0, k0 * kPage,
-                              min(C, k1 * kPage), wave, lane);
+                              min(C, k1 * kPage), wave, lane, (int)(x - x0), (int)(xe - x0));
       if (k0 == 0 && k1 == Pb) {
         store_final_rows(a, rows, st, b, g);        // the whole unit in this slice
       } else {
