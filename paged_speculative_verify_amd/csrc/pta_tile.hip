@@ -549,7 +549,7 @@ __global__ __launch_bounds__(256) void slice_merge_kernel(AttnArgs a, int NS) {
   constexpr float NEG_INF = -__builtin_huge_valf();
   constexpr int TPR = 8;                  // threads per row
   constexpr int IPT = D / 4 / TPR;        // 16-byte items per thread
-  constexpr int PB = 8;                   // slices per batch
+  constexpr int PB = 4;                   // slices per batch (all workgroups resident at once)
   __shared__ int red[2][4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int Rmax = a.G * a.Qmax;

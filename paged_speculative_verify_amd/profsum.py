@@ -36,8 +36,10 @@ KERNEL_SOURCES = ["pta_device.h", "pta_flash.h", "pta_launch.h", "pta_valu.hip",
                   "pta_tile.hip", "pta_aux.hip", "pta_api.hip"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30                      # bench.py --copy-calibration copies 1 GiB
+# every kernel an attention call launches (the balanced entry launches its grid, then
+# slice_merge_kernel)
 ATTN_KERNELS = ("stream_attn_kernel", "stream_balanced_kernel", "tile_dma_kernel", "tile_balanced_kernel",
-                "tile_attn_kernel", "valu_attn_kernel")
+                "tile_attn_kernel", "valu_attn_kernel", "slice_merge_kernel")
 
 
 def kernel_source_hash() -> str:
@@ -60,17 +62,18 @@ def _is_attention(name: str) -> bool:
 
 
 def counter_per_dispatch(path: str, counter: str, want) -> tuple[float, int, str]:
-    """Mean counter value over the dispatches whose kernel name passes ``want``."""
-    vals, names = [], set()
+    """Counter value per call: the mean over the dispatches of each kernel whose name
+    passes ``want``, summed over those kernels (a call launches each of them once)."""
+    vals = {}
     with open(path, newline="") as f:
         for row in csv.DictReader(f):
             if row["Counter_Name"] != counter or not want(row["Kernel_Name"]):
                 continue
-            vals.append(float(row["Counter_Value"]))
-            names.add(_short(row["Kernel_Name"]))
+            vals.setdefault(_short(row["Kernel_Name"]), []).append(float(row["Counter_Value"]))
     if not vals:
         raise SystemExit(f"{path}: no {counter} rows for the kernel asked for")
-    return statistics.fmean(vals), len(vals), ", ".join(sorted(names))
+    total = sum(statistics.fmean(v) for v in vals.values())
+    return total, min(len(v) for v in vals.values()), " + ".join(sorted(vals))
 
 
 def cmd_traffic(a) -> int:
