@@ -329,7 +329,9 @@ def main(argv=None) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "paged tree attention kernel (" + cfg["mode"] + " entry, merge fused)",
+                     "kernel": ("paged tree attention grid + slice merge launch (balanced entry)"
+                                if cfg["mode"] == "balanced" else
+                                "paged tree attention kernel (" + cfg["mode"] + " entry, merge fused)"),
                      "algorithmic_bytes_per_launch": int(kv_per_launch)},
         "kernel_source_hash": src_hash,
     }

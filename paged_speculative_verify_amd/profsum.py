@@ -115,9 +115,9 @@ def cmd_traffic(a) -> int:
         "",
         "| quantity | value |",
         "|---|---|",
-        f"| dispatches counted | {n_f} (FETCH_SIZE), {n_w} (WRITE_SIZE) |",
-        f"| FETCH_SIZE per dispatch | {fetch_kib:.1f} KiB |",
-        f"| WRITE_SIZE per dispatch | {write_kib:.1f} KiB |",
+        f"| calls counted | {n_f} (FETCH_SIZE), {n_w} (WRITE_SIZE) |",
+        f"| FETCH_SIZE per call (every kernel of the call) | {fetch_kib:.1f} KiB |",
+        f"| WRITE_SIZE per call (every kernel of the call) | {write_kib:.1f} KiB |",
         f"| 1 GiB copy reads as | {cf_kib:.1f} KiB fetched, {cw_kib:.1f} KiB written |",
         f"| scale (fetch, write) | {f_scale:.4f}, {w_scale:.4f} |",
         f"| HBM bytes per launch | {fetch_b + write_b:.4g} ({fetch_b:.4g} read, {write_b:.4g} written) |",
@@ -138,7 +138,7 @@ def cmd_trace(a) -> int:
     lines = [f"# Kernel trace: {a.title}", "", "Command:", "", "```", a.command, "```", ""]
     if a.bench_json and os.path.exists(a.bench_json):
         with open(a.bench_json) as f:
-            txt = f.read().strip().splitlines()
+            txt = [ln for ln in f.read().splitlines() if ln.startswith("{")]
         if txt:
             lines += ["Bench line of the same run:", "", "```", txt[-1], "```", ""]
     lines += ["| kernel | calls | mean (us) | min (us) | max (us) | total (ms) | share |",
