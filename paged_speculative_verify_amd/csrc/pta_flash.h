@@ -290,7 +290,7 @@ __device__ __forceinline__ void pair_p(StreamState<D, RB>& st, const float (&x)[
   }
 }
 
-template <int D, int RB, bool SWZ>
+template <int D, int RB, bool SWZ, bool LO = true>
 __device__ __forceinline__ void pair_pv_mma(StreamState<D, RB>& st, const bf16x8 (&phi)[RB],
                                             const bf16x8 (&plo)[RB], const char* vl0, const char* vl1,
                                             int lane) {
@@ -315,17 +315,22 @@ __device__ __forceinline__ void pair_pv_mma(StreamState<D, RB>& st, const bf16x8
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
         st.o[rb][db + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[e], phi[rb], st.o[rb][db + e], 0, 0, 0);
+    if constexpr (LO) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
+      for (int e = 0; e < 2; ++e)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        st.o[rb][db + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[e], plo[rb], st.o[rb][db + e], 0, 0, 0);
+        for (int rb = 0; rb < RB; ++rb)
+          st.o[rb][db + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[e], plo[rb], st.o[rb][db + e], 0, 0, 0);
+    }
   }
 }
 
 // The whole update of one pair for kernels that do not pipeline it: page
 // score scales c0, c1 > 0 (score_scale), V scales vs0, vs1 folded into P when
-// VS (fp8 pages).  Raw maxima are taken per page and scaled once.
+// VS (fp8 pages).  Raw maxima are taken per page and scaled once.  fp8 pages
+// take P as bf16 alone (no low half): the extra rounding moves the output by
+// at most 2^-9 of the page's largest |V|, far below the error fp8 storage of
+// V itself carries, and it saves a third of the matrix-core work.
 template <int D, int RB, bool SWZ, bool VS>
 __device__ __forceinline__ void pair_compute(const StreamRows<D, RB>& rows, StreamState<D, RB>& st,
                                              const char* kl0, const char* kl1, const char* vl0,
@@ -378,12 +383,13 @@ __device__ __forceinline__ void pair_compute(const StreamRows<D, RB>& rows, Stre
         p1 *= v;
       }
       h[k] = pack_bf16x2(p0, p1);
-      lo[k] = pack_bf16x2(p0 - bf16_lo(h[k]), p1 - bf16_hi(h[k]));
+      if constexpr (!VS) lo[k] = pack_bf16x2(p0 - bf16_lo(h[k]), p1 - bf16_hi(h[k]));
+      else lo[k] = 0u;
     }
     phi[rb] = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
     plo[rb] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
   }
-  pair_pv_mma<D, RB, SWZ>(st, phi, plo, vl0, vl1, lane);
+  pair_pv_mma<D, RB, SWZ, !VS>(st, phi, plo, vl0, vl1, lane);
 }
 
 // Row sums over the lane's four 16-lane groups (every group holds 4 of each
