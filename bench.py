@@ -9,7 +9,11 @@ the timed region; R independent input sets are rotated step to step so the
 256 MB last-level cache cannot serve the KV stream from a previous step.
 
 Prints ONE JSON line.  `value` is KV HBM bytes (algorithmic: every K/V byte of
-every sequence's context counted once) per second of attention time, in GB/s.
+every sequence's context counted once) per second of whole-step wall time
+(append + attention, K steps between two synchronisations with no timing events
+inside), in GB/s.  `roofline.achieved` is the same bytes per second of attention
+call time alone, from HIP events recorded on the launch stream in a separate pass
+of K steps that runs before the timed ones.
 """
 from __future__ import annotations
 
@@ -198,6 +202,9 @@ def main(argv=None) -> int:
                          "sequence, -1 = balanced page slices")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--qlen-floor", action="store_true",
+                    help="instead of the bench line: attention time against the number of candidates "
+                         "per sequence at the decode shape, T(q_len) / T(1)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -222,6 +229,9 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch_each_way": n, "launches": 5}))
         return 0
+
+    if args.qlen_floor:
+        return qlen_floor(psv, torch, args)
 
     name = args.config
     cfg = launch_config(name)
@@ -267,11 +277,12 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
 
     K = args.steps
+    order = [(args.warmup + i) % len(sets) for i in range(K)]
+    # 1. the steps with HIP events on the launch stream around each launch, for the per-kernel
+    #    times of the roofline (they also finish warming the clocks up)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    order = [(args.warmup + i) % len(sets) for i in range(K)]
     torch.cuda.synchronize()
-    t_wall = time.perf_counter()
     for i in range(K):
         ds = sets[order[i]]
         e0, e1, e2 = ev[i]
@@ -280,6 +291,15 @@ def main(argv=None) -> int:
         e1.record(stream)
         ds.attn_call()
         e2.record(stream)
+    torch.cuda.synchronize()
+    # 2. the timed steps: nothing but the step's own launches between the two synchronisations
+    #    (timing events inside the loop would add their own packets to every step)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(K):
+        ds = sets[order[i]]
+        ds.append_call()
+        ds.attn_call()
     t_enqueue = time.perf_counter() - t_wall
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
@@ -332,7 +352,9 @@ def main(argv=None) -> int:
                      "kernel": ("paged tree attention grid + slice merge launch (balanced entry)"
                                 if cfg["mode"] == "balanced" else
                                 "paged tree attention kernel (" + cfg["mode"] + " entry, merge fused)"),
-                     "algorithmic_bytes_per_launch": int(kv_per_launch)},
+                     "algorithmic_bytes_per_launch": int(kv_per_launch),
+                     "timing": f"HIP events on the launch stream around each attention call, over {K} "
+                               f"steps run before the timed ones"},
         "kernel_source_hash": src_hash,
     }
     if not args.no_cpu_baseline:
@@ -345,6 +367,59 @@ def main(argv=None) -> int:
     if sets[0].w.q.shape[1] > 1:
         result["accept_commit"] = time_accept_commit(psv, torch, sets[order[-1]], K)
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def qlen_floor(psv, torch, args):
+    """Verification cost against candidates per sequence (the pages' claim: checking several
+    candidates in one pass costs about one decode step).  The decode workload's batch, heads and
+    context draws are kept; each sequence carries q random-tree candidates (ctx_lens include
+    them, so the KV bytes are the same for every q).  One JSON line with the mean attention
+    time per q and its ratio to q = 1."""
+    from workload import make
+    stream = torch.cuda.current_stream()
+    rows, t1 = [], None
+    for q in (1, 2, 4, 8, 16, 32):
+        entries = ["whole", "balanced"] if q == 1 else ["balanced"]
+        sets = [DeviceSet(make("llama3_8b_decode", seed=None if r == 0 else 2000 + r, q_len=q,
+                               tree="chain" if q == 1 else "random"), torch) for r in range(2)]
+        for mode in entries:
+            calls = []
+            for ds in sets:
+                d = ds.d
+                if mode == "balanced":
+                    ds.workspace = torch.zeros(psv.taco_paged_tree_attn_balanced_workspace_size(
+                        d.q, d.k_cache, d.block_tables, max_ctx_len=d.max_ctx_len), dtype=torch.uint8,
+                        device="cuda")
+                calls.append(psv.prepare_paged_tree_attn(
+                    mode, d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens, d.tree_mask,
+                    d.scale, ds.out, lse=ds.lse, workspace=ds.workspace if mode == "balanced" else None,
+                    max_ctx_len=d.max_ctx_len))
+            for i in range(args.warmup):
+                calls[i % 2]()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            for i in range(args.steps):
+                ev[i][0].record(stream)
+                calls[i % 2]()
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+            kvb = sum(kv_bytes(sets[i % 2].w) for i in range(args.steps)) / args.steps
+            fl = sum(attn_flops(sets[i % 2].w) for i in range(args.steps)) / args.steps
+            if q == 1 and mode == "whole":
+                t1 = ms
+            rows.append({"q_len": q, "rows_per_kv_head": 4 * q, "entry": mode, "attention_ms": round(ms, 5),
+                         "ratio_to_q1": round(ms / t1, 3), "kv_gbs": round(kvb / (ms / 1e3) / 1e9, 1),
+                         "tflops": round(fl / (ms / 1e3) / 1e12, 1)})
+            print(f"[bench] q_len {q} {mode}: {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+        del sets
+        torch.cuda.empty_cache()
+    print(json.dumps({"qlen_floor": rows, "workload": "llama3_8b_decode shape (B 64, 32/8 heads, D 128, "
+                      "ctx U[512, 4096]) with q_len random-tree candidates", "steps": args.steps,
+                      "warmup": args.warmup, "timing": "HIP events on the launch stream, 2 input sets rotated"}),
+          flush=True)
     return 0
 
 
