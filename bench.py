@@ -12,8 +12,8 @@ Prints ONE JSON line.  `value` is KV HBM bytes (algorithmic: every K/V byte of
 every sequence's context counted once) per second of whole-step wall time
 (append + attention, K steps between two synchronisations with no timing events
 inside), in GB/s.  `roofline.achieved` is the same bytes per second of attention
-call time alone, from HIP events recorded on the launch stream in a separate pass
-of K steps that runs before the timed ones.
+call time alone: HIP events on the launch stream bracket K back-to-back attention
+calls in a pass of their own that runs before the timed steps.
 """
 from __future__ import annotations
 
@@ -34,6 +34,7 @@ METRIC = "KV HBM GB/s (% of peak) + verified candidate tokens/s, paged tree attn
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 HEADLINE = "llama3_8b_decode"
+SETTLE_S = 0.3                 # untimed steps after the warm-up, before any measurement
 
 # launch configuration of each workload: entry point ("whole": one pass per
 # sequence, "split": split-K partitions of `split` tokens, "balanced": equal
@@ -276,22 +277,37 @@ def main(argv=None) -> int:
         ds.attn_call()
     torch.cuda.synchronize()
 
+    # clock settling: a few warm-up steps are over in about a millisecond, well before the GPU
+    # clock has ramped up; untimed steps continue for at least SETTLE_S of wall time so that
+    # neither measurement pass below sees the ramp
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for _ in range(8):
+            ds = sets[n_settle % len(sets)]
+            ds.append_call()
+            ds.attn_call()
+            n_settle += 1
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
+
     K = args.steps
-    order = [(args.warmup + i) % len(sets) for i in range(K)]
-    # 1. the steps with HIP events on the launch stream around each launch, for the per-kernel
-    #    times of the roofline (they also finish warming the clocks up)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        ds = sets[order[i]]
-        e0, e1, e2 = ev[i]
+    order = [(args.warmup + n_settle + i) % len(sets) for i in range(K)]
+    # 1. per-call times for the roofline: K attention calls back to back between two HIP
+    #    events on the launch stream (an event pair around every single call adds its own
+    #    overhead to each call), then K append calls the same way; this pass also finishes
+    #    warming the clocks up
+    def bracketed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         e0.record(stream)
-        ds.append_call()
+        for i in range(K):
+            fn(sets[order[i]])
         e1.record(stream)
-        ds.attn_call()
-        e2.record(stream)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+    attn_avg_ms = bracketed(lambda ds: ds.attn_call())
+    append_avg_ms = bracketed(lambda ds: ds.append_call())
     # 2. the timed steps: nothing but the step's own launches between the two synchronisations
     #    (timing events inside the loop would add their own packets to every step)
     torch.cuda.synchronize()
@@ -303,13 +319,11 @@ def main(argv=None) -> int:
     t_enqueue = time.perf_counter() - t_wall
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    step_ms = [e0.elapsed_time(e2) for e0, _, e2 in ev]
-    attn_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev]
     kvb = [kv_bytes(sets[o].w) for o in order]
     cands = [int(sets[o].w.q_lens.sum()) for o in order]
     flops = {r: attn_flops(sets[r].w) for r in set(order)}
 
-    attn_avg_s = sum(attn_ms) / K / 1e3
+    attn_avg_s = attn_avg_ms / 1e3
     kv_per_launch = sum(kvb) / K
     achieved_gbs = kv_per_launch / attn_avg_s / 1e9
     ms_per_step = wall / K * 1e3
@@ -341,10 +355,9 @@ def main(argv=None) -> int:
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "candidates_per_s": round(cand_per_s, 1),
         "attention_ms": round(attn_avg_s * 1e3, 5),
-        "attention_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 5),
-                                 round(float(np.percentile(attn_ms, 90)), 5)],
-        "kv_append_ms": round(sum(a - b for a, b in zip(step_ms, attn_ms)) / K, 5),
+        "kv_append_ms": round(append_avg_ms, 5),
         "host_enqueue_ms_per_step": round(t_enqueue / K * 1e3, 5),
+        "clock_settle": {"untimed_steps": n_settle, "ms": round(settle_ms, 1)},
         "attention_tflops": round(tflops, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
@@ -353,8 +366,8 @@ def main(argv=None) -> int:
                                 if cfg["mode"] == "balanced" else
                                 "paged tree attention kernel (" + cfg["mode"] + " entry, merge fused)"),
                      "algorithmic_bytes_per_launch": int(kv_per_launch),
-                     "timing": f"HIP events on the launch stream around each attention call, over {K} "
-                               f"steps run before the timed ones"},
+                     "timing": f"HIP events on the launch stream around {K} back-to-back attention "
+                               f"calls, run before the timed steps"},
         "kernel_source_hash": src_hash,
     }
     if not args.no_cpu_baseline:
@@ -398,14 +411,19 @@ def qlen_floor(psv, torch, args):
             for i in range(args.warmup):
                 calls[i % 2]()
             torch.cuda.synchronize()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(args.steps)]
+            t_settle, n = time.perf_counter(), 0
+            while time.perf_counter() - t_settle < SETTLE_S:      # clock settling, untimed
+                for _ in range(8):
+                    calls[n % 2]()
+                    n += 1
+                torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
             for i in range(args.steps):
-                ev[i][0].record(stream)
                 calls[i % 2]()
-                ev[i][1].record(stream)
+            e1.record(stream)
             torch.cuda.synchronize()
-            ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+            ms = e0.elapsed_time(e1) / args.steps
             kvb = sum(kv_bytes(sets[i % 2].w) for i in range(args.steps)) / args.steps
             fl = sum(attn_flops(sets[i % 2].w) for i in range(args.steps)) / args.steps
             if q == 1 and mode == "whole":
@@ -418,7 +436,8 @@ def qlen_floor(psv, torch, args):
         torch.cuda.empty_cache()
     print(json.dumps({"qlen_floor": rows, "workload": "llama3_8b_decode shape (B 64, 32/8 heads, D 128, "
                       "ctx U[512, 4096]) with q_len random-tree candidates", "steps": args.steps,
-                      "warmup": args.warmup, "timing": "HIP events on the launch stream, 2 input sets rotated"}),
+                      "warmup": args.warmup, "timing": "HIP events on the launch stream around the back-to-back calls, 2 input sets "
+                      "rotated"}),
           flush=True)
     return 0
 

@@ -226,138 +226,6 @@ __device__ __forceinline__ void wait_stages(int k) {
   }
 }
 
-// One pipeline step of a wave (two row blocks of 16 rows) with its
-// instruction order written out.  Matrix-core and vector instructions of a
-// wave overlap only when they alternate in the instruction stream (a wave
-// issues in order, and a matrix-core instruction behind a busy matrix core
-// stalls every instruction after it), so the step is cut into chunks of one
-// v_mfma_f32_16x16x32_bf16 and about three vector instructions of
-// independent work, fenced so the compiler keeps them apart:
-//   phase A: the 16 score products of pair s + 1 (S^T = K Q^T) with P of row
-//            block 0 of pair s,
-//   phase B: the 16 P.V products of row block 0 with P of row block 1,
-//   phase C: the 16 P.V products of row block 1 (after the caller's mask of
-//            pair s + 1, so its lane maxima can fill the gaps).
-// LDS operands are read ahead: K one 32-dim step ahead, V^T two 16-dim
-// blocks ahead.  Every accumulator receives its products in the same order
-// as pair_scores / pair_p / pair_pv_mma (scores over the head dim, O over hi
-// then lo), and P and the row sums use the same arithmetic in the same order.
-#define PTA_FENCE() __builtin_amdgcn_sched_barrier(0)
-
-template <int D>
-struct StepP {
-  float nm[2];                 // -m of each row block (0 for an empty row)
-  float p0[2], p1[2];          // the score pair in flight per row block
-  uint32_t h[2][4], lo[2][4];  // P as bf16 hi/lo words per row block
-};
-
-// Part `part` (0..3) of score pair k of row block rb: about three vector
-// instructions each.
-template <int D>
-__device__ __forceinline__ void p_part(StepP<D>& P, StreamState<D, 2>& st, const float (&x)[2][8], int rb,
-                                       int k, int part, float c) {
-  switch (part) {
-    case 0:
-      P.p0[rb] = fast_exp2(fmaf(x[rb][2 * k], c, P.nm[rb]));
-      break;
-    case 1:
-      P.p1[rb] = fast_exp2(fmaf(x[rb][2 * k + 1], c, P.nm[rb]));
-      break;
-    case 2:
-      st.l[rb] += P.p0[rb] + P.p1[rb];
-      P.h[rb][k] = pack_bf16x2(P.p0[rb], P.p1[rb]);
-      break;
-    default:
-      P.lo[rb][k] = pack_bf16x2(P.p0[rb] - bf16_lo(P.h[rb][k]), P.p1[rb] - bf16_hi(P.h[rb][k]));
-      break;
-  }
-}
-
-template <int D>
-__device__ __forceinline__ bf16x8 v_operand(const char* vl0, const char* vl1, int db, int lane) {
-  const int g = lane >> 4, m = lane & 15;
-  const int voff = tile_off<D, true>(4 * g + (m >> 2), 2 * db + ((m & 3) >> 1)) + 8 * (m & 1);
-  const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl0 + voff));
-  const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl1 + voff));
-  return __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint2, va).x, __builtin_bit_cast(uint2, va).y,
-                                               __builtin_bit_cast(uint2, vb).x, __builtin_bit_cast(uint2, vb).y));
-}
-
-// Phases A and B.  On return P holds both row blocks' P and V^T operands of
-// blocks 0 and 1 are in flight for phase C.
-template <int D>
-__device__ __forceinline__ void step_ab(const StreamRows<D, 2>& rows, StreamState<D, 2>& st, PairScores<2>& S,
-                                        StepP<D>& P, bf16x8 (&vt)[3], const float (&x)[2][8], const char* kl0,
-                                        const char* kl1, const char* vl0, const char* vl1, int lane, float c) {
-  constexpr int KK = D / 32, DB = D / 16;
-  constexpr float NEG_INF = -__builtin_huge_valf();
-  static_assert(KK == 4 && DB == 8, "the chunk plan assumes a head dim of 128");
-  const int g = lane >> 4, m = lane & 15;
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) P.nm[rb] = st.m[rb] == NEG_INF ? 0.f : -st.m[rb];
-#pragma unroll
-  for (int pg = 0; pg < 2; ++pg)
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) S.s[pg][rb] = {};
-  bf16x8 kop[2][2];
-  kop[0][0] = *reinterpret_cast<const bf16x8*>(kl0 + tile_off<D, true>(m, g));
-  kop[0][1] = *reinterpret_cast<const bf16x8*>(kl1 + tile_off<D, true>(m, g));
-  PTA_FENCE();
-  // ---- phase A: chunk j = score product (kk, pg, rb) and part j % 4 of pair j / 4 of row block 0
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int kk = j >> 2, pg = (j >> 1) & 1, rb = j & 1;
-    if ((j & 3) == 0 && kk + 1 < KK) {
-      kop[(kk + 1) & 1][0] = *reinterpret_cast<const bf16x8*>(kl0 + tile_off<D, true>(m, 4 * (kk + 1) + g));
-      kop[(kk + 1) & 1][1] = *reinterpret_cast<const bf16x8*>(kl1 + tile_off<D, true>(m, 4 * (kk + 1) + g));
-    }
-    if (j == 12) vt[0] = v_operand<D>(vl0, vl1, 0, lane);
-    if (j == 14) vt[1] = v_operand<D>(vl0, vl1, 1, lane);
-    S.s[pg][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk & 1][pg], rows.qop[rb][kk], S.s[pg][rb], 0, 0, 0);
-    p_part<D>(P, st, x, 0, j >> 2, j & 3, c);
-    PTA_FENCE();
-  }
-  const bf16x8 phi0 = __builtin_bit_cast(bf16x8, make_uint4(P.h[0][0], P.h[0][1], P.h[0][2], P.h[0][3]));
-  const bf16x8 plo0 = __builtin_bit_cast(bf16x8, make_uint4(P.lo[0][0], P.lo[0][1], P.lo[0][2], P.lo[0][3]));
-  // ---- phase B: chunk j = P.V product (db = j / 2, hi or lo) of row block 0, part j % 4 of pair j / 4 of row block 1
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int db = j >> 1;
-    if ((j & 1) == 0) {
-      if (db + 2 < DB) vt[(db + 2) % 3] = v_operand<D>(vl0, vl1, db + 2, lane);
-      else vt[(db + 2) % 3] = v_operand<D>(vl0, vl1, db + 2 - DB, lane);   // phase C's blocks 0 and 1
-    }
-    st.o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[db % 3], (j & 1) ? plo0 : phi0, st.o[0][db], 0, 0, 0);
-    p_part<D>(P, st, x, 1, j >> 2, j & 3, c);
-    PTA_FENCE();
-  }
-  // Row block 1's P is only consumed after the caller's mask branch; an empty
-  // use here keeps the compiler from sinking its computation past it.
-#pragma unroll
-  for (int k = 0; k < 4; ++k) asm volatile("" ::"v"(P.h[1][k]), "v"(P.lo[1][k]));
-  asm volatile("" ::"v"(st.l[1]));
-}
-
-// Phase C: the P.V products of row block 1.  The V^T operands of blocks 0
-// and 1 come from step_ab; `fill(j)` is called in chunk j (independent vector
-// work of the caller).
-template <int D, typename Fill>
-__device__ __forceinline__ void step_c(StreamState<D, 2>& st, const StepP<D>& P, bf16x8 (&vt)[3], const char* vl0,
-                                       const char* vl1, int lane, Fill fill) {
-  constexpr int DB = D / 16;
-  const bf16x8 phi1 = __builtin_bit_cast(bf16x8, make_uint4(P.h[1][0], P.h[1][1], P.h[1][2], P.h[1][3]));
-  const bf16x8 plo1 = __builtin_bit_cast(bf16x8, make_uint4(P.lo[1][0], P.lo[1][1], P.lo[1][2], P.lo[1][3]));
-  // phase B left blocks 0 and 1 in slots (8 % 3, 9 % 3) = (2, 0); block db of phase C sits in slot (db + 2) % 3
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int db = j >> 1;
-    if ((j & 1) == 0 && db + 2 < DB) vt[(db + 4) % 3] = v_operand<D>(vl0, vl1, db + 2, lane);
-    st.o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[(db + 2) % 3], (j & 1) ? plo1 : phi1, st.o[1][db], 0, 0, 0);
-    fill(j);
-    PTA_FENCE();
-  }
-}
-
 template <int D, int NWR, int NBUF>
 struct DmaGeom {
   static constexpr int TILE = kPage * D * 2;                 // bf16 page tile, HBM and LDS
@@ -491,37 +359,16 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
 #pragma unroll
         for (int db = 0; db < D / 16; ++db) st.o[rb][db] *= alpha[rb];
     }
-    bool need = false;
-    if constexpr (D == 128) {
-      // 1. S of pair s + 1 with P of pair s (phases A and B, P.V of row block 0 in B)
-      PairScores<RB> sn;
-      StepP<D> P;
-      bf16x8 vt[3];
-      step_ab<D>(rows, st, sn, P, vt, x, sb, sb + Gm::TILE, sb + 2 * Gm::TILE, sb + 3 * Gm::TILE, lane, c);
-      if (pbase(s + 1) + 2 * kPage > plain_end) pair_mask<D, RB>(rows, sn, pbase(s + 1), L, t1, lane);
-      // 2. P.V of row block 1 with the lane maxima of pair s + 1 (phase C)
-      step_c<D>(st, P, vt, sb + 2 * Gm::TILE, sb + 3 * Gm::TILE, lane, [&](int j) {
-        if (j == 2 || j == 6) {
-          const int rb = j == 2 ? 0 : 1;
-          auto mx = [](float u, float v) { return __builtin_elementwise_maximum(u, v); };
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xn[rb][e] = sn.s[e >> 2][rb][e & 3];
-          const float pm = mx(mx(mx(xn[rb][0], xn[rb][1]), xn[rb][2]), mx(mx(xn[rb][3], xn[rb][4]), xn[rb][5]));
-          const float pm2 = mx(pm, mx(xn[rb][6], xn[rb][7]));
-          need |= c * pm2 > st.m[rb] + kLazyTau;
-        }
-      });
-    } else {
-      // 1. S of pair s + 1 with P of pair s
-      PairScores<RB> sn;
-      pair_scores<D, RB, true>(rows, sn, sb, sb + Gm::TILE, lane);
-      bf16x8 phi[RB], plo[RB];
-      pair_p<D, RB>(st, x, phi, plo, c);
-      // 2. P.V of pair s with the masked scores of pair s + 1
-      pair_pv_mma<D, RB, true>(st, phi, plo, sb + 2 * Gm::TILE, sb + 3 * Gm::TILE, lane);
-      if (pbase(s + 1) + 2 * kPage > plain_end) pair_mask<D, RB>(rows, sn, pbase(s + 1), L, t1, lane);
-      pair_max_prep<D, RB>(st, sn, xn, need, c);
-    }
+    // 1. S of pair s + 1 with P of pair s
+    PairScores<RB> sn;
+    pair_scores<D, RB, true>(rows, sn, sb, sb + Gm::TILE, lane);
+    bf16x8 phi[RB], plo[RB];
+    pair_p<D, RB>(st, x, phi, plo, c);
+    // 2. P.V of pair s with the masked scores of pair s + 1
+    pair_pv_mma<D, RB, true>(st, phi, plo, sb + 2 * Gm::TILE, sb + 3 * Gm::TILE, lane);
+    if (pbase(s + 1) + 2 * kPage > plain_end) pair_mask<D, RB>(rows, sn, pbase(s + 1), L, t1, lane);
+    bool need;
+    pair_max_prep<D, RB>(st, sn, xn, need, c);
     // 3. the rare reference-max move for pair s + 1
     pend = pair_max_finish<D, RB>(st, xn, need, alpha, c);
   };

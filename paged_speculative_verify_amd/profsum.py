@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 output for the kernels of libpta.
 
-Two summaries, both written as short text under ``profiles/``:
+Three summaries, all written as short text under ``profiles/``:
 
 * ``trace``: the ``--kernel-trace --stats`` table (calls, mean and total time
   per kernel) of one bench run, as Markdown.
@@ -11,6 +11,10 @@ Two summaries, both written as short text under ``profiles/``:
   0.5 GiB fetched and 1 GiB written. The JSON twin carries the hash of the
   kernel sources it was taken on, and the bench reports the figure only while
   that hash still matches.
+* ``sq``: per-dispatch means of SQ/GRBM counter passes of one kernel and the
+  rates derived from them (MFMA busy share of SIMD cycles, MFMA/VALU
+  co-execution, bf16 MFMA flop rate, issue and wait shares of wave cycles,
+  instructions per MFMA, LDS bank-conflict cycles).
 
 Usage::
 
@@ -155,6 +159,74 @@ def cmd_trace(a) -> int:
     return 0
 
 
+# MI355X: 256 compute units in 8 XCDs, 4 SIMDs each; dense bf16 MFMA peak at 2.4 GHz
+NUM_CU, NUM_XCD, SIMD_PER_CU = 256, 8, 4
+BF16_PEAK_FLOPS = 2.5e15
+
+
+def cmd_sq(a) -> int:
+    """SQ counter passes of one kernel: per-dispatch means and the derived rates.
+    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x CUs x SIMDs per CU)
+    (GRBM_GUI_ACTIVE is summed over the XCDs); bf16 MFMA flops = 512 x
+    SQ_INSTS_VALU_MFMA_MOPS_BF16."""
+    per = {}
+    durs = []
+    for path in a.csv:
+        by_dispatch = {}
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if a.kernel not in r["Kernel_Name"]:
+                    continue
+                d = by_dispatch.setdefault(r["Dispatch_Id"], {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                d["_dur_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if not by_dispatch:
+            raise SystemExit(f"{path}: no dispatch of a kernel matching {a.kernel!r}")
+        for d in by_dispatch.values():
+            durs.append(d.pop("_dur_ns"))
+            for k, v in d.items():
+                per.setdefault(k, []).append(v)
+    m = {k: statistics.fmean(v) for k, v in per.items()}
+    dur_s = statistics.fmean(durs) / 1e9
+    derived = []
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in m and "GRBM_GUI_ACTIVE" in m:
+        gui = m["GRBM_GUI_ACTIVE"] / NUM_XCD
+        derived.append(("MFMA busy (of SIMD cycles)", f"{100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * NUM_CU * SIMD_PER_CU):.1f}%"))
+        derived.append(("GPU clock while active (GRBM_GUI_ACTIVE per XCD / duration)", f"{gui / dur_s / 1e9:.2f} GHz"))
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in m:
+            derived.append(("MFMA and VALU co-executing (of SIMD cycles)",
+                            f"{100 * m['SQ_VALU_MFMA_COEXEC_CYCLES'] / (gui * NUM_CU * SIMD_PER_CU):.1f}%"))
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m:
+        fl = 512 * m["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+        derived.append(("bf16 MFMA flops per dispatch (512 x MOPS)", f"{fl:.4g}"))
+        derived.append(("bf16 MFMA rate", f"{fl / dur_s / 1e12:.0f} TFLOP/s ({100 * fl / dur_s / BF16_PEAK_FLOPS:.1f}% of 2.5 PFLOP/s)"))
+    if "SQ_WAVE_CYCLES" in m:
+        for k, label in (("SQ_ACTIVE_INST_ANY", "wave cycles issuing any instruction"),
+                         ("SQ_ACTIVE_INST_VALU", "wave cycles issuing VALU"),
+                         ("SQ_WAIT_INST_ANY", "wave cycles waiting on a dependency (s_waitcnt)")):
+            if k in m:
+                derived.append((label, f"{100 * m[k] / m['SQ_WAVE_CYCLES']:.1f}%"))
+    if "SQ_INSTS_MFMA" in m:
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS"):
+            if k in m:
+                derived.append((f"{k} per MFMA instruction", f"{m[k] / m['SQ_INSTS_MFMA']:.2f}"))
+    if "SQ_LDS_BANK_CONFLICT" in m and "GRBM_GUI_ACTIVE" in m:
+        gui = m["GRBM_GUI_ACTIVE"] / NUM_XCD
+        derived.append(("LDS bank-conflict cycles (of CU cycles)", f"{100 * m['SQ_LDS_BANK_CONFLICT'] / (gui * NUM_CU):.1f}%"))
+    lines = [f"# SQ counters: {a.title}", "", "Commands:", "", "```", a.command, "```", "",
+             f"Dispatches of the kernel matching `{a.kernel}`: {len(durs)} per pass; mean duration under "
+             f"counters {dur_s * 1e6:.1f} us; kernel source hash {kernel_source_hash()}.", "",
+             "| counter | mean per dispatch |", "|---|---|"]
+    lines += [f"| {k} | {v:.5g} |" for k, v in sorted(m.items())]
+    lines += ["", "| derived | value |", "|---|---|"]
+    lines += [f"| {k} | {v} |" for k, v in derived]
+    lines.append("")
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -172,8 +244,14 @@ def main(argv=None) -> int:
     k.add_argument("--command", required=True)
     k.add_argument("--bench-json", default=None)
     k.add_argument("--out", required=True)
+    q = sub.add_parser("sq", help="SQ counter passes of one kernel -> Markdown summary")
+    q.add_argument("--csv", nargs="+", required=True, help="run_counter_collection.csv of each pass")
+    q.add_argument("--kernel", required=True, help="substring of the kernel name")
+    q.add_argument("--title", required=True)
+    q.add_argument("--command", required=True)
+    q.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    return cmd_traffic(a) if a.cmd == "traffic" else cmd_trace(a)
+    return {"traffic": cmd_traffic, "trace": cmd_trace, "sq": cmd_sq}[a.cmd](a)
 
 
 if __name__ == "__main__":
