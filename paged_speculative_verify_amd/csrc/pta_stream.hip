@@ -133,6 +133,38 @@ __device__ __forceinline__ void stream_pairs(const AttnArgs& a, const StreamRows
 }
 
 // ============================================================ per-unit kernel
+// Sequence worked by grid index z of the whole-context entry.  Every unit of
+// that entry is resident at once (two workgroups per compute unit), so a CU's
+// time is the sum of the two contexts it holds, and the longest pair decides
+// the tail.  Indices z and z + ceil(B / 2) get the i-th longest and the i-th
+// shortest sequence: with workgroups handed out in index order, the two that
+// share a CU carry a long and a short context.  The order (by length, ties by
+// index) is recomputed in LDS by every workgroup; `scratch` holds 2 B ints and
+// is free again when this returns.  B > 256 keeps z.
+template <int NT>
+__device__ __forceinline__ int paired_sequence(const AttnArgs& a, int z, int* scratch, int tid) {
+  const int B = a.B;
+  if (B > 256) return z;
+  int* len = scratch;
+  int* order = scratch + B;
+  for (int i = tid; i < B; i += NT) len[i] = a.ctx[i];
+  __syncthreads();
+  for (int i = tid; i < B; i += NT) {
+    const int ci = len[i];
+    int r = 0;
+    for (int j = 0; j < B; ++j) {
+      const int cj = len[j];
+      r += (cj > ci) || (cj == ci && j < i);
+    }
+    order[r] = i;
+  }
+  __syncthreads();
+  const int h = (B + 1) / 2;
+  const int seq = order[z < h ? z : B - 1 - (z - h)];
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(seq);
+}
+
 template <typename KT, int D, int RB, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void stream_attn_kernel(AttnArgs a) {
   using T = StreamTile<KT, D>;
@@ -148,7 +180,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = lane >> 4;          // 16-lane group
   const int m = lane & 15;          // lane within the group
-  const int part = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  const int part = blockIdx.x, hkv = blockIdx.y;
+  static_assert(sizeof(vlds) >= 2 * 256 * sizeof(int), "the pairing scratch must fit the tiles");
+  const int b = a.part_tokens > 0 ? (int)blockIdx.z
+                                  : paired_sequence<NW * 64>(a, blockIdx.z, reinterpret_cast<int*>(&vlds[0][0]),
+                                                             threadIdx.x);
 
   const int C = a.ctx[b];
   const int qb = a.qlen[b];

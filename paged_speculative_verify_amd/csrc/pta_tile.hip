@@ -297,6 +297,7 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
     lds_copy4(tring0 + (uint32_t)((ch & 3) * 256), table + pgA + e);
   };
   const int crow = lane / Gm::UPR, cunit = lane % Gm::UPR;
+  __builtin_assume(wave >= 0 && wave < NWR);     // lets the copies' tile selection fold
   auto copy_stage = [&](int j) {
     const int kr = 2 * min(j + 1, nst - 1), vr = 2 * max(j, 0);      // relative pages
     const bool k2 = kr + 1 < npg, v2 = vr + 1 < npg;
@@ -395,7 +396,7 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
       const int ch = (s + NBUF - 1) / 32 + 3;
       if (ch < nch) issue_chunk(ch);
     }
-    pace(prog0 + 2 * s, prog_len);
+    if ((s & 3) == 0) pace(prog0 + 2 * s, prog_len);     // every 4th pair: the level moves 3 times
     if (s + NBUF - 1 < nst) copy_stage(s + NBUF - 1);     // into the buffer stage s - 1 used
     if (wave_rows) step(s, sb, x, xn);
   };
