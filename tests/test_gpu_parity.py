@@ -346,6 +346,28 @@ def test_full_size_sampled(torch_cuda, name, seqs):
         assert np.isnan(out[b, qb:]).all()
 
 
+# The whole-context stream grid takes its sequences in an order of their context lengths: long/short
+# pairs when the grid is resident at once, longest first when it is larger, grid order past 256
+# sequences.  Every sequence must still be computed exactly once, ties (equal lengths) included.
+ORDER_CASES = [
+    ("pairs_even", spec("o", 40, 32, 8, 128, "bf16", "bf16", (1, 600), 1, "chain", seed=161)),
+    ("pairs_odd_ties", spec("o", 41, 32, 8, 128, "bf16", "bf16", (50, 52), 1, "chain", seed=162)),
+    ("longest_first", spec("o", 90, 32, 8, 128, "bf16", "bf16", (1, 400), 1, "chain", seed=163)),
+    ("longest_first_fp8_chain", spec("o", 80, 32, 8, 128, "bf16", "fp8", (8, 300), 8, "chain", seed=164)),
+    ("grid_order_past_256", spec("o", 300, 4, 1, 128, "bf16", "bf16", (1, 100), 1, "chain", seed=165)),
+]
+
+
+@pytest.mark.parametrize("cid,sp", ORDER_CASES, ids=[c[0] for c in ORDER_CASES])
+def test_whole_grid_sequence_order(torch_cuda, cid, sp):
+    w = make(sp, poison=True)
+    say(cid, "B", w.q.shape[0], "Hkv", w.k_cache.shape[1], "ctx", w.ctx_lens.tolist()[:8])
+    out, lse = run_gpu(torch_cuda, w, mode="whole")
+    ref, ref_lse = run_oracle(w)
+    err = assert_parity(w, out, lse, ref, ref_lse)
+    say(cid, "max abs err", err)
+
+
 def test_splitk_workspace_reused_across_calls(torch_cuda):
     """One zero-filled workspace serves several split-K calls in a row (the
     fused merge resets its arrival counters), with changing partition lengths
