@@ -42,6 +42,7 @@ struct AttnArgs {
   int32_t B, Hq, Hkv, G, Qmax, MBS;
   int32_t part_tokens;     // partition length in tokens (split) or 0
   int32_t num_parts;       // partitions per sequence (grid.x)
+  int32_t seq_order;       // whole-context stream grid: 0 grid order, 1 long/short pairs, 2 longest first
   int64_t num_blocks;
 };
 

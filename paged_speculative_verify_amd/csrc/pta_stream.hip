@@ -133,16 +133,19 @@ __device__ __forceinline__ void stream_pairs(const AttnArgs& a, const StreamRows
 }
 
 // ============================================================ per-unit kernel
-// Sequence worked by grid index z of the whole-context entry.  Every unit of
-// that entry is resident at once (two workgroups per compute unit), so a CU's
-// time is the sum of the two contexts it holds, and the longest pair decides
-// the tail.  Indices z and z + ceil(B / 2) get the i-th longest and the i-th
-// shortest sequence: with workgroups handed out in index order, the two that
-// share a CU carry a long and a short context.  The order (by length, ties by
-// index) is recomputed in LDS by every workgroup; `scratch` holds 2 B ints and
-// is free again when this returns.  B > 256 keeps z.
+// Sequence worked by grid index z of the whole-context entry, by context
+// length (ties by index; the order is recomputed in LDS by every workgroup,
+// `scratch` holds 2 B ints and is free again when this returns).
+//   a.seq_order == 1, the whole grid resident at once (two workgroups per
+//     compute unit): a CU's time is the sum of the two contexts it holds, so
+//     indices z and z + ceil(B / 2) take the i-th longest and the i-th
+//     shortest sequence; with workgroups handed out in index order the two
+//     that share a CU carry a long and a short context.
+//   a.seq_order == 2, a grid larger than what is resident: longest first, so
+//     the short contexts fill the slots that free up at the end.
+// B > 256 keeps z.
 template <int NT>
-__device__ __forceinline__ int paired_sequence(const AttnArgs& a, int z, int* scratch, int tid) {
+__device__ __forceinline__ int ordered_sequence(const AttnArgs& a, int z, int* scratch, int tid) {
   const int B = a.B;
   if (B > 256) return z;
   int* len = scratch;
@@ -160,7 +163,7 @@ __device__ __forceinline__ int paired_sequence(const AttnArgs& a, int z, int* sc
   }
   __syncthreads();
   const int h = (B + 1) / 2;
-  const int seq = order[z < h ? z : B - 1 - (z - h)];
+  const int seq = order[a.seq_order == 1 && z >= h ? B - 1 - (z - h) : z];
   __syncthreads();
   return __builtin_amdgcn_readfirstlane(seq);
 }
@@ -182,9 +185,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int m = lane & 15;          // lane within the group
   const int part = blockIdx.x, hkv = blockIdx.y;
   static_assert(sizeof(vlds) >= 2 * 256 * sizeof(int), "the pairing scratch must fit the tiles");
-  const int b = a.part_tokens > 0 ? (int)blockIdx.z
-                                  : paired_sequence<NW * 64>(a, blockIdx.z, reinterpret_cast<int*>(&vlds[0][0]),
-                                                             threadIdx.x);
+  const int b = a.part_tokens > 0 || a.seq_order == 0
+                    ? (int)blockIdx.z
+                    : ordered_sequence<NW * 64>(a, blockIdx.z, reinterpret_cast<int*>(&vlds[0][0]), threadIdx.x);
 
   const int C = a.ctx[b];
   const int qb = a.qlen[b];
@@ -353,9 +356,31 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 // ---------------------------------------------------------------- launchers
+// Workgroups of stream_attn_kernel<KT, D, RB, NW> resident on the current
+// device at once (compute units times occupancy), asked once per process.
+template <typename KT, int D, int RB, int NW>
+static int resident_workgroups() {
+  static const int n = [] {
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, stream_attn_kernel<KT, D, RB, NW>, NW * 64, 0) !=
+            hipSuccess)
+      return 0;
+    return cus * per;
+  }();
+  return n;
+}
+
 template <typename KT, int D, int RB, int NW>
 static hipError_t launch_stream_t(const AttnArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((stream_attn_kernel<KT, D, RB, NW>), grid, dim3(NW * 64), 0, s, a);
+  AttnArgs b = a;
+  if (a.part_tokens == 0) {
+    const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
+    const int res = resident_workgroups<KT, D, RB, NW>();
+    b.seq_order = res <= 0 ? 0 : wgs <= res ? 1 : 2;
+  }
+  hipLaunchKernelGGL((stream_attn_kernel<KT, D, RB, NW>), grid, dim3(NW * 64), 0, s, b);
   return hipGetLastError();
 }
 
