@@ -203,7 +203,7 @@ def cmd_sq(a) -> int:
     if "SQ_WAVE_CYCLES" in m:
         for k, label in (("SQ_ACTIVE_INST_ANY", "wave cycles issuing any instruction"),
                          ("SQ_ACTIVE_INST_VALU", "wave cycles issuing VALU"),
-                         ("SQ_WAIT_INST_ANY", "wave cycles waiting on a dependency (s_waitcnt)")):
+                         ("SQ_WAIT_INST_ANY", "wave cycles waiting for an instruction to issue")):
             if k in m:
                 derived.append((label, f"{100 * m[k] / m['SQ_WAVE_CYCLES']:.1f}%"))
     if "SQ_INSTS_MFMA" in m:
