@@ -362,9 +362,9 @@ def main(argv=None) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": ("paged tree attention grid + slice merge launch (balanced entry)"
-                                if cfg["mode"] == "balanced" else
-                                "paged tree attention kernel (" + cfg["mode"] + " entry, merge fused)"),
+                     "kernel": {"balanced": "paged tree attention grid + slice merge launch (balanced entry)",
+                                "split": "paged tree attention kernel (split-K entry, partition merge fused)",
+                                "whole": "paged tree attention kernel (whole-context entry)"}[cfg["mode"]],
                      "algorithmic_bytes_per_launch": int(kv_per_launch),
                      "timing": f"HIP events on the launch stream around {K} back-to-back attention "
                                f"calls, run before the timed steps"},
