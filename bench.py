@@ -46,6 +46,7 @@ LAUNCH = {
     "llama31_70b_verify": dict(mode="balanced", split=None, path="auto"),
     "long_splitk_verify": dict(mode="balanced", split=None, path="auto"),
     "fp8_kv_chain": dict(mode="whole", split=None, path="auto"),
+    "shared_prefix_decode": dict(mode="whole", split=None, path="auto"),
 }
 
 
@@ -66,6 +67,20 @@ def kv_bytes(w) -> int:
     n = int(w.ctx_lens.astype(np.int64).sum()) * Hkv * D * 2 * elem
     if s.kv_dtype == "fp8":
         n += int(w.pages_used.astype(np.int64).sum()) * Hkv * 2 * 4
+    return n
+
+
+def unique_kv_bytes(w) -> int:
+    """KV bytes of the distinct (page, KV head) rows a pass must read at least once: with
+    shared-prefix pages every group's prefix counts once, not once per member."""
+    s = w.spec
+    n = kv_bytes(w)
+    if s.shared_prefix_pages > 0 and s.share_group > 1:
+        elem = {"f32": 4, "bf16": 2, "fp8": 1}[s.kv_dtype]
+        Hkv, D = w.k_cache.shape[1], w.k_cache.shape[3]
+        B = w.q.shape[0]
+        groups = (B + s.share_group - 1) // s.share_group
+        n -= (B - groups) * s.shared_prefix_pages * 16 * Hkv * D * 2 * elem
     return n
 
 
@@ -203,6 +218,9 @@ def main(argv=None) -> int:
                          "sequence, -1 = balanced page slices")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--private-pages", action="store_true",
+                    help="shared-prefix workload only: the same batch with every sequence on pages of "
+                         "its own (the reference the shared pages are compared with)")
     ap.add_argument("--qlen-floor", action="store_true",
                     help="instead of the bench line: attention time against the number of candidates "
                          "per sequence at the decode shape, T(q_len) / T(1)")
@@ -244,7 +262,7 @@ def main(argv=None) -> int:
     print(f"[bench] generating {args.sets} input set(s) for {name}", file=sys.stderr, flush=True)
     sets = []
     for r in range(args.sets):
-        w = make(name, seed=None if r == 0 else 1000 + r)
+        w = make(name, seed=None if r == 0 else 1000 + r, **({"share_group": 1} if args.private_pages else {}))
         sets.append(DeviceSet(w, torch))
         print(f"[bench] set {r}: ctx sum {int(w.ctx_lens.sum())}, KV {kv_bytes(w) / 1e6:.1f} MB",
               file=sys.stderr, flush=True)
@@ -320,12 +338,15 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     kvb = [kv_bytes(sets[o].w) for o in order]
+    ukvb = [unique_kv_bytes(sets[o].w) for o in order]     # = kvb unless pages are shared
     cands = [int(sets[o].w.q_lens.sum()) for o in order]
     flops = {r: attn_flops(sets[r].w) for r in set(order)}
 
     attn_avg_s = attn_avg_ms / 1e3
     kv_per_launch = sum(kvb) / K
-    achieved_gbs = kv_per_launch / attn_avg_s / 1e9
+    unique_per_launch = sum(ukvb) / K
+    # the roofline counts what must cross HBM at least once: distinct pages (a shared prefix once)
+    achieved_gbs = unique_per_launch / attn_avg_s / 1e9
     ms_per_step = wall / K * 1e3
     value = kv_per_launch / (ms_per_step / 1e3) / 1e9          # whole-step throughput
     cand_per_s = (sum(cands) / K) / (ms_per_step / 1e3)
@@ -347,12 +368,17 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 KV, bf16 Q"}[sets[0].w.spec.kv_dtype],
         "data": "synthetic",
-        "config": {"workload": name, "batch": sets[0].w.q.shape[0], "q_heads": sets[0].w.q.shape[2],
+        "config": {"workload": name + (" (private pages)" if args.private_pages else ""),
+                   "batch": sets[0].w.q.shape[0], "q_heads": sets[0].w.q.shape[2],
                    "kv_heads": sets[0].w.k_cache.shape[1], "head_dim": sets[0].w.q.shape[3],
                    "max_q_len": sets[0].w.q.shape[1], "page": 16, "entry": cfg["mode"],
                    "split_tokens": cfg["split"],
                    "path": cfg["path"], "input_sets_rotated": len(sets)},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        **({"shared_prefix": {"kv_bytes_all_sequences_per_step": int(kv_per_launch),
+                              "distinct_kv_bytes_per_step": int(unique_per_launch),
+                              "note": "value counts every sequence's context; roofline counts distinct pages"}}
+           if unique_per_launch != kv_per_launch else {}),
         "candidates_per_s": round(cand_per_s, 1),
         "attention_ms": round(attn_avg_s * 1e3, 5),
         "kv_append_ms": round(append_avg_ms, 5),
@@ -365,7 +391,7 @@ def main(argv=None) -> int:
                      "kernel": {"balanced": "paged tree attention grid + slice merge launch (balanced entry)",
                                 "split": "paged tree attention kernel (split-K entry, partition merge fused)",
                                 "whole": "paged tree attention kernel (whole-context entry)"}[cfg["mode"]],
-                     "algorithmic_bytes_per_launch": int(kv_per_launch),
+                     "algorithmic_bytes_per_launch": int(unique_per_launch),
                      "timing": f"HIP events on the launch stream around {K} back-to-back attention "
                                f"calls, run before the timed steps"},
         "kernel_source_hash": src_hash,

@@ -325,6 +325,7 @@ FULL = [
     ("llama31_70b_verify", [0, 9, 31]),
     ("long_splitk_verify", [1]),
     ("fp8_kv_chain", [0, 77, 127]),
+    ("shared_prefix_decode", [0, 9, 63]),
 ]
 
 
@@ -363,6 +364,29 @@ def test_whole_grid_sequence_order(torch_cuda, cid, sp):
     w = make(sp, poison=True)
     say(cid, "B", w.q.shape[0], "Hkv", w.k_cache.shape[1], "ctx", w.ctx_lens.tolist()[:8])
     out, lse = run_gpu(torch_cuda, w, mode="whole")
+    ref, ref_lse = run_oracle(w)
+    err = assert_parity(w, out, lse, ref, ref_lse)
+    say(cid, "max abs err", err)
+
+
+# Shared-prefix pages: groups of sequences alias their first pages in the block tables.
+SHARED_CASES = [
+    ("shared_decode_whole", spec("s", 24, 32, 8, 128, "bf16", "bf16", (300, 900), 1, "chain", seed=171,
+                                 share_group=8, shared_prefix_pages=12), "whole"),
+    ("shared_decode_balanced", spec("s", 24, 32, 8, 128, "bf16", "bf16", (300, 900), 1, "chain", seed=171,
+                                    share_group=8, shared_prefix_pages=12), "balanced"),
+    ("shared_tree16_balanced", spec("s", 8, 64, 8, 128, "bf16", "bf16", (200, 700), 16, "random", 6, seed=172,
+                                    share_group=4, shared_prefix_pages=8), "balanced"),
+    ("shared_fp8_chain_whole", spec("s", 16, 32, 8, 128, "bf16", "fp8", (200, 700), 8, "chain", seed=173,
+                                    share_group=4, shared_prefix_pages=8), "whole"),
+]
+
+
+@pytest.mark.parametrize("cid,sp,mode", SHARED_CASES, ids=[c[0] for c in SHARED_CASES])
+def test_shared_prefix_parity(torch_cuda, cid, sp, mode):
+    w = make(sp, poison=True)
+    say(cid, "B", w.q.shape[0], "group", sp.share_group, "shared pages", sp.shared_prefix_pages, "mode", mode)
+    out, lse = run_gpu(torch_cuda, w, mode=mode)
     ref, ref_lse = run_oracle(w)
     err = assert_parity(w, out, lse, ref, ref_lse)
     say(cid, "max abs err", err)

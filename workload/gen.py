@@ -127,6 +127,10 @@ class Spec:
     scale: Optional[float] = None             # softmax scale; None -> 1/sqrt(D)
     split_tokens: Optional[int] = None        # split-K partition length
     seed: int = 0
+    # shared prefix: consecutive groups of `share_group` sequences alias their first
+    # `shared_prefix_pages` pages (same physical pages, same K/V); 0 = no sharing
+    share_group: int = 1
+    shared_prefix_pages: int = 0
 
     @property
     def softmax_scale(self) -> float:
@@ -151,6 +155,11 @@ CONFIGS = {
     # fp8 e4m3fn KV with per-(page, KV head) scales, 8-candidate chain
     "fp8_kv_chain": Spec("fp8_kv_chain", 128, 32, 8, 128, "bf16", "fp8",
                          ctx_range=(2048, 16384), q_len=8, tree="chain", seed=4),
+    # the decode shape with groups of 8 sequences sharing a 2048-token prefix (same physical
+    # pages in their block tables), each with its own 512..2048-token continuation
+    "shared_prefix_decode": Spec("shared_prefix_decode", 64, 32, 8, 128, "bf16", "bf16",
+                                 ctx_range=(2560, 4096), q_len=1, tree="chain", seed=5,
+                                 share_group=8, shared_prefix_pages=128),
 }
 
 
@@ -227,10 +236,18 @@ def make(spec: Spec | str, *, seed: Optional[int] = None, poison: bool = False,
         lo, hi = spec.ctx_range
         ctx = rng.integers(lo, hi + 1, size=B).astype(np.int32)
     ctx = np.maximum(ctx, q_lens).astype(np.int32)
+    share = spec.shared_prefix_pages > 0 and spec.share_group > 1
+    SP = spec.shared_prefix_pages if share else 0
+    if share:
+        # the shared pages are whole pages of every member's committed prefix
+        ctx = np.maximum(ctx, SP * PAGE + q_lens).astype(np.int32)
+    group_of = np.arange(B) // max(1, spec.share_group)
+    n_groups = int(group_of.max()) + 1 if B else 0
 
-    # 2. pool and block tables: consecutive slices of one random permutation
+    # 2. pool and block tables: consecutive slices of one random permutation (with a shared
+    #    prefix, each group's first pages come once, then every member's own pages)
     pages = ((ctx + PAGE - 1) // PAGE).astype(np.int32)
-    used = int(pages.sum())
+    used = int(pages.sum()) - (B - n_groups) * SP
     NB = spec.pool_pages if spec.pool_pages is not None else int(math.ceil(spec.pool_factor * used))
     if NB < used:
         raise ValueError("pool smaller than the pages in use")
@@ -241,8 +258,13 @@ def make(spec: Spec | str, *, seed: Optional[int] = None, poison: bool = False,
     tables = np.full((B, MBS), pad_page, dtype=np.int32)
     off = 0
     for b in range(B):
-        tables[b, :pages[b]] = perm[off:off + pages[b]]
-        off += pages[b]
+        if share and (b == 0 or group_of[b] != group_of[b - 1]):
+            group_pages = perm[off:off + SP]
+            off += SP
+        if share:
+            tables[b, :SP] = group_pages
+        tables[b, SP:pages[b]] = perm[off:off + pages[b] - SP]
+        off += pages[b] - SP
 
     # 3. candidate trees
     rng = np.random.default_rng(s_tree)
@@ -279,12 +301,19 @@ def make(spec: Spec | str, *, seed: Optional[int] = None, poison: bool = False,
     contig_k = [None] * B if keep_contiguous else None
     contig_v = [None] * B if keep_contiguous else None
     seq_streams = s_kv.spawn(B)
+    group_streams = s_kv.spawn(n_groups) if share else None
 
     def fill_seq(b: int) -> None:
         g = np.random.default_rng(seq_streams[b])
         C, P = int(ctx[b]), int(pages[b])
+        gp = np.random.default_rng(group_streams[group_of[b]]) if share else None
         for which, cache, scl in ((0, k_cache, k_scale), (1, v_cache, v_scale)):
-            x = g.standard_normal((Hkv, C, D), dtype=np.float32)
+            if share:
+                # the group's prefix (the same draw for every member), then this sequence's own rows
+                x = np.concatenate([gp.standard_normal((Hkv, SP * PAGE, D), dtype=np.float32),
+                                    g.standard_normal((Hkv, C - SP * PAGE, D), dtype=np.float32)], axis=1)
+            else:
+                x = g.standard_normal((Hkv, C, D), dtype=np.float32)
             if spec.kv_dtype == "bf16":
                 x = bf16_bits_to_f32(f32_to_bf16_bits(x))   # values the kernel sees
             if keep_contiguous:
