@@ -52,7 +52,12 @@ LAUNCH = {
 
 
 def launch_config(name: str) -> dict:
-    return dict(LAUNCH[name])
+    cfg = dict(LAUNCH[name])
+    if cfg["mode"] == "shared":
+        # the shared-prefix entry works split-K with the shared prefix as partition 0
+        from workload.gen import CONFIGS
+        cfg["split"] = CONFIGS[name].shared_prefix_pages * 16
+    return cfg
 
 
 
@@ -135,6 +140,11 @@ class DeviceSet:
                 self.v_new = self.v_new.view(torch.bfloat16)
         self.slots = torch.from_numpy(slots).cuda()
         self.out = torch.empty_like(self.d.q)
+        # shared-prefix groups: the first sequence of each run of share_group sequences leads it
+        G = max(1, s.share_group) if s.shared_prefix_pages > 0 else 1
+        self.max_group = G
+        self.prefix_leader = torch.from_numpy(
+            np.array([(b // G) * G for b in range(B)], dtype=np.int32)).to(self.d.q.device)
         self.lse = torch.empty((B, Hq, Qmax), dtype=torch.float32, device=self.d.q.device)
         self.workspace = None
 
@@ -150,6 +160,12 @@ def run_attention(psv, ds, cfg):
         psv.taco_paged_tree_attn(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
                                  d.tree_mask, d.scale, out=ds.out, lse=ds.lse, k_scale=d.k_scale,
                                  v_scale=d.v_scale, max_ctx_len=d.max_ctx_len, path=cfg["path"])
+    elif cfg["mode"] == "shared":
+        psv.taco_paged_tree_attn_shared_prefix(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
+                                               d.q_lens, d.tree_mask, ds.prefix_leader, ds.max_group,
+                                               cfg["split"], d.scale, out=ds.out, lse=ds.lse,
+                                               k_scale=d.k_scale, v_scale=d.v_scale, workspace=ds.workspace,
+                                               max_ctx_len=d.max_ctx_len, path=cfg["path"])
     else:
         psv.taco_paged_tree_attn_splitk(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
                                         d.q_lens, d.tree_mask, d.scale, cfg["split"], out=ds.out,
@@ -218,6 +234,9 @@ def main(argv=None) -> int:
                          "sequence, -1 = balanced page slices")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--shared-entry", action="store_true",
+                    help="shared-prefix workload only: run taco_paged_tree_attn_shared_prefix (each "
+                         "group's prefix partition worked once) instead of the whole-context grid")
     ap.add_argument("--private-pages", action="store_true",
                     help="shared-prefix workload only: the same batch with every sequence on pages of "
                          "its own (the reference the shared pages are compared with)")
@@ -259,6 +278,12 @@ def main(argv=None) -> int:
     if args.split is not None:
         cfg["mode"] = "split" if args.split > 0 else ("whole" if args.split == 0 else "balanced")
         cfg["split"] = args.split if args.split > 0 else None
+    if args.shared_entry:
+        from workload.gen import CONFIGS
+        if CONFIGS[name].shared_prefix_pages <= 0 or args.private_pages:
+            print("--shared-entry needs a shared-prefix workload on shared pages", file=sys.stderr)
+            return 2
+        cfg["mode"], cfg["split"] = "shared", CONFIGS[name].shared_prefix_pages * 16
     print(f"[bench] generating {args.sets} input set(s) for {name}", file=sys.stderr, flush=True)
     sets = []
     for r in range(args.sets):
@@ -267,7 +292,7 @@ def main(argv=None) -> int:
         print(f"[bench] set {r}: ctx sum {int(w.ctx_lens.sum())}, KV {kv_bytes(w) / 1e6:.1f} MB",
               file=sys.stderr, flush=True)
     for ds in sets:
-        if cfg["mode"] == "split":
+        if cfg["mode"] in ("split", "shared"):
             nbytes = psv.taco_paged_tree_attn_splitk_workspace_size(
                 ds.d.q, ds.d.k_cache, ds.d.block_tables, cfg["split"], max_ctx_len=ds.d.max_ctx_len)
         elif cfg["mode"] == "balanced":
@@ -288,6 +313,7 @@ def main(argv=None) -> int:
             cfg["mode"], d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens, d.tree_mask,
             d.scale, ds.out, lse=ds.lse, k_scale=d.k_scale, v_scale=d.v_scale,
             partition_tokens=cfg["split"], workspace=ds.workspace, max_ctx_len=d.max_ctx_len,
+            prefix_leader=ds.prefix_leader, max_group=ds.max_group,
             path=cfg["path"])
     for i in range(args.warmup):
         ds = sets[i % len(sets)]
@@ -390,7 +416,9 @@ def main(argv=None) -> int:
                      "traffic": traffic,
                      "kernel": {"balanced": "paged tree attention grid + slice merge launch (balanced entry)",
                                 "split": "paged tree attention kernel (split-K entry, partition merge fused)",
-                                "whole": "paged tree attention kernel (whole-context entry)"}[cfg["mode"]],
+                                "whole": "paged tree attention kernel (whole-context entry)",
+                                "shared": "paged tree attention kernel (shared-prefix entry: each group's "
+                                          "prefix partition once, partition merge fused)"}[cfg["mode"]],
                      "algorithmic_bytes_per_launch": int(unique_per_launch),
                      "timing": f"HIP events on the launch stream around {K} back-to-back attention "
                                f"calls, run before the timed steps"},

@@ -144,6 +144,41 @@ pta_status taco_paged_tree_attn_splitk(const pta_dims* dims, const void* q, cons
                                        float* lse, int32_t partition_tokens, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/* Shared-prefix paged tree attention (the pages' prefix cache: sequences
+ * whose block tables alias the same physical pages for a common prefix,
+ * design talk "4. 支持 Paged Attention" and the 618zxw.cn article's Prefix
+ * Cache).  Split-K with partition_tokens = shared_tokens, where partition 0
+ * (logical positions 0 .. shared_tokens - 1) of every group of sequences is
+ * worked once for all of the group's rows: the pages are read once per group
+ * instead of once per sequence, and each member's later partitions are worked
+ * as in taco_paged_tree_attn_splitk; the last unit of each (sequence, KV head)
+ * merges its partitions by log-sum-exp in the same launch.
+ *
+ * prefix_leader: device int32 [num_seqs]; sequence b belongs to the group whose
+ *   first sequence is prefix_leader[b]; a group is a run of consecutive
+ *   sequences (prefix_leader[lead] == lead, then lead + 1, ... with the same
+ *   leader), at most max_group of them.  A sequence with prefix_leader[b] == b
+ *   and no followers is a group of one (its partition 0 is worked alone).
+ * Caller contract (results are undefined otherwise; not checked on the
+ *   device): within a group of two or more, the first shared_tokens / 16
+ *   block-table entries of every member are equal, and every member's
+ *   committed part (ctx_lens - q_lens) is at least shared_tokens.
+ * max_group * (num_q_heads / num_kv_heads) * max_q_len must be at most 32 and
+ *   q bf16 (the group's rows form one matrix-core stream unit), else
+ *   PTA_ERR_UNSUPPORTED; shared_tokens a positive multiple of 32 (else
+ *   PTA_ERR_BAD_DIMS).
+ * workspace: as taco_paged_tree_attn_splitk with partition_tokens =
+ *   shared_tokens (same size query, same zero-counter contract).  Other
+ *   arguments as taco_paged_tree_attn. */
+pta_status taco_paged_tree_attn_shared_prefix(const pta_dims* dims, const void* q, const void* k_cache,
+                                              const void* v_cache, const float* k_scale,
+                                              const float* v_scale, const int32_t* block_tables,
+                                              const int32_t* ctx_lens, const int32_t* q_lens,
+                                              const uint8_t* tree_mask, const int32_t* prefix_leader,
+                                              int32_t max_group, int32_t shared_tokens, float scale,
+                                              void* out, float* lse, void* workspace,
+                                              size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace taken by taco_paged_tree_attn_balanced for these
  * dims on the current device (0 on invalid input or when the balanced mode
  * does not serve these dims). */

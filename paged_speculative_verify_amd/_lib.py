@@ -72,6 +72,9 @@ def load() -> ctypes.CDLL:
     lib.taco_paged_tree_attn_splitk_workspace_size.restype = SZ
     lib.taco_paged_tree_attn_splitk.argtypes = [D, P, P, P, P, P, P, P, P, P, F, P, P, I32, P, SZ, P]
     lib.taco_paged_tree_attn_splitk.restype = ctypes.c_int
+    lib.taco_paged_tree_attn_shared_prefix.argtypes = [D, P, P, P, P, P, P, P, P, P, P, I32, I32, F, P, P, P,
+                                                       SZ, P]
+    lib.taco_paged_tree_attn_shared_prefix.restype = ctypes.c_int
     lib.taco_paged_tree_attn_balanced_workspace_size.argtypes = [D]
     lib.taco_paged_tree_attn_balanced_workspace_size.restype = SZ
     lib.taco_paged_tree_attn_balanced.argtypes = [D, P, P, P, P, P, P, P, P, P, F, P, P, P, SZ, P]
@@ -258,6 +261,38 @@ def taco_paged_tree_attn_splitk(q, k_cache, v_cache, block_tables, ctx_lens, q_l
     return out
 
 
+def taco_paged_tree_attn_shared_prefix(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask,
+                                       prefix_leader, max_group, shared_tokens, scale, out=None, lse=None,
+                                       k_scale=None, v_scale=None, workspace=None, max_ctx_len=None,
+                                       path="auto", stream=None):
+    """Shared-prefix paged tree attention (see include/pta.h): partition 0 of every group of
+    consecutive sequences that alias their first shared_tokens / 16 pages is worked once.
+
+    prefix_leader: int32 device tensor [B], the first sequence of each sequence's group.
+    workspace: as taco_paged_tree_attn_splitk with partition_tokens = shared_tokens
+    (allocated zero-filled here if None).
+    """
+    torch = _torch()
+    lib = load()
+    _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale)
+    _need(prefix_leader, "prefix_leader", 1, torch.int32, q.device)
+    out, lse = _alloc_out(q, out, lse)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    need = int(lib.taco_paged_tree_attn_splitk_workspace_size(ctypes.byref(dims), int(shared_tokens)))
+    if workspace is None:
+        if need == 0:
+            raise ValueError("invalid dims or shared_tokens")
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    else:
+        _need(workspace, "workspace", device=q.device)
+    _check(lib.taco_paged_tree_attn_shared_prefix(
+        ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask), _ptr(prefix_leader),
+        int(max_group), int(shared_tokens), float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
 def taco_paged_tree_attn_balanced_workspace_size(q, k_cache, block_tables, max_ctx_len=None,
                                                  path="auto") -> int:
     dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
@@ -413,11 +448,13 @@ class PreparedCall:
 
 def prepare_paged_tree_attn(mode, q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask,
                             scale, out, lse=None, k_scale=None, v_scale=None, partition_tokens=None,
-                            workspace=None, max_ctx_len=None, path="auto", stream=None) -> PreparedCall:
+                            workspace=None, max_ctx_len=None, path="auto", stream=None, prefix_leader=None,
+                            max_group=None) -> PreparedCall:
     """Validate once and return a PreparedCall for one of the attention entry points.
 
     mode: "whole" (taco_paged_tree_attn), "split" (taco_paged_tree_attn_splitk with
-    partition_tokens) or "balanced" (taco_paged_tree_attn_balanced).  out (and, for
+    partition_tokens), "shared" (taco_paged_tree_attn_shared_prefix with partition_tokens =
+    shared tokens, prefix_leader and max_group) or "balanced" (taco_paged_tree_attn_balanced).  out (and, for
     split/balanced, a zero-initialised workspace of sufficient size) must be given.
     """
     torch = _torch()
@@ -443,6 +480,16 @@ def prepare_paged_tree_attn(mode, q, k_cache, v_cache, block_tables, ctx_lens, q
             raise ValueError(f"split-K workspace must hold {need} bytes")
         return PreparedCall(lib.taco_paged_tree_attn_splitk,
                             common + (int(partition_tokens), _ptr(workspace), wbytes, st), keep)
+    if mode == "shared":
+        _need(prefix_leader, "prefix_leader", 1, torch.int32, q.device)
+        need = int(lib.taco_paged_tree_attn_splitk_workspace_size(ctypes.byref(dims), int(partition_tokens)))
+        if need == 0 or need > wbytes:
+            raise ValueError(f"shared-prefix workspace must hold {need} bytes")
+        args = (ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask), _ptr(prefix_leader),
+                int(max_group), int(partition_tokens), float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                wbytes, st)
+        return PreparedCall(lib.taco_paged_tree_attn_shared_prefix, args, keep + (prefix_leader,))
     if mode == "balanced":
         need = int(lib.taco_paged_tree_attn_balanced_workspace_size(ctypes.byref(dims)))
         if need == 0 or need > wbytes:

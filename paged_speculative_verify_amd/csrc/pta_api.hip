@@ -280,6 +280,48 @@ pta_status taco_paged_tree_attn_splitk(const pta_dims* d, const void* q, const v
   return run_attn(d, a, p, (hipStream_t)stream);
 }
 
+pta_status taco_paged_tree_attn_shared_prefix(const pta_dims* d, const void* q, const void* k_cache,
+                                              const void* v_cache, const float* k_scale,
+                                              const float* v_scale, const int32_t* block_tables,
+                                              const int32_t* ctx_lens, const int32_t* q_lens,
+                                              const uint8_t* tree_mask, const int32_t* prefix_leader,
+                                              int32_t max_group, int32_t shared_tokens, float scale,
+                                              void* out, float* lse, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  pta_status st = check_dims(d);
+  if (st != PTA_OK) return st;
+  if (!isfinite(scale)) return PTA_ERR_BAD_DIMS;
+  if (max_group < 1) return PTA_ERR_BAD_DIMS;
+  SplitLayout L;
+  if (!split_layout(d, shared_tokens, &L)) return PTA_ERR_BAD_DIMS;
+  if (L.parts > 65535) return PTA_ERR_UNSUPPORTED;
+  Plan p;
+  st = plan_for(d, &p);
+  if (st != PTA_OK) return st;
+  // the group's rows share one matrix-core stream unit of up to 32 rows
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (p.fam != FAM_STREAM || (int64_t)max_group * G * d->max_q_len > kStreamMaxRows) return PTA_ERR_UNSUPPORTED;
+  p.rb = 2;
+  if (d->num_seqs == 0) return PTA_OK;
+  st = check_attn_ptrs(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
+                       tree_mask, out);
+  if (st != PTA_OK) return st;
+  if (prefix_leader == nullptr || workspace == nullptr) return PTA_ERR_NULL_PTR;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return PTA_ERR_BAD_DIMS;
+  if (workspace_bytes < L.total) return PTA_ERR_WORKSPACE_TOO_SMALL;
+  AttnArgs a = make_args(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
+                         tree_mask, scale, out, lse);
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.counters = reinterpret_cast<int32_t*>(ws);
+  a.part_o = reinterpret_cast<float*>(ws + L.o_off);
+  a.part_lse = reinterpret_cast<float*>(ws + L.lse_off);
+  a.part_tokens = shared_tokens;
+  a.num_parts = (int32_t)L.parts;
+  a.prefix_leader = prefix_leader;
+  a.max_group = max_group;
+  return run_attn(d, a, p, (hipStream_t)stream);
+}
+
 size_t taco_paged_tree_attn_balanced_workspace_size(const pta_dims* d) {
   if (check_dims(d) != PTA_OK) return 0;
   Plan p;

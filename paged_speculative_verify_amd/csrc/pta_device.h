@@ -43,6 +43,10 @@ struct AttnArgs {
   int32_t part_tokens;     // partition length in tokens (split) or 0
   int32_t num_parts;       // partitions per sequence (grid.x)
   int32_t seq_order;       // whole-context stream grid: 0 grid order, 1 long/short pairs, 2 longest first
+  // shared-prefix entry: leader (first sequence) of each sequence's group of consecutive
+  // sequences sharing partition 0 (null otherwise), and the largest group size
+  const int32_t* prefix_leader;
+  int32_t max_group;
   int64_t num_blocks;
 };
 

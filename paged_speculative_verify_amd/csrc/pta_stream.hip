@@ -168,6 +168,49 @@ __device__ __forceinline__ int ordered_sequence(const AttnArgs& a, int z, int* s
   return __builtin_amdgcn_readfirstlane(seq);
 }
 
+// Rows of a shared-prefix group (sequences lead .. lead + n - 1, whose block
+// tables alias the pages of partition 0): the G * q_j rows of member j follow
+// those of member j - 1, row r of member j being q-head hkv * G + r / q_j,
+// candidate r % q_j.  Every row sees every token of the shared prefix (it lies
+// in each member's committed part), so no candidate mask bits are needed.
+// bj[rb] receives the member sequence of the lane's row block rb.
+template <int D, int RB>
+__device__ __forceinline__ void load_group_rows(StreamRows<D, RB>& R, int (&bj)[RB], const AttnArgs& a, int lead,
+                                                int n, int hkv, int g, int m) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = rb * 16 + m;
+    int base = 0, mem = -1, rl = 0, qj = 1;
+    for (int t = 0; t < n; ++t) {
+      const int qt = a.qlen[lead + t];
+      if (mem < 0 && row < base + a.G * qt) {
+        mem = t;
+        rl = row - base;
+        qj = qt;
+      }
+      base += a.G * qt;
+    }
+    R.ok[rb] = mem >= 0;
+    bj[rb] = lead + (mem >= 0 ? mem : 0);
+    R.h[rb] = hkv * a.G + (R.ok[rb] ? rl / qj : 0);
+    R.i[rb] = R.ok[rb] ? rl % qj : 0;
+    R.mbits[rb] = 0ull;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         (((int64_t)bj[rb] * a.Qmax + R.i[rb]) * a.Hq + R.h[rb]) * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      uint4 w = R.ok[rb] ? *reinterpret_cast<const uint4*>(qp + 32 * kk) : make_uint4(0, 0, 0, 0);
+      if (a.scale_log2 < 0.f) {                // a negative scale moves into the sign of Q
+        w.x ^= 0x80008000u;
+        w.y ^= 0x80008000u;
+        w.z ^= 0x80008000u;
+        w.w ^= 0x80008000u;
+      }
+      R.qop[rb][kk] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+}
+
 template <typename KT, int D, int RB, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void stream_attn_kernel(AttnArgs a) {
   using T = StreamTile<KT, D>;
@@ -191,7 +234,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   const int C = a.ctx[b];
   const int qb = a.qlen[b];
-  const int L = C - qb;
+  int L = C - qb;
   const int M = a.G * qb;
   int t0 = 0, t1 = C;
   if (a.part_tokens > 0) {
@@ -201,8 +244,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
   const bool split_out = unit_writes_partials(a, C);   // else: final output written directly
 
+  // Shared-prefix entry, partition 0: a group's leader works the shared pages
+  // once for the rows of every member; the other members skip the partition.
+  int grp = 0;
+  int bj[RB];
+  if (a.prefix_leader != nullptr && part == 0) {
+    // a follower within reach of its leader (the leader counts exactly these) leaves the
+    // partition to it; any other sequence works its own partition 0
+    const int lead = a.prefix_leader[b];
+    if (lead >= 0 && lead < b && b - lead < a.max_group) {
+      bool chain = true;                 // every sequence between the leader and b follows it too
+      for (int t = lead + 1; t < b; ++t) chain = chain && a.prefix_leader[t] == lead;
+      if (chain) return;
+    }
+    if (lead == b) {
+      grp = 1;
+      while (grp < a.max_group && b + grp < a.B && a.prefix_leader[b + grp] == b) ++grp;
+      grp = __builtin_amdgcn_readfirstlane(grp);
+    }
+    if (grp == 1) grp = 0;          // a group of one: the ordinary partition
+  }
+
   StreamRows<D, RB> rows;
-  load_rows(rows, a, b, hkv, qb, M, g, m);
+  if (grp > 1) {
+    load_group_rows(rows, bj, a, b, grp, hkv, g, m);
+    L = t1;                         // every shared token is visible to every row
+  } else {
+    load_rows(rows, a, b, hkv, qb, M, g, m);
+  }
   StreamState<D, RB> st;
   st.init();
 
@@ -254,6 +323,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 
   // ---- epilogue (last wave holds the merged rows)
+  if (grp > 1) {
+    if (wave == NW - 1) {
+      auto addr = [&](int rb, float*& o, float*& l) {
+        const int64_t prow = (((int64_t)bj[rb] * a.Hq + rows.h[rb]) * a.Qmax + rows.i[rb]) * a.num_parts;
+        o = a.part_o + prow * D;
+        l = a.part_lse + prow;
+      };
+      store_partial_rows(rows, st, g, addr);
+    }
+    for (int t = 0; t < grp; ++t) {
+      const int bt = b + t;
+      splitk_finish<BF16, D>(a, bt, hkv, a.ctx[bt], a.qlen[bt]);
+    }
+    return;
+  }
   if (wave == NW - 1) {
     if (split_out) {
       auto addr = [&](int rb, float*& o, float*& l) {

@@ -52,7 +52,14 @@ def run_gpu(torch, w, split=None, path="auto", want_lse=True, mode=None, workspa
     B, Qmax, Hq, D = w.q.shape
     lse = torch.full((B, Hq, Qmax), float("nan"), dtype=torch.float32, device=d.q.device) if want_lse else None
     mode = mode or ("whole" if split is None else "split")
-    if mode == "balanced":
+    if mode == "shared":
+        sg = w.spec.share_group
+        leader = torch.from_numpy(np.array([(b // sg) * sg for b in range(B)], dtype=np.int32)).to(d.q.device)
+        psv.taco_paged_tree_attn_shared_prefix(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
+                                               d.tree_mask, leader, sg, split, d.scale, out=out, lse=lse,
+                                               k_scale=d.k_scale, v_scale=d.v_scale, max_ctx_len=d.max_ctx_len,
+                                               path=path)
+    elif mode == "balanced":
         psv.taco_paged_tree_attn_balanced(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
                                           d.q_lens, d.tree_mask, d.scale, out=out, lse=lse,
                                           k_scale=d.k_scale, v_scale=d.v_scale, workspace=workspace,
@@ -390,6 +397,80 @@ def test_shared_prefix_parity(torch_cuda, cid, sp, mode):
     ref, ref_lse = run_oracle(w)
     err = assert_parity(w, out, lse, ref, ref_lse)
     say(cid, "max abs err", err)
+
+
+# taco_paged_tree_attn_shared_prefix: partition 0 of each group worked once for all members' rows.
+def leaders_by_group(B, alias, size):
+    """Leaders of runs of `size` consecutive sequences inside each run of `alias` sequences that
+    alias the same prefix pages (a group must never span two aliasing runs)."""
+    lead = []
+    for b in range(B):
+        g0 = (b // alias) * alias
+        lead.append(g0 + ((b - g0) // size) * size)
+    return np.array(lead, dtype=np.int32)
+
+
+SHARED_ENTRY_CASES = [
+    # (id, spec, group sizes handed to the entry (None: the workload's groups), max_group)
+    ("decode_groups8", spec("se", 24, 32, 8, 128, "bf16", "bf16", (300, 900), 1, "chain", seed=181,
+                            share_group=8, shared_prefix_pages=12), None, 8),
+    ("tree2_groups4", spec("se", 16, 32, 8, 128, "bf16", "bf16", (200, 700), 2, "random", seed=182,
+                           share_group=4, shared_prefix_pages=8), None, 4),
+    ("fp8_decode_groups8", spec("se", 16, 32, 8, 128, "bf16", "fp8", (300, 900), 1, "chain", seed=183,
+                                share_group=8, shared_prefix_pages=8), None, 8),
+    ("ragged_last_group", spec("se", 20, 32, 8, 128, "bf16", "bf16", (300, 900), 1, "chain", seed=184,
+                               share_group=8, shared_prefix_pages=10), None, 8),
+    # the workload's groups of 8 handed over as groups of 3, 3 and 2: any split of a run of aliased
+    # sequences into consecutive groups is valid
+    ("split_groups3", spec("se", 16, 32, 8, 128, "bf16", "bf16", (300, 900), 1, "chain", seed=185,
+                           share_group=8, shared_prefix_pages=12), 3, 8),
+    # groups of one: every sequence works its own partition 0
+    ("groups_of_one", spec("se", 8, 32, 8, 128, "bf16", "bf16", (300, 900), 1, "chain", seed=186,
+                           share_group=8, shared_prefix_pages=12), 1, 8),
+]
+
+
+@pytest.mark.parametrize("cid,sp,gsize,max_group", SHARED_ENTRY_CASES, ids=[c[0] for c in SHARED_ENTRY_CASES])
+def test_shared_prefix_entry_parity(torch_cuda, cid, sp, gsize, max_group):
+    import paged_speculative_verify_amd as psv
+    torch = torch_cuda
+    w = make(sp, poison=True)
+    d = to_device(w)
+    B, Qmax, Hq, D = w.q.shape
+    lead = leaders_by_group(B, sp.share_group, gsize or sp.share_group)
+    T = sp.shared_prefix_pages * 16
+    say(cid, "B", B, "groups of", gsize or sp.share_group, "shared tokens", T, "max_group", max_group)
+    leader = torch.from_numpy(lead).to(d.q.device)
+    ws = torch.zeros(psv.taco_paged_tree_attn_splitk_workspace_size(d.q, d.k_cache, d.block_tables, T,
+                                                                     max_ctx_len=d.max_ctx_len),
+                     dtype=torch.uint8, device=d.q.device)
+    outs = []
+    for _ in range(2):                       # the workspace's counters are left zero for reuse
+        out = torch.full_like(d.q, float("nan"))
+        lse = torch.full((B, Hq, Qmax), float("nan"), dtype=torch.float32, device=d.q.device)
+        psv.taco_paged_tree_attn_shared_prefix(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
+                                               d.tree_mask, leader, max_group, T, d.scale, out=out, lse=lse,
+                                               k_scale=d.k_scale, v_scale=d.v_scale, workspace=ws,
+                                               max_ctx_len=d.max_ctx_len)
+        torch.cuda.synchronize()
+        outs.append((out_to_f64(out), lse.cpu().numpy().astype(np.float64)))
+    ref, ref_lse = run_oracle(w)
+    err = assert_parity(w, outs[0][0], outs[0][1], ref, ref_lse)
+    assert np.array_equal(outs[0][0], outs[1][0], equal_nan=True), "repeat call differs"
+    assert int(ws[:B * 8 * 4].view(torch.int32).abs().sum()) == 0, "arrival counters not left zero"
+    say(cid, "max abs err", err)
+
+
+def test_shared_prefix_entry_rejects_too_many_rows(torch_cuda):
+    import paged_speculative_verify_amd as psv
+    torch = torch_cuda
+    w = make(spec("se", 8, 32, 8, 128, "bf16", "bf16", (300, 600), 1, "chain", seed=187,
+                  share_group=8, shared_prefix_pages=8))
+    d = to_device(w)
+    leader = torch.zeros(8, dtype=torch.int32, device=d.q.device)
+    with pytest.raises(psv.PtaError):        # 9 sequences x 4 rows exceed one 32-row unit
+        psv.taco_paged_tree_attn_shared_prefix(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
+                                               d.tree_mask, leader, 9, 128, d.scale, max_ctx_len=d.max_ctx_len)
 
 
 def test_splitk_workspace_reused_across_calls(torch_cuda):
