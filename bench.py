@@ -39,14 +39,18 @@ SETTLE_S = 0.3                 # untimed steps after the warm-up, before any mea
 # launch configuration of each workload: entry point ("whole": one pass per
 # sequence, "split": split-K partitions of `split` tokens, "balanced": equal
 # page slices per wave of a persistent grid) and kernel family (auto picks by
-# rows per KV head)
+# rows per KV head); fuse_append: the step's KV append runs inside the
+# attention launch (taco_paged_tree_attn_append) instead of as taco_kv_append
+# before it.  Fused where that measured faster; on the fp8 chain workload (1024
+# workgroups, each encoding 8 candidates) the in-kernel append costs what the
+# separate launch does.
 LAUNCH = {
     "tiny_decode": dict(mode="whole", split=None, path="auto"),
-    "llama3_8b_decode": dict(mode="whole", split=None, path="auto"),
+    "llama3_8b_decode": dict(mode="whole", split=None, path="auto", fuse_append=True),
     "llama31_70b_verify": dict(mode="balanced", split=None, path="auto"),
     "long_splitk_verify": dict(mode="balanced", split=None, path="auto"),
     "fp8_kv_chain": dict(mode="whole", split=None, path="auto"),
-    "shared_prefix_decode": dict(mode="whole", split=None, path="auto"),
+    "shared_prefix_decode": dict(mode="whole", split=None, path="auto", fuse_append=True),
 }
 
 
@@ -139,6 +143,16 @@ class DeviceSet:
                 self.k_new = self.k_new.view(torch.bfloat16)
                 self.v_new = self.v_new.view(torch.bfloat16)
         self.slots = torch.from_numpy(slots).cuda()
+        # the same rows laid out [B, Qmax, Hkv, D] for the append fused into the attention launch
+        full = torch.zeros((B, Qmax, Hkv, D), dtype=self.k_new.dtype, device=self.k_new.device)
+        fullv = torch.zeros_like(full)
+        n = 0
+        for b in range(B):
+            qb = int(w.q_lens[b])
+            full[b, :qb] = self.k_new[n:n + qb]
+            fullv[b, :qb] = self.v_new[n:n + qb]
+            n += qb
+        self.k_new_full, self.v_new_full = full, fullv
         self.out = torch.empty_like(self.d.q)
         # shared-prefix groups: the first sequence of each run of share_group sequences leads it
         G = max(1, s.share_group) if s.shared_prefix_pages > 0 else 1
@@ -234,6 +248,9 @@ def main(argv=None) -> int:
                          "sequence, -1 = balanced page slices")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="launch the KV append (taco_kv_append) apart from attention even where the "
+                         "workload fuses it into the attention call")
     ap.add_argument("--shared-entry", action="store_true",
                     help="shared-prefix workload only: run taco_paged_tree_attn_shared_prefix (each "
                          "group's prefix partition worked once) instead of the whole-context grid")
@@ -284,6 +301,8 @@ def main(argv=None) -> int:
             print("--shared-entry needs a shared-prefix workload on shared pages", file=sys.stderr)
             return 2
         cfg["mode"], cfg["split"] = "shared", CONFIGS[name].shared_prefix_pages * 16
+    if cfg["mode"] != "whole" or args.path not in (None, "auto") or args.separate_append:
+        cfg.pop("fuse_append", None)      # the fused append lives in the whole-context stream kernel
     print(f"[bench] generating {args.sets} input set(s) for {name}", file=sys.stderr, flush=True)
     sets = []
     for r in range(args.sets):
@@ -307,13 +326,18 @@ def main(argv=None) -> int:
     # validated once, then re-issued with no per-call Python checks so the host stays ahead
     for ds in sets:
         d = ds.d
-        ds.append_call = psv.prepare_kv_append(ds.k_new, ds.v_new, ds.slots, d.k_cache, d.v_cache,
-                                               k_scale=d.k_scale, v_scale=d.v_scale)
+        if cfg.get("fuse_append"):
+            # the append runs inside the attention launch: the step is one call
+            ds.append_call = lambda: None
+        else:
+            ds.append_call = psv.prepare_kv_append(ds.k_new, ds.v_new, ds.slots, d.k_cache, d.v_cache,
+                                                   k_scale=d.k_scale, v_scale=d.v_scale)
         ds.attn_call = psv.prepare_paged_tree_attn(
-            cfg["mode"], d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens, d.tree_mask,
+            "whole_append" if cfg.get("fuse_append") else cfg["mode"],
+            d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens, d.tree_mask,
             d.scale, ds.out, lse=ds.lse, k_scale=d.k_scale, v_scale=d.v_scale,
             partition_tokens=cfg["split"], workspace=ds.workspace, max_ctx_len=d.max_ctx_len,
-            prefix_leader=ds.prefix_leader, max_group=ds.max_group,
+            prefix_leader=ds.prefix_leader, max_group=ds.max_group, k_new=ds.k_new_full, v_new=ds.v_new_full,
             path=cfg["path"])
     for i in range(args.warmup):
         ds = sets[i % len(sets)]
@@ -351,7 +375,8 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / K
     attn_avg_ms = bracketed(lambda ds: ds.attn_call())
-    append_avg_ms = bracketed(lambda ds: ds.append_call())
+    # a fused append has no launch of its own: its time is inside attention_ms
+    append_avg_ms = None if cfg.get("fuse_append") else bracketed(lambda ds: ds.append_call())
     # 2. the timed steps: nothing but the step's own launches between the two synchronisations
     #    (timing events inside the loop would add their own packets to every step)
     torch.cuda.synchronize()
@@ -398,6 +423,7 @@ def main(argv=None) -> int:
                    "batch": sets[0].w.q.shape[0], "q_heads": sets[0].w.q.shape[2],
                    "kv_heads": sets[0].w.k_cache.shape[1], "head_dim": sets[0].w.q.shape[3],
                    "max_q_len": sets[0].w.q.shape[1], "page": 16, "entry": cfg["mode"],
+                   "kv_append": "fused into the attention call" if cfg.get("fuse_append") else "taco_kv_append",
                    "split_tokens": cfg["split"],
                    "path": cfg["path"], "input_sets_rotated": len(sets)},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -407,7 +433,7 @@ def main(argv=None) -> int:
            if unique_per_launch != kv_per_launch else {}),
         "candidates_per_s": round(cand_per_s, 1),
         "attention_ms": round(attn_avg_s * 1e3, 5),
-        "kv_append_ms": round(append_avg_ms, 5),
+        "kv_append_ms": None if append_avg_ms is None else round(append_avg_ms, 5),
         "host_enqueue_ms_per_step": round(t_enqueue / K * 1e3, 5),
         "clock_settle": {"untimed_steps": n_settle, "ms": round(settle_ms, 1)},
         "attention_tflops": round(tflops, 3),
@@ -416,7 +442,8 @@ def main(argv=None) -> int:
                      "traffic": traffic,
                      "kernel": {"balanced": "paged tree attention grid + slice merge launch (balanced entry)",
                                 "split": "paged tree attention kernel (split-K entry, partition merge fused)",
-                                "whole": "paged tree attention kernel (whole-context entry)",
+                                "whole": "paged tree attention kernel (whole-context entry"
+                                         + (", KV append fused)" if cfg.get("fuse_append") else ")"),
                                 "shared": "paged tree attention kernel (shared-prefix entry: each group's "
                                           "prefix partition once, partition merge fused)"}[cfg["mode"]],
                      "algorithmic_bytes_per_launch": int(unique_per_launch),

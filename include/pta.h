@@ -113,6 +113,29 @@ pta_status taco_paged_tree_attn(const pta_dims* dims, const void* q, const void*
                                 const int32_t* q_lens, const uint8_t* tree_mask, float scale,
                                 void* out, float* lse, void* stream);
 
+/* The verify step's KV append fused into the whole-context attention call:
+ * every sequence's q_lens[b] new K and V rows (the candidates, logical
+ * positions L .. C - 1 with L = ctx_lens[b] - q_lens[b]) are written into their
+ * paged slots of k_cache / v_cache, then attention runs as in
+ * taco_paged_tree_attn over the updated cache, in one launch (the candidates'
+ * K/V are appended before they are attended to, design talk "4. 支持 Paged
+ * Attention": blocks are filled as tokens arrive).
+ *   k_new, v_new  [num_seqs][max_q_len][num_kv_heads][head_dim], 16-byte
+ *                 aligned (else PTA_ERR_BAD_DIMS), rows past q_lens ignored; new_dtype = PTA_BF16 for bf16 caches,
+ *                 PTA_F32 or PTA_BF16 for fp8 caches, whose slots get
+ *                 RNE-saturated e4m3fn codes of x / scale with the slot's
+ *                 existing (block, KV head) scale (as taco_kv_append).
+ * Served where the whole-context matrix-core stream kernel runs (bf16 q,
+ * num_q_heads / num_kv_heads * max_q_len <= 32, no forced VALU or tile path),
+ * else PTA_ERR_UNSUPPORTED (use taco_kv_append, then taco_paged_tree_attn).
+ * Other arguments and errors as taco_paged_tree_attn. */
+pta_status taco_paged_tree_attn_append(const pta_dims* dims, const void* q, const void* k_new,
+                                       const void* v_new, int32_t new_dtype, void* k_cache, void* v_cache,
+                                       const float* k_scale, const float* v_scale,
+                                       const int32_t* block_tables, const int32_t* ctx_lens,
+                                       const int32_t* q_lens, const uint8_t* tree_mask, float scale,
+                                       void* out, float* lse, void* stream);
+
 /* Bytes of device workspace taken by taco_paged_tree_attn_splitk for these dims
  * and partition length (0 on invalid input). */
 size_t taco_paged_tree_attn_splitk_workspace_size(const pta_dims* dims, int32_t partition_tokens);

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     taco_paged_tree_attn_balanced,
     taco_paged_tree_attn_balanced_workspace_size,
     taco_paged_tree_attn,
+    taco_paged_tree_attn_append,
     taco_paged_tree_attn_shared_prefix,
     taco_paged_tree_attn_splitk,
     taco_paged_tree_attn_splitk_workspace_size,

@@ -72,6 +72,8 @@ def load() -> ctypes.CDLL:
     lib.taco_paged_tree_attn_splitk_workspace_size.restype = SZ
     lib.taco_paged_tree_attn_splitk.argtypes = [D, P, P, P, P, P, P, P, P, P, F, P, P, I32, P, SZ, P]
     lib.taco_paged_tree_attn_splitk.restype = ctypes.c_int
+    lib.taco_paged_tree_attn_append.argtypes = [D, P, P, P, I32, P, P, P, P, P, P, P, P, F, P, P, P]
+    lib.taco_paged_tree_attn_append.restype = ctypes.c_int
     lib.taco_paged_tree_attn_shared_prefix.argtypes = [D, P, P, P, P, P, P, P, P, P, P, I32, I32, F, P, P, P,
                                                        SZ, P]
     lib.taco_paged_tree_attn_shared_prefix.restype = ctypes.c_int
@@ -258,6 +260,30 @@ def taco_paged_tree_attn_splitk(q, k_cache, v_cache, block_tables, ctx_lens, q_l
         _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask), float(scale), _ptr(out),
         _ptr(lse), int(partition_tokens), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+    return out
+
+
+def taco_paged_tree_attn_append(q, k_new, v_new, k_cache, v_cache, block_tables, ctx_lens, q_lens,
+                                tree_mask, scale, out=None, lse=None, k_scale=None, v_scale=None,
+                                max_ctx_len=None, path="auto", stream=None):
+    """KV append fused into the whole-context attention call (see include/pta.h).
+
+    k_new, v_new: [B, Qmax, Hkv, D] device tensors, the candidates' K/V rows, written into their
+    paged slots (positions ctx_lens - q_lens .. ctx_lens - 1) before attention reads the cache.
+    """
+    lib = load()
+    _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale)
+    B, Qmax, Hq, D = q.shape
+    _need(k_new, "k_new", 4, device=q.device)
+    _need(v_new, "v_new", 4, k_new.dtype, q.device)
+    if tuple(k_new.shape) != (B, Qmax, k_cache.shape[1], D) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k_new / v_new must be [B, Qmax, Hkv, D]")
+    out, lse = _alloc_out(q, out, lse)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    _check(lib.taco_paged_tree_attn_append(
+        ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new), _q_code(k_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask),
+        float(scale), _ptr(out), _ptr(lse), _stream(stream)))
     return out
 
 
@@ -449,10 +475,11 @@ class PreparedCall:
 def prepare_paged_tree_attn(mode, q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask,
                             scale, out, lse=None, k_scale=None, v_scale=None, partition_tokens=None,
                             workspace=None, max_ctx_len=None, path="auto", stream=None, prefix_leader=None,
-                            max_group=None) -> PreparedCall:
+                            max_group=None, k_new=None, v_new=None) -> PreparedCall:
     """Validate once and return a PreparedCall for one of the attention entry points.
 
-    mode: "whole" (taco_paged_tree_attn), "split" (taco_paged_tree_attn_splitk with
+    mode: "whole" (taco_paged_tree_attn), "whole_append" (taco_paged_tree_attn_append with k_new,
+    v_new), "split" (taco_paged_tree_attn_splitk with
     partition_tokens), "shared" (taco_paged_tree_attn_shared_prefix with partition_tokens =
     shared tokens, prefix_leader and max_group) or "balanced" (taco_paged_tree_attn_balanced).  out (and, for
     split/balanced, a zero-initialised workspace of sufficient size) must be given.
@@ -470,6 +497,13 @@ def prepare_paged_tree_attn(mode, q, k_cache, v_cache, block_tables, ctx_lens, q
     st = _stream(stream)
     if mode == "whole":
         return PreparedCall(lib.taco_paged_tree_attn, common + (st,), keep)
+    if mode == "whole_append":
+        _need(k_new, "k_new", 4, device=q.device)
+        _need(v_new, "v_new", 4, k_new.dtype, q.device)
+        args = (ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new), _q_code(k_new), _ptr(k_cache),
+                _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens),
+                _ptr(tree_mask), float(scale), _ptr(out), _ptr(lse), st)
+        return PreparedCall(lib.taco_paged_tree_attn_append, args, keep + (k_new, v_new))
     if workspace is None:
         raise ValueError("prepared split/balanced calls need a caller-owned workspace")
     _need(workspace, "workspace", device=q.device)

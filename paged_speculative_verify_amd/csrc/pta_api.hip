@@ -239,6 +239,41 @@ pta_status taco_paged_tree_attn(const pta_dims* d, const void* q, const void* k_
   return run_attn(d, a, p, (hipStream_t)stream);
 }
 
+pta_status taco_paged_tree_attn_append(const pta_dims* d, const void* q, const void* k_new,
+                                       const void* v_new, int32_t new_dtype, void* k_cache, void* v_cache,
+                                       const float* k_scale, const float* v_scale,
+                                       const int32_t* block_tables, const int32_t* ctx_lens,
+                                       const int32_t* q_lens, const uint8_t* tree_mask, float scale,
+                                       void* out, float* lse, void* stream) {
+  pta_status st = check_dims(d);
+  if (st != PTA_OK) return st;
+  if (!isfinite(scale)) return PTA_ERR_BAD_DIMS;
+  if (d->kv_dtype == PTA_FP8_E4M3FN) {
+    if (new_dtype != PTA_F32 && new_dtype != PTA_BF16) return PTA_ERR_BAD_DTYPE;
+  } else if (new_dtype != d->kv_dtype) {
+    return PTA_ERR_BAD_DTYPE;
+  }
+  Plan p;
+  st = plan_for(d, &p);
+  if (st != PTA_OK) return st;
+  if (p.fam != FAM_STREAM) return PTA_ERR_UNSUPPORTED;   // fused into the stream kernel only
+  if (d->num_seqs == 0) return PTA_OK;
+  st = check_attn_ptrs(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
+                       tree_mask, out);
+  if (st != PTA_OK) return st;
+  if (!k_new || !v_new) return PTA_ERR_NULL_PTR;
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) % 16 != 0)
+    return PTA_ERR_BAD_DIMS;                              // rows are moved in 16-byte chunks
+  AttnArgs a = make_args(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
+                         tree_mask, scale, out, lse);
+  a.part_tokens = 0;
+  a.num_parts = 1;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_f32 = new_dtype == PTA_F32;
+  return run_attn(d, a, p, (hipStream_t)stream);
+}
+
 size_t taco_paged_tree_attn_splitk_workspace_size(const pta_dims* d, int32_t partition_tokens) {
   if (check_dims(d) != PTA_OK) return 0;
   SplitLayout L;

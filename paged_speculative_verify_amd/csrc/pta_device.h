@@ -47,6 +47,13 @@ struct AttnArgs {
   // sequences sharing partition 0 (null otherwise), and the largest group size
   const int32_t* prefix_leader;
   int32_t max_group;
+  // fused KV append (whole-context stream grid): the candidates' new K/V rows
+  // [B][Qmax][Hkv][D] (cache dtype, or bf16/f32 when new_f32 says so for fp8
+  // caches), written into their paged slots before the unit reads its pages;
+  // null otherwise
+  const void* k_new;
+  const void* v_new;
+  int32_t new_f32;
   int64_t num_blocks;
 };
 

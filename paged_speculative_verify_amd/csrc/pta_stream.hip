@@ -211,6 +211,69 @@ __device__ __forceinline__ void load_group_rows(StreamRows<D, RB>& R, int (&bj)[
   }
 }
 
+// The KV append of the verify step fused into the attention launch: the
+// unit's q_b new K and V rows (candidates at logical positions L .. C - 1,
+// KV head hkv) go to their paged slots, fp8 caches storing RNE-saturated codes
+// of x / scale with the slot's (page, KV head) scale, and the workgroup waits
+// for the stores before any page is read.  Only this workgroup reads this
+// unit's (page, KV head) tiles in the launch, so nothing else can see a half
+// written row.  Each thread moves whole 8-element chunks (q_b <= ROWS, so at
+// most MAXC of them) and issues every load before its first store, so the
+// append costs about one load and one store round trip.
+template <typename KT, int D, int ROWS, int NT>
+__device__ __forceinline__ void append_unit_rows(const AttnArgs& a, int b, int hkv, int L, int qb, int tid) {
+  constexpr int CPR = D / 8;                                  // chunks per row
+  constexpr int MAXC = (2 * ROWS * CPR + NT - 1) / NT;
+  typedef uint32_t Chunk __attribute__((ext_vector_type(KT::bytes * 2)));   // 8 cache elements
+  const int32_t* table = a.tables + (int64_t)b * a.MBS;
+  const int n = 2 * qb * CPR;
+  Chunk val[MAXC];
+  int64_t dst[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int e = tid + i * NT;
+    if (e >= n) continue;
+    const int which = e / (qb * CPR), r = (e / CPR) % qb, c = e % CPR;
+    const int t = L + r;
+    const int64_t page = table[t / kPage];
+    dst[i] = ((((page * a.Hkv + hkv) * kPage + t % kPage) * D + c * 8) << 1) | which;
+    const int64_t src = (((int64_t)b * a.Qmax + r) * a.Hkv + hkv) * D + c * 8;
+    const void* in = which ? a.v_new : a.k_new;
+    if constexpr (KT::bytes == 2) {
+      val[i] = *reinterpret_cast<const Chunk*>(reinterpret_cast<const uint16_t*>(in) + src);
+    } else {
+      float x[8];
+      if (a.new_f32) {
+        const float4 lo = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(in) + src);
+        const float4 hi = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(in) + src + 4);
+        x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w;
+        x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
+      } else {
+        const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(in) + src);
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[2 * k] = __uint_as_float(u[k] << 16);
+          x[2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
+        }
+      }
+      const float scl = (which ? a.v_scale : a.k_scale)[page * a.Hkv + hkv];
+      uint32_t code[2] = {0u, 0u};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) code[k >> 2] |= f32_to_e4m3fn_sat(__fdiv_rn(x[k], scl)) << (8 * (k & 3));
+      val[i] = Chunk{code[0], code[1]};
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    if (tid + i * NT >= n) continue;
+    void* cache = const_cast<void*>((dst[i] & 1) ? a.v : a.k);
+    *reinterpret_cast<Chunk*>(reinterpret_cast<char*>(cache) + (dst[i] >> 1) * KT::bytes) = val[i];
+  }
+  __builtin_amdgcn_s_waitcnt(0);    // this thread's stores have completed
+  __syncthreads();
+}
+
 template <typename KT, int D, int RB, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void stream_attn_kernel(AttnArgs a) {
   using T = StreamTile<KT, D>;
@@ -272,6 +335,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   } else {
     load_rows(rows, a, b, hkv, qb, M, g, m);
   }
+  // the append's round trips overlap the row loads above
+  if (a.k_new != nullptr && a.part_tokens == 0) append_unit_rows<KT, D, ROWS, NW * 64>(a, b, hkv, L, qb, threadIdx.x);
   StreamState<D, RB> st;
   st.init();
 

@@ -288,6 +288,85 @@ def test_kv_append_parity(torch_cuda):
         assert np.array_equal(gv.view(np.uint8), ref_v.view(np.uint8))
 
 
+# taco_paged_tree_attn_append: the candidates' K/V rows written by the attention launch itself.
+FUSED_CASES = [
+    ("decode_bf16", spec("fa", 6, 32, 8, 128, "bf16", "bf16", (1, 700), 1, "chain", seed=191), "bf16"),
+    ("tree4_bf16", spec("fa", 5, 16, 4, 128, "bf16", "bf16", (4, 500), 4, "random", seed=192), "bf16"),
+    ("ragged_tree8_d64", spec("fa", 5, 16, 4, 64, "bf16", "bf16", (8, 300), 8, "random", ragged=True,
+                              seed=193), "bf16"),
+    ("fp8_chain8_f32_rows", spec("fa", 6, 32, 8, 128, "bf16", "fp8", (8, 900), 8, "chain", seed=194), "f32"),
+    ("fp8_decode_bf16_rows", spec("fa", 6, 32, 8, 128, "bf16", "fp8", (1, 900), 1, "chain", seed=195), "bf16"),
+    # candidates straddling a 32-token page pair: two waves each write and read their own part
+    ("cross_pairs_q8", spec("fa", 24, 16, 4, 128, "bf16", "bf16", (8, 200), 8, "random", seed=197), "bf16"),
+    ("fp8_cross_pairs_q8", spec("fa", 24, 16, 4, 128, "bf16", "fp8", (8, 200), 8, "chain", seed=198), "f32"),
+]
+
+
+@pytest.mark.parametrize("cid,sp,new_dt", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_append_parity(torch_cuda, cid, sp, new_dt):
+    import torch
+    import paged_speculative_verify_amd as psv
+    from workload.gen import f32_to_bf16_bits
+    w = make(sp, poison=True)
+    B, Qmax, Hq, D = w.q.shape
+    Hkv = w.k_cache.shape[1]
+    kv = sp.kv_dtype
+    if "cross_pairs" in cid:
+        first, last = w.ctx_lens - w.q_lens, w.ctx_lens - 1
+        assert (first // 32 != last // 32).any()
+    rng = np.random.default_rng(sp.seed + 1)
+    # new keys twice the spread of the cache's, so the candidates carry weight; new values as the
+    # cache's, so outputs stay in the range the bf16 tolerance is set for
+    xk = (rng.standard_normal((B, Qmax, Hkv, D)) * 2).astype(np.float32)
+    xv = rng.standard_normal((B, Qmax, Hkv, D)).astype(np.float32)
+    enc = (lambda x: x) if new_dt == "f32" else f32_to_bf16_bits
+    pos = [(b, j) for b in range(B) for j in range(int(w.q_lens[b]))]
+    slots = np.array([int(w.block_tables[b, (int(w.ctx_lens[b]) - int(w.q_lens[b]) + j) // 16]) * 16
+                      + (int(w.ctx_lens[b]) - int(w.q_lens[b]) + j) % 16 for b, j in pos], np.int64)
+    rows_k = enc(np.stack([xk[b, j] for b, j in pos]))
+    rows_v = enc(np.stack([xv[b, j] for b, j in pos]))
+    ref_k, ref_v = oracle.kv_append(w.k_cache, w.v_cache, rows_k, rows_v, slots, cache_dtype=kv,
+                                    new_dtype=new_dt, k_scale=w.k_scale, v_scale=w.v_scale)
+    ref, ref_lse = oracle.paged_tree_attn(w.q, ref_k, ref_v, w.block_tables, w.ctx_lens, w.q_lens, w.tree_mask,
+                                          w.scale, q_dtype=sp.q_dtype, kv_dtype=kv, k_scale=w.k_scale,
+                                          v_scale=w.v_scale)
+    # the case can see a stale read: attention over the old rows misses every sequence's result
+    stale, _ = oracle.paged_tree_attn(w.q, w.k_cache, w.v_cache, w.block_tables, w.ctx_lens, w.q_lens,
+                                      w.tree_mask, w.scale, q_dtype=sp.q_dtype, kv_dtype=kv, k_scale=w.k_scale,
+                                      v_scale=w.v_scale)
+    assert all(np.nanmax(np.abs(ref[b] - stale[b])) > TOL[tol_key(sp)] for b in range(B))
+    say(cid, "B", B, "q", sp.q_len, "kv", kv, "new rows", new_dt)
+    d = to_device(w)                                  # the candidates' slots still hold the old rows
+    kn = torch.from_numpy(np.ascontiguousarray(enc(xk))).cuda()
+    vn = torch.from_numpy(np.ascontiguousarray(enc(xv))).cuda()
+    if new_dt == "bf16":
+        kn, vn = kn.view(torch.bfloat16), vn.view(torch.bfloat16)
+    out = torch.full_like(d.q, float("nan"))
+    lse = torch.full((B, Hq, Qmax), float("nan"), dtype=torch.float32, device=d.q.device)
+    psv.taco_paged_tree_attn_append(d.q, kn, vn, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
+                                    d.tree_mask, d.scale, out=out, lse=lse, k_scale=d.k_scale, v_scale=d.v_scale,
+                                    max_ctx_len=d.max_ctx_len)
+    torch.cuda.synchronize()
+    gk = d.k_cache.view(torch.uint8).cpu().numpy()
+    gv = d.v_cache.view(torch.uint8).cpu().numpy()
+    assert np.array_equal(gk.reshape(-1), ref_k.view(np.uint8).reshape(-1)), "K cache after the call"
+    assert np.array_equal(gv.reshape(-1), ref_v.view(np.uint8).reshape(-1)), "V cache after the call"
+    err = assert_parity(w, out_to_f64(out), lse.cpu().numpy().astype(np.float64), ref, ref_lse)
+    say(cid, "max abs err", err)
+
+
+def test_fused_append_unsupported_path(torch_cuda):
+    import torch
+    import paged_speculative_verify_amd as psv
+    w = make(spec("fa", 3, 64, 8, 128, "bf16", "bf16", (20, 200), 16, "random", seed=196))   # 128 rows: tile path
+    d = to_device(w)
+    B, Qmax, Hq, D = w.q.shape
+    kn = torch.zeros((B, Qmax, 8, D), dtype=torch.bfloat16, device=d.q.device)
+    with pytest.raises(psv.PtaError):
+        psv.taco_paged_tree_attn_append(d.q, kn, kn, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
+                                        d.tree_mask, d.scale, max_ctx_len=d.max_ctx_len)
+
+
 def test_validate_flags(torch_cuda):
     import torch
     import paged_speculative_verify_amd as psv
