@@ -172,7 +172,7 @@ __device__ __forceinline__ int tile_off(int r, int u) {
 // v_mfma_f32_16x16x32_bf16 (full rate on gfx950, where the 16-token
 // instruction runs at half rate).  The k index of that step runs over tokens
 // {4 g + e, 16 + 4 g + e} for lane group g: the B operand is the lane's two
-// S^T accumulators (P as a bf16 hi/lo pair) and the A operand is two
+// S^T accumulators (P in bf16, alone or as a hi/lo pair) and the A operand is two
 // ds_read_b64_tr_b16 reads, one from each V tile.  A missing second page must
 // be presented with its V tile zeroed and its tokens at or past t1 (masked).
 template <int RB>
@@ -211,8 +211,12 @@ __device__ __forceinline__ void pair_scores(const StreamRows<D, RB>& rows, PairS
 // is only needed for pairs that reach the candidates or the end of the range;
 // pair_max_prep takes lane maxima (straight-line, to share issue slots with
 // matrix-core work); pair_max_finish moves m and l at once when needed and
-// returns O's factor for later; pair_p forms P as a bf16 hi/lo pair; and
-// pair_pv_mma adds the P.V products.
+// returns O's factor for later; pair_p forms P in bf16; and pair_pv_mma adds
+// the P.V products.  The pipelined wide-tree kernels take P as one bf16 value
+// per element (the usual precision of bf16 flash kernels): the row sum l stays
+// in fp32, and the rounding moves an output by at most 2^-8 of the largest
+// |V| of the row's context, by far less for spread attention; dropping the low
+// half saves a third of their matrix-core work.
 template <int D, int RB>
 __device__ __forceinline__ void pair_mask(const StreamRows<D, RB>& rows, PairScores<RB>& S, int pbase, int L,
                                           int t1, int lane) {
@@ -271,22 +275,20 @@ __device__ __forceinline__ bool pair_max_finish(StreamState<D, RB>& st, const fl
 }
 
 template <int D, int RB>
-__device__ __forceinline__ void pair_p(StreamState<D, RB>& st, const float (&x)[RB][8], bf16x8 (&phi)[RB],
-                                       bf16x8 (&plo)[RB], float c) {
+__device__ __forceinline__ void pair_p(StreamState<D, RB>& st, const float (&x)[RB][8], bf16x8 (&p)[RB],
+                                       float c) {
   constexpr float NEG_INF = -__builtin_huge_valf();
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float nm = st.m[rb] == NEG_INF ? 0.f : -st.m[rb];
-    uint32_t h[4], lo[4];
+    uint32_t h[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float p0 = fast_exp2(fmaf(x[rb][2 * k], c, nm)), p1 = fast_exp2(fmaf(x[rb][2 * k + 1], c, nm));
       st.l[rb] += p0 + p1;
       h[k] = pack_bf16x2(p0, p1);
-      lo[k] = pack_bf16x2(p0 - bf16_lo(h[k]), p1 - bf16_hi(h[k]));
     }
-    phi[rb] = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
-    plo[rb] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+    p[rb] = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
   }
 }
 

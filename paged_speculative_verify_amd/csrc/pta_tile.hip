@@ -363,10 +363,10 @@ __device__ __forceinline__ void dma_range(const AttnArgs& a, char* lds, uint32_t
     // 1. S of pair s + 1 with P of pair s
     PairScores<RB> sn;
     pair_scores<D, RB, true>(rows, sn, sb, sb + Gm::TILE, lane);
-    bf16x8 phi[RB], plo[RB];
-    pair_p<D, RB>(st, x, phi, plo, c);
+    bf16x8 p[RB];
+    pair_p<D, RB>(st, x, p, c);
     // 2. P.V of pair s with the masked scores of pair s + 1
-    pair_pv_mma<D, RB, true>(st, phi, plo, sb + 2 * Gm::TILE, sb + 3 * Gm::TILE, lane);
+    pair_pv_mma<D, RB, true, false>(st, p, p, sb + 2 * Gm::TILE, sb + 3 * Gm::TILE, lane);
     if (pbase(s + 1) + 2 * kPage > plain_end) pair_mask<D, RB>(rows, sn, pbase(s + 1), L, t1, lane);
     bool need;
     pair_max_prep<D, RB>(st, sn, xn, need, c);
