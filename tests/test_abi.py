@@ -136,3 +136,35 @@ def test_accept_commit_host_checks(lib):
     assert f(dims(max_q_len=4), mask=None) == NULLP
     assert f(dims(kv_dtype=2)) == NULLP                 # fp8 cache without scales
     assert f(dims(head_dim=96)) == DIMS
+
+
+def test_attn_append_host_checks(lib):
+    """taco_paged_tree_attn_append: row dtype, kernel family, pointers and alignment are checked
+    on the host."""
+    def f(dd, new_dt=1, k=FAKE, v=FAKE, ks=None, vs=None, scale=0.1):
+        return lib.taco_paged_tree_attn_append(ctypes.byref(dd), FAKE, k, v, new_dt, FAKE, FAKE, ks, vs, FAKE,
+                                               FAKE, FAKE, FAKE, scale, FAKE, None, None)
+    assert f(dims(), new_dt=0) == DTYPE                              # f32 rows into a bf16 cache
+    assert f(dims(kv_dtype=2), new_dt=2, ks=FAKE, vs=FAKE) == DTYPE  # fp8 rows: f32 or bf16 only
+    assert f(dims(max_q_len=16, num_q_heads=64)) == UNSUP            # 128 rows: not the stream kernel
+    assert f(dims(path=1)) == UNSUP                                  # forced VALU path
+    assert f(dims(num_seqs=0)) == OK
+    assert f(dims(), k=None) == NULLP
+    assert f(dims(kv_dtype=2), new_dt=0) == NULLP                    # fp8 cache without scales
+    assert f(dims(), v=ctypes.c_void_p(0x10008)) == DIMS             # rows move in 16-byte chunks
+    assert f(dims(), scale=float("inf")) == DIMS
+
+
+def test_shared_prefix_host_checks(lib):
+    def f(dd, leader=FAKE, group=8, shared=2048, ws=FAKE, nbytes=1 << 30):
+        return lib.taco_paged_tree_attn_shared_prefix(ctypes.byref(dd), FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
+                                                      FAKE, FAKE, leader, group, shared, 0.1, FAKE, None, ws,
+                                                      nbytes, None)
+    assert f(dims(), group=0) == DIMS
+    assert f(dims(), shared=100) == DIMS                             # not a multiple of 32 tokens
+    assert f(dims(), group=9) == UNSUP                               # 9 members x 4 rows > 32
+    assert f(dims(num_seqs=0)) == OK
+    assert f(dims(), leader=None) == NULLP
+    assert f(dims(), ws=None) == NULLP
+    assert f(dims(), ws=ctypes.c_void_p(0x10010)) == DIMS            # workspace 256-byte aligned
+    assert f(dims(), nbytes=16) == WS
