@@ -189,6 +189,84 @@ def run_attention(psv, ds, cfg):
 
 
 # ------------------------------------------------------------------ CPU baseline (oracle)
+def accepted_walk(tok, par, cnt, truth):
+    """Greedy acceptance against the stream's true next tokens: the deepest candidate whose path
+    spells truth[0..d-1]; returns d."""
+    best, depth = 0, {}
+    for i in range(cnt):
+        d = 1 if par[i] < 0 else (depth.get(par[i], -1) + 1 if depth.get(par[i], -1) > 0 else -1)
+        if d > 0 and d <= len(truth) and tok[i] == truth[d - 1]:
+            depth[i] = d
+            best = max(best, d)
+        else:
+            depth[i] = -1
+    return best
+
+
+def lookahead_cache_bench(args, B=64, prompt=1024, steps=200, window=16, max_match=8, max_len=8,
+                          batch_cap=256):
+    """Host lookahead cache over a decode batch: every step proposes each sequence's candidate
+    tree, scores it against the synthetic stream's true continuation (greedy acceptance), feeds
+    the hit back into the budgets and appends the accepted tokens plus one.  Timed: the library
+    calls only."""
+    import numpy as np
+    import paged_speculative_verify_amd as psv
+    from workload.tokens import synthetic_streams
+    streams = synthetic_streams(B, prompt + steps * (max_len + 1) + 16, vocab=1000, seed=7)
+    cache = psv.LookaheadCache(window, max_match)
+    seqs = list(range(B))
+    seq_arr = np.arange(B, dtype=np.int32)
+    pos = [prompt] * B
+    t_lib = 0.0
+    prompts = np.concatenate([np.asarray(streams[s][:prompt], np.int32) for s in seqs])
+    t0 = time.perf_counter()
+    cache.append_packed(seq_arr, np.full(B, prompt, np.int32), prompts)
+    t_ingest = time.perf_counter() - t0
+    budgets = np.full(B, max_len, np.int32)
+    made = cand = 0
+    for _ in range(steps):
+        t0 = time.perf_counter()
+        tok, par, cnt = cache.propose(seq_arr, budgets, max_len)
+        t_lib += time.perf_counter() - t0
+        acc = [accepted_walk(tok[i], par[i], int(cnt[i]), streams[i][pos[i]:pos[i] + max_len]) for i in seqs]
+        lens = np.array([a + 1 for a in acc], np.int32)          # accepted tokens plus the bonus token
+        packed = np.concatenate([np.asarray(streams[i][pos[i]:pos[i] + acc[i] + 1], np.int32) for i in seqs])
+        acc = np.asarray(acc, np.int32)
+        t0 = time.perf_counter()
+        budgets = cache.update_budgets(seq_arr, cnt, acc, 1, max_len, batch_cap)
+        cache.append_packed(seq_arr, lens, packed)
+        t_lib += time.perf_counter() - t0
+        for i in seqs:
+            pos[i] += acc[i] + 1
+        made += sum(acc) + B
+        cand += int(np.sum(cnt))
+    # the oracle on a bounded sample: 2 sequences, 10 steps
+    import oracle
+    o = oracle.LookaheadOracle(window, max_match)
+    t0 = time.perf_counter()
+    for s in range(2):
+        o.append(s, streams[s][:prompt])
+    for _ in range(10):
+        for s in range(2):
+            o.propose(s, max_len)
+    t_or = time.perf_counter() - t0
+    rate = B * steps / t_lib
+    print(json.dumps({
+        "metric": "lookahead cache: candidate trees proposed per second (host, one thread)",
+        "value": round(rate, 1), "unit": "trees/s", "higher_is_better": True, "data": "synthetic",
+        "config": {"workload": "lookahead_cache_decode_batch", "batch": B, "prompt_tokens": prompt,
+                   "steps": steps, "window": window, "max_match": max_match, "max_len": max_len,
+                   "batch_cap": batch_cap},
+        "ms_per_batch_step": round(1e3 * t_lib / steps, 4),
+        "prompt_ingest_tokens_per_s": round(B * prompt / t_ingest, 1),
+        "tokens_per_step_mean": round(made / (B * steps), 3),
+        "candidates_per_step_mean": round(cand / (B * steps), 3),
+        "cpu_baseline": {"value": round(20 / t_or, 2), "unit": "trees/s", "cores": 1, "kind": "oracle",
+                         "sample": f"2 sequences, {prompt}-token prompts, 10 proposals each, in {t_or:.1f} s"},
+        "note": "tokens_per_step depends on the synthetic streams' repetition, not on real text"}))
+    return 0
+
+
 def cpu_baseline(w, gpu_out, budget_s=12.0):
     """Time the fp64 oracle on whole sequences of the same workload until the time budget is
     spent; report its KV GB/s and its max |difference| from the GPU output on that sample."""
@@ -257,10 +335,16 @@ def main(argv=None) -> int:
     ap.add_argument("--private-pages", action="store_true",
                     help="shared-prefix workload only: the same batch with every sequence on pages of "
                          "its own (the reference the shared pages are compared with)")
+    ap.add_argument("--lookahead-cache", action="store_true",
+                    help="instead of the bench line: the host lookahead cache (propose, budgets, append) "
+                         "over a decode batch of synthetic token streams, one JSON line; needs no GPU")
     ap.add_argument("--qlen-floor", action="store_true",
                     help="instead of the bench line: attention time against the number of candidates "
                          "per sequence at the decode shape, T(q_len) / T(1)")
     args = ap.parse_args(argv)
+
+    if args.lookahead_cache:
+        return lookahead_cache_bench(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

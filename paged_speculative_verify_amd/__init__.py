@@ -6,6 +6,7 @@ device memory and streams only.
 """
 from ._lib import (  # noqa: F401
     PATHS,
+    LookaheadCache,
     PreparedCall,
     prepare_kv_append,
     prepare_paged_tree_attn,
@@ -16,6 +17,7 @@ from ._lib import (  # noqa: F401
     make_dims,
     taco_accept_commit,
     taco_kv_append,
+    taco_la_tree_mask,
     taco_paged_tree_attn_balanced,
     taco_paged_tree_attn_balanced_workspace_size,
     taco_paged_tree_attn,

@@ -15,7 +15,8 @@ from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpta.so")
-HEADER = os.path.join(os.path.dirname(HERE), "include", "pta.h")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+HEADER = os.path.join(INCLUDE, "pta.h")
 
 PTA_F32, PTA_BF16, PTA_FP8_E4M3FN = 0, 1, 2
 PATHS = {"auto": 0, "valu": 1, "mfma": 2, "tile": 3}
@@ -51,10 +52,13 @@ _lib = None
 
 
 def declared_functions() -> list:
-    """Names of the functions include/pta.h declares."""
-    with open(HEADER, encoding="utf-8") as f:
-        text = f.read()
-    return sorted(set(re.findall(r"\b(taco_\w+)\s*\(", text)))
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            with open(os.path.join(INCLUDE, h), encoding="utf-8") as f:
+                names |= set(re.findall(r"\b(taco_\w+)\s*\(", f.read()))
+    return sorted(names)
 
 
 def load() -> ctypes.CDLL:
@@ -91,6 +95,22 @@ def load() -> ctypes.CDLL:
     lib.taco_pta_status_string.restype = ctypes.c_char_p
     lib.taco_pta_version.argtypes = []
     lib.taco_pta_version.restype = I32
+    lib.taco_la_create.argtypes = [I32, I32]
+    lib.taco_la_create.restype = P
+    lib.taco_la_destroy.argtypes = [P]
+    lib.taco_la_destroy.restype = None
+    lib.taco_la_append.argtypes = [P, I32, P, I32]
+    lib.taco_la_append.restype = ctypes.c_int
+    lib.taco_la_append_batch.argtypes = [P, I32, P, P, P]
+    lib.taco_la_append_batch.restype = ctypes.c_int
+    lib.taco_la_release.argtypes = [P, I32]
+    lib.taco_la_release.restype = ctypes.c_int
+    lib.taco_la_propose.argtypes = [P, I32, P, P, I32, P, P, P]
+    lib.taco_la_propose.restype = ctypes.c_int
+    lib.taco_la_update_budgets.argtypes = [P, I32, P, P, P, I32, I32, I32, P]
+    lib.taco_la_update_budgets.restype = ctypes.c_int
+    lib.taco_la_tree_mask.argtypes = [I32, I32, P, P, P]
+    lib.taco_la_tree_mask.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -551,3 +571,93 @@ def prepare_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None
             _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _stream(stream))
     return PreparedCall(lib.taco_kv_append, args,
                         (dims, k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale))
+
+
+# ---------------------------------------------------------------- lookahead cache (host)
+def _i32(a) -> "np.ndarray":
+    import numpy as np
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _np_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a.size else None
+
+
+class LookaheadCache:
+    """The lookahead cache of include/pta_lookahead.h (host memory, numpy int32 arrays)."""
+
+    def __init__(self, window: int = 16, max_match: int = 8):
+        self._lib = load()
+        self._h = self._lib.taco_la_create(int(window), int(max_match))
+        if not self._h:
+            raise PtaError(2, "taco_la_create: window 2..64 and max_match 1..window-1")
+        self.window, self.max_match = int(window), int(max_match)
+
+    def close(self):
+        if self._h:
+            self._lib.taco_la_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def append(self, seq: int, tokens) -> None:
+        t = _i32(tokens).reshape(-1)
+        _check(self._lib.taco_la_append(self._h, int(seq), _np_ptr(t), int(t.size)))
+
+    def append_batch(self, seqs, chunks) -> None:
+        """chunks[i] (a token sequence) appended to seqs[i], in one library call."""
+        import numpy as np
+        sq = _i32(seqs).reshape(-1)
+        lens = _i32([len(c) for c in chunks]).reshape(-1)
+        if sq.size != lens.size:
+            raise ValueError("seqs and chunks differ in length")
+        toks = _i32(np.concatenate([np.asarray(c, np.int32).reshape(-1) for c in chunks]) if len(chunks)
+                    else np.zeros(0, np.int32))
+        _check(self._lib.taco_la_append_batch(self._h, sq.size, _np_ptr(sq), _np_ptr(lens), _np_ptr(toks)))
+
+    def append_packed(self, seqs, lens, tokens) -> None:
+        """append_batch with the tokens already packed: int32 arrays seqs [n], lens [n] and
+        tokens [sum(lens)] (no per-call conversion beyond a dtype check)."""
+        sq, ln, tk = _i32(seqs).reshape(-1), _i32(lens).reshape(-1), _i32(tokens).reshape(-1)
+        if sq.size != ln.size or int(ln.sum()) != tk.size:
+            raise ValueError("lens must match seqs and sum to the token count")
+        _check(self._lib.taco_la_append_batch(self._h, sq.size, _np_ptr(sq), _np_ptr(ln), _np_ptr(tk)))
+
+    def release(self, seq: int) -> None:
+        _check(self._lib.taco_la_release(self._h, int(seq)))
+
+    def propose(self, seqs, budgets, max_q: int):
+        """(tokens [n, max_q], parents [n, max_q], counts [n]) as int32 arrays."""
+        import numpy as np
+        sq, bu = _i32(seqs).reshape(-1), _i32(budgets).reshape(-1)
+        if sq.size != bu.size:
+            raise ValueError("seqs and budgets differ in length")
+        n = sq.size
+        tok = np.empty((n, max_q), np.int32)
+        par = np.empty((n, max_q), np.int32)
+        cnt = np.empty(n, np.int32)
+        _check(self._lib.taco_la_propose(self._h, n, _np_ptr(sq), _np_ptr(bu), int(max_q), _np_ptr(tok),
+                                         _np_ptr(par), _np_ptr(cnt)))
+        return tok, par, cnt
+
+    def update_budgets(self, seqs, proposed, accepted, min_len: int, max_len: int, batch_cap: int = 0):
+        import numpy as np
+        sq, pr, ac = _i32(seqs).reshape(-1), _i32(proposed).reshape(-1), _i32(accepted).reshape(-1)
+        if not (sq.size == pr.size == ac.size):
+            raise ValueError("seqs, proposed and accepted differ in length")
+        out = np.empty(sq.size, np.int32)
+        _check(self._lib.taco_la_update_budgets(self._h, sq.size, _np_ptr(sq), _np_ptr(pr), _np_ptr(ac),
+                                                int(min_len), int(max_len), int(batch_cap), _np_ptr(out)))
+        return out
+
+
+def taco_la_tree_mask(parents, counts):
+    """Ancestor-or-self tree_mask [n, max_q, max_q] uint8 from parent arrays [n, max_q]."""
+    import numpy as np
+    par = _i32(parents)
+    cnt = _i32(counts).reshape(-1)
+    n, max_q = par.shape
+    mask = np.empty((n, max_q, max_q), np.uint8)
+    _check(load().taco_la_tree_mask(n, max_q, _np_ptr(par), _np_ptr(cnt), _np_ptr(mask)))
+    return mask

@@ -20,6 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpta.so")
 SOURCES = ["pta_api.hip", "pta_valu.hip", "pta_stream.hip", "pta_tile.hip", "pta_aux.hip", "pta_accept.hip"]
 HEADERS = ["pta_device.h", "pta_flash.h", "pta_launch.h"]
+HOST_SOURCES = ["pta_lookahead.cpp"]      # host-only C++ (the lookahead cache), built with the host compiler
 
 ARCH = "gfx950"
 FLAGS = [
@@ -48,10 +49,27 @@ def _compile(src: str) -> str:
     return obj
 
 
+def cxx() -> str:
+    for cand in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("no host C++ compiler found")
+
+
+def _compile_host(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [cxx(), "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-c",
+           os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host compile failed for {src}:\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
 def build(jobs: int = 4, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, SOURCES)) + list(ex.map(_compile_host, HOST_SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

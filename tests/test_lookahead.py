@@ -1,0 +1,197 @@
+"""Lookahead cache (host C++ in libpta, include/pta_lookahead.h) against the plain oracle
+(oracle/lookahead.py), and the oracle against a hand-worked example and the properties its
+definition fixes.  CPU only."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_speculative_verify_amd as psv
+from oracle.lookahead import LookaheadOracle, tree_mask_from_parents
+from workload.tokens import synthetic_streams
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "lookahead_worked_example.txt")
+
+
+def golden():
+    out = {}
+    with open(GOLDEN, encoding="utf-8") as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = (p.strip() for p in line.split("=", 1))
+                out[k] = [int(x) for x in v.split()]
+    return out
+
+
+# ---------------------------------------------------------------- oracle pins
+@pytest.mark.parametrize("mm,budget,key", [(2, 5, "mm2_budget5"), (4, 6, "mm4_budget6")])
+def test_oracle_worked_example(mm, budget, key):
+    g = golden()
+    o = LookaheadOracle(g["window"][0], mm)
+    o.append(0, g["history"])
+    tok, par = o.propose(0, budget)
+    assert tok == g[key + "_tokens"] and par == g[key + "_parents"]
+
+
+def test_oracle_budgets_worked_example():
+    g = golden()
+    o = LookaheadOracle(8, 4)
+    assert o.update_budgets([0], [8], [2], 1, 8) == g["budget_after_2_of_8"]
+    o2 = LookaheadOracle(8, 4)
+    assert o2.update_budgets([0, 1, 2], [0, 0, 0], [0, 0, 0], 1, 8, 0) == [8, 8, 8]
+    assert [max(1, b * 10 // 20) for b in (8, 8, 4)] == g["batch_cap_10_budgets"]
+
+
+def test_oracle_properties():
+    """Best-first picks never raise the score (a string occurs at most as often as its prefix),
+    a smaller budget gives a prefix of a larger one's answer, every candidate string occurs in
+    some history, and no longer suffix than the match has a continuation."""
+    streams = synthetic_streams(3, 300, vocab=40, seed=3)
+    o = LookaheadOracle(6, 4)
+    for s, t in enumerate(streams):
+        o.append(s, t)
+    for s in range(3):
+        p = o.match(s)
+        assert p is not None
+        h = o.hist[s]
+        for k in range(len(p) + 1, min(o.max_match, len(h)) + 1):
+            assert not o.continuations(s, h[len(h) - k:])
+        tok, par = o.propose(s, 12)
+        strings = []
+        for i, (x, q) in enumerate(zip(tok, par)):
+            strings.append((p if q < 0 else strings[q]) + [x])
+        scores = [o.score(s, st) for st in strings]
+        assert all(a >= b for a, b in zip(scores, scores[1:]))
+        assert all(o.count_global(st) > 0 for st in strings)
+        assert all(len(st) <= o.window for st in strings)
+        for b in range(13):
+            tb, pb = o.propose(s, b)
+            assert tb == tok[:b] and pb == par[:b]
+
+
+def test_oracle_no_match_and_distinct_tokens():
+    o = LookaheadOracle(8, 4)
+    o.append(0, list(range(50)))            # every token once: nothing ever continues the suffix
+    assert o.propose(0, 8) == ([], [])
+    assert o.propose(7, 8) == ([], [])       # unknown sequence
+    o.append(1, [49, 100])                   # another sequence continues 49 with 100 (global cache)
+    assert o.propose(0, 8) == ([100], [-1])
+
+
+def test_tree_mask_round_trip_with_accept_oracle():
+    """The mask built from a proposal gives back the same parents under the acceptance
+    oracle's own reading of the mask."""
+    streams = synthetic_streams(2, 400, vocab=30, seed=4)
+    o = LookaheadOracle(8, 4)
+    for s, t in enumerate(streams):
+        o.append(s, t)
+    for s in range(2):
+        tok, par = o.propose(s, 16)
+        m = np.array(tree_mask_from_parents(par, len(tok), 16), np.uint8)
+        assert list(oracle.tree_parents(m, len(tok))) == par
+
+
+# ---------------------------------------------------------------- library parity
+def run_both(window, mm, streams, queries, budget, max_q):
+    c = psv.LookaheadCache(window, mm)
+    o = LookaheadOracle(window, mm)
+    for s, t in enumerate(streams):
+        c.append(s, t)
+        o.append(s, t)
+    tok, par, cnt = c.propose(queries, [budget] * len(queries), max_q)
+    for i, s in enumerate(queries):
+        et, ep = o.propose(s, budget)
+        assert cnt[i] == len(et), (s, cnt[i], len(et))
+        assert list(tok[i, :cnt[i]]) == et and list(par[i, :cnt[i]]) == ep
+        assert (tok[i, cnt[i]:] == -1).all() and (par[i, cnt[i]:] == -1).all()
+    return c, o
+
+
+@pytest.mark.parametrize("window,mm,vocab,n,seed", [
+    (8, 4, 50, 400, 11), (4, 3, 20, 300, 12), (16, 8, 200, 600, 13), (2, 1, 10, 200, 14), (12, 2, 30, 500, 15),
+])
+def test_propose_matches_oracle(window, mm, vocab, n, seed):
+    streams = synthetic_streams(4, n, vocab=vocab, seed=seed)
+    run_both(window, mm, streams, [0, 1, 2, 3, 9], 10, 16)
+
+
+def test_incremental_appends_release_and_budgets():
+    streams = synthetic_streams(3, 240, vocab=25, seed=21)
+    c = psv.LookaheadCache(6, 3)
+    o = LookaheadOracle(6, 3)
+    rng = np.random.default_rng(22)
+    pos = [0, 0, 0]
+    budgets = [8, 8, 8]
+    for step in range(30):
+        for s in range(3):
+            k = int(rng.integers(0, 9))              # a step commits 0..8 tokens
+            chunk = streams[s][pos[s]:pos[s] + k]
+            pos[s] += k
+            c.append(s, chunk)
+            o.append(s, chunk)
+        if step == 15:
+            c.release(1)
+            o.release(1)
+        tok, par, cnt = c.propose([0, 1, 2], budgets, 8)
+        for i in range(3):
+            et, ep = o.propose(i, budgets[i])
+            assert list(tok[i, :cnt[i]]) == et and list(par[i, :cnt[i]]) == ep
+        acc = [int(rng.integers(0, x + 1)) for x in cnt]
+        got = c.update_budgets([0, 1, 2], cnt, acc, 1, 8, 16)
+        want = o.update_budgets([0, 1, 2], [int(x) for x in cnt], acc, 1, 8, 16)
+        assert list(got) == want
+        budgets = list(got)
+
+
+def test_tree_mask_matches_oracle():
+    streams = synthetic_streams(4, 300, vocab=20, seed=31)
+    c, o = run_both(8, 4, streams, [0, 1, 2, 3], 12, 12)
+    tok, par, cnt = c.propose([0, 1, 2, 3], [12, 5, 0, 12], 12)
+    mask = psv.taco_la_tree_mask(par, cnt)
+    for i in range(4):
+        assert np.array_equal(mask[i], np.array(tree_mask_from_parents(list(par[i]), int(cnt[i]), 12), np.uint8))
+
+
+def test_host_argument_checks():
+    lib = psv.load()
+    assert not lib.taco_la_create(1, 1) and not lib.taco_la_create(8, 8) and not lib.taco_la_create(65, 4)
+    c = psv.LookaheadCache(8, 4)
+    with pytest.raises(psv.PtaError):
+        c.append(-1, [1, 2])
+    with pytest.raises(psv.PtaError):
+        c.append(0, [1, -2])
+    with pytest.raises(psv.PtaError):
+        c.propose([0], [9], 8)                      # budget above max_q
+    with pytest.raises(psv.PtaError):
+        c.update_budgets([0], [2], [3], 1, 8)       # more accepted than proposed
+    with pytest.raises(psv.PtaError):
+        psv.taco_la_tree_mask(np.array([[0, -1]], np.int32), [1])   # a node its own parent
+    c.append(0, [])
+    assert c.propose([0], [4], 8)[2][0] == 0
+
+
+def test_append_batch_equals_single_appends():
+    streams = synthetic_streams(5, 200, vocab=15, seed=41)
+    a = psv.LookaheadCache(6, 4)
+    b = psv.LookaheadCache(6, 4)
+    pos = [0] * 5
+    rng = np.random.default_rng(42)
+    for _ in range(25):
+        chunks = []
+        for s in range(5):
+            k = int(rng.integers(0, 7))
+            chunks.append(streams[s][pos[s]:pos[s] + k])
+            pos[s] += k
+        a.append_batch([4, 3, 2, 1, 0], chunks[::-1])
+        for s in range(5):
+            b.append(s, chunks[s])
+        ra, rb = a.propose(range(5), [6] * 5, 6), b.propose(range(5), [6] * 5, 6)
+        assert all(np.array_equal(x, y) for x, y in zip(ra, rb))
+    with pytest.raises(psv.PtaError):
+        a.append_batch([0, 1], [[1, 2], [3, -1]])      # a negative token: nothing appended
+    assert all(np.array_equal(x, y) for x, y in zip(a.propose(range(5), [6] * 5, 6),
+                                                      b.propose(range(5), [6] * 5, 6)))
