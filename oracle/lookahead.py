@@ -8,7 +8,7 @@ multi-branch forest; each sequence's candidate length adapts to its hit rate
 and to the batch size.
 
 The talk fixes no data structure or formula; this module takes these
-readings (the same ones the library's header states):
+readings (the library header restates them):
   * count_local(s, p) = occurrences of the token string p inside sequence s's
     history; count_global(p) = the sum over every history ever appended
     (released sequences included); only strings of length <= window count;

@@ -37,13 +37,105 @@ def test_oracle_worked_example(mm, budget, key):
     assert tok == g[key + "_tokens"] and par == g[key + "_parents"]
 
 
-def test_oracle_budgets_worked_example():
+def pin_budgets(cls=LookaheadOracle):
+    """Budget arithmetic of the oracle class against the hand-worked golden values: hit-rate
+    steps, a capped batch where flooring bites and one where the min_len floor keeps the total
+    above the cap."""
     g = golden()
-    o = LookaheadOracle(8, 4)
+    o = cls(8, 4)
     assert o.update_budgets([0], [8], [2], 1, 8) == g["budget_after_2_of_8"]
-    o2 = LookaheadOracle(8, 4)
-    assert o2.update_budgets([0, 1, 2], [0, 0, 0], [0, 0, 0], 1, 8, 0) == [8, 8, 8]
-    assert [max(1, b * 10 // 20) for b in (8, 8, 4)] == g["batch_cap_10_budgets"]
+    o = cls(8, 4)
+    assert o.update_budgets([0, 1, 2], [0, 0, 8], [0, 0, 0], 1, 8, 10) == g["batch_cap_10_budgets"]
+    o = cls(8, 4)
+    assert o.update_budgets([0, 1, 2, 3], [0, 0, 8, 8], [0, 0, 0, 0], 1, 8, 11) == g["cap11_min1_budgets"]
+    o = cls(8, 4)
+    assert o.update_budgets([0, 1, 2, 3], [0, 0, 8, 8], [0, 0, 0, 0], 3, 8, 8) == g["cap8_min3_budgets"]
+    o = cls(8, 4)
+    steps = [o.update_budgets([0], [n], [a], 1, 8)[0] for n, a in ((8, 2), (4, 4), (0, 0), (3, 1))]
+    assert steps == g["hit_steps_budgets"] and o.hit[0] == g["hit_steps_final_rate"][0]
+    o = cls(8, 4)
+    assert o.update_budgets([0, 1, 2], [0, 0, 0], [0, 0, 0], 1, 8, 0) == [8, 8, 8]   # no cap
+
+
+def pin_released(cls=LookaheadOracle):
+    """Global counts keep a released sequence's history (golden, worked by hand)."""
+    g = golden()
+    o = cls(4, 2)
+    o.append(0, [1, 2, 3, 1, 2])
+    o.append(1, [1, 2, 4] * 3)
+    o.release(1)
+    assert o.propose(0, 2) == (g["released_query_tokens"], g["released_query_parents"])
+    assert o.propose(1, 2) == ([], [])
+    o.append(1, [1, 2])
+    assert o.propose(1, 2) == (g["reused_query_tokens"], g["reused_query_parents"])
+
+
+def test_oracle_budgets_worked_example():
+    pin_budgets()
+
+
+def test_oracle_released_history_worked_example():
+    pin_released()
+
+
+class _RoundedCap(LookaheadOracle):
+    """Planted mistake: the batch cap rounds to nearest instead of flooring."""
+    def update_budgets(self, seqs, proposed, accepted, min_len, max_len, batch_cap=0):
+        out = LookaheadOracle.update_budgets(self, seqs, proposed, accepted, min_len, max_len, 0)
+        total = sum(out)
+        if batch_cap > 0 and total > batch_cap:
+            out = [max(min_len, (2 * b * batch_cap + total) // (2 * total)) for b in out]
+        return out
+
+
+class _NoMinFloorUnderCap(LookaheadOracle):
+    """Planted mistake: the capped budgets lose their min_len floor."""
+    def update_budgets(self, seqs, proposed, accepted, min_len, max_len, batch_cap=0):
+        out = LookaheadOracle.update_budgets(self, seqs, proposed, accepted, min_len, max_len, 0)
+        total = sum(out)
+        if batch_cap > 0 and total > batch_cap:
+            out = [b * batch_cap // total for b in out]
+        return out
+
+
+class _RoundedHitRate(LookaheadOracle):
+    """Planted mistake: the accepted fraction is rounded up instead of floored."""
+    def update_budgets(self, seqs, proposed, accepted, min_len, max_len, batch_cap=0):
+        out = []
+        for s, n, a in zip(seqs, proposed, accepted):
+            h = self.hit.get(s, 1 << 16)
+            if n > 0:
+                h = (h + -(-(a << 16) // n)) >> 1
+            self.hit[s] = h
+            out.append(min(max((max_len * h + (1 << 15)) >> 16, min_len), max_len))
+        total = sum(out)
+        if batch_cap > 0 and total > batch_cap:
+            out = [max(min_len, b * batch_cap // total) for b in out]
+        return out
+
+
+class _ForgetsReleased(LookaheadOracle):
+    """Planted mistake: a released sequence's history leaves the global counts."""
+    def release(self, seq):
+        self.hist.pop(seq, None)
+        self.hit.pop(seq, None)
+
+
+class _KeepsReleasedLive(LookaheadOracle):
+    """Planted mistake: release keeps the history live and also files it as retired (counted
+    twice), and a re-used sequence id continues the old history."""
+    def release(self, seq):
+        if seq in self.hist:
+            self.retired.append(list(self.hist[seq]))
+        self.hit.pop(seq, None)
+
+
+@pytest.mark.parametrize("mutant,pin", [(_RoundedCap, pin_budgets), (_NoMinFloorUnderCap, pin_budgets),
+                                        (_RoundedHitRate, pin_budgets), (_ForgetsReleased, pin_released),
+                                        (_KeepsReleasedLive, pin_released)])
+def test_planted_mistakes_fail_a_pin(mutant, pin):
+    with pytest.raises(AssertionError):
+        pin(mutant)
 
 
 def test_oracle_properties():
@@ -195,3 +287,25 @@ def test_append_batch_equals_single_appends():
         a.append_batch([0, 1], [[1, 2], [3, -1]])      # a negative token: nothing appended
     assert all(np.array_equal(x, y) for x, y in zip(a.propose(range(5), [6] * 5, 6),
                                                       b.propose(range(5), [6] * 5, 6)))
+
+
+def test_library_matches_budget_and_release_goldens():
+    """The C++ cache against the hand-worked values themselves (not only against the oracle)."""
+    g = golden()
+    c = psv.LookaheadCache(8, 4)
+    assert list(c.update_budgets([0, 1, 2, 3], [0, 0, 8, 8], [0, 0, 0, 0], 1, 8, 11)) == g["cap11_min1_budgets"]
+    c = psv.LookaheadCache(8, 4)
+    assert list(c.update_budgets([0, 1, 2, 3], [0, 0, 8, 8], [0, 0, 0, 0], 3, 8, 8)) == g["cap8_min3_budgets"]
+    c = psv.LookaheadCache(8, 4)
+    steps = [int(c.update_budgets([0], [n], [a], 1, 8)[0]) for n, a in ((8, 2), (4, 4), (0, 0), (3, 1))]
+    assert steps == g["hit_steps_budgets"]
+    c = psv.LookaheadCache(4, 2)
+    c.append(0, [1, 2, 3, 1, 2])
+    c.append(1, [1, 2, 4] * 3)
+    c.release(1)
+    tok, par, cnt = c.propose([0, 1], [2, 2], 4)
+    assert list(tok[0, :cnt[0]]) == g["released_query_tokens"] and list(par[0, :cnt[0]]) == g["released_query_parents"]
+    assert cnt[1] == 0
+    c.append(1, [1, 2])
+    tok, par, cnt = c.propose([1], [2], 4)
+    assert list(tok[0, :cnt[0]]) == g["reused_query_tokens"] and list(par[0, :cnt[0]]) == g["reused_query_parents"]
