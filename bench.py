@@ -2,18 +2,24 @@
 """Benchmark of the paged tree attention hot path on one MI355X.
 
 One step = the whole hot path over one batch: append the candidates' K/V rows
-into their paged slots (taco_kv_append), then paged tree attention over every
-sequence's context (split-K partials merged by log-sum-exp inside the same launch where
-the workload is configured for it).  Inputs are synthetic, seeded and resident in HBM before
-the timed region; R independent input sets are rotated step to step so the
-256 MB last-level cache cannot serve the KV stream from a previous step.
+into their paged slots, then paged tree attention over every sequence's
+context (on the decode workloads the append runs inside the attention launch).
+Inputs are synthetic, seeded and resident in HBM before the timed region;
+R independent input sets are rotated step to step so the 256 MB last-level
+cache cannot serve the KV stream of a previous step.
 
-Prints ONE JSON line.  `value` is KV HBM bytes (algorithmic: every K/V byte of
-every sequence's context counted once) per second of whole-step wall time
-(append + attention, K steps between two synchronisations with no timing events
-inside), in GB/s.  `roofline.achieved` is the same bytes per second of attention
-call time alone: HIP events on the launch stream bracket K back-to-back attention
-calls in a pass of their own that runs before the timed steps.
+The default run measures the widest-tree, largest single-GPU workload
+(long_splitk_verify: 4 sequences of 32K-128K tokens, 64/8 heads, a 32-node
+candidate tree each) and prints ONE JSON line.  `value` is KV HBM bytes
+(algorithmic: every K/V byte of every sequence's context counted once) per
+second of whole-step wall time (append + attention, K steps between two
+synchronisations with no timing events inside), in GB/s.  `roofline` holds the
+attention call's HBM and matrix-core fractions: HIP events on the launch
+stream bracket K back-to-back attention calls in a pass of their own.  The
+same line carries the measured streaming-read and matrix-core ceilings of the
+device, the fp64 CPU oracle timed on the host's cores and compared with the
+timed call's output, and the other Llama-shaped workloads measured the same
+way (fewer steps) under `workloads`.
 """
 from __future__ import annotations
 
@@ -33,7 +39,11 @@ if ROOT not in sys.path:
 METRIC = "KV HBM GB/s (% of peak) + verified candidate tokens/s, paged tree attn, 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-HEADLINE = "llama3_8b_decode"
+HEADLINE = "long_splitk_verify"
+# measured in the same run as the headline (attention call, parity on sampled sequences)
+EXTRA_WORKLOADS = ("llama3_8b_decode", "llama31_70b_verify", "fp8_kv_chain")
+# max |GPU - oracle| bound per KV dtype
+TOLERANCE = {"f32": 1e-5, "bf16": 1e-2, "fp8": 3e-2}
 SETTLE_S = 0.3                 # untimed steps after the warm-up, before any measurement
 
 # launch configuration of each workload: entry point ("whole": one pass per
@@ -163,31 +173,6 @@ class DeviceSet:
         self.workspace = None
 
 
-def run_attention(psv, ds, cfg):
-    d = ds.d
-    if cfg["mode"] == "balanced":
-        psv.taco_paged_tree_attn_balanced(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
-                                          d.q_lens, d.tree_mask, d.scale, out=ds.out, lse=ds.lse,
-                                          k_scale=d.k_scale, v_scale=d.v_scale, workspace=ds.workspace,
-                                          max_ctx_len=d.max_ctx_len, path=cfg["path"])
-    elif cfg["mode"] == "whole":
-        psv.taco_paged_tree_attn(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
-                                 d.tree_mask, d.scale, out=ds.out, lse=ds.lse, k_scale=d.k_scale,
-                                 v_scale=d.v_scale, max_ctx_len=d.max_ctx_len, path=cfg["path"])
-    elif cfg["mode"] == "shared":
-        psv.taco_paged_tree_attn_shared_prefix(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
-                                               d.q_lens, d.tree_mask, ds.prefix_leader, ds.max_group,
-                                               cfg["split"], d.scale, out=ds.out, lse=ds.lse,
-                                               k_scale=d.k_scale, v_scale=d.v_scale, workspace=ds.workspace,
-                                               max_ctx_len=d.max_ctx_len, path=cfg["path"])
-    else:
-        psv.taco_paged_tree_attn_splitk(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
-                                        d.q_lens, d.tree_mask, d.scale, cfg["split"], out=ds.out,
-                                        lse=ds.lse, k_scale=d.k_scale, v_scale=d.v_scale,
-                                        workspace=ds.workspace, max_ctx_len=d.max_ctx_len,
-                                        path=cfg["path"])
-
-
 # ------------------------------------------------------------------ CPU baseline (oracle)
 def accepted_walk(tok, par, cnt, truth):
     """Greedy acceptance against the stream's true next tokens: the deepest candidate whose path
@@ -209,7 +194,6 @@ def lookahead_cache_bench(args, B=64, prompt=1024, steps=200, window=16, max_mat
     tree, scores it against the synthetic stream's true continuation (greedy acceptance), feeds
     the hit back into the budgets and appends the accepted tokens plus one.  Timed: the library
     calls only."""
-    import numpy as np
     import paged_speculative_verify_amd as psv
     from workload.tokens import synthetic_streams
     streams = synthetic_streams(B, prompt + steps * (max_len + 1) + 16, vocab=1000, seed=7)
@@ -267,35 +251,57 @@ def lookahead_cache_bench(args, B=64, prompt=1024, steps=200, window=16, max_mat
     return 0
 
 
-def cpu_baseline(w, gpu_out, budget_s=12.0):
-    """Time the fp64 oracle on whole sequences of the same workload until the time budget is
-    spent; report its KV GB/s and its max |difference| from the GPU output on that sample."""
+def blas_description() -> str:
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{x.get('internal_api')} {x.get('version')} ({x.get('threading_layer')})"
+                for x in threadpool_info() if x.get("user_api") == "blas"]
+        return ", ".join(libs) if libs else "unknown"
+    except Exception:                      # pragma: no cover - diagnostic only
+        return "unknown"
+
+
+def oracle_rows(w, sel):
+    """fp64 oracle output of sequences `sel` (index array) of workload w."""
     import oracle
+    s = w.spec
+    ref, _ = oracle.paged_tree_attn(w.q[sel], w.k_cache, w.v_cache, w.block_tables[sel], w.ctx_lens[sel],
+                                    w.q_lens[sel], w.tree_mask[sel], w.scale, q_dtype=s.q_dtype,
+                                    kv_dtype=s.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
+    return ref
+
+
+def max_diff(gpu_rows, ref) -> float:
+    v = ~np.isnan(ref)                     # padding rows (i >= q_b) are NaN in the oracle
+    return float(np.abs(gpu_rows[v] - ref[v]).max()) if v.any() else 0.0
+
+
+def cpu_baseline(w, gpu_out, budget_s=12.0):
+    """Time the fp64 oracle on whole sequences of the same workload, BLAS on every core of this
+    process's affinity set, until the time budget is spent; report its KV GB/s and its max
+    |difference| from the GPU output (of the timed call) on that sample."""
     from threadpoolctl import threadpool_limits
     s = w.spec
     elem = {"f32": 4, "bf16": 2, "fp8": 1}[s.kv_dtype]
     Hkv, D = w.k_cache.shape[1], w.k_cache.shape[3]
+    cores = len(os.sched_getaffinity(0))
     done, kvb, err = [], 0, 0.0
     t_total = 0.0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=cores, user_api="blas"):
         for b in range(w.q.shape[0]):
-            sel = np.array([b])
             t0 = time.perf_counter()
-            ref, _ = oracle.paged_tree_attn(w.q[sel], w.k_cache, w.v_cache, w.block_tables[sel],
-                                            w.ctx_lens[sel], w.q_lens[sel], w.tree_mask[sel], w.scale,
-                                            q_dtype=s.q_dtype, kv_dtype=s.kv_dtype, k_scale=w.k_scale,
-                                            v_scale=w.v_scale)
+            ref = oracle_rows(w, np.array([b]))
             t_total += time.perf_counter() - t0
             done.append(b)
             kvb += int(w.ctx_lens[b]) * Hkv * D * 2 * elem
-            v = ~np.isnan(ref[0])
-            err = max(err, float(np.abs(gpu_out[b][v] - ref[0][v]).max()))
+            err = max(err, max_diff(gpu_out[b], ref[0]))
             if t_total >= budget_s:
                 break
-    return {"value": kvb / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(kvb / t_total / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{len(done)} of {w.q.shape[0]} sequences (whole contexts, {kvb / 1e6:.0f} MB of KV) "
-                      f"in {t_total:.1f} s, fp64 numpy, BLAS limited to 1 thread",
-            "max_abs_diff_vs_gpu": err}
+                      f"in {t_total:.1f} s, fp64 numpy; matrix products on {cores} BLAS threads "
+                      f"({blas_description()}), element-wise steps on one thread",
+            "sequences": done, "max_abs_diff_vs_gpu": err}
 
 
 def load_traffic(config_name: str, src_hash: str):
@@ -310,6 +316,243 @@ def load_traffic(config_name: str, src_hash: str):
     return t.get("hbm_bytes_per_launch")
 
 
+# ------------------------------------------------------------------ device ceilings
+def calibrate(psv, torch, read_bytes=2 << 30, reps=5):
+    """Measured ceilings of this device with the library's own kernels: a streaming read of a
+    2 GiB buffer (far beyond the caches) and a bf16 matrix-core loop."""
+    dev = torch.device("cuda")
+    props = torch.cuda.get_device_properties(dev)
+    cus = props.multi_processor_count
+    buf = torch.empty(read_bytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(65535, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for wg_per_cu in (4, 8):
+        wgs = cus * wg_per_cu
+        for _ in range(2):
+            psv.taco_pta_calib_stream_read(buf, sink, wgs)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            psv.taco_pta_calib_stream_read(buf, sink, wgs)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[wgs] = read_bytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    best_wgs = max(res, key=res.get)
+    del buf
+    fsink = torch.zeros(65535, dtype=torch.float32, device=dev)
+    wgs, iters = cus * 2, 4096
+    for _ in range(2):
+        psv.taco_pta_calib_mfma_bf16(wgs, iters, fsink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    flops = 0
+    for _ in range(reps):
+        flops += psv.taco_pta_calib_mfma_bf16(wgs, iters, fsink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    tflops = flops / (e0.elapsed_time(e1) / 1e3) / 1e12
+    return {"stream_read_gbs": round(res[best_wgs], 1),
+            "stream_read": f"{read_bytes >> 30} GiB read once per launch with 16-byte loads, {best_wgs} "
+                           f"workgroups of 256 lanes (best of {sorted(res)}), {reps} launches",
+            "mfma_bf16_tflops": round(tflops, 1),
+            "mfma_bf16": f"v_mfma_f32_32x32x16_bf16, 4 independent chains per wave, {wgs} workgroups of "
+                         f"4 waves, {iters} rounds, {reps} launches",
+            "compute_units": cus}
+
+
+# ------------------------------------------------------------------ one workload
+def resolve_cfg(name, args):
+    """The workload's launch configuration with the command-line overrides applied."""
+    cfg = launch_config(name)
+    if args.path is not None:
+        cfg["path"] = args.path
+    if args.split is not None:
+        cfg["mode"] = "split" if args.split > 0 else ("whole" if args.split == 0 else "balanced")
+        cfg["split"] = args.split if args.split > 0 else None
+    if args.shared_entry:
+        from workload.gen import CONFIGS
+        if CONFIGS[name].shared_prefix_pages <= 0 or args.private_pages:
+            raise SystemExit("--shared-entry needs a shared-prefix workload on shared pages")
+        cfg["mode"], cfg["split"] = "shared", CONFIGS[name].shared_prefix_pages * 16
+    if cfg["mode"] != "whole" or args.path not in (None, "auto") or args.separate_append:
+        cfg.pop("fuse_append", None)      # the fused append lives in the whole-context stream kernel
+    return cfg
+
+
+def build_sets(psv, torch, name, cfg, nsets, private_pages=False):
+    """Generate, upload and prepare `nsets` independent input sets of workload `name`."""
+    from workload import make
+    sets = []
+    for r in range(nsets):
+        w = make(name, seed=None if r == 0 else 1000 + r, **({"share_group": 1} if private_pages else {}))
+        sets.append(DeviceSet(w, torch))
+        print(f"[bench] {name} set {r}: ctx sum {int(w.ctx_lens.sum())}, KV {kv_bytes(w) / 1e6:.1f} MB",
+              file=sys.stderr, flush=True)
+    for ds in sets:
+        d = ds.d
+        if cfg["mode"] in ("split", "shared"):
+            nbytes = psv.taco_paged_tree_attn_splitk_workspace_size(
+                d.q, d.k_cache, d.block_tables, cfg["split"], max_ctx_len=d.max_ctx_len)
+        elif cfg["mode"] == "balanced":
+            nbytes = psv.taco_paged_tree_attn_balanced_workspace_size(
+                d.q, d.k_cache, d.block_tables, max_ctx_len=d.max_ctx_len)
+        else:
+            nbytes = 0
+        if nbytes:
+            ds.workspace = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        # validated once, then re-issued with no per-call Python checks so the host stays ahead
+        if cfg.get("fuse_append"):
+            ds.append_call = lambda: None        # the append runs inside the attention launch
+        else:
+            ds.append_call = psv.prepare_kv_append(ds.k_new, ds.v_new, ds.slots, d.k_cache, d.v_cache,
+                                                   k_scale=d.k_scale, v_scale=d.v_scale)
+        ds.attn_call = psv.prepare_paged_tree_attn(
+            "whole_append" if cfg.get("fuse_append") else cfg["mode"],
+            d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens, d.tree_mask,
+            d.scale, ds.out, lse=ds.lse, k_scale=d.k_scale, v_scale=d.v_scale,
+            partition_tokens=cfg["split"], workspace=ds.workspace, max_ctx_len=d.max_ctx_len,
+            prefix_leader=ds.prefix_leader, max_group=ds.max_group, k_new=ds.k_new_full, v_new=ds.v_new_full,
+            path=cfg["path"])
+    torch.cuda.synchronize()
+    return sets
+
+
+def measure(torch, sets, cfg, K, warmup, per_call=True):
+    """Timings of one workload: warm-up, clock settling, the attention calls bracketed by HIP
+    events on the launch stream (rotating sets: no cache reuse across calls), the same set
+    repeated (warm), one event pair per call (percentiles), the append calls, and the whole
+    steps between two synchronisations with nothing else in between."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        ds = sets[i % len(sets)]
+        ds.append_call()
+        ds.attn_call()
+    torch.cuda.synchronize()
+    # clock settling: a few warm-up steps are over in about a millisecond, well before the GPU
+    # clock has ramped up; untimed steps continue for at least SETTLE_S of wall time so that
+    # no measurement below sees the ramp
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for _ in range(8):
+            ds = sets[n_settle % len(sets)]
+            ds.append_call()
+            ds.attn_call()
+            n_settle += 1
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
+    order = [(warmup + n_settle + i) % len(sets) for i in range(K)]
+
+    def bracketed(fn, idx):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(K):
+            fn(sets[idx[i]])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    # K attention calls back to back between two events (an event pair around every single
+    # call adds its own overhead to each call)
+    attn_ms = bracketed(lambda ds: ds.attn_call(), order)
+    warm_ms = bracketed(lambda ds: ds.attn_call(), [order[0]] * K)
+    pct = None
+    if per_call:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        torch.cuda.synchronize()
+        for i in range(K):
+            evs[i][0].record(stream)
+            sets[order[i]].attn_call()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+        pct = {"p10": round(float(np.percentile(t, 10)), 2), "p50": round(float(np.percentile(t, 50)), 2),
+               "p90": round(float(np.percentile(t, 90)), 2)}
+    append_ms = None if cfg.get("fuse_append") else bracketed(lambda ds: ds.append_call(), order)
+    # the timed steps: nothing but the step's own launches between the two synchronisations
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(K):
+        ds = sets[order[i]]
+        ds.append_call()
+        ds.attn_call()
+    t_enqueue = time.perf_counter() - t_wall
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    return {"order": order, "attn_ms": attn_ms, "warm_ms": warm_ms, "pct_us": pct, "append_ms": append_ms,
+            "ms_per_step": wall / K * 1e3, "enqueue_ms": t_enqueue / K * 1e3, "n_settle": n_settle,
+            "settle_ms": settle_ms}
+
+
+def accounting(sets, order):
+    """Per-launch means over the timed order: KV bytes (every sequence), distinct KV bytes,
+    candidates and algorithmic flops."""
+    K = len(order)
+    flops = {r: attn_flops(sets[r].w) for r in set(order)}
+    return {"kv": sum(kv_bytes(sets[o].w) for o in order) / K,
+            "unique_kv": sum(unique_kv_bytes(sets[o].w) for o in order) / K,
+            "cands": sum(int(sets[o].w.q_lens.sum()) for o in order) / K,
+            "flops": sum(flops[o] for o in order) / K}
+
+
+def timed_output(torch, ds):
+    """The output of the prepared (timed) call on set ds, as float64 on the host."""
+    ds.append_call()
+    ds.attn_call()
+    torch.cuda.synchronize()
+    return ds.out.to(torch.float64).cpu().numpy()
+
+
+def ceilings(acc, attn_ms):
+    """Both roofline fractions of one attention call and the bound its intensity implies."""
+    s = attn_ms / 1e3
+    gbs = acc["unique_kv"] / s / 1e9
+    tfl = acc["flops"] / s / 1e12
+    intensity = acc["flops"] / acc["unique_kv"]
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    floor_s = max(acc["unique_kv"] / (HBM_PEAK_GBS * 1e9), acc["flops"] / (BF16_PEAK_TFLOPS * 1e12))
+    return {"gbs": gbs, "tflops": tfl, "intensity": intensity, "ridge": ridge,
+            "bound": "mfma" if intensity > ridge else "hbm", "floor_us": floor_s * 1e6,
+            "frac_of_floor": floor_s / s}
+
+
+def extra_workload(psv, torch, name, args):
+    """One more Llama-shaped workload in the same run: fewer steps, parity of the timed call on
+    sampled sequences."""
+    cfg = resolve_cfg(name, argparse.Namespace(path=None, split=None, shared_entry=False, private_pages=False,
+                                               separate_append=False))
+    nsets = 1 if name == "fp8_kv_chain" else 2          # fp8: 2.4 GB of KV per set, ten times the LLC
+    sets = build_sets(psv, torch, name, cfg, nsets)
+    K = min(args.steps, 20)
+    m = measure(torch, sets, cfg, K, args.warmup, per_call=False)
+    acc = accounting(sets, m["order"])
+    c = ceilings(acc, m["attn_ms"])
+    w = sets[0].w
+    gpu = timed_output(torch, sets[0])
+    B = w.q.shape[0]
+    sel = sorted(set([0, B // 3, (2 * B) // 3, B - 1]))
+    ref = oracle_rows(w, np.array(sel))
+    err = max(max_diff(gpu[b], ref[i]) for i, b in enumerate(sel))
+    tol = TOLERANCE[w.spec.kv_dtype]
+    res = {"entry": cfg["mode"] + (" (KV append fused)" if cfg.get("fuse_append") else ""),
+           "attention_us": round(m["attn_ms"] * 1e3, 2), "attention_us_warm": round(m["warm_ms"] * 1e3, 2),
+           "ms_per_step": round(m["ms_per_step"], 5), "kv_bytes_per_step": int(acc["kv"]),
+           "hbm_gbs": round(c["gbs"], 1), "hbm_frac": round(c["gbs"] / HBM_PEAK_GBS, 4),
+           "mfma_tflops": round(c["tflops"], 1), "mfma_frac": round(c["tflops"] / BF16_PEAK_TFLOPS, 4),
+           "bound": c["bound"], "frac_of_roofline_time": round(c["frac_of_floor"], 4),
+           "candidates_per_s": round(acc["cands"] / (m["ms_per_step"] / 1e3), 1), "steps": K,
+           "input_sets_rotated": nsets, "parity_sequences": sel, "max_abs_diff_vs_oracle": err,
+           "tolerance": tol, "parity_ok": bool(err <= tol)}
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------ main
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
@@ -317,8 +560,10 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=HEADLINE, choices=sorted(LAUNCH))
-    ap.add_argument("--sets", type=int, default=3, help="input sets rotated step to step")
+    ap.add_argument("--sets", type=int, default=2, help="input sets rotated step to step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="measure only --config (no calibration kernels, no other workloads)")
     ap.add_argument("--path", choices=["auto", "valu", "mfma", "tile"], default=None,
                     help="override the kernel family of the workload's launch configuration")
     ap.add_argument("--split", type=int, default=None,
@@ -356,7 +601,6 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     import paged_speculative_verify_amd as psv
-    from workload import make
     psv.load()
 
     if args.copy_calibration:
@@ -373,123 +617,58 @@ def main(argv=None) -> int:
         return qlen_floor(psv, torch, args)
 
     name = args.config
-    cfg = launch_config(name)
-    if args.path is not None:
-        cfg["path"] = args.path
-    if args.split is not None:
-        cfg["mode"] = "split" if args.split > 0 else ("whole" if args.split == 0 else "balanced")
-        cfg["split"] = args.split if args.split > 0 else None
-    if args.shared_entry:
-        from workload.gen import CONFIGS
-        if CONFIGS[name].shared_prefix_pages <= 0 or args.private_pages:
-            print("--shared-entry needs a shared-prefix workload on shared pages", file=sys.stderr)
-            return 2
-        cfg["mode"], cfg["split"] = "shared", CONFIGS[name].shared_prefix_pages * 16
-    if cfg["mode"] != "whole" or args.path not in (None, "auto") or args.separate_append:
-        cfg.pop("fuse_append", None)      # the fused append lives in the whole-context stream kernel
+    cfg = resolve_cfg(name, args)
+    extras = not args.no_extra and name == HEADLINE
+    calib = None
+    if extras:
+        print("[bench] device ceilings (streaming read, matrix-core loop)", file=sys.stderr, flush=True)
+        calib = calibrate(psv, torch)
     print(f"[bench] generating {args.sets} input set(s) for {name}", file=sys.stderr, flush=True)
-    sets = []
-    for r in range(args.sets):
-        w = make(name, seed=None if r == 0 else 1000 + r, **({"share_group": 1} if args.private_pages else {}))
-        sets.append(DeviceSet(w, torch))
-        print(f"[bench] set {r}: ctx sum {int(w.ctx_lens.sum())}, KV {kv_bytes(w) / 1e6:.1f} MB",
-              file=sys.stderr, flush=True)
-    for ds in sets:
-        if cfg["mode"] in ("split", "shared"):
-            nbytes = psv.taco_paged_tree_attn_splitk_workspace_size(
-                ds.d.q, ds.d.k_cache, ds.d.block_tables, cfg["split"], max_ctx_len=ds.d.max_ctx_len)
-        elif cfg["mode"] == "balanced":
-            nbytes = psv.taco_paged_tree_attn_balanced_workspace_size(
-                ds.d.q, ds.d.k_cache, ds.d.block_tables, max_ctx_len=ds.d.max_ctx_len)
-        else:
-            continue
-        ds.workspace = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-    # validated once, then re-issued with no per-call Python checks so the host stays ahead
-    for ds in sets:
-        d = ds.d
-        if cfg.get("fuse_append"):
-            # the append runs inside the attention launch: the step is one call
-            ds.append_call = lambda: None
-        else:
-            ds.append_call = psv.prepare_kv_append(ds.k_new, ds.v_new, ds.slots, d.k_cache, d.v_cache,
-                                                   k_scale=d.k_scale, v_scale=d.v_scale)
-        ds.attn_call = psv.prepare_paged_tree_attn(
-            "whole_append" if cfg.get("fuse_append") else cfg["mode"],
-            d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens, d.tree_mask,
-            d.scale, ds.out, lse=ds.lse, k_scale=d.k_scale, v_scale=d.v_scale,
-            partition_tokens=cfg["split"], workspace=ds.workspace, max_ctx_len=d.max_ctx_len,
-            prefix_leader=ds.prefix_leader, max_group=ds.max_group, k_new=ds.k_new_full, v_new=ds.v_new_full,
-            path=cfg["path"])
-    for i in range(args.warmup):
-        ds = sets[i % len(sets)]
-        ds.append_call()
-        ds.attn_call()
-    torch.cuda.synchronize()
-
-    # clock settling: a few warm-up steps are over in about a millisecond, well before the GPU
-    # clock has ramped up; untimed steps continue for at least SETTLE_S of wall time so that
-    # neither measurement pass below sees the ramp
-    t_settle = time.perf_counter()
-    n_settle = 0
-    while time.perf_counter() - t_settle < SETTLE_S:
-        for _ in range(8):
-            ds = sets[n_settle % len(sets)]
-            ds.append_call()
-            ds.attn_call()
-            n_settle += 1
-        torch.cuda.synchronize()
-    settle_ms = (time.perf_counter() - t_settle) * 1e3
-
+    sets = build_sets(psv, torch, name, cfg, args.sets, private_pages=args.private_pages)
     K = args.steps
-    order = [(args.warmup + n_settle + i) % len(sets) for i in range(K)]
-    # 1. per-call times for the roofline: K attention calls back to back between two HIP
-    #    events on the launch stream (an event pair around every single call adds its own
-    #    overhead to each call), then K append calls the same way; this pass also finishes
-    #    warming the clocks up
-    def bracketed(fn):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(K):
-            fn(sets[order[i]])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / K
-    attn_avg_ms = bracketed(lambda ds: ds.attn_call())
-    # a fused append has no launch of its own: its time is inside attention_ms
-    append_avg_ms = None if cfg.get("fuse_append") else bracketed(lambda ds: ds.append_call())
-    # 2. the timed steps: nothing but the step's own launches between the two synchronisations
-    #    (timing events inside the loop would add their own packets to every step)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    for i in range(K):
-        ds = sets[order[i]]
-        ds.append_call()
-        ds.attn_call()
-    t_enqueue = time.perf_counter() - t_wall
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    kvb = [kv_bytes(sets[o].w) for o in order]
-    ukvb = [unique_kv_bytes(sets[o].w) for o in order]     # = kvb unless pages are shared
-    cands = [int(sets[o].w.q_lens.sum()) for o in order]
-    flops = {r: attn_flops(sets[r].w) for r in set(order)}
-
-    attn_avg_s = attn_avg_ms / 1e3
-    kv_per_launch = sum(kvb) / K
-    unique_per_launch = sum(ukvb) / K
-    # the roofline counts what must cross HBM at least once: distinct pages (a shared prefix once)
-    achieved_gbs = unique_per_launch / attn_avg_s / 1e9
-    ms_per_step = wall / K * 1e3
-    value = kv_per_launch / (ms_per_step / 1e3) / 1e9          # whole-step throughput
-    cand_per_s = (sum(cands) / K) / (ms_per_step / 1e3)
-    tflops = (sum(flops[o] for o in order) / K) / attn_avg_s / 1e12
+    m = measure(torch, sets, cfg, K, args.warmup)
+    acc = accounting(sets, m["order"])
+    c = ceilings(acc, m["attn_ms"])
+    ms_per_step = m["ms_per_step"]
+    value = acc["kv"] / (ms_per_step / 1e3) / 1e9          # whole-step throughput, every sequence's KV
+    cand_per_s = acc["cands"] / (ms_per_step / 1e3)
 
     from paged_speculative_verify_amd.profsum import kernel_source_hash
     src_hash = kernel_source_hash()
-    traffic = load_traffic(name, src_hash)
+    traffic = load_traffic(name + ("_private_pages" if args.private_pages else ""), src_hash)
+    spec0 = sets[0].w.spec
+    kernel = {"balanced": "paged tree attention grid + slice merge launch (balanced entry; one call = "
+                          "both launches)",
+              "split": "paged tree attention kernel (split-K entry, partition merge fused)",
+              "whole": "paged tree attention kernel (whole-context entry"
+                       + (", KV append fused)" if cfg.get("fuse_append") else ")"),
+              "shared": "paged tree attention kernel (shared-prefix entry: each group's prefix partition once, "
+                        "partition merge fused)"}[cfg["mode"]]
+    hbm_frac = c["gbs"] / HBM_PEAK_GBS
+    mfma_frac = c["tflops"] / BF16_PEAK_TFLOPS
+    roofline = {
+        "bound": c["bound"],
+        "achieved": round(c["gbs"] if c["bound"] == "hbm" else c["tflops"], 2),
+        "peak": HBM_PEAK_GBS if c["bound"] == "hbm" else BF16_PEAK_TFLOPS,
+        "unit": "GB/s" if c["bound"] == "hbm" else "TFLOP/s",
+        "frac": round(hbm_frac if c["bound"] == "hbm" else mfma_frac, 4),
+        "traffic": traffic,
+        "hbm": {"achieved_gbs": round(c["gbs"], 2), "peak_gbs": HBM_PEAK_GBS, "frac": round(hbm_frac, 4)},
+        "mfma": {"achieved_tflops": round(c["tflops"], 2), "peak_tflops": BF16_PEAK_TFLOPS,
+                 "frac": round(mfma_frac, 4), "flops": "4 * head_dim per visible (q-head, candidate, key) pair"},
+        "arithmetic_intensity_flop_per_byte": round(c["intensity"], 2),
+        "ridge_flop_per_byte": round(c["ridge"], 2),
+        "roofline_time_us": round(c["floor_us"], 2),
+        "frac_of_roofline_time": round(c["frac_of_floor"], 4),
+        "kernel": kernel,
+        "algorithmic_bytes_per_launch": int(acc["unique_kv"]),
+        "algorithmic_flops_per_launch": int(acc["flops"]),
+        "timing": f"HIP events on the launch stream around {K} back-to-back attention calls "
+                  f"(input sets rotated), run before the timed steps",
+    }
+    if calib is not None:
+        roofline["hbm"]["frac_of_measured_stream_read"] = round(c["gbs"] / calib["stream_read_gbs"], 4)
+        roofline["mfma"]["frac_of_measured_mfma_loop"] = round(c["tflops"] / calib["mfma_bf16_tflops"], 4)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -501,7 +680,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 KV, bf16 Q"}[sets[0].w.spec.kv_dtype],
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 KV, bf16 Q"}[spec0.kv_dtype],
         "data": "synthetic",
         "config": {"workload": name + (" (private pages)" if args.private_pages else ""),
                    "batch": sets[0].w.q.shape[0], "q_heads": sets[0].w.q.shape[2],
@@ -511,40 +690,52 @@ def main(argv=None) -> int:
                    "split_tokens": cfg["split"],
                    "path": cfg["path"], "input_sets_rotated": len(sets)},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        **({"shared_prefix": {"kv_bytes_all_sequences_per_step": int(kv_per_launch),
-                              "distinct_kv_bytes_per_step": int(unique_per_launch),
+        **({"shared_prefix": {"kv_bytes_all_sequences_per_step": int(acc["kv"]),
+                              "distinct_kv_bytes_per_step": int(acc["unique_kv"]),
                               "note": "value counts every sequence's context; roofline counts distinct pages"}}
-           if unique_per_launch != kv_per_launch else {}),
+           if acc["unique_kv"] != acc["kv"] else {}),
         "candidates_per_s": round(cand_per_s, 1),
-        "attention_ms": round(attn_avg_s * 1e3, 5),
-        "kv_append_ms": None if append_avg_ms is None else round(append_avg_ms, 5),
-        "host_enqueue_ms_per_step": round(t_enqueue / K * 1e3, 5),
-        "clock_settle": {"untimed_steps": n_settle, "ms": round(settle_ms, 1)},
-        "attention_tflops": round(tflops, 3),
-        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": {"balanced": "paged tree attention grid + slice merge launch (balanced entry)",
-                                "split": "paged tree attention kernel (split-K entry, partition merge fused)",
-                                "whole": "paged tree attention kernel (whole-context entry"
-                                         + (", KV append fused)" if cfg.get("fuse_append") else ")"),
-                                "shared": "paged tree attention kernel (shared-prefix entry: each group's "
-                                          "prefix partition once, partition merge fused)"}[cfg["mode"]],
-                     "algorithmic_bytes_per_launch": int(unique_per_launch),
-                     "timing": f"HIP events on the launch stream around {K} back-to-back attention "
-                               f"calls, run before the timed steps"},
+        "attention_ms": round(m["attn_ms"], 5),
+        "attention_us_warm": round(m["warm_ms"] * 1e3, 2),
+        "attention_us_per_call_events": m["pct_us"],
+        "kv_append_ms": None if m["append_ms"] is None else round(m["append_ms"], 5),
+        "host_enqueue_ms_per_step": round(m["enqueue_ms"], 5),
+        "clock_settle": {"untimed_steps": m["n_settle"], "ms": round(m["settle_ms"], 1)},
+        "attention_tflops": round(c["tflops"], 3),
+        "roofline": roofline,
         "kernel_source_hash": src_hash,
     }
+    if calib is not None:
+        result["device_ceilings"] = calib
+    parity_ok = True
     if not args.no_cpu_baseline:
-        w0 = sets[order[-1]].w
-        run_attention(psv, sets[order[-1]], cfg)
-        torch.cuda.synchronize()
-        gpu_out = sets[order[-1]].out.to(torch.float64).cpu().numpy()
+        ds = sets[m["order"][-1]]
+        gpu_out = timed_output(torch, ds)
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w0, gpu_out)
+        cb = cpu_baseline(ds.w, gpu_out)
+        tol = TOLERANCE[ds.w.spec.kv_dtype]
+        cb["compared_with"] = "output of the timed call (" + kernel + ")"
+        cb["tolerance"] = tol
+        parity_ok = cb["max_abs_diff_vs_gpu"] <= tol
+        cb["parity_ok"] = bool(parity_ok)
+        result["cpu_baseline"] = cb
     if sets[0].w.q.shape[1] > 1:
-        result["accept_commit"] = time_accept_commit(psv, torch, sets[order[-1]], K)
+        result["accept_commit"] = time_accept_commit(psv, torch, sets[m["order"][-1]], K)
+    if extras:
+        del sets
+        torch.cuda.empty_cache()
+        result["workloads"] = {}
+        for other in EXTRA_WORKLOADS:
+            print(f"[bench] extra workload {other}", file=sys.stderr, flush=True)
+            r = extra_workload(psv, torch, other, args)
+            parity_ok = parity_ok and r["parity_ok"]
+            result["workloads"][other] = r
+    result["parity_ok"] = bool(parity_ok)
     print(json.dumps(result), flush=True)
+    if not parity_ok:
+        print("[bench] a timed call's output is outside the parity tolerance against the oracle",
+              file=sys.stderr, flush=True)
+        return 3
     return 0
 
 

@@ -8,7 +8,9 @@
  * enqueued asynchronously on `stream` (a hipStream_t; NULL = default stream).
  * Errors are returned as a status, never thrown: all host-checkable errors
  * are detected before any HIP call is made; a failed launch returns
- * PTA_ERR_HIP.  The library has no global mutable state.
+ * PTA_ERR_HIP.  Global state: a per-device table of kernel occupancies,
+ * filled on the first launch on each device (idempotent, so calls from
+ * several threads are safe); nothing else persists between calls.
  *
  * What is computed (sources: the TACO-LLM pages):
  *   - KV cache split into fixed-size blocks of tokens; each sequence's

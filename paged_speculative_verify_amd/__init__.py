@@ -25,6 +25,8 @@ from ._lib import (  # noqa: F401
     taco_paged_tree_attn_shared_prefix,
     taco_paged_tree_attn_splitk,
     taco_paged_tree_attn_splitk_workspace_size,
+    taco_pta_calib_mfma_bf16,
+    taco_pta_calib_stream_read,
     taco_pta_status_string,
     taco_pta_validate,
     taco_pta_version,

@@ -95,6 +95,10 @@ def load() -> ctypes.CDLL:
     lib.taco_pta_status_string.restype = ctypes.c_char_p
     lib.taco_pta_version.argtypes = []
     lib.taco_pta_version.restype = I32
+    lib.taco_pta_calib_stream_read.argtypes = [P, SZ, P, I32, P]
+    lib.taco_pta_calib_stream_read.restype = ctypes.c_int
+    lib.taco_pta_calib_mfma_bf16.argtypes = [I32, I32, P, P]
+    lib.taco_pta_calib_mfma_bf16.restype = ctypes.c_int
     lib.taco_la_create.argtypes = [I32, I32]
     lib.taco_la_create.restype = P
     lib.taco_la_destroy.argtypes = [P]
@@ -463,6 +467,29 @@ def taco_pta_validate(block_tables, ctx_lens, q_lens, max_q_len, num_blocks, max
     _check(lib.taco_pta_validate(ctypes.byref(dims), _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens),
                                  _ptr(flags), _stream(stream)))
     return int(flags.item())
+
+
+def taco_pta_calib_stream_read(buf, sink, workgroups: int, stream=None) -> None:
+    """Streaming read of every byte of buf (a contiguous device tensor; its size a multiple of
+    16 KiB) by `workgroups` workgroups; sink: int32 device tensor of at least `workgroups`."""
+    torch = _torch()
+    _need(buf, "buf")
+    _need(sink, "sink", dtype=torch.int32, device=buf.device)
+    if sink.numel() < workgroups:
+        raise ValueError("sink needs one word per workgroup")
+    _check(load().taco_pta_calib_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                             workgroups, _stream(stream)))
+
+
+def taco_pta_calib_mfma_bf16(workgroups: int, iters: int, sink, stream=None) -> int:
+    """bf16 matrix-core loop; returns the flops one launch performs.  sink: float32 device
+    tensor of at least `workgroups`."""
+    torch = _torch()
+    _need(sink, "sink", dtype=torch.float32)
+    if sink.numel() < workgroups:
+        raise ValueError("sink needs one word per workgroup")
+    _check(load().taco_pta_calib_mfma_bf16(workgroups, iters, sink.data_ptr(), _stream(stream)))
+    return workgroups * 4 * iters * 4 * 32 * 32 * 16 * 2
 
 
 def taco_pta_status_string(status: int) -> str:

@@ -300,19 +300,23 @@ struct PartSlot {
 // its normalised partial output and log-sum-exp are stored with
 // store_coherent.  The last unit of (b, hkv) to arrive merges the partitions
 // of all its rows and resets the arrival counter to zero for the next call.
+// Ordering through the memory model: every thread's agent-scope release fence
+// orders its partial stores before the workgroup barrier, and the barrier
+// before thread 0's acq_rel arrival at agent scope; in the last arriver, that
+// arrival (acquire) and the barrier come before every thread's agent-scope
+// acquire fence, which comes before its partial loads.
 template <typename QT, int D>
 __device__ __forceinline__ void splitk_finish(const AttnArgs& a, int b, int hkv, int C, int qb) {
   __shared__ int s_last;
-  __builtin_amdgcn_s_waitcnt(0);            // this thread's partial stores have completed
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   const int np = (C + a.part_tokens - 1) / a.part_tokens;
   int32_t* cnt = a.counters + (int64_t)b * a.Hkv + hkv;
   if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
+    s_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
   __syncthreads();
   if (!s_last) return;
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   auto slot = [&](int r, int p) {
     const int h = hkv * a.G + r / qb, i = r % qb;
     const int64_t prow = (((int64_t)b * a.Hq + h) * a.Qmax + i) * a.num_parts + p;

@@ -43,8 +43,10 @@
 //                           end to end and every wave takes an equal
 //                           contiguous slice, so ragged context lengths cost
 //                           no load imbalance.  A slice that ends inside a
-//                           unit leaves a partial that the unit's last slice
-//                           merges.
+//                           unit leaves a partial in the workspace, and a
+//                           second launch on the same stream
+//                           (slice_merge_kernel) merges each unit's partials
+//                           in slice order; no counters.
 #include "pta_device.h"
 #include "pta_flash.h"
 #include "pta_launch.h"
@@ -315,7 +317,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // a follower within reach of its leader (the leader counts exactly these) leaves the
     // partition to it; any other sequence works its own partition 0
     const int lead = a.prefix_leader[b];
-    if (lead >= 0 && lead < b && b - lead < a.max_group) {
+    // (a leader that does not lead itself leaves its would-be followers to work their own
+    // partition 0: a malformed leader array degrades to ordinary split-K, never to a lost row)
+    if (lead >= 0 && lead < b && b - lead < a.max_group && a.prefix_leader[lead] == lead) {
       bool chain = true;                 // every sequence between the leader and b follows it too
       for (int t = lead + 1; t < b; ++t) chain = chain && a.prefix_leader[t] == lead;
       if (chain) return;
@@ -506,18 +510,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 // ---------------------------------------------------------------- launchers
 // Workgroups of stream_attn_kernel<KT, D, RB, NW> resident on the current
-// device at once (compute units times occupancy), asked once per process.
+// device at once (compute units times occupancy).  Looked up once per device
+// and kept in a per-device table (every thread that fills an entry writes the
+// same value, so concurrent first calls are harmless); 0 when unknown.
+constexpr int kMaxDevices = 64;
 template <typename KT, int D, int RB, int NW>
 static int resident_workgroups() {
-  static const int n = [] {
-    int dev = 0, cus = 0, per = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, stream_attn_kernel<KT, D, RB, NW>, NW * 64, 0) !=
-            hipSuccess)
-      return 0;
-    return cus * per;
-  }();
+  static int cache[kMaxDevices];          // 0 = not looked up yet
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (c > 0) return c;
+  }
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, stream_attn_kernel<KT, D, RB, NW>, NW * 64, 0) !=
+          hipSuccess)
+    return 0;
+  const int n = cus * per;
+  if (dev >= 0 && dev < kMaxDevices) __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
   return n;
 }
 

@@ -168,3 +168,4 @@ def test_shared_prefix_host_checks(lib):
     assert f(dims(), ws=None) == NULLP
     assert f(dims(), ws=ctypes.c_void_p(0x10010)) == DIMS            # workspace 256-byte aligned
     assert f(dims(), nbytes=16) == WS
+

@@ -406,31 +406,91 @@ def test_empty_batch_and_errors(torch_cuda):
 
 
 # -------------------------------------------------------------- full-size configs, sampled sequences
+# (case id, workload, entry override or None for the workload's launch configuration, split, sampled sequences)
 FULL = [
-    ("llama3_8b_decode", [0, 17, 42, 63]),
-    ("llama31_70b_verify", [0, 9, 31]),
-    ("long_splitk_verify", [1]),
-    ("fp8_kv_chain", [0, 77, 127]),
-    ("shared_prefix_decode", [0, 9, 63]),
+    ("llama3_8b_decode", "llama3_8b_decode", None, None, [0, 17, 42, 63]),
+    ("llama31_70b_verify", "llama31_70b_verify", None, None, [0, 5, 9, 17, 24, 31]),
+    ("long_splitk_verify", "long_splitk_verify", None, None, [1, 2]),
+    # fixed 2048-token partitions: up to 64 partials per (sequence, KV head) merged in the launch
+    ("long_splitk_verify_split2048", "long_splitk_verify", "split", 2048, [0, 3]),
+    ("fp8_kv_chain", "fp8_kv_chain", None, None, [0, 31, 64, 77, 100, 127]),
+    ("shared_prefix_decode", "shared_prefix_decode", None, None, [0, 9, 63]),
 ]
 
 
-@pytest.mark.parametrize("name,seqs", FULL, ids=[f[0] for f in FULL])
-def test_full_size_sampled(torch_cuda, name, seqs):
+@pytest.mark.parametrize("cid,name,mode,split,seqs", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(torch_cuda, cid, name, mode, split, seqs):
     import bench
     w = make(name)
     cfg = bench.launch_config(name)
-    say("full", name, "entry", cfg["mode"], "split", cfg["split"], "path", cfg["path"], "sampled seqs", seqs)
+    if mode is not None:
+        cfg["mode"], cfg["split"] = mode, split
+    say("full", cid, "entry", cfg["mode"], "split", cfg["split"], "path", cfg["path"], "sampled seqs", seqs)
     out, lse = run_gpu(torch_cuda, w, split=cfg["split"], path=cfg["path"], mode=cfg["mode"])
     ref, ref_lse = run_oracle(w, rows=np.array(seqs))
     err = assert_parity(w, out, lse, ref, ref_lse, seqs=np.array(seqs))
-    say("full", name, "max abs err", err)
+    say("full", cid, "max abs err", err)
     # every other row is finite and every padding row untouched
     B = w.q.shape[0]
     for b in range(B):
         qb = int(w.q_lens[b])
         assert np.isfinite(out[b, :qb]).all()
         assert np.isnan(out[b, qb:]).all()
+
+
+# The exact prepared call bench.py times (entry, kernel family, KV append fused into the launch or
+# launched before it), at the workload's full size, on the same input set the bench builds first.
+# The candidates' cache slots are poisoned before the step, so a step whose append did not run,
+# or ran after the pages were read, fails.
+TIMED = [
+    ("llama3_8b_decode", [0, 17, 42, 63]),
+    ("shared_prefix_decode", [0, 9, 63]),
+    ("llama31_70b_verify", [0, 9, 31]),
+    ("long_splitk_verify", [0, 3]),
+    ("fp8_kv_chain", [0, 77, 127]),
+]
+
+
+@pytest.mark.parametrize("name,seqs", TIMED, ids=[t[0] for t in TIMED])
+def test_full_size_timed_call(torch_cuda, name, seqs):
+    import argparse
+
+    import torch
+    import bench
+    import paged_speculative_verify_amd as psv
+    cfg = bench.resolve_cfg(name, argparse.Namespace(path=None, split=None, shared_entry=False,
+                                                     private_pages=False, separate_append=False))
+    say("timed", name, "entry", cfg["mode"], "fused append", bool(cfg.get("fuse_append")), "seqs", seqs)
+    ds = bench.build_sets(psv, torch, name, cfg, 1)[0]
+    w, d = ds.w, ds.d
+    pages, offs = [], []
+    for b in range(w.q.shape[0]):
+        for t in range(int(w.ctx_lens[b]) - int(w.q_lens[b]), int(w.ctx_lens[b])):
+            pages.append(int(w.block_tables[b, t // 16]))
+            offs.append(t % 16)
+    P = torch.tensor(pages, dtype=torch.int64, device=d.q.device)
+    O = torch.tensor(offs, dtype=torch.int64, device=d.q.device)
+    poison = 0x7F if w.spec.kv_dtype == "fp8" else float("nan")
+    d.k_cache[P, :, O] = poison
+    d.v_cache[P, :, O] = poison
+    ds.out.fill_(float("nan"))
+    ds.lse.fill_(float("nan"))
+    ds.append_call()
+    ds.attn_call()
+    torch.cuda.synchronize()
+    view = torch.uint8 if w.spec.kv_dtype == "fp8" else torch.int16
+    for cache, host in ((d.k_cache, w.k_cache), (d.v_cache, w.v_cache)):
+        got = cache[P, :, O].contiguous().view(view).cpu().numpy()
+        want = np.stack([host[p, :, o] for p, o in zip(pages, offs)])
+        assert np.array_equal(got.view(np.uint8), np.ascontiguousarray(want).view(np.uint8)), "candidate rows"
+    out = out_to_f64(ds.out)
+    lse = ds.lse.cpu().numpy().astype(np.float64)
+    ref, ref_lse = run_oracle(w, rows=np.array(seqs))
+    err = assert_parity(w, out, lse, ref, ref_lse, seqs=np.array(seqs))
+    say("timed", name, "max abs err", err)
+    for b in range(w.q.shape[0]):
+        qb = int(w.q_lens[b])
+        assert np.isfinite(out[b, :qb]).all() and np.isnan(out[b, qb:]).all()
 
 
 # The whole-context stream grid takes its sequences in an order of their context lengths: long/short
