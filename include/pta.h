@@ -10,7 +10,10 @@
  * are detected before any HIP call is made; a failed launch returns
  * PTA_ERR_HIP.  Global state: a per-device table of kernel occupancies,
  * filled on the first launch on each device (idempotent, so calls from
- * several threads are safe); nothing else persists between calls.
+ * several threads are safe), and the device array behind
+ * taco_paged_tree_attn_balanced_noalloc (PTA_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the library's first use on that GPU until the process ends);
+ * nothing else persists between calls.
  *
  * What is computed (sources: the TACO-LLM pages):
  *   - KV cache split into fixed-size blocks of tokens; each sequence's
@@ -235,6 +238,34 @@ pta_status taco_paged_tree_attn_balanced(const pta_dims* dims, const void* q, co
                                          const uint8_t* tree_mask, float scale, void* out,
                                          float* lse, void* workspace, size_t workspace_bytes,
                                          void* stream);
+
+/* Largest balanced-entry workspace, in bytes, that
+ * taco_paged_tree_attn_balanced_noalloc can serve (64 MiB). */
+#define PTA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* taco_paged_tree_attn_balanced for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same kernels, same results and same arguments, minus the
+ * workspace: it lives in a library-owned device array of
+ * PTA_NOALLOC_SCRATCH_BYTES bytes per GPU.  The call allocates, frees and
+ * synchronises nothing.
+ *   - Needs taco_paged_tree_attn_balanced_workspace_size(dims) <=
+ *     PTA_NOALLOC_SCRATCH_BYTES, else PTA_ERR_WORKSPACE_TOO_SMALL (the
+ *     workloads this library is measured on take at most about 59 MB).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents; it needs no initialisation (the grid writes every
+ *     partial before the merge launch reads it).  Calls that may overlap on
+ *     one GPU (other streams, other host threads) RACE and give undefined
+ *     results; calls issued in order on one stream are safe.
+ *   - The first call on a device looks up the address of that device's copy
+ *     with the device current (a failure returns PTA_ERR_HIP).
+ * Other arguments, semantics and errors as taco_paged_tree_attn_balanced. */
+pta_status taco_paged_tree_attn_balanced_noalloc(const pta_dims* dims, const void* q, const void* k_cache,
+                                                 const void* v_cache, const float* k_scale,
+                                                 const float* v_scale, const int32_t* block_tables,
+                                                 const int32_t* ctx_lens, const int32_t* q_lens,
+                                                 const uint8_t* tree_mask, float scale, void* out,
+                                                 float* lse, void* stream);
 
 /* KV append: write num_tokens new K/V rows into their cache slots, as blocks
  * are handed out while tokens are generated (Paged Attention section of the

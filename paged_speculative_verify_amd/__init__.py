@@ -18,7 +18,9 @@ from ._lib import (  # noqa: F401
     taco_accept_commit,
     taco_kv_append,
     taco_la_tree_mask,
+    NOALLOC_SCRATCH_BYTES,
     taco_paged_tree_attn_balanced,
+    taco_paged_tree_attn_balanced_noalloc,
     taco_paged_tree_attn_balanced_workspace_size,
     taco_paged_tree_attn,
     taco_paged_tree_attn_append,

@@ -85,6 +85,8 @@ def load() -> ctypes.CDLL:
     lib.taco_paged_tree_attn_balanced_workspace_size.restype = SZ
     lib.taco_paged_tree_attn_balanced.argtypes = [D, P, P, P, P, P, P, P, P, P, F, P, P, P, SZ, P]
     lib.taco_paged_tree_attn_balanced.restype = ctypes.c_int
+    lib.taco_paged_tree_attn_balanced_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, F, P, P, P]
+    lib.taco_paged_tree_attn_balanced_noalloc.restype = ctypes.c_int
     lib.taco_kv_append.argtypes = [D, P, P, I32, P, I32, P, P, P, P, P]
     lib.taco_kv_append.restype = ctypes.c_int
     lib.taco_accept_commit.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
@@ -374,6 +376,27 @@ def taco_paged_tree_attn_balanced(q, k_cache, v_cache, block_tables, ctx_lens, q
         ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask), float(scale), _ptr(out),
         _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+# PTA_NOALLOC_SCRATCH_BYTES of include/pta.h
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def taco_paged_tree_attn_balanced_noalloc(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask,
+                                          scale, out=None, lse=None, k_scale=None, v_scale=None,
+                                          max_ctx_len=None, path="auto", stream=None):
+    """taco_paged_tree_attn_balanced with the library's own per-GPU scratch array as the workspace
+    (no allocation by the library; see include/pta.h for the size limit and the rule that calls
+    overlapping on one GPU race).  Allocates out/lse here only when they are not given."""
+    lib = load()
+    _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale)
+    out, lse = _alloc_out(q, out, lse)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    _check(lib.taco_paged_tree_attn_balanced_noalloc(
+        ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask), float(scale), _ptr(out),
+        _ptr(lse), _stream(stream)))
     return out
 
 

@@ -213,6 +213,76 @@ pta_status balanced_layout(const pta_dims* d, const Plan& p, BalancedLayout* L) 
   return PTA_OK;
 }
 
+// ---- allocation-free balanced entry: the workspace lives in this file-scope
+// device array, one copy per GPU (each device that loads the library holds it
+// until the process ends).  Host code never passes `scratch` itself to a
+// kernel (its host-side name is only a handle): the device address of the
+// current device's copy is looked up with hipGetSymbolAddress, once per device
+// with that device current, and that pointer is what the kernels receive.
+static __device__ __align__(256) char scratch[PTA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+void* g_scratch_ptr[kMaxScratchDevices];     // device address of each device's copy, or null
+
+pta_status scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PTA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return PTA_ERR_UNSUPPORTED;
+  void* p = __atomic_load_n(&g_scratch_ptr[dev], __ATOMIC_ACQUIRE);
+  if (p == nullptr) {
+    // every thread that races here gets the same address, so storing it twice is harmless
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return PTA_ERR_HIP;
+    __atomic_store_n(&g_scratch_ptr[dev], p, __ATOMIC_RELEASE);
+  }
+  *out = p;
+  return PTA_OK;
+}
+
+// Balanced entry body: workspace from the caller, or (noalloc) this device's
+// copy of `scratch`, whose size is the limit.
+pta_status balanced_call(const pta_dims* d, const void* q, const void* k_cache, const void* v_cache,
+                         const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                         const int32_t* ctx_lens, const int32_t* q_lens, const uint8_t* tree_mask, float scale,
+                         void* out, float* lse, void* workspace, size_t workspace_bytes, bool noalloc,
+                         hipStream_t stream) {
+  pta_status st = check_dims(d);
+  if (st != PTA_OK) return st;
+  if (!isfinite(scale)) return PTA_ERR_BAD_DIMS;
+  Plan p;
+  st = plan_for(d, &p);
+  if (st != PTA_OK) return st;
+  if (p.fam != FAM_STREAM && !(p.fam == FAM_TILE && d->kv_dtype == PTA_BF16)) return PTA_ERR_UNSUPPORTED;
+  if (d->num_seqs == 0) return PTA_OK;
+  st = check_attn_ptrs(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
+                       tree_mask, out);
+  if (st != PTA_OK) return st;
+  if (!noalloc) {
+    if (workspace == nullptr) return PTA_ERR_NULL_PTR;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return PTA_ERR_BAD_DIMS;
+  }
+  BalancedLayout L;
+  st = balanced_layout(d, p, &L);
+  if (st != PTA_OK) return st;
+  if (workspace_bytes < L.total) return PTA_ERR_WORKSPACE_TOO_SMALL;
+  if (noalloc) {
+    st = scratch_for_current_device(&workspace);
+    if (st != PTA_OK) return st;
+  }
+  AttnArgs a = make_args(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
+                         tree_mask, scale, out, lse);
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.counters = nullptr;                  // both balanced grids merge in a second launch
+  a.part_o = reinterpret_cast<float*>(ws + L.o_off);
+  a.part_lse = reinterpret_cast<float*>(ws + L.lse_off);
+  a.total_waves = L.nwg * L.nw;
+  int nwg = L.nwg;
+  if (p.fam == FAM_TILE)
+    return tile_balanced(&a, d->head_dim, L.nw, d->num_seqs, &nwg, stream) == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+  return stream_balanced(&a, d->kv_dtype, d->head_dim, p.rb, L.nw, d->num_seqs, &nwg, stream) == hipSuccess
+             ? PTA_OK
+             : PTA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -372,39 +442,18 @@ pta_status taco_paged_tree_attn_balanced(const pta_dims* d, const void* q, const
                                          const int32_t* ctx_lens, const int32_t* q_lens,
                                          const uint8_t* tree_mask, float scale, void* out, float* lse,
                                          void* workspace, size_t workspace_bytes, void* stream) {
-  pta_status st = check_dims(d);
-  if (st != PTA_OK) return st;
-  if (!isfinite(scale)) return PTA_ERR_BAD_DIMS;
-  Plan p;
-  st = plan_for(d, &p);
-  if (st != PTA_OK) return st;
-  if (p.fam != FAM_STREAM && !(p.fam == FAM_TILE && d->kv_dtype == PTA_BF16)) return PTA_ERR_UNSUPPORTED;
-  if (d->num_seqs == 0) return PTA_OK;
-  st = check_attn_ptrs(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
-                       tree_mask, out);
-  if (st != PTA_OK) return st;
-  if (workspace == nullptr) return PTA_ERR_NULL_PTR;
-  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return PTA_ERR_BAD_DIMS;
-  BalancedLayout L;
-  st = balanced_layout(d, p, &L);
-  if (st != PTA_OK) return st;
-  if (workspace_bytes < L.total) return PTA_ERR_WORKSPACE_TOO_SMALL;
-  AttnArgs a = make_args(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
-                         tree_mask, scale, out, lse);
-  char* ws = reinterpret_cast<char*>(workspace);
-  a.counters = nullptr;                  // both balanced grids merge in a second launch
-  a.part_o = reinterpret_cast<float*>(ws + L.o_off);
-  a.part_lse = reinterpret_cast<float*>(ws + L.lse_off);
-  a.total_waves = L.nwg * L.nw;
-  int nwg = L.nwg;
-  if (p.fam == FAM_TILE)
-    return tile_balanced(&a, d->head_dim, L.nw, d->num_seqs, &nwg, (hipStream_t)stream) == hipSuccess
-               ? PTA_OK
-               : PTA_ERR_HIP;
-  return stream_balanced(&a, d->kv_dtype, d->head_dim, p.rb, L.nw, d->num_seqs, &nwg, (hipStream_t)stream) ==
-                 hipSuccess
-             ? PTA_OK
-             : PTA_ERR_HIP;
+  return balanced_call(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens, tree_mask, scale,
+                       out, lse, workspace, workspace_bytes, false, (hipStream_t)stream);
+}
+
+pta_status taco_paged_tree_attn_balanced_noalloc(const pta_dims* d, const void* q, const void* k_cache,
+                                                 const void* v_cache, const float* k_scale,
+                                                 const float* v_scale, const int32_t* block_tables,
+                                                 const int32_t* ctx_lens, const int32_t* q_lens,
+                                                 const uint8_t* tree_mask, float scale, void* out, float* lse,
+                                                 void* stream) {
+  return balanced_call(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens, tree_mask, scale,
+                       out, lse, nullptr, PTA_NOALLOC_SCRATCH_BYTES, true, (hipStream_t)stream);
 }
 
 pta_status taco_kv_append(const pta_dims* d, const void* k_new, const void* v_new,

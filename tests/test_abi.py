@@ -169,3 +169,25 @@ def test_shared_prefix_host_checks(lib):
     assert f(dims(), ws=ctypes.c_void_p(0x10010)) == DIMS            # workspace 256-byte aligned
     assert f(dims(), nbytes=16) == WS
 
+
+def test_noalloc_host_checks(lib):
+    """The allocation-free balanced entry rejects bad arguments on the host, before any HIP call,
+    and the scratch size the binding states is the header's."""
+    import os
+    import re
+    hdr = open(os.path.join(os.path.dirname(psv._lib.HEADER), "pta.h"), encoding="utf-8").read()
+    m = re.search(r"#define PTA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == psv.NOALLOC_SCRATCH_BYTES
+    f = lib.taco_paged_tree_attn_balanced_noalloc
+    call = lambda d, q=FAKE, out=FAKE, mask=FAKE, scale=0.1: f(
+        ctypes.byref(d) if d is not None else None, q, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, mask, scale,
+        out, None, None)
+    assert call(None) == NULLP
+    assert call(dims(head_dim=96)) == DIMS
+    assert call(dims(), scale=float("inf")) == DIMS
+    assert call(dims(q_dtype=0, kv_dtype=1)) == DTYPE
+    assert call(dims(), q=None) == NULLP
+    assert call(dims(), out=None) == NULLP
+    assert call(dims(max_q_len=4), mask=None) == NULLP
+    assert call(dims(q_dtype=0, kv_dtype=0, path=1)) == UNSUP      # vector-ALU rows: no balanced grid
+    assert call(dims(num_seqs=0)) == OK
