@@ -564,7 +564,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="measure only --config (no calibration kernels, no other workloads)")
-    ap.add_argument("--path", choices=["auto", "valu", "mfma", "tile"], default=None,
+    ap.add_argument("--path", choices=["auto", "valu", "mfma", "tile", "tile16"], default=None,
                     help="override the kernel family of the workload's launch configuration")
     ap.add_argument("--split", type=int, default=None,
                     help="override the entry point: split-K partition length, 0 = one pass per "

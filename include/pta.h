@@ -91,8 +91,18 @@ typedef enum { PTA_F32 = 0, PTA_BF16 = 1, PTA_FP8_E4M3FN = 2 } pta_dtype;
 /* Kernel family selection.  AUTO picks per call from the rows per KV head
  * (G * max_q_len): vector ALU for small row counts, MFMA otherwise.  TILE
  * forces the shared-tile matrix-core family (every wave of a workgroup reads
- * the same LDS pages) for any row count up to 256 with bf16 q. */
-typedef enum { PTA_PATH_AUTO = 0, PTA_PATH_VALU = 1, PTA_PATH_MFMA = 2, PTA_PATH_TILE = 3 } pta_path;
+ * the same LDS pages) for any row count up to 256 with bf16 q.  TILE16 is TILE
+ * with the balanced entry's shared-tile grid held to its 16x16x32-product
+ * kernel (the one also used when a bf16 cache tensor exceeds 4 GiB; otherwise
+ * the balanced entry runs the 32x32x16-product kernel); same results within
+ * rounding. */
+typedef enum {
+  PTA_PATH_AUTO = 0,
+  PTA_PATH_VALU = 1,
+  PTA_PATH_MFMA = 2,
+  PTA_PATH_TILE = 3,
+  PTA_PATH_TILE16 = 4
+} pta_path;
 
 typedef struct {
   int32_t num_seqs;            /* B >= 0 (0 is a no-op) */

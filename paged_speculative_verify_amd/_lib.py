@@ -19,7 +19,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HEADER = os.path.join(INCLUDE, "pta.h")
 
 PTA_F32, PTA_BF16, PTA_FP8_E4M3FN = 0, 1, 2
-PATHS = {"auto": 0, "valu": 1, "mfma": 2, "tile": 3}
+PATHS = {"auto": 0, "valu": 1, "mfma": 2, "tile": 3, "tile16": 4}
 STATUS = {0: "PTA_OK", 1: "PTA_ERR_NULL_PTR", 2: "PTA_ERR_BAD_DIMS", 3: "PTA_ERR_BAD_DTYPE",
           4: "PTA_ERR_UNSUPPORTED", 5: "PTA_ERR_WORKSPACE_TOO_SMALL", 6: "PTA_ERR_HIP"}
 

@@ -39,7 +39,7 @@ pta_status check_dims(const pta_dims* d) {
   if (d->num_blocks < 1) return PTA_ERR_BAD_DIMS;
   if (d->reserved != 0) return PTA_ERR_BAD_DIMS;
   if (!dtype_ok(d->q_dtype, d->kv_dtype)) return PTA_ERR_BAD_DTYPE;
-  if (d->path < PTA_PATH_AUTO || d->path > PTA_PATH_TILE) return PTA_ERR_BAD_DIMS;
+  if (d->path < PTA_PATH_AUTO || d->path > PTA_PATH_TILE16) return PTA_ERR_BAD_DIMS;
   return PTA_OK;
 }
 
@@ -65,7 +65,7 @@ pta_status plan_for(const pta_dims* d, Plan* p) {
   const bool mfma_ok = d->q_dtype == PTA_BF16 && rows <= kMfmaMaxRows;
   bool mfma;
   p->rows_pow2 = pow2_at_least(rows);
-  if (d->path == PTA_PATH_TILE) {
+  if (d->path == PTA_PATH_TILE || d->path == PTA_PATH_TILE16) {
     if (!mfma_ok) return PTA_ERR_UNSUPPORTED;
     p->fam = FAM_TILE;
     p->nw = max(2, pow2_at_least((rows + 31) / 32));
@@ -168,13 +168,31 @@ struct BalancedLayout {
 
 constexpr int kBalancedMaxSeqs = 16383;   // sequence page prefix lives in LDS
 
+// The balanced shared-tile grid runs the 32x32x16-product kernel (pta_wide.hip)
+// unless the caller holds it to the 16x16x32 one or a cache tensor is too large
+// for its 32-bit buffer offsets (the tile past the last one must still be
+// addressable: offsets stay below 2^32).
+bool wide_tiles(const pta_dims* d) {
+  const uint64_t tile = (uint64_t)kPage * (uint64_t)d->head_dim * 2u;
+  return d->path != PTA_PATH_TILE16 &&
+         (uint64_t)d->num_blocks * (uint64_t)d->num_kv_heads * tile + tile <= 0xFFFFFFFFull;
+}
+
+hipError_t balanced_tiles(const pta_dims* d, const AttnArgs* a, int nw, int* nwg, hipStream_t s) {
+  return wide_tiles(d) ? wide_balanced(a, d->head_dim, nw, d->num_seqs, nwg, s)
+                       : tile_balanced(a, d->head_dim, nw, d->num_seqs, nwg, s);
+}
+
 pta_status tile_balanced_layout(const pta_dims* d, BalancedLayout* L) {
   const int rows = (d->num_q_heads / d->num_kv_heads) * d->max_q_len;
   const int waves = (rows + 31) / 32;
+  // at most 4 waves per row group: two 4-wave workgroups per compute unit overlap one's
+  // barrier waits with the other's work (one 8-wave workgroup of 256 rows per compute
+  // unit, which loads every page tile into LDS once, measured no faster on the widest tree)
   const int nw = waves <= 2 ? 2 : 4;
   const int rg = (waves + nw - 1) / nw;
   int fit = 0;
-  if (tile_balanced(nullptr, d->head_dim, nw, d->num_seqs, &fit, nullptr) != hipSuccess) return PTA_ERR_HIP;
+  if (balanced_tiles(d, nullptr, nw, &fit, nullptr) != hipSuccess) return PTA_ERR_HIP;
   const int ns = (fit / rg) & ~7;
   if (ns < 8) return PTA_ERR_UNSUPPORTED;
   const int64_t units = (int64_t)d->num_seqs * d->num_kv_heads;
@@ -276,8 +294,7 @@ pta_status balanced_call(const pta_dims* d, const void* q, const void* k_cache, 
   a.part_lse = reinterpret_cast<float*>(ws + L.lse_off);
   a.total_waves = L.nwg * L.nw;
   int nwg = L.nwg;
-  if (p.fam == FAM_TILE)
-    return tile_balanced(&a, d->head_dim, L.nw, d->num_seqs, &nwg, stream) == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+  if (p.fam == FAM_TILE) return balanced_tiles(d, &a, L.nw, &nwg, stream) == hipSuccess ? PTA_OK : PTA_ERR_HIP;
   return stream_balanced(&a, d->kv_dtype, d->head_dim, p.rb, L.nw, d->num_seqs, &nwg, stream) == hipSuccess
              ? PTA_OK
              : PTA_ERR_HIP;

@@ -26,6 +26,9 @@ hipError_t launch_tile(const AttnArgs& a, int kv_dtype, int head_dim, int nwr, d
 // per slice.  With a == nullptr, *nwg receives the workgroups that fit the
 // device at once; otherwise *nwg workgroups are launched.
 hipError_t tile_balanced(const AttnArgs* a, int head_dim, int nwr, int B, int* nwg, hipStream_t s);
+// The same grid with the 32x32x16-product pipeline (pta_wide.hip), nwr in
+// {2, 4, 8}; needs every bf16 cache tensor below 4 GiB (32-bit buffer offsets).
+hipError_t wide_balanced(const AttnArgs* a, int head_dim, int nwr, int B, int* nwg, hipStream_t s);
 // Second launch of both balanced grids: merge of the slice partials (bf16 out),
 // NS = slices of the attention launch.
 hipError_t launch_slice_merge(const AttnArgs& a, int head_dim, int NS, hipStream_t s);

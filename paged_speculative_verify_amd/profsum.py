@@ -37,13 +37,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 KERNEL_SOURCES = ["pta_device.h", "pta_flash.h", "pta_launch.h", "pta_valu.hip", "pta_stream.hip",
-                  "pta_tile.hip", "pta_aux.hip", "pta_api.hip"]
+                  "pta_tile.hip", "pta_wide.hip", "pta_aux.hip", "pta_api.hip"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30                      # bench.py --copy-calibration copies 1 GiB
 # every kernel an attention call launches (the balanced entry launches its grid, then
 # slice_merge_kernel)
 ATTN_KERNELS = ("stream_attn_kernel", "stream_balanced_kernel", "tile_dma_kernel", "tile_balanced_kernel",
-                "tile_attn_kernel", "valu_attn_kernel", "slice_merge_kernel")
+                "wide_balanced_kernel", "tile_attn_kernel", "valu_attn_kernel", "slice_merge_kernel")
 
 
 def kernel_source_hash() -> str:

@@ -63,7 +63,7 @@ def test_dims_struct_layout():
     (dict(num_blocks=0), DIMS),
     (dict(num_seqs=-1), DIMS),
     (dict(reserved=1), DIMS),
-    (dict(path=4), DIMS),
+    (dict(path=5), DIMS),                        # past PTA_PATH_TILE16
     (dict(q_dtype=0, kv_dtype=0, path=3), UNSUP),  # the shared-tile family needs bf16 q
     (dict(q_dtype=0, kv_dtype=1), DTYPE),         # fp32 q with bf16 KV
     (dict(q_dtype=0, kv_dtype=2), DTYPE),

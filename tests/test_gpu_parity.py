@@ -233,6 +233,44 @@ def test_one_hot_indexing_bit_exact(torch_cuda, cid, sp, path):
         assert np.array_equal(out[..., :2][v], want[v]), (cid, split)
 
 
+@pytest.mark.parametrize("cid,sp,path", [
+    # 96 rows per KV head (G 8 x 12 candidates): the balanced shared-tile grid, 32x32x16 kernel
+    ("probe_bal_wide", spec("o", 3, 8, 1, 128, "bf16", "bf16", (12, 700), 12, "random", seed=46), "auto"),
+    ("probe_bal_wide_d64_rows64", spec("o", 3, 8, 1, 64, "bf16", "bf16", (8, 500), 6, "random", seed=47), "auto"),
+    ("probe_bal_tile16", spec("o", 3, 8, 1, 128, "bf16", "bf16", (12, 700), 12, "random", seed=48), "tile16"),
+], ids=["probe_bal_wide", "probe_bal_wide_d64_rows64", "probe_bal_tile16"])
+def test_one_hot_indexing_bit_exact_balanced(torch_cuda, cid, sp, path):
+    """The balanced entry's slices, page walk and slice merge read exactly the intended
+    (page, slot, head): every output equals its one dominant V row bit for bit."""
+    w, want = _probe_workload(sp)
+    say(cid)
+    out, _ = run_gpu(torch_cuda, w, mode="balanced", path=path, want_lse=False)
+    v = ~np.isnan(want[..., 0])
+    assert np.array_equal(out[..., :2][v], want[v]), cid
+
+
+@pytest.mark.parametrize("path,D", [("auto", 64), ("auto", 128), ("tile16", 128)])
+def test_mask_bit_exact_balanced(torch_cuda, path, D):
+    """The mask probe through the balanced shared-tile grid (256 rows per KV head)."""
+    from tests.test_oracle_pins import enc
+    w = make(spec("mb", 3, 16, 1, D, "bf16", "bf16", (20, 400), 16, "random", 5, seed=52))
+    say("mask probe balanced", path, D)
+    w.k_cache[...] = 0
+    w.v_cache[...] = 0
+    for b in range(3):
+        C, Qb = int(w.ctx_lens[b]), int(w.q_lens[b])
+        for j in range(Qb):
+            t = C - Qb + j
+            w.v_cache[w.block_tables[b, t // 16], :, t % 16, j] = enc(1.0, "bf16")
+    out, _ = run_gpu(torch_cuda, w, mode="balanced", path=path, want_lse=False)
+    for b in range(3):
+        Qb = int(w.q_lens[b])
+        got = out[b, :Qb, :, :Qb] > 0
+        want = (w.tree_mask[b, :Qb, :Qb] != 0)[:, None, :].repeat(out.shape[2], axis=1)
+        assert np.array_equal(got, want)
+        assert (out[b, :Qb, :, Qb:] == 0).all()
+
+
 @pytest.mark.parametrize("path", ["mfma", "valu"])
 def test_mask_bit_exact(torch_cuda, path):
     """K = 0, prefix V = 0, candidate j's V = e_j: out_i[j] > 0 exactly where the mask is set."""
@@ -676,6 +714,21 @@ def test_balanced_parity(torch_cuda, cid, sp):
     ref, ref_lse = run_oracle(w)
     err = assert_parity(w, out, lse, ref, ref_lse)
     say(cid, "max abs err", err)
+
+
+# the 16x16x32-product shared-tile kernel (path tile16; also what the balanced entry runs when a
+# cache tensor exceeds 4 GiB) on the shared-tile cases
+TILE16 = [c for c in BALANCED if c[0].startswith("bal_tile")]
+
+
+@pytest.mark.parametrize("cid,sp", TILE16, ids=[c[0] + "_tile16" for c in TILE16])
+def test_balanced_tile16_parity(torch_cuda, cid, sp):
+    w = make(sp, poison=True)
+    say(cid, "tile16")
+    out, lse = run_gpu(torch_cuda, w, mode="balanced", path="tile16")
+    ref, ref_lse = run_oracle(w)
+    err = assert_parity(w, out, lse, ref, ref_lse)
+    say(cid, "tile16 max abs err", err)
 
 
 def test_balanced_repeat_and_workspace_reuse(torch_cuda):
