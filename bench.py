@@ -553,6 +553,93 @@ def extra_workload(psv, torch, name, args):
     return res
 
 
+# ------------------------------------------------------------------ quantized GEMM
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+GEMM_SHAPES = {
+    # Llama-3.1-70B MLP gate + up projections (N = 2 x 28672, K = 8192) over the verify step's
+    # 512 candidate tokens (32 sequences x 16), and over a 64-sequence decode step
+    "llama70b_gate_up_verify512": (512, 57344, 8192),
+    "llama70b_gate_up_decode64": (64, 57344, 8192),
+}
+
+
+def gemm_bench(psv, torch, name, steps=30, warmup=5, cpu_rows=2, parity_rows=(0, 1, 255, 511)):
+    """W8A8 GEMM on one Llama-70B-shaped projection: timed calls (HIP events around back-to-back
+    calls), roofline against the fp8 matrix-core peak or HBM (whichever the shape's intensity
+    says bounds it), parity of sampled output rows against the fp64 oracle, the oracle timed on
+    a few rows."""
+    import oracle
+    from workload.gemm import make_w8a8_device
+    M, N, K = GEMM_SHAPES[name]
+    a, sa, w, sw = make_w8a8_device(M, N, K, seed=11, torch=torch)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    for _ in range(warmup):
+        psv.taco_gemm_w8a8(a, sa, w, sw, y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(8):
+            psv.taco_gemm_w8a8(a, sa, w, sw, y)
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        psv.taco_gemm_w8a8(a, sa, w, sw, y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2.0 * M * N * K
+    nbytes = M * K + N * K + 2 * M * N + 4 * (M + N)
+    tflops = flops / (ms / 1e3) / 1e12
+    gbs = nbytes / (ms / 1e3) / 1e9
+    intensity = flops / nbytes
+    ridge = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    bound = "mfma" if intensity > ridge else "hbm"
+    # parity: sampled rows of the timed call's output against the oracle
+    rows = np.array([r for r in parity_rows if r < M])
+    wc, wsc = w.cpu().numpy(), sw.cpu().numpy()
+    ac, asc = a[torch.from_numpy(rows).cuda()].cpu().numpy(), sa.cpu().numpy()[rows]
+    ref = oracle.w8a8_gemm(ac, asc, wc, wsc)
+    got = y[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    from oracle.formats import decode_fp8_e4m3fn
+    S = (np.abs(decode_fp8_e4m3fn(ac)) * asc.astype(np.float64)[:, None]) @ \
+        (np.abs(decode_fp8_e4m3fn(wc)) * wsc.astype(np.float64)[:, None]).T
+    excess = float((np.abs(got - ref) - (2.0 ** -8 * np.abs(ref) + 2.0 ** -14 * S)).max())
+    # the oracle on a few rows, all cores
+    from threadpoolctl import threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores, user_api="blas"):
+        t0 = time.perf_counter()
+        oracle.w8a8_gemm(ac[:cpu_rows], asc[:cpu_rows], wc, wsc)
+        t_cpu = time.perf_counter() - t0
+    res = {
+        "metric": "W8A8 GEMM TFLOP/s (fp8 e4m3fn operands, per-row scales, bf16 out), 1 GPU",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "higher_is_better": True, "data": "synthetic",
+        "dtype": "fp8-e4m3 x fp8-e4m3 -> f32 -> bf16",
+        "config": {"workload": name, "M": M, "N": N, "K": K},
+        "us_per_call": round(ms * 1e3, 2), "steps": steps, "warmup": warmup,
+        "roofline": {"bound": bound, "achieved": round(tflops if bound == "mfma" else gbs, 2),
+                     "peak": FP8_PEAK_TFLOPS if bound == "mfma" else HBM_PEAK_GBS,
+                     "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                     "frac": round(tflops / FP8_PEAK_TFLOPS if bound == "mfma" else gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "mfma_frac": round(tflops / FP8_PEAK_TFLOPS, 4),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": int(flops),
+                     "arithmetic_intensity_flop_per_byte": round(intensity, 1),
+                     "ridge_flop_per_byte": round(ridge, 1), "kernel": "gemm_w8a8_kernel",
+                     "timing": f"HIP events on the launch stream around {steps} back-to-back calls"},
+        "parity": {"rows": rows.tolist(), "max_excess_over_bound": excess, "parity_ok": bool(excess <= 0),
+                   "bound": "2^-8 |y_ref| + 2^-14 a_scale w_scale sum|a||w| per output"},
+        "cpu_baseline": {"value": round(2.0 * cpu_rows * N * K / t_cpu / 1e12, 6), "unit": "TFLOP/s",
+                         "cores": cores, "kind": "oracle",
+                         "sample": f"{cpu_rows} output rows x {N} columns, fp64 numpy, {t_cpu:.1f} s"},
+    }
+    del a, w, y
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------ main
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
@@ -583,6 +670,8 @@ def main(argv=None) -> int:
     ap.add_argument("--lookahead-cache", action="store_true",
                     help="instead of the bench line: the host lookahead cache (propose, budgets, append) "
                          "over a decode batch of synthetic token streams, one JSON line; needs no GPU")
+    ap.add_argument("--gemm", choices=sorted(GEMM_SHAPES), default=None,
+                    help="instead of the bench line: the W8A8 GEMM on one Llama-70B-shaped projection")
     ap.add_argument("--qlen-floor", action="store_true",
                     help="instead of the bench line: attention time against the number of candidates "
                          "per sequence at the decode shape, T(q_len) / T(1)")
@@ -615,6 +704,11 @@ def main(argv=None) -> int:
 
     if args.qlen_floor:
         return qlen_floor(psv, torch, args)
+
+    if args.gemm:
+        r = gemm_bench(psv, torch, args.gemm, steps=args.steps, warmup=args.warmup)
+        print(json.dumps(r), flush=True)
+        return 0 if r["parity"]["parity_ok"] else 3
 
     name = args.config
     cfg = resolve_cfg(name, args)
@@ -730,6 +824,13 @@ def main(argv=None) -> int:
             r = extra_workload(psv, torch, other, args)
             parity_ok = parity_ok and r["parity_ok"]
             result["workloads"][other] = r
+        result["quantized_gemm"] = {}
+        for g in sorted(GEMM_SHAPES):
+            print(f"[bench] W8A8 GEMM {g}", file=sys.stderr, flush=True)
+            r = gemm_bench(psv, torch, g, steps=min(args.steps, 20), warmup=args.warmup, cpu_rows=1)
+            parity_ok = parity_ok and r["parity"]["parity_ok"]
+            result["quantized_gemm"][g] = {k: r[k] for k in ("value", "unit", "us_per_call", "roofline", "parity",
+                                                             "cpu_baseline", "config")}
     result["parity_ok"] = bool(parity_ok)
     print(json.dumps(result), flush=True)
     if not parity_ok:

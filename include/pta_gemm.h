@@ -1,0 +1,54 @@
+/*
+ * libpta quantized GEMM operators (gfx950).
+ *
+ * The TACO-LLM pages list quantized GEMM operators next to the attention
+ * kernels (17173xz.com article, section "TACO-LLM如何实现降本增效?": W4A8,
+ * W4A16, W8A16 and W8A8 operators; 618zxw.cn article, section
+ * "LLM量子化技術による推論コストの削減": weight-aware rearrangement, task
+ * scheduling, fast dequantisation and integer scales for the GEMM and
+ * attention operators; design talk "大模型倍速推理引擎 TACO-LLM 的设计与实践",
+ * section "5. 支持 Quantization（模型量化）": weights held as INT8/FP8 to cut
+ * storage and bandwidth, run on low-precision matrix instructions).
+ *
+ * Computed (rounding aside), with A [M][K] the activations (one row per token)
+ * and W [N][K] the weights (one row per output channel):
+ *   W8A8:   Y[m][n] = a_scale[m] * w_scale[n] * sum_k A[m][k] * W[n][k],
+ *           A and W OCP fp8 e4m3fn codes, scales float32.
+ * Y is bf16 [M][N] row-major, rounded to nearest even from float32.
+ *
+ * Conventions as in pta.h: device pointers, caller-owned buffers, work
+ * enqueued asynchronously on `stream`, errors returned as pta_status before
+ * any HIP call when they can be checked on the host.
+ */
+#ifndef PTA_GEMM_H
+#define PTA_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pta.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* fp8 x fp8 GEMM on the fp8 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4),
+ * float32 accumulation, per-row activation and per-output-channel weight
+ * scales applied to the float32 sums.
+ *   a        uint8 [M][K]  e4m3fn codes, row-major, 16-byte aligned
+ *   a_scale  float [M]
+ *   w        uint8 [N][K]  e4m3fn codes, row-major, 16-byte aligned
+ *   w_scale  float [N]
+ *   y        bf16  [M][N]  row-major (written; every element)
+ * M >= 1, N >= 1, K a positive multiple of 64, M and N rounded up to multiples of
+ * 128, times K, below 2^32
+ * (else PTA_ERR_BAD_DIMS); NULL pointers PTA_ERR_NULL_PTR; a failed launch
+ * PTA_ERR_HIP.  NaN codes propagate to the affected outputs. */
+pta_status taco_gemm_w8a8(const void* a, const float* a_scale, const void* w, const float* w_scale, void* y,
+                          int32_t M, int32_t N, int32_t K, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PTA_GEMM_H */

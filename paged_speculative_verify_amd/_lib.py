@@ -101,6 +101,8 @@ def load() -> ctypes.CDLL:
     lib.taco_pta_calib_stream_read.restype = ctypes.c_int
     lib.taco_pta_calib_mfma_bf16.argtypes = [I32, I32, P, P]
     lib.taco_pta_calib_mfma_bf16.restype = ctypes.c_int
+    lib.taco_gemm_w8a8.argtypes = [P, P, P, P, P, I32, I32, I32, P]
+    lib.taco_gemm_w8a8.restype = ctypes.c_int
     lib.taco_la_create.argtypes = [I32, I32]
     lib.taco_la_create.restype = P
     lib.taco_la_destroy.argtypes = [P]
@@ -513,6 +515,32 @@ def taco_pta_calib_mfma_bf16(workgroups: int, iters: int, sink, stream=None) -> 
         raise ValueError("sink needs one word per workgroup")
     _check(load().taco_pta_calib_mfma_bf16(workgroups, iters, sink.data_ptr(), _stream(stream)))
     return workgroups * 4 * iters * 4 * 32 * 32 * 16 * 2
+
+
+def taco_gemm_w8a8(a, a_scale, w, w_scale, y=None, stream=None):
+    """W8A8 GEMM (include/pta_gemm.h): a uint8 [M, K] and w uint8 [N, K] e4m3fn codes (or
+    float8_e4m3fn tensors), float32 scales [M] and [N]; returns y bf16 [M, N]."""
+    torch = _torch()
+    for t, n in ((a, "a"), (w, "w")):
+        _need(t, n, 2)
+        if t.element_size() != 1:
+            raise ValueError(f"{n} must hold 1-byte fp8 codes")
+    M, K = a.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("a and w disagree on K")
+    _need(a_scale, "a_scale", 1, torch.float32, a.device)
+    _need(w_scale, "w_scale", 1, torch.float32, a.device)
+    if a_scale.numel() != M or w_scale.numel() != N:
+        raise ValueError("one scale per row of a and of w")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _need(y, "y", 2, torch.bfloat16, a.device)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y must be [M, N]")
+    _check(load().taco_gemm_w8a8(a.data_ptr(), a_scale.data_ptr(), w.data_ptr(), w_scale.data_ptr(), y.data_ptr(),
+                                 M, N, K, _stream(stream)))
+    return y
 
 
 def taco_pta_status_string(status: int) -> str:

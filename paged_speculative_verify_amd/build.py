@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpta.so")
 SOURCES = ["pta_api.hip", "pta_valu.hip", "pta_stream.hip", "pta_tile.hip", "pta_aux.hip", "pta_accept.hip",
-           "pta_calib.hip", "pta_wide.hip"]
+           "pta_calib.hip", "pta_wide.hip", "pta_gemm.hip"]
 HEADERS = ["pta_device.h", "pta_flash.h", "pta_launch.h"]
 HOST_SOURCES = ["pta_lookahead.cpp"]      # host-only C++ (the lookahead cache), built with the host compiler
 

@@ -1,0 +1,211 @@
+// W8A8 GEMM on gfx950 fp8 matrix cores (include/pta_gemm.h): the quantized
+// GEMM operators the TACO-LLM pages list beside the attention kernels
+// (17173xz.com article, section "TACO-LLM如何实现降本增效?"; 618zxw.cn article,
+// section "LLM量子化技術による推論コストの削減"; design talk section
+// "5. 支持 Quantization（模型量化）": 8-bit weights on low-precision matrix
+// instructions).
+//
+//   * Workgroup tile 128 (M) x 128 (N), four waves of 64 x 64 (2 x 2 blocks of
+//     v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales: e4m3fn x e4m3fn,
+//     float32 accumulators).  A lane supplies 32 consecutive k-bytes of its row
+//     of A and of its column of W^T (k = 32 h + 0..31 of the 64-step, h = lane
+//     / 32); any consistent assignment of k to (lane half, byte) gives the same
+//     sums, and this one makes each operand two 16-byte LDS reads.
+//   * k-steps of 64 bytes staged in LDS (A tile 8 KiB + W tile 8 KiB), four
+//     stages, three in flight, moved by buffer_load_dwordx4 ... lds (the buffer
+//     resource's size makes rows past M or N read as zero, so ragged edges need
+//     no other handling).  16-byte units of a row are swizzled by the row's bits
+//     2..3, so the 16 rows one pass of an operand read touches hit 16 distinct
+//     bank groups.
+//   * Workgroups are numbered so that the M tiles of one N tile run one after
+//     the other on the same XCD: its weight tile reaches that XCD's L2 from HBM
+//     once for all of them.
+//   * Epilogue: y = acc * a_scale[m] * w_scale[n] in float32, rounded to bf16.
+#include "../../include/pta_gemm.h"
+#include "pta_device.h"
+
+#include <type_traits>
+
+using namespace pta;
+
+namespace {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int BM = 128, BN = 128, BK = 64, NBUF = 4, NT = 256;
+constexpr int A_TILE = BM * BK;                 // 8 KiB
+constexpr int W_TILE = BN * BK;                 // 8 KiB
+constexpr int W_REG = NBUF * A_TILE;            // W region after the A region
+constexpr int LOADS = (A_TILE + W_TILE) / 1024 / (NT / 64);   // copies per wave per stage (4)
+static_assert(W_REG + NBUF * W_TILE <= 65536, "LDS offsets must be 16-bit immediates");
+
+__device__ __forceinline__ i32x4 gemm_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = (int32_t)(uint32_t)p;
+  r[1] = (int32_t)(uint32_t)(p >> 32);
+  r[2] = (int32_t)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// One 1 KiB chunk (16 rows x 64 bytes) of a tile into LDS at m0val (the s_nop
+// covers the wait state an M0 write needs before an LDS-DMA load).
+__device__ __forceinline__ void gemm_copy(uint32_t m0val, const i32x4& rsrc, uint32_t soff, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0val), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void gemm_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int K>
+__device__ __forceinline__ void gemm_wait_stages(int k) {   // at most k later stages in flight
+  if constexpr (K == 0) {
+    gemm_wait_vm<0>();
+  } else {
+    if (k >= K) gemm_wait_vm<K * LOADS>();
+    else gemm_wait_stages<K - 1>(k);
+  }
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void gemm_static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    gemm_static_for<I + 1, N>(f);
+  }
+}
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w8a8_kernel(
+    const uint8_t* a, const float* a_scale, const uint8_t* w, const float* w_scale, uint16_t* y, int M, int N,
+    int K, int tm, int tn) {
+  __shared__ __attribute__((aligned(1024))) char lds[W_REG + NBUF * W_TILE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  // XCD-grouped order: workgroup b runs on XCD b % 8; there, slots take the tm
+  // M tiles of one N tile in a row
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int nt = (slot / tm) * 8 + xcd, mt = slot % tm;
+  if (nt >= tn) return;
+  const int m0 = mt * BM, n0 = nt * BN;
+
+  const i32x4 ars = gemm_rsrc(a, (uint32_t)((uint64_t)M * (uint64_t)K));
+  const i32x4 wrs = gemm_rsrc(w, (uint32_t)((uint64_t)N * (uint64_t)K));
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&lds[0];
+  // copy lanes: row l / 4 of a chunk, physical unit l % 4 holding logical unit
+  // (l % 4) ^ ((row >> 2) & 3), with row >> 2 & 3 = (l / 16) & 3 for every chunk
+  const uint32_t voff = (uint32_t)((lane >> 2) * K + ((((lane & 3) ^ ((lane >> 4) & 3))) << 4));
+  const int nk = K / BK;
+  auto copy_stage = [&](int s, int buf) {
+    const uint32_t kb = (uint32_t)(s * BK);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = wave + 4 * i;                  // chunk of the A tile and of the W tile
+      gemm_copy(lds0 + (uint32_t)(buf * A_TILE + c * 1024), ars, (uint32_t)(m0 + 16 * c) * (uint32_t)K + kb, voff);
+      gemm_copy(lds0 + (uint32_t)(W_REG + buf * W_TILE + c * 1024), wrs, (uint32_t)(n0 + 16 * c) * (uint32_t)K + kb,
+                voff);
+    }
+  };
+  // operand read offsets (bytes) inside a tile: row 32 blk + l % 32 of the
+  // wave's 64 rows, units 2 h and 2 h + 1 (swizzled)
+  const int r32 = lane & 31, h = lane >> 5;
+  uint32_t aoff[2], woff[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t u = (uint32_t)(((2 * h + e) ^ ((r32 >> 2) & 3)) << 4);
+    aoff[e] = (uint32_t)((64 * wm + r32) * BK) + u;
+    woff[e] = (uint32_t)(W_REG + (64 * wn + r32) * BK) + u;
+  }
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = {};
+
+  const int pro = min(NBUF - 1, nk);
+  for (int s = 0; s < pro; ++s) copy_stage(s, s);
+
+  auto step = [&](auto bc, int s) {
+    constexpr int BUF = decltype(bc)::value;
+    gemm_wait_stages<NBUF - 2>(min(NBUF - 2, nk - 1 - s));
+    __syncthreads();                          // stage s in LDS; stage s - 1 consumed by every wave
+    if (s + NBUF - 1 < nk) copy_stage(s + NBUF - 1, (BUF + NBUF - 1) % NBUF);
+    i32x8 ao[2], wo[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(lds + aoff[0] + BUF * A_TILE + i * 32 * BK);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(lds + aoff[1] + BUF * A_TILE + i * 32 * BK);
+      ao[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(lds + woff[0] + BUF * W_TILE + j * 32 * BK);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(lds + woff[1] + BUF * W_TILE + j * 32 * BK);
+      wo[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ao[i], wo[j], acc[i][j], 0, 0, 0, 0x7f, 0, 0x7f);
+  };
+  for (int s = 0; s < nk; s += NBUF) {
+    bool more = true;
+    gemm_static_for<0, NBUF>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if (!more) return;
+      if (s + i >= nk) {
+        more = false;
+        return;
+      }
+      step(std::integral_constant<int, i>{}, s + i);
+    });
+  }
+
+  // epilogue: lane owns column n0 + 64 wn + 32 j + l % 32 and rows 8 q + 4 h + r
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + 64 * wn + 32 * j + r32;
+    if (n >= N) continue;
+    const float sw = w_scale[n];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m < M) y[(int64_t)m * N + n] = f32_to_bf16(acc[i][j][e] * a_scale[m] * sw);
+      }
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+pta_status taco_gemm_w8a8(const void* a, const float* a_scale, const void* w, const float* w_scale, void* y,
+                          int32_t M, int32_t N, int32_t K, void* stream) {
+  if (!a || !a_scale || !w || !w_scale || !y) return PTA_ERR_NULL_PTR;
+  if (M < 1 || N < 1 || K < BK || K % BK != 0) return PTA_ERR_BAD_DIMS;
+  // every tile row (those past M or N included) must have a 32-bit buffer offset
+  const uint64_t mpad = (uint64_t)((M + BM - 1) / BM) * BM, npad = (uint64_t)((N + BN - 1) / BN) * BN;
+  if (mpad * (uint64_t)K >= ((uint64_t)1 << 32) || npad * (uint64_t)K >= ((uint64_t)1 << 32)) return PTA_ERR_BAD_DIMS;
+  if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(w)) % 16 != 0) return PTA_ERR_BAD_DIMS;
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  const int64_t blocks = (int64_t)8 * tm * ((tn + 7) / 8);
+  if (blocks > 0x7fffffff) return PTA_ERR_BAD_DIMS;
+  hipLaunchKernelGGL(gemm_w8a8_kernel, dim3((unsigned)blocks), dim3(NT), 0, (hipStream_t)stream,
+                     reinterpret_cast<const uint8_t*>(a), a_scale, reinterpret_cast<const uint8_t*>(w), w_scale,
+                     reinterpret_cast<uint16_t*>(y), M, N, K, tm, tn);
+  return hipGetLastError() == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+}
+
+}  // extern "C"

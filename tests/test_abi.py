@@ -191,3 +191,16 @@ def test_noalloc_host_checks(lib):
     assert call(dims(max_q_len=4), mask=None) == NULLP
     assert call(dims(q_dtype=0, kv_dtype=0, path=1)) == UNSUP      # vector-ALU rows: no balanced grid
     assert call(dims(num_seqs=0)) == OK
+
+
+def test_gemm_host_checks(lib):
+    """taco_gemm_w8a8 rejects bad arguments on the host, before any HIP call."""
+    f = lib.taco_gemm_w8a8
+    ok = dict(a=FAKE, sa=FAKE, w=FAKE, sw=FAKE, y=FAKE, M=4, N=4, K=128)
+    def call(**kw):
+        d = dict(ok, **kw)
+        return f(d["a"], d["sa"], d["w"], d["sw"], d["y"], d["M"], d["N"], d["K"], None)
+    assert call(a=None) == NULLP and call(sw=None) == NULLP and call(y=None) == NULLP
+    assert call(K=100) == DIMS and call(K=0) == DIMS and call(M=0) == DIMS and call(N=-1) == DIMS
+    assert call(a=ctypes.c_void_p(0x10008)) == DIMS                 # not 16-byte aligned
+    assert call(M=1 << 20, K=1 << 13) == DIMS                       # rows x K past 32-bit offsets
