@@ -33,12 +33,24 @@ namespace {
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int BM = 128, BN = 128, BK = 64, NBUF = 4, NT = 256;
-constexpr int A_TILE = BM * BK;                 // 8 KiB
-constexpr int W_TILE = BN * BK;                 // 8 KiB
-constexpr int W_REG = NBUF * A_TILE;            // W region after the A region
-constexpr int LOADS = (A_TILE + W_TILE) / 1024 / (NT / 64);   // copies per wave per stage (4)
-static_assert(W_REG + NBUF * W_TILE <= 65536, "LDS offsets must be 16-bit immediates");
+constexpr int BM = 128, BK = 64, NT = 256;
+
+// Tile geometry for WNB 32-column blocks per wave (2: 128 x 128 workgroup
+// tiles, four stages; 4: 128 x 256, three stages).
+template <int WNB>
+struct GemmGeom {
+  static constexpr int BN = 64 * WNB;                     // two waves side by side along N
+  static constexpr int NBUF = WNB == 2 ? 4 : 3;
+  static constexpr int A_TILE = BM * BK;                  // 8 KiB
+  static constexpr int W_TILE = BN * BK;
+  static constexpr int W_REG = NBUF * A_TILE;             // W region after the A region
+  static constexpr int CHUNKS_A = A_TILE / 1024, CHUNKS_W = W_TILE / 1024;
+  static constexpr int LOADS = (CHUNKS_A + CHUNKS_W) / (NT / 64);   // copies per wave per stage
+  static constexpr int LDS_BYTES = W_REG + NBUF * W_TILE;
+  static_assert((CHUNKS_A + CHUNKS_W) % (NT / 64) == 0, "whole copies per wave");
+  static_assert(W_REG + (NBUF - 1) * W_TILE < 65536, "stage offsets must be 16-bit immediates");
+  static_assert(LDS_BYTES <= 81920, "two workgroups per compute unit");
+};
 
 __device__ __forceinline__ i32x4 gemm_rsrc(const void* base, uint32_t bytes) {
   const uint64_t p = (uint64_t)(uintptr_t)base;
@@ -65,13 +77,13 @@ __device__ __forceinline__ void gemm_wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int K>
-__device__ __forceinline__ void gemm_wait_stages(int k) {   // at most k later stages in flight
+template <int L, int K>
+__device__ __forceinline__ void gemm_wait_stages(int k) {   // at most k later stages of L copies in flight
   if constexpr (K == 0) {
     gemm_wait_vm<0>();
   } else {
-    if (k >= K) gemm_wait_vm<K * LOADS>();
-    else gemm_wait_stages<K - 1>(k);
+    if (k >= K) gemm_wait_vm<K * L>();
+    else gemm_wait_stages<L, K - 1>(k);
   }
 }
 
@@ -83,10 +95,13 @@ __device__ __forceinline__ void gemm_static_for(F&& f) {
   }
 }
 
+template <int WNB>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w8a8_kernel(
     const uint8_t* a, const float* a_scale, const uint8_t* w, const float* w_scale, uint16_t* y, int M, int N,
     int K, int tm, int tn) {
-  __shared__ __attribute__((aligned(1024))) char lds[W_REG + NBUF * W_TILE];
+  using Gm = GemmGeom<WNB>;
+  constexpr int BN = Gm::BN, NBUF = Gm::NBUF, A_TILE = Gm::A_TILE, W_TILE = Gm::W_TILE, W_REG = Gm::W_REG;
+  __shared__ __attribute__((aligned(1024))) char lds[Gm::LDS_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
@@ -107,11 +122,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
   auto copy_stage = [&](int s, int buf) {
     const uint32_t kb = (uint32_t)(s * BK);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = wave + 4 * i;                  // chunk of the A tile and of the W tile
-      gemm_copy(lds0 + (uint32_t)(buf * A_TILE + c * 1024), ars, (uint32_t)(m0 + 16 * c) * (uint32_t)K + kb, voff);
-      gemm_copy(lds0 + (uint32_t)(W_REG + buf * W_TILE + c * 1024), wrs, (uint32_t)(n0 + 16 * c) * (uint32_t)K + kb,
-                voff);
+    for (int i = 0; i < Gm::LOADS; ++i) {
+      const int c = wave + 4 * i;                  // chunk c of the stage: A chunks, then W chunks
+      if (c < Gm::CHUNKS_A)
+        gemm_copy(lds0 + (uint32_t)(buf * A_TILE + c * 1024), ars, (uint32_t)(m0 + 16 * c) * (uint32_t)K + kb, voff);
+      else
+        gemm_copy(lds0 + (uint32_t)(W_REG + buf * W_TILE + (c - Gm::CHUNKS_A) * 1024), wrs,
+                  (uint32_t)(n0 + 16 * (c - Gm::CHUNKS_A)) * (uint32_t)K + kb, voff);
     }
   };
   // operand read offsets (bytes) inside a tile: row 32 blk + l % 32 of the
@@ -122,24 +139,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
   for (int e = 0; e < 2; ++e) {
     const uint32_t u = (uint32_t)(((2 * h + e) ^ ((r32 >> 2) & 3)) << 4);
     aoff[e] = (uint32_t)((64 * wm + r32) * BK) + u;
-    woff[e] = (uint32_t)(W_REG + (64 * wn + r32) * BK) + u;
+    woff[e] = (uint32_t)(W_REG + (32 * WNB * wn + r32) * BK) + u;
   }
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][WNB];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = {};
+    for (int j = 0; j < WNB; ++j) acc[i][j] = {};
 
   const int pro = min(NBUF - 1, nk);
   for (int s = 0; s < pro; ++s) copy_stage(s, s);
 
   auto step = [&](auto bc, int s) {
     constexpr int BUF = decltype(bc)::value;
-    gemm_wait_stages<NBUF - 2>(min(NBUF - 2, nk - 1 - s));
+    gemm_wait_stages<Gm::LOADS, NBUF - 2>(min(NBUF - 2, nk - 1 - s));
     __syncthreads();                          // stage s in LDS; stage s - 1 consumed by every wave
     if (s + NBUF - 1 < nk) copy_stage(s + NBUF - 1, (BUF + NBUF - 1) % NBUF);
-    i32x8 ao[2], wo[2];
+    i32x8 ao[2], wo[WNB];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const i32x4 lo = *reinterpret_cast<const i32x4*>(lds + aoff[0] + BUF * A_TILE + i * 32 * BK);
@@ -147,7 +164,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
       ao[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < WNB; ++j) {
       const i32x4 lo = *reinterpret_cast<const i32x4*>(lds + woff[0] + BUF * W_TILE + j * 32 * BK);
       const i32x4 hi = *reinterpret_cast<const i32x4*>(lds + woff[1] + BUF * W_TILE + j * 32 * BK);
       wo[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -155,7 +172,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < WNB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ao[i], wo[j], acc[i][j], 0, 0, 0, 0x7f, 0, 0x7f);
   };
   for (int s = 0; s < nk; s += NBUF) {
@@ -171,10 +188,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
     });
   }
 
-  // epilogue: lane owns column n0 + 64 wn + 32 j + l % 32 and rows 8 q + 4 h + r
+  // epilogue: lane owns column n0 + 32 WNB wn + 32 j + l % 32 and rows 8 q + 4 h + r
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + 64 * wn + 32 * j + r32;
+  for (int j = 0; j < WNB; ++j) {
+    const int n = n0 + 32 * WNB * wn + 32 * j + r32;
     if (n >= N) continue;
     const float sw = w_scale[n];
 #pragma unroll
@@ -196,15 +213,23 @@ pta_status taco_gemm_w8a8(const void* a, const float* a_scale, const void* w, co
   if (!a || !a_scale || !w || !w_scale || !y) return PTA_ERR_NULL_PTR;
   if (M < 1 || N < 1 || K < BK || K % BK != 0) return PTA_ERR_BAD_DIMS;
   // every tile row (those past M or N included) must have a 32-bit buffer offset
-  const uint64_t mpad = (uint64_t)((M + BM - 1) / BM) * BM, npad = (uint64_t)((N + BN - 1) / BN) * BN;
+  const uint64_t mpad = (uint64_t)((M + BM - 1) / BM) * BM, npad = (uint64_t)((N + 255) / 256) * 256;
   if (mpad * (uint64_t)K >= ((uint64_t)1 << 32) || npad * (uint64_t)K >= ((uint64_t)1 << 32)) return PTA_ERR_BAD_DIMS;
   if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(w)) % 16 != 0) return PTA_ERR_BAD_DIMS;
+  // wide column tiles once the M tiles alone would not fill the device
+  const bool wide = M > 128;
+  const int BN = wide ? GemmGeom<4>::BN : GemmGeom<2>::BN;
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   const int64_t blocks = (int64_t)8 * tm * ((tn + 7) / 8);
   if (blocks > 0x7fffffff) return PTA_ERR_BAD_DIMS;
-  hipLaunchKernelGGL(gemm_w8a8_kernel, dim3((unsigned)blocks), dim3(NT), 0, (hipStream_t)stream,
-                     reinterpret_cast<const uint8_t*>(a), a_scale, reinterpret_cast<const uint8_t*>(w), w_scale,
-                     reinterpret_cast<uint16_t*>(y), M, N, K, tm, tn);
+  if (wide)
+    hipLaunchKernelGGL(gemm_w8a8_kernel<4>, dim3((unsigned)blocks), dim3(NT), 0, (hipStream_t)stream,
+                       reinterpret_cast<const uint8_t*>(a), a_scale, reinterpret_cast<const uint8_t*>(w), w_scale,
+                       reinterpret_cast<uint16_t*>(y), M, N, K, tm, tn);
+  else
+    hipLaunchKernelGGL(gemm_w8a8_kernel<2>, dim3((unsigned)blocks), dim3(NT), 0, (hipStream_t)stream,
+                       reinterpret_cast<const uint8_t*>(a), a_scale, reinterpret_cast<const uint8_t*>(w), w_scale,
+                       reinterpret_cast<uint16_t*>(y), M, N, K, tm, tn);
   return hipGetLastError() == hipSuccess ? PTA_OK : PTA_ERR_HIP;
 }
 

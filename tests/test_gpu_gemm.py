@@ -87,12 +87,14 @@ def test_w8a8_full_size_sampled_rows(torch_cuda):
     say("full size worst error / bound", r)
 
 
-def test_w8a8_integer_exact(torch_cuda):
+@pytest.mark.parametrize("M,N,K", [(70, 90, 256), (200, 600, 512)], ids=["narrow_tiles", "wide_tiles"])
+def test_w8a8_integer_exact(torch_cuda, M, N, K):
     """Small integers with power-of-two scales: every partial sum is exact in float32, so the
-    output is the bf16 rounding of the exact integer result."""
+    output is the bf16 rounding of the exact integer result (both tile widths: up to 128 rows
+    and beyond)."""
     import torch
     rng = np.random.default_rng(5)
-    M, N, K = 70, 90, 256
+    say("integer exact", M, N, K)
     from tests.test_oracle_gemm import fp8_codes_of
     ai, wi = rng.integers(-4, 5, (M, K)), rng.integers(-4, 5, (N, K))
     sa, sw = (2.0 ** rng.integers(-2, 3, M)).astype(np.float32), (2.0 ** rng.integers(-2, 3, N)).astype(np.float32)
