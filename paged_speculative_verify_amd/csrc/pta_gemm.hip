@@ -64,10 +64,14 @@ __device__ __forceinline__ i32x4 gemm_rsrc(const void* base, uint32_t bytes) {
 
 // One 1 KiB chunk (16 rows x 64 bytes) of a tile into LDS at m0val (the s_nop
 // covers the wait state an M0 write needs before an LDS-DMA load).
-__device__ __forceinline__ void gemm_copy(uint32_t m0val, const i32x4& rsrc, uint32_t soff, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+// The whole byte offset goes in the vector offset, which the buffer range
+// check covers (the scalar offset is outside it): rows of a ragged tile past M
+// or N read zero instead of memory past the operand.
+__device__ __forceinline__ void gemm_copy(uint32_t m0val, const i32x4& rsrc, uint32_t off, uint32_t voff) {
+  const uint32_t v = voff + off;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(m0val), "v"(voff), "s"(rsrc), "s"(soff)
+               : "s"(m0val), "v"(v), "s"(rsrc)
                : "memory", "m0");
 }
 

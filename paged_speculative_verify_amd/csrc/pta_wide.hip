@@ -245,11 +245,20 @@ __device__ __forceinline__ void wide_offsets(WideOffsets<D>& W, int lane, uint32
 template <int D, int KB>
 __device__ __forceinline__ f32x16 wide_scores(const WideRows<D>& R, const WideOffsets<D>& W, const char* lds) {
   f32x16 s = {};
+  bf16x8 k[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const bf16x8 k = *reinterpret_cast<const bf16x8*>(lds + W.k[ks] + KB);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, R.qop[ks], s, 0, 0, 0);
+  for (int ks = 0; ks < D / 16; ++ks) k[ks] = *reinterpret_cast<const bf16x8*>(lds + W.k[ks] + KB);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[ks], R.qop[ks], s, 0, 0, 0);
+  // keep three operand reads in flight ahead of the products
+  constexpr int KS = D / 16, AHEAD = 3;
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < KS - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
   return s;
 }
 
@@ -318,19 +327,31 @@ __device__ __forceinline__ void wide_p(WideState<D>& st, const f32x16& x, float 
 template <int D, int VB>
 __device__ __forceinline__ void wide_pv(WideState<D>& st, const WideOffsets<D>& W, const bf16x8 (&p)[2],
                                         const char* lds) {
-  constexpr int TILE = kPage * D * 2;
+  constexpr int TILE = kPage * D * 2, DB = D / 32;
+  auto rd = [&](uint32_t off) { return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + off)); };
+  auto cat = [](s16x4 va, s16x4 vb) {
+    return __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint2, va).x, __builtin_bit_cast(uint2, va).y,
+                                                 __builtin_bit_cast(uint2, vb).x, __builtin_bit_cast(uint2, vb).y));
+  };
+  // the first page's operands are all read before its products, and each
+  // product of the first page is followed by the read of the matching operand
+  // of the second page, so every product finds its operand in registers
+  s16x4 va[DB], vb[DB];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int db = 0; db < DB; ++db) {
+    va[db] = rd(W.v[db][0] + VB);
+    vb[db] = rd(W.v[db][1] + VB);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + W.v[db][0] + VB + t * TILE));
-      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + W.v[db][1] + VB + t * TILE));
-      const bf16x8 vt = __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint2, va).x,
-                                                              __builtin_bit_cast(uint2, va).y,
-                                                              __builtin_bit_cast(uint2, vb).x,
-                                                              __builtin_bit_cast(uint2, vb).y));
-      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, p[t], st.o[db], 0, 0, 0);
-    }
+  for (int db = 0; db < DB; ++db) {
+    st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat(va[db], vb[db]), p[0], st.o[db], 0, 0, 0);
+    va[db] = rd(W.v[db][0] + VB + TILE);
+    vb[db] = rd(W.v[db][1] + VB + TILE);
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat(va[db], vb[db]), p[1], st.o[db], 0, 0, 0);
 }
 
 // The unit's rows row0 + 32 wave .. over tokens [t0, t1) of sequence b, KV
@@ -448,16 +469,20 @@ __device__ __forceinline__ void wide_range(const AttnArgs& a, char* lds, uint32_
       __syncthreads();
     }
     if ((s & 3) == 0) pace(prog0 + 2 * s, prog_len);
-    if (s + NBUF - 1 < nst) {
-      copy_stage(s + NBUF - 1, ph, PREV);
-      if (s + NBUF < nst) page_ids(s + NBUF, ph);
-    }
+    if (s + NBUF - 1 < nst) copy_stage(s + NBUF - 1, ph, PREV);
     if (wave_rows) {
       if (pend) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) st.o[db] *= alpha;
       }
       xn = wide_scores<D, Gm::tile_lds(BUF, 0)>(R, W, lds);            // S of pair s + 1
+    }
+    // next stage's page ids, issued after the score reads so that their waits
+    // do not include the table load
+    asm volatile("" ::: "memory");
+    if (s + NBUF < nst) page_ids(s + NBUF, ph);
+    asm volatile("" ::: "memory");
+    if (wave_rows) {
       bf16x8 p[2];
       wide_p<D>(st, x, c, p);                                          // P of pair s
       wide_pv<D, BUF * Gm::PAIR>(st, W, p, lds);                       // P.V of pair s
