@@ -75,8 +75,10 @@ struct WideGeom {
   static constexpr int tile_lds(int b, int t) { return (t < 2 ? 0 : VREG) + b * PAIR + (t & 1) * TILE; }
 };
 
-// Buffer resource over `bytes` bytes at `base` (raw, stride 0): reads past the
-// end return zero instead of touching memory.
+// Buffer resource over `bytes` bytes at `base` (raw, stride 0).  The copies
+// put a page tile's base in the scalar offset, which the range check does not
+// cover, so every page id must name a page of the pool (the call's contract);
+// the check covers the in-tile vector and instruction offsets.
 __device__ __forceinline__ i32x4 wide_rsrc(const void* base, uint32_t bytes) {
   const uint64_t p = (uint64_t)(uintptr_t)base;
   i32x4 r;
