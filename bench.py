@@ -555,82 +555,131 @@ def extra_workload(psv, torch, name, args):
 
 # ------------------------------------------------------------------ quantized GEMM
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+W4_GROUP = 128
 GEMM_SHAPES = {
     # Llama-3.1-70B MLP gate + up projections (N = 2 x 28672, K = 8192) over the verify step's
-    # 512 candidate tokens (32 sequences x 16), and over a 64-sequence decode step
-    "llama70b_gate_up_verify512": (512, 57344, 8192),
-    "llama70b_gate_up_decode64": (64, 57344, 8192),
+    # 512 candidate tokens (32 sequences x 16), and over a 64-sequence decode step; W8A8 (fp8
+    # activations and weights) and W4A16 (bf16 activations, int4 weights in groups of 128)
+    "llama70b_gate_up_verify512": ("w8a8", 512, 57344, 8192),
+    "llama70b_gate_up_decode64": ("w8a8", 64, 57344, 8192),
+    "w4a16_llama70b_gate_up_verify512": ("w4a16", 512, 57344, 8192),
+    "w4a16_llama70b_gate_up_decode64": ("w4a16", 64, 57344, 8192),
 }
 
 
+def w4a16_oracle_rows(oracle, a_bits, w_packed, w_scale, group, with_bound=True):
+    """(fp64 reference, bound 2^-8 |ref| + 2^-14 sum|a||q|s) of a few rows, column chunk by column
+    chunk (the decoded weights of the whole matrix would not fit in host memory at once)."""
+    from oracle.formats import decode_bf16
+    K = a_bits.shape[1]
+    ref = np.empty((a_bits.shape[0], w_packed.shape[0]))
+    S = np.empty_like(ref)
+    A = np.abs(decode_bf16(a_bits))
+    for c0 in range(0, w_packed.shape[0], 4096):
+        c1 = min(c0 + 4096, w_packed.shape[0])
+        ref[:, c0:c1] = oracle.w4a16_gemm(a_bits, w_packed[c0:c1], w_scale[c0:c1], group)
+        if with_bound:
+            q = np.abs(oracle.decode_int4_packed(w_packed[c0:c1], K)).astype(np.float64)
+            S[:, c0:c1] = A @ (q * np.repeat(w_scale[c0:c1].astype(np.float64), group, axis=1)).T
+    return ref, 2.0 ** -8 * np.abs(ref) + 2.0 ** -14 * S
+
+
 def gemm_bench(psv, torch, name, steps=30, warmup=5, cpu_rows=2, parity_rows=(0, 1, 255, 511)):
-    """W8A8 GEMM on one Llama-70B-shaped projection: timed calls (HIP events around back-to-back
-    calls), roofline against the fp8 matrix-core peak or HBM (whichever the shape's intensity
-    says bounds it), parity of sampled output rows against the fp64 oracle, the oracle timed on
-    a few rows."""
+    """A quantized GEMM on one Llama-70B-shaped projection: timed calls (HIP events around
+    back-to-back calls), roofline against the matrix-core peak of the operand type or HBM
+    (whichever the shape's intensity says bounds it), parity of sampled output rows against the
+    fp64 oracle, the oracle timed on a few rows."""
     import oracle
-    from workload.gemm import make_w8a8_device
-    M, N, K = GEMM_SHAPES[name]
-    a, sa, w, sw = make_w8a8_device(M, N, K, seed=11, torch=torch)
+    from workload.gemm import make_w4a16_device, make_w8a8_device
+    op, M, N, K = GEMM_SHAPES[name]
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    if op == "w8a8":
+        a, sa, w, sw = make_w8a8_device(M, N, K, seed=11, torch=torch)
+        call = lambda: psv.taco_gemm_w8a8(a, sa, w, sw, y)
+        peak, kernel = FP8_PEAK_TFLOPS, "gemm_w8a8_kernel"
+        nbytes = M * K + N * K + 2 * M * N + 4 * (M + N)
+    else:
+        G = W4_GROUP
+        a, w, sw = make_w4a16_device(M, N, K, G, seed=11, torch=torch)
+        call = lambda: psv.taco_gemm_w4a16(a, w, sw, G, y)
+        peak, kernel = BF16_PEAK_TFLOPS, "gemm_w4a16_kernel"
+        nbytes = 2 * M * K + N * K // 2 + 4 * N * (K // G) + 2 * M * N
     for _ in range(warmup):
-        psv.taco_gemm_w8a8(a, sa, w, sw, y)
+        call()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < SETTLE_S:
         for _ in range(8):
-            psv.taco_gemm_w8a8(a, sa, w, sw, y)
+            call()
         torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(steps):
-        psv.taco_gemm_w8a8(a, sa, w, sw, y)
+        call()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     flops = 2.0 * M * N * K
-    nbytes = M * K + N * K + 2 * M * N + 4 * (M + N)
     tflops = flops / (ms / 1e3) / 1e12
     gbs = nbytes / (ms / 1e3) / 1e9
     intensity = flops / nbytes
-    ridge = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     bound = "mfma" if intensity > ridge else "hbm"
-    # parity: sampled rows of the timed call's output against the oracle
+    # parity: sampled rows of the timed call's output against the oracle; the oracle on a few
+    # rows, all cores
     rows = np.array([r for r in parity_rows if r < M])
-    wc, wsc = w.cpu().numpy(), sw.cpu().numpy()
-    ac, asc = a[torch.from_numpy(rows).cuda()].cpu().numpy(), sa.cpu().numpy()[rows]
-    ref = oracle.w8a8_gemm(ac, asc, wc, wsc)
-    got = y[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
-    from oracle.formats import decode_fp8_e4m3fn
-    S = (np.abs(decode_fp8_e4m3fn(ac)) * asc.astype(np.float64)[:, None]) @ \
-        (np.abs(decode_fp8_e4m3fn(wc)) * wsc.astype(np.float64)[:, None]).T
-    excess = float((np.abs(got - ref) - (2.0 ** -8 * np.abs(ref) + 2.0 ** -14 * S)).max())
-    # the oracle on a few rows, all cores
+    sel = torch.from_numpy(rows).cuda()
+    got = y[sel].float().cpu().numpy().astype(np.float64)
     from threadpoolctl import threadpool_limits
     cores = len(os.sched_getaffinity(0))
-    with threadpool_limits(limits=cores, user_api="blas"):
-        t0 = time.perf_counter()
-        oracle.w8a8_gemm(ac[:cpu_rows], asc[:cpu_rows], wc, wsc)
-        t_cpu = time.perf_counter() - t0
+    if op == "w8a8":
+        wc, wsc = w.cpu().numpy(), sw.cpu().numpy()
+        ac, asc = a[sel].cpu().numpy(), sa.cpu().numpy()[rows]
+        ref = oracle.w8a8_gemm(ac, asc, wc, wsc)
+        from oracle.formats import decode_fp8_e4m3fn
+        S = (np.abs(decode_fp8_e4m3fn(ac)) * asc.astype(np.float64)[:, None]) @ \
+            (np.abs(decode_fp8_e4m3fn(wc)) * wsc.astype(np.float64)[:, None]).T
+        bnd = 2.0 ** -8 * np.abs(ref) + 2.0 ** -14 * S
+        with threadpool_limits(limits=cores, user_api="blas"):
+            t0 = time.perf_counter()
+            oracle.w8a8_gemm(ac[:cpu_rows], asc[:cpu_rows], wc, wsc)
+            t_cpu = time.perf_counter() - t0
+        dtype = "fp8-e4m3 x fp8-e4m3 -> f32 -> bf16"
+        metric = "W8A8 GEMM TFLOP/s (fp8 e4m3fn operands, per-row scales, bf16 out), 1 GPU"
+        bound_text = "2^-8 |y_ref| + 2^-14 a_scale w_scale sum|a||w| per output"
+        config = {"workload": name, "M": M, "N": N, "K": K}
+    else:
+        a_bits = a[sel].view(torch.int16).cpu().numpy().view(np.uint16)
+        wp, wsc = w.cpu().numpy(), sw.cpu().numpy()
+        ref, bnd = w4a16_oracle_rows(oracle, a_bits, wp, wsc, W4_GROUP)
+        with threadpool_limits(limits=cores, user_api="blas"):
+            t0 = time.perf_counter()
+            w4a16_oracle_rows(oracle, a_bits[:cpu_rows], wp, wsc, W4_GROUP, with_bound=False)
+            t_cpu = time.perf_counter() - t0
+        dtype = "bf16 x int4 (exact to bf16) -> f32, group scales in f32 -> bf16"
+        metric = "W4A16 GEMM TFLOP/s (bf16 activations, int4 weights, group-128 scales, bf16 out), 1 GPU"
+        bound_text = "2^-8 |y_ref| + 2^-14 sum_k |a||q| w_scale per output"
+        config = {"workload": name, "M": M, "N": N, "K": K, "group": W4_GROUP}
+    excess = float((np.abs(got - ref) - bnd).max())
     res = {
-        "metric": "W8A8 GEMM TFLOP/s (fp8 e4m3fn operands, per-row scales, bf16 out), 1 GPU",
+        "metric": metric,
         "value": round(tflops, 2), "unit": "TFLOP/s", "higher_is_better": True, "data": "synthetic",
-        "dtype": "fp8-e4m3 x fp8-e4m3 -> f32 -> bf16",
-        "config": {"workload": name, "M": M, "N": N, "K": K},
+        "dtype": dtype, "config": config,
         "us_per_call": round(ms * 1e3, 2), "steps": steps, "warmup": warmup,
         "roofline": {"bound": bound, "achieved": round(tflops if bound == "mfma" else gbs, 2),
-                     "peak": FP8_PEAK_TFLOPS if bound == "mfma" else HBM_PEAK_GBS,
+                     "peak": peak if bound == "mfma" else HBM_PEAK_GBS,
                      "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
-                     "frac": round(tflops / FP8_PEAK_TFLOPS if bound == "mfma" else gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "mfma_frac": round(tflops / FP8_PEAK_TFLOPS, 4),
+                     "frac": round(tflops / peak if bound == "mfma" else gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "mfma_frac": round(tflops / peak, 4),
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": int(flops),
                      "arithmetic_intensity_flop_per_byte": round(intensity, 1),
-                     "ridge_flop_per_byte": round(ridge, 1), "kernel": "gemm_w8a8_kernel",
+                     "ridge_flop_per_byte": round(ridge, 1), "kernel": kernel,
                      "timing": f"HIP events on the launch stream around {steps} back-to-back calls"},
         "parity": {"rows": rows.tolist(), "max_excess_over_bound": excess, "parity_ok": bool(excess <= 0),
-                   "bound": "2^-8 |y_ref| + 2^-14 a_scale w_scale sum|a||w| per output"},
+                   "bound": bound_text},
         "cpu_baseline": {"value": round(2.0 * cpu_rows * N * K / t_cpu / 1e12, 6), "unit": "TFLOP/s",
                          "cores": cores, "kind": "oracle",
                          "sample": f"{cpu_rows} output rows x {N} columns, fp64 numpy, {t_cpu:.1f} s"},
@@ -671,7 +720,7 @@ def main(argv=None) -> int:
                     help="instead of the bench line: the host lookahead cache (propose, budgets, append) "
                          "over a decode batch of synthetic token streams, one JSON line; needs no GPU")
     ap.add_argument("--gemm", choices=sorted(GEMM_SHAPES), default=None,
-                    help="instead of the bench line: the W8A8 GEMM on one Llama-70B-shaped projection")
+                    help="instead of the bench line: one quantized GEMM (W8A8 or W4A16) on a Llama-70B-shaped projection")
     ap.add_argument("--qlen-floor", action="store_true",
                     help="instead of the bench line: attention time against the number of candidates "
                          "per sequence at the decode shape, T(q_len) / T(1)")
@@ -826,7 +875,7 @@ def main(argv=None) -> int:
             result["workloads"][other] = r
         result["quantized_gemm"] = {}
         for g in sorted(GEMM_SHAPES):
-            print(f"[bench] W8A8 GEMM {g}", file=sys.stderr, flush=True)
+            print(f"[bench] quantized GEMM {g}", file=sys.stderr, flush=True)
             r = gemm_bench(psv, torch, g, steps=min(args.steps, 20), warmup=args.warmup, cpu_rows=1)
             parity_ok = parity_ok and r["parity"]["parity_ok"]
             result["quantized_gemm"][g] = {k: r[k] for k in ("value", "unit", "us_per_call", "roofline", "parity",

@@ -14,6 +14,9 @@
  * and W [N][K] the weights (one row per output channel):
  *   W8A8:   Y[m][n] = a_scale[m] * w_scale[n] * sum_k A[m][k] * W[n][k],
  *           A and W OCP fp8 e4m3fn codes, scales float32.
+ *   W4A16:  Y[m][n] = sum_k A[m][k] * q[n][k] * w_scale[n][k / group],
+ *           A bf16, q signed 4-bit integers (-8..7), scales float32 per
+ *           (output channel, group of `group` consecutive k).
  * Y is bf16 [M][N] row-major, rounded to nearest even from float32.
  *
  * Conventions as in pta.h: device pointers, caller-owned buffers, work
@@ -46,6 +49,24 @@ extern "C" {
  * PTA_ERR_HIP.  NaN codes propagate to the affected outputs. */
 pta_status taco_gemm_w8a8(const void* a, const float* a_scale, const void* w, const float* w_scale, void* y,
                           int32_t M, int32_t N, int32_t K, void* stream);
+
+/* bf16 x group-scaled int4 GEMM on the bf16 matrix cores
+ * (v_mfma_f32_32x32x16_bf16).  Every int4 weight is converted exactly to bf16;
+ * each group's products are summed in float32 and scaled by w_scale in
+ * float32.
+ *   a        bf16  [M][K]      row-major, 16-byte aligned
+ *   w        uint8 [N][K / 2]  row-major, 16-byte aligned; byte j of a row holds
+ *                              k = 2 j in its low nibble and k = 2 j + 1 in its
+ *                              high nibble, two's complement
+ *   w_scale  float [N][K / group], 4-byte aligned
+ *   y        bf16  [M][N]      row-major (written; every element)
+ * M >= 1, N >= 1, K a positive multiple of 64, group a multiple of 64 that
+ * divides K; M rounded up to a multiple of 128 (64 when M <= 64) times 2 K,
+ * N rounded up to a multiple of 128 times K / 2 and times 4 K / group, below
+ * 2^32 (else PTA_ERR_BAD_DIMS); NULL pointers PTA_ERR_NULL_PTR; a failed launch
+ * PTA_ERR_HIP.  NaN activations propagate to the affected outputs. */
+pta_status taco_gemm_w4a16(const void* a, const void* w, const float* w_scale, void* y, int32_t M, int32_t N,
+                           int32_t K, int32_t group, void* stream);
 
 #ifdef __cplusplus
 }

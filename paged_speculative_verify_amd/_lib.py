@@ -103,6 +103,8 @@ def load() -> ctypes.CDLL:
     lib.taco_pta_calib_mfma_bf16.restype = ctypes.c_int
     lib.taco_gemm_w8a8.argtypes = [P, P, P, P, P, I32, I32, I32, P]
     lib.taco_gemm_w8a8.restype = ctypes.c_int
+    lib.taco_gemm_w4a16.argtypes = [P, P, P, P, I32, I32, I32, I32, P]
+    lib.taco_gemm_w4a16.restype = ctypes.c_int
     lib.taco_la_create.argtypes = [I32, I32]
     lib.taco_la_create.restype = P
     lib.taco_la_destroy.argtypes = [P]
@@ -540,6 +542,33 @@ def taco_gemm_w8a8(a, a_scale, w, w_scale, y=None, stream=None):
         raise ValueError("y must be [M, N]")
     _check(load().taco_gemm_w8a8(a.data_ptr(), a_scale.data_ptr(), w.data_ptr(), w_scale.data_ptr(), y.data_ptr(),
                                  M, N, K, _stream(stream)))
+    return y
+
+
+def taco_gemm_w4a16(a, w_packed, w_scale, group, y=None, stream=None):
+    """W4A16 GEMM (include/pta_gemm.h): a bf16 [M, K], w_packed uint8 [N, K / 2] (two's
+    complement int4, k = 2 j in the low nibble of byte j), w_scale float32 [N, K / group];
+    returns y bf16 [M, N] = sum_k a[m, k] q[n, k] w_scale[n, k // group]."""
+    torch = _torch()
+    _need(a, "a", 2, torch.bfloat16)
+    _need(w_packed, "w_packed", 2, torch.uint8, a.device)
+    M, K = a.shape
+    N = w_packed.shape[0]
+    if w_packed.shape[1] * 2 != K:
+        raise ValueError("w_packed must hold K / 2 bytes per row")
+    group = int(group)
+    if group <= 0 or K % group:
+        raise ValueError("group must divide K")
+    _need(w_scale, "w_scale", 2, torch.float32, a.device)
+    if tuple(w_scale.shape) != (N, K // group):
+        raise ValueError("w_scale must be [N, K / group]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _need(y, "y", 2, torch.bfloat16, a.device)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y must be [M, N]")
+    _check(load().taco_gemm_w4a16(a.data_ptr(), w_packed.data_ptr(), w_scale.data_ptr(), y.data_ptr(),
+                                  M, N, K, group, _stream(stream)))
     return y
 
 

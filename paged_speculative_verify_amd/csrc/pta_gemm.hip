@@ -208,6 +208,185 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
   }
 }
 
+
+// ------------------------------------------------------------------ W4A16
+// bf16 activations x group-scaled signed int4 weights on the bf16 matrix cores
+// (v_mfma_f32_32x32x16_bf16, float32 accumulation):
+//   * Workgroup tile 32 WM (M) x 128 (N), BK = 64 k per stage; each of the four
+//     waves owns 32 columns and all 32 WM rows (WM 32-row blocks), so every
+//     weight fragment it converts feeds WM products.
+//   * k assignment: in a stage, lane half h of k-step ks covers the k-octet
+//     4 h + ks of both operands (any consistent assignment gives the same
+//     sums).  A lane's packed weights for the whole stage are then one 16-byte
+//     LDS read (octets 4 h .. 4 h + 3 of its column), and its activations one
+//     16-byte read per k-step and row block.
+//   * Conversion is exact: each nibble is sign-extended (v_bfe_i32), converted
+//     to float32 and packed to bf16 (integers -8..7 are exact in bf16), so the
+//     only roundings are the matrix cores' float32 sums and the final bf16.
+//   * Group scales apply in float32: each group's products accumulate apart
+//     (the first product of a group starts from zero) and acc += s[n][g] * acc_g
+//     at the group's end.  The scales of a group's 128 columns arrive by
+//     LDS-DMA (buffer_load_dword ... lds, a strided gather) with the group's
+//     first stage, into one of four slots (group & 3).
+//   * Staging as the W8A8 kernel: buffer-resource LDS-DMA with the whole offset
+//     in the range-checked vector offset (rows past M or N read zero), NBUF
+//     stages, XCD-grouped tile order.  Swizzles: the 16-byte unit u of
+//     activation row r sits at u ^ ((r >> 1) & 7) (rows are 128 bytes), the
+//     unit u of weight row r at u ^ ((r >> 3) & 1) (rows are 32 bytes): the 16
+//     lanes of one read pass touch 16 distinct bank groups.
+template <int WM>
+struct W4Geom {
+  static constexpr int BM = 32 * WM, BN = 128, BK = 64;
+  static constexpr int NBUF = WM == 4 ? 3 : 4;
+  static constexpr int A_TILE = BM * BK * 2;               // bf16
+  static constexpr int W_TILE = BN * BK / 2;               // packed int4 (4 KiB)
+  static constexpr int W_REG = NBUF * A_TILE;
+  static constexpr int S_REG = W_REG + NBUF * W_TILE;      // 4 scale slots of 128 floats
+  static constexpr int CHUNKS_A = A_TILE / 1024, CHUNKS_W = W_TILE / 1024;
+  static constexpr int LOADS = (CHUNKS_A + CHUNKS_W) / 4;  // copies per wave per stage
+  static constexpr int LDS_BYTES = S_REG + 4 * 512;
+  static_assert((CHUNKS_A + CHUNKS_W) % 4 == 0, "whole copies per wave");
+  static_assert(LDS_BYTES <= 81920, "two workgroups per compute unit");
+};
+
+__device__ __forceinline__ void gemm_copy_dword(uint32_t m0val, const i32x4& rsrc, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(m0val), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Signed nibbles 0..7 of w (nibble i = bits 4 i .. 4 i + 3) as bf16, element i.
+__device__ __forceinline__ bf16x8 int4x8_to_bf16(uint32_t w) {
+  uint32_t r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int lo = (int)(w << (28 - 8 * j)) >> 28, hi = (int)(w << (24 - 8 * j)) >> 28;
+    r[j] = pack_bf16x2((float)lo, (float)hi);
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(r[0], r[1], r[2], r[3]));
+}
+
+template <int WM>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w4a16_kernel(
+    const uint16_t* a, const uint8_t* w, const float* w_scale, uint16_t* y, int M, int N, int K, int G, int tm,
+    int tn) {
+  using Gm = W4Geom<WM>;
+  constexpr int BM = Gm::BM, BN = Gm::BN, NBUF = Gm::NBUF;
+  __shared__ __attribute__((aligned(1024))) char lds[Gm::LDS_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int nt = (slot / tm) * 8 + xcd, mt = slot % tm;
+  if (nt >= tn) return;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int KG = K / G;                                     // groups per row
+
+  const i32x4 ars = gemm_rsrc(a, (uint32_t)((uint64_t)M * (uint64_t)K * 2u));
+  const i32x4 wrs = gemm_rsrc(w, (uint32_t)((uint64_t)N * (uint64_t)K / 2u));
+  const i32x4 srs = gemm_rsrc(w_scale, (uint32_t)((uint64_t)N * (uint64_t)KG * 4u));
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&lds[0];
+
+  // copy lanes.  Activation chunk c (8 rows of 128 bytes): lane l fills row
+  // 8 c + l / 8, physical unit l % 8, holding logical unit (l % 8) ^ ((row >> 1) & 7),
+  // where (row >> 1) & 7 = (4 (c & 1) + l / 16) & 7.  Weight chunk (32 rows of
+  // 32 bytes): lane l fills row l / 2, physical unit l % 2, holding logical unit
+  // (l % 2) ^ ((l / 16) & 1).
+  uint32_t voffA[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    voffA[par] = (uint32_t)((lane >> 3) * 2 * K + 16 * ((lane & 7) ^ ((4 * par + (lane >> 4)) & 7)));
+  const uint32_t voffW = (uint32_t)((lane >> 1) * (K / 2) + 16 * ((lane & 1) ^ ((lane >> 4) & 1)));
+  const int nk = K / Gm::BK, GS = G / Gm::BK;              // stages, stages per group
+  auto copy_stage = [&](int s, int buf) {
+    const uint32_t kb = (uint32_t)(s * Gm::BK);
+#pragma unroll
+    for (int i = 0; i < Gm::LOADS; ++i) {
+      const int c = wave + 4 * i;
+      if (c < Gm::CHUNKS_A)
+        gemm_copy(lds0 + (uint32_t)(buf * Gm::A_TILE + c * 1024), ars,
+                  (uint32_t)(m0 + 8 * c) * (uint32_t)(2 * K) + 2u * kb, voffA[c & 1]);
+      else
+        gemm_copy(lds0 + (uint32_t)(Gm::W_REG + buf * Gm::W_TILE + (c - Gm::CHUNKS_A) * 1024), wrs,
+                  (uint32_t)(n0 + 32 * (c - Gm::CHUNKS_A)) * (uint32_t)(K / 2) + kb / 2u, voffW);
+    }
+    if (wave == 0 && s % GS == 0) {
+      const int g = s / GS;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        gemm_copy_dword(lds0 + (uint32_t)(Gm::S_REG + (g & 3) * 512 + 256 * j), srs,
+                        ((uint32_t)(n0 + 64 * j + lane) * (uint32_t)KG + (uint32_t)g) * 4u);
+    }
+  };
+
+  // operand read offsets: activation row 32 mb + l % 32, logical unit 4 h + ks;
+  // weight row 32 wave + l % 32, logical unit h
+  const int r32 = lane & 31, h = lane >> 5;
+  const uint32_t arow = (uint32_t)(r32 * 128);
+  const int asw = (r32 >> 1) & 7;                            // same for every row block (32 mb is even)
+  const int wr = 32 * wave + r32;
+  const uint32_t woff = (uint32_t)(Gm::W_REG + wr * 32 + 16 * (h ^ ((wr >> 3) & 1)));
+
+  f32x16 acc[WM], accg[WM];
+#pragma unroll
+  for (int i = 0; i < WM; ++i) acc[i] = {};
+
+  const int pro = min(NBUF - 1, nk);
+  for (int s = 0; s < pro; ++s) copy_stage(s, s);
+
+  auto step = [&](auto bc, int s) {
+    constexpr int BUF = decltype(bc)::value;
+    gemm_wait_stages<Gm::LOADS, NBUF - 2>(min(NBUF - 2, nk - 1 - s));
+    __syncthreads();                          // stage s in LDS; stage s - 1 consumed by every wave
+    if (s + NBUF - 1 < nk) copy_stage(s + NBUF - 1, (BUF + NBUF - 1) % NBUF);
+    const bool first = s % GS == 0;
+    const uint4 wq = *reinterpret_cast<const uint4*>(lds + woff + BUF * Gm::W_TILE);
+    const uint32_t wd[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 b = int4x8_to_bf16(wd[ks]);
+      const uint32_t au = (uint32_t)(16 * ((4 * h + ks) ^ asw));
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(lds + BUF * Gm::A_TILE + mb * 32 * 128 + arow + au);
+        if (ks == 0 && first) accg[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, f32x16{}, 0, 0, 0);
+        else accg[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, accg[mb], 0, 0, 0);
+      }
+    }
+    if (s % GS == GS - 1) {                   // the group's last stage: acc += s[n][g] * acc_g
+      const float sc = *reinterpret_cast<const float*>(lds + Gm::S_REG + ((s / GS) & 3) * 512 + 4 * wr);
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[mb][e] = fmaf(sc, accg[mb][e], acc[mb][e]);
+    }
+  };
+  for (int s = 0; s < nk; s += NBUF) {
+    bool more = true;
+    gemm_static_for<0, NBUF>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if (!more) return;
+      if (s + i >= nk) {
+        more = false;
+        return;
+      }
+      step(std::integral_constant<int, i>{}, s + i);
+    });
+  }
+
+  // epilogue: lane owns column n0 + 32 wave + l % 32 and rows 8 q + 4 h + r of each block
+  const int n = n0 + wr;
+  if (n < N) {
+#pragma unroll
+    for (int mb = 0; mb < WM; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 32 * mb + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m < M) y[(int64_t)m * N + n] = f32_to_bf16(acc[mb][e]);
+      }
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -234,6 +413,36 @@ pta_status taco_gemm_w8a8(const void* a, const float* a_scale, const void* w, co
     hipLaunchKernelGGL(gemm_w8a8_kernel<2>, dim3((unsigned)blocks), dim3(NT), 0, (hipStream_t)stream,
                        reinterpret_cast<const uint8_t*>(a), a_scale, reinterpret_cast<const uint8_t*>(w), w_scale,
                        reinterpret_cast<uint16_t*>(y), M, N, K, tm, tn);
+  return hipGetLastError() == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+}
+
+pta_status taco_gemm_w4a16(const void* a, const void* w, const float* w_scale, void* y, int32_t M, int32_t N,
+                           int32_t K, int32_t group, void* stream) {
+  if (!a || !w || !w_scale || !y) return PTA_ERR_NULL_PTR;
+  if (M < 1 || N < 1 || K < 64 || K % 64 != 0 || group < 64 || group % 64 != 0 || K % group != 0)
+    return PTA_ERR_BAD_DIMS;
+  if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(w)) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(w_scale) % 4 != 0)
+    return PTA_ERR_BAD_DIMS;
+  // row blocks of 64 rows up to 64 rows, else of 128
+  const bool tall = M > 64;
+  const int BM = tall ? W4Geom<4>::BM : W4Geom<2>::BM, BN = 128;
+  // every tile row (those past M or N included) must have a 32-bit buffer offset
+  const uint64_t mpad = (uint64_t)((M + BM - 1) / BM) * BM, npad = (uint64_t)((N + BN - 1) / BN) * BN;
+  if (mpad * (uint64_t)K * 2u >= ((uint64_t)1 << 32) || npad * (uint64_t)K / 2u >= ((uint64_t)1 << 32) ||
+      npad * (uint64_t)(K / group) * 4u >= ((uint64_t)1 << 32))
+    return PTA_ERR_BAD_DIMS;
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  const int64_t blocks = (int64_t)8 * tm * ((tn + 7) / 8);
+  if (blocks > 0x7fffffff) return PTA_ERR_BAD_DIMS;
+  if (tall)
+    hipLaunchKernelGGL(gemm_w4a16_kernel<4>, dim3((unsigned)blocks), dim3(NT), 0, (hipStream_t)stream,
+                       reinterpret_cast<const uint16_t*>(a), reinterpret_cast<const uint8_t*>(w), w_scale,
+                       reinterpret_cast<uint16_t*>(y), M, N, K, group, tm, tn);
+  else
+    hipLaunchKernelGGL(gemm_w4a16_kernel<2>, dim3((unsigned)blocks), dim3(NT), 0, (hipStream_t)stream,
+                       reinterpret_cast<const uint16_t*>(a), reinterpret_cast<const uint8_t*>(w), w_scale,
+                       reinterpret_cast<uint16_t*>(y), M, N, K, group, tm, tn);
   return hipGetLastError() == hipSuccess ? PTA_OK : PTA_ERR_HIP;
 }
 

@@ -204,3 +204,19 @@ def test_gemm_host_checks(lib):
     assert call(K=100) == DIMS and call(K=0) == DIMS and call(M=0) == DIMS and call(N=-1) == DIMS
     assert call(a=ctypes.c_void_p(0x10008)) == DIMS                 # not 16-byte aligned
     assert call(M=1 << 20, K=1 << 13) == DIMS                       # rows x K past 32-bit offsets
+
+
+def test_gemm_w4a16_host_checks(lib):
+    """taco_gemm_w4a16 rejects bad arguments on the host, before any HIP call."""
+    f = lib.taco_gemm_w4a16
+    ok = dict(a=FAKE, w=FAKE, s=FAKE, y=FAKE, M=4, N=4, K=256, G=128)
+    def call(**kw):
+        d = dict(ok, **kw)
+        return f(d["a"], d["w"], d["s"], d["y"], d["M"], d["N"], d["K"], d["G"], None)
+    assert call(a=None) == NULLP and call(w=None) == NULLP and call(s=None) == NULLP and call(y=None) == NULLP
+    assert call(K=100) == DIMS and call(K=0) == DIMS and call(M=0) == DIMS and call(N=-1) == DIMS
+    assert call(G=96) == DIMS and call(G=32) == DIMS and call(G=0) == DIMS   # group: a multiple of 64
+    assert call(K=192, G=128) == DIMS                                       # group must divide K
+    assert call(a=ctypes.c_void_p(0x10008)) == DIMS                         # not 16-byte aligned
+    assert call(s=ctypes.c_void_p(0x10002)) == DIMS                         # scales not 4-byte aligned
+    assert call(M=1 << 20, K=1 << 12) == DIMS                               # 2 K bytes x rows past 2^32

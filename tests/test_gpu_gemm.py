@@ -1,4 +1,5 @@
-"""GPU parity of the W8A8 GEMM (taco_gemm_w8a8, include/pta_gemm.h) against the fp64 oracle.
+"""GPU parity of the quantized GEMMs (taco_gemm_w8a8, taco_gemm_w4a16; include/pta_gemm.h) against the
+fp64 oracle.  W8A8:
 
 Bound per output, from the arithmetic: the products of two e4m3fn values are exact in float32,
 the matrix core adds them in float32 (K / 64 accumulator updates), the scales multiply the
@@ -123,3 +124,130 @@ def test_w8a8_argument_checks(torch_cuda):
     s = torch.ones(8, dtype=torch.float32, device="cuda")
     with pytest.raises(psv.PtaError):
         psv.taco_gemm_w8a8(a, s, w, s)
+
+
+# ------------------------------------------------------------------ W4A16
+# Bound per output, from the arithmetic: every int4 weight converts exactly to bf16, the products
+# bf16 x bf16 are exact in float32, each group's sum is a float32 matrix-core sum of group / 16
+# accumulator updates, the group scale multiplies it in float32 and the groups add in float32;
+# the result is rounded to bf16:
+#     |y - y_ref| <= 2^-8 |y_ref| + 2^-14 * S,   S = sum_k |a_mk| |q_nk| w_scale[n, k / group]
+# (the same form as W8A8's: 2^-8 covers the bf16 result, 2^-14 S is far above the float32 sums).
+from oracle.formats import decode_bf16  # noqa: E402
+from workload.gemm import W4A16, make_w4a16, make_w4a16_device, pack_int4  # noqa: E402
+
+
+def run4(torch, g, rows=None):
+    import paged_speculative_verify_amd as psv
+    a = torch.from_numpy(np.ascontiguousarray(g.a_bits).view(np.int16)).cuda().view(torch.bfloat16)
+    w = torch.from_numpy(np.ascontiguousarray(g.w_packed)).cuda()
+    s = torch.from_numpy(np.ascontiguousarray(g.w_scale)).cuda()
+    y = psv.taco_gemm_w4a16(a, w, s, g.group)
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy().astype(np.float64)
+    return y if rows is None else y[rows]
+
+
+def bound4(a_bits, w_packed, w_scale, group, y):
+    """(reference, bound) of W4A16 outputs, column chunk by column chunk (the decoded weights of a
+    full-size matrix would not fit in memory at once)."""
+    K = a_bits.shape[1]
+    A = np.abs(decode_bf16(a_bits))
+    ref = np.empty(y.shape)
+    S = np.empty(y.shape)
+    for c0 in range(0, w_packed.shape[0], 4096):
+        c1 = min(c0 + 4096, w_packed.shape[0])
+        ref[:, c0:c1] = oracle.w4a16_gemm(a_bits, w_packed[c0:c1], w_scale[c0:c1], group)
+        q = np.abs(oracle.decode_int4_packed(w_packed[c0:c1], K)).astype(np.float64)
+        S[:, c0:c1] = A @ (q * np.repeat(w_scale[c0:c1].astype(np.float64), group, axis=1)).T
+    return ref, 2.0 ** -8 * np.abs(ref) + 2.0 ** -14 * S
+
+
+def check4(g, y, rows=None):
+    sel = slice(None) if rows is None else rows
+    ref, bound = bound4(g.a_bits[sel], g.w_packed, g.w_scale, g.group, y)
+    err = np.abs(y - ref)
+    assert np.isfinite(y).all()
+    assert (err <= bound).all(), f"worst excess {float((err - bound).max())}"
+    return float((err / np.maximum(bound, 1e-30)).max())
+
+
+W4_CASES = [
+    ("one_by_one", 1, 1, 64, 64, 41),
+    ("ragged_small", 37, 200, 256, 128, 42),
+    ("ragged_tall", 130, 260, 384, 128, 43),
+    ("group64_tall", 300, 1100, 1024, 64, 44),
+    ("single_group", 70, 300, 512, 512, 45),
+    ("decode_rows", 64, 2048, 8192, 128, 46),
+]
+
+
+@pytest.mark.parametrize("cid,M,N,K,G,seed", W4_CASES, ids=[c[0] for c in W4_CASES])
+def test_w4a16_parity(torch_cuda, cid, M, N, K, G, seed):
+    g = make_w4a16(M, N, K, G, seed=seed)
+    say(cid, M, N, K, G)
+    y = run4(torch_cuda, g)
+    r = check4(g, y)
+    say(cid, "worst error / bound", r)
+
+
+def test_w4a16_full_size_sampled_rows(torch_cuda):
+    """Llama-3.1-70B gate+up at the verify step's 512 rows, group 128 (the timed shape): operands
+    drawn on the GPU, rows spanning both tile rows checked against the oracle."""
+    import torch
+    import paged_speculative_verify_amd as psv
+    s = LLAMA70B_GATE_UP
+    M, N, K, G = s["M"], s["N"], s["K"], 128
+    a, w, sc = make_w4a16_device(M, N, K, G, seed=7, torch=torch)
+    rows = np.array([0, 127, 128, 300, 511])
+    say("full size", s, "group", G, "rows", rows.tolist())
+    y = psv.taco_gemm_w4a16(a, w, sc, G)
+    torch.cuda.synchronize()
+    yr = y.float().cpu().numpy().astype(np.float64)[rows]
+    a_bits = a.view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+    ref, bound = bound4(a_bits, w.cpu().numpy(), sc.cpu().numpy(), G, yr)
+    err = np.abs(yr - ref)
+    assert np.isfinite(yr).all()
+    assert (err <= bound).all(), f"worst excess {float((err - bound).max())}"
+
+
+@pytest.mark.parametrize("M,N,K,G", [(40, 90, 256, 128), (200, 300, 512, 64)], ids=["short_rows", "tall_rows"])
+def test_w4a16_integer_exact(torch_cuda, M, N, K, G):
+    """Small integer activations and power-of-two group scales: every product, group sum, scaled
+    group and total is exact in float32, so the output is the bf16 rounding of the exact result."""
+    import torch
+    rng = np.random.default_rng(11)
+    ai = rng.integers(-4, 5, (M, K))
+    q = rng.integers(-8, 8, (N, K))
+    sc = (2.0 ** rng.integers(-3, 3, (N, K // G))).astype(np.float32)
+    from workload.gemm import bf16_bits_of
+    g = W4A16(bf16_bits_of(ai.astype(np.float32)), pack_int4(q), sc, G)
+    say("integer exact", M, N, K, G)
+    y = run4(torch_cuda, g)
+    exact = ai.astype(np.float64) @ (q.astype(np.float64) * np.repeat(sc.astype(np.float64), G, axis=1)).T
+    want = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(y, want)
+
+
+def test_w4a16_nan_rows(torch_cuda):
+    """A NaN activation makes its output row NaN and leaves the others finite."""
+    g = make_w4a16(40, 130, 256, 128, seed=9)
+    g.a_bits[3, 17] = 0x7FC0
+    y = run4(torch_cuda, g)
+    assert np.isnan(y[3]).all()
+    assert np.isfinite(np.delete(y, 3, axis=0)).all()
+
+
+def test_w4a16_argument_checks(torch_cuda):
+    import torch
+    import paged_speculative_verify_amd as psv
+    a = torch.zeros((8, 192), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((8, 96), dtype=torch.uint8, device="cuda")
+    s = torch.ones((8, 3), dtype=torch.float32, device="cuda")
+    with pytest.raises(psv.PtaError):                     # group 32: not a multiple of 64
+        psv.taco_gemm_w4a16(a, w, torch.ones((8, 6), dtype=torch.float32, device="cuda"), 32)
+    y = psv.taco_gemm_w4a16(a, w, s, 64)                  # K = 192, group 64: served
+    torch.cuda.synchronize()
+    assert float(y.float().abs().max()) == 0.0
+    with pytest.raises(ValueError):
+        psv.taco_gemm_w4a16(a, w, s, 128)                 # 128 does not divide 192

@@ -59,3 +59,60 @@ def make_w8a8_device(M: int, N: int, K: int, seed: int, torch, device="cuda"):
         out += [q.to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), scale.contiguous()]
         del x, q
     return tuple(out)
+
+
+@dataclass
+class W4A16:
+    a_bits: np.ndarray     # uint16 [M, K] bf16 bit patterns
+    w_packed: np.ndarray   # uint8 [N, K / 2]: k = 2 j in the low nibble of byte j, 2 j + 1 in the high
+    w_scale: np.ndarray    # float32 [N, K / group]
+    group: int
+
+
+def bf16_bits_of(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (torch's cast)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy() \
+        .view(np.uint16)
+
+
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """int [N, K] in -8..7 -> uint8 [N, K / 2], two's complement nibbles, low nibble first."""
+    u = (np.asarray(q, np.int64) & 0xF).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def quantize_int4_groups(w: np.ndarray, group: int):
+    """Symmetric group quantization of float32 [N, K]: scale = max |x| / 7 over each group of
+    `group` consecutive k (1.0 for an all-zero group), q = round-half-even(x / scale) clipped to
+    -8..7.  Returns (q int8 [N, K], scale float32 [N, K / group])."""
+    N, K = w.shape
+    g = w.reshape(N, K // group, group)
+    amax = np.abs(g).max(axis=2)
+    scale = np.where(amax > 0, amax / 7.0, 1.0).astype(np.float32)
+    q = np.clip(np.rint(g / scale[:, :, None]), -8, 7).astype(np.int8).reshape(N, K)
+    return q, scale
+
+
+def make_w4a16(M: int, N: int, K: int, group: int = 128, seed: int = 0) -> W4A16:
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((M, K), dtype=np.float32)
+    w = rng.standard_normal((N, K), dtype=np.float32)
+    q, scale = quantize_int4_groups(w, group)
+    return W4A16(bf16_bits_of(a), pack_int4(q), scale, group)
+
+
+def make_w4a16_device(M: int, N: int, K: int, group: int, seed: int, torch, device="cuda"):
+    """The same recipe drawn on the GPU: returns (a bf16 [M, K], w_packed uint8 [N, K / 2],
+    w_scale float32 [N, K / group]) device tensors."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    a = torch.randn((M, K), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16).contiguous()
+    w = torch.randn((N, K // group, group), generator=g, device=device, dtype=torch.float32)
+    amax = w.abs().amax(dim=2)
+    scale = torch.where(amax > 0, amax / 7.0, torch.ones_like(amax))
+    q = torch.round(w / scale[:, :, None]).clamp(-8, 7).to(torch.int32).reshape(N, K)
+    del w
+    u = (q & 0xF).to(torch.uint8)
+    packed = (u[:, 0::2] | (u[:, 1::2] << 4)).contiguous()
+    return a, packed, scale.contiguous()
