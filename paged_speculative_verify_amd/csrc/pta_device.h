@@ -300,23 +300,29 @@ struct PartSlot {
 // its normalised partial output and log-sum-exp are stored with
 // store_coherent.  The last unit of (b, hkv) to arrive merges the partitions
 // of all its rows and resets the arrival counter to zero for the next call.
-// Ordering through the memory model: every thread's agent-scope release fence
-// orders its partial stores before the workgroup barrier, and the barrier
-// before thread 0's acq_rel arrival at agent scope; in the last arriver, that
-// arrival (acquire) and the barrier come before every thread's agent-scope
-// acquire fence, which comes before its partial loads.
+// Ordering through the memory model, with one agent-scope release per arrival
+// and one acquire per unit: every wave's partial stores complete (vmcnt) and
+// precede the workgroup barrier; the barrier precedes thread 0's release
+// arrival at agent scope (release is cumulative over what happens before it);
+// the last arriver's thread 0 follows its arrival with an agent-scope acquire
+// fence, and the second barrier orders that fence before every thread's
+// partial loads.  (A release and an acquire in every wave of every arrival
+// write back and invalidate the L2 several times per unit: on the
+// shared-prefix decode entry that measured 3.5x slower.)
 template <typename QT, int D>
 __device__ __forceinline__ void splitk_finish(const AttnArgs& a, int b, int hkv, int C, int qb) {
   __shared__ int s_last;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): this wave's partial stores are complete
   __syncthreads();
   const int np = (C + a.part_tokens - 1) / a.part_tokens;
   int32_t* cnt = a.counters + (int64_t)b * a.Hkv + hkv;
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
+  if (threadIdx.x == 0) {
+    const bool last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_last = last;
+  }
   __syncthreads();
   if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   auto slot = [&](int r, int p) {
     const int h = hkv * a.G + r / qb, i = r % qb;
     const int64_t prow = (((int64_t)b * a.Hq + h) * a.Qmax + i) * a.num_parts + p;
