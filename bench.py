@@ -555,7 +555,6 @@ def extra_workload(psv, torch, name, args):
 
 # ------------------------------------------------------------------ quantized GEMM
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
-BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 W4_GROUP = 128
 GEMM_SHAPES = {
     # Llama-3.1-70B MLP gate + up projections (N = 2 x 28672, K = 8192) over the verify step's
