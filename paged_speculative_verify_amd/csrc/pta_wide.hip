@@ -252,15 +252,6 @@ __device__ __forceinline__ f32x16 wide_scores(const WideRows<D>& R, const WideOf
   for (int ks = 0; ks < D / 16; ++ks) k[ks] = *reinterpret_cast<const bf16x8*>(lds + W.k[ks] + KB);
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[ks], R.qop[ks], s, 0, 0, 0);
-  // keep three operand reads in flight ahead of the products
-  constexpr int KS = D / 16, AHEAD = 3;
-  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
-#pragma unroll
-  for (int i = 0; i < KS - AHEAD; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
   return s;
 }
 
@@ -344,7 +335,6 @@ __device__ __forceinline__ void wide_pv(WideState<D>& st, const WideOffsets<D>& 
     va[db] = rd(W.v[db][0] + VB);
     vb[db] = rd(W.v[db][1] + VB);
   }
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat(va[db], vb[db]), p[0], st.o[db], 0, 0, 0);
@@ -471,23 +461,36 @@ __device__ __forceinline__ void wide_range(const AttnArgs& a, char* lds, uint32_
       __syncthreads();
     }
     if ((s & 3) == 0) pace(prog0 + 2 * s, prog_len);
-    if (s + NBUF - 1 < nst) copy_stage(s + NBUF - 1, ph, PREV);
+    if (s + NBUF - 1 < nst) {
+      copy_stage(s + NBUF - 1, ph, PREV);
+      if (s + NBUF < nst) page_ids(s + NBUF, ph);
+    }
     if (wave_rows) {
       if (pend) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) st.o[db] *= alpha;
       }
       xn = wide_scores<D, Gm::tile_lds(BUF, 0)>(R, W, lds);            // S of pair s + 1
-    }
-    // next stage's page ids, issued after the score reads so that their waits
-    // do not include the table load
-    asm volatile("" ::: "memory");
-    if (s + NBUF < nst) page_ids(s + NBUF, ph);
-    asm volatile("" ::: "memory");
-    if (wave_rows) {
       bf16x8 p[2];
       wide_p<D>(st, x, c, p);                                          // P of pair s
       wide_pv<D, BUF * Gm::PAIR>(st, W, p, lds);                       // P.V of pair s
+      // K reads three ahead; each score product of pair s + 1 followed by six vector
+      // instructions of pair s's P; the V^T reads of the first page, then each P.V
+      // product of the first page followed by the matching reads of the second
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 5) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x080, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x080, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       const int pbn = (pgA + 2 * (s + 1)) * kPage;
       if (pbn + 2 * kPage > plain_end) wide_mask(xn, R.mbits, pbn, L, t1, lane);
       float pm;
