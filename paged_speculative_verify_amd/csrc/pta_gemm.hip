@@ -1,22 +1,25 @@
-// W8A8 GEMM on gfx950 fp8 matrix cores (include/pta_gemm.h): the quantized
+// Quantized GEMMs on gfx950 matrix cores (include/pta_gemm.h): the quantized
 // GEMM operators the TACO-LLM pages list beside the attention kernels
 // (17173xz.com article, section "TACO-LLM如何实现降本增效?"; 618zxw.cn article,
 // section "LLM量子化技術による推論コストの削減"; design talk section
-// "5. 支持 Quantization（模型量化）": 8-bit weights on low-precision matrix
-// instructions).
+// "5. 支持 Quantization（模型量化）": low-bit weights on low-precision matrix
+// instructions).  W8A8 first, W4A16 below.
 //
-//   * Workgroup tile 128 (M) x 128 (N), four waves of 64 x 64 (2 x 2 blocks of
-//     v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales: e4m3fn x e4m3fn,
-//     float32 accumulators).  A lane supplies 32 consecutive k-bytes of its row
-//     of A and of its column of W^T (k = 32 h + 0..31 of the 64-step, h = lane
-//     / 32); any consistent assignment of k to (lane half, byte) gives the same
-//     sums, and this one makes each operand two 16-byte LDS reads.
-//   * k-steps of 64 bytes staged in LDS (A tile 8 KiB + W tile 8 KiB), four
-//     stages, three in flight, moved by buffer_load_dwordx4 ... lds (the buffer
-//     resource's size makes rows past M or N read as zero, so ragged edges need
-//     no other handling).  16-byte units of a row are swizzled by the row's bits
-//     2..3, so the 16 rows one pass of an operand read touches hit 16 distinct
-//     bank groups.
+// W8A8:
+//   * Workgroup tile 128 (M) x 64 WNB (N), four waves of 64 x 32 WNB (2 x WNB
+//     blocks of v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales:
+//     e4m3fn x e4m3fn, float32 accumulators); WNB = 2 up to 128 rows, 4 above
+//     (each activation tile then feeds twice the columns).  A lane supplies 32
+//     consecutive k-bytes of its row of A and of its column of W^T (k = 32 h +
+//     0..31 of the 64-step, h = lane / 32); any consistent assignment of k to
+//     (lane half, byte) gives the same sums, and this one makes each operand two
+//     16-byte LDS reads.
+//   * k-steps of 64 bytes staged in LDS (A tile 8 KiB + W tile 8 or 16 KiB),
+//     four or three stages, moved by buffer_load_dwordx4 ... lds with the whole
+//     offset in the range-checked vector offset, so rows past M or N read as
+//     zero and ragged edges need no other handling.  16-byte units of a row are
+//     swizzled by the row's bits 2..3, so the 16 rows one pass of an operand
+//     read touches hit 16 distinct bank groups.
 //   * Workgroups are numbered so that the M tiles of one N tile run one after
 //     the other on the same XCD: its weight tile reaches that XCD's L2 from HBM
 //     once for all of them.

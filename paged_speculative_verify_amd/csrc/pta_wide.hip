@@ -24,14 +24,18 @@
 //     moves whole page tiles (one m0 setup, the chunks addressed by the
 //     instruction's offset field, the page by a scalar offset), so a copy
 //     costs no vector address arithmetic.  The buffer resource's size bounds
-//     every read to the cache tensor.  Page ids arrive by scalar loads one
-//     stage ahead.
+//     the in-tile offsets; the page base rides in the scalar offset, outside
+//     the range check, so page ids must name pool pages (the call's contract).
+//     Page ids arrive by scalar loads one stage ahead.
 //   * Row sums take the bf16 P values already packed for the matrix core
 //     (v_dot2c_f32_bf16 against (1, 1)), so l is the sum of exactly the
 //     weights P.V used.
 //   * Tiles are swizzled so that both operand reads touch every LDS bank once
 //     per pass (wide_unit): no bank conflicts (the 16x16x32 kernel's layout
 //     costs its reads about a quarter of the compute unit's cycles here).
+//   * One schedule per stage (scheduling groups): K reads three products ahead,
+//     the vector work of pair s's P between pair s + 1's score products, a
+//     page's V^T reads ahead of its P.V products.
 // Measured on the widest tree (256 rows per KV head, 32K-128K tokens), the
 // call is 4-5% faster than the 16x16x32 kernel's on the same box; with the
 // copies and the per-stage barrier taken out (a timing-only build) the same
