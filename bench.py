@@ -50,15 +50,16 @@ SETTLE_S = 0.3                 # untimed steps after the warm-up, before any mea
 # sequence, "split": split-K partitions of `split` tokens, "balanced": equal
 # page slices per wave of a persistent grid) and kernel family (auto picks by
 # rows per KV head); fuse_append: the step's KV append runs inside the
-# attention launch (taco_paged_tree_attn_append) instead of as taco_kv_append
-# before it.  Fused where that measured faster; on the fp8 chain workload (1024
-# workgroups, each encoding 8 candidates) the in-kernel append costs what the
-# separate launch does.
+# attention launch (taco_paged_tree_attn_append for the whole-context entry,
+# taco_paged_tree_attn_balanced_append for the balanced one) instead of as
+# taco_kv_append before it.  Fused where that measured faster; on the fp8 chain
+# workload (1024 workgroups, each encoding 8 candidates) the in-kernel append
+# costs what the separate launch does.
 LAUNCH = {
     "tiny_decode": dict(mode="whole", split=None, path="auto"),
     "llama3_8b_decode": dict(mode="whole", split=None, path="auto", fuse_append=True),
-    "llama31_70b_verify": dict(mode="balanced", split=None, path="auto"),
-    "long_splitk_verify": dict(mode="balanced", split=None, path="auto"),
+    "llama31_70b_verify": dict(mode="balanced", split=None, path="auto", fuse_append=True),
+    "long_splitk_verify": dict(mode="balanced", split=None, path="auto", fuse_append=True),
     "fp8_kv_chain": dict(mode="whole", split=None, path="auto"),
     "shared_prefix_decode": dict(mode="whole", split=None, path="auto", fuse_append=True),
 }
@@ -378,8 +379,8 @@ def resolve_cfg(name, args):
         if CONFIGS[name].shared_prefix_pages <= 0 or args.private_pages:
             raise SystemExit("--shared-entry needs a shared-prefix workload on shared pages")
         cfg["mode"], cfg["split"] = "shared", CONFIGS[name].shared_prefix_pages * 16
-    if cfg["mode"] != "whole" or args.path not in (None, "auto") or args.separate_append:
-        cfg.pop("fuse_append", None)      # the fused append lives in the whole-context stream kernel
+    if cfg["mode"] not in ("whole", "balanced") or args.path not in (None, "auto") or args.separate_append:
+        cfg.pop("fuse_append", None)      # the fused appends live in the whole-context and wide grids
     return cfg
 
 
@@ -411,7 +412,7 @@ def build_sets(psv, torch, name, cfg, nsets, private_pages=False):
             ds.append_call = psv.prepare_kv_append(ds.k_new, ds.v_new, ds.slots, d.k_cache, d.v_cache,
                                                    k_scale=d.k_scale, v_scale=d.v_scale)
         ds.attn_call = psv.prepare_paged_tree_attn(
-            "whole_append" if cfg.get("fuse_append") else cfg["mode"],
+            cfg["mode"] + "_append" if cfg.get("fuse_append") else cfg["mode"],
             d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens, d.tree_mask,
             d.scale, ds.out, lse=ds.lse, k_scale=d.k_scale, v_scale=d.v_scale,
             partition_tokens=cfg["split"], workspace=ds.workspace, max_ctx_len=d.max_ctx_len,

@@ -249,6 +249,28 @@ pta_status taco_paged_tree_attn_balanced(const pta_dims* dims, const void* q, co
                                          float* lse, void* workspace, size_t workspace_bytes,
                                          void* stream);
 
+/* The verify step's KV append fused into the balanced entry (as
+ * taco_paged_tree_attn_append does for the whole-context one): every
+ * sequence's q_lens[b] candidate K and V rows are written into their paged
+ * slots (logical positions ctx_lens[b] - q_lens[b] ...), then attention runs as
+ * in taco_paged_tree_attn_balanced over the updated cache, in the same grid.
+ * Inside the grid, each slice writes the candidates that lie on its own pages
+ * before it copies them, so the step needs no separate append launch.
+ *   k_new, v_new  [num_seqs][max_q_len][num_kv_heads][head_dim] bf16, 16-byte
+ *                 aligned (else PTA_ERR_BAD_DIMS), rows past q_lens ignored;
+ *                 new_dtype must be PTA_BF16 (else PTA_ERR_BAD_DTYPE).
+ * Served where the balanced entry runs its 32x32x16-product shared-tile grid
+ * (bf16 q and KV, more than 32 rows per KV head or path PTA_PATH_TILE, caches
+ * addressable with 32-bit offsets), else PTA_ERR_UNSUPPORTED (use
+ * taco_kv_append, then taco_paged_tree_attn_balanced).  Workspace and other
+ * arguments as taco_paged_tree_attn_balanced. */
+pta_status taco_paged_tree_attn_balanced_append(const pta_dims* dims, const void* q, const void* k_new,
+                                                const void* v_new, int32_t new_dtype, void* k_cache,
+                                                void* v_cache, const int32_t* block_tables,
+                                                const int32_t* ctx_lens, const int32_t* q_lens,
+                                                const uint8_t* tree_mask, float scale, void* out, float* lse,
+                                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Largest balanced-entry workspace, in bytes, that
  * taco_paged_tree_attn_balanced_noalloc can serve (64 MiB). */
 #define PTA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)

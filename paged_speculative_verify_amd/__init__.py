@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     taco_la_tree_mask,
     NOALLOC_SCRATCH_BYTES,
     taco_paged_tree_attn_balanced,
+    taco_paged_tree_attn_balanced_append,
     taco_paged_tree_attn_balanced_noalloc,
     taco_paged_tree_attn_balanced_workspace_size,
     taco_paged_tree_attn,

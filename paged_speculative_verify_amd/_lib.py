@@ -78,6 +78,8 @@ def load() -> ctypes.CDLL:
     lib.taco_paged_tree_attn_splitk.restype = ctypes.c_int
     lib.taco_paged_tree_attn_append.argtypes = [D, P, P, P, I32, P, P, P, P, P, P, P, P, F, P, P, P]
     lib.taco_paged_tree_attn_append.restype = ctypes.c_int
+    lib.taco_paged_tree_attn_balanced_append.argtypes = [D, P, P, P, I32, P, P, P, P, P, P, F, P, P, P, SZ, P]
+    lib.taco_paged_tree_attn_balanced_append.restype = ctypes.c_int
     lib.taco_paged_tree_attn_shared_prefix.argtypes = [D, P, P, P, P, P, P, P, P, P, P, I32, I32, F, P, P, P,
                                                        SZ, P]
     lib.taco_paged_tree_attn_shared_prefix.restype = ctypes.c_int
@@ -197,7 +199,7 @@ def make_dims(q, k_cache, block_tables, max_ctx_len=None, path="auto") -> PtaDim
                    path=PATHS[path], reserved=0)
 
 
-def _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale):
+def _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale, scales=True):
     torch = _torch()
     _need(q, "q", 4)
     dev = q.device
@@ -215,7 +217,7 @@ def _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, 
         _need(tree_mask, "tree_mask", 3, torch.uint8, dev)
         if tuple(tree_mask.shape) != (B, Qmax, Qmax):
             raise ValueError(f"tree_mask must be [{B}, {Qmax}, {Qmax}]")
-    if _kv_code(k_cache) == PTA_FP8_E4M3FN:
+    if scales and _kv_code(k_cache) == PTA_FP8_E4M3FN:
         for nm, s in (("k_scale", k_scale), ("v_scale", v_scale)):
             if s is None:
                 raise ValueError(f"{nm} is required for an fp8 cache")
@@ -314,6 +316,39 @@ def taco_paged_tree_attn_append(q, k_new, v_new, k_cache, v_cache, block_tables,
         ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new), _q_code(k_new), _ptr(k_cache), _ptr(v_cache),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask),
         float(scale), _ptr(out), _ptr(lse), _stream(stream)))
+    return out
+
+
+def taco_paged_tree_attn_balanced_append(q, k_new, v_new, k_cache, v_cache, block_tables, ctx_lens, q_lens,
+                                         tree_mask, scale, out=None, lse=None, workspace=None, max_ctx_len=None,
+                                         path="auto", stream=None):
+    """KV append fused into the balanced entry (see include/pta.h): bf16 k_new, v_new
+    [B, Qmax, Hkv, D] written into their paged slots by the grid before it reads them.
+
+    workspace: as taco_paged_tree_attn_balanced (allocated zero-filled here if None).
+    """
+    torch = _torch()
+    lib = load()
+    # no scales: an fp8 cache is passed through, for the library to refuse (bf16 caches only)
+    _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, None, None, scales=False)
+    B, Qmax, Hq, D = q.shape
+    _need(k_new, "k_new", 4, torch.bfloat16, q.device)
+    _need(v_new, "v_new", 4, torch.bfloat16, q.device)
+    if tuple(k_new.shape) != (B, Qmax, k_cache.shape[1], D) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k_new / v_new must be [B, Qmax, Hkv, D]")
+    out, lse = _alloc_out(q, out, lse)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    need = int(lib.taco_paged_tree_attn_balanced_workspace_size(ctypes.byref(dims)))
+    if workspace is None:
+        if need == 0:
+            raise PtaError(4, "the balanced mode does not serve these dims")
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    else:
+        _need(workspace, "workspace", device=q.device)
+    _check(lib.taco_paged_tree_attn_balanced_append(
+        ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new), _q_code(k_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask), float(scale), _ptr(out), _ptr(lse),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 
@@ -608,7 +643,8 @@ def prepare_paged_tree_attn(mode, q, k_cache, v_cache, block_tables, ctx_lens, q
     mode: "whole" (taco_paged_tree_attn), "whole_append" (taco_paged_tree_attn_append with k_new,
     v_new), "split" (taco_paged_tree_attn_splitk with
     partition_tokens), "shared" (taco_paged_tree_attn_shared_prefix with partition_tokens =
-    shared tokens, prefix_leader and max_group) or "balanced" (taco_paged_tree_attn_balanced).  out (and, for
+    shared tokens, prefix_leader and max_group), "balanced" (taco_paged_tree_attn_balanced) or
+    "balanced_append" (taco_paged_tree_attn_balanced_append with k_new, v_new).  out (and, for
     split/balanced, a zero-initialised workspace of sufficient size) must be given.
     """
     torch = _torch()
@@ -651,11 +687,18 @@ def prepare_paged_tree_attn(mode, q, k_cache, v_cache, block_tables, ctx_lens, q
                 int(max_group), int(partition_tokens), float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
                 wbytes, st)
         return PreparedCall(lib.taco_paged_tree_attn_shared_prefix, args, keep + (prefix_leader,))
-    if mode == "balanced":
+    if mode in ("balanced", "balanced_append"):
         need = int(lib.taco_paged_tree_attn_balanced_workspace_size(ctypes.byref(dims)))
         if need == 0 or need > wbytes:
             raise ValueError(f"balanced workspace must hold {need} bytes (0: dims not served)")
-        return PreparedCall(lib.taco_paged_tree_attn_balanced, common + (_ptr(workspace), wbytes, st), keep)
+        if mode == "balanced":
+            return PreparedCall(lib.taco_paged_tree_attn_balanced, common + (_ptr(workspace), wbytes, st), keep)
+        _need(k_new, "k_new", 4, torch.bfloat16, q.device)
+        _need(v_new, "v_new", 4, torch.bfloat16, q.device)
+        args = (ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new), _q_code(k_new), _ptr(k_cache),
+                _ptr(v_cache), _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask), float(scale),
+                _ptr(out), _ptr(lse), _ptr(workspace), wbytes, st)
+        return PreparedCall(lib.taco_paged_tree_attn_balanced_append, args, keep + (k_new, v_new))
     raise ValueError(f"unknown mode {mode!r}")
 
 

@@ -257,12 +257,13 @@ pta_status scratch_for_current_device(void** out) {
 }
 
 // Balanced entry body: workspace from the caller, or (noalloc) this device's
-// copy of `scratch`, whose size is the limit.
+// copy of `scratch`, whose size is the limit; k_new / v_new (bf16 rows) set by
+// the fused-append entry, which only the 32x32x16 grid serves.
 pta_status balanced_call(const pta_dims* d, const void* q, const void* k_cache, const void* v_cache,
                          const float* k_scale, const float* v_scale, const int32_t* block_tables,
                          const int32_t* ctx_lens, const int32_t* q_lens, const uint8_t* tree_mask, float scale,
                          void* out, float* lse, void* workspace, size_t workspace_bytes, bool noalloc,
-                         hipStream_t stream) {
+                         hipStream_t stream, const void* k_new = nullptr, const void* v_new = nullptr) {
   pta_status st = check_dims(d);
   if (st != PTA_OK) return st;
   if (!isfinite(scale)) return PTA_ERR_BAD_DIMS;
@@ -270,6 +271,7 @@ pta_status balanced_call(const pta_dims* d, const void* q, const void* k_cache, 
   st = plan_for(d, &p);
   if (st != PTA_OK) return st;
   if (p.fam != FAM_STREAM && !(p.fam == FAM_TILE && d->kv_dtype == PTA_BF16)) return PTA_ERR_UNSUPPORTED;
+  if (k_new != nullptr && !(p.fam == FAM_TILE && wide_tiles(d))) return PTA_ERR_UNSUPPORTED;
   if (d->num_seqs == 0) return PTA_OK;
   st = check_attn_ptrs(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
                        tree_mask, out);
@@ -288,6 +290,8 @@ pta_status balanced_call(const pta_dims* d, const void* q, const void* k_cache, 
   }
   AttnArgs a = make_args(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens,
                          tree_mask, scale, out, lse);
+  a.k_new = k_new;
+  a.v_new = v_new;
   char* ws = reinterpret_cast<char*>(workspace);
   a.counters = nullptr;                  // both balanced grids merge in a second launch
   a.part_o = reinterpret_cast<float*>(ws + L.o_off);
@@ -461,6 +465,21 @@ pta_status taco_paged_tree_attn_balanced(const pta_dims* d, const void* q, const
                                          void* workspace, size_t workspace_bytes, void* stream) {
   return balanced_call(d, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, q_lens, tree_mask, scale,
                        out, lse, workspace, workspace_bytes, false, (hipStream_t)stream);
+}
+
+pta_status taco_paged_tree_attn_balanced_append(const pta_dims* d, const void* q, const void* k_new,
+                                                const void* v_new, int32_t new_dtype, void* k_cache, void* v_cache,
+                                                const int32_t* block_tables, const int32_t* ctx_lens,
+                                                const int32_t* q_lens, const uint8_t* tree_mask, float scale,
+                                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                                void* stream) {
+  if (d == nullptr) return PTA_ERR_NULL_PTR;
+  if (new_dtype != PTA_BF16) return PTA_ERR_BAD_DTYPE;   // rows in the cache's dtype (bf16 caches only)
+  if (!k_new || !v_new) return PTA_ERR_NULL_PTR;
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) % 16 != 0)
+    return PTA_ERR_BAD_DIMS;                              // rows are moved in 16-byte chunks
+  return balanced_call(d, q, k_cache, v_cache, nullptr, nullptr, block_tables, ctx_lens, q_lens, tree_mask, scale,
+                       out, lse, workspace, workspace_bytes, false, (hipStream_t)stream, k_new, v_new);
 }
 
 pta_status taco_paged_tree_attn_balanced_noalloc(const pta_dims* d, const void* q, const void* k_cache,

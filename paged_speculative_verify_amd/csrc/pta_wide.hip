@@ -37,12 +37,14 @@
 //     the vector work of pair s's P between pair s + 1's score products, a
 //     page's V^T reads ahead of its P.V products.
 // Measured on the widest tree (256 rows per KV head, 32K-128K tokens), the
-// call is 4-5% faster than the 16x16x32 kernel's on the same box; with the
-// copies and the per-stage barrier taken out (a timing-only build) the same
-// arithmetic takes about 22% less time than the whole kernel.
+// call is 4-5% faster than the 16x16x32 kernel's, measured back to back; with
+// the copies and the per-stage barrier taken out (a timing-only build) the
+// same arithmetic takes about 22% less time than the whole kernel.
 // Pipeline, stages and masks follow the shared-tile kernel of pta_tile.hip:
 // DMA stage j holds K of page pair j + 1 and V of pair j; iteration s computes
 // S of pair s + 1 and P, P.V of pair s; reference maxima move lazily.
+// The verify step's KV append can ride in the same grid (the fused-append
+// entry): each unit piece writes the candidate rows on its own pages first.
 #include "pta_device.h"
 #include "pta_flash.h"
 #include "pta_launch.h"
@@ -573,6 +575,45 @@ __device__ __forceinline__ void wide_store_partial(const WideRows<D>& R, const W
   }
 }
 
+// The fused KV append of one unit piece: the candidate rows r of (b, hkv) whose
+// positions L + r fall in [lo, hi) (the piece's tokens) are copied from k_new /
+// v_new ([B][Qmax][Hkv][D] bf16) into their paged slots, 16 bytes per thread
+// and step, every load issued before the first store; the caller's barrier
+// follows the wait here, so the piece's page copies see the rows.  Each row
+// group of a unit writes the rows of the pieces it works (identical bytes), and
+// only the piece that holds a page reads it, so no other workgroup waits.
+template <int D, int NT>
+__device__ __forceinline__ void wide_append_rows(const AttnArgs& a, int b, int hkv, int L, int qb, int lo, int hi,
+                                                 int tid) {
+  constexpr int CPR = D / 8;                                    // 16-byte chunks per row
+  const int r0 = max(0, lo - L), r1 = min(qb, hi - L);
+  if (r1 <= r0) return;
+  const int n = 2 * (r1 - r0) * CPR;
+  const int32_t* table = a.tables + (int64_t)b * a.MBS;
+  for (int e0 = 0; e0 < n; e0 += 4 * NT) {
+    uint4 val[4];
+    int64_t dst[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + tid + i * NT;
+      if (e >= n) continue;
+      const int which = e / ((r1 - r0) * CPR), r = r0 + (e / CPR) % (r1 - r0), c = e % CPR;
+      const int t = L + r;
+      const int64_t page = table[t / kPage];
+      dst[i] = ((((page * a.Hkv + hkv) * kPage + t % kPage) * D + c * 8) << 1) | which;
+      const int64_t src = (((int64_t)b * a.Qmax + r) * a.Hkv + hkv) * D + c * 8;
+      val[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(which ? a.v_new : a.k_new) + src);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (e0 + tid + i * NT >= n) continue;
+      void* cache = const_cast<void*>((dst[i] & 1) ? a.v : a.k);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(cache) + (dst[i] >> 1)) = val[i];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);    // this thread's stores have completed
+}
+
 // ------------------------------------------------------------ balanced grid
 // Same page line, slices, row groups and partial slots as tile_balanced_kernel
 // (pta_tile.hip); slice_merge_kernel merges the partials in a second launch.
@@ -626,6 +667,10 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     const int qb = a.qlen[b];
     const int M = a.G * qb;
 
+    // the step's KV append, for the candidates on this piece's pages (k_new set by the
+    // fused entry); the barrier below orders it before the piece's page copies
+    if (a.k_new != nullptr && row0 < M)
+      wide_append_rows<D, NWR * 64>(a, b, hkv, C - qb, qb, k0 * kPage, min(C, k1 * kPage), tid);
     __syncthreads();          // LDS stage buffers free from the previous unit
     if (row0 < M) {
       WideRows<D> R;

@@ -155,6 +155,25 @@ def test_attn_append_host_checks(lib):
     assert f(dims(), scale=float("inf")) == DIMS
 
 
+def test_balanced_append_host_checks(lib):
+    """taco_paged_tree_attn_balanced_append: row dtype, pointers, alignment and the kernel family
+    (the 32x32x16 shared-tile grid only) are checked on the host."""
+    def f(dd, new_dt=1, k=FAKE, v=FAKE, scale=0.1):
+        return lib.taco_paged_tree_attn_balanced_append(
+            ctypes.byref(dd) if dd is not None else None, FAKE, k, v, new_dt, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+            scale, FAKE, None, FAKE, 1 << 30, None)
+    wide = dict(max_q_len=16, num_q_heads=64)                        # 128 rows per KV head
+    assert f(None) == NULLP
+    assert f(dims(**wide), new_dt=0) == DTYPE                        # bf16 rows only
+    assert f(dims(**wide), k=None) == NULLP
+    assert f(dims(**wide), v=ctypes.c_void_p(0x10008)) == DIMS       # rows move in 16-byte chunks
+    assert f(dims(**wide), scale=float("inf")) == DIMS
+    assert f(dims()) == UNSUP                                        # 4 rows: streaming balanced grid
+    assert f(dims(kv_dtype=2, **wide)) == UNSUP                      # fp8 cache
+    assert f(dims(path=4, **wide)) == UNSUP                          # 16x16x32 grid
+    assert f(dims(num_seqs=0, **wide)) == OK
+
+
 def test_shared_prefix_host_checks(lib):
     def f(dd, leader=FAKE, group=8, shared=2048, ws=FAKE, nbytes=1 << 30):
         return lib.taco_paged_tree_attn_shared_prefix(ctypes.byref(dd), FAKE, FAKE, FAKE, None, None, FAKE, FAKE,

@@ -340,10 +340,11 @@ FUSED_CASES = [
 ]
 
 
-@pytest.mark.parametrize("cid,sp,new_dt", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
-def test_fused_append_parity(torch_cuda, cid, sp, new_dt):
+def check_fused_append(cid, sp, new_dt, call):
+    """Poisoned workload whose candidates' slots still hold the old rows; call(d, k_new, v_new,
+    out, lse) must write the new rows into the cache (byte-exact against the oracle's append) and
+    attend over them (parity against the oracle over the appended cache)."""
     import torch
-    import paged_speculative_verify_amd as psv
     from workload.gen import f32_to_bf16_bits
     w = make(sp, poison=True)
     B, Qmax, Hq, D = w.q.shape
@@ -381,9 +382,7 @@ def test_fused_append_parity(torch_cuda, cid, sp, new_dt):
         kn, vn = kn.view(torch.bfloat16), vn.view(torch.bfloat16)
     out = torch.full_like(d.q, float("nan"))
     lse = torch.full((B, Hq, Qmax), float("nan"), dtype=torch.float32, device=d.q.device)
-    psv.taco_paged_tree_attn_append(d.q, kn, vn, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
-                                    d.tree_mask, d.scale, out=out, lse=lse, k_scale=d.k_scale, v_scale=d.v_scale,
-                                    max_ctx_len=d.max_ctx_len)
+    call(d, kn, vn, out, lse)
     torch.cuda.synchronize()
     gk = d.k_cache.view(torch.uint8).cpu().numpy()
     gv = d.v_cache.view(torch.uint8).cpu().numpy()
@@ -391,6 +390,18 @@ def test_fused_append_parity(torch_cuda, cid, sp, new_dt):
     assert np.array_equal(gv.reshape(-1), ref_v.view(np.uint8).reshape(-1)), "V cache after the call"
     err = assert_parity(w, out_to_f64(out), lse.cpu().numpy().astype(np.float64), ref, ref_lse)
     say(cid, "max abs err", err)
+    return w
+
+
+@pytest.mark.parametrize("cid,sp,new_dt", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_append_parity(torch_cuda, cid, sp, new_dt):
+    import paged_speculative_verify_amd as psv
+
+    def call(d, kn, vn, out, lse):
+        psv.taco_paged_tree_attn_append(d.q, kn, vn, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
+                                        d.tree_mask, d.scale, out=out, lse=lse, k_scale=d.k_scale,
+                                        v_scale=d.v_scale, max_ctx_len=d.max_ctx_len)
+    check_fused_append(cid, sp, new_dt, call)
 
 
 def test_fused_append_unsupported_path(torch_cuda):
@@ -403,6 +414,65 @@ def test_fused_append_unsupported_path(torch_cuda):
     with pytest.raises(psv.PtaError):
         psv.taco_paged_tree_attn_append(d.q, kn, kn, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
                                         d.tree_mask, d.scale, max_ctx_len=d.max_ctx_len)
+
+
+# the append fused into the balanced entry's 32x32x16 grid: more than 32 rows per KV head;
+# long contexts over few units make slices of one or two pages, so a sequence's candidates
+# often fall on pages of two slices (each slice writes and reads only its own)
+BALANCED_FUSED_CASES = [
+    ("g8_q8", spec("fb", 3, 64, 8, 128, "bf16", "bf16", (300, 900), 8, "random", seed=211)),
+    ("g16_q16_two_row_groups", spec("fb", 2, 64, 4, 128, "bf16", "bf16", (500, 900), 16, "random", seed=212)),
+    ("ragged_q16_d64", spec("fb", 5, 32, 4, 64, "bf16", "bf16", (1, 400), 16, "random", ragged=True, seed=213)),
+    ("g8_q32_chain", spec("fb", 2, 64, 8, 128, "bf16", "bf16", (33, 1500), 32, "chain", seed=214)),
+]
+
+
+@pytest.mark.parametrize("cid,sp", BALANCED_FUSED_CASES, ids=[c[0] for c in BALANCED_FUSED_CASES])
+def test_balanced_fused_append_parity(torch_cuda, cid, sp):
+    import torch
+    import paged_speculative_verify_amd as psv
+    seen = {}
+
+    def call(d, kn, vn, out, lse):
+        need = psv.taco_paged_tree_attn_balanced_workspace_size(d.q, d.k_cache, d.block_tables,
+                                                                max_ctx_len=d.max_ctx_len)
+        seen["ws"] = torch.zeros(need, dtype=torch.uint8, device=d.q.device)
+        psv.taco_paged_tree_attn_balanced_append(d.q, kn, vn, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
+                                                 d.q_lens, d.tree_mask, d.scale, out=out, lse=lse,
+                                                 workspace=seen["ws"], max_ctx_len=d.max_ctx_len)
+        seen.update(d=d, kn=kn, vn=vn, out=out)
+    w = check_fused_append(cid, sp, "bf16", call)
+    # a second call on the appended cache and the same workspace: same bytes, same outputs
+    d, ws = seen["d"], seen["ws"]
+    k_before = d.k_cache.clone()
+    out2 = torch.full_like(d.q, float("nan"))
+    psv.taco_paged_tree_attn_balanced_append(d.q, seen["kn"], seen["vn"], d.k_cache, d.v_cache, d.block_tables,
+                                             d.ctx_lens, d.q_lens, d.tree_mask, d.scale, out=out2, workspace=ws,
+                                             max_ctx_len=d.max_ctx_len)
+    torch.cuda.synchronize()
+    assert torch.equal(d.k_cache.view(torch.int16), k_before.view(torch.int16))
+    a, b = seen["out"].float().cpu().numpy(), out2.float().cpu().numpy()
+    for i in range(w.q.shape[0]):
+        qb = int(w.q_lens[i])
+        assert np.array_equal(a[i, :qb], b[i, :qb]), "repeat call"
+
+
+def test_balanced_fused_append_unsupported(torch_cuda):
+    """Served only by the 32x32x16 grid: fp8 KV (streaming balanced grid) and the 16x16x32
+    path are refused, and so are rows in another dtype."""
+    import torch
+    import paged_speculative_verify_amd as psv
+    for kv, path in (("fp8", "auto"), ("bf16", "tile16")):
+        w = make(spec("fb", 3, 64, 8, 128, "bf16", kv, (20, 200), 8, "random", seed=215))
+        d = to_device(w)
+        B, Qmax, Hq, D = w.q.shape
+        kn = torch.zeros((B, Qmax, 8, D), dtype=torch.bfloat16, device=d.q.device)
+        say("balanced fused unsupported", kv, path)
+        with pytest.raises(psv.PtaError) as e:
+            psv.taco_paged_tree_attn_balanced_append(d.q, kn, kn, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
+                                                     d.q_lens, d.tree_mask, d.scale, max_ctx_len=d.max_ctx_len,
+                                                     path=path)
+        assert e.value.status == 4, e.value
 
 
 def test_validate_flags(torch_cuda):
