@@ -130,9 +130,25 @@ __device__ __forceinline__ uint64_t load_mask_row(const uint8_t* mask, int b, in
                                                   int Qmax) {
   if (mask == nullptr) return 1ull;          // Qmax == 1: the candidate sees itself
   const uint8_t* row = mask + ((int64_t)b * Qmax + i) * Qmax;
+  uint64_t bits = 0;
+  if (((reinterpret_cast<uintptr_t>(mask) | (uintptr_t)Qmax) & 3) == 0) {
+    // rows 4-byte aligned: one dword per 4 candidates (inside the row, since qb <= Qmax and
+    // Qmax is a multiple of 4), all loads issued before the first use: one round trip
+    const uint32_t* r4 = reinterpret_cast<const uint32_t*>(row);
+    const int nw = (qb + 3) >> 2;
+    uint32_t w[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) w[e] = e < nw ? r4[e] : 0u;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      // the top bit of each nonzero byte, then those four bits gathered into bits 24..27
+      const uint32_t t = (((w[e] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w[e]) & 0x80808080u;
+      bits |= (uint64_t)((((t >> 7) * 0x01020408u) >> 24) & 0xFu) << (4 * e);
+    }
+    return qb >= 64 ? bits : bits & ((1ull << qb) - 1ull);
+  }
   // 16 independent byte loads per group (indices clamped into the row), so a
   // row costs one memory round trip per 16 candidates rather than one each
-  uint64_t bits = 0;
   for (int j0 = 0; j0 < qb; j0 += 16) {
     uint8_t v[16];
 #pragma unroll

@@ -195,17 +195,25 @@ __device__ __forceinline__ void wide_load_rows(WideRows<D>& R, const AttnArgs& a
   R.i = R.ok ? row % qb : 0;
   const uint16_t* qp =
       reinterpret_cast<const uint16_t*>(a.q) + (((int64_t)b * a.Qmax + R.i) * a.Hq + R.hq) * D + 8 * h;
-  const uint32_t sgn = a.scale_log2 < 0.f ? 0x80008000u : 0u;   // a negative scale moves into Q's sign
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    uint4 w = R.ok ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
-    w.x ^= sgn;
-    w.y ^= sgn;
-    w.z ^= sgn;
-    w.w ^= sgn;
+    const uint4 w = R.ok ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
     R.qop[ks] = __builtin_bit_cast(bf16x8, w);
   }
   R.mbits = R.ok ? load_mask_row(a.mask, b, R.i, qb, a.Qmax) : 0ull;
+  // a negative scale moves into Q's sign (after the mask loads are issued, so the
+  // row's loads share one round trip)
+  if (a.scale_log2 < 0.f) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      uint4 w = __builtin_bit_cast(uint4, R.qop[ks]);
+      w.x ^= 0x80008000u;
+      w.y ^= 0x80008000u;
+      w.z ^= 0x80008000u;
+      w.w ^= 0x80008000u;
+      R.qop[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
 }
 
 // Physical 16-byte unit holding logical unit u of tile row r (an involution,
@@ -426,7 +434,6 @@ __device__ __forceinline__ void wide_range(const AttnArgs& a, char* lds, uint32_
   const int pro = min(NBUF, nst + 1);
   int ph[Gm::NTW];
   page_ids(-1, ph);
-  wide_wait_vm<0>();                       // the row loads are done before any copy is in flight
   for (int j = -1; j < pro - 1; ++j) {
     copy_stage(j, ph, (j + 1) % NBUF);
     page_ids(j + 1, ph);
