@@ -43,8 +43,8 @@ extern "C" {
  *   w        uint8 [N][K]  e4m3fn codes, row-major, 16-byte aligned
  *   w_scale  float [N]
  *   y        bf16  [M][N]  row-major (written; every element)
- * M >= 1, N >= 1, K a positive multiple of 64, M rounded up to a multiple of 128
- * and N rounded up to a multiple of 256, each times K, below 2^32
+ * M >= 1, N >= 1, K a positive multiple of 64, M and N rounded up to multiples
+ * of 256, each times K, below 2^32
  * (else PTA_ERR_BAD_DIMS); NULL pointers PTA_ERR_NULL_PTR; a failed launch
  * PTA_ERR_HIP.  NaN codes propagate to the affected outputs. */
 pta_status taco_gemm_w8a8(const void* a, const float* a_scale, const void* w, const float* w_scale, void* y,

@@ -6,16 +6,19 @@
 // instructions).  W8A8 first, W4A16 below.
 //
 // W8A8:
-//   * Workgroup tile 128 (M) x 64 WNB (N), four waves of 64 x 32 WNB (2 x WNB
-//     blocks of v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales:
-//     e4m3fn x e4m3fn, float32 accumulators); WNB = 2 up to 128 rows, 4 above
-//     (each activation tile then feeds twice the columns).  A lane supplies 32
+//   * Waves of 64 x 32 WNB (2 x WNB blocks of v_mfma_scale_f32_32x32x64_f8f6f4
+//     with unit block scales: e4m3fn x e4m3fn, float32 accumulators), WMW of
+//     them along M and two along N: 128 x 128 workgroup tiles up to 128 rows,
+//     128 x 256 up to 256 (each activation tile feeds twice the columns), and
+//     256 x 256 with eight waves above (a third fewer bytes staged per product;
+//     the staging, not the matrix cores, bounds this kernel: without its copies
+//     the 512-row shape runs in 171 us instead of 270).  A lane supplies 32
 //     consecutive k-bytes of its row of A and of its column of W^T (k = 32 h +
 //     0..31 of the 64-step, h = lane / 32); any consistent assignment of k to
 //     (lane half, byte) gives the same sums, and this one makes each operand two
 //     16-byte LDS reads.
-//   * k-steps of 64 bytes staged in LDS (A tile 8 KiB + W tile 8 or 16 KiB),
-//     four or three stages, moved by buffer_load_dwordx4 ... lds with the whole
+//   * k-steps of 64 bytes staged in LDS (A tile 8 or 16 KiB + W tile 8 or 16
+//     KiB), four or three stages, moved by buffer_load_dwordx4 ... lds with the whole
 //     offset in the range-checked vector offset, so rows past M or N read as
 //     zero and ragged edges need no other handling.  16-byte units of a row are
 //     swizzled by the row's bits 2..3, so the 16 rows one pass of an operand
@@ -38,21 +41,29 @@ typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 128, BK = 64, NT = 256;
 
-// Tile geometry for WNB 32-column blocks per wave (2: 128 x 128 workgroup
-// tiles, four stages; 4: 128 x 256, three stages).
-template <int WNB>
+// Tile geometry for WNB 32-column blocks per wave and WMW waves along M (each
+// 64 rows), two waves along N:
+//   WMW 2, WNB 2: 128 x 128 workgroup tiles, 4 waves, four stages
+//   WMW 2, WNB 4: 128 x 256, 4 waves, three stages (two workgroups per CU)
+//   WMW 4, WNB 4: 256 x 256, 8 waves, four stages (one workgroup per CU): a third
+//                 fewer bytes staged per product than 128 x 256
+template <int WNB, int WMW = 2>
 struct GemmGeom {
+  static constexpr int BM = 64 * WMW;
   static constexpr int BN = 64 * WNB;                     // two waves side by side along N
-  static constexpr int NBUF = WNB == 2 ? 4 : 3;
-  static constexpr int A_TILE = BM * BK;                  // 8 KiB
+  static constexpr int NWAVES = 2 * WMW, NT = 64 * NWAVES;
+  static constexpr int NBUF = WNB == 2 || WMW == 4 ? 4 : 3;
+  static constexpr int A_TILE = BM * BK;                  // 8 or 16 KiB
   static constexpr int W_TILE = BN * BK;
   static constexpr int W_REG = NBUF * A_TILE;             // W region after the A region
   static constexpr int CHUNKS_A = A_TILE / 1024, CHUNKS_W = W_TILE / 1024;
-  static constexpr int LOADS = (CHUNKS_A + CHUNKS_W) / (NT / 64);   // copies per wave per stage
+  static constexpr int LOADS = (CHUNKS_A + CHUNKS_W) / NWAVES;     // copies per wave per stage
   static constexpr int LDS_BYTES = W_REG + NBUF * W_TILE;
-  static_assert((CHUNKS_A + CHUNKS_W) % (NT / 64) == 0, "whole copies per wave");
-  static_assert(W_REG + (NBUF - 1) * W_TILE < 65536, "stage offsets must be 16-bit immediates");
-  static_assert(LDS_BYTES <= 81920, "two workgroups per compute unit");
+  static_assert(CHUNKS_A % NWAVES == 0 && CHUNKS_W % NWAVES == 0, "whole copy rounds per operand");
+  // the read offsets' per-stage parts are immediates (W_REG rides in the address register)
+  static_assert((NBUF - 1) * W_TILE + (WNB - 1) * 32 * BK < 65536 && (NBUF - 1) * A_TILE + 32 * BK < 65536,
+                "stage offsets must be 16-bit immediates");
+  static_assert(LDS_BYTES <= (WMW == 2 ? 81920 : 163840), "workgroups per compute unit");
 };
 
 __device__ __forceinline__ i32x4 gemm_rsrc(const void* base, uint32_t bytes) {
@@ -102,16 +113,17 @@ __device__ __forceinline__ void gemm_static_for(F&& f) {
   }
 }
 
-template <int WNB>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w8a8_kernel(
+template <int WNB, int WMW>
+__global__ __launch_bounds__(128 * WMW) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w8a8_kernel(
     const uint8_t* a, const float* a_scale, const uint8_t* w, const float* w_scale, uint16_t* y, int M, int N,
     int K, int tm, int tn) {
-  using Gm = GemmGeom<WNB>;
-  constexpr int BN = Gm::BN, NBUF = Gm::NBUF, A_TILE = Gm::A_TILE, W_TILE = Gm::W_TILE, W_REG = Gm::W_REG;
+  using Gm = GemmGeom<WNB, WMW>;
+  constexpr int BM = Gm::BM, BN = Gm::BN, NBUF = Gm::NBUF, A_TILE = Gm::A_TILE, W_TILE = Gm::W_TILE,
+                W_REG = Gm::W_REG, NWAVES = Gm::NWAVES;
   __shared__ __attribute__((aligned(1024))) char lds[Gm::LDS_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WMW, wn = wave / WMW;
   // XCD-grouped order: workgroup b runs on XCD b % 8; there, slots take the tm
   // M tiles of one N tile in a row
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -130,8 +142,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
     const uint32_t kb = (uint32_t)(s * BK);
 #pragma unroll
     for (int i = 0; i < Gm::LOADS; ++i) {
-      const int c = wave + 4 * i;                  // chunk c of the stage: A chunks, then W chunks
-      if (c < Gm::CHUNKS_A)
+      const int c = wave + NWAVES * i;             // chunk c of the stage: A chunks, then W chunks
+      if (i < Gm::CHUNKS_A / NWAVES)               // (whole rounds of A chunks: known per i)
         gemm_copy(lds0 + (uint32_t)(buf * A_TILE + c * 1024), ars, (uint32_t)(m0 + 16 * c) * (uint32_t)K + kb, voff);
       else
         gemm_copy(lds0 + (uint32_t)(W_REG + buf * W_TILE + (c - Gm::CHUNKS_A) * 1024), wrs,
@@ -399,23 +411,25 @@ pta_status taco_gemm_w8a8(const void* a, const float* a_scale, const void* w, co
   if (!a || !a_scale || !w || !w_scale || !y) return PTA_ERR_NULL_PTR;
   if (M < 1 || N < 1 || K < BK || K % BK != 0) return PTA_ERR_BAD_DIMS;
   // every tile row (those past M or N included) must have a 32-bit buffer offset
-  const uint64_t mpad = (uint64_t)((M + BM - 1) / BM) * BM, npad = (uint64_t)((N + 255) / 256) * 256;
+  const uint64_t mpad = (uint64_t)((M + 255) / 256) * 256, npad = (uint64_t)((N + 255) / 256) * 256;
   if (mpad * (uint64_t)K >= ((uint64_t)1 << 32) || npad * (uint64_t)K >= ((uint64_t)1 << 32)) return PTA_ERR_BAD_DIMS;
   if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(w)) % 16 != 0) return PTA_ERR_BAD_DIMS;
-  // wide column tiles once the M tiles alone would not fill the device
-  const bool wide = M > 128;
-  const int BN = wide ? GemmGeom<4>::BN : GemmGeom<2>::BN;
-  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  // wide column tiles once the M tiles alone would not fill the device; 256-row
+  // tiles past 256 rows
+  const int kind = M > 256 ? 2 : (M > 128 ? 1 : 0);
+  const int TBM = kind == 2 ? GemmGeom<4, 4>::BM : BM;
+  const int BN = kind == 0 ? GemmGeom<2>::BN : GemmGeom<4>::BN;
+  const int tm = (M + TBM - 1) / TBM, tn = (N + BN - 1) / BN;
   const int64_t blocks = (int64_t)8 * tm * ((tn + 7) / 8);
   if (blocks > 0x7fffffff) return PTA_ERR_BAD_DIMS;
-  if (wide)
-    hipLaunchKernelGGL(gemm_w8a8_kernel<4>, dim3((unsigned)blocks), dim3(NT), 0, (hipStream_t)stream,
+  auto launch = [&](auto kern, int nt) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(nt), 0, (hipStream_t)stream,
                        reinterpret_cast<const uint8_t*>(a), a_scale, reinterpret_cast<const uint8_t*>(w), w_scale,
                        reinterpret_cast<uint16_t*>(y), M, N, K, tm, tn);
-  else
-    hipLaunchKernelGGL(gemm_w8a8_kernel<2>, dim3((unsigned)blocks), dim3(NT), 0, (hipStream_t)stream,
-                       reinterpret_cast<const uint8_t*>(a), a_scale, reinterpret_cast<const uint8_t*>(w), w_scale,
-                       reinterpret_cast<uint16_t*>(y), M, N, K, tm, tn);
+  };
+  if (kind == 2) launch(gemm_w8a8_kernel<4, 4>, GemmGeom<4, 4>::NT);
+  else if (kind == 1) launch(gemm_w8a8_kernel<4, 2>, GemmGeom<4, 2>::NT);
+  else launch(gemm_w8a8_kernel<2, 2>, GemmGeom<2, 2>::NT);
   return hipGetLastError() == hipSuccess ? PTA_OK : PTA_ERR_HIP;
 }
 

@@ -223,6 +223,8 @@ def test_gemm_host_checks(lib):
     assert call(K=100) == DIMS and call(K=0) == DIMS and call(M=0) == DIMS and call(N=-1) == DIMS
     assert call(a=ctypes.c_void_p(0x10008)) == DIMS                 # not 16-byte aligned
     assert call(M=1 << 20, K=1 << 13) == DIMS                       # rows x K past 32-bit offsets
+    # 66817 rows pad to 67072 in 256-row tiles: 67072 x 64064 passes 2^32 (66944 x 64064 would not)
+    assert call(M=66817, K=64064) == DIMS
 
 
 def test_gemm_w4a16_host_checks(lib):

@@ -64,6 +64,7 @@ CASES = [
     ("ragged_tiles", 130, 260, 320, 33),
     ("one_tile_long_k", 128, 128, 4096, 34),
     ("many_tiles", 300, 1100, 1024, 35),
+    ("tall_three_row_tiles", 520, 600, 512, 37),
     ("decode_rows", 64, 2048, 8192, 36),
 ]
 
