@@ -11,8 +11,8 @@
 //     them along M and two along N: 128 x 128 workgroup tiles up to 128 rows,
 //     128 x 256 up to 256 (each activation tile feeds twice the columns), and
 //     256 x 256 with eight waves above (a third fewer bytes staged per product;
-//     the staging, not the matrix cores, bounds this kernel: without its copies
-//     the 512-row shape runs in 171 us instead of 270).  A lane supplies 32
+//     the staging, not the matrix cores, bounds these kernels), there with
+//     128-byte k-steps when K is a multiple of 128 (gemm_w8a8_k128_kernel).  A lane supplies 32
 //     consecutive k-bytes of its row of A and of its column of W^T (k = 32 h +
 //     0..31 of the 64-step, h = lane / 32); any consistent assignment of k to
 //     (lane half, byte) gives the same sums, and this one makes each operand two
@@ -224,6 +224,129 @@ __global__ __launch_bounds__(128 * WMW) __attribute__((amdgpu_waves_per_eu(2))) 
 }
 
 
+// 256 x 256 tiles with 128-byte k-steps (K a multiple of 128): each copy moves
+// 8 rows x 128 bytes, whole 128-byte lines, where a 64-byte k-step moves 16
+// half lines per copy and the copy path then carries about half the bytes per
+// clock.  Eight waves of 64 x 128 as gemm_w8a8_kernel<4, 4>, two stages (the
+// next one in flight), two 64-byte halves per stage.  LDS rows are 128 bytes:
+// the 16-byte unit u of tile row r sits in slot u ^ ((r >> 1) & 7), so the 16
+// rows of one read pass land in 16 distinct bank groups.
+template <int N_>
+struct GemmK128 {
+  static constexpr int BM = 256, BN = 256, BKS = 128, NWAVES = 8, NT = 512, NBUF = 2;
+  static constexpr int A_TILE = BM * BKS, W_TILE = BN * BKS;       // 32 KiB each
+  static constexpr int W_REG = NBUF * A_TILE;
+  static constexpr int CHUNKS_A = A_TILE / 1024, CHUNKS_W = W_TILE / 1024;
+  static constexpr int LOADS = (CHUNKS_A + CHUNKS_W) / NWAVES;
+  static constexpr int LDS_BYTES = W_REG + NBUF * W_TILE;          // 128 KiB: one workgroup per CU
+  static_assert(CHUNKS_A % NWAVES == 0 && CHUNKS_W % NWAVES == 0, "whole copy rounds per operand");
+  static_assert((NBUF - 1) * W_TILE + 3 * 32 * BKS < 65536, "stage offsets must be 16-bit immediates");
+};
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w8a8_k128_kernel(
+    const uint8_t* a, const float* a_scale, const uint8_t* w, const float* w_scale, uint16_t* y, int M, int N,
+    int K, int tm, int tn) {
+  using Gm = GemmK128<0>;
+  constexpr int BM = Gm::BM, BN = Gm::BN, BKS = Gm::BKS, A_TILE = Gm::A_TILE, W_TILE = Gm::W_TILE,
+                W_REG = Gm::W_REG, NWAVES = Gm::NWAVES, WNB = 4;
+  __shared__ __attribute__((aligned(1024))) char lds[Gm::LDS_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3, wn = wave >> 2;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int nt = (slot / tm) * 8 + xcd, mt = slot % tm;
+  if (nt >= tn) return;
+  const int m0 = mt * BM, n0 = nt * BN;
+
+  const i32x4 ars = gemm_rsrc(a, (uint32_t)((uint64_t)M * (uint64_t)K));
+  const i32x4 wrs = gemm_rsrc(w, (uint32_t)((uint64_t)N * (uint64_t)K));
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&lds[0];
+  // copy lanes: chunk row l / 8 (tile row 8 c + l / 8), slot l % 8 holding logical
+  // unit (l % 8) ^ ((row >> 1) & 7) = (l % 8) ^ (4 (c & 1) + l / 16); a wave's
+  // chunks c = wave + 8 i all have the parity of the wave
+  const uint32_t voff =
+      (uint32_t)((lane >> 3) * K + (((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7)) << 4));
+  const int nk = K / BKS;
+  auto copy_stage = [&](int s, int buf) {
+    const uint32_t kb = (uint32_t)(s * BKS);
+#pragma unroll
+    for (int i = 0; i < Gm::LOADS; ++i) {
+      const int c = wave + NWAVES * i;
+      if (i < Gm::CHUNKS_A / NWAVES)
+        gemm_copy(lds0 + (uint32_t)(buf * A_TILE + c * 1024), ars, (uint32_t)(m0 + 8 * c) * (uint32_t)K + kb, voff);
+      else
+        gemm_copy(lds0 + (uint32_t)(W_REG + buf * W_TILE + (c - Gm::CHUNKS_A) * 1024), wrs,
+                  (uint32_t)(n0 + 8 * (c - Gm::CHUNKS_A)) * (uint32_t)K + kb, voff);
+    }
+  };
+  // operand reads: row 32 blk + l % 32 of the wave's rows, logical units 4 q + 2 h + e
+  // of half q of the stage
+  const int r32 = lane & 31, h = lane >> 5, sw = (r32 >> 1) & 7;
+  uint32_t aoff[2][2], woff[2][2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t u = (uint32_t)(((4 * q + 2 * h + e) ^ sw) << 4);
+      aoff[q][e] = (uint32_t)((64 * wm + r32) * BKS) + u;
+      woff[q][e] = (uint32_t)(W_REG + (32 * WNB * wn + r32) * BKS) + u;
+    }
+
+  f32x16 acc[2][WNB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < WNB; ++j) acc[i][j] = {};
+
+  copy_stage(0, 0);
+  auto step = [&](auto bc, int s) {
+    constexpr int BUF = decltype(bc)::value;
+    gemm_wait_vm<0>();
+    __syncthreads();                          // stage s in LDS; stage s - 1 consumed by every wave
+    if (s + 1 < nk) copy_stage(s + 1, BUF ^ 1);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      i32x8 ao[2], wo[WNB];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(lds + aoff[q][0] + BUF * A_TILE + i * 32 * BKS);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(lds + aoff[q][1] + BUF * A_TILE + i * 32 * BKS);
+        ao[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+#pragma unroll
+      for (int j = 0; j < WNB; ++j) {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(lds + woff[q][0] + BUF * W_TILE + j * 32 * BKS);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(lds + woff[q][1] + BUF * W_TILE + j * 32 * BKS);
+        wo[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < WNB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ao[i], wo[j], acc[i][j], 0, 0, 0, 0x7f, 0, 0x7f);
+    }
+  };
+  for (int s = 0; s < nk; s += 2) {
+    step(std::integral_constant<int, 0>{}, s);
+    if (s + 1 < nk) step(std::integral_constant<int, 1>{}, s + 1);
+  }
+
+#pragma unroll
+  for (int j = 0; j < WNB; ++j) {
+    const int n = n0 + 32 * WNB * wn + 32 * j + r32;
+    if (n >= N) continue;
+    const float sw_n = w_scale[n];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m < M) y[(int64_t)m * N + n] = f32_to_bf16(acc[i][j][e] * a_scale[m] * sw_n);
+      }
+  }
+}
+
+
 // ------------------------------------------------------------------ W4A16
 // bf16 activations x group-scaled signed int4 weights on the bf16 matrix cores
 // (v_mfma_f32_32x32x16_bf16, float32 accumulation):
@@ -427,7 +550,8 @@ pta_status taco_gemm_w8a8(const void* a, const float* a_scale, const void* w, co
                        reinterpret_cast<const uint8_t*>(a), a_scale, reinterpret_cast<const uint8_t*>(w), w_scale,
                        reinterpret_cast<uint16_t*>(y), M, N, K, tm, tn);
   };
-  if (kind == 2) launch(gemm_w8a8_kernel<4, 4>, GemmGeom<4, 4>::NT);
+  if (kind == 2 && K % 128 == 0) launch(gemm_w8a8_k128_kernel, GemmK128<0>::NT);
+  else if (kind == 2) launch(gemm_w8a8_kernel<4, 4>, GemmGeom<4, 4>::NT);
   else if (kind == 1) launch(gemm_w8a8_kernel<4, 2>, GemmGeom<4, 2>::NT);
   else launch(gemm_w8a8_kernel<2, 2>, GemmGeom<2, 2>::NT);
   return hipGetLastError() == hipSuccess ? PTA_OK : PTA_ERR_HIP;
