@@ -602,7 +602,9 @@ def gemm_bench(psv, torch, name, steps=30, warmup=5, cpu_rows=2, parity_rows=(0,
     else:
         G = W4_GROUP
         a, w, sw = make_w4a16_device(M, N, K, G, seed=11, torch=torch)
-        call = lambda: psv.taco_gemm_w4a16(a, w, sw, G, y)
+        # weights rearranged into the kernel's load order once, as at model load (untimed)
+        wt = psv.taco_gemm_w4a16_pack(w)
+        call = lambda: psv.taco_gemm_w4a16(a, wt, sw, G, y, tiled=(N, K))
         peak, kernel = BF16_PEAK_TFLOPS, "gemm_w4a16_kernel"
         nbytes = 2 * M * K + N * K // 2 + 4 * N * (K // G) + 2 * M * N
     for _ in range(warmup):
@@ -661,7 +663,8 @@ def gemm_bench(psv, torch, name, steps=30, warmup=5, cpu_rows=2, parity_rows=(0,
         dtype = "bf16 x int4 (exact to bf16) -> f32, group scales in f32 -> bf16"
         metric = "W4A16 GEMM TFLOP/s (bf16 activations, int4 weights, group-128 scales, bf16 out), 1 GPU"
         bound_text = "2^-8 |y_ref| + 2^-14 sum_k |a||q| w_scale per output"
-        config = {"workload": name, "M": M, "N": N, "K": K, "group": W4_GROUP}
+        config = {"workload": name, "M": M, "N": N, "K": K, "group": W4_GROUP,
+                  "weights": "rearranged by taco_gemm_w4a16_pack before timing (taco_gemm_w4a16_tiled)"}
     excess = float((np.abs(got - ref) - bnd).max())
     res = {
         "metric": metric,
@@ -684,7 +687,7 @@ def gemm_bench(psv, torch, name, steps=30, warmup=5, cpu_rows=2, parity_rows=(0,
                          "cores": cores, "kind": "oracle",
                          "sample": f"{cpu_rows} output rows x {N} columns, fp64 numpy, {t_cpu:.1f} s"},
     }
-    del a, w, y
+    del a, w, y, call
     torch.cuda.empty_cache()
     return res
 

@@ -68,6 +68,28 @@ pta_status taco_gemm_w8a8(const void* a, const float* a_scale, const void* w, co
 pta_status taco_gemm_w4a16(const void* a, const void* w, const float* w_scale, void* y, int32_t M, int32_t N,
                            int32_t K, int32_t group, void* stream);
 
+/* Weight-aware rearrangement of W4A16 weights (the 618zxw.cn article, section
+ * "LLM量子化技術による推論コストの削減", lists weight rearrangement among the
+ * quantized operators' techniques): the int4 weights of taco_gemm_w4a16 laid
+ * out in the GEMM's load order, so that each 64-k step of a 128-column tile is
+ * one contiguous 4 KiB block (whole cache lines) instead of 32 bytes of each
+ * of 128 rows.  Done once per weight matrix, outside the per-token path.
+ *   taco_gemm_w4a16_tiled_bytes: size of the rearranged buffer for N x K
+ *     weights (N rounded up to 128 columns, zero filled), 0 when N < 1, K is
+ *     not a positive multiple of 64 or the size reaches 2^32.
+ *   taco_gemm_w4a16_pack: w (row-major [N][K / 2], as taco_gemm_w4a16) into
+ *     w_tiled (that many bytes, caller-allocated); both 16-byte aligned, else
+ *     PTA_ERR_BAD_DIMS; bad N or K PTA_ERR_BAD_DIMS; NULL pointers
+ *     PTA_ERR_NULL_PTR; asynchronous on stream.  Block (t, s) of w_tiled, at
+ *     byte (t * K / 64 + s) * 4096, holds at byte 32 r + 16 p the 16 bytes of
+ *     column 128 t + r at k-bytes 32 s + 16 (p ^ ((r >> 3) & 1)).
+ *   taco_gemm_w4a16_tiled: taco_gemm_w4a16 on the rearranged weights (same
+ *     arguments, limits, errors and results, bit for bit). */
+size_t taco_gemm_w4a16_tiled_bytes(int32_t N, int32_t K);
+pta_status taco_gemm_w4a16_pack(const void* w, void* w_tiled, int32_t N, int32_t K, void* stream);
+pta_status taco_gemm_w4a16_tiled(const void* a, const void* w_tiled, const float* w_scale, void* y, int32_t M,
+                                 int32_t N, int32_t K, int32_t group, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

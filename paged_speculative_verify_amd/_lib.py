@@ -107,6 +107,12 @@ def load() -> ctypes.CDLL:
     lib.taco_gemm_w8a8.restype = ctypes.c_int
     lib.taco_gemm_w4a16.argtypes = [P, P, P, P, I32, I32, I32, I32, P]
     lib.taco_gemm_w4a16.restype = ctypes.c_int
+    lib.taco_gemm_w4a16_tiled_bytes.argtypes = [I32, I32]
+    lib.taco_gemm_w4a16_tiled_bytes.restype = SZ
+    lib.taco_gemm_w4a16_pack.argtypes = [P, P, I32, I32, P]
+    lib.taco_gemm_w4a16_pack.restype = ctypes.c_int
+    lib.taco_gemm_w4a16_tiled.argtypes = [P, P, P, P, I32, I32, I32, I32, P]
+    lib.taco_gemm_w4a16_tiled.restype = ctypes.c_int
     lib.taco_la_create.argtypes = [I32, I32]
     lib.taco_la_create.restype = P
     lib.taco_la_destroy.argtypes = [P]
@@ -580,17 +586,40 @@ def taco_gemm_w8a8(a, a_scale, w, w_scale, y=None, stream=None):
     return y
 
 
-def taco_gemm_w4a16(a, w_packed, w_scale, group, y=None, stream=None):
+def taco_gemm_w4a16_pack(w_packed, stream=None):
+    """Weights of taco_gemm_w4a16 (uint8 [N, K / 2]) rearranged into the GEMM's load order
+    (taco_gemm_w4a16_pack, include/pta_gemm.h); returns the new uint8 buffer, whose use
+    needs N and K: pass it to taco_gemm_w4a16 with tiled=(N, K)."""
+    torch = _torch()
+    _need(w_packed, "w_packed", 2, torch.uint8)
+    N, K = w_packed.shape[0], w_packed.shape[1] * 2
+    lib = load()
+    nbytes = int(lib.taco_gemm_w4a16_tiled_bytes(N, K))
+    if nbytes == 0:
+        raise ValueError("N and K out of range for the rearranged layout")
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w_packed.device)
+    _check(lib.taco_gemm_w4a16_pack(w_packed.data_ptr(), out.data_ptr(), N, K, _stream(stream)))
+    return out
+
+
+def taco_gemm_w4a16(a, w_packed, w_scale, group, y=None, stream=None, tiled=None):
     """W4A16 GEMM (include/pta_gemm.h): a bf16 [M, K], w_packed uint8 [N, K / 2] (two's
     complement int4, k = 2 j in the low nibble of byte j), w_scale float32 [N, K / group];
-    returns y bf16 [M, N] = sum_k a[m, k] q[n, k] w_scale[n, k // group]."""
+    returns y bf16 [M, N] = sum_k a[m, k] q[n, k] w_scale[n, k // group].  tiled=(N, K):
+    w_packed is the 1-D output of taco_gemm_w4a16_pack (taco_gemm_w4a16_tiled)."""
     torch = _torch()
     _need(a, "a", 2, torch.bfloat16)
-    _need(w_packed, "w_packed", 2, torch.uint8, a.device)
     M, K = a.shape
-    N = w_packed.shape[0]
-    if w_packed.shape[1] * 2 != K:
-        raise ValueError("w_packed must hold K / 2 bytes per row")
+    if tiled is not None:
+        N, Kt = (int(v) for v in tiled)
+        _need(w_packed, "w_packed", 1, torch.uint8, a.device)
+        if Kt != K or w_packed.numel() != int(load().taco_gemm_w4a16_tiled_bytes(N, K)):
+            raise ValueError("tiled weights must come from taco_gemm_w4a16_pack of an [N, K / 2] matrix")
+    else:
+        _need(w_packed, "w_packed", 2, torch.uint8, a.device)
+        N = w_packed.shape[0]
+        if w_packed.shape[1] * 2 != K:
+            raise ValueError("w_packed must hold K / 2 bytes per row")
     group = int(group)
     if group <= 0 or K % group:
         raise ValueError("group must divide K")
@@ -602,8 +631,9 @@ def taco_gemm_w4a16(a, w_packed, w_scale, group, y=None, stream=None):
     _need(y, "y", 2, torch.bfloat16, a.device)
     if tuple(y.shape) != (M, N):
         raise ValueError("y must be [M, N]")
-    _check(load().taco_gemm_w4a16(a.data_ptr(), w_packed.data_ptr(), w_scale.data_ptr(), y.data_ptr(),
-                                  M, N, K, group, _stream(stream)))
+    fn = load().taco_gemm_w4a16_tiled if tiled is not None else load().taco_gemm_w4a16
+    _check(fn(a.data_ptr(), w_packed.data_ptr(), w_scale.data_ptr(), y.data_ptr(), M, N, K, group,
+              _stream(stream)))
     return y
 
 

@@ -368,7 +368,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
 //     first stage, into one of four slots (group & 3).
 //   * Staging as the W8A8 kernel: buffer-resource LDS-DMA with the whole offset
 //     in the range-checked vector offset (rows past M or N read zero), NBUF
-//     stages, XCD-grouped tile order.  Swizzles: the 16-byte unit u of
+//     stages, XCD-grouped tile order.  With weights rearranged by
+//     taco_gemm_w4a16_pack (TILED) a stage's weight tile is one contiguous
+//     4 KiB block, copied as is.  Swizzles: the 16-byte unit u of
 //     activation row r sits at u ^ ((r >> 1) & 7) (rows are 128 bytes), the
 //     unit u of weight row r at u ^ ((r >> 3) & 1) (rows are 32 bytes): the 16
 //     lanes of one read pass touch 16 distinct bank groups.
@@ -405,7 +407,29 @@ __device__ __forceinline__ bf16x8 int4x8_to_bf16(uint32_t w) {
   return __builtin_bit_cast(bf16x8, make_uint4(r[0], r[1], r[2], r[3]));
 }
 
-template <int WM>
+// Weight tiles in load order (the rearranged layout of taco_gemm_w4a16_pack):
+// the 4 KiB block of 128-column tile nt and 64-k stage s sits at byte
+// (nt * (K / 64) + s) * 4096 and is the LDS image of that stage's weight tile:
+// byte 32 r + 16 p holds the 16 bytes of column 128 nt + r at k-bytes
+// 32 s + 16 (p ^ ((r >> 3) & 1)) (zero past N).  A stage's weights then arrive
+// as four contiguous 1 KiB copies, whole 128-byte lines, where the row-major
+// layout moves 32 bytes of each of 32 rows per copy.
+__global__ __launch_bounds__(256) void w4a16_pack_kernel(const uint8_t* w, uint8_t* wt, int N, int K,
+                                                        int64_t units) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one 16-byte unit of the tiled buffer
+  if (u >= units) return;
+  const int nk = K / 64;
+  const int64_t blk = u >> 8;                                   // 256 units per 4 KiB block
+  const int within = (int)(u & 255), r = within >> 1, p = within & 1;
+  const int nt = (int)(blk / nk), st = (int)(blk % nk);
+  const int n = nt * 128 + r;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (n < N)
+    v = *reinterpret_cast<const uint4*>(w + (int64_t)n * (K / 2) + 32 * st + 16 * (p ^ ((r >> 3) & 1)));
+  *reinterpret_cast<uint4*>(wt + u * 16) = v;
+}
+
+template <int WM, bool TILED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w4a16_kernel(
     const uint16_t* a, const uint8_t* w, const float* w_scale, uint16_t* y, int M, int N, int K, int G, int tm,
     int tn) {
@@ -421,7 +445,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
   const int KG = K / G;                                     // groups per row
 
   const i32x4 ars = gemm_rsrc(a, (uint32_t)((uint64_t)M * (uint64_t)K * 2u));
-  const i32x4 wrs = gemm_rsrc(w, (uint32_t)((uint64_t)N * (uint64_t)K / 2u));
+  const i32x4 wrs = gemm_rsrc(w, TILED ? (uint32_t)((uint64_t)tn * 128u * (uint64_t)K / 2u)
+                                       : (uint32_t)((uint64_t)N * (uint64_t)K / 2u));
   const i32x4 srs = gemm_rsrc(w_scale, (uint32_t)((uint64_t)N * (uint64_t)KG * 4u));
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&lds[0];
 
@@ -434,7 +459,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
 #pragma unroll
   for (int par = 0; par < 2; ++par)
     voffA[par] = (uint32_t)((lane >> 3) * 2 * K + 16 * ((lane & 7) ^ ((4 * par + (lane >> 4)) & 7)));
-  const uint32_t voffW = (uint32_t)((lane >> 1) * (K / 2) + 16 * ((lane & 1) ^ ((lane >> 4) & 1)));
+  const uint32_t voffW =
+      TILED ? (uint32_t)(16 * lane) : (uint32_t)((lane >> 1) * (K / 2) + 16 * ((lane & 1) ^ ((lane >> 4) & 1)));
   const int nk = K / Gm::BK, GS = G / Gm::BK;              // stages, stages per group
   auto copy_stage = [&](int s, int buf) {
     const uint32_t kb = (uint32_t)(s * Gm::BK);
@@ -444,6 +470,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
       if (c < Gm::CHUNKS_A)
         gemm_copy(lds0 + (uint32_t)(buf * Gm::A_TILE + c * 1024), ars,
                   (uint32_t)(m0 + 8 * c) * (uint32_t)(2 * K) + 2u * kb, voffA[c & 1]);
+      else if (TILED)
+        gemm_copy(lds0 + (uint32_t)(Gm::W_REG + buf * Gm::W_TILE + (c - Gm::CHUNKS_A) * 1024), wrs,
+                  ((uint32_t)nt * (uint32_t)nk + (uint32_t)s) * 4096u + 1024u * (uint32_t)(c - Gm::CHUNKS_A), voffW);
       else
         gemm_copy(lds0 + (uint32_t)(Gm::W_REG + buf * Gm::W_TILE + (c - Gm::CHUNKS_A) * 1024), wrs,
                   (uint32_t)(n0 + 32 * (c - Gm::CHUNKS_A)) * (uint32_t)(K / 2) + kb / 2u, voffW);
@@ -557,8 +586,12 @@ pta_status taco_gemm_w8a8(const void* a, const float* a_scale, const void* w, co
   return hipGetLastError() == hipSuccess ? PTA_OK : PTA_ERR_HIP;
 }
 
-pta_status taco_gemm_w4a16(const void* a, const void* w, const float* w_scale, void* y, int32_t M, int32_t N,
-                           int32_t K, int32_t group, void* stream) {
+}  // extern "C"
+
+namespace {
+
+pta_status w4a16_call(const void* a, const void* w, const float* w_scale, void* y, int32_t M, int32_t N,
+                      int32_t K, int32_t group, void* stream, bool tiled) {
   if (!a || !w || !w_scale || !y) return PTA_ERR_NULL_PTR;
   if (M < 1 || N < 1 || K < 64 || K % 64 != 0 || group < 64 || group % 64 != 0 || K % group != 0)
     return PTA_ERR_BAD_DIMS;
@@ -576,15 +609,50 @@ pta_status taco_gemm_w4a16(const void* a, const void* w, const float* w_scale, v
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   const int64_t blocks = (int64_t)8 * tm * ((tn + 7) / 8);
   if (blocks > 0x7fffffff) return PTA_ERR_BAD_DIMS;
-  if (tall)
-    hipLaunchKernelGGL(gemm_w4a16_kernel<4>, dim3((unsigned)blocks), dim3(NT), 0, (hipStream_t)stream,
+  auto launch = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NT), 0, (hipStream_t)stream,
                        reinterpret_cast<const uint16_t*>(a), reinterpret_cast<const uint8_t*>(w), w_scale,
                        reinterpret_cast<uint16_t*>(y), M, N, K, group, tm, tn);
-  else
-    hipLaunchKernelGGL(gemm_w4a16_kernel<2>, dim3((unsigned)blocks), dim3(NT), 0, (hipStream_t)stream,
-                       reinterpret_cast<const uint16_t*>(a), reinterpret_cast<const uint8_t*>(w), w_scale,
-                       reinterpret_cast<uint16_t*>(y), M, N, K, group, tm, tn);
+  };
+  if (tall) {
+    if (tiled) launch(gemm_w4a16_kernel<4, true>);
+    else launch(gemm_w4a16_kernel<4, false>);
+  } else {
+    if (tiled) launch(gemm_w4a16_kernel<2, true>);
+    else launch(gemm_w4a16_kernel<2, false>);
+  }
   return hipGetLastError() == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+pta_status taco_gemm_w4a16(const void* a, const void* w, const float* w_scale, void* y, int32_t M, int32_t N,
+                           int32_t K, int32_t group, void* stream) {
+  return w4a16_call(a, w, w_scale, y, M, N, K, group, stream, false);
+}
+
+size_t taco_gemm_w4a16_tiled_bytes(int32_t N, int32_t K) {
+  if (N < 1 || K < 64 || K % 64 != 0) return 0;
+  const uint64_t bytes = (uint64_t)((N + 127) / 128) * 128u * (uint64_t)K / 2u;
+  return bytes < ((uint64_t)1 << 32) ? (size_t)bytes : 0;
+}
+
+pta_status taco_gemm_w4a16_pack(const void* w, void* w_tiled, int32_t N, int32_t K, void* stream) {
+  if (!w || !w_tiled) return PTA_ERR_NULL_PTR;
+  const size_t bytes = taco_gemm_w4a16_tiled_bytes(N, K);
+  if (bytes == 0) return PTA_ERR_BAD_DIMS;
+  if ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(w_tiled)) % 16 != 0) return PTA_ERR_BAD_DIMS;
+  const int64_t units = (int64_t)(bytes / 16);
+  hipLaunchKernelGGL(w4a16_pack_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                     reinterpret_cast<const uint8_t*>(w), reinterpret_cast<uint8_t*>(w_tiled), N, K, units);
+  return hipGetLastError() == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+}
+
+pta_status taco_gemm_w4a16_tiled(const void* a, const void* w_tiled, const float* w_scale, void* y, int32_t M,
+                                 int32_t N, int32_t K, int32_t group, void* stream) {
+  return w4a16_call(a, w_tiled, w_scale, y, M, N, K, group, stream, true);
 }
 
 }  // extern "C"

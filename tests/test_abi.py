@@ -227,6 +227,21 @@ def test_gemm_host_checks(lib):
     assert call(M=66817, K=64064) == DIMS
 
 
+def test_gemm_w4a16_tiled_host_checks(lib):
+    """Rearranged-weight entries: sizes, pointers and alignment checked on the host."""
+    assert lib.taco_gemm_w4a16_tiled_bytes(0, 64) == 0 and lib.taco_gemm_w4a16_tiled_bytes(4, 100) == 0
+    assert lib.taco_gemm_w4a16_tiled_bytes(4, 128) == 128 * 64           # N padded to 128 columns
+    assert lib.taco_gemm_w4a16_tiled_bytes(57344, 8192) == 57344 * 4096
+    assert lib.taco_gemm_w4a16_tiled_bytes(1 << 20, 1 << 13) == 0         # 2^32 bytes
+    pack = lib.taco_gemm_w4a16_pack
+    assert pack(None, FAKE, 4, 128, None) == NULLP and pack(FAKE, None, 4, 128, None) == NULLP
+    assert pack(FAKE, FAKE, 4, 100, None) == DIMS and pack(FAKE, FAKE, 0, 128, None) == DIMS
+    assert pack(ctypes.c_void_p(0x10008), FAKE, 4, 128, None) == DIMS
+    f = lib.taco_gemm_w4a16_tiled
+    assert f(FAKE, None, FAKE, FAKE, 4, 4, 128, 64, None) == NULLP
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 4, 128, 96, None) == DIMS       # group not a multiple of 64
+
+
 def test_gemm_w4a16_host_checks(lib):
     """taco_gemm_w4a16 rejects bad arguments on the host, before any HIP call."""
     f = lib.taco_gemm_w4a16

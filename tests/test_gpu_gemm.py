@@ -138,12 +138,16 @@ from oracle.formats import decode_bf16  # noqa: E402
 from workload.gemm import W4A16, make_w4a16, make_w4a16_device, pack_int4  # noqa: E402
 
 
-def run4(torch, g, rows=None):
+def run4(torch, g, rows=None, tiled=False):
     import paged_speculative_verify_amd as psv
     a = torch.from_numpy(np.ascontiguousarray(g.a_bits).view(np.int16)).cuda().view(torch.bfloat16)
     w = torch.from_numpy(np.ascontiguousarray(g.w_packed)).cuda()
     s = torch.from_numpy(np.ascontiguousarray(g.w_scale)).cuda()
-    y = psv.taco_gemm_w4a16(a, w, s, g.group)
+    if tiled:
+        N, K = w.shape[0], w.shape[1] * 2
+        y = psv.taco_gemm_w4a16(a, psv.taco_gemm_w4a16_pack(w), s, g.group, tiled=(N, K))
+    else:
+        y = psv.taco_gemm_w4a16(a, w, s, g.group)
     torch.cuda.synchronize()
     y = y.float().cpu().numpy().astype(np.float64)
     return y if rows is None else y[rows]
@@ -190,6 +194,61 @@ def test_w4a16_parity(torch_cuda, cid, M, N, K, G, seed):
     y = run4(torch_cuda, g)
     r = check4(g, y)
     say(cid, "worst error / bound", r)
+
+
+def tiled_layout(w_packed):
+    """The rearranged weight buffer as include/pta_gemm.h defines it, built with numpy loops over
+    its blocks: block (t, s) at byte (t * K / 64 + s) * 4096 holds at byte 32 r + 16 p the 16
+    bytes of column 128 t + r at k-bytes 32 s + 16 (p ^ ((r >> 3) & 1)), zero past N."""
+    N, KB = w_packed.shape
+    K = 2 * KB
+    T, S = (N + 127) // 128, K // 64
+    out = np.zeros(T * S * 4096, np.uint8)
+    for t in range(T):
+        for st in range(S):
+            blk = out[(t * S + st) * 4096:(t * S + st + 1) * 4096].reshape(128, 2, 16)
+            for r in range(128):
+                n = 128 * t + r
+                if n >= N:
+                    continue
+                for p in range(2):
+                    u = p ^ ((r >> 3) & 1)
+                    blk[r, p] = w_packed[n, 32 * st + 16 * u:32 * st + 16 * u + 16]
+    return out
+
+
+@pytest.mark.parametrize("cid,M,N,K,G,seed", W4_CASES[:5], ids=[c[0] for c in W4_CASES[:5]])
+def test_w4a16_tiled_parity(torch_cuda, cid, M, N, K, G, seed):
+    """The rearranged weights match the header's layout byte for byte, and the GEMM on them
+    gives exactly the row-major GEMM's output (itself checked against the oracle above) and
+    stays within the oracle's bound."""
+    import torch
+    import paged_speculative_verify_amd as psv
+    g = make_w4a16(M, N, K, G, seed=seed)
+    say("tiled", cid, M, N, K, G)
+    w = torch.from_numpy(np.ascontiguousarray(g.w_packed)).cuda()
+    wt = psv.taco_gemm_w4a16_pack(w)
+    torch.cuda.synchronize()
+    assert np.array_equal(wt.cpu().numpy(), tiled_layout(g.w_packed))
+    y_t = run4(torch_cuda, g, tiled=True)
+    y_r = run4(torch_cuda, g)
+    assert np.array_equal(y_t, y_r)
+    check4(g, y_t)
+
+
+def test_w4a16_tiled_full_size(torch_cuda):
+    """The timed shape (512 x 57344 x 8192, group 128) on rearranged weights: the whole output
+    equals the row-major GEMM's bit for bit."""
+    import torch
+    import paged_speculative_verify_amd as psv
+    s = LLAMA70B_GATE_UP
+    M, N, K, G = s["M"], s["N"], s["K"], 128
+    a, w, sc = make_w4a16_device(M, N, K, G, seed=8, torch=torch)
+    say("tiled full size", s)
+    y_r = psv.taco_gemm_w4a16(a, w, sc, G)
+    y_t = psv.taco_gemm_w4a16(a, psv.taco_gemm_w4a16_pack(w), sc, G, tiled=(N, K))
+    torch.cuda.synchronize()
+    assert torch.equal(y_r.view(torch.int16), y_t.view(torch.int16))
 
 
 def test_w4a16_full_size_sampled_rows(torch_cuda):
