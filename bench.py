@@ -411,13 +411,15 @@ def build_sets(psv, torch, name, cfg, nsets, private_pages=False):
         else:
             ds.append_call = psv.prepare_kv_append(ds.k_new, ds.v_new, ds.slots, d.k_cache, d.v_cache,
                                                    k_scale=d.k_scale, v_scale=d.v_scale)
+        # block tables that alias a shared prefix's pages say so (they keep the default cache policy)
+        shared = ds.w.spec.shared_prefix_pages > 0 and ds.w.spec.share_group > 1
         ds.attn_call = psv.prepare_paged_tree_attn(
             cfg["mode"] + "_append" if cfg.get("fuse_append") else cfg["mode"],
             d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens, d.tree_mask,
             d.scale, ds.out, lse=ds.lse, k_scale=d.k_scale, v_scale=d.v_scale,
             partition_tokens=cfg["split"], workspace=ds.workspace, max_ctx_len=d.max_ctx_len,
             prefix_leader=ds.prefix_leader, max_group=ds.max_group, k_new=ds.k_new_full, v_new=ds.v_new_full,
-            path=cfg["path"])
+            path=cfg["path"], shared_pages=shared)
     torch.cuda.synchronize()
     return sets
 

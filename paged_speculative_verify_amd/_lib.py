@@ -38,7 +38,7 @@ class PtaDims(ctypes.Structure):
         ("q_dtype", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
         ("path", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -192,7 +192,12 @@ def _need(t, name, ndim=None, dtype=None, device=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
-def make_dims(q, k_cache, block_tables, max_ctx_len=None, path="auto") -> PtaDims:
+PTA_FLAG_SHARED_PAGES = 1
+
+
+def make_dims(q, k_cache, block_tables, max_ctx_len=None, path="auto", shared_pages=False) -> PtaDims:
+    """shared_pages: the block tables may name one physical page for several sequences
+    (PTA_FLAG_SHARED_PAGES: page tiles then keep the default cache policy)."""
     B, Qmax, Hq, D = q.shape
     NB, Hkv, page, D2 = k_cache.shape
     if D2 != D:
@@ -202,7 +207,7 @@ def make_dims(q, k_cache, block_tables, max_ctx_len=None, path="auto") -> PtaDim
                    max_q_len=Qmax, max_blocks_per_seq=MBS,
                    max_ctx_len=int(max_ctx_len) if max_ctx_len is not None else MBS * page,
                    num_blocks=NB, q_dtype=_q_code(q), kv_dtype=_kv_code(k_cache),
-                   path=PATHS[path], reserved=0)
+                   path=PATHS[path], flags=PTA_FLAG_SHARED_PAGES if shared_pages else 0)
 
 
 def _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale, scales=True):
@@ -251,12 +256,12 @@ def _alloc_out(q, out, lse):
 # ---------------------------------------------------------------- entry points
 def taco_paged_tree_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, scale,
                          out=None, lse=None, k_scale=None, v_scale=None, max_ctx_len=None,
-                         path="auto", stream=None):
+                         path="auto", stream=None, shared_pages=False):
     """Paged tree attention over each sequence's whole context (see include/pta.h)."""
     lib = load()
     _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale)
     out, lse = _alloc_out(q, out, lse)
-    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path, shared_pages)
     _check(lib.taco_paged_tree_attn(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), _ptr(ctx_lens),
                                     _ptr(q_lens), _ptr(tree_mask), float(scale), _ptr(out), _ptr(lse),
@@ -265,15 +270,15 @@ def taco_paged_tree_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tr
 
 
 def taco_paged_tree_attn_splitk_workspace_size(q, k_cache, block_tables, partition_tokens,
-                                               max_ctx_len=None, path="auto") -> int:
-    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+                                               max_ctx_len=None, path="auto", shared_pages=False) -> int:
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path, shared_pages)
     return int(load().taco_paged_tree_attn_splitk_workspace_size(ctypes.byref(dims), int(partition_tokens)))
 
 
 def taco_paged_tree_attn_splitk(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask,
                                 scale, partition_tokens, out=None, lse=None, k_scale=None,
                                 v_scale=None, workspace=None, max_ctx_len=None, path="auto",
-                                stream=None):
+                                stream=None, shared_pages=False):
     """Split-K paged tree attention with a log-sum-exp merge (see include/pta.h).
 
     workspace: a caller-owned uint8 device tensor of at least
@@ -285,7 +290,7 @@ def taco_paged_tree_attn_splitk(q, k_cache, v_cache, block_tables, ctx_lens, q_l
     lib = load()
     _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale)
     out, lse = _alloc_out(q, out, lse)
-    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path, shared_pages)
     need = int(lib.taco_paged_tree_attn_splitk_workspace_size(ctypes.byref(dims), int(partition_tokens)))
     if workspace is None:
         if need == 0:
@@ -303,7 +308,7 @@ def taco_paged_tree_attn_splitk(q, k_cache, v_cache, block_tables, ctx_lens, q_l
 
 def taco_paged_tree_attn_append(q, k_new, v_new, k_cache, v_cache, block_tables, ctx_lens, q_lens,
                                 tree_mask, scale, out=None, lse=None, k_scale=None, v_scale=None,
-                                max_ctx_len=None, path="auto", stream=None):
+                                max_ctx_len=None, path="auto", stream=None, shared_pages=False):
     """KV append fused into the whole-context attention call (see include/pta.h).
 
     k_new, v_new: [B, Qmax, Hkv, D] device tensors, the candidates' K/V rows, written into their
@@ -317,7 +322,7 @@ def taco_paged_tree_attn_append(q, k_new, v_new, k_cache, v_cache, block_tables,
     if tuple(k_new.shape) != (B, Qmax, k_cache.shape[1], D) or tuple(v_new.shape) != tuple(k_new.shape):
         raise ValueError("k_new / v_new must be [B, Qmax, Hkv, D]")
     out, lse = _alloc_out(q, out, lse)
-    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path, shared_pages)
     _check(lib.taco_paged_tree_attn_append(
         ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new), _q_code(k_new), _ptr(k_cache), _ptr(v_cache),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask),
@@ -327,7 +332,7 @@ def taco_paged_tree_attn_append(q, k_new, v_new, k_cache, v_cache, block_tables,
 
 def taco_paged_tree_attn_balanced_append(q, k_new, v_new, k_cache, v_cache, block_tables, ctx_lens, q_lens,
                                          tree_mask, scale, out=None, lse=None, workspace=None, max_ctx_len=None,
-                                         path="auto", stream=None):
+                                         path="auto", stream=None, shared_pages=False):
     """KV append fused into the balanced entry (see include/pta.h): bf16 k_new, v_new
     [B, Qmax, Hkv, D] written into their paged slots by the grid before it reads them.
 
@@ -343,7 +348,7 @@ def taco_paged_tree_attn_balanced_append(q, k_new, v_new, k_cache, v_cache, bloc
     if tuple(k_new.shape) != (B, Qmax, k_cache.shape[1], D) or tuple(v_new.shape) != tuple(k_new.shape):
         raise ValueError("k_new / v_new must be [B, Qmax, Hkv, D]")
     out, lse = _alloc_out(q, out, lse)
-    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path, shared_pages)
     need = int(lib.taco_paged_tree_attn_balanced_workspace_size(ctypes.byref(dims)))
     if workspace is None:
         if need == 0:
@@ -361,7 +366,7 @@ def taco_paged_tree_attn_balanced_append(q, k_new, v_new, k_cache, v_cache, bloc
 def taco_paged_tree_attn_shared_prefix(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask,
                                        prefix_leader, max_group, shared_tokens, scale, out=None, lse=None,
                                        k_scale=None, v_scale=None, workspace=None, max_ctx_len=None,
-                                       path="auto", stream=None):
+                                       path="auto", stream=None, shared_pages=False):
     """Shared-prefix paged tree attention (see include/pta.h): partition 0 of every group of
     consecutive sequences that alias their first shared_tokens / 16 pages is worked once.
 
@@ -374,7 +379,7 @@ def taco_paged_tree_attn_shared_prefix(q, k_cache, v_cache, block_tables, ctx_le
     _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale)
     _need(prefix_leader, "prefix_leader", 1, torch.int32, q.device)
     out, lse = _alloc_out(q, out, lse)
-    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path, shared_pages)
     need = int(lib.taco_paged_tree_attn_splitk_workspace_size(ctypes.byref(dims), int(shared_tokens)))
     if workspace is None:
         if need == 0:
@@ -391,14 +396,14 @@ def taco_paged_tree_attn_shared_prefix(q, k_cache, v_cache, block_tables, ctx_le
 
 
 def taco_paged_tree_attn_balanced_workspace_size(q, k_cache, block_tables, max_ctx_len=None,
-                                                 path="auto") -> int:
-    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+                                                 path="auto", shared_pages=False) -> int:
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path, shared_pages)
     return int(load().taco_paged_tree_attn_balanced_workspace_size(ctypes.byref(dims)))
 
 
 def taco_paged_tree_attn_balanced(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask,
                                   scale, out=None, lse=None, k_scale=None, v_scale=None,
-                                  workspace=None, max_ctx_len=None, path="auto", stream=None):
+                                  workspace=None, max_ctx_len=None, path="auto", stream=None, shared_pages=False):
     """Work-balanced paged tree attention (see include/pta.h).
 
     workspace: a caller-owned uint8 device tensor of at least
@@ -409,7 +414,7 @@ def taco_paged_tree_attn_balanced(q, k_cache, v_cache, block_tables, ctx_lens, q
     lib = load()
     _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale)
     out, lse = _alloc_out(q, out, lse)
-    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path, shared_pages)
     need = int(lib.taco_paged_tree_attn_balanced_workspace_size(ctypes.byref(dims)))
     if workspace is None:
         if need == 0:
@@ -430,14 +435,14 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 
 def taco_paged_tree_attn_balanced_noalloc(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask,
                                           scale, out=None, lse=None, k_scale=None, v_scale=None,
-                                          max_ctx_len=None, path="auto", stream=None):
+                                          max_ctx_len=None, path="auto", stream=None, shared_pages=False):
     """taco_paged_tree_attn_balanced with the library's own per-GPU scratch array as the workspace
     (no allocation by the library; see include/pta.h for the size limit and the rule that calls
     overlapping on one GPU race).  Allocates out/lse here only when they are not given."""
     lib = load()
     _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale)
     out, lse = _alloc_out(q, out, lse)
-    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path, shared_pages)
     _check(lib.taco_paged_tree_attn_balanced_noalloc(
         ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask), float(scale), _ptr(out),
@@ -463,7 +468,7 @@ def taco_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v
         raise ValueError("new rows and caches disagree on heads / head_dim")
     dims = PtaDims(num_seqs=0, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=D, page_size=k_cache.shape[2],
                    max_q_len=1, max_blocks_per_seq=1, max_ctx_len=1, num_blocks=k_cache.shape[0],
-                   q_dtype=PTA_BF16, kv_dtype=_kv_code(k_cache), path=0, reserved=0)
+                   q_dtype=PTA_BF16, kv_dtype=_kv_code(k_cache), path=0, flags=0)
     _check(lib.taco_kv_append(ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _q_code(k_new),
                               _ptr(slot_mapping), N, _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                               _ptr(v_scale), _stream(stream)))
@@ -507,7 +512,7 @@ def taco_accept_commit(cand_tokens, target_tokens, target_prev, ctx_lens, q_lens
                    max_q_len=Qmax, max_blocks_per_seq=block_tables.shape[1],
                    max_ctx_len=block_tables.shape[1] * page, num_blocks=NB,
                    q_dtype=PTA_BF16 if _kv_code(k_cache) != 0 else 0, kv_dtype=_kv_code(k_cache),
-                   path=0, reserved=0)
+                   path=0, flags=0)
     _check(lib.taco_accept_commit(ctypes.byref(dims), _ptr(cand_tokens), _ptr(target_tokens),
                                   _ptr(target_prev), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask),
                                   _ptr(block_tables), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
@@ -531,7 +536,7 @@ def taco_pta_validate(block_tables, ctx_lens, q_lens, max_q_len, num_blocks, max
     dims = PtaDims(num_seqs=B, num_q_heads=1, num_kv_heads=1, head_dim=128, page_size=16,
                    max_q_len=int(max_q_len), max_blocks_per_seq=MBS,
                    max_ctx_len=int(max_ctx_len) if max_ctx_len is not None else MBS * 16,
-                   num_blocks=int(num_blocks), q_dtype=PTA_BF16, kv_dtype=PTA_BF16, path=0, reserved=0)
+                   num_blocks=int(num_blocks), q_dtype=PTA_BF16, kv_dtype=PTA_BF16, path=0, flags=0)
     _check(lib.taco_pta_validate(ctypes.byref(dims), _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens),
                                  _ptr(flags), _stream(stream)))
     return int(flags.item())
@@ -667,7 +672,7 @@ class PreparedCall:
 def prepare_paged_tree_attn(mode, q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask,
                             scale, out, lse=None, k_scale=None, v_scale=None, partition_tokens=None,
                             workspace=None, max_ctx_len=None, path="auto", stream=None, prefix_leader=None,
-                            max_group=None, k_new=None, v_new=None) -> PreparedCall:
+                            max_group=None, k_new=None, v_new=None, shared_pages=False) -> PreparedCall:
     """Validate once and return a PreparedCall for one of the attention entry points.
 
     mode: "whole" (taco_paged_tree_attn), "whole_append" (taco_paged_tree_attn_append with k_new,
@@ -681,7 +686,7 @@ def prepare_paged_tree_attn(mode, q, k_cache, v_cache, block_tables, ctx_lens, q
     lib = load()
     _check_attn(q, k_cache, v_cache, block_tables, ctx_lens, q_lens, tree_mask, k_scale, v_scale)
     out, lse = _alloc_out(q, out, lse)
-    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path)
+    dims = make_dims(q, k_cache, block_tables, max_ctx_len, path, shared_pages)
     common = (ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
               _ptr(block_tables), _ptr(ctx_lens), _ptr(q_lens), _ptr(tree_mask), float(scale),
               _ptr(out), _ptr(lse))
@@ -746,7 +751,7 @@ def prepare_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None
     N, Hkv, D = k_new.shape
     dims = PtaDims(num_seqs=0, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=D, page_size=k_cache.shape[2],
                    max_q_len=1, max_blocks_per_seq=1, max_ctx_len=1, num_blocks=k_cache.shape[0],
-                   q_dtype=PTA_BF16, kv_dtype=_kv_code(k_cache), path=0, reserved=0)
+                   q_dtype=PTA_BF16, kv_dtype=_kv_code(k_cache), path=0, flags=0)
     args = (ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _q_code(k_new), _ptr(slot_mapping), N,
             _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _stream(stream))
     return PreparedCall(lib.taco_kv_append, args,

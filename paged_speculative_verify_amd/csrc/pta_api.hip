@@ -37,7 +37,7 @@ pta_status check_dims(const pta_dims* d) {
       (int64_t)d->max_ctx_len > (int64_t)d->page_size * d->max_blocks_per_seq)
     return PTA_ERR_BAD_DIMS;
   if (d->num_blocks < 1) return PTA_ERR_BAD_DIMS;
-  if (d->reserved != 0) return PTA_ERR_BAD_DIMS;
+  if ((d->flags & ~PTA_FLAG_SHARED_PAGES) != 0) return PTA_ERR_BAD_DIMS;
   if (!dtype_ok(d->q_dtype, d->kv_dtype)) return PTA_ERR_BAD_DTYPE;
   if (d->path < PTA_PATH_AUTO || d->path > PTA_PATH_TILE16) return PTA_ERR_BAD_DIMS;
   return PTA_OK;
@@ -121,6 +121,7 @@ AttnArgs make_args(const pta_dims* d, const void* q, const void* k, const void* 
   a.G = d->num_q_heads / d->num_kv_heads;
   a.Qmax = d->max_q_len; a.MBS = d->max_blocks_per_seq;
   a.num_blocks = d->num_blocks;
+  a.stream_pages = (d->flags & PTA_FLAG_SHARED_PAGES) == 0;
   return a;
 }
 

@@ -55,6 +55,9 @@ struct AttnArgs {
   const void* v_new;
   int32_t new_f32;
   int64_t num_blocks;
+  // no page is named by two sequences' block tables: page tiles that one
+  // workgroup alone reads take the nontemporal (streaming) load hint
+  int32_t stream_pages;
 };
 
 // ---------------------------------------------------------------- conversions

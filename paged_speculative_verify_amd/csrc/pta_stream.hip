@@ -53,6 +53,17 @@
 
 namespace pta {
 
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// 16 bytes of a page tile; nontemporal (streaming) when no other workgroup reads the
+// page (a template choice: a runtime one lets the compiler merge both loads into one
+// without the hint)
+template <bool NT>
+__device__ __forceinline__ uint4 tile_load(const char* p) {
+  if constexpr (NT) return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p)));
+  else return *reinterpret_cast<const uint4*>(p);
+}
+
 // Page pairs j = j0, j0 + js, ... of the range [pA, pB): pair j is pages
 // pA + 2j and, if it is in the range, pA + 2j + 1 (else the first page again,
 // its tokens masked and its V rows zeroed).  One pair's K and V chunks are in
@@ -69,7 +80,7 @@ struct PairRegs {
 
 // prog_len > 0: the wave owns a slice of prog_len pages of which prog0 come
 // before this range, and paces itself by its progress through the slice.
-template <typename KT, int D, int RB>
+template <typename KT, int D, int RB, bool NT>
 __device__ __forceinline__ void stream_pairs(const AttnArgs& a, const StreamRows<D, RB>& rows,
                                              StreamState<D, RB>& st, int b, int hkv, int L, int t_end,
                                              int pA, int pB, int j0, int js, char* wl, int lane,
@@ -99,9 +110,9 @@ __device__ __forceinline__ void stream_pairs(const AttnArgs& a, const StreamRows
     for (int pg = 0; pg < 2; ++pg) {
       const int64_t tile = (ph[pg] * a.Hkv + hkv) * TILE_BYTES + 16 * lane;
 #pragma unroll
-      for (int j = 0; j < T::LOADS; ++j) R.k[pg][j] = *reinterpret_cast<const uint4*>(kbase + tile + 1024 * j);
+      for (int j = 0; j < T::LOADS; ++j) R.k[pg][j] = tile_load<NT>(kbase + tile + 1024 * j);
 #pragma unroll
-      for (int j = 0; j < T::LOADS; ++j) R.v[pg][j] = *reinterpret_cast<const uint4*>(vbase + tile + 1024 * j);
+      for (int j = 0; j < T::LOADS; ++j) R.v[pg][j] = tile_load<NT>(vbase + tile + 1024 * j);
       if constexpr (KT::bytes == 1) {
         R.ks[pg] = a.k_scale[ph[pg] * a.Hkv + hkv];
         R.vs[pg] = a.v_scale[ph[pg] * a.Hkv + hkv];
@@ -347,7 +358,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // this wave's page pairs: wave, wave + NW, ... of the unit's range
   const int pgA = t0 / kPage;
   const int pgB = (t1 + kPage - 1) / kPage;
-  stream_pairs<KT, D, RB>(a, rows, st, b, hkv, L, t1, pgA, pgB, wave, NW, vlds[wave], lane);
+  // every (page, KV head) tile of a unit is read by this workgroup alone unless block
+  // tables share pages (the shared-prefix entry's partition 0 is read once per group)
+  if (a.stream_pages) stream_pairs<KT, D, RB, true>(a, rows, st, b, hkv, L, t1, pgA, pgB, wave, NW, vlds[wave], lane);
+  else stream_pairs<KT, D, RB, false>(a, rows, st, b, hkv, L, t1, pgA, pgB, wave, NW, vlds[wave], lane);
   reduce_row_sums(st);
 
   // ---- merge the waves: row max, row sum, then O^T accumulated in LDS in wave order
@@ -490,8 +504,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     load_rows(rows, a, b, hkv, qb, M, g, m);
     StreamState<D, RB> st;
     st.init();
-    stream_pairs<KT, D, RB>(a, rows, st, b, hkv, L, min(C, k1 * kPage), k0, k1, 0, 1, vlds[wave], lane,
-                            (int)(x - x0), (int)(xe - x0));
+    if (a.stream_pages)
+      stream_pairs<KT, D, RB, true>(a, rows, st, b, hkv, L, min(C, k1 * kPage), k0, k1, 0, 1, vlds[wave], lane,
+                                    (int)(x - x0), (int)(xe - x0));
+    else
+      stream_pairs<KT, D, RB, false>(a, rows, st, b, hkv, L, min(C, k1 * kPage), k0, k1, 0, 1, vlds[wave], lane,
+                                     (int)(x - x0), (int)(xe - x0));
     reduce_row_sums(st);
 
     if (k0 == 0 && k1 == Pb) {

@@ -99,37 +99,44 @@ __device__ __forceinline__ i32x4 wide_rsrc(const void* base, uint32_t bytes) {
 // m0val: chunk c reads rsrc + soff + voff[c] + 1024 c and writes m0val +
 // 1024 c + 16 lane (the instruction offset moves both addresses alike).  The
 // s_nop covers the wait state an M0 write needs before an LDS-DMA load.
-template <int CPT>
+// NTH: the nontemporal (streaming) hint, for page tiles no other workgroup reads.
+#define PTA_WIDE_COPIES(H)                                                                              \
+  if constexpr (CPT == 1) {                                                                             \
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"                                                    \
+                 "buffer_load_dwordx4 %1, %2, %3 offen" H " lds"                                        \
+                 :                                                                                      \
+                 : "s"(m0val), "v"(voff[0]), "s"(rsrc), "s"(soff)                                       \
+                 : "memory", "m0");                                                                     \
+  } else if constexpr (CPT == 4) {                                                                      \
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"                                                    \
+                 "buffer_load_dwordx4 %1, %5, %6 offen" H " lds\n\t"                                   \
+                 "buffer_load_dwordx4 %2, %5, %6 offen offset:1024" H " lds\n\t"                       \
+                 "buffer_load_dwordx4 %3, %5, %6 offen offset:2048" H " lds\n\t"                       \
+                 "buffer_load_dwordx4 %4, %5, %6 offen offset:3072" H " lds"                            \
+                 :                                                                                      \
+                 : "s"(m0val), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rsrc),       \
+                   "s"(soff)                                                                            \
+                 : "memory", "m0");                                                                     \
+  } else {                                                                                              \
+    static_assert(CPT == 2, "1, 2 or 4 chunks");                                                        \
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"                                                    \
+                 "buffer_load_dwordx4 %1, %3, %4 offen" H " lds\n\t"                                   \
+                 "buffer_load_dwordx4 %2, %3, %4 offen offset:1024" H " lds"                            \
+                 :                                                                                      \
+                 : "s"(m0val), "v"(voff[0]), "v"(voff[1]), "s"(rsrc), "s"(soff)                         \
+                 : "memory", "m0");                                                                     \
+  }
+
+template <int CPT, bool NTH>
 __device__ __forceinline__ void wide_copy_tile(uint32_t m0val, const i32x4& rsrc, uint32_t soff,
                                                const uint32_t (&voff)[CPT]) {
-  if constexpr (CPT == 1) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %2, %3 offen lds"
-        :
-        : "s"(m0val), "v"(voff[0]), "s"(rsrc), "s"(soff)
-        : "memory", "m0");
-  } else if constexpr (CPT == 4) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %5, %6 offen lds\n\t"
-        "buffer_load_dwordx4 %2, %5, %6 offen offset:1024 lds\n\t"
-        "buffer_load_dwordx4 %3, %5, %6 offen offset:2048 lds\n\t"
-        "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 lds"
-        :
-        : "s"(m0val), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rsrc), "s"(soff)
-        : "memory", "m0");
+  if constexpr (NTH) {
+    PTA_WIDE_COPIES(" nt")
   } else {
-    static_assert(CPT == 2, "1, 2 or 4 chunks");
-    asm volatile(
-        "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %3, %4 offen lds\n\t"
-        "buffer_load_dwordx4 %2, %3, %4 offen offset:1024 lds"
-        :
-        : "s"(m0val), "v"(voff[0]), "v"(voff[1]), "s"(rsrc), "s"(soff)
-        : "memory", "m0");
+    PTA_WIDE_COPIES("")
   }
 }
+#undef PTA_WIDE_COPIES
 
 // A wave-uniform table entry through the scalar cache (s_load): a vector load
 // would join the vmcnt queue behind the page copies, and waiting for it would
@@ -382,6 +389,10 @@ __device__ __forceinline__ void wide_range(const AttnArgs& a, char* lds, uint32_
   const int npg = (t1 + kPage - 1) / kPage - pgA;
   const int nst = (npg + 1) / 2;
   const uint32_t hk_off = (uint32_t)hkv * (uint32_t)Gm::TILE;
+  // the streaming hint when this workgroup alone reads the unit's tiles: a single row
+  // group and no page shared between block tables (row groups of one slice share
+  // each tile through L2)
+  const bool nt_pages = a.stream_pages != 0 && a.G * a.Qmax <= NWR * 32;
   const uint32_t ph_stride = (uint32_t)a.Hkv * (uint32_t)Gm::TILE;
 
   // This wave's copies: chunks wave * CPW .. + CPW - 1 of the stage's 4 * CPT
@@ -421,7 +432,8 @@ __device__ __forceinline__ void wide_range(const AttnArgs& a, char* lds, uint32_
       const uint32_t soff = (uint32_t)ph[k] * ph_stride + hk_off;
       const uint32_t dst = lds0 + (uint32_t)((tile < 2 ? 0 : Gm::VREG) + buf * Gm::PAIR + (tile & 1) * Gm::TILE +
                                              1024 * jj0);
-      wide_copy_tile<Gm::CPTW>(dst, tile < 2 ? krs : vrs, soff, voff);
+      if (nt_pages) wide_copy_tile<Gm::CPTW, true>(dst, tile < 2 ? krs : vrs, soff, voff);
+      else wide_copy_tile<Gm::CPTW, false>(dst, tile < 2 ? krs : vrs, soff, voff);
     }
   };
 

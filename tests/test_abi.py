@@ -22,7 +22,7 @@ def lib():
 def dims(**kw):
     base = dict(num_seqs=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, max_q_len=1,
                 max_blocks_per_seq=256, max_ctx_len=4096, num_blocks=20000, q_dtype=1, kv_dtype=1,
-                path=0, reserved=0)
+                path=0, flags=0)
     base.update(kw)
     return PtaDims(**base)
 
@@ -62,7 +62,8 @@ def test_dims_struct_layout():
     (dict(max_ctx_len=4097), DIMS),               # > page * max_blocks
     (dict(num_blocks=0), DIMS),
     (dict(num_seqs=-1), DIMS),
-    (dict(reserved=1), DIMS),
+    (dict(flags=2), DIMS),                        # only PTA_FLAG_SHARED_PAGES is defined
+    (dict(num_seqs=0, flags=1), OK),
     (dict(path=5), DIMS),                        # past PTA_PATH_TILE16
     (dict(q_dtype=0, kv_dtype=0, path=3), UNSUP),  # the shared-tile family needs bf16 q
     (dict(q_dtype=0, kv_dtype=1), DTYPE),         # fp32 q with bf16 KV

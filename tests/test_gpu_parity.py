@@ -43,36 +43,40 @@ def tol_key(spec):
     return "fp8" if spec.kv_dtype == "fp8" else spec.q_dtype
 
 
-def run_gpu(torch, w, split=None, path="auto", want_lse=True, mode=None, workspace=None):
+def run_gpu(torch, w, split=None, path="auto", want_lse=True, mode=None, workspace=None, shared_pages=None):
     """mode: "whole", "split" (split-K with `split` tokens) or "balanced"; by default
-    "split" when split is given, else "whole"."""
+    "split" when split is given, else "whole".  shared_pages (the cache hint): by default set
+    exactly when the workload's block tables alias a shared prefix."""
     import paged_speculative_verify_amd as psv
     d = to_device(w)
     out = torch.full_like(d.q, float("nan"))
     B, Qmax, Hq, D = w.q.shape
     lse = torch.full((B, Hq, Qmax), float("nan"), dtype=torch.float32, device=d.q.device) if want_lse else None
     mode = mode or ("whole" if split is None else "split")
+    if shared_pages is None:
+        shared_pages = w.spec.shared_prefix_pages > 0 and w.spec.share_group > 1
+    hint = dict(shared_pages=bool(shared_pages))
     if mode == "shared":
         sg = w.spec.share_group
         leader = torch.from_numpy(np.array([(b // sg) * sg for b in range(B)], dtype=np.int32)).to(d.q.device)
         psv.taco_paged_tree_attn_shared_prefix(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
                                                d.tree_mask, leader, sg, split, d.scale, out=out, lse=lse,
                                                k_scale=d.k_scale, v_scale=d.v_scale, max_ctx_len=d.max_ctx_len,
-                                               path=path)
+                                               path=path, **hint)
     elif mode == "balanced":
         psv.taco_paged_tree_attn_balanced(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
                                           d.q_lens, d.tree_mask, d.scale, out=out, lse=lse,
                                           k_scale=d.k_scale, v_scale=d.v_scale, workspace=workspace,
-                                          max_ctx_len=d.max_ctx_len, path=path)
+                                          max_ctx_len=d.max_ctx_len, path=path, **hint)
     elif mode == "whole":
         psv.taco_paged_tree_attn(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens, d.q_lens,
                                  d.tree_mask, d.scale, out=out, lse=lse, k_scale=d.k_scale,
-                                 v_scale=d.v_scale, max_ctx_len=d.max_ctx_len, path=path)
+                                 v_scale=d.v_scale, max_ctx_len=d.max_ctx_len, path=path, **hint)
     else:
         psv.taco_paged_tree_attn_splitk(d.q, d.k_cache, d.v_cache, d.block_tables, d.ctx_lens,
                                         d.q_lens, d.tree_mask, d.scale, split, out=out, lse=lse,
                                         k_scale=d.k_scale, v_scale=d.v_scale,
-                                        max_ctx_len=d.max_ctx_len, path=path)
+                                        max_ctx_len=d.max_ctx_len, path=path, **hint)
     torch.cuda.synchronize()
     return out_to_f64(out), (lse.cpu().numpy().astype(np.float64) if want_lse else None)
 
@@ -473,6 +477,32 @@ def test_balanced_fused_append_unsupported(torch_cuda):
                                                      d.q_lens, d.tree_mask, d.scale, max_ctx_len=d.max_ctx_len,
                                                      path=path)
         assert e.value.status == 4, e.value
+
+
+# The cache hint (PTA_FLAG_SHARED_PAGES) changes how page tiles are loaded, never what is
+# computed: both settings give the same bits, on the streaming kernel (decode, fp8), the wide
+# kernel with one row group (streamed) and two (cached either way), and shared-prefix tables.
+HINT_CASES = [
+    ("decode_stream", spec("h", 6, 32, 8, 128, "bf16", "bf16", (1, 700), 1, "chain", seed=231), "whole"),
+    ("fp8_chain_stream", spec("h", 6, 32, 8, 128, "bf16", "fp8", (8, 900), 8, "chain", seed=232), "whole"),
+    ("wide_one_row_group", spec("h", 3, 64, 8, 128, "bf16", "bf16", (300, 900), 16, "random", seed=233),
+     "balanced"),
+    ("wide_two_row_groups", spec("h", 2, 64, 8, 128, "bf16", "bf16", (500, 900), 32, "random", 8, seed=234),
+     "balanced"),
+    ("shared_prefix_tables", spec("h", 16, 32, 8, 128, "bf16", "bf16", (300, 900), 1, "chain", seed=235,
+                                  share_group=4, shared_prefix_pages=8), "whole"),
+]
+
+
+@pytest.mark.parametrize("cid,sp,mode", HINT_CASES, ids=[c[0] for c in HINT_CASES])
+def test_cache_hint_same_results(torch_cuda, cid, sp, mode):
+    w = make(sp, poison=True)
+    say("cache hint", cid, mode)
+    o1, l1 = run_gpu(torch_cuda, w, mode=mode, shared_pages=False)
+    o2, l2 = run_gpu(torch_cuda, w, mode=mode, shared_pages=True)
+    assert np.array_equal(o1, o2, equal_nan=True) and np.array_equal(l1, l2, equal_nan=True)
+    ref, ref_lse = run_oracle(w)
+    assert_parity(w, o1, l1, ref, ref_lse)
 
 
 def test_validate_flags(torch_cuda):
