@@ -379,8 +379,10 @@ def resolve_cfg(name, args):
         if CONFIGS[name].shared_prefix_pages <= 0 or args.private_pages:
             raise SystemExit("--shared-entry needs a shared-prefix workload on shared pages")
         cfg["mode"], cfg["split"] = "shared", CONFIGS[name].shared_prefix_pages * 16
-    if cfg["mode"] not in ("whole", "balanced") or args.path not in (None, "auto") or args.separate_append:
-        cfg.pop("fuse_append", None)      # the fused appends live in the whole-context and wide grids
+    # the fused appends live in the whole-context stream grid and the wide balanced grid, as each
+    # workload's own launch configuration uses them; any entry or path override runs the append apart
+    if (cfg["mode"] != launch_config(name)["mode"] or args.path not in (None, "auto") or args.separate_append):
+        cfg.pop("fuse_append", None)
     return cfg
 
 

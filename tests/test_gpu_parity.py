@@ -481,25 +481,32 @@ def test_balanced_fused_append_unsupported(torch_cuda):
 
 # The cache hint (PTA_FLAG_SHARED_PAGES) changes how page tiles are loaded, never what is
 # computed: both settings give the same bits, on the streaming kernel (decode, fp8), the wide
-# kernel with one row group (streamed) and two (cached either way), and shared-prefix tables.
+# kernel with one row group (streamed) and two (cached either way), the 16x16x32 tile kernels
+# (whole entry, and the balanced entry on path tile16: the hint leaves them alone), and
+# shared-prefix tables.
 HINT_CASES = [
-    ("decode_stream", spec("h", 6, 32, 8, 128, "bf16", "bf16", (1, 700), 1, "chain", seed=231), "whole"),
-    ("fp8_chain_stream", spec("h", 6, 32, 8, 128, "bf16", "fp8", (8, 900), 8, "chain", seed=232), "whole"),
+    ("decode_stream", spec("h", 6, 32, 8, 128, "bf16", "bf16", (1, 700), 1, "chain", seed=231), "whole", "auto"),
+    ("fp8_chain_stream", spec("h", 6, 32, 8, 128, "bf16", "fp8", (8, 900), 8, "chain", seed=232), "whole",
+     "auto"),
     ("wide_one_row_group", spec("h", 3, 64, 8, 128, "bf16", "bf16", (300, 900), 16, "random", seed=233),
-     "balanced"),
+     "balanced", "auto"),
     ("wide_two_row_groups", spec("h", 2, 64, 8, 128, "bf16", "bf16", (500, 900), 32, "random", 8, seed=234),
-     "balanced"),
+     "balanced", "auto"),
+    ("tile_whole", spec("h", 3, 64, 8, 128, "bf16", "bf16", (300, 900), 16, "random", seed=236), "whole",
+     "auto"),
+    ("tile16_balanced", spec("h", 3, 64, 8, 128, "bf16", "bf16", (300, 900), 16, "random", seed=237),
+     "balanced", "tile16"),
     ("shared_prefix_tables", spec("h", 16, 32, 8, 128, "bf16", "bf16", (300, 900), 1, "chain", seed=235,
-                                  share_group=4, shared_prefix_pages=8), "whole"),
+                                  share_group=4, shared_prefix_pages=8), "whole", "auto"),
 ]
 
 
-@pytest.mark.parametrize("cid,sp,mode", HINT_CASES, ids=[c[0] for c in HINT_CASES])
-def test_cache_hint_same_results(torch_cuda, cid, sp, mode):
+@pytest.mark.parametrize("cid,sp,mode,path", HINT_CASES, ids=[c[0] for c in HINT_CASES])
+def test_cache_hint_same_results(torch_cuda, cid, sp, mode, path):
     w = make(sp, poison=True)
-    say("cache hint", cid, mode)
-    o1, l1 = run_gpu(torch_cuda, w, mode=mode, shared_pages=False)
-    o2, l2 = run_gpu(torch_cuda, w, mode=mode, shared_pages=True)
+    say("cache hint", cid, mode, path)
+    o1, l1 = run_gpu(torch_cuda, w, mode=mode, path=path, shared_pages=False)
+    o2, l2 = run_gpu(torch_cuda, w, mode=mode, path=path, shared_pages=True)
     assert np.array_equal(o1, o2, equal_nan=True) and np.array_equal(l1, l2, equal_nan=True)
     ref, ref_lse = run_oracle(w)
     assert_parity(w, o1, l1, ref, ref_lse)
