@@ -56,9 +56,19 @@ def kernel_source_hash() -> str:
 
 
 def _short(name: str) -> str:
-    """Kernel name without the argument list (rocprofv3 prints demangled names)."""
+    """Kernel name without its trailing argument list (rocprofv3 prints demangled names, which
+    may hold other parentheses, as in "(anonymous namespace)::k(int)")."""
     name = name.strip('"')
-    return name.split("(")[0] if "(" in name else name
+    if name.endswith(")"):
+        depth = 0
+        for i in range(len(name) - 1, -1, -1):
+            if name[i] == ")":
+                depth += 1
+            elif name[i] == "(":
+                depth -= 1
+                if depth == 0:
+                    return name[:i].rstrip()
+    return name
 
 
 def _is_attention(name: str) -> bool:
