@@ -11,6 +11,7 @@ using namespace pta;
 namespace {
 
 constexpr int kMaxQLen = 64;
+constexpr int kPiecePad = 32;        // wide balanced grid: page-line padding per unit
 constexpr int kValuMaxRows = 8;     // largest G * max_q_len of the vector-ALU path
 constexpr int kMfmaMaxRows = 256;   // 8 waves x 32 rows
 constexpr int kStreamMaxRows = 32;  // largest G * max_q_len of the streaming matrix-core path
@@ -293,6 +294,10 @@ pta_status balanced_call(const pta_dims* d, const void* q, const void* k_cache, 
                          tree_mask, scale, out, lse);
   a.k_new = k_new;
   a.v_new = v_new;
+  // the wide grid's slices even out pages plus a fixed cost per unit piece (each piece
+  // refills the copy pipeline and stores its rows, 12-14 us per extra piece measured on the
+  // wide-tree calls; 32 pages of padding measured best of 8, 16, 32 and 48)
+  a.slice_pad = p.fam == FAM_TILE && wide_tiles(d) ? kPiecePad : 0;
   char* ws = reinterpret_cast<char*>(workspace);
   a.counters = nullptr;                  // both balanced grids merge in a second launch
   a.part_o = reinterpret_cast<float*>(ws + L.o_off);

@@ -58,6 +58,9 @@ struct AttnArgs {
   // no page is named by two sequences' block tables: page tiles that one
   // workgroup alone reads take the nontemporal (streaming) load hint
   int32_t stream_pages;
+  // balanced grids: pages of padding in front of every unit on the page line
+  // (the slices then even out pages plus a fixed cost per unit piece); 0 = none
+  int32_t slice_pad;
 };
 
 // ---------------------------------------------------------------- conversions
@@ -282,14 +285,16 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int b, int hkv, in
 // Exclusive prefix of KV pages over the sequences, into ps[0..B] (ps[B] =
 // all pages), by the NT threads of a workgroup: each thread sums a contiguous
 // chunk of sequences, a wave scans its threads with shuffles, and the wave
-// totals (wave_tot, NT / 64 words of LDS) are added in front.
+// totals (wave_tot, NT / 64 words of LDS) are added in front.  Each sequence
+// counts a.slice_pad pages more than it holds (each of its units is that much
+// longer on the page line).
 template <int NT>
 __device__ __forceinline__ void page_prefix(const AttnArgs& a, int* ps, int* wave_tot, int tid) {
   const int B = a.B;
   const int chunk = (B + NT - 1) / NT;
   const int lo = min(B, tid * chunk), hi = min(B, lo + chunk);
   int s = 0;
-  for (int bb = lo; bb < hi; ++bb) s += (a.ctx[bb] + kPage - 1) / kPage;
+  for (int bb = lo; bb < hi; ++bb) s += (a.ctx[bb] + kPage - 1) / kPage + a.slice_pad;
   const int lane = tid & 63, wv = tid >> 6;
   int inc = s;
 #pragma unroll
@@ -305,7 +310,7 @@ __device__ __forceinline__ void page_prefix(const AttnArgs& a, int* ps, int* wav
   if (tid == NT - 1) ps[B] = before + inc;
   for (int bb = lo; bb < hi; ++bb) {
     ps[bb] = base;
-    base += (a.ctx[bb] + kPage - 1) / kPage;
+    base += (a.ctx[bb] + kPage - 1) / kPage + a.slice_pad;
   }
   __syncthreads();
 }

@@ -563,7 +563,7 @@ __global__ __launch_bounds__(256) void slice_merge_kernel(AttnArgs a, int NS) {
 
   int before = 0, total = 0;              // pages of sequences < b, of all sequences
   for (int j = tid; j < a.B; j += 256) {
-    const int p = (a.ctx[j] + kPage - 1) / kPage;
+    const int p = (a.ctx[j] + kPage - 1) / kPage + a.slice_pad;   // the unit's length on the line
     total += p;
     before += j < b ? p : 0;
   }
@@ -580,9 +580,11 @@ __global__ __launch_bounds__(256) void slice_merge_kernel(AttnArgs a, int NS) {
   before = red[0][0] + red[0][1] + red[0][2] + red[0][3];
   total = red[1][0] + red[1][1] + red[1][2] + red[1][3];
   const int Pb = (a.ctx[b] + kPage - 1) / kPage;
+  const int Pl = Pb + a.slice_pad;
   const int64_t W = (int64_t)a.Hkv * total;
   const int64_t N = min((int64_t)NS, max((int64_t)1, W / kMinSlicePages));
-  const int64_t S = (int64_t)a.Hkv * before + (int64_t)hkv * Pb;
+  // the unit's pages sit at line positions S + slice_pad .. S + Pl - 1
+  const int64_t S = (int64_t)a.Hkv * before + (int64_t)hkv * Pl + a.slice_pad;
   auto wg_of = [&](int64_t x) -> int64_t { return ((x + 1) * N - 1) / W; };
   const int64_t wfirst = wg_of(S);
   const int np = (int)(wg_of(S + Pb - 1) - wfirst + 1);

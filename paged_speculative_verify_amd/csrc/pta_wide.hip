@@ -676,11 +676,17 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     const int b = lo;
     const int psb = __builtin_amdgcn_readfirstlane(ps[b]);
-    const int Pb = __builtin_amdgcn_readfirstlane(ps[b + 1]) - psb;
+    const int Pl = __builtin_amdgcn_readfirstlane(ps[b + 1]) - psb;   // unit length on the line
     const int64_t off = x - (int64_t)a.Hkv * psb;
-    const int hkv = (int)(off / Pb);
-    const int k0 = (int)(off % Pb);
-    const int k1 = (int)min((int64_t)Pb, k0 + (xe - x));
+    const int hkv = (int)(off / Pl);
+    const int k0l = (int)(off % Pl);
+    const int k1l = (int)min((int64_t)Pl, k0l + (xe - x));
+    const int prog0 = (int)(x - x0) + max(0, a.slice_pad - k0l);   // slice progress at the first page
+    x += k1l - k0l;
+    // the unit's pages follow slice_pad positions of padding on the line
+    const int Pb = Pl - a.slice_pad;
+    const int k0 = max(0, k0l - a.slice_pad), k1 = max(0, k1l - a.slice_pad);
+    if (k1 <= k0) continue;                  // only padding of this unit in the slice
     const int u = b * a.Hkv + hkv;
     const int C = a.ctx[b];
     const int qb = a.qlen[b];
@@ -695,7 +701,7 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
       WideRows<D> R;
       WideState<D> st;
       wide_range<D, NWR, NBUF>(a, lds, lds0, krs, vrs, R, st, b, hkv, qb, row0, k0 * kPage, min(C, k1 * kPage),
-                               wave, lane, (int)(x - x0), (int)(xe - x0));
+                               wave, lane, prog0, (int)(xe - x0));
       if (k0 == 0 && k1 == Pb) {
         wide_store_final<D>(a, R, st, b, lane);
       } else {
@@ -703,7 +709,6 @@ __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2))) v
         wide_store_partial<D, false>(R, st, a.part_o + r * D, a.part_lse + r, lane);
       }
     }
-    x += k1 - k0;
   }
 }
 
