@@ -194,37 +194,73 @@ def lookahead_cache_bench(args, B=64, prompt=1024, steps=200, window=16, max_mat
     """Host lookahead cache over a decode batch: every step proposes each sequence's candidate
     tree, scores it against the synthetic stream's true continuation (greedy acceptance), feeds
     the hit back into the budgets and appends the accepted tokens plus one.  Timed: the library
-    calls only."""
+    calls only (through the Python binding).  Run once on one thread and once on
+    --la-threads threads; the proposals must agree."""
     import paged_speculative_verify_amd as psv
     from workload.tokens import synthetic_streams
     streams = synthetic_streams(B, prompt + steps * (max_len + 1) + 16, vocab=1000, seed=7)
-    cache = psv.LookaheadCache(window, max_match)
-    seqs = list(range(B))
     seq_arr = np.arange(B, dtype=np.int32)
-    pos = [prompt] * B
-    t_lib = 0.0
-    prompts = np.concatenate([np.asarray(streams[s][:prompt], np.int32) for s in seqs])
-    t0 = time.perf_counter()
-    cache.append_packed(seq_arr, np.full(B, prompt, np.int32), prompts)
-    t_ingest = time.perf_counter() - t0
-    budgets = np.full(B, max_len, np.int32)
-    made = cand = 0
-    for _ in range(steps):
+    prompts = np.concatenate([np.asarray(streams[s][:prompt], np.int32) for s in range(B)])
+
+    def run(threads, plan=None):
+        """The decode loop; with plan (the per-step budgets and appended tokens of an earlier
+        run) the calls are replayed back to back without the acceptance walk in between."""
+        cache = psv.LookaheadCache(window, max_match, threads=threads)
+        pos = [prompt] * B
         t0 = time.perf_counter()
-        tok, par, cnt = cache.propose(seq_arr, budgets, max_len)
-        t_lib += time.perf_counter() - t0
-        acc = [accepted_walk(tok[i], par[i], int(cnt[i]), streams[i][pos[i]:pos[i] + max_len]) for i in seqs]
-        lens = np.array([a + 1 for a in acc], np.int32)          # accepted tokens plus the bonus token
-        packed = np.concatenate([np.asarray(streams[i][pos[i]:pos[i] + acc[i] + 1], np.int32) for i in seqs])
-        acc = np.asarray(acc, np.int32)
-        t0 = time.perf_counter()
-        budgets = cache.update_budgets(seq_arr, cnt, acc, 1, max_len, batch_cap)
-        cache.append_packed(seq_arr, lens, packed)
-        t_lib += time.perf_counter() - t0
-        for i in seqs:
-            pos[i] += acc[i] + 1
-        made += sum(acc) + B
-        cand += int(np.sum(cnt))
+        cache.append_packed(seq_arr, np.full(B, prompt, np.int32), prompts)
+        t_ingest = time.perf_counter() - t0
+        budgets = np.full(B, max_len, np.int32)
+        made = cand = 0
+        t_prop = t_rest = 0.0
+        digest = 0
+        record = []
+        for step in range(steps):
+            if plan is not None:
+                budgets = plan[step][0]
+            t0 = time.perf_counter()
+            tok, par, cnt = cache.propose(seq_arr, budgets, max_len)
+            t_prop += time.perf_counter() - t0
+            if plan is None:
+                digest = hash((digest, tok.tobytes(), par.tobytes()))
+                acc = [accepted_walk(tok[i], par[i], int(cnt[i]), streams[i][pos[i]:pos[i] + max_len])
+                       for i in range(B)]
+                lens = np.array([a + 1 for a in acc], np.int32)      # accepted tokens plus the bonus token
+                packed = np.concatenate([np.asarray(streams[i][pos[i]:pos[i] + acc[i] + 1], np.int32)
+                                         for i in range(B)])
+                acc = np.asarray(acc, np.int32)
+                record.append((budgets, cnt, acc, lens, packed))
+            else:
+                _, cnt, acc, lens, packed = plan[step]
+            t0 = time.perf_counter()
+            budgets = cache.update_budgets(seq_arr, cnt, acc, 1, max_len, batch_cap)
+            cache.append_packed(seq_arr, lens, packed)
+            t_rest += time.perf_counter() - t0
+            if plan is None:
+                for i in range(B):
+                    pos[i] += acc[i] + 1
+                made += int(acc.sum()) + B
+                cand += int(np.sum(cnt))
+            else:
+                digest = hash((digest, tok.tobytes(), par.tobytes()))
+        t_lib = t_prop + t_rest
+        return {"rate": B * steps / t_lib, "ms_step": 1e3 * t_lib / steps, "ms_propose": 1e3 * t_prop / steps,
+                "ms_budgets_append": 1e3 * t_rest / steps, "ingest": B * prompt / t_ingest,
+                "made": made, "cand": cand, "digest": digest, "record": record}
+
+    def summary(r):
+        return {"value": round(r["rate"], 1), "ms_per_batch_step": round(r["ms_step"], 4),
+                "ms_propose": round(r["ms_propose"], 4), "ms_budgets_append": round(r["ms_budgets_append"], 4),
+                "prompt_ingest_tokens_per_s": round(r["ingest"], 1)}
+
+    loop1 = run(1)
+    plan = loop1["record"]
+    loopn = run(args.la_threads)
+    back1 = run(1, plan)
+    backn = run(args.la_threads, plan)
+    if not (loop1["digest"] == loopn["digest"] and back1["digest"] == backn["digest"]):
+        print("lookahead cache: proposals differ between 1 and %d threads" % args.la_threads, file=sys.stderr)
+        return 1
     # the oracle on a bounded sample: 2 sequences, 10 steps
     import oracle
     o = oracle.LookaheadOracle(window, max_match)
@@ -235,20 +271,24 @@ def lookahead_cache_bench(args, B=64, prompt=1024, steps=200, window=16, max_mat
         for s in range(2):
             o.propose(s, max_len)
     t_or = time.perf_counter() - t0
-    rate = B * steps / t_lib
     print(json.dumps({
-        "metric": "lookahead cache: candidate trees proposed per second (host, one thread)",
-        "value": round(rate, 1), "unit": "trees/s", "higher_is_better": True, "data": "synthetic",
+        "metric": "lookahead cache: candidate trees proposed per second (host)",
+        "value": round(backn["rate"], 1), "unit": "trees/s", "higher_is_better": True, "data": "synthetic",
+        "threads": args.la_threads,
         "config": {"workload": "lookahead_cache_decode_batch", "batch": B, "prompt_tokens": prompt,
                    "steps": steps, "window": window, "max_match": max_match, "max_len": max_len,
                    "batch_cap": batch_cap},
-        "ms_per_batch_step": round(1e3 * t_lib / steps, 4),
-        "prompt_ingest_tokens_per_s": round(B * prompt / t_ingest, 1),
-        "tokens_per_step_mean": round(made / (B * steps), 3),
-        "candidates_per_step_mean": round(cand / (B * steps), 3),
+        "back_to_back": summary(backn), "back_to_back_one_thread": summary(back1),
+        "in_loop": summary(loopn), "in_loop_one_thread": summary(loop1),
+        "tokens_per_step_mean": round(loop1["made"] / (B * steps), 3),
+        "candidates_per_step_mean": round(loop1["cand"] / (B * steps), 3),
         "cpu_baseline": {"value": round(20 / t_or, 2), "unit": "trees/s", "cores": 1, "kind": "oracle",
                          "sample": f"2 sequences, {prompt}-token prompts, 10 proposals each, in {t_or:.1f} s"},
-        "note": "tokens_per_step depends on the synthetic streams' repetition, not on real text"}))
+        "note": "value: the calls of the decode loop (propose, budgets, append) replayed back to back "
+                "on the cache's threads; in_loop: the same calls with the Python acceptance walk "
+                "(about a millisecond) between them, long enough for idle workers to sleep. Times "
+                "include the Python binding's argument handling. tokens_per_step depends on the "
+                "synthetic streams' repetition, not on real text"}))
     return 0
 
 
@@ -728,6 +768,8 @@ def main(argv=None) -> int:
     ap.add_argument("--lookahead-cache", action="store_true",
                     help="instead of the bench line: the host lookahead cache (propose, budgets, append) "
                          "over a decode batch of synthetic token streams, one JSON line; needs no GPU")
+    ap.add_argument("--la-threads", type=int, default=8,
+                    help="with --lookahead-cache: threads of the cache's batch calls (also timed on one)")
     ap.add_argument("--gemm", choices=sorted(GEMM_SHAPES), default=None,
                     help="instead of the bench line: one quantized GEMM (W8A8 or W4A16) on a Llama-70B-shaped projection")
     ap.add_argument("--qlen-floor", action="store_true",

@@ -29,8 +29,9 @@
  * Everything is integer arithmetic: results are exact and repeatable.
  *
  * Host memory only (plain host pointers); one cache must not be used from two
- * threads at once.  Errors are pta_status codes (pta.h); nothing is changed
- * when a call fails its argument checks. */
+ * threads at once (its calls may run on the cache's own worker threads, see
+ * taco_la_set_threads).  Errors are pta_status codes (pta.h); nothing is
+ * changed when a call fails its argument checks. */
 #ifndef PTA_LOOKAHEAD_H
 #define PTA_LOOKAHEAD_H
 
@@ -49,6 +50,20 @@ typedef struct taco_la_cache taco_la_cache;
  * or out of memory.  Free with taco_la_destroy. */
 taco_la_cache* taco_la_create(int32_t window, int32_t max_match);
 void taco_la_destroy(taco_la_cache* cache);
+
+/* Run the cache's batch calls (taco_la_append_batch, taco_la_append,
+ * taco_la_propose) on n threads: the calling thread and n - 1 workers owned by
+ * the cache (1 .. 64; a new cache has 1, no workers).  An append batch splits
+ * into one task per sequence (its local counts) and one per shard of the
+ * global counts (strings grouped by their first token); a query batch into one
+ * task per sequence.  Results do not depend on n.  Idle workers spin for about
+ * a millisecond before they sleep (a call after a longer pause first wakes
+ * them).  PTA_ERR_BAD_DIMS for n outside 1 .. 64; PTA_ERR_UNSUPPORTED when the
+ * system refuses a thread (the cache is then left with 1). */
+pta_status taco_la_set_threads(taco_la_cache* cache, int32_t n);
+
+/* The cache's thread count (0 for a NULL cache). */
+int32_t taco_la_threads(const taco_la_cache* cache);
 
 /* Append n >= 0 tokens (ids >= 0) to the history of sequence seq (>= 0; a
  * sequence not seen before starts empty), counting the new strings in its

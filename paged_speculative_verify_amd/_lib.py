@@ -117,6 +117,10 @@ def load() -> ctypes.CDLL:
     lib.taco_la_create.restype = P
     lib.taco_la_destroy.argtypes = [P]
     lib.taco_la_destroy.restype = None
+    lib.taco_la_set_threads.argtypes = [P, I32]
+    lib.taco_la_set_threads.restype = ctypes.c_int
+    lib.taco_la_threads.argtypes = [P]
+    lib.taco_la_threads.restype = I32
     lib.taco_la_append.argtypes = [P, I32, P, I32]
     lib.taco_la_append.restype = ctypes.c_int
     lib.taco_la_append_batch.argtypes = [P, I32, P, P, P]
@@ -771,12 +775,22 @@ def _np_ptr(a):
 class LookaheadCache:
     """The lookahead cache of include/pta_lookahead.h (host memory, numpy int32 arrays)."""
 
-    def __init__(self, window: int = 16, max_match: int = 8):
+    def __init__(self, window: int = 16, max_match: int = 8, threads: int = 1):
         self._lib = load()
         self._h = self._lib.taco_la_create(int(window), int(max_match))
         if not self._h:
             raise PtaError(2, "taco_la_create: window 2..64 and max_match 1..window-1")
         self.window, self.max_match = int(window), int(max_match)
+        if threads != 1:
+            self.set_threads(threads)
+
+    def set_threads(self, n: int) -> None:
+        """Batch calls run on n threads (the caller and n - 1 workers of the cache)."""
+        _check(self._lib.taco_la_set_threads(self._h, int(n)))
+
+    @property
+    def threads(self) -> int:
+        return int(self._lib.taco_la_threads(self._h))
 
     def close(self):
         if self._h:

@@ -309,3 +309,114 @@ def test_library_matches_budget_and_release_goldens():
     c.append(1, [1, 2])
     tok, par, cnt = c.propose([1], [2], 4)
     assert list(tok[0, :cnt[0]]) == g["reused_query_tokens"] and list(par[0, :cnt[0]]) == g["reused_query_parents"]
+
+
+# ---------------------------------------------------------------- worker threads
+def replay(threads, streams, window, mm, plan, budget, max_q):
+    """Run an append/propose plan on a cache with the given thread count; every proposal."""
+    c = psv.LookaheadCache(window, mm, threads=threads)
+    assert c.threads == threads
+    out = []
+    for kind, arg in plan:
+        if kind == "append":
+            c.append_batch([s for s, _ in arg], [ch for _, ch in arg])
+        elif kind == "release":
+            c.release(arg)
+        else:
+            tok, par, cnt = c.propose(arg, [budget] * len(arg), max_q)
+            out.append((tok.copy(), par.copy(), cnt.copy()))
+    return out
+
+
+def make_plan(streams, seed, steps, long_every=0):
+    rng = np.random.default_rng(seed)
+    n = len(streams)
+    pos = [0] * n
+    plan = []
+    for step in range(steps):
+        batch = []
+        for s in rng.permutation(n):
+            k = int(rng.integers(0, 9))
+            if long_every and step % long_every == long_every - 1 and s % 2 == 0:
+                k = int(rng.integers(40, 140))           # a chunk longer than the ring
+            batch.append((int(s), streams[s][pos[s]:pos[s] + k]))
+            pos[s] += k
+        if step % 5 == 2:                                 # one sequence named twice in a batch
+            s = int(rng.integers(0, n))
+            batch.append((s, streams[s][pos[s]:pos[s] + 3]))
+            pos[s] += 3
+        plan.append(("append", batch))
+        if step == steps // 2:
+            plan.append(("release", 1))
+        plan.append(("propose", list(range(n)) + [n + 5]))
+    return plan
+
+
+@pytest.mark.parametrize("window,mm", [(16, 8), (6, 3), (64, 63)])
+def test_thread_count_does_not_change_results(window, mm):
+    """The same appends and queries on 1, 3 and 8 threads give identical proposals: the global
+    counts split by first token and the local ones by sequence count the same strings."""
+    streams = synthetic_streams(12, 1200, vocab=60, seed=51)
+    plan = make_plan(streams, 52, 40, long_every=7)
+    ref = replay(1, streams, window, mm, plan, 10, 12)
+    for t in (3, 8):
+        got = replay(t, streams, window, mm, plan, 10, 12)
+        for (a, b, c), (x, y, z) in zip(ref, got):
+            assert np.array_equal(a, x) and np.array_equal(b, y) and np.array_equal(c, z)
+
+
+@pytest.mark.parametrize("threads", [1, 4])
+@pytest.mark.parametrize("chunk", [1, 40, 57, 70, 75, 130])
+def test_long_chunks_match_oracle(threads, chunk):
+    """Appends to an existing history in chunks around the ring length (64 tracked starts):
+    a chunk of 50 .. 78 tokens makes a start read before the append share its ring slot with a
+    start written by it."""
+    window, mm = 16, 8
+    streams = synthetic_streams(3, 700, vocab=25, seed=61 + chunk)
+    c = psv.LookaheadCache(window, mm, threads=threads)
+    o = LookaheadOracle(window, mm)
+    pos = [0, 0, 0]
+    for _ in range(4):
+        batch = []
+        for s in range(3):
+            ch = streams[s][pos[s]:pos[s] + chunk + 3 * s]
+            pos[s] += len(ch)
+            batch.append(ch)
+            o.append(s, ch)
+        c.append_batch([0, 1, 2], batch)
+        tok, par, cnt = c.propose([0, 1, 2], [9, 9, 9], 9)
+        for s in range(3):
+            et, ep = o.propose(s, 9)
+            assert list(tok[s, :cnt[s]]) == et and list(par[s, :cnt[s]]) == ep
+
+
+def test_set_threads_checks():
+    lib = psv.load()
+    c = psv.LookaheadCache(8, 4)
+    assert c.threads == 1
+    for bad in (0, -1, 65):
+        with pytest.raises(psv.PtaError):
+            c.set_threads(bad)
+    assert c.threads == 1
+    c.set_threads(5)
+    assert c.threads == 5
+    c.append(0, [1, 2, 3, 1, 2])
+    c.set_threads(2)                                   # resized with history in place
+    assert c.threads == 2 and list(c.propose([0], [2], 4)[0][0, :1]) == [3]
+    c.set_threads(1)
+    assert c.threads == 1
+    assert lib.taco_la_set_threads(None, 2) == 1      # PTA_ERR_NULL_PTR
+    assert lib.taco_la_threads(None) == 0
+
+
+def test_bench_lookahead_line(capsys):
+    """bench.py's lookahead-cache line on a small batch: it checks that 1 and 3 threads propose
+    the same trees, and reports the back-to-back and in-loop rates."""
+    import argparse
+    import json
+    import bench
+    assert bench.lookahead_cache_bench(argparse.Namespace(la_threads=3), B=6, prompt=64, steps=10) == 0
+    line = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    assert line["threads"] == 3 and line["value"] > 0 and line["unit"] == "trees/s"
+    for k in ("back_to_back", "back_to_back_one_thread", "in_loop", "in_loop_one_thread"):
+        assert line[k]["value"] > 0
