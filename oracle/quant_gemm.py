@@ -19,6 +19,9 @@ scale granularity; these readings are taken:
     k = 2 j + 1 in the high nibble), one float32 scale per (row n, group of G
     consecutive k):
         Y[m, n] = sum_k A[m, k] * q[n, k] * w_scale[n, k // G].
+  * W8A16: A bf16; W fp8 e4m3fn codes (the W8A8 weight format, which carries
+    its own exponent), one float32 scale per weight row:
+        Y[m, n] = w_scale[n] * sum_k A[m, k] * dec(W[n, k]).
 
 Nothing here is shared with the library.
 """
@@ -57,3 +60,10 @@ def w4a16_gemm(a_bits, w_packed, w_scale, group: int) -> np.ndarray:
     s = np.repeat(np.asarray(w_scale, np.float64), group, axis=1)
     assert s.shape == q.shape
     return a @ (q * s).T
+
+
+def w8a16_gemm(a_bits, w_codes, w_scale) -> np.ndarray:
+    """bf16 activations x fp8 e4m3fn weights with one scale per output channel, fp64 [M, N]."""
+    a = decode_bf16(a_bits)
+    w = decode_fp8_e4m3fn(w_codes) * np.asarray(w_scale, np.float64)[:, None]
+    return a @ w.T

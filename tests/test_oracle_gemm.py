@@ -64,6 +64,10 @@ def pin_worked_example(mod=qg):
     wc = np.array(g["w8a8_w_codes"], np.uint8).reshape(1, 2)
     y = mod.w8a8_gemm(ac, np.array(g["w8a8_a_scale"], np.float32), wc, np.array(g["w8a8_w_scale"], np.float32))
     assert list(y[:, 0]) == g["w8a8_y"]
+    a = bf16_bits(np.array([g["w8a16_a"]]))
+    wc = np.array(g["w8a16_w_codes"], np.uint8).reshape(2, 2)
+    y = mod.w8a16_gemm(a, wc, np.array(g["w8a16_w_scale"], np.float32))
+    assert list(y[0]) == g["w8a16_y"]
 
 
 def pin_integers(mod=qg, seed=0):
@@ -85,6 +89,9 @@ def pin_integers(mod=qg, seed=0):
         ks = slice(g * G, (g + 1) * G)
         ref += (ai[:, ks] @ qi[:, ks].T).astype(np.float64) * gs[None, :, g]
     y = mod.w4a16_gemm(bf16_bits(ai.astype(np.float32)), pack_int4(qi), gs.astype(np.float32), G)
+    assert np.array_equal(y, ref)
+    ref = (ai @ wi.T).astype(np.float64) * sw[None, :]
+    y = mod.w8a16_gemm(bf16_bits(ai.astype(np.float32)), fp8_codes_of(wi), sw.astype(np.float32))
     assert np.array_equal(y, ref)
 
 
@@ -111,6 +118,10 @@ def pin_brute_force(mod=qg, seed=1):
     for m, n in itertools.product(range(M), range(N)):
         ref = sum(av[m, k] * qi[n, k] * float(gs[n, k // G]) for k in range(K))
         assert abs(y[m, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+    y = mod.w8a16_gemm(ab, wc, sw)
+    for m, n in itertools.product(range(M), range(N)):
+        ref = sum(av[m, k] * float(tab[wc[n, k]]) for k in range(K)) * float(sw[n])
+        assert abs(y[m, n] - ref) <= 1e-12 * max(1.0, abs(ref))
 
 
 def pin_closed_forms(mod=qg, seed=2):
@@ -129,6 +140,13 @@ def pin_closed_forms(mod=qg, seed=2):
     y1 = mod.w4a16_gemm(ab, pack_int4(qi), np.full((N, 4), 0.375, np.float32), 8)
     y2 = mod.w4a16_gemm(ab, pack_int4(qi), np.ones((N, 4), np.float32), 8)
     assert np.allclose(y1, 0.375 * y2, rtol=1e-14, atol=0)
+    # W8A16 with A = identity (bf16 1.0) gives each channel's decoded weights times its scale
+    y = mod.w8a16_gemm(bf16_bits(np.eye(K, dtype=np.float32)), wc, sw)
+    assert np.array_equal(y, (decode_fp8_e4m3fn(wc) * sw.astype(np.float64)[:, None]).T)
+    # and fp8-representable activations with unit activation scales agree with W8A8
+    ai = rng.integers(-6, 7, (3, K)) * 0.25
+    y = mod.w8a16_gemm(bf16_bits(ai.astype(np.float32)), wc, sw)
+    assert np.array_equal(y, mod.w8a8_gemm(fp8_codes_of(ai), np.ones(3, np.float32), wc, sw))
 
 
 PINS = [pin_worked_example, pin_integers, pin_brute_force, pin_closed_forms]
@@ -143,7 +161,8 @@ def test_pins(pin):
 class _Mutant:
     """The oracle module with one function replaced."""
     def __init__(self, **over):
-        self.__dict__.update({k: getattr(qg, k) for k in ("decode_int4_packed", "w8a8_gemm", "w4a16_gemm")})
+        self.__dict__.update({k: getattr(qg, k) for k in ("decode_int4_packed", "w8a8_gemm", "w4a16_gemm",
+                                                          "w8a16_gemm")})
         self.__dict__.update(over)
 
 
@@ -182,13 +201,28 @@ def _w4a16_group_by_rows(a_bits, w_packed, w_scale, group):
     return qg.w4a16_gemm(a_bits, w_packed, np.resize(s.T.copy(), s.shape), group)
 
 
+def _w8a16_scale_by_k(a_bits, w_codes, w_scale):
+    """The channel scales applied along k instead of along the output channels."""
+    a = qg.decode_bf16(a_bits)
+    w = decode_fp8_e4m3fn(w_codes)
+    return a @ (w * np.resize(np.asarray(w_scale, np.float64), w.shape[1])[None, :]).T
+
+
+def _w8a16_weights_as_bf16_bits(a_bits, w_codes, w_scale):
+    """Weight codes read as the high byte of a bf16 value instead of as e4m3fn."""
+    w_bits = (np.asarray(w_codes, np.uint16) << 8).astype(np.uint16)
+    return qg.decode_bf16(a_bits) @ (qg.decode_bf16(w_bits) * np.asarray(w_scale, np.float64)[:, None]).T
+
+
 @pytest.mark.parametrize("mutant", [
+    _Mutant(w8a16_gemm=_w8a16_scale_by_k),
+    _Mutant(w8a16_gemm=_w8a16_weights_as_bf16_bits),
     _Mutant(decode_int4_packed=_nibbles_swapped),
     _Mutant(decode_int4_packed=_unsigned_nibbles),
     _Mutant(w8a8_gemm=_w8a8_scale_axis_swapped),
     _Mutant(w4a16_gemm=_w4a16_first_group_scale),
     _Mutant(w4a16_gemm=_w4a16_group_by_rows),
-], ids=["nibbles_swapped", "unsigned_nibbles", "w8a8_scale_axes", "w4a16_one_group_scale", "w4a16_groups_by_rows"])
+], ids=["w8a16_scale_along_k", "w8a16_codes_as_bf16", "nibbles_swapped", "unsigned_nibbles", "w8a8_scale_axes", "w4a16_one_group_scale", "w4a16_groups_by_rows"])
 def test_planted_mistakes_fail_a_pin(mutant):
     # the W4A16 mutants call the real decoder; make them use the mutant's too where it differs
     failed = 0
