@@ -604,12 +604,31 @@ W4_GROUP = 128
 GEMM_SHAPES = {
     # Llama-3.1-70B MLP gate + up projections (N = 2 x 28672, K = 8192) over the verify step's
     # 512 candidate tokens (32 sequences x 16), and over a 64-sequence decode step; W8A8 (fp8
-    # activations and weights) and W4A16 (bf16 activations, int4 weights in groups of 128)
+    # activations and weights), W4A16 (bf16 activations, int4 weights in groups of 128) and W8A16
+    # (bf16 activations, fp8 weights with per-channel scales)
     "llama70b_gate_up_verify512": ("w8a8", 512, 57344, 8192),
     "llama70b_gate_up_decode64": ("w8a8", 64, 57344, 8192),
     "w4a16_llama70b_gate_up_verify512": ("w4a16", 512, 57344, 8192),
     "w4a16_llama70b_gate_up_decode64": ("w4a16", 64, 57344, 8192),
+    "w8a16_llama70b_gate_up_verify512": ("w8a16", 512, 57344, 8192),
+    "w8a16_llama70b_gate_up_decode64": ("w8a16", 64, 57344, 8192),
 }
+
+
+def w8a16_oracle_rows(oracle, a_bits, w_codes, w_scale, with_bound=True):
+    """(fp64 reference, bound 2^-8 |ref| + 2^-14 w_scale sum|a||w|) of a few rows, column chunk by
+    column chunk."""
+    from oracle.formats import decode_bf16, decode_fp8_e4m3fn
+    ref = np.empty((a_bits.shape[0], w_codes.shape[0]))
+    S = np.empty_like(ref)
+    A = np.abs(decode_bf16(a_bits))
+    for c0 in range(0, w_codes.shape[0], 4096):
+        c1 = min(c0 + 4096, w_codes.shape[0])
+        ref[:, c0:c1] = oracle.w8a16_gemm(a_bits, w_codes[c0:c1], w_scale[c0:c1])
+        if with_bound:
+            S[:, c0:c1] = A @ (np.abs(decode_fp8_e4m3fn(w_codes[c0:c1])) *
+                               w_scale[c0:c1].astype(np.float64)[:, None]).T
+    return ref, 2.0 ** -8 * np.abs(ref) + 2.0 ** -14 * S
 
 
 def w4a16_oracle_rows(oracle, a_bits, w_packed, w_scale, group, with_bound=True):
@@ -635,7 +654,7 @@ def gemm_bench(psv, torch, name, steps=30, warmup=5, cpu_rows=2, parity_rows=(0,
     (whichever the shape's intensity says bounds it), parity of sampled output rows against the
     fp64 oracle, the oracle timed on a few rows."""
     import oracle
-    from workload.gemm import make_w4a16_device, make_w8a8_device
+    from workload.gemm import make_w4a16_device, make_w8a8_device, make_w8a16_device
     op, M, N, K = GEMM_SHAPES[name]
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     if op == "w8a8":
@@ -645,6 +664,11 @@ def gemm_bench(psv, torch, name, steps=30, warmup=5, cpu_rows=2, parity_rows=(0,
         peak = FP8_PEAK_TFLOPS
         kernel = "gemm_w8a8_k128_kernel" if M > 256 and K % 128 == 0 else "gemm_w8a8_kernel"
         nbytes = M * K + N * K + 2 * M * N + 4 * (M + N)
+    elif op == "w8a16":
+        a, w, sw = make_w8a16_device(M, N, K, seed=11, torch=torch)
+        call = lambda: psv.taco_gemm_w8a16(a, w, sw, y)
+        peak, kernel = BF16_PEAK_TFLOPS, "gemm_w8a16_kernel"
+        nbytes = 2 * M * K + N * K + 4 * N + 2 * M * N
     else:
         G = W4_GROUP
         a, w, sw = make_w4a16_device(M, N, K, G, seed=11, torch=torch)
@@ -697,6 +721,18 @@ def gemm_bench(psv, torch, name, steps=30, warmup=5, cpu_rows=2, parity_rows=(0,
         dtype = "fp8-e4m3 x fp8-e4m3 -> f32 -> bf16"
         metric = "W8A8 GEMM TFLOP/s (fp8 e4m3fn operands, per-row scales, bf16 out), 1 GPU"
         bound_text = "2^-8 |y_ref| + 2^-14 a_scale w_scale sum|a||w| per output"
+        config = {"workload": name, "M": M, "N": N, "K": K}
+    elif op == "w8a16":
+        a_bits = a[sel].view(torch.int16).cpu().numpy().view(np.uint16)
+        wc, wsc = w.cpu().numpy(), sw.cpu().numpy()
+        ref, bnd = w8a16_oracle_rows(oracle, a_bits, wc, wsc)
+        with threadpool_limits(limits=cores, user_api="blas"):
+            t0 = time.perf_counter()
+            w8a16_oracle_rows(oracle, a_bits[:cpu_rows], wc, wsc, with_bound=False)
+            t_cpu = time.perf_counter() - t0
+        dtype = "bf16 x fp8-e4m3 (exact to bf16) -> f32, channel scale in f32 -> bf16"
+        metric = "W8A16 GEMM TFLOP/s (bf16 activations, fp8 e4m3fn weights, per-channel scales, bf16 out), 1 GPU"
+        bound_text = "2^-8 |y_ref| + 2^-14 w_scale sum_k |a||w| per output"
         config = {"workload": name, "M": M, "N": N, "K": K}
     else:
         a_bits = a[sel].view(torch.int16).cpu().numpy().view(np.uint16)
@@ -771,7 +807,7 @@ def main(argv=None) -> int:
     ap.add_argument("--la-threads", type=int, default=8,
                     help="with --lookahead-cache: threads of the cache's batch calls (also timed on one)")
     ap.add_argument("--gemm", choices=sorted(GEMM_SHAPES), default=None,
-                    help="instead of the bench line: one quantized GEMM (W8A8 or W4A16) on a Llama-70B-shaped projection")
+                    help="instead of the bench line: one quantized GEMM (W8A8, W4A16 or W8A16) on a Llama-70B-shaped projection")
     ap.add_argument("--qlen-floor", action="store_true",
                     help="instead of the bench line: attention time against the number of candidates "
                          "per sequence at the decode shape, T(q_len) / T(1)")

@@ -17,6 +17,8 @@
  *   W4A16:  Y[m][n] = sum_k A[m][k] * q[n][k] * w_scale[n][k / group],
  *           A bf16, q signed 4-bit integers (-8..7), scales float32 per
  *           (output channel, group of `group` consecutive k).
+ *   W8A16:  Y[m][n] = w_scale[n] * sum_k A[m][k] * W[n][k],
+ *           A bf16, W fp8 e4m3fn codes, one float32 scale per output channel.
  * Y is bf16 [M][N] row-major, rounded to nearest even from float32.
  *
  * Conventions as in pta.h: device pointers, caller-owned buffers, work
@@ -89,6 +91,22 @@ size_t taco_gemm_w4a16_tiled_bytes(int32_t N, int32_t K);
 pta_status taco_gemm_w4a16_pack(const void* w, void* w_tiled, int32_t N, int32_t K, void* stream);
 pta_status taco_gemm_w4a16_tiled(const void* a, const void* w_tiled, const float* w_scale, void* y, int32_t M,
                                  int32_t N, int32_t K, int32_t group, void* stream);
+
+/* bf16 x fp8 GEMM on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16): the
+ * W8A16 operator the 17173xz.com article lists ("TACO-LLM如何实现降本增效?").
+ * Every weight code is decoded exactly to bf16, the products are summed in
+ * float32, and the channel scale multiplies the float32 sum.
+ *   a        bf16  [M][K]  row-major, 16-byte aligned
+ *   w        uint8 [N][K]  e4m3fn codes, row-major, 16-byte aligned
+ *   w_scale  float [N], 4-byte aligned
+ *   y        bf16  [M][N]  row-major (written; every element)
+ * M >= 1, N >= 1, K a positive multiple of 64; M rounded up to a multiple of
+ * 128 (64 when M <= 64) times 2 K, and N rounded up to a multiple of 128 times
+ * K, below 2^32 (else PTA_ERR_BAD_DIMS); misaligned pointers PTA_ERR_BAD_DIMS;
+ * NULL pointers PTA_ERR_NULL_PTR; a failed launch PTA_ERR_HIP.  NaN codes and
+ * activations propagate to the affected outputs. */
+pta_status taco_gemm_w8a16(const void* a, const void* w, const float* w_scale, void* y, int32_t M, int32_t N,
+                           int32_t K, void* stream);
 
 #ifdef __cplusplus
 }

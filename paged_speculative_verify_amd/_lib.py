@@ -107,6 +107,8 @@ def load() -> ctypes.CDLL:
     lib.taco_gemm_w8a8.restype = ctypes.c_int
     lib.taco_gemm_w4a16.argtypes = [P, P, P, P, I32, I32, I32, I32, P]
     lib.taco_gemm_w4a16.restype = ctypes.c_int
+    lib.taco_gemm_w8a16.argtypes = [P, P, P, P, I32, I32, I32, P]
+    lib.taco_gemm_w8a16.restype = ctypes.c_int
     lib.taco_gemm_w4a16_tiled_bytes.argtypes = [I32, I32]
     lib.taco_gemm_w4a16_tiled_bytes.restype = SZ
     lib.taco_gemm_w4a16_pack.argtypes = [P, P, I32, I32, P]
@@ -592,6 +594,32 @@ def taco_gemm_w8a8(a, a_scale, w, w_scale, y=None, stream=None):
         raise ValueError("y must be [M, N]")
     _check(load().taco_gemm_w8a8(a.data_ptr(), a_scale.data_ptr(), w.data_ptr(), w_scale.data_ptr(), y.data_ptr(),
                                  M, N, K, _stream(stream)))
+    return y
+
+
+def taco_gemm_w8a16(a, w, w_scale, y=None, stream=None):
+    """W8A16 GEMM (include/pta_gemm.h): a bf16 [M, K], w uint8 [N, K] e4m3fn codes (or a
+    float8_e4m3fn tensor), w_scale float32 [N]; returns y bf16 [M, N] =
+    w_scale[n] * sum_k a[m, k] dec(w[n, k])."""
+    torch = _torch()
+    _need(a, "a", 2, torch.bfloat16)
+    M, K = a.shape
+    _need(w, "w", 2, device=a.device)
+    if w.element_size() != 1:
+        raise ValueError("w must hold 1-byte fp8 codes")
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("a and w disagree on K")
+    _need(w_scale, "w_scale", 1, torch.float32, a.device)
+    if w_scale.numel() != N:
+        raise ValueError("one scale per row of w")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _need(y, "y", 2, torch.bfloat16, a.device)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y must be [M, N]")
+    _check(load().taco_gemm_w8a16(a.data_ptr(), w.data_ptr(), w_scale.data_ptr(), y.data_ptr(), M, N, K,
+                                  _stream(stream)))
     return y
 
 

@@ -3,7 +3,7 @@
 // (17173xz.com article, section "TACO-LLM如何实现降本增效?"; 618zxw.cn article,
 // section "LLM量子化技術による推論コストの削減"; design talk section
 // "5. 支持 Quantization（模型量化）": low-bit weights on low-precision matrix
-// instructions).  W8A8 first, W4A16 below.
+// instructions).  W8A8 first, W4A16 and W8A16 below.
 //
 // W8A8:
 //   * Waves of 64 x 32 WNB (2 x WNB blocks of v_mfma_scale_f32_32x32x64_f8f6f4
@@ -554,6 +554,143 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
   }
 }
 
+
+// ------------------------------------------------------------------ W8A16
+// bf16 activations x fp8 e4m3fn weights with one scale per output channel, on
+// the bf16 matrix cores (v_mfma_f32_32x32x16_bf16, float32 accumulation):
+//   * Tiles, waves, k assignment, staging and tile order as the W4A16 kernel:
+//     32 WM x 128 workgroup tiles, 64 k per stage, each wave 32 columns and all
+//     32 WM rows; lane half h of k-step ks covers k-octet 4 h + ks, so a lane's
+//     weights for a stage are the 32 bytes at k-bytes 32 h .. 32 h + 31 of its
+//     column (two 16-byte LDS reads).
+//   * Weights are decoded exactly (every finite e4m3fn value is a bf16 value;
+//     v_cvt_scalef32_pk_bf16_fp8 with unit scale), so the only roundings are
+//     the float32 sums and the final bf16; the channel scale multiplies the
+//     float32 sum in the epilogue.
+//   * A weight row of a stage is 64 bytes (four 16-byte units); unit u of row r
+//     sits at u ^ ((r >> 2) & 3), so the 16 rows of one read pass touch 16
+//     distinct bank groups.  Activation rows are swizzled as in W4A16.
+template <int WM>
+struct W8Geom {
+  static constexpr int BM = 32 * WM, BN = 128, BK = 64;
+  static constexpr int NBUF = WM == 4 ? 3 : 4;
+  static constexpr int A_TILE = BM * BK * 2;               // bf16
+  static constexpr int W_TILE = BN * BK;                   // fp8 codes (8 KiB)
+  static constexpr int W_REG = NBUF * A_TILE;
+  static constexpr int CHUNKS_A = A_TILE / 1024, CHUNKS_W = W_TILE / 1024;
+  static constexpr int LOADS = (CHUNKS_A + CHUNKS_W) / 4;  // copies per wave per stage
+  static constexpr int LDS_BYTES = W_REG + NBUF * W_TILE;
+  static_assert((CHUNKS_A + CHUNKS_W) % 4 == 0, "whole copies per wave");
+  static_assert(LDS_BYTES <= 81920, "two workgroups per compute unit");
+};
+
+// Eight e4m3fn codes (bytes of lo, then hi) as eight bf16, element i = byte i.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(bf16x8, make_uint4(fp8x2_to_bf16x2<false>(lo), fp8x2_to_bf16x2<true>(lo),
+                                               fp8x2_to_bf16x2<false>(hi), fp8x2_to_bf16x2<true>(hi)));
+}
+
+template <int WM>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w8a16_kernel(
+    const uint16_t* a, const uint8_t* w, const float* w_scale, uint16_t* y, int M, int N, int K, int tm, int tn) {
+  using Gm = W8Geom<WM>;
+  constexpr int BM = Gm::BM, BN = Gm::BN, NBUF = Gm::NBUF;
+  __shared__ __attribute__((aligned(1024))) char lds[Gm::LDS_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int nt = (slot / tm) * 8 + xcd, mt = slot % tm;
+  if (nt >= tn) return;
+  const int m0 = mt * BM, n0 = nt * BN;
+
+  const i32x4 ars = gemm_rsrc(a, (uint32_t)((uint64_t)M * (uint64_t)K * 2u));
+  const i32x4 wrs = gemm_rsrc(w, (uint32_t)((uint64_t)N * (uint64_t)K));
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&lds[0];
+
+  // copy lanes.  Activation chunk c (8 rows of 128 bytes) as in W4A16.  Weight
+  // chunk c (16 rows of 64 bytes): lane l fills row 16 c + l / 4, physical unit
+  // l % 4, holding logical unit (l % 4) ^ ((row >> 2) & 3) = (l % 4) ^ ((l / 16) & 3).
+  uint32_t voffA[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    voffA[par] = (uint32_t)((lane >> 3) * 2 * K + 16 * ((lane & 7) ^ ((4 * par + (lane >> 4)) & 7)));
+  const uint32_t voffW = (uint32_t)((lane >> 2) * K + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
+  const int nk = K / Gm::BK;
+  auto copy_stage = [&](int s, int buf) {
+    const uint32_t kb = (uint32_t)(s * Gm::BK);
+#pragma unroll
+    for (int i = 0; i < Gm::LOADS; ++i) {
+      const int c = wave + 4 * i;
+      if (c < Gm::CHUNKS_A)
+        gemm_copy(lds0 + (uint32_t)(buf * Gm::A_TILE + c * 1024), ars,
+                  (uint32_t)(m0 + 8 * c) * (uint32_t)(2 * K) + 2u * kb, voffA[c & 1]);
+      else
+        gemm_copy(lds0 + (uint32_t)(Gm::W_REG + buf * Gm::W_TILE + (c - Gm::CHUNKS_A) * 1024), wrs,
+                  (uint32_t)(n0 + 16 * (c - Gm::CHUNKS_A)) * (uint32_t)K + kb, voffW);
+    }
+  };
+
+  // operand read offsets: activation row 32 mb + l % 32, logical unit 4 h + ks;
+  // weight row 32 wave + l % 32, logical units 2 h and 2 h + 1
+  const int r32 = lane & 31, h = lane >> 5;
+  const uint32_t arow = (uint32_t)(r32 * 128);
+  const int asw = (r32 >> 1) & 7;
+  const int wr = 32 * wave + r32;
+  const uint32_t woff0 = (uint32_t)(Gm::W_REG + wr * 64 + 16 * ((2 * h) ^ ((wr >> 2) & 3)));
+  const uint32_t woff1 = (uint32_t)(Gm::W_REG + wr * 64 + 16 * ((2 * h + 1) ^ ((wr >> 2) & 3)));
+
+  f32x16 acc[WM];
+#pragma unroll
+  for (int i = 0; i < WM; ++i) acc[i] = {};
+
+  const int pro = min(NBUF - 1, nk);
+  for (int s = 0; s < pro; ++s) copy_stage(s, s);
+
+  auto step = [&](auto bc, int s) {
+    constexpr int BUF = decltype(bc)::value;
+    gemm_wait_stages<Gm::LOADS, NBUF - 2>(min(NBUF - 2, nk - 1 - s));
+    __syncthreads();                          // stage s in LDS; stage s - 1 consumed by every wave
+    if (s + NBUF - 1 < nk) copy_stage(s + NBUF - 1, (BUF + NBUF - 1) % NBUF);
+    const uint4 w0 = *reinterpret_cast<const uint4*>(lds + woff0 + BUF * Gm::W_TILE);
+    const uint4 w1 = *reinterpret_cast<const uint4*>(lds + woff1 + BUF * Gm::W_TILE);
+    const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 b = fp8x8_to_bf16(wd[2 * ks], wd[2 * ks + 1]);
+      const uint32_t au = (uint32_t)(16 * ((4 * h + ks) ^ asw));
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(lds + BUF * Gm::A_TILE + mb * 32 * 128 + arow + au);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, acc[mb], 0, 0, 0);
+      }
+    }
+  };
+  for (int s = 0; s < nk; s += NBUF) {
+    bool more = true;
+    gemm_static_for<0, NBUF>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if (!more) return;
+      if (s + i >= nk) {
+        more = false;
+        return;
+      }
+      step(std::integral_constant<int, i>{}, s + i);
+    });
+  }
+
+  // epilogue: lane owns column n0 + 32 wave + l % 32 and rows 8 q + 4 h + r of each block
+  const int n = n0 + wr;
+  if (n < N) {
+    const float sc = w_scale[n];
+#pragma unroll
+    for (int mb = 0; mb < WM; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 32 * mb + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m < M) y[(int64_t)m * N + n] = f32_to_bf16(sc * acc[mb][e]);
+      }
+  }
+}
 }  // namespace
 
 extern "C" {
@@ -653,6 +790,33 @@ pta_status taco_gemm_w4a16_pack(const void* w, void* w_tiled, int32_t N, int32_t
 pta_status taco_gemm_w4a16_tiled(const void* a, const void* w_tiled, const float* w_scale, void* y, int32_t M,
                                  int32_t N, int32_t K, int32_t group, void* stream) {
   return w4a16_call(a, w_tiled, w_scale, y, M, N, K, group, stream, true);
+}
+
+pta_status taco_gemm_w8a16(const void* a, const void* w, const float* w_scale, void* y, int32_t M, int32_t N,
+                           int32_t K, void* stream) {
+  if (!a || !w || !w_scale || !y) return PTA_ERR_NULL_PTR;
+  if (M < 1 || N < 1 || K < 64 || K % 64 != 0) return PTA_ERR_BAD_DIMS;
+  if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(w)) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(w_scale) % 4 != 0)
+    return PTA_ERR_BAD_DIMS;
+  // row blocks of 64 rows up to 64 rows, else of 128
+  const bool tall = M > 64;
+  const int BM = tall ? W8Geom<4>::BM : W8Geom<2>::BM, BN = 128;
+  // every tile row (those past M or N included) must have a 32-bit buffer offset
+  const uint64_t mpad = (uint64_t)((M + BM - 1) / BM) * BM, npad = (uint64_t)((N + BN - 1) / BN) * BN;
+  if (mpad * (uint64_t)K * 2u >= ((uint64_t)1 << 32) || npad * (uint64_t)K >= ((uint64_t)1 << 32))
+    return PTA_ERR_BAD_DIMS;
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  const int64_t blocks = (int64_t)8 * tm * ((tn + 7) / 8);
+  if (blocks > 0x7fffffff) return PTA_ERR_BAD_DIMS;
+  auto launch = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NT), 0, (hipStream_t)stream,
+                       reinterpret_cast<const uint16_t*>(a), reinterpret_cast<const uint8_t*>(w), w_scale,
+                       reinterpret_cast<uint16_t*>(y), M, N, K, tm, tn);
+  };
+  if (tall) launch(gemm_w8a16_kernel<4>);
+  else launch(gemm_w8a16_kernel<2>);
+  return hipGetLastError() == hipSuccess ? PTA_OK : PTA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -228,6 +228,23 @@ def test_gemm_host_checks(lib):
     assert call(M=66817, K=64064) == DIMS
 
 
+def test_gemm_w8a16_host_checks(lib):
+    """taco_gemm_w8a16 rejects bad arguments on the host, before any HIP call."""
+    f = lib.taco_gemm_w8a16
+    ok = dict(a=FAKE, w=FAKE, s=FAKE, y=FAKE, M=4, N=4, K=256)
+    def call(**kw):
+        d = dict(ok, **kw)
+        return f(d["a"], d["w"], d["s"], d["y"], d["M"], d["N"], d["K"], None)
+    assert call(a=None) == NULLP and call(w=None) == NULLP and call(s=None) == NULLP and call(y=None) == NULLP
+    assert call(K=100) == DIMS and call(K=0) == DIMS and call(M=0) == DIMS and call(N=-1) == DIMS
+    assert call(a=ctypes.c_void_p(0x10008)) == DIMS and call(w=ctypes.c_void_p(0x10004)) == DIMS
+    assert call(s=ctypes.c_void_p(0x10002)) == DIMS                         # scales not 4-byte aligned
+    # 65409 columns pad to 65536 in 128-column tiles: 65536 x 65536 bytes reach 2^32
+    assert call(N=65409, K=65536) == DIMS
+    # 32769 rows pad to 32896: 32896 x 2 x 65536 bytes pass 2^32
+    assert call(M=32769, K=65536) == DIMS
+
+
 def test_gemm_w4a16_tiled_host_checks(lib):
     """Rearranged-weight entries: sizes, pointers and alignment checked on the host."""
     assert lib.taco_gemm_w4a16_tiled_bytes(0, 64) == 0 and lib.taco_gemm_w4a16_tiled_bytes(4, 100) == 0

@@ -311,3 +311,125 @@ def test_w4a16_argument_checks(torch_cuda):
     assert float(y.float().abs().max()) == 0.0
     with pytest.raises(ValueError):
         psv.taco_gemm_w4a16(a, w, s, 128)                 # 128 does not divide 192
+
+
+# ------------------------------------------------------------------ W8A16
+# Bound per output, from the arithmetic: every e4m3fn weight decodes exactly to bf16, the products
+# bf16 x bf16 are exact in float32, the matrix core sums them in float32, the channel scale
+# multiplies the float32 sum and the result is rounded to bf16:
+#     |y - y_ref| <= 2^-8 |y_ref| + 2^-14 * S,   S = w_scale[n] sum_k |a_mk| |w_nk|
+# (the W8A8 form: 2^-8 covers the bf16 result, 2^-14 S is far above the float32 sums).
+from workload.gemm import W8A16, make_w8a16, make_w8a16_device  # noqa: E402
+
+
+def run8(torch, g, rows=None):
+    import paged_speculative_verify_amd as psv
+    a = torch.from_numpy(np.ascontiguousarray(g.a_bits).view(np.int16)).cuda().view(torch.bfloat16)
+    w = torch.from_numpy(np.ascontiguousarray(g.w_codes)).cuda()
+    s = torch.from_numpy(np.ascontiguousarray(g.w_scale)).cuda()
+    y = psv.taco_gemm_w8a16(a, w, s)
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy().astype(np.float64)
+    return y if rows is None else y[rows]
+
+
+def bound8(a_bits, w_codes, w_scale, y):
+    """(reference, bound) of W8A16 outputs, column chunk by column chunk."""
+    A = np.abs(decode_bf16(a_bits))
+    ref = np.empty(y.shape)
+    S = np.empty(y.shape)
+    for c0 in range(0, w_codes.shape[0], 4096):
+        c1 = min(c0 + 4096, w_codes.shape[0])
+        ref[:, c0:c1] = oracle.w8a16_gemm(a_bits, w_codes[c0:c1], w_scale[c0:c1])
+        S[:, c0:c1] = A @ (np.abs(decode_fp8_e4m3fn(w_codes[c0:c1])) *
+                           w_scale[c0:c1].astype(np.float64)[:, None]).T
+    return ref, 2.0 ** -8 * np.abs(ref) + 2.0 ** -14 * S
+
+
+def check8(g, y, rows=None):
+    sel = slice(None) if rows is None else rows
+    ref, bound = bound8(g.a_bits[sel], g.w_codes, g.w_scale, y)
+    err = np.abs(y - ref)
+    assert np.isfinite(y).all()
+    assert (err <= bound).all(), f"worst excess {float((err - bound).max())}"
+    return float((err / np.maximum(bound, 1e-30)).max())
+
+
+W8_CASES = [
+    ("one_by_one", 1, 1, 64, 51),
+    ("ragged_small", 37, 200, 128, 52),
+    ("ragged_tall", 130, 260, 384, 53),
+    ("many_tiles", 300, 1100, 1024, 54),
+    ("decode_rows", 64, 2048, 8192, 55),
+]
+
+
+@pytest.mark.parametrize("cid,M,N,K,seed", W8_CASES, ids=[c[0] for c in W8_CASES])
+def test_w8a16_parity(torch_cuda, cid, M, N, K, seed):
+    g = make_w8a16(M, N, K, seed=seed)
+    say("w8a16", cid, M, N, K)
+    y = run8(torch_cuda, g)
+    r = check8(g, y)
+    say("w8a16", cid, "worst error / bound", r)
+
+
+def test_w8a16_full_size_sampled_rows(torch_cuda):
+    """Llama-3.1-70B gate+up at the verify step's 512 rows (the timed shape): operands drawn on
+    the GPU, rows spanning both row tiles and the ragged-free edge checked against the oracle."""
+    import torch
+    import paged_speculative_verify_amd as psv
+    s = LLAMA70B_GATE_UP
+    M, N, K = s["M"], s["N"], s["K"]
+    a, w, sc = make_w8a16_device(M, N, K, seed=7, torch=torch)
+    rows = np.array([0, 127, 128, 300, 511])
+    say("w8a16 full size", s, "rows", rows.tolist())
+    y = psv.taco_gemm_w8a16(a, w, sc)
+    torch.cuda.synchronize()
+    yr = y.float().cpu().numpy().astype(np.float64)[rows]
+    a_bits = a.view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+    ref, bound = bound8(a_bits, w.cpu().numpy(), sc.cpu().numpy(), yr)
+    err = np.abs(yr - ref)
+    assert np.isfinite(yr).all()
+    assert (err <= bound).all(), f"worst excess {float((err - bound).max())}"
+
+
+@pytest.mark.parametrize("M,N,K", [(40, 90, 256), (200, 300, 512)], ids=["short_rows", "tall_rows"])
+def test_w8a16_integer_exact(torch_cuda, M, N, K):
+    """Small integer activations and weights with power-of-two channel scales: every product and
+    partial sum is exact in float32, so the output is the bf16 rounding of the exact result."""
+    import torch
+    from tests.test_oracle_gemm import fp8_codes_of
+    from workload.gemm import bf16_bits_of
+    rng = np.random.default_rng(12)
+    ai, wi = rng.integers(-4, 5, (M, K)), rng.integers(-4, 5, (N, K))
+    sc = (2.0 ** rng.integers(-3, 3, N)).astype(np.float32)
+    g = W8A16(bf16_bits_of(ai.astype(np.float32)), fp8_codes_of(wi), sc)
+    say("w8a16 integer exact", M, N, K)
+    y = run8(torch_cuda, g)
+    exact = (ai @ wi.T).astype(np.float64) * sc[None, :].astype(np.float64)
+    want = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(y, want)
+
+
+def test_w8a16_nan_rows_and_columns(torch_cuda):
+    """A NaN activation makes its output row NaN, a NaN weight code its output column; the other
+    outputs stay finite."""
+    g = make_w8a16(40, 130, 256, seed=13)
+    g.a_bits[3, 17] = 0x7FC0
+    g.w_codes[100, 200] = 0x7F
+    y = run8(torch_cuda, g)
+    assert np.isnan(y[3]).all() and np.isnan(y[:, 100]).all()
+    rest = np.delete(np.delete(y, 3, axis=0), 100, axis=1)
+    assert np.isfinite(rest).all()
+
+
+def test_w8a16_argument_checks(torch_cuda):
+    import torch
+    import paged_speculative_verify_amd as psv
+    a = torch.zeros((8, 100), dtype=torch.bfloat16, device="cuda")      # K not a multiple of 64
+    w = torch.zeros((8, 100), dtype=torch.uint8, device="cuda")
+    s = torch.ones(8, dtype=torch.float32, device="cuda")
+    with pytest.raises(psv.PtaError):
+        psv.taco_gemm_w8a16(a, w, s)
+    with pytest.raises(ValueError):
+        psv.taco_gemm_w8a16(a[:, :64].contiguous(), w[:, :64].contiguous(), s[:4].contiguous())

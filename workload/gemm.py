@@ -116,3 +116,34 @@ def make_w4a16_device(M: int, N: int, K: int, group: int, seed: int, torch, devi
     u = (q & 0xF).to(torch.uint8)
     packed = (u[:, 0::2] | (u[:, 1::2] << 4)).contiguous()
     return a, packed, scale.contiguous()
+
+
+@dataclass
+class W8A16:
+    a_bits: np.ndarray     # uint16 [M, K] bf16 bit patterns
+    w_codes: np.ndarray    # uint8 [N, K] e4m3fn codes
+    w_scale: np.ndarray    # float32 [N]
+
+
+def make_w8a16(M: int, N: int, K: int, seed: int = 0) -> W8A16:
+    """bf16 N(0, 1) activations; N(0, 1) weights quantized to e4m3fn with one scale per row
+    (the W8A8 weight recipe)."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((M, K), dtype=np.float32)
+    w = rng.standard_normal((N, K), dtype=np.float32)
+    wc, wsc = _rowwise_fp8(w)
+    return W8A16(bf16_bits_of(a), wc, wsc)
+
+
+def make_w8a16_device(M: int, N: int, K: int, seed: int, torch, device="cuda"):
+    """The same recipe drawn on the GPU: returns (a bf16 [M, K], w_codes uint8 [N, K],
+    w_scale float32 [N]) device tensors."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    a = torch.randn((M, K), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16).contiguous()
+    x = torch.randn((N, K), generator=g, device=device, dtype=torch.float32)
+    amax = x.abs().amax(dim=1)
+    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+    codes = (x / scale[:, None]).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    del x
+    return a, codes, scale.contiguous()
