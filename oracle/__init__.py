@@ -25,4 +25,4 @@ from .kv_append import kv_append  # noqa: F401
 from .accept import accept_commit, accept_path, tree_parents  # noqa: F401
 from .roofline import decode_io_compute_ms, lookahead_speedup  # noqa: F401
 from .lookahead import LookaheadOracle, tree_mask_from_parents  # noqa: F401
-from .quant_gemm import decode_int4_packed, w4a16_gemm, w8a8_gemm, w8a16_gemm  # noqa: F401
+from .quant_gemm import decode_int4_packed, w4a8_gemm, w4a16_gemm, w8a8_gemm, w8a16_gemm  # noqa: F401

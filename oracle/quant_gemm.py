@@ -22,6 +22,11 @@ scale granularity; these readings are taken:
   * W8A16: A bf16; W fp8 e4m3fn codes (the W8A8 weight format, which carries
     its own exponent), one float32 scale per weight row:
         Y[m, n] = w_scale[n] * sum_k A[m, k] * dec(W[n, k]).
+  * W4A8: A signed 8-bit integers (-128 .. 127) with one float32 scale per
+    activation row; W the W4A16 int4 codes and group scales:
+        Y[m, n] = a_scale[m] * sum_k A[m, k] * q[n, k] * w_scale[n, k // G].
+    (8-bit integers rather than fp8 on the activation side: int4 weights widen
+    to int8 exactly, so the products run on integer matrix cores.)
 
 Nothing here is shared with the library.
 """
@@ -67,3 +72,14 @@ def w8a16_gemm(a_bits, w_codes, w_scale) -> np.ndarray:
     a = decode_bf16(a_bits)
     w = decode_fp8_e4m3fn(w_codes) * np.asarray(w_scale, np.float64)[:, None]
     return a @ w.T
+
+
+def w4a8_gemm(a_codes, a_scale, w_packed, w_scale, group: int) -> np.ndarray:
+    """int8 activations (per-row scales) x group-scaled int4 weights, fp64 [M, N]."""
+    a = np.asarray(a_codes).astype(np.int8).astype(np.float64) * np.asarray(a_scale, np.float64)[:, None]
+    k = a.shape[1]
+    assert k % group == 0
+    q = decode_int4_packed(w_packed, k).astype(np.float64)
+    s = np.repeat(np.asarray(w_scale, np.float64), group, axis=1)
+    assert s.shape == q.shape
+    return a @ (q * s).T

@@ -64,6 +64,10 @@ def pin_worked_example(mod=qg):
     wc = np.array(g["w8a8_w_codes"], np.uint8).reshape(1, 2)
     y = mod.w8a8_gemm(ac, np.array(g["w8a8_a_scale"], np.float32), wc, np.array(g["w8a8_w_scale"], np.float32))
     assert list(y[:, 0]) == g["w8a8_y"]
+    ac = np.array([g["w4a8_a_codes"]], np.uint8)
+    y = mod.w4a8_gemm(ac, np.array(g["w4a8_a_scale"], np.float32), np.array([[0x7F, 0x18], [0x10, 0x32]], np.uint8),
+                      np.array(g["w4a16_scales"], np.float32).reshape(2, 2), 2)
+    assert list(y[0]) == g["w4a8_y"]
     a = bf16_bits(np.array([g["w8a16_a"]]))
     wc = np.array(g["w8a16_w_codes"], np.uint8).reshape(2, 2)
     y = mod.w8a16_gemm(a, wc, np.array(g["w8a16_w_scale"], np.float32))
@@ -92,6 +96,14 @@ def pin_integers(mod=qg, seed=0):
     assert np.array_equal(y, ref)
     ref = (ai @ wi.T).astype(np.float64) * sw[None, :]
     y = mod.w8a16_gemm(bf16_bits(ai.astype(np.float32)), fp8_codes_of(wi), sw.astype(np.float32))
+    assert np.array_equal(y, ref)
+    a8 = rng.integers(-128, 128, (M, K))
+    ref = np.zeros((M, N))
+    for g in range(K // G):
+        ks = slice(g * G, (g + 1) * G)
+        ref += (a8[:, ks] @ qi[:, ks].T).astype(np.float64) * gs[None, :, g]
+    ref *= sa[:, None]
+    y = mod.w4a8_gemm(a8.astype(np.int8).view(np.uint8), sa.astype(np.float32), pack_int4(qi), gs.astype(np.float32), G)
     assert np.array_equal(y, ref)
 
 
@@ -122,6 +134,12 @@ def pin_brute_force(mod=qg, seed=1):
     for m, n in itertools.product(range(M), range(N)):
         ref = sum(av[m, k] * float(tab[wc[n, k]]) for k in range(K)) * float(sw[n])
         assert abs(y[m, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+    a8 = rng.integers(0, 256, (M, K)).astype(np.uint8)            # any byte: two's complement codes
+    y = mod.w4a8_gemm(a8, sa, pack_int4(qi), gs, G)
+    for m, n in itertools.product(range(M), range(N)):
+        ref = sum((int(a8[m, k]) - 256 * (a8[m, k] >= 128)) * qi[n, k] * float(gs[n, k // G])
+                  for k in range(K)) * float(sa[m])
+        assert abs(y[m, n] - ref) <= 1e-12 * max(1.0, abs(ref))
 
 
 def pin_closed_forms(mod=qg, seed=2):
@@ -147,6 +165,15 @@ def pin_closed_forms(mod=qg, seed=2):
     ai = rng.integers(-6, 7, (3, K)) * 0.25
     y = mod.w8a16_gemm(bf16_bits(ai.astype(np.float32)), wc, sw)
     assert np.array_equal(y, mod.w8a8_gemm(fp8_codes_of(ai), np.ones(3, np.float32), wc, sw))
+    # W4A8 with unit activation scales is W4A16 on the same integers (every int8 is a bf16
+    # value); a constant activation scale factors out
+    a8 = rng.integers(-128, 128, (3, 32))
+    gsc = rng.uniform(0.5, 2, (N, 4)).astype(np.float32)
+    y1 = mod.w4a8_gemm(a8.astype(np.int8).view(np.uint8), np.ones(3, np.float32), pack_int4(qi), gsc, 8)
+    y2 = mod.w4a16_gemm(bf16_bits(a8.astype(np.float32)), pack_int4(qi), gsc, 8)
+    assert np.array_equal(y1, y2)
+    y3 = mod.w4a8_gemm(a8.astype(np.int8).view(np.uint8), np.full(3, 0.375, np.float32), pack_int4(qi), gsc, 8)
+    assert np.allclose(y3, 0.375 * y1, rtol=1e-14, atol=0)
 
 
 PINS = [pin_worked_example, pin_integers, pin_brute_force, pin_closed_forms]
@@ -162,7 +189,7 @@ class _Mutant:
     """The oracle module with one function replaced."""
     def __init__(self, **over):
         self.__dict__.update({k: getattr(qg, k) for k in ("decode_int4_packed", "w8a8_gemm", "w4a16_gemm",
-                                                          "w8a16_gemm")})
+                                                          "w8a16_gemm", "w4a8_gemm")})
         self.__dict__.update(over)
 
 
@@ -214,7 +241,22 @@ def _w8a16_weights_as_bf16_bits(a_bits, w_codes, w_scale):
     return qg.decode_bf16(a_bits) @ (qg.decode_bf16(w_bits) * np.asarray(w_scale, np.float64)[:, None]).T
 
 
+def _w4a8_unsigned_activations(a_codes, a_scale, w_packed, w_scale, group):
+    """Activation bytes read as unsigned 0..255."""
+    a = np.asarray(a_codes, np.uint8).astype(np.float64) * np.asarray(a_scale, np.float64)[:, None]
+    q = qg.decode_int4_packed(w_packed, a.shape[1]).astype(np.float64)
+    return a @ (q * np.repeat(np.asarray(w_scale, np.float64), group, axis=1)).T
+
+
+def _w4a8_scale_per_column(a_codes, a_scale, w_packed, w_scale, group):
+    """The activation scales applied along the output columns."""
+    y = qg.w4a8_gemm(a_codes, np.ones(len(a_scale), np.float32), w_packed, w_scale, group)
+    return y * np.resize(np.asarray(a_scale, np.float64), y.shape[1])[None, :]
+
+
 @pytest.mark.parametrize("mutant", [
+    _Mutant(w4a8_gemm=_w4a8_unsigned_activations),
+    _Mutant(w4a8_gemm=_w4a8_scale_per_column),
     _Mutant(w8a16_gemm=_w8a16_scale_by_k),
     _Mutant(w8a16_gemm=_w8a16_weights_as_bf16_bits),
     _Mutant(decode_int4_packed=_nibbles_swapped),
@@ -222,7 +264,7 @@ def _w8a16_weights_as_bf16_bits(a_bits, w_codes, w_scale):
     _Mutant(w8a8_gemm=_w8a8_scale_axis_swapped),
     _Mutant(w4a16_gemm=_w4a16_first_group_scale),
     _Mutant(w4a16_gemm=_w4a16_group_by_rows),
-], ids=["w8a16_scale_along_k", "w8a16_codes_as_bf16", "nibbles_swapped", "unsigned_nibbles", "w8a8_scale_axes", "w4a16_one_group_scale", "w4a16_groups_by_rows"])
+], ids=["w4a8_unsigned_activations", "w4a8_scale_per_column", "w8a16_scale_along_k", "w8a16_codes_as_bf16", "nibbles_swapped", "unsigned_nibbles", "w8a8_scale_axes", "w4a16_one_group_scale", "w4a16_groups_by_rows"])
 def test_planted_mistakes_fail_a_pin(mutant):
     # the W4A16 mutants call the real decoder; make them use the mutant's too where it differs
     failed = 0
