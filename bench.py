@@ -612,7 +612,26 @@ GEMM_SHAPES = {
     "w4a16_llama70b_gate_up_decode64": ("w4a16", 64, 57344, 8192),
     "w8a16_llama70b_gate_up_verify512": ("w8a16", 512, 57344, 8192),
     "w8a16_llama70b_gate_up_decode64": ("w8a16", 64, 57344, 8192),
+    "w4a8_llama70b_gate_up_verify512": ("w4a8", 512, 57344, 8192),
+    "w4a8_llama70b_gate_up_decode64": ("w4a8", 64, 57344, 8192),
 }
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (POP/s x 1000)
+
+
+def w4a8_oracle_rows(oracle, a_codes, a_scale, w_packed, w_scale, group, with_bound=True):
+    """(fp64 reference, bound 2^-8 |ref| + 2^-14 a_scale sum|a||q|s) of a few rows, column chunk by
+    column chunk."""
+    K = a_codes.shape[1]
+    ref = np.empty((a_codes.shape[0], w_packed.shape[0]))
+    S = np.empty_like(ref)
+    A = np.abs(a_codes.view(np.int8).astype(np.float64)) * a_scale.astype(np.float64)[:, None]
+    for c0 in range(0, w_packed.shape[0], 4096):
+        c1 = min(c0 + 4096, w_packed.shape[0])
+        ref[:, c0:c1] = oracle.w4a8_gemm(a_codes, a_scale, w_packed[c0:c1], w_scale[c0:c1], group)
+        if with_bound:
+            q = np.abs(oracle.decode_int4_packed(w_packed[c0:c1], K)).astype(np.float64)
+            S[:, c0:c1] = A @ (q * np.repeat(w_scale[c0:c1].astype(np.float64), group, axis=1)).T
+    return ref, 2.0 ** -8 * np.abs(ref) + 2.0 ** -14 * S
 
 
 def w8a16_oracle_rows(oracle, a_bits, w_codes, w_scale, with_bound=True):
@@ -654,7 +673,7 @@ def gemm_bench(psv, torch, name, steps=30, warmup=5, cpu_rows=2, parity_rows=(0,
     (whichever the shape's intensity says bounds it), parity of sampled output rows against the
     fp64 oracle, the oracle timed on a few rows."""
     import oracle
-    from workload.gemm import make_w4a16_device, make_w8a8_device, make_w8a16_device
+    from workload.gemm import make_w4a8_device, make_w4a16_device, make_w8a8_device, make_w8a16_device
     op, M, N, K = GEMM_SHAPES[name]
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     if op == "w8a8":
@@ -669,6 +688,12 @@ def gemm_bench(psv, torch, name, steps=30, warmup=5, cpu_rows=2, parity_rows=(0,
         call = lambda: psv.taco_gemm_w8a16(a, w, sw, y)
         peak, kernel = BF16_PEAK_TFLOPS, "gemm_w8a16_kernel"
         nbytes = 2 * M * K + N * K + 4 * N + 2 * M * N
+    elif op == "w4a8":
+        G = W4_GROUP
+        a, sa, w, sw = make_w4a8_device(M, N, K, G, seed=11, torch=torch)
+        call = lambda: psv.taco_gemm_w4a8(a, sa, w, sw, G, y)
+        peak, kernel = INT8_PEAK_TOPS, "gemm_w4a8_kernel"
+        nbytes = M * K + 4 * M + N * K // 2 + 4 * N * (K // G) + 2 * M * N
     else:
         G = W4_GROUP
         a, w, sw = make_w4a16_device(M, N, K, G, seed=11, torch=torch)
@@ -734,6 +759,19 @@ def gemm_bench(psv, torch, name, steps=30, warmup=5, cpu_rows=2, parity_rows=(0,
         metric = "W8A16 GEMM TFLOP/s (bf16 activations, fp8 e4m3fn weights, per-channel scales, bf16 out), 1 GPU"
         bound_text = "2^-8 |y_ref| + 2^-14 w_scale sum_k |a||w| per output"
         config = {"workload": name, "M": M, "N": N, "K": K}
+    elif op == "w4a8":
+        ac, asc = a[sel].cpu().numpy().view(np.uint8), sa.cpu().numpy()[rows]
+        wp, wsc = w.cpu().numpy(), sw.cpu().numpy()
+        ref, bnd = w4a8_oracle_rows(oracle, ac, asc, wp, wsc, W4_GROUP)
+        with threadpool_limits(limits=cores, user_api="blas"):
+            t0 = time.perf_counter()
+            w4a8_oracle_rows(oracle, ac[:cpu_rows], asc[:cpu_rows], wp, wsc, W4_GROUP, with_bound=False)
+            t_cpu = time.perf_counter() - t0
+        dtype = "int8 x int4 (exact to int8) -> i32 per group, group scales in f32 -> bf16"
+        metric = ("W4A8 GEMM TOP/s (int8 activations with row scales, int4 weights, group-128 scales, "
+                  "bf16 out), 1 GPU")
+        bound_text = "2^-8 |y_ref| + 2^-14 a_scale sum_k |a||q| w_scale per output"
+        config = {"workload": name, "M": M, "N": N, "K": K, "group": W4_GROUP}
     else:
         a_bits = a[sel].view(torch.int16).cpu().numpy().view(np.uint16)
         wp, wsc = w.cpu().numpy(), sw.cpu().numpy()
@@ -748,14 +786,15 @@ def gemm_bench(psv, torch, name, steps=30, warmup=5, cpu_rows=2, parity_rows=(0,
         config = {"workload": name, "M": M, "N": N, "K": K, "group": W4_GROUP,
                   "weights": "rearranged by taco_gemm_w4a16_pack before timing (taco_gemm_w4a16_tiled)"}
     excess = float((np.abs(got - ref) - bnd).max())
+    ops = "TOP/s" if op == "w4a8" else "TFLOP/s"          # integer products count as operations
     res = {
         "metric": metric,
-        "value": round(tflops, 2), "unit": "TFLOP/s", "higher_is_better": True, "data": "synthetic",
+        "value": round(tflops, 2), "unit": ops, "higher_is_better": True, "data": "synthetic",
         "dtype": dtype, "config": config,
         "us_per_call": round(ms * 1e3, 2), "steps": steps, "warmup": warmup,
         "roofline": {"bound": bound, "achieved": round(tflops if bound == "mfma" else gbs, 2),
                      "peak": peak if bound == "mfma" else HBM_PEAK_GBS,
-                     "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                     "unit": ops if bound == "mfma" else "GB/s",
                      "frac": round(tflops / peak if bound == "mfma" else gbs / HBM_PEAK_GBS, 4),
                      "traffic": None, "mfma_frac": round(tflops / peak, 4),
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -765,7 +804,7 @@ def gemm_bench(psv, torch, name, steps=30, warmup=5, cpu_rows=2, parity_rows=(0,
                      "timing": f"HIP events on the launch stream around {steps} back-to-back calls"},
         "parity": {"rows": rows.tolist(), "max_excess_over_bound": excess, "parity_ok": bool(excess <= 0),
                    "bound": bound_text},
-        "cpu_baseline": {"value": round(2.0 * cpu_rows * N * K / t_cpu / 1e12, 6), "unit": "TFLOP/s",
+        "cpu_baseline": {"value": round(2.0 * cpu_rows * N * K / t_cpu / 1e12, 6), "unit": ops,
                          "cores": cores, "kind": "oracle",
                          "sample": f"{cpu_rows} output rows x {N} columns, fp64 numpy, {t_cpu:.1f} s"},
     }
@@ -807,7 +846,7 @@ def main(argv=None) -> int:
     ap.add_argument("--la-threads", type=int, default=8,
                     help="with --lookahead-cache: threads of the cache's batch calls (also timed on one)")
     ap.add_argument("--gemm", choices=sorted(GEMM_SHAPES), default=None,
-                    help="instead of the bench line: one quantized GEMM (W8A8, W4A16 or W8A16) on a Llama-70B-shaped projection")
+                    help="instead of the bench line: one quantized GEMM (W8A8, W4A16, W8A16 or W4A8) on a Llama-70B-shaped projection")
     ap.add_argument("--qlen-floor", action="store_true",
                     help="instead of the bench line: attention time against the number of candidates "
                          "per sequence at the decode shape, T(q_len) / T(1)")

@@ -19,6 +19,8 @@
  *           (output channel, group of `group` consecutive k).
  *   W8A16:  Y[m][n] = w_scale[n] * sum_k A[m][k] * W[n][k],
  *           A bf16, W fp8 e4m3fn codes, one float32 scale per output channel.
+ *   W4A8:   Y[m][n] = a_scale[m] * sum_k A[m][k] * q[n][k] * w_scale[n][k / group],
+ *           A signed 8-bit integers, q and w_scale as W4A16.
  * Y is bf16 [M][N] row-major, rounded to nearest even from float32.
  *
  * Conventions as in pta.h: device pointers, caller-owned buffers, work
@@ -107,6 +109,24 @@ pta_status taco_gemm_w4a16_tiled(const void* a, const void* w_tiled, const float
  * activations propagate to the affected outputs. */
 pta_status taco_gemm_w8a16(const void* a, const void* w, const float* w_scale, void* y, int32_t M, int32_t N,
                            int32_t K, void* stream);
+
+/* int8 x group-scaled int4 GEMM on the integer matrix cores
+ * (v_mfma_i32_32x32x32_i8): the W4A8 operator the 17173xz.com article lists
+ * ("TACO-LLM如何实现降本增效?"), with 8-bit integer activations (int4 weights
+ * widen to int8 exactly).  Each group's products are summed exactly in int32,
+ * scaled by w_scale in float32, and the float32 total multiplied by a_scale.
+ *   a        int8  [M][K]      two's complement, row-major, 16-byte aligned
+ *   a_scale  float [M], 4-byte aligned
+ *   w        uint8 [N][K / 2]  as taco_gemm_w4a16 (low nibble = even k), 16-byte aligned
+ *   w_scale  float [N][K / group], 4-byte aligned
+ *   y        bf16  [M][N]      row-major (written; every element)
+ * M >= 1, N >= 1, K a positive multiple of 64, group a multiple of 64 that
+ * divides K; M rounded up to a multiple of 128 (64 when M <= 64) times K, N
+ * rounded up to a multiple of 128 times K / 2 and times 4 K / group, below
+ * 2^32 (else PTA_ERR_BAD_DIMS); misaligned pointers PTA_ERR_BAD_DIMS; NULL
+ * pointers PTA_ERR_NULL_PTR; a failed launch PTA_ERR_HIP. */
+pta_status taco_gemm_w4a8(const void* a, const float* a_scale, const void* w, const float* w_scale, void* y,
+                          int32_t M, int32_t N, int32_t K, int32_t group, void* stream);
 
 #ifdef __cplusplus
 }

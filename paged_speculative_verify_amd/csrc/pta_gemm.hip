@@ -3,7 +3,7 @@
 // (17173xz.com article, section "TACO-LLM如何实现降本增效?"; 618zxw.cn article,
 // section "LLM量子化技術による推論コストの削減"; design talk section
 // "5. 支持 Quantization（模型量化）": low-bit weights on low-precision matrix
-// instructions).  W8A8 first, W4A16 and W8A16 below.
+// instructions).  W8A8 first, W4A16, W8A16 and W4A8 below.
 //
 // W8A8:
 //   * Waves of 64 x 32 WNB (2 x WNB blocks of v_mfma_scale_f32_32x32x64_f8f6f4
@@ -37,6 +37,7 @@ using namespace pta;
 namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 128, BK = 64, NT = 256;
@@ -691,6 +692,168 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
       }
   }
 }
+
+// ------------------------------------------------------------------ W4A8
+// int8 activations (per-row scales) x group-scaled int4 weights on the integer
+// matrix cores (v_mfma_i32_32x32x32_i8, int32 accumulation):
+//   * Tiles 32 WM x 128, 64 k per stage, each of four waves 32 columns and all
+//     32 WM rows, weights in the W4A16 layout and staging (packed rows of 32
+//     bytes per stage, group scales by LDS-DMA into four slots), activation
+//     rows of 64 bytes per stage with unit u of row r at u ^ ((r >> 2) & 3).
+//   * k assignment: in k-step ks (32 k) lane half h covers the 16 k at
+//     16 (2 h + ks) of the stage, so a lane's weights for the stage are one
+//     16-byte LDS read and its activations one 16-byte read per k-step and row
+//     block.
+//   * Widening is exact and cheap: a nibble moved to the top of its byte is the
+//     int8 value 16 q, so (w << 4) & 0xF0F0F0F0 and w & 0xF0F0F0F0 hold the
+//     even and odd k of eight weights and one byte permute each restores k
+//     order; the factor 16 comes out with the activation scale (a power of
+//     two, exact).
+//   * A group's products sum exactly in int32 (|16 q a| <= 2^14 per product);
+//     at the group's end acc += s[n][g] * float(acc_g) in float32, and the
+//     epilogue multiplies by a_scale[m] / 16 and rounds to bf16.
+template <int WM>
+struct W48Geom {
+  static constexpr int BM = 32 * WM, BN = 128, BK = 64;
+  static constexpr int NBUF = 4;
+  static constexpr int A_TILE = BM * BK;                   // int8
+  static constexpr int W_TILE = BN * BK / 2;               // packed int4 (4 KiB)
+  static constexpr int W_REG = NBUF * A_TILE;
+  static constexpr int S_REG = W_REG + NBUF * W_TILE;      // 4 scale slots of 128 floats
+  static constexpr int CHUNKS_A = A_TILE / 1024, CHUNKS_W = W_TILE / 1024;
+  static constexpr int LOADS = (CHUNKS_A + CHUNKS_W) / 4;  // copies per wave per stage
+  static constexpr int LDS_BYTES = S_REG + 4 * 512;
+  static_assert((CHUNKS_A + CHUNKS_W) % 4 == 0, "whole copies per wave");
+  static_assert(LDS_BYTES <= 81920, "two workgroups per compute unit");
+};
+
+// Eight int4 weights (low nibble = even k) as eight int8 values 16 q, in k
+// order, as two words.
+__device__ __forceinline__ void int4x8_to_i8x16q(uint32_t w, uint32_t& k0to3, uint32_t& k4to7) {
+  const uint32_t lo = (w << 4) & 0xF0F0F0F0u, hi = w & 0xF0F0F0F0u;   // k 0 2 4 6 / k 1 3 5 7
+  k0to3 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  k4to7 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+
+template <int WM>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w4a8_kernel(
+    const uint8_t* a, const float* a_scale, const uint8_t* w, const float* w_scale, uint16_t* y, int M, int N, int K,
+    int G, int tm, int tn) {
+  using Gm = W48Geom<WM>;
+  constexpr int BM = Gm::BM, BN = Gm::BN, NBUF = Gm::NBUF;
+  __shared__ __attribute__((aligned(1024))) char lds[Gm::LDS_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int nt = (slot / tm) * 8 + xcd, mt = slot % tm;
+  if (nt >= tn) return;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int KG = K / G;                                     // groups per row
+
+  const i32x4 ars = gemm_rsrc(a, (uint32_t)((uint64_t)M * (uint64_t)K));
+  const i32x4 wrs = gemm_rsrc(w, (uint32_t)((uint64_t)N * (uint64_t)K / 2u));
+  const i32x4 srs = gemm_rsrc(w_scale, (uint32_t)((uint64_t)N * (uint64_t)KG * 4u));
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&lds[0];
+
+  // copy lanes.  Activation chunk c (16 rows of 64 bytes): lane l fills row
+  // 16 c + l / 4, physical unit l % 4, holding logical unit (l % 4) ^ ((l / 16) & 3).
+  // Weight chunk (32 rows of 32 bytes) as in W4A16.
+  const uint32_t voffA = (uint32_t)((lane >> 2) * K + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
+  const uint32_t voffW = (uint32_t)((lane >> 1) * (K / 2) + 16 * ((lane & 1) ^ ((lane >> 4) & 1)));
+  const int nk = K / Gm::BK, GS = G / Gm::BK;              // stages, stages per group
+  auto copy_stage = [&](int s, int buf) {
+    const uint32_t kb = (uint32_t)(s * Gm::BK);
+#pragma unroll
+    for (int i = 0; i < Gm::LOADS; ++i) {
+      const int c = wave + 4 * i;
+      if (c < Gm::CHUNKS_A)
+        gemm_copy(lds0 + (uint32_t)(buf * Gm::A_TILE + c * 1024), ars, (uint32_t)(m0 + 16 * c) * (uint32_t)K + kb,
+                  voffA);
+      else
+        gemm_copy(lds0 + (uint32_t)(Gm::W_REG + buf * Gm::W_TILE + (c - Gm::CHUNKS_A) * 1024), wrs,
+                  (uint32_t)(n0 + 32 * (c - Gm::CHUNKS_A)) * (uint32_t)(K / 2) + kb / 2u, voffW);
+    }
+    if (wave == 0 && s % GS == 0) {
+      const int g = s / GS;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        gemm_copy_dword(lds0 + (uint32_t)(Gm::S_REG + (g & 3) * 512 + 256 * j), srs,
+                        ((uint32_t)(n0 + 64 * j + lane) * (uint32_t)KG + (uint32_t)g) * 4u);
+    }
+  };
+
+  // operand read offsets: activation row 32 mb + l % 32, logical unit 2 h + ks;
+  // weight row 32 wave + l % 32, logical unit h
+  const int r32 = lane & 31, h = lane >> 5;
+  const uint32_t arow = (uint32_t)(r32 * 64);
+  const int asw = (r32 >> 2) & 3;                            // same for every row block
+  const int wr = 32 * wave + r32;
+  const uint32_t woff = (uint32_t)(Gm::W_REG + wr * 32 + 16 * (h ^ ((wr >> 3) & 1)));
+
+  f32x16 acc[WM];
+  i32x16 accg[WM];
+#pragma unroll
+  for (int i = 0; i < WM; ++i) acc[i] = {};
+
+  const int pro = min(NBUF - 1, nk);
+  for (int s = 0; s < pro; ++s) copy_stage(s, s);
+
+  auto step = [&](auto bc, int s) {
+    constexpr int BUF = decltype(bc)::value;
+    gemm_wait_stages<Gm::LOADS, NBUF - 2>(min(NBUF - 2, nk - 1 - s));
+    __syncthreads();                          // stage s in LDS; stage s - 1 consumed by every wave
+    if (s + NBUF - 1 < nk) copy_stage(s + NBUF - 1, (BUF + NBUF - 1) % NBUF);
+    const bool first = s % GS == 0;
+    const uint4 wq = *reinterpret_cast<const uint4*>(lds + woff + BUF * Gm::W_TILE);
+    const uint32_t wd[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      i32x4 b;
+      uint32_t b0, b1, b2, b3;
+      int4x8_to_i8x16q(wd[2 * ks], b0, b1);
+      int4x8_to_i8x16q(wd[2 * ks + 1], b2, b3);
+      b = i32x4{(int32_t)b0, (int32_t)b1, (int32_t)b2, (int32_t)b3};
+      const uint32_t au = (uint32_t)(16 * ((2 * h + ks) ^ asw));
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb) {
+        const i32x4 av = *reinterpret_cast<const i32x4*>(lds + BUF * Gm::A_TILE + mb * 32 * 64 + arow + au);
+        if (ks == 0 && first) accg[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, b, i32x16{}, 0, 0, 0);
+        else accg[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, b, accg[mb], 0, 0, 0);
+      }
+    }
+    if (s % GS == GS - 1) {                   // the group's last stage: acc += s[n][g] * acc_g
+      const float sc = *reinterpret_cast<const float*>(lds + Gm::S_REG + ((s / GS) & 3) * 512 + 4 * wr);
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[mb][e] = fmaf(sc, (float)accg[mb][e], acc[mb][e]);
+    }
+  };
+  for (int s = 0; s < nk; s += NBUF) {
+    bool more = true;
+    gemm_static_for<0, NBUF>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if (!more) return;
+      if (s + i >= nk) {
+        more = false;
+        return;
+      }
+      step(std::integral_constant<int, i>{}, s + i);
+    });
+  }
+
+  // epilogue: lane owns column n0 + 32 wave + l % 32 and rows 8 q + 4 h + r of each block
+  const int n = n0 + wr;
+  if (n < N) {
+#pragma unroll
+    for (int mb = 0; mb < WM; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 32 * mb + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m < M) y[(int64_t)m * N + n] = f32_to_bf16(acc[mb][e] * (a_scale[m] * 0.0625f));
+      }
+  }
+}
 }  // namespace
 
 extern "C" {
@@ -790,6 +953,35 @@ pta_status taco_gemm_w4a16_pack(const void* w, void* w_tiled, int32_t N, int32_t
 pta_status taco_gemm_w4a16_tiled(const void* a, const void* w_tiled, const float* w_scale, void* y, int32_t M,
                                  int32_t N, int32_t K, int32_t group, void* stream) {
   return w4a16_call(a, w_tiled, w_scale, y, M, N, K, group, stream, true);
+}
+
+pta_status taco_gemm_w4a8(const void* a, const float* a_scale, const void* w, const float* w_scale, void* y,
+                          int32_t M, int32_t N, int32_t K, int32_t group, void* stream) {
+  if (!a || !a_scale || !w || !w_scale || !y) return PTA_ERR_NULL_PTR;
+  if (M < 1 || N < 1 || K < 64 || K % 64 != 0 || group < 64 || group % 64 != 0 || K % group != 0)
+    return PTA_ERR_BAD_DIMS;
+  if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(w)) % 16 != 0 ||
+      (reinterpret_cast<uintptr_t>(a_scale) | reinterpret_cast<uintptr_t>(w_scale)) % 4 != 0)
+    return PTA_ERR_BAD_DIMS;
+  // row blocks of 64 rows up to 64 rows, else of 128
+  const bool tall = M > 64;
+  const int BM = tall ? W48Geom<4>::BM : W48Geom<2>::BM, BN = 128;
+  // every tile row (those past M or N included) must have a 32-bit buffer offset
+  const uint64_t mpad = (uint64_t)((M + BM - 1) / BM) * BM, npad = (uint64_t)((N + BN - 1) / BN) * BN;
+  if (mpad * (uint64_t)K >= ((uint64_t)1 << 32) || npad * (uint64_t)K / 2u >= ((uint64_t)1 << 32) ||
+      npad * (uint64_t)(K / group) * 4u >= ((uint64_t)1 << 32))
+    return PTA_ERR_BAD_DIMS;
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  const int64_t blocks = (int64_t)8 * tm * ((tn + 7) / 8);
+  if (blocks > 0x7fffffff) return PTA_ERR_BAD_DIMS;
+  auto launch = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NT), 0, (hipStream_t)stream,
+                       reinterpret_cast<const uint8_t*>(a), a_scale, reinterpret_cast<const uint8_t*>(w), w_scale,
+                       reinterpret_cast<uint16_t*>(y), M, N, K, group, tm, tn);
+  };
+  if (tall) launch(gemm_w4a8_kernel<4>);
+  else launch(gemm_w4a8_kernel<2>);
+  return hipGetLastError() == hipSuccess ? PTA_OK : PTA_ERR_HIP;
 }
 
 pta_status taco_gemm_w8a16(const void* a, const void* w, const float* w_scale, void* y, int32_t M, int32_t N,

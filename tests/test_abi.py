@@ -245,6 +245,23 @@ def test_gemm_w8a16_host_checks(lib):
     assert call(M=32769, K=65536) == DIMS
 
 
+def test_gemm_w4a8_host_checks(lib):
+    """taco_gemm_w4a8 rejects bad arguments on the host, before any HIP call."""
+    f = lib.taco_gemm_w4a8
+    ok = dict(a=FAKE, sa=FAKE, w=FAKE, s=FAKE, y=FAKE, M=4, N=4, K=256, G=128)
+    def call(**kw):
+        d = dict(ok, **kw)
+        return f(d["a"], d["sa"], d["w"], d["s"], d["y"], d["M"], d["N"], d["K"], d["G"], None)
+    assert call(a=None) == NULLP and call(sa=None) == NULLP and call(w=None) == NULLP
+    assert call(s=None) == NULLP and call(y=None) == NULLP
+    assert call(K=100) == DIMS and call(K=0) == DIMS and call(M=0) == DIMS and call(N=-1) == DIMS
+    assert call(G=96) == DIMS and call(G=32) == DIMS and call(K=192, G=128) == DIMS
+    assert call(a=ctypes.c_void_p(0x10008)) == DIMS and call(w=ctypes.c_void_p(0x10004)) == DIMS
+    assert call(sa=ctypes.c_void_p(0x10002)) == DIMS and call(s=ctypes.c_void_p(0x10001)) == DIMS
+    # 65537 rows pad to 65664: 65664 x 65536 bytes pass 2^32
+    assert call(M=65537, K=65536, G=64) == DIMS
+
+
 def test_gemm_w4a16_tiled_host_checks(lib):
     """Rearranged-weight entries: sizes, pointers and alignment checked on the host."""
     assert lib.taco_gemm_w4a16_tiled_bytes(0, 64) == 0 and lib.taco_gemm_w4a16_tiled_bytes(4, 100) == 0

@@ -433,3 +433,125 @@ def test_w8a16_argument_checks(torch_cuda):
         psv.taco_gemm_w8a16(a, w, s)
     with pytest.raises(ValueError):
         psv.taco_gemm_w8a16(a[:, :64].contiguous(), w[:, :64].contiguous(), s[:4].contiguous())
+
+
+# ------------------------------------------------------------------ W4A8
+# Bound per output, from the arithmetic: each group's products sum exactly in int32 (the weights
+# widen exactly to int8), the group scale multiplies the group sum in float32, the groups add in
+# float32, the activation scale multiplies the total and the result is rounded to bf16:
+#     |y - y_ref| <= 2^-8 |y_ref| + 2^-14 * S,   S = a_scale[m] sum_k |a_mk| |q_nk| w_scale[n, k / group]
+from workload.gemm import W4A8, make_w4a8, make_w4a8_device  # noqa: E402
+
+
+def run48(torch, g, rows=None):
+    import paged_speculative_verify_amd as psv
+    a = torch.from_numpy(np.ascontiguousarray(g.a_codes).view(np.int8)).cuda()
+    sa = torch.from_numpy(np.ascontiguousarray(g.a_scale)).cuda()
+    w = torch.from_numpy(np.ascontiguousarray(g.w_packed)).cuda()
+    s = torch.from_numpy(np.ascontiguousarray(g.w_scale)).cuda()
+    y = psv.taco_gemm_w4a8(a, sa, w, s, g.group)
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy().astype(np.float64)
+    return y if rows is None else y[rows]
+
+
+def bound48(a_codes, a_scale, w_packed, w_scale, group, y):
+    """(reference, bound) of W4A8 outputs, column chunk by column chunk."""
+    K = a_codes.shape[1]
+    A = np.abs(np.asarray(a_codes).view(np.int8).astype(np.float64)) * np.asarray(a_scale, np.float64)[:, None]
+    ref = np.empty(y.shape)
+    S = np.empty(y.shape)
+    for c0 in range(0, w_packed.shape[0], 4096):
+        c1 = min(c0 + 4096, w_packed.shape[0])
+        ref[:, c0:c1] = oracle.w4a8_gemm(a_codes, a_scale, w_packed[c0:c1], w_scale[c0:c1], group)
+        q = np.abs(oracle.decode_int4_packed(w_packed[c0:c1], K)).astype(np.float64)
+        S[:, c0:c1] = A @ (q * np.repeat(w_scale[c0:c1].astype(np.float64), group, axis=1)).T
+    return ref, 2.0 ** -8 * np.abs(ref) + 2.0 ** -14 * S
+
+
+def check48(g, y, rows=None):
+    sel = slice(None) if rows is None else rows
+    ref, bound = bound48(g.a_codes[sel], g.a_scale[sel], g.w_packed, g.w_scale, g.group, y)
+    err = np.abs(y - ref)
+    assert np.isfinite(y).all()
+    assert (err <= bound).all(), f"worst excess {float((err - bound).max())}"
+    return float((err / np.maximum(bound, 1e-30)).max())
+
+
+W48_CASES = [
+    ("one_by_one", 1, 1, 64, 64, 61),
+    ("ragged_small", 37, 200, 256, 128, 62),
+    ("ragged_tall", 130, 260, 384, 128, 63),
+    ("group64_tall", 300, 1100, 1024, 64, 64),
+    ("single_group", 70, 300, 512, 512, 65),
+    ("decode_rows", 64, 2048, 8192, 128, 66),
+]
+
+
+@pytest.mark.parametrize("cid,M,N,K,G,seed", W48_CASES, ids=[c[0] for c in W48_CASES])
+def test_w4a8_parity(torch_cuda, cid, M, N, K, G, seed):
+    g = make_w4a8(M, N, K, G, seed=seed)
+    say("w4a8", cid, M, N, K, G)
+    y = run48(torch_cuda, g)
+    r = check48(g, y)
+    say("w4a8", cid, "worst error / bound", r)
+
+
+def test_w4a8_full_size_sampled_rows(torch_cuda):
+    """Llama-3.1-70B gate+up at the verify step's 512 rows, group 128 (the timed shape): operands
+    drawn on the GPU, rows spanning both row tiles checked against the oracle."""
+    import torch
+    import paged_speculative_verify_amd as psv
+    s = LLAMA70B_GATE_UP
+    M, N, K, G = s["M"], s["N"], s["K"], 128
+    a, sa, w, sc = make_w4a8_device(M, N, K, G, seed=7, torch=torch)
+    rows = np.array([0, 127, 128, 300, 511])
+    say("w4a8 full size", s, "group", G, "rows", rows.tolist())
+    y = psv.taco_gemm_w4a8(a, sa, w, sc, G)
+    torch.cuda.synchronize()
+    yr = y.float().cpu().numpy().astype(np.float64)[rows]
+    ac = a.cpu().numpy().view(np.uint8)[rows]
+    ref, bound = bound48(ac, sa.cpu().numpy()[rows], w.cpu().numpy(), sc.cpu().numpy(), G, yr)
+    err = np.abs(yr - ref)
+    assert np.isfinite(yr).all()
+    assert (err <= bound).all(), f"worst excess {float((err - bound).max())}"
+
+
+@pytest.mark.parametrize("M,N,K,G", [(40, 90, 256, 128), (200, 300, 512, 64)], ids=["short_rows", "tall_rows"])
+def test_w4a8_integer_exact(torch_cuda, M, N, K, G):
+    """Full-range int8 activations (-128 included), every int4 code, power-of-two scales: every
+    group sum is exact in int32 and every scaled sum exact in float32, so the output is the bf16
+    rounding of the exact result."""
+    import torch
+    from workload.gemm import pack_int4
+    rng = np.random.default_rng(14)
+    ai = rng.integers(-128, 128, (M, K))
+    q = rng.integers(-8, 8, (N, K))
+    sa = (2.0 ** rng.integers(-3, 3, M)).astype(np.float32)
+    sc = (2.0 ** rng.integers(-3, 3, (N, K // G))).astype(np.float32)
+    g = W4A8(ai.astype(np.int8).view(np.uint8), sa, pack_int4(q), sc, G)
+    say("w4a8 integer exact", M, N, K, G)
+    y = run48(torch_cuda, g)
+    exact = np.zeros((M, N))
+    for gi in range(K // G):
+        ks = slice(gi * G, (gi + 1) * G)
+        exact += (ai[:, ks] @ q[:, ks].T).astype(np.float64) * sc[None, :, gi].astype(np.float64)
+    exact *= sa[:, None].astype(np.float64)
+    want = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(y, want)
+
+
+def test_w4a8_argument_checks(torch_cuda):
+    import torch
+    import paged_speculative_verify_amd as psv
+    a = torch.zeros((8, 192), dtype=torch.int8, device="cuda")
+    sa = torch.ones(8, dtype=torch.float32, device="cuda")
+    w = torch.zeros((8, 96), dtype=torch.uint8, device="cuda")
+    s = torch.ones((8, 3), dtype=torch.float32, device="cuda")
+    with pytest.raises(psv.PtaError):                     # group 32: not a multiple of 64
+        psv.taco_gemm_w4a8(a, sa, w, torch.ones((8, 6), dtype=torch.float32, device="cuda"), 32)
+    y = psv.taco_gemm_w4a8(a, sa, w, s, 64)               # K = 192, group 64: served
+    torch.cuda.synchronize()
+    assert float(y.float().abs().max()) == 0.0
+    with pytest.raises(ValueError):
+        psv.taco_gemm_w4a8(a.to(torch.bfloat16), sa, w, s, 64)

@@ -147,3 +147,50 @@ def make_w8a16_device(M: int, N: int, K: int, seed: int, torch, device="cuda"):
     codes = (x / scale[:, None]).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
     del x
     return a, codes, scale.contiguous()
+
+
+@dataclass
+class W4A8:
+    a_codes: np.ndarray    # uint8 [M, K] two's complement int8 codes
+    a_scale: np.ndarray    # float32 [M]
+    w_packed: np.ndarray   # uint8 [N, K / 2], as W4A16
+    w_scale: np.ndarray    # float32 [N, K / group]
+    group: int
+
+
+def _rowwise_int8(x: np.ndarray):
+    """Symmetric per-row int8 quantization: scale = max |x| / 127 (1.0 for an all-zero row),
+    code = round-half-even(x / scale) (|x / scale| <= 127 already)."""
+    amax = np.abs(x).max(axis=1)
+    scale = np.where(amax > 0, amax / 127.0, 1.0).astype(np.float32)
+    q = np.clip(np.rint(x / scale[:, None]), -127, 127).astype(np.int8)
+    return q.view(np.uint8), scale
+
+
+def make_w4a8(M: int, N: int, K: int, group: int = 128, seed: int = 0) -> W4A8:
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((M, K), dtype=np.float32)
+    w = rng.standard_normal((N, K), dtype=np.float32)
+    ac, asc = _rowwise_int8(a)
+    q, scale = quantize_int4_groups(w, group)
+    return W4A8(ac, asc, pack_int4(q), scale, group)
+
+
+def make_w4a8_device(M: int, N: int, K: int, group: int, seed: int, torch, device="cuda"):
+    """The same recipe drawn on the GPU: returns (a int8 [M, K], a_scale float32 [M], w_packed
+    uint8 [N, K / 2], w_scale float32 [N, K / group]) device tensors."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn((M, K), generator=g, device=device, dtype=torch.float32)
+    amax = x.abs().amax(dim=1)
+    a_scale = torch.where(amax > 0, amax / 127.0, torch.ones_like(amax))
+    a = torch.round(x / a_scale[:, None]).clamp(-127, 127).to(torch.int8).contiguous()
+    del x
+    w = torch.randn((N, K // group, group), generator=g, device=device, dtype=torch.float32)
+    wmax = w.abs().amax(dim=2)
+    w_scale = torch.where(wmax > 0, wmax / 7.0, torch.ones_like(wmax))
+    q = torch.round(w / w_scale[:, :, None]).clamp(-8, 7).to(torch.int32).reshape(N, K)
+    del w
+    u = (q & 0xF).to(torch.uint8)
+    packed = (u[:, 0::2] | (u[:, 1::2] << 4)).contiguous()
+    return a, a_scale.contiguous(), packed, w_scale.contiguous()
