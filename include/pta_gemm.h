@@ -128,6 +128,12 @@ pta_status taco_gemm_w8a16(const void* a, const void* w, const float* w_scale, v
 pta_status taco_gemm_w4a8(const void* a, const float* a_scale, const void* w, const float* w_scale, void* y,
                           int32_t M, int32_t N, int32_t K, int32_t group, void* stream);
 
+/* taco_gemm_w4a8 on weights rearranged by taco_gemm_w4a16_pack (the same
+ * nibble codes, so the same rearranged buffer serves both GEMMs): same
+ * arguments, limits, errors and results, bit for bit. */
+pta_status taco_gemm_w4a8_tiled(const void* a, const float* a_scale, const void* w_tiled, const float* w_scale,
+                                void* y, int32_t M, int32_t N, int32_t K, int32_t group, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -111,6 +111,8 @@ def load() -> ctypes.CDLL:
     lib.taco_gemm_w8a16.restype = ctypes.c_int
     lib.taco_gemm_w4a8.argtypes = [P, P, P, P, P, I32, I32, I32, I32, P]
     lib.taco_gemm_w4a8.restype = ctypes.c_int
+    lib.taco_gemm_w4a8_tiled.argtypes = [P, P, P, P, P, I32, I32, I32, I32, P]
+    lib.taco_gemm_w4a8_tiled.restype = ctypes.c_int
     lib.taco_gemm_w4a16_tiled_bytes.argtypes = [I32, I32]
     lib.taco_gemm_w4a16_tiled_bytes.restype = SZ
     lib.taco_gemm_w4a16_pack.argtypes = [P, P, I32, I32, P]
@@ -625,10 +627,11 @@ def taco_gemm_w8a16(a, w, w_scale, y=None, stream=None):
     return y
 
 
-def taco_gemm_w4a8(a, a_scale, w_packed, w_scale, group, y=None, stream=None):
+def taco_gemm_w4a8(a, a_scale, w_packed, w_scale, group, y=None, stream=None, tiled=None):
     """W4A8 GEMM (include/pta_gemm.h): a int8 [M, K] (or uint8 holding two's complement
     codes), a_scale float32 [M], w_packed uint8 [N, K / 2] (as taco_gemm_w4a16), w_scale float32
-    [N, K / group]; returns y bf16 [M, N] = a_scale[m] sum_k a[m, k] q[n, k] w_scale[n, k // group]."""
+    [N, K / group]; returns y bf16 [M, N] = a_scale[m] sum_k a[m, k] q[n, k] w_scale[n, k // group].
+    tiled=(N, K): w_packed is the 1-D output of taco_gemm_w4a16_pack (taco_gemm_w4a8_tiled)."""
     torch = _torch()
     _need(a, "a", 2)
     if a.dtype not in (torch.int8, torch.uint8):
@@ -637,10 +640,16 @@ def taco_gemm_w4a8(a, a_scale, w_packed, w_scale, group, y=None, stream=None):
     _need(a_scale, "a_scale", 1, torch.float32, a.device)
     if a_scale.numel() != M:
         raise ValueError("one scale per row of a")
-    _need(w_packed, "w_packed", 2, torch.uint8, a.device)
-    N = w_packed.shape[0]
-    if w_packed.shape[1] * 2 != K:
-        raise ValueError("w_packed must hold K / 2 bytes per row")
+    if tiled is not None:
+        N, Kt = (int(v) for v in tiled)
+        _need(w_packed, "w_packed", 1, torch.uint8, a.device)
+        if Kt != K or w_packed.numel() != int(load().taco_gemm_w4a16_tiled_bytes(N, K)):
+            raise ValueError("tiled weights must come from taco_gemm_w4a16_pack of an [N, K / 2] matrix")
+    else:
+        _need(w_packed, "w_packed", 2, torch.uint8, a.device)
+        N = w_packed.shape[0]
+        if w_packed.shape[1] * 2 != K:
+            raise ValueError("w_packed must hold K / 2 bytes per row")
     group = int(group)
     if group <= 0 or K % group:
         raise ValueError("group must divide K")
@@ -652,8 +661,9 @@ def taco_gemm_w4a8(a, a_scale, w_packed, w_scale, group, y=None, stream=None):
     _need(y, "y", 2, torch.bfloat16, a.device)
     if tuple(y.shape) != (M, N):
         raise ValueError("y must be [M, N]")
-    _check(load().taco_gemm_w4a8(a.data_ptr(), a_scale.data_ptr(), w_packed.data_ptr(), w_scale.data_ptr(),
-                                 y.data_ptr(), M, N, K, group, _stream(stream)))
+    fn = load().taco_gemm_w4a8_tiled if tiled is not None else load().taco_gemm_w4a8
+    _check(fn(a.data_ptr(), a_scale.data_ptr(), w_packed.data_ptr(), w_scale.data_ptr(), y.data_ptr(), M, N, K,
+              group, _stream(stream)))
     return y
 
 

@@ -735,7 +735,7 @@ __device__ __forceinline__ void int4x8_to_i8x16q(uint32_t w, uint32_t& k0to3, ui
   k4to7 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
 }
 
-template <int WM>
+template <int WM, bool TILED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w4a8_kernel(
     const uint8_t* a, const float* a_scale, const uint8_t* w, const float* w_scale, uint16_t* y, int M, int N, int K,
     int G, int tm, int tn) {
@@ -751,15 +751,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
   const int KG = K / G;                                     // groups per row
 
   const i32x4 ars = gemm_rsrc(a, (uint32_t)((uint64_t)M * (uint64_t)K));
-  const i32x4 wrs = gemm_rsrc(w, (uint32_t)((uint64_t)N * (uint64_t)K / 2u));
+  const i32x4 wrs = gemm_rsrc(w, TILED ? (uint32_t)((uint64_t)tn * 128u * (uint64_t)K / 2u)
+                                       : (uint32_t)((uint64_t)N * (uint64_t)K / 2u));
   const i32x4 srs = gemm_rsrc(w_scale, (uint32_t)((uint64_t)N * (uint64_t)KG * 4u));
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&lds[0];
 
   // copy lanes.  Activation chunk c (16 rows of 64 bytes): lane l fills row
   // 16 c + l / 4, physical unit l % 4, holding logical unit (l % 4) ^ ((l / 16) & 3).
-  // Weight chunk (32 rows of 32 bytes) as in W4A16.
+  // Weight chunk (32 rows of 32 bytes) as in W4A16, or (TILED) a contiguous
+  // 1 KiB piece of the stage's rearranged 4 KiB block.
   const uint32_t voffA = (uint32_t)((lane >> 2) * K + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
-  const uint32_t voffW = (uint32_t)((lane >> 1) * (K / 2) + 16 * ((lane & 1) ^ ((lane >> 4) & 1)));
+  const uint32_t voffW =
+      TILED ? (uint32_t)(16 * lane) : (uint32_t)((lane >> 1) * (K / 2) + 16 * ((lane & 1) ^ ((lane >> 4) & 1)));
   const int nk = K / Gm::BK, GS = G / Gm::BK;              // stages, stages per group
   auto copy_stage = [&](int s, int buf) {
     const uint32_t kb = (uint32_t)(s * Gm::BK);
@@ -769,6 +772,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
       if (c < Gm::CHUNKS_A)
         gemm_copy(lds0 + (uint32_t)(buf * Gm::A_TILE + c * 1024), ars, (uint32_t)(m0 + 16 * c) * (uint32_t)K + kb,
                   voffA);
+      else if (TILED)
+        gemm_copy(lds0 + (uint32_t)(Gm::W_REG + buf * Gm::W_TILE + (c - Gm::CHUNKS_A) * 1024), wrs,
+                  ((uint32_t)nt * (uint32_t)nk + (uint32_t)s) * 4096u + 1024u * (uint32_t)(c - Gm::CHUNKS_A), voffW);
       else
         gemm_copy(lds0 + (uint32_t)(Gm::W_REG + buf * Gm::W_TILE + (c - Gm::CHUNKS_A) * 1024), wrs,
                   (uint32_t)(n0 + 32 * (c - Gm::CHUNKS_A)) * (uint32_t)(K / 2) + kb / 2u, voffW);
@@ -955,8 +961,12 @@ pta_status taco_gemm_w4a16_tiled(const void* a, const void* w_tiled, const float
   return w4a16_call(a, w_tiled, w_scale, y, M, N, K, group, stream, true);
 }
 
-pta_status taco_gemm_w4a8(const void* a, const float* a_scale, const void* w, const float* w_scale, void* y,
-                          int32_t M, int32_t N, int32_t K, int32_t group, void* stream) {
+}  // extern "C"
+
+namespace {
+
+pta_status w4a8_call(const void* a, const float* a_scale, const void* w, const float* w_scale, void* y, int32_t M,
+                     int32_t N, int32_t K, int32_t group, void* stream, bool tiled) {
   if (!a || !a_scale || !w || !w_scale || !y) return PTA_ERR_NULL_PTR;
   if (M < 1 || N < 1 || K < 64 || K % 64 != 0 || group < 64 || group % 64 != 0 || K % group != 0)
     return PTA_ERR_BAD_DIMS;
@@ -979,9 +989,28 @@ pta_status taco_gemm_w4a8(const void* a, const float* a_scale, const void* w, co
                        reinterpret_cast<const uint8_t*>(a), a_scale, reinterpret_cast<const uint8_t*>(w), w_scale,
                        reinterpret_cast<uint16_t*>(y), M, N, K, group, tm, tn);
   };
-  if (tall) launch(gemm_w4a8_kernel<4>);
-  else launch(gemm_w4a8_kernel<2>);
+  if (tall) {
+    if (tiled) launch(gemm_w4a8_kernel<4, true>);
+    else launch(gemm_w4a8_kernel<4, false>);
+  } else {
+    if (tiled) launch(gemm_w4a8_kernel<2, true>);
+    else launch(gemm_w4a8_kernel<2, false>);
+  }
   return hipGetLastError() == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+pta_status taco_gemm_w4a8(const void* a, const float* a_scale, const void* w, const float* w_scale, void* y,
+                          int32_t M, int32_t N, int32_t K, int32_t group, void* stream) {
+  return w4a8_call(a, a_scale, w, w_scale, y, M, N, K, group, stream, false);
+}
+
+pta_status taco_gemm_w4a8_tiled(const void* a, const float* a_scale, const void* w_tiled, const float* w_scale,
+                                void* y, int32_t M, int32_t N, int32_t K, int32_t group, void* stream) {
+  return w4a8_call(a, a_scale, w_tiled, w_scale, y, M, N, K, group, stream, true);
 }
 
 pta_status taco_gemm_w8a16(const void* a, const void* w, const float* w_scale, void* y, int32_t M, int32_t N,

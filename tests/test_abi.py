@@ -260,6 +260,9 @@ def test_gemm_w4a8_host_checks(lib):
     assert call(sa=ctypes.c_void_p(0x10002)) == DIMS and call(s=ctypes.c_void_p(0x10001)) == DIMS
     # 65537 rows pad to 65664: 65664 x 65536 bytes pass 2^32
     assert call(M=65537, K=65536, G=64) == DIMS
+    t = lib.taco_gemm_w4a8_tiled
+    assert t(FAKE, FAKE, None, FAKE, FAKE, 4, 4, 256, 128, None) == NULLP
+    assert t(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 256, 96, None) == DIMS
 
 
 def test_gemm_w4a16_tiled_host_checks(lib):

@@ -443,13 +443,17 @@ def test_w8a16_argument_checks(torch_cuda):
 from workload.gemm import W4A8, make_w4a8, make_w4a8_device  # noqa: E402
 
 
-def run48(torch, g, rows=None):
+def run48(torch, g, rows=None, tiled=False):
     import paged_speculative_verify_amd as psv
     a = torch.from_numpy(np.ascontiguousarray(g.a_codes).view(np.int8)).cuda()
     sa = torch.from_numpy(np.ascontiguousarray(g.a_scale)).cuda()
     w = torch.from_numpy(np.ascontiguousarray(g.w_packed)).cuda()
     s = torch.from_numpy(np.ascontiguousarray(g.w_scale)).cuda()
-    y = psv.taco_gemm_w4a8(a, sa, w, s, g.group)
+    if tiled:
+        N, K = w.shape[0], w.shape[1] * 2
+        y = psv.taco_gemm_w4a8(a, sa, psv.taco_gemm_w4a16_pack(w), s, g.group, tiled=(N, K))
+    else:
+        y = psv.taco_gemm_w4a8(a, sa, w, s, g.group)
     torch.cuda.synchronize()
     y = y.float().cpu().numpy().astype(np.float64)
     return y if rows is None else y[rows]
@@ -497,6 +501,18 @@ def test_w4a8_parity(torch_cuda, cid, M, N, K, G, seed):
     say("w4a8", cid, "worst error / bound", r)
 
 
+@pytest.mark.parametrize("cid,M,N,K,G,seed", W48_CASES[:5], ids=[c[0] for c in W48_CASES[:5]])
+def test_w4a8_tiled_parity(torch_cuda, cid, M, N, K, G, seed):
+    """On weights rearranged by taco_gemm_w4a16_pack the W4A8 GEMM gives exactly the row-major
+    GEMM's output (itself checked against the oracle above) and stays within the oracle's bound."""
+    g = make_w4a8(M, N, K, G, seed=seed)
+    say("w4a8 tiled", cid, M, N, K, G)
+    y_t = run48(torch_cuda, g, tiled=True)
+    y_r = run48(torch_cuda, g)
+    assert np.array_equal(y_t, y_r)
+    check48(g, y_t)
+
+
 def test_w4a8_full_size_sampled_rows(torch_cuda):
     """Llama-3.1-70B gate+up at the verify step's 512 rows, group 128 (the timed shape): operands
     drawn on the GPU, rows spanning both row tiles checked against the oracle."""
@@ -508,7 +524,9 @@ def test_w4a8_full_size_sampled_rows(torch_cuda):
     rows = np.array([0, 127, 128, 300, 511])
     say("w4a8 full size", s, "group", G, "rows", rows.tolist())
     y = psv.taco_gemm_w4a8(a, sa, w, sc, G)
+    y_t = psv.taco_gemm_w4a8(a, sa, psv.taco_gemm_w4a16_pack(w), sc, G, tiled=(N, K))
     torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_t.view(torch.int16))     # the timed layout, whole output
     yr = y.float().cpu().numpy().astype(np.float64)[rows]
     ac = a.cpu().numpy().view(np.uint8)[rows]
     ref, bound = bound48(ac, sa.cpu().numpy()[rows], w.cpu().numpy(), sc.cpu().numpy(), G, yr)
