@@ -110,6 +110,26 @@ pta_status taco_gemm_w4a16_tiled(const void* a, const void* w_tiled, const float
 pta_status taco_gemm_w8a16(const void* a, const void* w, const float* w_scale, void* y, int32_t M, int32_t N,
                            int32_t K, void* stream);
 
+/* Weight-aware rearrangement of W8A16 weights (as for W4A16 above): the fp8
+ * codes of taco_gemm_w8a16 laid out in the GEMM's load order, so each 64-k
+ * step of a 128-column tile is one contiguous 8 KiB block instead of 64 bytes
+ * (half a cache line) of each of 128 rows.
+ *   taco_gemm_w8a16_tiled_bytes: size of the rearranged buffer for N x K
+ *     weights (N rounded up to 128 columns, zero filled), 0 when N < 1, K is
+ *     not a positive multiple of 64 or the size reaches 2^32.
+ *   taco_gemm_w8a16_pack: w (row-major [N][K]) into w_tiled (that many
+ *     bytes, caller-allocated); both 16-byte aligned, else PTA_ERR_BAD_DIMS;
+ *     bad N or K PTA_ERR_BAD_DIMS; NULL pointers PTA_ERR_NULL_PTR;
+ *     asynchronous on stream.  Block (t, s) of w_tiled, at byte
+ *     (t * K / 64 + s) * 8192, holds at byte 64 r + 16 p the 16 bytes of column
+ *     128 t + r at k-bytes 64 s + 16 (p ^ ((r >> 2) & 3)).
+ *   taco_gemm_w8a16_tiled: taco_gemm_w8a16 on the rearranged weights (same
+ *     arguments, limits, errors and results, bit for bit). */
+size_t taco_gemm_w8a16_tiled_bytes(int32_t N, int32_t K);
+pta_status taco_gemm_w8a16_pack(const void* w, void* w_tiled, int32_t N, int32_t K, void* stream);
+pta_status taco_gemm_w8a16_tiled(const void* a, const void* w_tiled, const float* w_scale, void* y, int32_t M,
+                                 int32_t N, int32_t K, void* stream);
+
 /* int8 x group-scaled int4 GEMM on the integer matrix cores
  * (v_mfma_i32_32x32x32_i8): the W4A8 operator the 17173xz.com article lists
  * ("TACO-LLM如何实现降本增效?"), with 8-bit integer activations (int4 weights

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     taco_gemm_w4a16_pack,
     taco_gemm_w8a8,
     taco_gemm_w8a16,
+    taco_gemm_w8a16_pack,
     taco_gemm_w4a8,
     taco_kv_append,
     taco_la_tree_mask,

@@ -109,6 +109,12 @@ def load() -> ctypes.CDLL:
     lib.taco_gemm_w4a16.restype = ctypes.c_int
     lib.taco_gemm_w8a16.argtypes = [P, P, P, P, I32, I32, I32, P]
     lib.taco_gemm_w8a16.restype = ctypes.c_int
+    lib.taco_gemm_w8a16_tiled_bytes.argtypes = [I32, I32]
+    lib.taco_gemm_w8a16_tiled_bytes.restype = SZ
+    lib.taco_gemm_w8a16_pack.argtypes = [P, P, I32, I32, P]
+    lib.taco_gemm_w8a16_pack.restype = ctypes.c_int
+    lib.taco_gemm_w8a16_tiled.argtypes = [P, P, P, P, I32, I32, I32, P]
+    lib.taco_gemm_w8a16_tiled.restype = ctypes.c_int
     lib.taco_gemm_w4a8.argtypes = [P, P, P, P, P, I32, I32, I32, I32, P]
     lib.taco_gemm_w4a8.restype = ctypes.c_int
     lib.taco_gemm_w4a8_tiled.argtypes = [P, P, P, P, P, I32, I32, I32, I32, P]
@@ -601,19 +607,44 @@ def taco_gemm_w8a8(a, a_scale, w, w_scale, y=None, stream=None):
     return y
 
 
-def taco_gemm_w8a16(a, w, w_scale, y=None, stream=None):
+def taco_gemm_w8a16_pack(w, stream=None):
+    """Weights of taco_gemm_w8a16 (uint8 [N, K] e4m3fn codes) rearranged into the GEMM's load
+    order (taco_gemm_w8a16_pack, include/pta_gemm.h); returns the new uint8 buffer: pass it to
+    taco_gemm_w8a16 with tiled=(N, K)."""
+    torch = _torch()
+    _need(w, "w", 2)
+    if w.element_size() != 1:
+        raise ValueError("w must hold 1-byte fp8 codes")
+    N, K = w.shape
+    lib = load()
+    nbytes = int(lib.taco_gemm_w8a16_tiled_bytes(N, K))
+    if nbytes == 0:
+        raise ValueError("N and K out of range for the rearranged layout")
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    _check(lib.taco_gemm_w8a16_pack(w.data_ptr(), out.data_ptr(), N, K, _stream(stream)))
+    return out
+
+
+def taco_gemm_w8a16(a, w, w_scale, y=None, stream=None, tiled=None):
     """W8A16 GEMM (include/pta_gemm.h): a bf16 [M, K], w uint8 [N, K] e4m3fn codes (or a
     float8_e4m3fn tensor), w_scale float32 [N]; returns y bf16 [M, N] =
-    w_scale[n] * sum_k a[m, k] dec(w[n, k])."""
+    w_scale[n] * sum_k a[m, k] dec(w[n, k]).  tiled=(N, K): w is the 1-D output of
+    taco_gemm_w8a16_pack (taco_gemm_w8a16_tiled)."""
     torch = _torch()
     _need(a, "a", 2, torch.bfloat16)
     M, K = a.shape
-    _need(w, "w", 2, device=a.device)
-    if w.element_size() != 1:
-        raise ValueError("w must hold 1-byte fp8 codes")
-    N = w.shape[0]
-    if w.shape[1] != K:
-        raise ValueError("a and w disagree on K")
+    if tiled is not None:
+        N, Kt = (int(v) for v in tiled)
+        _need(w, "w", 1, torch.uint8, a.device)
+        if Kt != K or w.numel() != int(load().taco_gemm_w8a16_tiled_bytes(N, K)):
+            raise ValueError("tiled weights must come from taco_gemm_w8a16_pack of an [N, K] matrix")
+    else:
+        _need(w, "w", 2, device=a.device)
+        if w.element_size() != 1:
+            raise ValueError("w must hold 1-byte fp8 codes")
+        N = w.shape[0]
+        if w.shape[1] != K:
+            raise ValueError("a and w disagree on K")
     _need(w_scale, "w_scale", 1, torch.float32, a.device)
     if w_scale.numel() != N:
         raise ValueError("one scale per row of w")
@@ -622,8 +653,8 @@ def taco_gemm_w8a16(a, w, w_scale, y=None, stream=None):
     _need(y, "y", 2, torch.bfloat16, a.device)
     if tuple(y.shape) != (M, N):
         raise ValueError("y must be [M, N]")
-    _check(load().taco_gemm_w8a16(a.data_ptr(), w.data_ptr(), w_scale.data_ptr(), y.data_ptr(), M, N, K,
-                                  _stream(stream)))
+    fn = load().taco_gemm_w8a16_tiled if tiled is not None else load().taco_gemm_w8a16
+    _check(fn(a.data_ptr(), w.data_ptr(), w_scale.data_ptr(), y.data_ptr(), M, N, K, _stream(stream)))
     return y
 
 

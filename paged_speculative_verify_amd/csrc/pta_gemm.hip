@@ -591,7 +591,25 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
                                                fp8x2_to_bf16x2<false>(hi), fp8x2_to_bf16x2<true>(hi)));
 }
 
-template <int WM>
+// Weight tiles of W8A16 in load order (taco_gemm_w8a16_pack): the 8 KiB block
+// of 128-column tile nt and 64-k stage s sits at byte (nt * (K / 64) + s) * 8192
+// and is the LDS image of that stage's weight tile: byte 64 r + 16 p holds the
+// 16 bytes of column 128 nt + r at k-bytes 64 s + 16 (p ^ ((r >> 2) & 3)) (zero
+// past N), so a stage arrives as eight contiguous 1 KiB copies of whole lines.
+__global__ __launch_bounds__(256) void w8a16_pack_kernel(const uint8_t* w, uint8_t* wt, int N, int K, int64_t units) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one 16-byte unit of the tiled buffer
+  if (u >= units) return;
+  const int nk = K / 64;
+  const int64_t blk = u >> 9;                                   // 512 units per 8 KiB block
+  const int within = (int)(u & 511), r = within >> 2, p = within & 3;
+  const int nt = (int)(blk / nk), st = (int)(blk % nk);
+  const int n = nt * 128 + r;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (n < N) v = *reinterpret_cast<const uint4*>(w + (int64_t)n * K + 64 * st + 16 * (p ^ ((r >> 2) & 3)));
+  *reinterpret_cast<uint4*>(wt + u * 16) = v;
+}
+
+template <int WM, bool TILED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w8a16_kernel(
     const uint16_t* a, const uint8_t* w, const float* w_scale, uint16_t* y, int M, int N, int K, int tm, int tn) {
   using Gm = W8Geom<WM>;
@@ -605,17 +623,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
   const int m0 = mt * BM, n0 = nt * BN;
 
   const i32x4 ars = gemm_rsrc(a, (uint32_t)((uint64_t)M * (uint64_t)K * 2u));
-  const i32x4 wrs = gemm_rsrc(w, (uint32_t)((uint64_t)N * (uint64_t)K));
+  const i32x4 wrs = gemm_rsrc(w, TILED ? (uint32_t)((uint64_t)tn * 128u * (uint64_t)K)
+                                       : (uint32_t)((uint64_t)N * (uint64_t)K));
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&lds[0];
 
   // copy lanes.  Activation chunk c (8 rows of 128 bytes) as in W4A16.  Weight
   // chunk c (16 rows of 64 bytes): lane l fills row 16 c + l / 4, physical unit
-  // l % 4, holding logical unit (l % 4) ^ ((row >> 2) & 3) = (l % 4) ^ ((l / 16) & 3).
+  // l % 4, holding logical unit (l % 4) ^ ((row >> 2) & 3) = (l % 4) ^ ((l / 16) & 3);
+  // TILED: a contiguous 1 KiB piece of the stage's rearranged 8 KiB block.
   uint32_t voffA[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par)
     voffA[par] = (uint32_t)((lane >> 3) * 2 * K + 16 * ((lane & 7) ^ ((4 * par + (lane >> 4)) & 7)));
-  const uint32_t voffW = (uint32_t)((lane >> 2) * K + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
+  const uint32_t voffW = TILED ? (uint32_t)(16 * lane) : (uint32_t)((lane >> 2) * K + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
   const int nk = K / Gm::BK;
   auto copy_stage = [&](int s, int buf) {
     const uint32_t kb = (uint32_t)(s * Gm::BK);
@@ -625,6 +645,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
       if (c < Gm::CHUNKS_A)
         gemm_copy(lds0 + (uint32_t)(buf * Gm::A_TILE + c * 1024), ars,
                   (uint32_t)(m0 + 8 * c) * (uint32_t)(2 * K) + 2u * kb, voffA[c & 1]);
+      else if (TILED)
+        gemm_copy(lds0 + (uint32_t)(Gm::W_REG + buf * Gm::W_TILE + (c - Gm::CHUNKS_A) * 1024), wrs,
+                  ((uint32_t)nt * (uint32_t)nk + (uint32_t)s) * 8192u + 1024u * (uint32_t)(c - Gm::CHUNKS_A), voffW);
       else
         gemm_copy(lds0 + (uint32_t)(Gm::W_REG + buf * Gm::W_TILE + (c - Gm::CHUNKS_A) * 1024), wrs,
                   (uint32_t)(n0 + 16 * (c - Gm::CHUNKS_A)) * (uint32_t)K + kb, voffW);
@@ -1013,8 +1036,12 @@ pta_status taco_gemm_w4a8_tiled(const void* a, const float* a_scale, const void*
   return w4a8_call(a, a_scale, w_tiled, w_scale, y, M, N, K, group, stream, true);
 }
 
-pta_status taco_gemm_w8a16(const void* a, const void* w, const float* w_scale, void* y, int32_t M, int32_t N,
-                           int32_t K, void* stream) {
+}  // extern "C"
+
+namespace {
+
+pta_status w8a16_call(const void* a, const void* w, const float* w_scale, void* y, int32_t M, int32_t N, int32_t K,
+                      void* stream, bool tiled) {
   if (!a || !w || !w_scale || !y) return PTA_ERR_NULL_PTR;
   if (M < 1 || N < 1 || K < 64 || K % 64 != 0) return PTA_ERR_BAD_DIMS;
   if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(w)) % 16 != 0 ||
@@ -1035,9 +1062,45 @@ pta_status taco_gemm_w8a16(const void* a, const void* w, const float* w_scale, v
                        reinterpret_cast<const uint16_t*>(a), reinterpret_cast<const uint8_t*>(w), w_scale,
                        reinterpret_cast<uint16_t*>(y), M, N, K, tm, tn);
   };
-  if (tall) launch(gemm_w8a16_kernel<4>);
-  else launch(gemm_w8a16_kernel<2>);
+  if (tall) {
+    if (tiled) launch(gemm_w8a16_kernel<4, true>);
+    else launch(gemm_w8a16_kernel<4, false>);
+  } else {
+    if (tiled) launch(gemm_w8a16_kernel<2, true>);
+    else launch(gemm_w8a16_kernel<2, false>);
+  }
   return hipGetLastError() == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+pta_status taco_gemm_w8a16(const void* a, const void* w, const float* w_scale, void* y, int32_t M, int32_t N,
+                           int32_t K, void* stream) {
+  return w8a16_call(a, w, w_scale, y, M, N, K, stream, false);
+}
+
+size_t taco_gemm_w8a16_tiled_bytes(int32_t N, int32_t K) {
+  if (N < 1 || K < 64 || K % 64 != 0) return 0;
+  const uint64_t bytes = (uint64_t)((N + 127) / 128) * 128u * (uint64_t)K;
+  return bytes < ((uint64_t)1 << 32) ? (size_t)bytes : 0;
+}
+
+pta_status taco_gemm_w8a16_pack(const void* w, void* w_tiled, int32_t N, int32_t K, void* stream) {
+  if (!w || !w_tiled) return PTA_ERR_NULL_PTR;
+  const size_t bytes = taco_gemm_w8a16_tiled_bytes(N, K);
+  if (bytes == 0) return PTA_ERR_BAD_DIMS;
+  if ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(w_tiled)) % 16 != 0) return PTA_ERR_BAD_DIMS;
+  const int64_t units = (int64_t)(bytes / 16);
+  hipLaunchKernelGGL(w8a16_pack_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                     reinterpret_cast<const uint8_t*>(w), reinterpret_cast<uint8_t*>(w_tiled), N, K, units);
+  return hipGetLastError() == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+}
+
+pta_status taco_gemm_w8a16_tiled(const void* a, const void* w_tiled, const float* w_scale, void* y, int32_t M,
+                                 int32_t N, int32_t K, void* stream) {
+  return w8a16_call(a, w_tiled, w_scale, y, M, N, K, stream, true);
 }
 
 }  // extern "C"

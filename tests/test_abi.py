@@ -243,6 +243,16 @@ def test_gemm_w8a16_host_checks(lib):
     assert call(N=65409, K=65536) == DIMS
     # 32769 rows pad to 32896: 32896 x 2 x 65536 bytes pass 2^32
     assert call(M=32769, K=65536) == DIMS
+    assert lib.taco_gemm_w8a16_tiled_bytes(0, 64) == 0 and lib.taco_gemm_w8a16_tiled_bytes(4, 100) == 0
+    assert lib.taco_gemm_w8a16_tiled_bytes(4, 128) == 128 * 128           # N padded to 128 columns
+    assert lib.taco_gemm_w8a16_tiled_bytes(57344, 8192) == 57344 * 8192
+    assert lib.taco_gemm_w8a16_tiled_bytes(1 << 19, 1 << 13) == 0         # 2^32 bytes
+    pack = lib.taco_gemm_w8a16_pack
+    assert pack(None, FAKE, 4, 128, None) == NULLP and pack(FAKE, None, 4, 128, None) == NULLP
+    assert pack(FAKE, FAKE, 4, 100, None) == DIMS and pack(FAKE, FAKE, 0, 128, None) == DIMS
+    assert pack(ctypes.c_void_p(0x10008), FAKE, 4, 128, None) == DIMS
+    t = lib.taco_gemm_w8a16_tiled
+    assert t(FAKE, None, FAKE, FAKE, 4, 4, 128, None) == NULLP and t(FAKE, FAKE, FAKE, FAKE, 4, 4, 100, None) == DIMS
 
 
 def test_gemm_w4a8_host_checks(lib):

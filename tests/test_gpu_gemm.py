@@ -322,12 +322,15 @@ def test_w4a16_argument_checks(torch_cuda):
 from workload.gemm import W8A16, make_w8a16, make_w8a16_device  # noqa: E402
 
 
-def run8(torch, g, rows=None):
+def run8(torch, g, rows=None, tiled=False):
     import paged_speculative_verify_amd as psv
     a = torch.from_numpy(np.ascontiguousarray(g.a_bits).view(np.int16)).cuda().view(torch.bfloat16)
     w = torch.from_numpy(np.ascontiguousarray(g.w_codes)).cuda()
     s = torch.from_numpy(np.ascontiguousarray(g.w_scale)).cuda()
-    y = psv.taco_gemm_w8a16(a, w, s)
+    if tiled:
+        y = psv.taco_gemm_w8a16(a, psv.taco_gemm_w8a16_pack(w), s, tiled=tuple(w.shape))
+    else:
+        y = psv.taco_gemm_w8a16(a, w, s)
     torch.cuda.synchronize()
     y = y.float().cpu().numpy().astype(np.float64)
     return y if rows is None else y[rows]
@@ -373,6 +376,43 @@ def test_w8a16_parity(torch_cuda, cid, M, N, K, seed):
     say("w8a16", cid, "worst error / bound", r)
 
 
+def tiled_layout8(w_codes):
+    """The rearranged W8A16 buffer as include/pta_gemm.h defines it, built with numpy loops over
+    its blocks: block (t, s) at byte (t * K / 64 + s) * 8192 holds at byte 64 r + 16 p the 16
+    bytes of column 128 t + r at k-bytes 64 s + 16 (p ^ ((r >> 2) & 3)), zero past N."""
+    N, K = w_codes.shape
+    T, S = (N + 127) // 128, K // 64
+    out = np.zeros(T * S * 8192, np.uint8)
+    for t in range(T):
+        for st in range(S):
+            blk = out[(t * S + st) * 8192:(t * S + st + 1) * 8192].reshape(128, 4, 16)
+            for r in range(128):
+                n = 128 * t + r
+                if n >= N:
+                    continue
+                for p in range(4):
+                    u = p ^ ((r >> 2) & 3)
+                    blk[r, p] = w_codes[n, 64 * st + 16 * u:64 * st + 16 * u + 16]
+    return out
+
+
+@pytest.mark.parametrize("cid,M,N,K,seed", W8_CASES[:4], ids=[c[0] for c in W8_CASES[:4]])
+def test_w8a16_tiled_parity(torch_cuda, cid, M, N, K, seed):
+    """The rearranged weights match the header's layout byte for byte, and the GEMM on them
+    gives exactly the row-major GEMM's output and stays within the oracle's bound."""
+    import torch
+    import paged_speculative_verify_amd as psv
+    g = make_w8a16(M, N, K, seed=seed)
+    say("w8a16 tiled", cid, M, N, K)
+    wt = psv.taco_gemm_w8a16_pack(torch.from_numpy(np.ascontiguousarray(g.w_codes)).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(wt.cpu().numpy(), tiled_layout8(g.w_codes))
+    y_t = run8(torch_cuda, g, tiled=True)
+    y_r = run8(torch_cuda, g)
+    assert np.array_equal(y_t, y_r)
+    check8(g, y_t)
+
+
 def test_w8a16_full_size_sampled_rows(torch_cuda):
     """Llama-3.1-70B gate+up at the verify step's 512 rows (the timed shape): operands drawn on
     the GPU, rows spanning both row tiles and the ragged-free edge checked against the oracle."""
@@ -384,7 +424,9 @@ def test_w8a16_full_size_sampled_rows(torch_cuda):
     rows = np.array([0, 127, 128, 300, 511])
     say("w8a16 full size", s, "rows", rows.tolist())
     y = psv.taco_gemm_w8a16(a, w, sc)
+    y_t = psv.taco_gemm_w8a16(a, psv.taco_gemm_w8a16_pack(w), sc, tiled=(N, K))
     torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_t.view(torch.int16))     # the timed layout, whole output
     yr = y.float().cpu().numpy().astype(np.float64)[rows]
     a_bits = a.view(torch.int16).cpu().numpy().view(np.uint16)[rows]
     ref, bound = bound8(a_bits, w.cpu().numpy(), sc.cpu().numpy(), yr)
