@@ -37,7 +37,7 @@ def test_verify_step_end_to_end(kv, seed):
     L = (w.ctx_lens - w.q_lens).astype(np.int32)
 
     streams = synthetic_streams(B, H + Qmax + 1, vocab=60, seed=seed)
-    cache = psv.LookaheadCache(12, 6)
+    cache = psv.LookaheadCache(12, 6, threads=3 if kv == "fp8" else 1)   # the threaded cache on one case
     cache.append_batch(range(B), [s[:H] for s in streams])
     tok, par, cnt = cache.propose(range(B), [Qmax] * B, Qmax)
     for b in range(B):                        # nothing matched: a single guess, as plain decode would verify
