@@ -172,6 +172,7 @@ def cmd_trace(a) -> int:
 # MI355X: 256 compute units in 8 XCDs, 4 SIMDs each; dense bf16 MFMA peak at 2.4 GHz
 NUM_CU, NUM_XCD, SIMD_PER_CU = 256, 8, 4
 BF16_PEAK_FLOPS = 2.5e15
+I8_PEAK_OPS = 5.0e15
 
 
 def cmd_sq(a) -> int:
@@ -210,6 +211,10 @@ def cmd_sq(a) -> int:
         fl = 512 * m["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
         derived.append(("bf16 MFMA flops per dispatch (512 x MOPS)", f"{fl:.4g}"))
         derived.append(("bf16 MFMA rate", f"{fl / dur_s / 1e12:.0f} TFLOP/s ({100 * fl / dur_s / BF16_PEAK_FLOPS:.1f}% of 2.5 PFLOP/s)"))
+    if "SQ_INSTS_VALU_MFMA_MOPS_I8" in m:
+        ops = 512 * m["SQ_INSTS_VALU_MFMA_MOPS_I8"]
+        derived.append(("int8 MFMA ops per dispatch (512 x MOPS)", f"{ops:.4g}"))
+        derived.append(("int8 MFMA rate", f"{ops / dur_s / 1e12:.0f} TOP/s ({100 * ops / dur_s / I8_PEAK_OPS:.1f}% of 5 POP/s)"))
     if "SQ_WAVE_CYCLES" in m:
         for k, label in (("SQ_ACTIVE_INST_ANY", "wave cycles issuing any instruction"),
                          ("SQ_ACTIVE_INST_VALU", "wave cycles issuing VALU"),
