@@ -58,8 +58,11 @@ void taco_la_destroy(taco_la_cache* cache);
  * global counts (strings grouped by their first token); a query batch into one
  * task per sequence.  Results do not depend on n.  Idle workers spin for about
  * a millisecond before they sleep (a call after a longer pause first wakes
- * them).  PTA_ERR_BAD_DIMS for n outside 1 .. 64; PTA_ERR_UNSUPPORTED when the
- * system refuses a thread (the cache is then left with 1). */
+ * them).  A child process after fork() finds none of the workers: there the
+ * cache runs on the calling thread (and reports 1) until taco_la_set_threads
+ * starts new ones.  PTA_ERR_BAD_DIMS for n outside 1 .. 64;
+ * PTA_ERR_UNSUPPORTED when the system refuses a thread (the cache is then left
+ * with 1). */
 pta_status taco_la_set_threads(taco_la_cache* cache, int32_t n);
 
 /* The cache's thread count (0 for a NULL cache). */

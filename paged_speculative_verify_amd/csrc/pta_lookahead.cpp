@@ -32,6 +32,7 @@
 #include <queue>
 #include <system_error>
 #include <thread>
+#include <unistd.h>
 #include <unordered_map>
 #include <utility>
 #include <vector>
@@ -177,10 +178,16 @@ void run_walks(Trie& t, std::vector<Walk>& ws) {
 class Pool {
  public:
   ~Pool() { resize(1); }
-  int size() const { return (int)workers_.size() + 1; }
+  int size() const { return orphaned() ? 1 : (int)workers_.size() + 1; }
 
   // false when the system refuses a thread (the pool then keeps none)
   bool resize(int n) {
+    if (orphaned()) {
+      // a child process after fork() has none of the parent's workers: their
+      // handles are set aside unused (joining them here would wait forever)
+      (void)new std::vector<std::thread>(std::move(workers_));
+      workers_.clear();
+    }
     if (!workers_.empty()) {
       {
         std::lock_guard<std::mutex> lk(m_);
@@ -195,6 +202,7 @@ class Pool {
     // the batch number a worker starts from is taken here, not by the new
     // thread, which may first run after the next batch is published
     const uint64_t g0 = gen(state_.load(std::memory_order_acquire));
+    owner_ = getpid();
     try {
       for (int i = 1; i < n; ++i) workers_.emplace_back([this, g0] { loop(g0); });
     } catch (const std::system_error&) {
@@ -206,7 +214,7 @@ class Pool {
 
   // f(i) for every i in [0, count), in any order over the threads
   void run(int64_t count, const std::function<void(int64_t)>& f) {
-    if (workers_.empty() || count <= 1) {
+    if (workers_.empty() || count <= 1 || orphaned()) {
       for (int64_t i = 0; i < count; ++i) f(i);
       return;
     }
@@ -244,6 +252,8 @@ class Pool {
     return (g & 0xffffff) << 40 | count << 20 | next;
   }
   static uint64_t gen(uint64_t s) { return s >> 40; }
+  // the workers belong to another process (this one is a child after fork())
+  bool orphaned() const { return !workers_.empty() && getpid() != owner_; }
 
   void drain(uint64_t g) {
     uint64_t s = state_.load(std::memory_order_acquire);
@@ -275,6 +285,7 @@ class Pool {
   }
 
   std::vector<std::thread> workers_;
+  pid_t owner_ = 0;   // the process the workers were started in
   std::mutex m_;
   std::condition_variable cv_;
   std::atomic<uint64_t> state_{0};

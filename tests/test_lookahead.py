@@ -420,3 +420,37 @@ def test_bench_lookahead_line(capsys):
     assert line["threads"] == 3 and line["value"] > 0 and line["unit"] == "trees/s"
     for k in ("back_to_back", "back_to_back_one_thread", "in_loop", "in_loop_one_thread"):
         assert line[k]["value"] > 0
+
+
+def test_threaded_cache_in_a_forked_child():
+    """A child process after fork() has none of the cache's workers: its calls run on the calling
+    thread, give the parent's results, and taco_la_set_threads can start new workers there."""
+    import multiprocessing as mp
+    streams = synthetic_streams(4, 300, vocab=20, seed=71)
+    c = psv.LookaheadCache(8, 4, threads=4)
+    c.append_batch(range(4), streams)
+    want = c.propose(range(4), [6] * 4, 6)
+    ctx = mp.get_context("fork")
+    q = ctx.Queue()
+
+    def child():
+        try:
+            n0 = c.threads
+            got = c.propose(range(4), [6] * 4, 6)
+            c.append_batch(range(4), [s[:5] for s in streams])
+            c.set_threads(3)
+            again = c.propose(range(4), [6] * 4, 6)
+            q.put((n0, c.threads, [x.tolist() for x in got], [x.tolist() for x in again]))
+        except Exception as e:          # reported to the parent
+            q.put(repr(e))
+
+    p = ctx.Process(target=child)
+    p.start()
+    out = q.get(timeout=60)
+    p.join(timeout=60)
+    assert not isinstance(out, str), out
+    n0, n1, got, again = out
+    assert n0 == 1 and n1 == 3
+    assert all(np.array_equal(np.array(g), w) for g, w in zip(got, want))
+    assert p.exitcode == 0
+    assert c.threads == 4                            # the parent keeps its workers
