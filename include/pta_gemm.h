@@ -130,6 +130,14 @@ pta_status taco_gemm_w8a16_pack(const void* w, void* w_tiled, int32_t N, int32_t
 pta_status taco_gemm_w8a16_tiled(const void* a, const void* w_tiled, const float* w_scale, void* y, int32_t M,
                                  int32_t N, int32_t K, void* stream);
 
+/* taco_gemm_w8a8 on weights rearranged by taco_gemm_w8a16_pack (the same fp8
+ * codes and the same layout: each block is also the W8A8 kernels' image of a
+ * 64-k stage of 128 columns).  Same arguments, limits, errors and results as
+ * taco_gemm_w8a8, bit for bit; past 256 rows it runs the 64-k-step kernel
+ * where taco_gemm_w8a8 runs the 128-k-step one (the sums are the same). */
+pta_status taco_gemm_w8a8_tiled(const void* a, const float* a_scale, const void* w_tiled, const float* w_scale,
+                                void* y, int32_t M, int32_t N, int32_t K, void* stream);
+
 /* int8 x group-scaled int4 GEMM on the integer matrix cores
  * (v_mfma_i32_32x32x32_i8): the W4A8 operator the 17173xz.com article lists
  * ("TACO-LLM如何实现降本增效?"), with 8-bit integer activations (int4 weights

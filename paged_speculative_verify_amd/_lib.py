@@ -115,6 +115,8 @@ def load() -> ctypes.CDLL:
     lib.taco_gemm_w8a16_pack.restype = ctypes.c_int
     lib.taco_gemm_w8a16_tiled.argtypes = [P, P, P, P, I32, I32, I32, P]
     lib.taco_gemm_w8a16_tiled.restype = ctypes.c_int
+    lib.taco_gemm_w8a8_tiled.argtypes = [P, P, P, P, P, I32, I32, I32, P]
+    lib.taco_gemm_w8a8_tiled.restype = ctypes.c_int
     lib.taco_gemm_w4a8.argtypes = [P, P, P, P, P, I32, I32, I32, I32, P]
     lib.taco_gemm_w4a8.restype = ctypes.c_int
     lib.taco_gemm_w4a8_tiled.argtypes = [P, P, P, P, P, I32, I32, I32, I32, P]
@@ -581,18 +583,27 @@ def taco_pta_calib_mfma_bf16(workgroups: int, iters: int, sink, stream=None) -> 
     return workgroups * 4 * iters * 4 * 32 * 32 * 16 * 2
 
 
-def taco_gemm_w8a8(a, a_scale, w, w_scale, y=None, stream=None):
+def taco_gemm_w8a8(a, a_scale, w, w_scale, y=None, stream=None, tiled=None):
     """W8A8 GEMM (include/pta_gemm.h): a uint8 [M, K] and w uint8 [N, K] e4m3fn codes (or
-    float8_e4m3fn tensors), float32 scales [M] and [N]; returns y bf16 [M, N]."""
+    float8_e4m3fn tensors), float32 scales [M] and [N]; returns y bf16 [M, N].  tiled=(N, K): w
+    is the 1-D output of taco_gemm_w8a16_pack (taco_gemm_w8a8_tiled)."""
     torch = _torch()
-    for t, n in ((a, "a"), (w, "w")):
-        _need(t, n, 2)
-        if t.element_size() != 1:
-            raise ValueError(f"{n} must hold 1-byte fp8 codes")
+    _need(a, "a", 2)
+    if a.element_size() != 1:
+        raise ValueError("a must hold 1-byte fp8 codes")
     M, K = a.shape
-    N = w.shape[0]
-    if w.shape[1] != K:
-        raise ValueError("a and w disagree on K")
+    if tiled is not None:
+        N, Kt = (int(v) for v in tiled)
+        _need(w, "w", 1, torch.uint8, a.device)
+        if Kt != K or w.numel() != int(load().taco_gemm_w8a16_tiled_bytes(N, K)):
+            raise ValueError("tiled weights must come from taco_gemm_w8a16_pack of an [N, K] matrix")
+    else:
+        _need(w, "w", 2)
+        if w.element_size() != 1:
+            raise ValueError("w must hold 1-byte fp8 codes")
+        N = w.shape[0]
+        if w.shape[1] != K:
+            raise ValueError("a and w disagree on K")
     _need(a_scale, "a_scale", 1, torch.float32, a.device)
     _need(w_scale, "w_scale", 1, torch.float32, a.device)
     if a_scale.numel() != M or w_scale.numel() != N:
@@ -602,8 +613,9 @@ def taco_gemm_w8a8(a, a_scale, w, w_scale, y=None, stream=None):
     _need(y, "y", 2, torch.bfloat16, a.device)
     if tuple(y.shape) != (M, N):
         raise ValueError("y must be [M, N]")
-    _check(load().taco_gemm_w8a8(a.data_ptr(), a_scale.data_ptr(), w.data_ptr(), w_scale.data_ptr(), y.data_ptr(),
-                                 M, N, K, _stream(stream)))
+    fn = load().taco_gemm_w8a8_tiled if tiled is not None else load().taco_gemm_w8a8
+    _check(fn(a.data_ptr(), a_scale.data_ptr(), w.data_ptr(), w_scale.data_ptr(), y.data_ptr(), M, N, K,
+              _stream(stream)))
     return y
 
 

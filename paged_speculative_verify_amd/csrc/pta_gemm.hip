@@ -114,7 +114,7 @@ __device__ __forceinline__ void gemm_static_for(F&& f) {
   }
 }
 
-template <int WNB, int WMW>
+template <int WNB, int WMW, bool TILED = false>
 __global__ __launch_bounds__(128 * WMW) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w8a8_kernel(
     const uint8_t* a, const float* a_scale, const uint8_t* w, const float* w_scale, uint16_t* y, int M, int N,
     int K, int tm, int tn) {
@@ -133,11 +133,15 @@ __global__ __launch_bounds__(128 * WMW) __attribute__((amdgpu_waves_per_eu(2))) 
   const int m0 = mt * BM, n0 = nt * BN;
 
   const i32x4 ars = gemm_rsrc(a, (uint32_t)((uint64_t)M * (uint64_t)K));
-  const i32x4 wrs = gemm_rsrc(w, (uint32_t)((uint64_t)N * (uint64_t)K));
+  // TILED: weights rearranged by taco_gemm_w8a16_pack, whose 8 KiB block per
+  // (128-column tile, 64-k stage) is this kernel's LDS image of those columns
+  const i32x4 wrs = gemm_rsrc(w, TILED ? (uint32_t)((uint64_t)((N + 127) / 128) * 128u * (uint64_t)K)
+                                       : (uint32_t)((uint64_t)N * (uint64_t)K));
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&lds[0];
   // copy lanes: row l / 4 of a chunk, physical unit l % 4 holding logical unit
   // (l % 4) ^ ((row >> 2) & 3), with row >> 2 & 3 = (l / 16) & 3 for every chunk
   const uint32_t voff = (uint32_t)((lane >> 2) * K + ((((lane & 3) ^ ((lane >> 4) & 3))) << 4));
+  const uint32_t voffT = (uint32_t)(16 * lane);
   const int nk = K / BK;
   auto copy_stage = [&](int s, int buf) {
     const uint32_t kb = (uint32_t)(s * BK);
@@ -146,7 +150,12 @@ __global__ __launch_bounds__(128 * WMW) __attribute__((amdgpu_waves_per_eu(2))) 
       const int c = wave + NWAVES * i;             // chunk c of the stage: A chunks, then W chunks
       if (i < Gm::CHUNKS_A / NWAVES)               // (whole rounds of A chunks: known per i)
         gemm_copy(lds0 + (uint32_t)(buf * A_TILE + c * 1024), ars, (uint32_t)(m0 + 16 * c) * (uint32_t)K + kb, voff);
-      else
+      else if (TILED) {                            // chunk cw: block of columns n0 + 128 (cw / 8) on
+        const int cw = c - Gm::CHUNKS_A;
+        gemm_copy(lds0 + (uint32_t)(W_REG + buf * W_TILE + cw * 1024), wrs,
+                  ((uint32_t)(n0 / 128 + (cw >> 3)) * (uint32_t)nk + (uint32_t)s) * 8192u + 1024u * (uint32_t)(cw & 7),
+                  voffT);
+      } else
         gemm_copy(lds0 + (uint32_t)(W_REG + buf * W_TILE + (c - Gm::CHUNKS_A) * 1024), wrs,
                   (uint32_t)(n0 + 16 * (c - Gm::CHUNKS_A)) * (uint32_t)K + kb, voff);
     }
@@ -887,8 +896,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
 
 extern "C" {
 
-pta_status taco_gemm_w8a8(const void* a, const float* a_scale, const void* w, const float* w_scale, void* y,
-                          int32_t M, int32_t N, int32_t K, void* stream) {
+}  // extern "C"
+
+namespace {
+
+pta_status w8a8_call(const void* a, const float* a_scale, const void* w, const float* w_scale, void* y, int32_t M,
+                     int32_t N, int32_t K, void* stream, bool tiled) {
   if (!a || !a_scale || !w || !w_scale || !y) return PTA_ERR_NULL_PTR;
   if (M < 1 || N < 1 || K < BK || K % BK != 0) return PTA_ERR_BAD_DIMS;
   // every tile row (those past M or N included) must have a 32-bit buffer offset
@@ -908,11 +921,34 @@ pta_status taco_gemm_w8a8(const void* a, const float* a_scale, const void* w, co
                        reinterpret_cast<const uint8_t*>(a), a_scale, reinterpret_cast<const uint8_t*>(w), w_scale,
                        reinterpret_cast<uint16_t*>(y), M, N, K, tm, tn);
   };
-  if (kind == 2 && K % 128 == 0) launch(gemm_w8a8_k128_kernel, GemmK128<0>::NT);
-  else if (kind == 2) launch(gemm_w8a8_kernel<4, 4>, GemmGeom<4, 4>::NT);
-  else if (kind == 1) launch(gemm_w8a8_kernel<4, 2>, GemmGeom<4, 2>::NT);
-  else launch(gemm_w8a8_kernel<2, 2>, GemmGeom<2, 2>::NT);
+  if (tiled) {   // the 64-k kernels only: the 128-k kernel stages 128-byte rows
+    if (kind == 2) launch(gemm_w8a8_kernel<4, 4, true>, GemmGeom<4, 4>::NT);
+    else if (kind == 1) launch(gemm_w8a8_kernel<4, 2, true>, GemmGeom<4, 2>::NT);
+    else launch(gemm_w8a8_kernel<2, 2, true>, GemmGeom<2, 2>::NT);
+  } else if (kind == 2 && K % 128 == 0) {
+    launch(gemm_w8a8_k128_kernel, GemmK128<0>::NT);
+  } else if (kind == 2) {
+    launch(gemm_w8a8_kernel<4, 4>, GemmGeom<4, 4>::NT);
+  } else if (kind == 1) {
+    launch(gemm_w8a8_kernel<4, 2>, GemmGeom<4, 2>::NT);
+  } else {
+    launch(gemm_w8a8_kernel<2, 2>, GemmGeom<2, 2>::NT);
+  }
   return hipGetLastError() == hipSuccess ? PTA_OK : PTA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+pta_status taco_gemm_w8a8(const void* a, const float* a_scale, const void* w, const float* w_scale, void* y,
+                          int32_t M, int32_t N, int32_t K, void* stream) {
+  return w8a8_call(a, a_scale, w, w_scale, y, M, N, K, stream, false);
+}
+
+pta_status taco_gemm_w8a8_tiled(const void* a, const float* a_scale, const void* w_tiled, const float* w_scale,
+                                void* y, int32_t M, int32_t N, int32_t K, void* stream) {
+  return w8a8_call(a, a_scale, w_tiled, w_scale, y, M, N, K, stream, true);
 }
 
 }  // extern "C"

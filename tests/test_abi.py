@@ -226,6 +226,9 @@ def test_gemm_host_checks(lib):
     assert call(M=1 << 20, K=1 << 13) == DIMS                       # rows x K past 32-bit offsets
     # 66817 rows pad to 67072 in 256-row tiles: 67072 x 64064 passes 2^32 (66944 x 64064 would not)
     assert call(M=66817, K=64064) == DIMS
+    t = lib.taco_gemm_w8a8_tiled
+    assert t(FAKE, FAKE, None, FAKE, FAKE, 4, 4, 128, None) == NULLP
+    assert t(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 100, None) == DIMS
 
 
 def test_gemm_w8a16_host_checks(lib):

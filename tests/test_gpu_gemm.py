@@ -78,6 +78,23 @@ def test_w8a8_parity(torch_cuda, cid, M, N, K, seed):
     say(cid, "worst error / bound", r)
 
 
+@pytest.mark.parametrize("cid,M,N,K,seed", CASES, ids=[c[0] for c in CASES])
+def test_w8a8_tiled_equals_row_major(torch_cuda, cid, M, N, K, seed):
+    """On weights rearranged by taco_gemm_w8a16_pack the W8A8 GEMM gives exactly the row-major
+    entry's output (itself checked against the oracle above), for every tile width, 128-column
+    tiles reading one block per stage and 256-column tiles two."""
+    import torch
+    import paged_speculative_verify_amd as psv
+    g = make_w8a8(M, N, K, seed=seed)
+    say("w8a8 tiled", cid, M, N, K)
+    T = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    a, sa, w, sw = T(g.a_codes), T(g.a_scale), T(g.w_codes), T(g.w_scale)
+    y_r = psv.taco_gemm_w8a8(a, sa, w, sw)
+    y_t = psv.taco_gemm_w8a8(a, sa, psv.taco_gemm_w8a16_pack(w), sw, tiled=(N, K))
+    torch.cuda.synchronize()
+    assert torch.equal(y_r.view(torch.int16), y_t.view(torch.int16))
+
+
 def test_w8a8_full_size_sampled_rows(torch_cuda):
     """The benchmarked shape (Llama-3.1-70B gate+up, 512 verify tokens), sampled rows."""
     s = LLAMA70B_GATE_UP
